@@ -1,0 +1,147 @@
+"""CPU oracle for the DSpark draft-head hot path -- test infrastructure.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its binding) never calls it.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, single-threaded); this
+module only compiles it with gcc and marshals numpy arrays.  Each function
+cites the passage of the pages it follows in ``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32, BF16 = 0, 1
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(_SO):
+        tmp = _SO + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-o", tmp, os.path.join(_HERE, "oracle.c"), "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build(force=False)
+        lib = ctypes.CDLL(_SO)
+        i64, vp, d = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
+        lib.oracle_head_sample.restype = ctypes.c_int
+        lib.oracle_head_sample.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, d,
+                                           vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_accept_rate.restype = ctypes.c_int
+        lib.oracle_accept_rate.argtypes = [i64, i64, ctypes.c_int, vp, i64, vp, i64, vp, vp]
+        lib.oracle_prefix_schedule.restype = ctypes.c_int
+        lib.oracle_prefix_schedule.argtypes = [i64, i64, vp, vp, i64, vp, vp, vp, vp, vp]
+        _lib = lib
+    return _lib
+
+
+def _dtype_of(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle inputs are float32 or bfloat16 bit patterns (uint16), got {a.dtype}")
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data
+
+
+def head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=None, want_logits=False):
+    """Markov-head block sampler + confidence head + survival (fp64).
+
+    U [B, gamma, V], h [B, gamma, H], W1/W2 [V, r], w_conf [H + r] share one
+    dtype (float32, or uint16 bfloat16 bits).  x0 [B] int32, gumbel
+    [B, gamma, V] float32 or None, force [B, gamma] int32 (-1 = sample) or
+    None.  Returns a dict of tokens, conf, survival, margin (and logits, bias
+    when ``want_logits``).
+    """
+    U, h, W1, W2, w_conf = (np.ascontiguousarray(a) for a in (U, h, W1, W2, w_conf))
+    dt = _dtype_of(U)
+    for a in (h, W1, W2, w_conf):
+        assert _dtype_of(a) == dt
+    B, gamma, V = U.shape
+    H = h.shape[2]
+    r = W1.shape[1]
+    assert h.shape[:2] == (B, gamma) and W1.shape == (V, r) and W2.shape == (V, r) and w_conf.shape == (H + r,)
+    x0 = np.ascontiguousarray(x0, dtype=np.int32)
+    if gumbel is not None:
+        gumbel = np.ascontiguousarray(gumbel, dtype=np.float32)
+        assert gumbel.shape == U.shape
+    if force is not None:
+        force = np.ascontiguousarray(force, dtype=np.int32)
+        assert force.shape == (B, gamma)
+    out = {
+        "tokens": np.empty((B, gamma), np.int32),
+        "conf": np.empty((B, gamma), np.float64),
+        "survival": np.empty((B, gamma), np.float64),
+        "margin": np.empty((B, gamma), np.float64),
+    }
+    if want_logits:
+        out["logits"] = np.empty((B, gamma, V), np.float64)
+        out["bias"] = np.empty((B, gamma, V), np.float64)
+    rc = _load().oracle_head_sample(B, gamma, V, H, r, dt, _p(U), _p(h), _p(W1), _p(W2), _p(w_conf),
+                                    float(b_conf), _p(x0), _p(gumbel), _p(force), _p(out["tokens"]),
+                                    _p(out["conf"]), _p(out["survival"]), _p(out["margin"]),
+                                    _p(out.get("logits")), _p(out.get("bias")))
+    if rc != 0:
+        raise ValueError(f"oracle_head_sample failed ({rc}): token id out of range")
+    return out
+
+
+def accept_rate(d, t, V=None, with_summin=False):
+    """c*_n = 1 - 1/2 ||softmax(d_n) - softmax(t_n)||_1 per row (fp64).
+
+    d, t [N, ld] float32 or bfloat16 bits; the first V columns form a row."""
+    d = np.ascontiguousarray(d)
+    t = np.ascontiguousarray(t)
+    dt = _dtype_of(d)
+    assert _dtype_of(t) == dt
+    N = d.shape[0]
+    assert t.shape[0] == N
+    V = d.shape[1] if V is None else V
+    cs = np.empty(N, np.float64)
+    sm = np.empty(N, np.float64) if with_summin else None
+    _load().oracle_accept_rate(N, V, dt, _p(d), d.shape[1], _p(t), t.shape[1], _p(cs), _p(sm))
+    return (cs, sm) if with_summin else cs
+
+
+def prefix_schedule(conf, sps):
+    """Algorithm 1 on conf [B, gamma] float32 and sps [n_sps] float64.
+
+    Returns dict(prefix_len [B] int32, survival [B, gamma] float32,
+    order [B*gamma] int32, theta float, n_selected int)."""
+    conf = np.ascontiguousarray(conf, dtype=np.float32)
+    sps = np.ascontiguousarray(sps, dtype=np.float64)
+    B, gamma = conf.shape
+    out = {
+        "prefix_len": np.empty(B, np.int32),
+        "survival": np.empty((B, gamma), np.float32),
+        "order": np.empty(B * gamma, np.int32),
+    }
+    th = np.empty(1, np.float64)
+    ns = np.empty(1, np.int64)
+    rc = _load().oracle_prefix_schedule(B, gamma, _p(conf), _p(sps), sps.shape[0], _p(out["prefix_len"]),
+                                        _p(out["survival"]), _p(out["order"]), _p(th), _p(ns))
+    if rc != 0:
+        raise ValueError("oracle_prefix_schedule: need B >= 1 and a table of at least B entries")
+    out["theta"] = float(th[0])
+    out["n_selected"] = int(ns[0])
+    return out

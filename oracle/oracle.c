@@ -1,0 +1,241 @@
+/*
+ * CPU oracle for the DSpark draft-head hot path.  TEST INFRASTRUCTURE ONLY:
+ * nothing but the test suite, the smoke check and the benchmark's CPU-baseline
+ * leg may load or call this library.  The product path never routes here.
+ *
+ * Plain, slow, single-threaded definitions, accumulated in double.  Inputs in
+ * bfloat16 are widened exactly (a bfloat16 is the upper half of a binary32).
+ * This file shares no code with the HIP path.
+ *
+ * Sources (the pages describing the method):
+ *   [W]  "基于 DSpark 的投机解码训练框架原理与实现（论文+代码对照）",
+ *        wangjunjian.com -- section 3.2 (semi-autoregressive generation:
+ *        p_k(v) = softmax(U_k(v) + B_k(x_0, x_<k, v)); the vanilla Markov head,
+ *        paper eq. 5, B(x_{k-1}, .) = W2 . W1[x_{k-1}], rank r; the block
+ *        sampling loop of sample_block_tokens), section 3.3 (confidence head
+ *        fed with h_k and the previous token's Markov embedding W1[x_{k-1}];
+ *        analytic accept rate, paper eq. 8, c* = 1 - 1/2 ||p_d - p_t||_1;
+ *        Algorithm 1, the hardware-aware prefix scheduler), section 8.2
+ *        (rejection-sampling verification, accept with min(1, p_t/p_d)).
+ *   [D]  dpshk.com article on the Qwen3.8-27B-DSpark confidence head,
+ *        section 2 (AcceptRatePredictor is one nn.Linear(input_dim, 1) that
+ *        returns a logit) and section 3 (config.json: confidence head fed with
+ *        the Markov feature, markov_rank 256, hidden 5120, block 7).
+ *
+ * Readings where the pages leave a step open (each also listed in the
+ * design notes):
+ *   - sample(): greedy = argmax of the step logits; Gumbel-max = argmax of
+ *     logits + supplied Gumbel noise (temperature 1).  The argmax decision is
+ *     taken in binary32, the precision of the GPU kernels, on the fp64 score
+ *     rounded once to binary32; exact ties go to the lowest token id.
+ *   - the confidence head's sigmoid is applied to the linear head's logit;
+ *     its input is [h_k ; W1[x_{k-1}]], x_0 = the anchor.
+ *   - survival a_k = prod_{i<=k} c_i.
+ *   - scheduler: survivals are binary32 sequential products; pairs are sorted
+ *     by (survival desc, request asc, position asc); the empty selection has
+ *     tau = B (one bonus token per request) and Btok = B; a pair is accepted
+ *     iff Theta = (tau + a) * SPS(Btok + 1) > Theta_best strictly; the first
+ *     pair that fails, or that would need a batch beyond the table, stops
+ *     the scan.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+/* Exact value of element i of a float32 or bfloat16 buffer. */
+static double val(const void* p, int dtype, int64_t i) {
+    if (dtype == ORACLE_F32) return (double)((const float*)p)[i];
+    uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/*
+ * Block sampler with the vanilla Markov head and the confidence head.
+ *
+ * For each request b, x = x0[b], A = 1.  For k = 1..gamma ([W] 3.2, the
+ * sampling loop; eq. 5; [W] 3.3 and [D] 2 for the confidence head):
+ *   e[j]      = W1[x, j]                               (previous-token embedding)
+ *   bias[v]   = sum_j W2[v, j] * e[j]                  (eq. 5)
+ *   logit[v]  = U[b, k, v] + bias[v]                   (step logits)
+ *   score[v]  = logit[v] + G[b, k, v]   (G absent -> 0; Gumbel-max draw)
+ *   tokens    = lowest v maximising binary32(score[v])
+ *   margin    = largest minus second-largest score (fp64, over distinct v)
+ *   c_k       = sigmoid(sum_i w[i] h[b,k,i] + sum_j w[H+j] e[j] + b_conf)
+ *   A_k       = A_{k-1} * c_k
+ *   x         = force[b, k] if given (>= 0) else the sampled token
+ *
+ * Shapes: U, G [B][gamma][V]; h [B][gamma][H]; W1, W2 [V][r]; w [H + r].
+ * Outputs tokens, conf, survival, margin [B][gamma]; logits and bias
+ * [B][gamma][V] may be NULL.  Returns 0, or -1 on a token id outside [0, V).
+ */
+int oracle_head_sample(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int dtype, const void* U,
+                       const void* h, const void* W1, const void* W2, const void* w, double b_conf,
+                       const int32_t* x0, const float* gumbel, const int32_t* force, int32_t* tokens,
+                       double* conf, double* survival, double* margin, double* logits, double* bias) {
+    double* e = (double*)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
+    if (!e) return -2;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t x = x0[b];
+        double A = 1.0;
+        for (int64_t k = 0; k < gamma; ++k) {
+            if (x < 0 || x >= V) {
+                free(e);
+                return -1;
+            }
+            for (int64_t j = 0; j < r; ++j) e[j] = val(W1, dtype, x * r + j);
+
+            const int64_t row = (b * gamma + k) * V;
+            int64_t best = -1;
+            float best32 = 0.0f;
+            double top1 = -INFINITY, top2 = -INFINITY;
+            for (int64_t v = 0; v < V; ++v) {
+                double s = 0.0;
+                for (int64_t j = 0; j < r; ++j) s += val(W2, dtype, v * r + j) * e[j];
+                double lg = val(U, dtype, row + v) + s;
+                double sc = lg + (gumbel ? (double)gumbel[row + v] : 0.0);
+                if (bias) bias[row + v] = s;
+                if (logits) logits[row + v] = lg;
+                float sc32 = (float)sc;
+                if (best < 0 || sc32 > best32) {
+                    best = v;
+                    best32 = sc32;
+                }
+                if (sc > top1) {
+                    top2 = top1;
+                    top1 = sc;
+                } else if (sc > top2) {
+                    top2 = sc;
+                }
+            }
+            tokens[b * gamma + k] = (int32_t)best;
+            if (margin) margin[b * gamma + k] = top1 - top2;
+
+            double z = b_conf;
+            for (int64_t i = 0; i < H; ++i) z += val(w, dtype, i) * val(h, dtype, (b * gamma + k) * H + i);
+            for (int64_t j = 0; j < r; ++j) z += val(w, dtype, H + j) * e[j];
+            double c = 1.0 / (1.0 + exp(-z));
+            A *= c;
+            conf[b * gamma + k] = c;
+            survival[b * gamma + k] = A;
+
+            x = (force && force[b * gamma + k] >= 0) ? force[b * gamma + k] : best;
+        }
+    }
+    free(e);
+    return 0;
+}
+
+/*
+ * Analytic accept rate, [W] 3.3, paper eq. 8: per row n
+ *   p = softmax(d_n), q = softmax(t_n)
+ *   cstar[n] = 1 - 1/2 sum_v |p_v - q_v|
+ * and, as a second route to the same number, summin[n] = sum_v min(p_v, q_v)
+ * (may be NULL).  Rows are ld elements apart.
+ */
+int oracle_accept_rate(int64_t N, int64_t V, int dtype, const void* d, int64_t ld_d, const void* t,
+                       int64_t ld_t, double* cstar, double* summin) {
+    for (int64_t n = 0; n < N; ++n) {
+        const int64_t od = n * ld_d, ot = n * ld_t;
+        double md = -INFINITY, mt = -INFINITY;
+        for (int64_t v = 0; v < V; ++v) {
+            double a = val(d, dtype, od + v), b = val(t, dtype, ot + v);
+            if (a > md) md = a;
+            if (b > mt) mt = b;
+        }
+        double sd = 0.0, st = 0.0;
+        for (int64_t v = 0; v < V; ++v) {
+            sd += exp(val(d, dtype, od + v) - md);
+            st += exp(val(t, dtype, ot + v) - mt);
+        }
+        double l1 = 0.0, mn = 0.0;
+        for (int64_t v = 0; v < V; ++v) {
+            double p = exp(val(d, dtype, od + v) - md) / sd;
+            double q = exp(val(t, dtype, ot + v) - mt) / st;
+            l1 += fabs(p - q);
+            mn += p < q ? p : q;
+        }
+        cstar[n] = 1.0 - 0.5 * l1;
+        if (summin) summin[n] = mn;
+    }
+    return 0;
+}
+
+/* Sort order of Algorithm 1: survival descending, then request, then
+ * position ascending (a total order on distinct pairs). */
+static const float* g_surv;
+static int cmp_pairs(const void* pa, const void* pb) {
+    int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
+    float sa = g_surv[a], sb = g_surv[b];
+    if (sa > sb) return -1;
+    if (sa < sb) return 1;
+    return (a > b) - (a < b); /* pair id r*gamma + j orders by (r, j) */
+}
+
+/*
+ * Hardware-aware prefix scheduler, [W] 3.3, Algorithm 1 (flowchart):
+ *   a[r][j]  = c[r][0] * ... * c[r][j]         (binary32, left to right)
+ *   sort all (r, j) by a descending
+ *   tau = B, Btok = B, Theta_best = B * SPS(B)
+ *   for each pair in order:
+ *       stop if Btok + 1 > n_sps
+ *       Theta = (tau + a) * SPS(Btok + 1)
+ *       if Theta > Theta_best: accept, tau += a, Btok += 1,
+ *                              l[r] = j + 1, Theta_best = Theta
+ *       else stop
+ * sps[n-1] = SPS(n).  conf values are in [0, 1].
+ * Outputs: prefix_len [B]; survival [B][gamma] and order [B*gamma] (pair ids
+ * r*gamma + j in sorted order) may be NULL; theta [1] = Theta_best;
+ * n_selected [1] = number of accepted pairs.  Returns 0, -1 if n_sps < B.
+ */
+int oracle_prefix_schedule(int64_t B, int64_t gamma, const float* conf, const double* sps, int64_t n_sps,
+                           int32_t* prefix_len, float* survival, int32_t* order, double* theta,
+                           int64_t* n_selected) {
+    if (B < 1 || n_sps < B) return -1;
+    const int64_t n = B * gamma;
+    float* a = (float*)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+    int32_t* ord = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    if (!a || !ord) {
+        free(a);
+        free(ord);
+        return -2;
+    }
+    for (int64_t r = 0; r < B; ++r) {
+        float p = 1.0f;
+        for (int64_t j = 0; j < gamma; ++j) {
+            p = p * conf[r * gamma + j];
+            a[r * gamma + j] = p;
+        }
+    }
+    for (int64_t i = 0; i < n; ++i) ord[i] = (int32_t)i;
+    g_surv = a;
+    qsort(ord, (size_t)n, sizeof(int32_t), cmp_pairs);
+
+    for (int64_t r = 0; r < B; ++r) prefix_len[r] = 0;
+    double tau = (double)B;
+    int64_t btok = B;
+    double best = tau * sps[btok - 1];
+    int64_t sel = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (btok + 1 > n_sps) break;
+        double ai = (double)a[ord[i]];
+        double th = (tau + ai) * sps[btok];
+        if (!(th > best)) break;
+        tau += ai;
+        btok += 1;
+        best = th;
+        prefix_len[ord[i] / gamma] = (int32_t)(ord[i] % gamma + 1);
+        ++sel;
+    }
+    if (survival) memcpy(survival, a, sizeof(float) * (size_t)n);
+    if (order) memcpy(order, ord, sizeof(int32_t) * (size_t)n);
+    if (theta) *theta = best;
+    if (n_selected) *n_selected = sel;
+    free(a);
+    free(ord);
+    return 0;
+}

@@ -1,0 +1,22 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; runs the HIP library")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _host_libs():
+    """Compile the gcc-built helpers (input generator, oracle) if absent."""
+    import oracle
+    import synth
+
+    synth.build(force=False)
+    oracle.build(force=False)

@@ -1,0 +1,402 @@
+"""Pins for the CPU oracle: closed forms, invariants, brute force and
+distributional identities that the pages and the mathematics fix.
+
+Each test targets a mistake the oracle could plausibly make (a swapped
+factor, the wrong previous token, a missing term, a non-strict comparison,
+the wrong tie-break) so that such a mistake fails here.  No test here uses
+the GPU.
+"""
+import itertools
+
+import numpy as np
+import pytest
+from scipy import special, stats
+
+import oracle
+import synth
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _sampler_inputs(rng, B, gamma, V, H, r, w_sd=0.5, U_sd=1.0):
+    return dict(
+        U=rng.normal(0, U_sd, (B, gamma, V)).astype(np.float32),
+        h=rng.normal(0, 1, (B, gamma, H)).astype(np.float32),
+        W1=rng.normal(0, w_sd, (V, r)).astype(np.float32),
+        W2=rng.normal(0, w_sd, (V, r)).astype(np.float32),
+        w_conf=rng.normal(0, 0.3, (H + r,)).astype(np.float32),
+        b_conf=0.1,
+        x0=rng.integers(0, V, B).astype(np.int32),
+    )
+
+
+def _prev_tokens(x0, force):
+    """x_{k-1} for every (b, k) when every step is teacher-forced."""
+    return np.concatenate([x0[:, None], force[:, :-1]], axis=1)
+
+
+# ---------------------------------------------------------------------------
+# Markov bias (eq. 5) and the step logits
+# ---------------------------------------------------------------------------
+def test_zero_W2_gives_plain_argmax_of_U():
+    rng = _rng(1)
+    a = _sampler_inputs(rng, B=3, gamma=4, V=97, H=8, r=6)
+    a["W2"][:] = 0
+    o = oracle.head_sample(**a, want_logits=True)
+    assert np.all(o["bias"] == 0.0)
+    np.testing.assert_array_equal(o["logits"], a["U"].astype(np.float64))
+    np.testing.assert_array_equal(o["tokens"], np.argmax(a["U"], axis=2))
+
+
+def test_one_hot_factors_give_indicator_bias():
+    # W1[v] = e_f(v), W2[v] = e_g(v)  =>  bias[v] = [g(v) == f(x_{k-1})].
+    # f != g, so swapping the roles of W1 and W2 gives a different answer.
+    V, r, B, gamma = 40, 7, 2, 5
+    f = (np.arange(V) * 3) % r
+    g = (np.arange(V) * 5 + 1) % r
+    W1 = np.zeros((V, r), np.float32)
+    W2 = np.zeros((V, r), np.float32)
+    W1[np.arange(V), f] = 1
+    W2[np.arange(V), g] = 1
+    rng = _rng(2)
+    x0 = np.array([3, 17], np.int32)
+    force = rng.integers(0, V, (B, gamma)).astype(np.int32)
+    o = oracle.head_sample(U=np.zeros((B, gamma, V), np.float32), h=np.zeros((B, gamma, 1), np.float32),
+                           W1=W1, W2=W2, w_conf=np.zeros(1 + r, np.float32), b_conf=0.0, x0=x0, force=force,
+                           want_logits=True)
+    prev = _prev_tokens(x0, force)
+    expect = (g[None, None, :] == f[prev][:, :, None]).astype(np.float64)
+    np.testing.assert_array_equal(o["bias"], expect)
+
+
+def test_bias_is_W2_times_previous_W1_row():
+    # library matmul against the oracle's loops, previous tokens pinned by force
+    rng = _rng(3)
+    a = _sampler_inputs(rng, B=2, gamma=6, V=53, H=5, r=9)
+    force = rng.integers(0, 53, (2, 6)).astype(np.int32)
+    o = oracle.head_sample(**a, force=force, want_logits=True)
+    prev = _prev_tokens(a["x0"], force)
+    W1 = a["W1"].astype(np.float64)
+    W2 = a["W2"].astype(np.float64)
+    for b in range(2):
+        for k in range(6):
+            ref = W2 @ W1[prev[b, k]]
+            np.testing.assert_allclose(o["bias"][b, k], ref, rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(o["logits"][b, k], a["U"][b, k] + ref, rtol=1e-12, atol=1e-14)
+
+
+def test_bigram_walk_worked_by_hand():
+    # U = 0, W1 = identity, W2 = permutation matrix with W2[pi(x), x] = 1: the
+    # greedy chain follows pi.  pi = 0->2, 1->4, 2->1, 3->0, 4->3.
+    pi = [2, 4, 1, 0, 3]
+    V = 5
+    W1 = np.eye(V, dtype=np.float32)
+    W2 = np.zeros((V, V), np.float32)
+    for x, y in enumerate(pi):
+        W2[y, x] = 1.0
+    o = oracle.head_sample(U=np.zeros((2, 6, V), np.float32), h=np.zeros((2, 6, 1), np.float32), W1=W1, W2=W2,
+                           w_conf=np.zeros(1 + V, np.float32), b_conf=0.0, x0=np.array([0, 3], np.int32))
+    np.testing.assert_array_equal(o["tokens"][0], [2, 1, 4, 3, 0, 2])
+    np.testing.assert_array_equal(o["tokens"][1], [0, 2, 1, 4, 3, 0])
+
+
+def test_all_equal_scores_pick_lowest_token():
+    V = 31
+    o = oracle.head_sample(U=np.full((2, 3, V), 0.25, np.float32), h=np.zeros((2, 3, 2), np.float32),
+                           W1=np.ones((V, 4), np.float32), W2=np.zeros((V, 4), np.float32),
+                           w_conf=np.zeros(6, np.float32), b_conf=0.0, x0=np.array([5, 30], np.int32))
+    assert np.all(o["tokens"] == 0)
+    assert np.all(o["margin"] == 0.0)
+
+
+def test_decision_is_taken_in_binary32():
+    # Two scores differing by less than half a binary32 ulp at 1.0 round to
+    # the same float, so the lower token id wins the argmax.  The fp64
+    # margin still reports the difference.
+    V = 4
+    U = np.zeros((1, 1, V), np.float32)
+    U[0, 0, 1] = 1.0
+    U[0, 0, 3] = 1.0
+    W1 = np.ones((V, 1), np.float32)
+    W2 = np.zeros((V, 1), np.float32)
+    W2[3, 0] = 2.0**-30  # token 3 larger by 2^-30 in fp64, equal in binary32
+    o = oracle.head_sample(U=U, h=np.zeros((1, 1, 1), np.float32), W1=W1, W2=W2, w_conf=np.zeros(2, np.float32),
+                           b_conf=0.0, x0=np.array([0], np.int32))
+    assert o["tokens"][0, 0] == 1
+    assert o["margin"][0, 0] == pytest.approx(2.0**-30, rel=1e-9)
+
+
+def test_bf16_inputs_are_widened_exactly():
+    # values exactly representable in bfloat16 give identical results in both dtypes
+    rng = _rng(4)
+    a = _sampler_inputs(rng, B=2, gamma=3, V=64, H=6, r=8)
+    for k in ("U", "h", "W1", "W2", "w_conf"):
+        a[k] = np.round(a[k] * 16) / 16  # few mantissa bits: exact in bf16
+    o32 = oracle.head_sample(**a, want_logits=True)
+    a16 = dict(a)
+    for k in ("U", "h", "W1", "W2", "w_conf"):
+        a16[k] = synth.f32_to_bf16(a[k])
+        assert np.array_equal(synth.bf16_to_f32(a16[k]), a[k])
+    o16 = oracle.head_sample(**a16, want_logits=True)
+    for k in ("tokens", "conf", "survival", "logits", "bias"):
+        np.testing.assert_array_equal(o32[k], o16[k])
+
+
+def test_gumbel_max_draws_follow_the_softmax_chain():
+    # Gumbel-max is an exact sampler of softmax(logits); across two dependent
+    # steps the sequence (x1, x2) has probability
+    # softmax(U_1 + W2 W1[x0])[x1] * softmax(U_2 + W2 W1[x1])[x2].
+    rng = _rng(5)
+    V, r, gamma, n = 4, 2, 2, 200_000
+    U1 = rng.normal(0, 1, (gamma, V)).astype(np.float32)
+    W1 = rng.normal(0, 1, (V, r)).astype(np.float32)
+    W2 = rng.normal(0, 1, (V, r)).astype(np.float32)
+    x0 = 2
+    U = np.broadcast_to(U1, (n, gamma, V)).copy()
+    G = synth.gumbel(synth.key(77, 1), (n, gamma, V))
+    o = oracle.head_sample(U=U, h=np.zeros((n, gamma, 1), np.float32), W1=W1, W2=W2,
+                           w_conf=np.zeros(1 + r, np.float32), b_conf=0.0, x0=np.full(n, x0, np.int32), gumbel=G)
+    W1d, W2d = W1.astype(np.float64), W2.astype(np.float64)
+    p1 = special.softmax(U1[0] + W2d @ W1d[x0])
+    prob = np.array([p1[a] * special.softmax(U1[1] + W2d @ W1d[a])[b] for a in range(V) for b in range(V)])
+    counts = np.bincount(o["tokens"][:, 0] * V + o["tokens"][:, 1], minlength=V * V)
+    chi2 = np.sum((counts - n * prob) ** 2 / (n * prob))
+    assert stats.chi2.sf(chi2, df=V * V - 1) > 1e-3, chi2
+
+
+# ---------------------------------------------------------------------------
+# Confidence head and survival
+# ---------------------------------------------------------------------------
+def test_confidence_closed_forms():
+    rng = _rng(6)
+    B, gamma, V, H, r = 2, 5, 30, 7, 4
+    a = _sampler_inputs(rng, B, gamma, V, H, r)
+    force = rng.integers(0, V, (B, gamma)).astype(np.int32)
+    prev = _prev_tokens(a["x0"], force)
+
+    a0 = dict(a, w_conf=np.zeros(H + r, np.float32), b_conf=0.3)
+    o = oracle.head_sample(**a0, force=force)
+    np.testing.assert_allclose(o["conf"], special.expit(0.3), rtol=1e-15)
+
+    i = 4  # one-hot on the hidden part picks h[b, k, i]
+    w = np.zeros(H + r, np.float32)
+    w[i] = 1.0
+    o = oracle.head_sample(**dict(a, w_conf=w, b_conf=-0.2), force=force)
+    np.testing.assert_allclose(o["conf"], special.expit(a["h"][:, :, i].astype(np.float64) - 0.2), rtol=1e-14)
+
+    j = 2  # one-hot on the Markov part picks W1[x_{k-1}, j]: the PREVIOUS token
+    w = np.zeros(H + r, np.float32)
+    w[H + j] = 1.0
+    o = oracle.head_sample(**dict(a, w_conf=w, b_conf=0.5), force=force)
+    np.testing.assert_allclose(o["conf"], special.expit(a["W1"][prev, j].astype(np.float64) + 0.5), rtol=1e-14)
+
+
+def test_survival_is_running_product_of_conf():
+    rng = _rng(7)
+    a = _sampler_inputs(rng, B=3, gamma=9, V=41, H=6, r=5)
+    o = oracle.head_sample(**a)
+    np.testing.assert_allclose(o["survival"], np.cumprod(o["conf"], axis=1), rtol=1e-15)
+    assert np.all(o["survival"][:, 0] == o["conf"][:, 0])
+    assert np.all(np.diff(o["survival"], axis=1) <= 0)
+    assert np.all((o["survival"] > 0) & (o["survival"] <= 1))
+
+
+def test_force_feeds_the_next_step_but_not_the_reported_token():
+    rng = _rng(8)
+    a = _sampler_inputs(rng, B=1, gamma=4, V=23, H=3, r=4, w_sd=1.0)
+    free = oracle.head_sample(**a)
+    force = np.full((1, 4), -1, np.int32)
+    alt = (free["tokens"][0, 0] + 7) % 23
+    force[0, 0] = alt
+    forced = oracle.head_sample(**a, force=force)
+    assert forced["tokens"][0, 0] == free["tokens"][0, 0]  # step 1 still reports its own sample
+    # step 2 onwards continues from the forced token: same as a fresh call whose anchor is it
+    a2 = dict(a, U=a["U"][:, 1:], h=a["h"][:, 1:], x0=np.array([alt], np.int32))
+    tail = oracle.head_sample(**a2)
+    np.testing.assert_array_equal(forced["tokens"][:, 1:], tail["tokens"])
+
+
+# ---------------------------------------------------------------------------
+# Analytic accept rate (eq. 8)
+# ---------------------------------------------------------------------------
+def test_accept_rate_identical_rows_is_exactly_one():
+    rng = _rng(9)
+    d = rng.normal(0, 3, (5, 300)).astype(np.float32)
+    np.testing.assert_array_equal(oracle.accept_rate(d, d.copy()), 1.0)
+    db = synth.f32_to_bf16(d)
+    np.testing.assert_array_equal(oracle.accept_rate(db, db.copy()), 1.0)
+
+
+def test_accept_rate_shift_invariance():
+    rng = _rng(10)
+    d = (np.round(rng.normal(0, 2, (4, 200)) * 64) / 64).astype(np.float32)
+    t = d + np.float32(3.0)  # exact in binary32 for these values
+    np.testing.assert_allclose(oracle.accept_rate(d, t), 1.0, atol=1e-13)
+
+
+def test_accept_rate_two_token_closed_form():
+    rng = _rng(11)
+    d = rng.normal(0, 2, (50, 2)).astype(np.float32)
+    t = rng.normal(0, 2, (50, 2)).astype(np.float32)
+    d64, t64 = d.astype(np.float64), t.astype(np.float64)
+    ref = 1 - np.abs(special.expit(d64[:, 1] - d64[:, 0]) - special.expit(t64[:, 1] - t64[:, 0]))
+    np.testing.assert_allclose(oracle.accept_rate(d, t), ref, atol=1e-14)
+
+
+def test_accept_rate_equals_rejection_sampling_acceptance():
+    # Verification accepts a draft token x ~ p_d with probability
+    # min(1, p_t(x)/p_d(x)); its expectation is the accept rate.
+    rng = _rng(12)
+    d = rng.normal(0, 2, (8, 500)).astype(np.float32)
+    t = (0.8 * d + rng.normal(0, 1.5, d.shape)).astype(np.float32)
+    p = special.softmax(d.astype(np.float64), axis=1)
+    q = special.softmax(t.astype(np.float64), axis=1)
+    expect = np.sum(p * np.minimum(1.0, q / p), axis=1)
+    cs, sm = oracle.accept_rate(d, t, with_summin=True)
+    np.testing.assert_allclose(cs, expect, atol=1e-12)
+    np.testing.assert_allclose(sm, expect, atol=1e-12)
+
+
+def test_accept_rate_monte_carlo_of_the_verify_rule():
+    rng = _rng(13)
+    V, n = 6, 400_000
+    d = rng.normal(0, 1, (1, V)).astype(np.float32)
+    t = rng.normal(0, 1, (1, V)).astype(np.float32)
+    p = special.softmax(d[0].astype(np.float64))
+    q = special.softmax(t[0].astype(np.float64))
+    x = rng.choice(V, size=n, p=p)
+    acc = rng.random(n) < np.minimum(1.0, q[x] / p[x])
+    c = oracle.accept_rate(d, t)[0]
+    assert abs(acc.mean() - c) < 5 * np.sqrt(c * (1 - c) / n)
+
+
+def test_accept_rate_disjoint_and_bounds_and_symmetry():
+    d = np.full((1, 10), -60.0, np.float32)
+    t = np.full((1, 10), -60.0, np.float32)
+    d[0, 2] = 60.0
+    t[0, 7] = 60.0
+    assert oracle.accept_rate(d, t)[0] < 1e-40
+    rng = _rng(14)
+    d = rng.normal(0, 4, (20, 333)).astype(np.float32)
+    t = rng.normal(0, 4, (20, 333)).astype(np.float32)
+    c1 = oracle.accept_rate(d, t)
+    assert np.all(c1 >= -1e-15) and np.all(c1 <= 1 + 1e-15)
+    np.testing.assert_allclose(oracle.accept_rate(t, d), c1, atol=1e-15)
+    perm = rng.permutation(333)
+    np.testing.assert_allclose(oracle.accept_rate(d[:, perm], t[:, perm]), c1, atol=1e-13)
+
+
+def test_accept_rate_row_stride():
+    rng = _rng(15)
+    V, ld = 70, 96
+    d = rng.normal(0, 2, (6, ld)).astype(np.float32)
+    t = rng.normal(0, 2, (6, ld)).astype(np.float32)
+    d[:, V:] = 1e30  # padding beyond V is never read
+    t[:, V:] = -1e30
+    ref = oracle.accept_rate(np.ascontiguousarray(d[:, :V]), np.ascontiguousarray(t[:, :V]))
+    np.testing.assert_array_equal(oracle.accept_rate(d, t, V=V), ref)
+
+
+# ---------------------------------------------------------------------------
+# Prefix scheduler (Algorithm 1)
+# ---------------------------------------------------------------------------
+def test_schedule_worked_by_hand():
+    conf = np.array([[0.9, 0.5], [0.8, 0.8]], np.float32)
+    sps = np.array([1.0, 1.0, 0.9, 0.8, 0.7, 0.5])
+    # survivals: (0,1) 0.9, (1,1) 0.8, (1,2) 0.64, (0,2) 0.45
+    # Theta0 = 2*1.0; 2.9*0.9 = 2.61 > 2; 3.7*0.8 = 2.96 > 2.61;
+    # 4.34*0.7 = 3.038 > 2.96; 4.79*0.5 = 2.395 -> stop
+    o = oracle.prefix_schedule(conf, sps)
+    np.testing.assert_array_equal(o["prefix_len"], [1, 2])
+    np.testing.assert_array_equal(o["order"], [0, 2, 3, 1])
+    assert o["n_selected"] == 3
+    assert o["theta"] == pytest.approx(3.038, abs=1e-6)
+    # a table of 4 entries caps the batch at 4 tokens: 2 pairs only
+    o = oracle.prefix_schedule(conf, sps[:4])
+    np.testing.assert_array_equal(o["prefix_len"], [1, 1])
+    assert o["theta"] == pytest.approx(2.96, abs=1e-6)
+
+
+def test_schedule_strict_improvement_and_empty_selection():
+    # equal Theta stops the scan
+    o = oracle.prefix_schedule(np.array([[1.0, 0.0]], np.float32), np.ones(3))
+    np.testing.assert_array_equal(o["prefix_len"], [1])
+    assert o["theta"] == 2.0
+    # a first pair that lowers Theta leaves every request at length 0
+    o = oracle.prefix_schedule(np.array([[0.5, 0.5], [0.5, 0.5]], np.float32), np.array([1.0, 3.0, 0.1, 0.1, 0.1]))
+    np.testing.assert_array_equal(o["prefix_len"], [0, 0])
+    assert o["theta"] == 6.0 and o["n_selected"] == 0
+
+
+def test_schedule_tie_order_and_fp32_survival():
+    conf = np.full((3, 2), 0.5, np.float32)
+    o = oracle.prefix_schedule(conf, np.ones(10))
+    np.testing.assert_array_equal(o["order"], [0, 2, 4, 1, 3, 5])
+    rng = _rng(16)
+    conf = rng.random((7, 9)).astype(np.float32)
+    o = oracle.prefix_schedule(conf, np.ones(80))
+    np.testing.assert_array_equal(o["survival"], np.cumprod(conf, axis=1, dtype=np.float32))
+
+
+def _exhaustive_best(conf, sps):
+    B, gamma = conf.shape
+    a = np.cumprod(conf, axis=1, dtype=np.float32).astype(np.float64)
+    best = -np.inf
+    for ell in itertools.product(range(gamma + 1), repeat=B):
+        n = B + sum(ell)
+        if n > len(sps):
+            continue
+        tau = B + sum(a[r, :l].sum() for r, l in enumerate(ell))
+        best = max(best, tau * sps[n - 1])
+    return best
+
+
+def test_schedule_matches_exhaustive_search_for_step_rate_tables():
+    # With SPS(n) = 1/(alpha + beta n) the throughput of the best selection of
+    # n pairs is unimodal in n, so the greedy scan's first stop is the global
+    # optimum over every choice of prefix lengths.
+    rng = _rng(17)
+    for trial in range(150):
+        B, gamma = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        conf = (1 / (1 + np.exp(-rng.normal(1.0, 1.5, (B, gamma))))).astype(np.float32)
+        alpha, beta = rng.uniform(0.5, 3.0), rng.uniform(0.01, 1.5)
+        n_sps = B * (gamma + 1) + int(rng.integers(0, 3))
+        sps = 1.0 / (alpha + beta * np.arange(1, n_sps + 1))
+        o = oracle.prefix_schedule(conf, sps)
+        best = _exhaustive_best(conf, sps)
+        assert o["theta"] == pytest.approx(best, rel=1e-12), trial
+        a = np.cumprod(conf, axis=1, dtype=np.float32).astype(np.float64)
+        ell = o["prefix_len"]
+        tau = B + sum(a[r, :l].sum() for r, l in enumerate(ell))
+        assert tau * sps[B + ell.sum() - 1] == pytest.approx(o["theta"], rel=1e-12)
+
+
+def test_schedule_increasing_table_takes_every_pair_up_to_capacity():
+    s = synth.SCHEDULE_TRAIN
+    conf = synth.schedule_conf(s)
+    o = oracle.prefix_schedule(conf, synth.sps_table(s.n_sps, "tokens"))
+    # SPS(n) = n/(2 + 0.004 n) increases, so every pair improves Theta until
+    # the table runs out at Btok = n_sps.
+    assert o["n_selected"] == min(s.B * s.gamma, s.n_sps - s.B)
+    surv = o["survival"].reshape(-1)
+    chosen = o["order"][: o["n_selected"]]
+    rest = o["order"][o["n_selected"]:]
+    assert surv[chosen].min() >= surv[rest].max()
+
+
+def test_schedule_invariants_on_training_workload():
+    s = synth.SCHEDULE_TRAIN
+    conf = synth.schedule_conf(s)
+    o = oracle.prefix_schedule(conf, synth.sps_table(s.n_sps, "steps"))
+    ell, order = o["prefix_len"], o["order"]
+    assert np.array_equal(np.sort(order), np.arange(s.B * s.gamma))
+    surv = o["survival"].reshape(-1)
+    assert np.all(np.diff(surv[order]) <= 0)
+    assert ell.sum() == o["n_selected"] and np.all((ell >= 0) & (ell <= s.gamma))
+    sel = order[: o["n_selected"]]
+    for pid in sel:  # every selected (r, j) has (r, j' < j) selected too
+        r, j = divmod(int(pid), s.gamma)
+        assert j < ell[r]
+    assert 0 < o["n_selected"] < s.B * s.gamma  # the step-rate curve stops early

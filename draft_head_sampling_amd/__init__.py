@@ -1,0 +1,228 @@
+"""Python binding of libdspark.so, the MI355X (gfx950) draft-head hot path.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/dspark.h``.  PyTorch supplies
+device memory and the current stream, nothing else.  There is no fallback:
+if the library is missing or no GPU is present, calls raise.
+
+Entry points (same names as the C ABI):
+  head_sample      Markov-head block sampler + confidence head + survival
+  accept_rate      analytic accept rate 1 - 1/2 ||softmax(d) - softmax(t)||_1
+  prefix_schedule  hardware-aware prefix scheduler (Algorithm 1)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from functools import partial
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdspark.so")
+
+DSPARK_F32, DSPARK_BF16 = 0, 1
+_STATUS = {0: "ok", 1: "null argument", 2: "bad shape", 3: "bad dtype", 4: "workspace", 5: "HIP error"}
+
+_lib = None
+
+
+class DsparkError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status} ({_STATUS.get(status, '?')})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library, with argument types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m draft_head_sampling_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp, sz, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
+    L.dspark_head_sample.restype = i32
+    L.dspark_head_sample.argtypes = [i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp,
+                                     vp, vp, vp, sz, vp]
+    L.dspark_accept_rate.restype = i32
+    L.dspark_accept_rate.argtypes = [i64, i64, i32, vp, i64, vp, i64, vp, vp, sz, vp]
+    L.dspark_prefix_schedule.restype = i32
+    L.dspark_prefix_schedule.argtypes = [i64, i64, vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dspark_status_string.restype = ctypes.c_char_p
+    L.dspark_status_string.argtypes = [i32]
+    L.dspark_head_sample_workspace_size.restype = sz
+    L.dspark_head_sample_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32]
+    L.dspark_accept_rate_workspace_size.restype = sz
+    L.dspark_accept_rate_workspace_size.argtypes = [i64, i64, i32]
+    L.dspark_prefix_schedule_workspace_size.restype = sz
+    L.dspark_prefix_schedule_workspace_size.argtypes = [i64, i64]
+    _lib = L
+    return L
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DSPARK_F32
+    if t.dtype == torch.bfloat16:
+        return DSPARK_BF16
+    raise TypeError(f"expected float32 or bfloat16, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _opt(t, name, dtype=None, shape=None) -> int | None:
+    return None if t is None else _dev(t, name, dtype, shape)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise DsparkError(fn, status)
+
+
+def head_sample_workspace_size(B, gamma, V, H, r, dtype=DSPARK_BF16) -> int:
+    return int(lib().dspark_head_sample_workspace_size(B, gamma, V, H, r, dtype))
+
+
+def prepare_head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=None, *, tokens=None, conf=None,
+                        survival=None, logits_out=None, bias_out=None, workspace=None, stream=None):
+    """Validate once and return (call, outputs): ``call()`` enqueues
+    dspark_head_sample on the stream with these exact buffers."""
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    H = h.shape[2] if h is not None else 0
+    dt = _dtype_code(U)
+    dev = U.device
+    tokens = torch.empty((B, gamma), dtype=torch.int32, device=dev) if tokens is None else tokens
+    conf = torch.empty((B, gamma), dtype=torch.float32, device=dev) if conf is None else conf
+    survival = torch.empty((B, gamma), dtype=torch.float32, device=dev) if survival is None else survival
+    args = (
+        B, gamma, V, H, r, dt,
+        _dev(U, "U", U.dtype, (B, gamma, V)),
+        _opt(h, "h", U.dtype, (B, gamma, H)),
+        _dev(W1, "W1", U.dtype, (V, r)),
+        _dev(W2, "W2", U.dtype, (V, r)),
+        _dev(w_conf, "w_conf", U.dtype, (H + r,)),
+        float(b_conf),
+        _dev(x0, "x0", torch.int32, (B,)),
+        _opt(gumbel, "gumbel", torch.float32, (B, gamma, V)),
+        _opt(force, "force", torch.int32, (B, gamma)),
+        _dev(tokens, "tokens", torch.int32, (B, gamma)),
+        _dev(conf, "conf", torch.float32, (B, gamma)),
+        _dev(survival, "survival", torch.float32, (B, gamma)),
+        _opt(logits_out, "logits_out", torch.float32, (B, gamma, V)),
+        _opt(bias_out, "bias_out", torch.float32, (B, gamma, V)),
+    )
+    ws, wsb = _workspace(head_sample_workspace_size(B, gamma, V, H, r, dt), dev, workspace)
+    st = _stream(dev) if stream is None else stream
+    fn = partial(lib().dspark_head_sample, *args, None if ws is None else ws.data_ptr(), wsb, st)
+    outs = {"tokens": tokens, "conf": conf, "survival": survival, "_workspace": ws}
+    if logits_out is not None:
+        outs["logits"] = logits_out
+    if bias_out is not None:
+        outs["bias"] = bias_out
+    return (lambda: _check("dspark_head_sample", fn())), outs
+
+
+def head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=None, *, want_logits=False, workspace=None):
+    """Sample one draft block per request.
+
+    U [B, gamma, V], h [B, gamma, H], W1/W2 [V, r], w_conf [H + r]: float32 or
+    bfloat16 CUDA tensors of one dtype; x0 [B] int32; gumbel [B, gamma, V]
+    float32 or None (greedy); force [B, gamma] int32 (-1 = sample) or None.
+    Returns dict(tokens [B, gamma] int32, conf, survival [B, gamma] float32
+    [, logits, bias [B, gamma, V] float32 when want_logits]).
+    """
+    lo = bo = None
+    if want_logits:
+        lo = torch.empty(U.shape, dtype=torch.float32, device=U.device)
+        bo = torch.empty(U.shape, dtype=torch.float32, device=U.device)
+    call, outs = prepare_head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel, force, logits_out=lo, bias_out=bo,
+                                     workspace=workspace)
+    call()
+    outs.pop("_workspace")
+    return outs
+
+
+def prepare_accept_rate(draft, target, V=None, *, out=None, workspace=None, stream=None):
+    N, ldd = draft.shape
+    ldt = target.shape[1]
+    V = ldd if V is None else V
+    dt = _dtype_code(draft)
+    dev = draft.device
+    if target.shape[0] != N:
+        raise ValueError("draft and target need the same number of rows")
+    out = torch.empty(N, dtype=torch.float32, device=dev) if out is None else out
+    ws, wsb = _workspace(int(lib().dspark_accept_rate_workspace_size(N, V, dt)), dev, workspace)
+    args = (N, V, dt, _dev(draft, "draft", draft.dtype), ldd, _dev(target, "target", draft.dtype), ldt,
+            _dev(out, "accept_rate", torch.float32, (N,)), None if ws is None else ws.data_ptr(), wsb,
+            _stream(dev) if stream is None else stream)
+    fn = partial(lib().dspark_accept_rate, *args)
+    return (lambda: _check("dspark_accept_rate", fn())), {"accept_rate": out, "_workspace": ws}
+
+
+def accept_rate(draft, target, V=None, *, workspace=None):
+    """c*_n = 1 - 1/2 ||softmax(draft_n[:V]) - softmax(target_n[:V])||_1.
+
+    draft [N, ld_d], target [N, ld_t]: float32 or bfloat16 CUDA tensors (the
+    row stride may exceed V).  Returns float32 [N]."""
+    call, outs = prepare_accept_rate(draft, target, V, workspace=workspace)
+    call()
+    return outs["accept_rate"]
+
+
+def prepare_prefix_schedule(conf, sps, *, want_order=True, workspace=None, stream=None):
+    B, gamma = conf.shape
+    dev = conf.device
+    n_sps = sps.shape[0]
+    outs = {
+        "prefix_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "survival": torch.empty((B, gamma), dtype=torch.float32, device=dev),
+        "order": torch.empty(B * gamma, dtype=torch.int32, device=dev) if want_order else None,
+        "theta": torch.empty(1, dtype=torch.float64, device=dev),
+        "n_selected": torch.empty(1, dtype=torch.int32, device=dev),
+    }
+    ws, wsb = _workspace(int(lib().dspark_prefix_schedule_workspace_size(B, gamma)), dev, workspace)
+    args = (B, gamma, _dev(conf, "conf", torch.float32, (B, gamma)), _dev(sps, "sps", torch.float64, (n_sps,)), n_sps,
+            _dev(outs["prefix_len"], "prefix_len"), _dev(outs["survival"], "survival"),
+            _opt(outs["order"], "order"), _dev(outs["theta"], "theta"), _dev(outs["n_selected"], "n_selected"),
+            None if ws is None else ws.data_ptr(), wsb, _stream(dev) if stream is None else stream)
+    fn = partial(lib().dspark_prefix_schedule, *args)
+    outs["_workspace"] = ws
+    return (lambda: _check("dspark_prefix_schedule", fn())), outs
+
+
+def prefix_schedule(conf, sps, *, want_order=True, workspace=None):
+    """Algorithm 1 on conf [B, gamma] float32 and sps [n_sps] float64 (CUDA).
+
+    Returns dict(prefix_len [B] int32, survival [B, gamma] float32,
+    order [B*gamma] int32, theta [1] float64, n_selected [1] int32)."""
+    call, outs = prepare_prefix_schedule(conf, sps, want_order=want_order, workspace=workspace)
+    call()
+    outs.pop("_workspace")
+    return outs

@@ -1,0 +1,110 @@
+// C ABI of the draft-head hot path: host-side argument checks, workspace
+// queries and dispatch to the kernels.  Every check runs before anything is
+// enqueued, and no C++ exception crosses the interface.
+#include "../../include/dspark.h"
+#include "internal.h"
+
+#define DSPARK_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int64_t kMaxV = 0x7fffffff;
+constexpr int64_t kMaxRank = 1024;      // Markov rank: the gathered rows of W1 live in LDS
+constexpr int64_t kMaxSchedPairs = 8192;  // one workgroup sorts all pairs in LDS
+constexpr int64_t kMaxRequests = 65535 * 8;  // request groups of 8 along grid.y
+
+bool mul_ok(int64_t a, int64_t b, int64_t limit = INT64_MAX / 16) {
+    return a == 0 || b == 0 || (a <= limit / b);
+}
+
+dspark_status_t check_workspace(void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return DSPARK_OK;
+    if (!ws || ws_bytes < need || ((uintptr_t)ws % 256) != 0) return DSPARK_ERR_WORKSPACE;
+    return DSPARK_OK;
+}
+
+bool sampler_shape_ok(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r) {
+    if (B < 0 || B > kMaxRequests || gamma < 0 || V < 1 || V > kMaxV || H < 0 || r < 1 || r > kMaxRank)
+        return false;
+    return mul_ok(B, gamma) && mul_ok(B * gamma, V) && mul_ok(B * gamma, H) && mul_ok(V, r) &&
+           B * gamma <= 0x7fffffff;
+}
+
+dspark_status_t hip_status(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP; }
+
+}  // namespace
+
+DSPARK_EXPORT const char* dspark_status_string(dspark_status_t s) {
+    switch (s) {
+        case DSPARK_OK: return "ok";
+        case DSPARK_ERR_NULL_ARG: return "a required pointer argument is NULL";
+        case DSPARK_ERR_BAD_SHAPE: return "a size argument is out of range";
+        case DSPARK_ERR_BAD_DTYPE: return "unknown dtype";
+        case DSPARK_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+        case DSPARK_ERR_HIP: return "HIP launch or runtime error";
+    }
+    return "unknown status";
+}
+
+DSPARK_EXPORT dspark_status_t dspark_head_sample(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r,
+                                                 int32_t dtype, const void* U, const void* h, const void* W1,
+                                                 const void* W2, const void* w_conf, float b_conf, const int32_t* x0,
+                                                 const float* gumbel, const int32_t* force, int32_t* tokens,
+                                                 float* conf, float* survival, float* logits_out, float* bias_out,
+                                                 void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return DSPARK_ERR_BAD_DTYPE;
+    if (!sampler_shape_ok(B, gamma, V, H, r)) return DSPARK_ERR_BAD_SHAPE;
+    if (B == 0 || gamma == 0) return DSPARK_OK;
+    dspark_status_t st = check_workspace(workspace, workspace_bytes, dspark::head_sample_workspace(B, gamma, V, r));
+    if (st != DSPARK_OK) return st;
+    if (!U || !W1 || !W2 || !w_conf || !x0 || !tokens || !conf || !survival || (H > 0 && !h))
+        return DSPARK_ERR_NULL_ARG;
+    return hip_status(dspark::head_sample_launch(B, gamma, V, H, r, dtype, U, h, W1, W2, w_conf, b_conf, x0, gumbel,
+                                                 force, tokens, conf, survival, logits_out, bias_out, workspace,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+DSPARK_EXPORT dspark_status_t dspark_accept_rate(int64_t N, int64_t V, int32_t dtype, const void* draft,
+                                                 int64_t ld_draft, const void* target, int64_t ld_target,
+                                                 float* accept_rate, void* workspace, size_t workspace_bytes,
+                                                 void* stream) {
+    if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return DSPARK_ERR_BAD_DTYPE;
+    if (N < 0 || V < 1 || V > kMaxV || ld_draft < V || ld_target < V) return DSPARK_ERR_BAD_SHAPE;
+    if (!mul_ok(N, ld_draft) || !mul_ok(N, ld_target)) return DSPARK_ERR_BAD_SHAPE;
+    if (N == 0) return DSPARK_OK;
+    dspark_status_t st = check_workspace(workspace, workspace_bytes, dspark::accept_rate_workspace(N, V));
+    if (st != DSPARK_OK) return st;
+    if (!draft || !target || !accept_rate) return DSPARK_ERR_NULL_ARG;
+    return hip_status(dspark::accept_rate_launch(N, V, dtype, draft, ld_draft, target, ld_target, accept_rate,
+                                                 workspace, static_cast<hipStream_t>(stream)));
+}
+
+DSPARK_EXPORT dspark_status_t dspark_prefix_schedule(int64_t B, int64_t gamma, const float* conf, const double* sps,
+                                                     int64_t n_sps, int32_t* prefix_len, float* survival_out,
+                                                     int32_t* order_out, double* theta_out, int32_t* n_selected_out,
+                                                     void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 1 || gamma < 0 || n_sps < B || !mul_ok(B, gamma) || B * gamma > kMaxSchedPairs)
+        return DSPARK_ERR_BAD_SHAPE;
+    dspark_status_t st = check_workspace(workspace, workspace_bytes, dspark::prefix_schedule_workspace(B, gamma));
+    if (st != DSPARK_OK) return st;
+    if (!sps || !prefix_len || (gamma > 0 && !conf)) return DSPARK_ERR_NULL_ARG;
+    return hip_status(dspark::prefix_schedule_launch(B, gamma, conf, sps, n_sps, prefix_len, survival_out, order_out,
+                                                     theta_out, n_selected_out, workspace,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
+DSPARK_EXPORT size_t dspark_head_sample_workspace_size(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r,
+                                                       int32_t) {
+    if (!sampler_shape_ok(B, gamma, V, H, r)) return 0;
+    return dspark::head_sample_workspace(B, gamma, V, r);
+}
+
+DSPARK_EXPORT size_t dspark_accept_rate_workspace_size(int64_t N, int64_t V, int32_t) {
+    if (N < 0 || V < 1 || V > kMaxV) return 0;
+    return dspark::accept_rate_workspace(N, V);
+}
+
+DSPARK_EXPORT size_t dspark_prefix_schedule_workspace_size(int64_t B, int64_t gamma) {
+    if (B < 1 || gamma < 0 || !mul_ok(B, gamma) || B * gamma > kMaxSchedPairs) return 0;
+    return dspark::prefix_schedule_workspace(B, gamma);
+}

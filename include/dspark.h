@@ -1,0 +1,164 @@
+/*
+ * dspark.h -- C ABI of the MI355X (gfx950) draft-head hot path of DSpark's
+ * semi-autoregressive drafter: the Markov-head block sampler with its
+ * confidence head, the analytic accept rate, and the hardware-aware prefix
+ * scheduler.
+ *
+ * Sources:
+ *   [W] "基于 DSpark 的投机解码训练框架原理与实现（论文+代码对照）" (wangjunjian.com),
+ *       sections 3.2, 3.3 and 8.2.
+ *   [D] dpshk.com article on the Qwen3.8-27B-DSpark confidence head
+ *       (AcceptRatePredictor), sections 2 and 3.
+ *
+ * Conventions shared by every entry point:
+ *   - Array pointers are DEVICE pointers on the current HIP device, owned by
+ *     the caller.  Scalars are host values.  The library keeps no pointer
+ *     after a call returns, allocates no memory and holds no mutable global
+ *     state; concurrent calls are safe when they use distinct workspaces.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) without host synchronisation.  Outputs are valid once the
+ *     stream has reached the point of the call.
+ *   - Workspace: device scratch owned by the caller.  dspark_*_workspace_size
+ *     returns the bytes an entry point needs for given shapes (0 means the
+ *     workspace argument may be NULL).  A workspace must be at least that
+ *     large and 256-byte aligned; workspace_bytes is its size.  It needs no
+ *     initialisation and its contents after a call are unspecified.  Calls
+ *     that may overlap in time must not share a workspace.
+ *   - Errors: every argument check runs on the host before anything is
+ *     enqueued; on failure a non-zero status is returned and nothing is
+ *     enqueued.  A failed launch returns DSPARK_ERR_HIP.  No C++ exception
+ *     crosses this interface.
+ *   - Empty sampler and accept-rate problems (B == 0, gamma == 0, N == 0)
+ *     are valid and enqueue nothing.  The scheduler needs B >= 1 and always
+ *     writes its outputs (gamma == 0 selects nothing).
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSPARK_OK = 0,
+    DSPARK_ERR_NULL_ARG = 1,  /* a required pointer is NULL */
+    DSPARK_ERR_BAD_SHAPE = 2, /* a size is negative, zero where it may not be, or too large */
+    DSPARK_ERR_BAD_DTYPE = 3, /* dtype is not one of dspark_dtype_t */
+    DSPARK_ERR_WORKSPACE = 4, /* workspace too small or misaligned */
+    DSPARK_ERR_HIP = 5        /* a HIP call or kernel launch failed */
+} dspark_status_t;
+
+typedef enum {
+    DSPARK_F32 = 0, /* IEEE binary32 */
+    DSPARK_BF16 = 1 /* bfloat16: the upper 16 bits of a binary32 */
+} dspark_dtype_t;
+
+/*
+ * dspark_head_sample -- sequential Markov-head block sampler, confidence head
+ * and survival products for one draft block of `gamma` positions for each of
+ * `B` requests ([W] 3.2: p_k(v) proportional to exp(U_k(v) + B_k(x_{k-1}, v)),
+ * the vanilla Markov head B(x_{k-1}, .) = W2 . W1[x_{k-1}] of paper eq. 5,
+ * and the block sampling loop in which each sampled token feeds the next
+ * step; [W] 3.3 and [D] 2 for the confidence head; [W] 3.3 Algorithm 1 for
+ * the survival products).
+ *
+ * For every request b, with x_0 = x0[b], and k = 1..gamma:
+ *   e          = W1[x_{k-1}, :]                          (row gather)
+ *   bias[v]    = sum_j W2[v, j] * e[j]                   (fp32 accumulation)
+ *   logit[v]   = U[b, k, v] + bias[v]
+ *   tokens[b,k]= argmax_v (logit[v] + G[b, k, v])        (G = 0 if gumbel == NULL;
+ *                                                         exact ties -> lowest v)
+ *   conf[b,k]  = sigmoid(sum_i w_conf[i] h[b,k,i] + sum_j w_conf[H+j] e[j] + b_conf)
+ *   survival   = conf[b,1] * ... * conf[b,k]
+ *   x_k        = force[b,k] if force != NULL and force[b,k] >= 0, else tokens[b,k]
+ * All arithmetic is binary32; bf16 inputs are widened exactly.
+ *
+ * Arguments (row-major, innermost dimension last):
+ *   B, gamma, V, H, r  requests, block width, vocabulary, hidden size, Markov
+ *                      rank.  0 <= B <= 524280; gamma >= 0; 1 <= V < 2^31;
+ *                      H >= 0; 1 <= r <= 1024.
+ *   dtype              dtype of U, h, W1, W2 and w_conf (all the same).
+ *   U      [B][gamma][V]  base logits of the parallel backbone.
+ *   h      [B][gamma][H]  backbone hidden states (may be NULL if H == 0).
+ *   W1     [V][r]         Markov embedding, gathered by the previous token.
+ *   W2     [V][r]         Markov output factor.
+ *   w_conf [H + r]        confidence weights, ordered [hidden part; Markov part].
+ *   b_conf                confidence bias.
+ *   x0     [B] int32      anchor tokens.
+ *   gumbel [B][gamma][V] fp32 Gumbel noise for Gumbel-max sampling, or NULL
+ *                         for greedy argmax.
+ *   force  [B][gamma] int32 teacher-forced tokens (-1 = use the sample), or NULL.
+ *   tokens [B][gamma] int32      out: sampled tokens.
+ *   conf, survival [B][gamma] fp32 out.
+ *   logits_out [B][gamma][V] fp32 out, optional (NULL = not written): U + bias.
+ *   bias_out   [B][gamma][V] fp32 out, optional (NULL = not written).
+ * A token id outside [0, V) in x0 or force makes that request's tokens -1 and
+ * its conf and survival NaN from that step on; other requests are unaffected.
+ * NaN scores order above +inf.
+ */
+dspark_status_t dspark_head_sample(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int32_t dtype,
+                                   const void* U, const void* h, const void* W1, const void* W2,
+                                   const void* w_conf, float b_conf, const int32_t* x0, const float* gumbel,
+                                   const int32_t* force, int32_t* tokens, float* conf, float* survival,
+                                   float* logits_out, float* bias_out, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
+ * dspark_accept_rate -- analytic accept rate per row ([W] 3.3, paper eq. 8):
+ *   accept_rate[n] = 1 - 1/2 * || softmax(draft[n, :V]) - softmax(target[n, :V]) ||_1
+ * computed in binary32 with max-shifted exponentials.  No clamp is applied:
+ * identical rows give exactly 1; rounding can put a result a few 1e-8
+ * outside [0, 1].
+ *
+ *   N >= 0 rows, V >= 1 columns (V < 2^31); dtype of both logit arrays.
+ *   draft, target  row n starts at element n * ld (ld >= V); the two strides
+ *                  may differ.
+ *   accept_rate [N] fp32 out.
+ */
+dspark_status_t dspark_accept_rate(int64_t N, int64_t V, int32_t dtype, const void* draft, int64_t ld_draft,
+                                   const void* target, int64_t ld_target, float* accept_rate, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
+ * dspark_prefix_schedule -- hardware-aware prefix scheduler ([W] 3.3,
+ * Algorithm 1).
+ *   a[r][j] = conf[r][0] * ... * conf[r][j]   (binary32, left to right)
+ *   Sort all B*gamma pairs by (a descending, r ascending, j ascending).
+ *   Start from the empty selection: tau = B (one bonus token per request),
+ *   Btok = B, Theta_best = B * SPS(B).  Scan the sorted pairs: stop when
+ *   Btok + 1 > n_sps; otherwise Theta = (tau + a) * SPS(Btok + 1) in binary64;
+ *   accept the pair if Theta > Theta_best (tau += a, Btok += 1,
+ *   Theta_best = Theta), else stop.  prefix_len[r] = number of accepted pairs
+ *   of request r.  The result equals that sequential binary64 scan bit for bit.
+ *
+ *   B >= 1, gamma >= 0, B * gamma <= 8192.
+ *   conf [B][gamma] fp32, values in [0, 1].
+ *   sps  [n_sps] fp64, sps[n-1] = SPS(n): the throughput of a verification
+ *        batch of n tokens; n_sps >= B.
+ *   prefix_len [B] int32 out.
+ *   survival_out [B][gamma] fp32 out, optional (NULL = not written).
+ *   order_out [B*gamma] int32 out, optional: pair ids r*gamma + j in sorted order.
+ *   theta_out [1] fp64 out, optional: Theta_best at the stop.
+ *   n_selected_out [1] int32 out, optional: number of accepted pairs.
+ */
+dspark_status_t dspark_prefix_schedule(int64_t B, int64_t gamma, const float* conf, const double* sps,
+                                       int64_t n_sps, int32_t* prefix_len, float* survival_out, int32_t* order_out,
+                                       double* theta_out, int32_t* n_selected_out, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/* Workspace bytes needed by the entry point of the same name for these
+ * shapes; 0 if it needs none.  Pure host functions with no side effects. */
+size_t dspark_head_sample_workspace_size(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int32_t dtype);
+size_t dspark_accept_rate_workspace_size(int64_t N, int64_t V, int32_t dtype);
+size_t dspark_prefix_schedule_workspace_size(int64_t B, int64_t gamma);
+
+/* Static, NUL-terminated description of a status code. */
+const char* dspark_status_string(dspark_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSPARK_H */

@@ -1,0 +1,80 @@
+"""GPU parity of dspark_prefix_schedule against the CPU oracle: prefix
+lengths, sorted order, survivals, Theta and the selection count bit-exact."""
+import numpy as np
+import pytest
+
+import draft_head_sampling_amd as dh
+import oracle
+import synth
+from helpers import dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(conf, sps):
+    conf = np.ascontiguousarray(conf, np.float32)
+    sps = np.ascontiguousarray(sps, np.float64)
+    g = {k: (v.cpu().numpy() if v is not None else None) for k, v in dh.prefix_schedule(dev(conf), dev(sps)).items()}
+    r = oracle.prefix_schedule(conf, sps)
+    np.testing.assert_array_equal(g["prefix_len"], r["prefix_len"])
+    np.testing.assert_array_equal(g["order"], r["order"])
+    np.testing.assert_array_equal(g["survival"].view(np.uint32), r["survival"].view(np.uint32))
+    assert g["n_selected"][0] == r["n_selected"]
+    assert g["theta"][0] == r["theta"], (g["theta"][0], r["theta"])
+    return r
+
+
+def test_training_workload_stated_curve():
+    s = synth.SCHEDULE_TRAIN
+    r = _check(synth.schedule_conf(s), synth.sps_table(s.n_sps, "tokens"))
+    assert r["n_selected"] == s.n_sps - s.B  # increasing curve: stops at the table's end
+
+
+def test_training_workload_step_rate_curve():
+    s = synth.SCHEDULE_TRAIN
+    r = _check(synth.schedule_conf(s), synth.sps_table(s.n_sps, "steps"))
+    assert 0 < r["n_selected"] < s.B * s.gamma
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_small(seed):
+    rng = np.random.default_rng(seed)
+    B, gamma = int(rng.integers(1, 40)), int(rng.integers(1, 20))
+    conf = (1 / (1 + np.exp(-rng.normal(1.0, 2.0, (B, gamma))))).astype(np.float32)
+    n_sps = B + int(rng.integers(0, B * gamma + 5))
+    kind = seed % 3
+    n = np.arange(1, n_sps + 1, dtype=np.float64)
+    sps = {0: 1.0 / (rng.uniform(0.5, 3) + rng.uniform(0.001, 0.5) * n), 1: n / (2.0 + 0.004 * n),
+           2: np.where(n <= n_sps // 2, 1.0, 0.6) * n / (1 + 0.01 * n)}[kind]
+    _check(conf, sps)
+
+
+def test_ties_zeros_ones_and_empty_block():
+    _check(np.full((5, 3), 0.5), np.ones(40))
+    conf = np.array([[1.0, 1.0, 0.0], [0.0, 1.0, 1.0], [1.0, 0.5, 0.25]], np.float32)
+    _check(conf, synth.sps_table(12, "tokens"))
+    _check(conf, synth.sps_table(12, "steps"))
+    _check(np.zeros((4, 0), np.float32), synth.sps_table(8, "steps"))
+    _check(np.full((3, 2), 0.5), np.array([1.0, 1.0, 3.0, 0.1, 0.1, 0.1, 0.1, 0.1]))  # first pair lowers Theta
+
+
+def test_tiny_survivals_take_the_sequential_finish():
+    # survivals far below 2^-17 under an increasing curve: the scan runs past
+    # the exactly-summable run and finishes pair by pair
+    rng = np.random.default_rng(5)
+    conf = rng.uniform(1e-4, 0.05, (64, 16)).astype(np.float32)
+    conf[:, 0] = rng.uniform(0.5, 1.0, 64).astype(np.float32)
+    r = _check(conf, synth.sps_table(64 * 17, "tokens"))
+    assert r["n_selected"] == 64 * 16
+
+
+def test_largest_supported_pair_count():
+    rng = np.random.default_rng(6)
+    conf = (1 / (1 + np.exp(-rng.normal(1.5, 1.5, (512, 16))))).astype(np.float32)
+    _check(conf, synth.sps_table(9000, "steps"))
+    _check(conf, synth.sps_table(9000, "tokens"))
+
+
+def test_single_request():
+    _check(np.array([[0.9, 0.8, 0.7, 0.2]], np.float32), synth.sps_table(5, "steps"))
+    _check(np.array([[0.9, 0.8, 0.7, 0.2]], np.float32), np.array([1.0]))

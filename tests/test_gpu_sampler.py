@@ -1,0 +1,139 @@
+"""GPU parity of dspark_head_sample against the CPU oracle.
+
+Workloads: the tiny fp32 sampler (B=4, gamma=7, V=4096, H=256, r=32), the
+full-vocabulary single request (B=1, V=151936, H=5120, r=256, bf16, greedy)
+and the batched Gumbel-max sampler (B=64, same shapes) in the launch
+configuration the benchmark times; plus ragged and degenerate shapes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import draft_head_sampling_amd as dh
+import oracle
+import synth
+from helpers import dev, sampler_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _random_case(seed, B, gamma, V, H, r, dtype, w_sd, gumbel, U_sd=2.0):
+    s = synth.SamplerShape(B=B, gamma=gamma, V=V, H=H, r=r, dtype=dtype, w_sd=w_sd, U_sd=U_sd, wc_sd=0.05,
+                           gumbel=gumbel, seed=seed)
+    w = synth.sampler_weights(s)
+    w["b_conf"] = 0.25
+    x = synth.sampler_batch(s)
+    return x, w
+
+
+def test_tiny_workload_with_logits():
+    s = synth.SAMPLER_TINY
+    w, x = synth.sampler_weights(s), synth.sampler_batch(s)
+    got, ref, ties = sampler_parity(x, w, want_logits=True)
+    print(f"tiny: {ties} near-tie steps")
+
+
+@pytest.mark.parametrize(
+    "B,gamma,V,H,r,dtype,w_sd,gumbel",
+    [
+        (1, 7, 4099, 64, 32, "bf16", 0.5, False),  # ragged V, strong bias
+        (3, 1, 1000, 16, 256, "bf16", 0.5, True),  # gamma = 1, Gumbel
+        (2, 5, 777, 0, 8, "f32", 0.5, False),  # no hidden part, 32-byte rows
+        (17, 3, 2053, 32, 64, "bf16", 0.3, True),  # B spans several request groups
+        (5, 4, 513, 8, 3, "f32", 0.5, False),  # rank 3: rows not 16-byte multiples
+        (1, 16, 8192, 128, 256, "f32", 0.2, False),  # training block width, fp32 rank 256
+        (64, 2, 1024, 16, 256, "bf16", 0.5, True),  # 64 requests
+        (2, 3, 1, 4, 16, "bf16", 0.5, False),  # single-token vocabulary
+    ],
+)
+def test_shapes(B, gamma, V, H, r, dtype, w_sd, gumbel):
+    x, w = _random_case(0xC0FFEE + B * 131 + V, B, gamma, V, H, r, dtype, w_sd, gumbel)
+    sampler_parity(x, w, want_logits=True)
+
+
+def test_all_equal_scores_pick_token_zero():
+    B, gamma, V, H, r = 3, 4, 3000, 8, 32
+    x = {"U": np.zeros((B, gamma, V), np.float32), "h": np.zeros((B, gamma, H), np.float32),
+         "x0": np.array([0, 1234, 2999], np.int32)}
+    w = {"W1": np.ones((V, r), np.float32), "W2": np.zeros((V, r), np.float32),
+         "w_conf": np.zeros(H + r, np.float32), "b_conf": 0.0}
+    got, ref, _ = sampler_parity(x, w)
+    assert np.all(got["tokens"] == 0)
+
+
+def test_invalid_token_ids_poison_only_their_request():
+    s = synth.SamplerShape(B=4, gamma=3, V=500, H=8, r=16, dtype="f32", w_sd=0.3, U_sd=2.0, wc_sd=0.05,
+                           gumbel=False, seed=99)
+    w, x = synth.sampler_weights(s), synth.sampler_batch(s)
+    x["x0"][1] = -1
+    x["x0"][2] = 500
+    force = np.full((4, 3), -1, np.int32)
+    force[3, 0] = 10_000  # out of range from step 2 on
+    out = dh.head_sample(dev(x["U"]), dev(x["h"]), dev(w["W1"]), dev(w["W2"]), dev(w["w_conf"]), 0.0, dev(x["x0"]),
+                         force=dev(force))
+    tok, conf, surv = (out[k].cpu().numpy() for k in ("tokens", "conf", "survival"))
+    assert np.all(tok[1:3] == -1) and np.all(np.isnan(conf[1:3])) and np.all(np.isnan(surv[1:3]))
+    assert tok[3, 0] >= 0 and np.all(tok[3, 1:] == -1) and np.isnan(conf[3, 1:]).all() and np.isfinite(conf[3, 0])
+    ref = oracle.head_sample(x["U"][:1], x["h"][:1], w["W1"], w["W2"], w["w_conf"], 0.0, x["x0"][:1])
+    np.testing.assert_array_equal(tok[0], ref["tokens"][0])
+
+
+def test_empty_problem_is_a_noop():
+    z = torch.zeros((0, 7, 16), device="cuda")
+    out = dh.head_sample(z, torch.zeros((0, 7, 4), device="cuda"), torch.zeros((16, 4), device="cuda"),
+                         torch.zeros((16, 4), device="cuda"), torch.zeros(8, device="cuda"), 0.0,
+                         torch.zeros(0, dtype=torch.int32, device="cuda"))
+    assert out["tokens"].shape == (0, 7)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    x, w = _random_case(7, 17, 4, 5000, 32, 256, "bf16", 0.3, True)
+    a = dh.head_sample(*(dev(v) for v in (x["U"], x["h"], w["W1"], w["W2"], w["w_conf"])), 0.1, dev(x["x0"]),
+                       dev(x["G"]), want_logits=True)
+    b = dh.head_sample(*(dev(v) for v in (x["U"], x["h"], w["W1"], w["W2"], w["w_conf"])), 0.1, dev(x["x0"]),
+                       dev(x["G"]), want_logits=True)
+    for k in a:
+        assert torch.equal(a[k].view(torch.int32) if a[k].dtype == torch.float32 else a[k],
+                           b[k].view(torch.int32) if b[k].dtype == torch.float32 else b[k]), k
+
+
+def test_single_request_full_vocabulary():
+    """B=1, V=151936, H=5120, r=256, bf16, greedy: three seeded anchors."""
+    s = synth.SAMPLER_B1
+    w = synth.sampler_weights(s)
+    total_ties = 0
+    for anchor in range(3):
+        x = synth.sampler_batch(s, batch_id=anchor)
+        _, _, ties = sampler_parity(x, w, want_logits=(anchor == 0))
+        total_ties += ties
+    print(f"B=1 full vocabulary: {total_ties} near-tie steps over 3 anchors")
+
+
+def test_single_request_strong_bias():
+    """Full vocabulary with a bias large enough to decide most tokens."""
+    s = synth.SAMPLER_B1
+    w = synth.sampler_weights(s, w_sd=0.5)
+    x = synth.sampler_batch(s, batch_id=11)
+    got, ref, _ = sampler_parity(x, w)
+    plain = np.argmax(synth.bf16_to_f32(x["U"][0]), axis=1)
+    assert np.mean(plain != ref["tokens"][0]) > 0.5  # the Markov chain does decide here
+
+
+def test_batched_gumbel_full_vocabulary_sampled_requests():
+    """B=64 Gumbel-max at full size, all 64 requests in one call; the oracle
+    checks 4 sampled requests one by one."""
+    s = synth.SAMPLER_B64
+    w = synth.sampler_weights(s)
+    x = synth.sampler_batch(s)
+    out = dh.head_sample(dev(x["U"]), dev(x["h"]), dev(w["W1"]), dev(w["W2"]), dev(w["w_conf"]), w["b_conf"],
+                         dev(x["x0"]), dev(x["G"]))
+    tok, conf, surv = (out[k].cpu().numpy() for k in ("tokens", "conf", "survival"))
+    for b in (0, 17, 42, 63):
+        xb = {k: (v[b:b + 1] if v is not None else None) for k, v in x.items()}
+        ref = oracle.head_sample(xb["U"], xb["h"], w["W1"], w["W2"], w["w_conf"], w["b_conf"], xb["x0"], xb["G"])
+        if not np.array_equal(tok[b], ref["tokens"][0]):
+            k = int(np.argmax(tok[b] != ref["tokens"][0]))
+            assert ref["margin"][0, k] < 1e-3, (b, k)
+            continue  # a near-tie changes the rest of this request's chain
+        assert np.abs(conf[b] - ref["conf"][0]).max() <= 1e-4
+        assert np.abs(surv[b] - ref["survival"][0]).max() <= 1e-4

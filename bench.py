@@ -1,0 +1,285 @@
+"""Benchmark of the draft-head hot path on one MI355X.
+
+One step is one serving round of the full-vocabulary single-request workload
+(B=1, gamma=7, V=151936, H=5120, r=256, bf16 weights, greedy argmax): the
+Markov-head block sampler with its confidence head and survival products is
+called once for each of 1000 seeded anchors, back to back, then the prefix
+scheduler runs once over the 1000 x 7 confidences.  `value` is draft
+positions per second (bias + sample + confidence) over the timed steps.
+
+The same run also times the analytic accept rate on the training-width
+workload (2048 positions x V=151936, bf16) and reports it as GB/s under
+`accept_rate`, and times the CPU oracle on a bounded sample of the step
+(`cpu_baseline`).  Inputs are synthetic (seeded generator), resident in HBM
+before the timed region starts.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--anchors 1000]
+                       [--no-cpu] [--no-accept] [--extra]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def to_dev(a, device):
+    import numpy as np
+    import torch
+
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def sampler_call_bytes(B, gamma, V, H, r, elem=2):
+    """Compulsory HBM bytes of one sampler call: W2 once, U, gathered W1
+    rows, h, w_conf, anchors, and the three [B, gamma] outputs."""
+    return (V * r + B * gamma * V + B * gamma * r + B * gamma * H + (H + r)) * elem + 4 * B + 12 * B * gamma
+
+
+def accept_call_bytes(N, V, elem=2):
+    return 2 * N * V * elem + 4 * N
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--anchors", type=int, default=1000)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-accept", action="store_true", help="skip the accept-rate measurement")
+    ap.add_argument("--extra", action="store_true", help="also time the B=64 sampler and the scheduler workload")
+    ap.add_argument("--calib-copy", action="store_true", help="run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the draft-head path is data-parallel by request and this build runs "
+              "on a single MI355X; --gpus above 1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import draft_head_sampling_amd as dh
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dh.lib()  # fails loudly if the HIP library is missing
+    stream = torch.cuda.current_stream(dev)
+
+    # ---------------- inputs (host generation, then resident in HBM) ----------------
+    s = synth.SAMPLER_B1
+    n_anch = args.anchors
+    w = synth.sampler_weights(s)
+    W = {k: to_dev(v, dev) for k, v in w.items() if k != "b_conf"}
+    U = torch.empty((n_anch, s.gamma, s.V), dtype=torch.bfloat16, device=dev)
+    Hh = torch.empty((n_anch, s.gamma, s.H), dtype=torch.bfloat16, device=dev)
+    X0 = torch.empty((n_anch,), dtype=torch.int32, device=dev)
+    host_batches = []
+    for a in range(n_anch):
+        x = synth.sampler_batch(s, batch_id=a)
+        U[a].copy_(to_dev(x["U"][0], dev))
+        Hh[a].copy_(to_dev(x["h"][0], dev))
+        X0[a : a + 1].copy_(torch.from_numpy(x["x0"]))
+        if a < 64:
+            host_batches.append(x)
+    tokens = torch.empty((n_anch, s.gamma), dtype=torch.int32, device=dev)
+    conf = torch.empty((n_anch, s.gamma), dtype=torch.float32, device=dev)
+    surv = torch.empty((n_anch, s.gamma), dtype=torch.float32, device=dev)
+    ws = torch.zeros(max(dh.head_sample_workspace_size(1, s.gamma, s.V, s.H, s.r), 256), dtype=torch.uint8,
+                     device=dev)
+    calls = []
+    for a in range(n_anch):
+        c, _ = dh.prepare_head_sample(U[a : a + 1], Hh[a : a + 1], W["W1"], W["W2"], W["w_conf"], w["b_conf"],
+                                      X0[a : a + 1], tokens=tokens[a : a + 1], conf=conf[a : a + 1],
+                                      survival=surv[a : a + 1], workspace=ws)
+        calls.append(c)
+    n_sps = n_anch * (s.gamma + 1)
+    sps_host = synth.sps_table(n_sps, "steps")
+    sps = to_dev(sps_host, dev)
+    sched, sched_out = dh.prepare_prefix_schedule(conf, sps, want_order=False)
+    torch.cuda.synchronize()
+
+    e_s0 = torch.cuda.Event(enable_timing=True)
+    e_s1 = torch.cuda.Event(enable_timing=True)
+    samp_ms = []
+
+    def step(record):
+        if record:
+            e_s0.record(stream)
+        for c in calls:
+            c()
+        if record:
+            e_s1.record(stream)
+        sched()
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()  # harvest the sampler-only interval of this step
+        samp_ms.append(e_s0.elapsed_time(e_s1))
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / args.steps
+    positions = n_anch * s.gamma
+    value = positions * args.steps / (total_ms / 1e3)
+
+    call_us = float(np.mean(samp_ms)) * 1e3 / n_anch
+    call_bytes = sampler_call_bytes(1, s.gamma, s.V, s.H, s.r)
+    achieved = call_bytes / (call_us * 1e-6) / 1e9
+
+    line = {
+        "metric": "draft positions/sec (bias+sample+conf) and accept-rate GB/s vs HBM roofline",
+        "value": round(value, 1),
+        "unit": "draft positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, fp32 accumulate",
+        "data": "synthetic (seeded SplitMix64/Box-Muller), random weights",
+        "config": {
+            "workload": f"Markov-head block sampler, {n_anch} anchors back to back, B=1 gamma=7 V=151936 H=5120 "
+                        f"r=256 bf16 greedy + prefix scheduler over {n_anch}x7 confidences",
+            "B": 1, "gamma": s.gamma, "V": s.V, "H": s.H, "r": s.r, "anchors_per_step": n_anch,
+        },
+        "roofline": {
+            "kernel": "dspark_head_sample (one call = one anchor)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": call_bytes,
+            "us_per_launch": round(call_us, 3),
+        },
+        "wall_s": round(wall, 3),
+    }
+
+    # ---------------- accept rate on the training-width workload ----------------
+    if not args.no_accept:
+        sa = synth.ACCEPT_TRAIN
+        d, t = synth.accept_inputs(sa)
+        D, T = to_dev(d, dev), to_dev(t, dev)
+        del d, t
+        acall, aout = dh.prepare_accept_rate(D, T)
+        for _ in range(3):
+            acall()
+        torch.cuda.synchronize()
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        reps = 20
+        a0.record(stream)
+        for _ in range(reps):
+            acall()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        a_us = a0.elapsed_time(a1) * 1e3 / reps
+        a_bytes = accept_call_bytes(sa.N, sa.V)
+        gbs = a_bytes / (a_us * 1e-6) / 1e9
+        line["accept_rate"] = {
+            "value": round(gbs, 1), "unit": "GB/s",
+            "workload": "analytic accept rate, 2048 positions x V=151936 bf16 draft/target logits",
+            "us_per_call": round(a_us, 2), "positions_per_s": round(sa.N / (a_us * 1e-6), 1),
+            "roofline": {"kernel": "dspark_accept_rate", "bound": "hbm", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": None, "bytes_per_launch": a_bytes},
+        }
+        del D, T
+
+    if args.extra:
+        s3 = synth.SAMPLER_B64
+        x3 = synth.sampler_batch(s3)
+        c3, _ = dh.prepare_head_sample(to_dev(x3["U"], dev), to_dev(x3["h"], dev), W["W1"], W["W2"], W["w_conf"],
+                                       0.0, to_dev(x3["x0"], dev), to_dev(x3["G"], dev))
+        for _ in range(3):
+            c3()
+        torch.cuda.synchronize()
+        b0 = torch.cuda.Event(enable_timing=True)
+        b1 = torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(10):
+            c3()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        us3 = b0.elapsed_time(b1) * 1e3 / 10
+        flops = 2.0 * 64 * s3.gamma * s3.V * s3.r
+        by3 = sampler_call_bytes(64, 7, s3.V, s3.H, s3.r) + 64 * 7 * s3.V * 4
+        line["extra_b64"] = {"us_per_call": round(us3, 2), "positions_per_s": round(64 * 7 / (us3 * 1e-6), 1),
+                             "GB_s": round(by3 / (us3 * 1e-6) / 1e9, 1),
+                             "mfma_tflops": round(flops / (us3 * 1e-6) / 1e12, 2)}
+        s5 = synth.SCHEDULE_TRAIN
+        for kind in ("tokens", "steps"):
+            c5, _ = dh.prepare_prefix_schedule(to_dev(synth.schedule_conf(s5), dev),
+                                               to_dev(synth.sps_table(s5.n_sps, kind), dev))
+            for _ in range(5):
+                c5()
+            torch.cuda.synchronize()
+            b0.record(stream)
+            for _ in range(50):
+                c5()
+            b1.record(stream)
+            torch.cuda.synchronize()
+            line[f"extra_sched_{kind}_us"] = round(b0.elapsed_time(b1) * 1e3 / 50, 2)
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["calib_copy_bytes"] = 1 << 30
+
+    # ---------------- CPU oracle on a bounded sample ----------------
+    if not args.no_cpu:
+        import oracle
+
+        n_cpu = 0
+        tc0 = time.perf_counter()
+        while n_cpu < len(host_batches) and (time.perf_counter() - tc0) < 12.0:
+            x = host_batches[n_cpu]
+            oracle.head_sample(x["U"], x["h"], w["W1"], w["W2"], w["w_conf"], w["b_conf"], x["x0"])
+            n_cpu += 1
+        t_samp = time.perf_counter() - tc0
+        conf_host = conf.cpu().numpy()
+        tc1 = time.perf_counter()
+        oracle.prefix_schedule(conf_host, sps_host)
+        t_sched = time.perf_counter() - tc1
+        # one step = n_anch sampler calls + one schedule: scale the sample
+        cpu_step_s = t_samp / n_cpu * n_anch + t_sched
+        line["cpu_baseline"] = {
+            "value": round(positions / cpu_step_s, 2), "unit": "draft positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle sampler on {n_cpu} of the {n_anch} anchors ({t_samp:.1f} s, fp64, single thread), "
+                      f"scaled to {n_anch}, plus one oracle schedule of the {n_anch}x7 confidences "
+                      f"({t_sched * 1e3:.1f} ms); host: {os.cpu_count()} logical CPUs",
+        }
+
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -93,8 +93,8 @@ def _stream(device) -> int:
 def _workspace(nbytes: int, device, workspace):
     if nbytes == 0:
         return None, 0
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace is None:  # zero-filled before first use, as the C ABI requires
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     if workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace needs {nbytes} bytes")
     return workspace, workspace.numel() * workspace.element_size()

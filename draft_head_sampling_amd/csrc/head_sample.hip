@@ -212,6 +212,283 @@ __global__ __launch_bounds__(64) void sample_finish(int64_t B, int64_t gamma, in
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Single-request chain kernel (B = 1, bf16, rank 256).
+//
+// One persistent workgroup per CU owns a contiguous slice of the vocabulary
+// and keeps its W2 rows in registers for the whole block, so W2 crosses HBM
+// once per call instead of once per step.  A row is split over 8 lanes (32
+// bf16 each); a step is 16 v_dot2c_f32_bf16 per held row slot plus a 3-level
+// xor reduction.  The grid-wide dependency between steps goes through one
+// 64-bit slot per workgroup and step: each workgroup stores its packed argmax
+// key (never zero), and every workgroup polls all slots of the step until
+// none is zero, taking their maximum as the winner.  The data is its own
+// flag, so the exchange needs no counter and no fence.  U and G for the next
+// step are prefetched before the wait; workgroup 0 computes the confidence
+// logit while the others finish.  The last workgroup to leave zeroes the
+// slots, so the workspace is ready for the next call.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
+}
+
+constexpr int kChainThreads = 512;  // 8 waves: 256 registers per lane hold the W2 slice
+constexpr int kChainLanesPerRow = 8;
+constexpr int kChainGroups = kChainThreads / kChainLanesPerRow;  // rows per slot
+constexpr int kChainRank = 256;
+constexpr int kChainMaxSlots = 10;  // 160 registers of W2 per lane; more spills
+constexpr int kChainMaxWGs = 1024;
+constexpr int kChainSpinLimit = 1 << 21;
+constexpr size_t kChainHeader = 256;  // exit counter, status word
+
+__device__ __forceinline__ void load64B(const bf16_t* p, uint32_t (&r)[16]) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 t = q[i];
+        r[4 * i] = t.x, r[4 * i + 1] = t.y, r[4 * i + 2] = t.z, r[4 * i + 3] = t.w;
+    }
+}
+
+template <int NSLOT>
+__global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
+    int gamma, int64_t V, int64_t H, int rows_per_wg, const bf16_t* __restrict__ U, const bf16_t* __restrict__ h,
+    const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W2, const bf16_t* __restrict__ w_conf, float b_conf,
+    const int32_t* __restrict__ x0, const float* __restrict__ G, const int32_t* __restrict__ force,
+    int32_t* __restrict__ tokens, float* __restrict__ conf, float* __restrict__ survival,
+    float* __restrict__ logits_out, float* __restrict__ bias_out, uint64_t* slots, uint32_t* header) {
+    __shared__ uint64_t red[kChainThreads / 64];
+    __shared__ float fred[kChainThreads / 64];
+    __shared__ uint64_t winner;
+    __shared__ int last_flag;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = tid >> 3, sub = tid & 7;
+    const int g = blockIdx.x, nwg = gridDim.x;
+    const int64_t row0 = (int64_t)g * rows_per_wg;
+
+    // W2 rows of this workgroup, resident for the whole call
+    uint32_t w2[NSLOT][16];
+#pragma unroll
+    for (int i = 0; i < NSLOT; ++i) {
+        const int lr = i * kChainGroups + grp;
+        const int64_t v = row0 + lr;
+        if (lr < rows_per_wg && v < V) {
+            load64B(W2 + v * kChainRank + sub * 32, w2[i]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) w2[i][q] = 0u;
+        }
+    }
+    // lane `sub` finishes slots sub and sub + 8 of its row group
+    constexpr int NMINE = NSLOT > 8 ? 2 : 1;
+    int64_t my_v[NMINE];
+    bool my_ok[NMINE];
+    float u_next[NMINE], g_next[NMINE];
+#pragma unroll
+    for (int m = 0; m < NMINE; ++m) {
+        const int slot = sub + 8 * m;
+        const int lr = slot * kChainGroups + grp;
+        my_v[m] = row0 + lr;
+        my_ok[m] = slot < NSLOT && lr < rows_per_wg && my_v[m] < V;
+        u_next[m] = my_ok[m] ? load_elem(U, my_v[m]) : 0.f;
+        g_next[m] = (my_ok[m] && G) ? G[my_v[m]] : 0.f;
+    }
+    // confidence weights of the Markov part, held by lanes 0..7 of workgroup 0
+    uint32_t we[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) we[q] = 0u;
+    if (g == 0 && tid < 8) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            we[q] = (uint32_t)w_conf[H + tid * 32 + 2 * q].bits | ((uint32_t)w_conf[H + tid * 32 + 2 * q + 1].bits << 16);
+    }
+
+    int64_t x = x0[0];
+    bool valid = x >= 0 && x < V;
+    float A = 1.f;
+    for (int k = 0; k < gamma; ++k) {
+        if (!valid) {  // identical in every workgroup: no exchange needed
+            if (g == 0 && tid == 0) tokens[k] = -1, conf[k] = __builtin_nanf(""), survival[k] = __builtin_nanf("");
+            continue;
+        }
+        uint32_t e[16];
+        load64B(W1 + x * kChainRank + sub * 32, e);
+        float acc[NSLOT];
+#pragma unroll
+        for (int i = 0; i < NSLOT; ++i) {
+            float a = 0.f;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) a = dot2(w2[i][q], e[q], a);
+            acc[i] = a;
+        }
+#pragma unroll
+        for (int o = 4; o > 0; o >>= 1)
+#pragma unroll
+            for (int i = 0; i < NSLOT; ++i) acc[i] += __shfl_xor(acc[i], o);
+        uint64_t key = 0;
+#pragma unroll
+        for (int m = 0; m < NMINE; ++m) {
+            float bias = 0.f;
+#pragma unroll
+            for (int i = 0; i < NSLOT; ++i) bias = (sub + 8 * m == i) ? acc[i] : bias;
+            if (my_ok[m]) {
+                const float lg = u_next[m] + bias;
+                const float sc = G ? lg + g_next[m] : lg;
+                if (bias_out) bias_out[(int64_t)k * V + my_v[m]] = bias;
+                if (logits_out) logits_out[(int64_t)k * V + my_v[m]] = lg;
+                key = umax64(key, argmax_key(sc, (uint32_t)my_v[m]));
+                if (k + 1 < gamma) {  // next step's inputs do not depend on this step's token
+                    u_next[m] = load_elem(U, (int64_t)(k + 1) * V + my_v[m]);
+                    if (G) g_next[m] = G[(int64_t)(k + 1) * V + my_v[m]];
+                }
+            }
+        }
+        for (int o = 32; o > 0; o >>= 1) key = umax64(key, shfl_xor_u64(key, o));
+        if (lane == 0) red[wave] = key;
+        __syncthreads();
+        if (tid == 0) {
+            uint64_t m = 1;  // a workgroup without rows still publishes a non-zero key
+            for (int w = 0; w < kChainThreads / 64; ++w) m = umax64(m, red[w]);
+            __hip_atomic_store(&slots[(int64_t)k * nwg + g], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+
+        if (g == 0) {  // confidence logit of step k while the other workgroups finish
+            float p = 0.f;
+            for (int64_t i = tid; i < H; i += kChainThreads)
+                p += load_elem(w_conf, i) * load_elem(h, (int64_t)k * H + i);
+            if (tid < 8)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) p = dot2(we[q], e[q], p);
+            for (int o = 32; o > 0; o >>= 1) p += __shfl_xor(p, o);
+            if (lane == 0) fred[wave] = p;
+            __syncthreads();
+            if (tid == 0) {
+                float z = b_conf;
+                for (int w = 0; w < kChainThreads / 64; ++w) z += fred[w];
+                const float c = 1.f / (1.f + expf(-z));
+                A = A * c;
+                conf[k] = c;
+                survival[k] = A;
+            }
+        }
+
+        if (wave == 0) {
+            uint64_t best = 0;
+            for (int spin = 0; spin < kChainSpinLimit; ++spin) {
+                bool all = true;
+                uint64_t m = 0;
+                for (int j = lane; j < nwg; j += 64) {
+                    const uint64_t sv =
+                        __hip_atomic_load(&slots[(int64_t)k * nwg + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    all = all && sv != 0;
+                    m = umax64(m, sv);
+                }
+                if (__all(all)) {
+                    for (int o = 32; o > 0; o >>= 1) m = umax64(m, shfl_xor_u64(m, o));
+                    best = m;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (lane == 0) {
+                winner = best;
+                if (best == 0 && g == 0) header[1] = 1u;  // timed out: reported as token -1
+            }
+        }
+        __syncthreads();
+        const uint64_t wk = winner;
+        const int32_t tok = key_token(wk);
+        if (g == 0 && tid == 0) tokens[k] = tok;
+        const int32_t f = (force && wk != 0) ? force[k] : -1;
+        x = f >= 0 ? f : tok;
+        valid = wk != 0 && x >= 0 && x < V;
+        if (wk == 0 && g == 0 && tid == 0) conf[k] = __builtin_nanf(""), survival[k] = __builtin_nanf("");
+    }
+
+    // leave: the last workgroup out clears the slots for the next call
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&header[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = old == (uint32_t)(nwg - 1);
+    }
+    __syncthreads();
+    if (last_flag) {
+        for (int64_t i = tid; i < (int64_t)gamma * nwg; i += kChainThreads)
+            __hip_atomic_store(&slots[i], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) __hip_atomic_store(&header[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+struct ChainPlan {
+    int nwg = 0, rows_per_wg = 0, nslot = 0;
+};
+
+// Number of compute units of the current device (queried once per device).
+int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+ChainPlan chain_plan(int64_t V) {
+    ChainPlan p;
+    const int cus = device_cus();
+    if (cus <= 0) return p;
+    int64_t nwg = (V + kChainGroups - 1) / kChainGroups;  // at least one full slot of rows per workgroup
+    if (nwg > cus) nwg = cus;
+    if (nwg > kChainMaxWGs) nwg = kChainMaxWGs;
+    const int64_t rows = (V + nwg - 1) / nwg;
+    const int64_t nslot = (rows + kChainGroups - 1) / kChainGroups;
+    if (nslot > kChainMaxSlots) return p;
+    p.nwg = (int)nwg;
+    p.rows_per_wg = (int)rows;
+    p.nslot = (int)nslot;
+    return p;
+}
+
+hipError_t launch_chain(const ChainPlan& p, int64_t gamma, int64_t V, int64_t H, const void* U, const void* h,
+                        const void* W1, const void* W2, const void* w_conf, float b_conf, const int32_t* x0,
+                        const float* G, const int32_t* force, int32_t* tokens, float* conf, float* survival,
+                        float* lo, float* bo, void* ws, hipStream_t stream) {
+    int g = (int)gamma;
+    int64_t Vv = V, Hh = H;
+    int rows = p.rows_per_wg;
+    const bf16_t* Ut = static_cast<const bf16_t*>(U);
+    const bf16_t* ht = static_cast<const bf16_t*>(h);
+    const bf16_t* W1t = static_cast<const bf16_t*>(W1);
+    const bf16_t* W2t = static_cast<const bf16_t*>(W2);
+    const bf16_t* wt = static_cast<const bf16_t*>(w_conf);
+    uint32_t* header = static_cast<uint32_t*>(ws);
+    uint64_t* slots = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kChainHeader);
+    void* args[] = {&g,  &Vv,    &Hh, &rows,   &Ut,     &ht,       &W1t, &W2t, &wt,    &b_conf,
+                    &x0, &G,     &force, &tokens, &conf, &survival, &lo,  &bo,  &slots, &header};
+    const void* fn = nullptr;
+    switch (p.nslot) {
+        case 1: fn = reinterpret_cast<const void*>(&sample_chain_b1<1>); break;
+        case 2: fn = reinterpret_cast<const void*>(&sample_chain_b1<2>); break;
+        case 3: fn = reinterpret_cast<const void*>(&sample_chain_b1<3>); break;
+        case 4: fn = reinterpret_cast<const void*>(&sample_chain_b1<4>); break;
+        case 5: fn = reinterpret_cast<const void*>(&sample_chain_b1<5>); break;
+        case 6: fn = reinterpret_cast<const void*>(&sample_chain_b1<6>); break;
+        case 7: fn = reinterpret_cast<const void*>(&sample_chain_b1<7>); break;
+        case 8: fn = reinterpret_cast<const void*>(&sample_chain_b1<8>); break;
+        case 9: fn = reinterpret_cast<const void*>(&sample_chain_b1<9>); break;
+        default: fn = reinterpret_cast<const void*>(&sample_chain_b1<10>); break;
+    }
+    return hipLaunchCooperativeKernel(fn, dim3(p.nwg), dim3(kChainThreads), args, 0, stream);
+}
+
 struct Buffers {
     uint64_t* keys;
     float* hdot;
@@ -247,6 +524,10 @@ hipError_t launch_steps(int lpr, int64_t B, int64_t gamma, int k, int64_t V, int
     }
 #undef DSPARK_STEP
     return hipGetLastError();
+}
+
+bool chain_eligible(int64_t B, int64_t r, int dtype, const void* W1, const void* W2) {
+    return B == 1 && r == kChainRank && dtype == kBF16 && ((uintptr_t)W1 % 16 == 0) && ((uintptr_t)W2 % 16 == 0);
 }
 
 template <typename T>
@@ -290,8 +571,13 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
 
 }  // namespace
 
-size_t head_sample_workspace(int64_t B, int64_t gamma, int64_t, int64_t) {
-    return ((size_t)(8 * B * gamma) + 255) / 256 * 256 + ((size_t)(4 * B * gamma) + 255) / 256 * 256;
+size_t head_sample_workspace(int64_t B, int64_t gamma, int64_t, int64_t r) {
+    size_t steps = ((size_t)(8 * B * gamma) + 255) / 256 * 256 + ((size_t)(4 * B * gamma) + 255) / 256 * 256;
+    if (B == 1 && r == kChainRank) {
+        const size_t chain = kChainHeader + (size_t)8 * gamma * kChainMaxWGs;
+        if (chain > steps) steps = chain;
+    }
+    return steps;
 }
 
 hipError_t head_sample_launch(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int dtype, const void* U,
@@ -299,6 +585,12 @@ hipError_t head_sample_launch(int64_t B, int64_t gamma, int64_t V, int64_t H, in
                               const int32_t* x0, const float* gumbel, const int32_t* force, int32_t* tokens,
                               float* conf, float* survival, float* logits_out, float* bias_out, void* ws,
                               hipStream_t stream) {
+    if (chain_eligible(B, r, dtype, W1, W2)) {
+        const ChainPlan p = chain_plan(V);
+        if (p.nwg > 0)
+            return launch_chain(p, gamma, V, H, U, h, W1, W2, w_conf, b_conf, x0, gumbel, force, tokens, conf,
+                                survival, logits_out, bias_out, ws, stream);
+    }
     if (dtype == kBF16)
         return launch_typed<bf16_t>(B, gamma, V, H, r, U, h, W1, W2, w_conf, b_conf, x0, gumbel, force, tokens,
                                     conf, survival, logits_out, bias_out, ws, stream);

@@ -21,9 +21,11 @@
  *   - Workspace: device scratch owned by the caller.  dspark_*_workspace_size
  *     returns the bytes an entry point needs for given shapes (0 means the
  *     workspace argument may be NULL).  A workspace must be at least that
- *     large and 256-byte aligned; workspace_bytes is its size.  It needs no
- *     initialisation and its contents after a call are unspecified.  Calls
- *     that may overlap in time must not share a workspace.
+ *     large and 256-byte aligned; workspace_bytes is its size.  It must be
+ *     zero-filled before its first use; every call that completes leaves it
+ *     zero-filled again, so one workspace serves any number of calls in
+ *     stream order (after a call that reports a timeout, zero it again).
+ *     Calls that may overlap in time must not share a workspace.
  *   - Errors: every argument check runs on the host before anything is
  *     enqueued; on failure a non-zero status is returned and nothing is
  *     enqueued.  A failed launch returns DSPARK_ERR_HIP.  No C++ exception

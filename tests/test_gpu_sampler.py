@@ -44,6 +44,12 @@ def test_tiny_workload_with_logits():
         (1, 16, 8192, 128, 256, "f32", 0.2, False),  # training block width, fp32 rank 256
         (64, 2, 1024, 16, 256, "bf16", 0.5, True),  # 64 requests
         (2, 3, 1, 4, 16, "bf16", 0.5, False),  # single-token vocabulary
+        # single request, bf16, rank 256: the persistent chain kernel
+        (1, 7, 1000, 16, 256, "bf16", 0.5, True),  # few workgroups, Gumbel
+        (1, 5, 70001, 72, 256, "bf16", 0.3, False),  # ragged slices, H not a multiple of 64
+        (1, 9, 163840, 8, 256, "bf16", 0.2, False),  # largest vocabulary held on chip
+        (1, 4, 200003, 8, 256, "bf16", 0.2, True),  # beyond it: per-step kernels
+        (1, 2, 1, 8, 256, "bf16", 0.5, False),  # single-token vocabulary
     ],
 )
 def test_shapes(B, gamma, V, H, r, dtype, w_sd, gumbel):

@@ -1,7 +1,7 @@
 // C ABI of the draft-head hot path: host-side argument checks, workspace
 // queries and dispatch to the kernels.  Every check runs before anything is
 // enqueued, and no C++ exception crosses the interface.
-#include "../../include/dspark.h"
+#include "dspark.h"
 #include "internal.h"
 
 #define DSPARK_EXPORT extern "C" __attribute__((visibility("default")))

@@ -120,7 +120,6 @@ __global__ __launch_bounds__(kThreads) void sample_step(int64_t B, int64_t gamma
         for (int bb = 0; bb < BG; ++bb)
 #pragma unroll
             for (int i = 0; i < E; ++i) ereg[bb][i] = e_lds[bb * r + c * E + i];
-#pragma unroll 4
         for (int rr = wave * RPW + lane / LPR; rr < kTile; rr += (kThreads / 64) * RPW) {
             const int64_t v = v0 + rr;
             float acc[BG];
@@ -220,14 +219,17 @@ __global__ __launch_bounds__(64) void sample_finish(int64_t B, int64_t gamma, in
 // and keeps its W2 rows in registers for the whole block, so W2 crosses HBM
 // once per call instead of once per step.  A row is split over 8 lanes (32
 // bf16 each); a step is 16 v_dot2c_f32_bf16 per held row slot plus a 3-level
-// xor reduction.  The grid-wide dependency between steps goes through one
-// 64-bit slot per workgroup and step: each workgroup stores its packed argmax
-// key (never zero), and every workgroup polls all slots of the step until
-// none is zero, taking their maximum as the winner.  The data is its own
-// flag, so the exchange needs no counter and no fence.  U and G for the next
-// step are prefetched before the wait; workgroup 0 computes the confidence
-// logit while the others finish.  The last workgroup to leave zeroes the
-// slots, so the workspace is ready for the next call.
+// DPP reduction across the 8 lanes.  The grid-wide dependency between steps
+// goes through one 128-byte slot per workgroup and step holding two 64-bit
+// words: the workgroup's packed argmax key (never zero) and its partial sum
+// of the confidence logit, w_h . h over a 1/nwg slice of the hidden state,
+// tagged with a set bit 32 so it is never zero either.  Every workgroup polls
+// all slots of the step until no word is zero, then takes the maximum key as
+// the winner and sums the partials in slot order.  Each word is its own flag,
+// so the exchange needs no counter and no fence; spacing the slots one
+// 128-byte line apart spreads the polling over memory channels.  U and G of
+// the next step are loaded before they are needed.  The last workgroup to
+// leave zeroes the slots, so the workspace is ready for the next call.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -236,12 +238,61 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                            false);
 }
 
+// DPP lane permutations: quad_perm [1,0,3,2] (xor 1), quad_perm [2,3,0,1]
+// (xor 2), row_half_mirror (lane i <- 7-i in each group of 8), row_mirror
+// (lane i <- 15-i in each row of 16).
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+// Sum over each aligned group of 8 lanes, result in all 8 lanes.
+__device__ __forceinline__ float sum8(float v) {
+    v += dpp_f32<kDppXor1>(v);
+    v += dpp_f32<kDppXor2>(v);
+    v += dpp_f32<kDppHalfMirror>(v);
+    return v;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+// Maximum over the 64 lanes of a wave (wave-uniform result).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+    k = umax64(k, dpp_u64<kDppXor1>(k));
+    k = umax64(k, dpp_u64<kDppXor2>(k));
+    k = umax64(k, dpp_u64<kDppHalfMirror>(k));
+    k = umax64(k, dpp_u64<kDppMirror>(k));
+    return umax64(umax64(readlane_u64(k, 0), readlane_u64(k, 16)), umax64(readlane_u64(k, 32), readlane_u64(k, 48)));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v += dpp_f32<kDppXor1>(v);
+    v += dpp_f32<kDppXor2>(v);
+    v += dpp_f32<kDppHalfMirror>(v);
+    v += dpp_f32<kDppMirror>(v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+}
+
 constexpr int kChainThreads = 512;  // 8 waves: 256 registers per lane hold the W2 slice
+constexpr int kChainWaves = kChainThreads / 64;
 constexpr int kChainLanesPerRow = 8;
 constexpr int kChainGroups = kChainThreads / kChainLanesPerRow;  // rows per slot
 constexpr int kChainRank = 256;
 constexpr int kChainMaxSlots = 10;  // 160 registers of W2 per lane; more spills
-constexpr int kChainMaxWGs = 1024;
+constexpr int kChainMaxWGs = 256;   // 4 slots per lane when polling
+constexpr int kSlotWords = 16;      // 128-byte stride between slots (key, partial logit, padding)
+constexpr int kChainPoll = kChainMaxWGs / 64;
 constexpr int kChainSpinLimit = 1 << 21;
 constexpr size_t kChainHeader = 256;  // exit counter, status word
 
@@ -261,17 +312,23 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
     const int32_t* __restrict__ x0, const float* __restrict__ G, const int32_t* __restrict__ force,
     int32_t* __restrict__ tokens, float* __restrict__ conf, float* __restrict__ survival,
     float* __restrict__ logits_out, float* __restrict__ bias_out, uint64_t* slots, uint32_t* header) {
-    __shared__ uint64_t red[kChainThreads / 64];
-    __shared__ float fred[kChainThreads / 64];
+    __shared__ uint64_t red[kChainWaves];
+    __shared__ float fred[kChainWaves];
+    __shared__ uint32_t we_lds[kChainRank / 2];  // Markov part of the confidence weights (workgroup 0)
     __shared__ uint64_t winner;
+    __shared__ float zpart;
     __shared__ int last_flag;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = tid >> 3, sub = tid & 7;
     const int g = blockIdx.x, nwg = gridDim.x;
     const int64_t row0 = (int64_t)g * rows_per_wg;
+    const bool wg0 = g == 0;
+    const int64_t h_per = (H + nwg - 1) / nwg;  // hidden elements of this workgroup's confidence partial
+    const int64_t h_lo = (int64_t)g * h_per < H ? (int64_t)g * h_per : H;
+    const int64_t h_hi = h_lo + h_per < H ? h_lo + h_per : H;
 
-    // W2 rows of this workgroup, resident for the whole call
+    // this workgroup's W2 rows first: the largest load and independent of the anchor
     uint32_t w2[NSLOT][16];
 #pragma unroll
     for (int i = 0; i < NSLOT; ++i) {
@@ -284,8 +341,14 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             for (int q = 0; q < 16; ++q) w2[i][q] = 0u;
         }
     }
-    // lane `sub` finishes slots sub and sub + 8 of its row group
-    constexpr int NMINE = NSLOT > 8 ? 2 : 1;
+
+    // step-0 row gather (it waits on the anchor id)
+    int64_t x = x0[0];
+    bool valid = x >= 0 && x < V;
+    uint32_t e[16];
+    if (valid) load64B(W1 + x * kChainRank + sub * 32, e);
+
+    constexpr int NMINE = NSLOT > 8 ? 2 : 1;  // lane `sub` finishes slots sub and sub + 8
     int64_t my_v[NMINE];
     bool my_ok[NMINE];
     float u_next[NMINE], g_next[NMINE];
@@ -298,38 +361,30 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
         u_next[m] = my_ok[m] ? load_elem(U, my_v[m]) : 0.f;
         g_next[m] = (my_ok[m] && G) ? G[my_v[m]] : 0.f;
     }
-    // confidence weights of the Markov part, held by lanes 0..7 of workgroup 0
-    uint32_t we[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) we[q] = 0u;
-    if (g == 0 && tid < 8) {
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-            we[q] = (uint32_t)w_conf[H + tid * 32 + 2 * q].bits | ((uint32_t)w_conf[H + tid * 32 + 2 * q + 1].bits << 16);
-    }
+    if (wg0 && tid < kChainRank / 2)
+        we_lds[tid] = (uint32_t)w_conf[H + 2 * tid].bits | ((uint32_t)w_conf[H + 2 * tid + 1].bits << 16);
+    __syncthreads();
 
-    int64_t x = x0[0];
-    bool valid = x >= 0 && x < V;
     float A = 1.f;
     for (int k = 0; k < gamma; ++k) {
         if (!valid) {  // identical in every workgroup: no exchange needed
-            if (g == 0 && tid == 0) tokens[k] = -1, conf[k] = __builtin_nanf(""), survival[k] = __builtin_nanf("");
+            if (wg0 && tid == 0) tokens[k] = -1, conf[k] = __builtin_nanf(""), survival[k] = __builtin_nanf("");
             continue;
         }
-        uint32_t e[16];
-        load64B(W1 + x * kChainRank + sub * 32, e);
+        // this workgroup's share of the confidence logit: a slice of w_h . h_k
+        // (loaded here, summed after the dot products), plus (workgroup 0) the
+        // Markov part w_e . e
+        float p = 0.f;
+        for (int64_t i = h_lo + tid; i < h_hi; i += kChainThreads)
+            p += load_elem(w_conf, i) * load_elem(h, (int64_t)k * H + i);
         float acc[NSLOT];
 #pragma unroll
         for (int i = 0; i < NSLOT; ++i) {
             float a = 0.f;
 #pragma unroll
             for (int q = 0; q < 16; ++q) a = dot2(w2[i][q], e[q], a);
-            acc[i] = a;
+            acc[i] = sum8(a);
         }
-#pragma unroll
-        for (int o = 4; o > 0; o >>= 1)
-#pragma unroll
-            for (int i = 0; i < NSLOT; ++i) acc[i] += __shfl_xor(acc[i], o);
         uint64_t key = 0;
 #pragma unroll
         for (int m = 0; m < NMINE; ++m) {
@@ -348,66 +403,76 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 }
             }
         }
-        for (int o = 32; o > 0; o >>= 1) key = umax64(key, shfl_xor_u64(key, o));
-        if (lane == 0) red[wave] = key;
+        if (wg0 && tid < 8)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) p = dot2(we_lds[tid * 16 + q], e[q], p);
+        p = wave_sum_f32(p);
+        key = wave_max_u64(key);
+        if (lane == 0) red[wave] = key, fred[wave] = p;
         __syncthreads();
         if (tid == 0) {
             uint64_t m = 1;  // a workgroup without rows still publishes a non-zero key
-            for (int w = 0; w < kChainThreads / 64; ++w) m = umax64(m, red[w]);
-            __hip_atomic_store(&slots[(int64_t)k * nwg + g], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-
-        if (g == 0) {  // confidence logit of step k while the other workgroups finish
-            float p = 0.f;
-            for (int64_t i = tid; i < H; i += kChainThreads)
-                p += load_elem(w_conf, i) * load_elem(h, (int64_t)k * H + i);
-            if (tid < 8)
+            float ps = 0.f;
 #pragma unroll
-                for (int q = 0; q < 16; ++q) p = dot2(we[q], e[q], p);
-            for (int o = 32; o > 0; o >>= 1) p += __shfl_xor(p, o);
-            if (lane == 0) fred[wave] = p;
-            __syncthreads();
-            if (tid == 0) {
-                float z = b_conf;
-                for (int w = 0; w < kChainThreads / 64; ++w) z += fred[w];
-                const float c = 1.f / (1.f + expf(-z));
-                A = A * c;
-                conf[k] = c;
-                survival[k] = A;
-            }
+            for (int w = 0; w < kChainWaves; ++w) m = umax64(m, red[w]), ps += fred[w];
+            uint64_t* slot = slots + ((int64_t)k * nwg + g) * kSlotWords;
+            __hip_atomic_store(slot, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(slot + 1, (1ull << 32) | __float_as_uint(ps), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
         }
 
         if (wave == 0) {
             uint64_t best = 0;
+            float zsum = 0.f;
             for (int spin = 0; spin < kChainSpinLimit; ++spin) {
+                uint64_t sk[kChainPoll], sp[kChainPoll];
+#pragma unroll
+                for (int i = 0; i < kChainPoll; ++i) {
+                    const int j = lane + 64 * i;
+                    const uint64_t* slot = slots + ((int64_t)k * nwg + j) * kSlotWords;
+                    sk[i] = j < nwg ? __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1ull;
+                    sp[i] = j < nwg ? __hip_atomic_load(slot + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                    : (1ull << 32);
+                }
                 bool all = true;
                 uint64_t m = 0;
-                for (int j = lane; j < nwg; j += 64) {
-                    const uint64_t sv =
-                        __hip_atomic_load(&slots[(int64_t)k * nwg + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    all = all && sv != 0;
-                    m = umax64(m, sv);
+                float ps = 0.f;
+#pragma unroll
+                for (int i = 0; i < kChainPoll; ++i) {
+                    all = all && sk[i] != 0 && sp[i] != 0;
+                    m = umax64(m, sk[i]);
+                    ps += __uint_as_float((uint32_t)sp[i]);
                 }
                 if (__all(all)) {
-                    for (int o = 32; o > 0; o >>= 1) m = umax64(m, shfl_xor_u64(m, o));
-                    best = m;
+                    best = wave_max_u64(m);
+                    zsum = wave_sum_f32(ps);
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
             }
             if (lane == 0) {
                 winner = best;
-                if (best == 0 && g == 0) header[1] = 1u;  // timed out: reported as token -1
+                zpart = zsum;
+                if (best == 0 && wg0) header[1] = 1u;  // timed out: reported as token -1
             }
         }
         __syncthreads();
         const uint64_t wk = winner;
+        if (wg0 && tid == 0) {
+            const float c = 1.f / (1.f + expf(-(zpart + b_conf)));
+            A = A * c;
+            conf[k] = c;
+            survival[k] = A;
+        }
         const int32_t tok = key_token(wk);
-        if (g == 0 && tid == 0) tokens[k] = tok;
         const int32_t f = (force && wk != 0) ? force[k] : -1;
         x = f >= 0 ? f : tok;
         valid = wk != 0 && x >= 0 && x < V;
-        if (wk == 0 && g == 0 && tid == 0) conf[k] = __builtin_nanf(""), survival[k] = __builtin_nanf("");
+        if (valid && k + 1 < gamma) load64B(W1 + x * kChainRank + sub * 32, e);
+        if (wg0 && tid == 0) {
+            tokens[k] = tok;
+            if (wk == 0) conf[k] = __builtin_nanf(""), survival[k] = __builtin_nanf("");
+        }
     }
 
     // leave: the last workgroup out clears the slots for the next call
@@ -418,9 +483,26 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
     }
     __syncthreads();
     if (last_flag) {
-        for (int64_t i = tid; i < (int64_t)gamma * nwg; i += kChainThreads)
-            __hip_atomic_store(&slots[i], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int64_t i = tid; i < (int64_t)gamma * nwg; i += kChainThreads) {
+            __hip_atomic_store(&slots[i * kSlotWords], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&slots[i * kSlotWords + 1], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         if (tid == 0) __hip_atomic_store(&header[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+const void* chain_fn(int nslot) {
+    switch (nslot) {
+        case 1: return reinterpret_cast<const void*>(&sample_chain_b1<1>);
+        case 2: return reinterpret_cast<const void*>(&sample_chain_b1<2>);
+        case 3: return reinterpret_cast<const void*>(&sample_chain_b1<3>);
+        case 4: return reinterpret_cast<const void*>(&sample_chain_b1<4>);
+        case 5: return reinterpret_cast<const void*>(&sample_chain_b1<5>);
+        case 6: return reinterpret_cast<const void*>(&sample_chain_b1<6>);
+        case 7: return reinterpret_cast<const void*>(&sample_chain_b1<7>);
+        case 8: return reinterpret_cast<const void*>(&sample_chain_b1<8>);
+        case 9: return reinterpret_cast<const void*>(&sample_chain_b1<9>);
+        default: return reinterpret_cast<const void*>(&sample_chain_b1<10>);
     }
 }
 
@@ -441,7 +523,7 @@ int device_cus() {
     return cache[dev];
 }
 
-ChainPlan chain_plan(int64_t V) {
+ChainPlan chain_plan(int64_t V, int64_t H) {
     ChainPlan p;
     const int cus = device_cus();
     if (cus <= 0) return p;
@@ -451,6 +533,10 @@ ChainPlan chain_plan(int64_t V) {
     const int64_t rows = (V + nwg - 1) / nwg;
     const int64_t nslot = (rows + kChainGroups - 1) / kChainGroups;
     if (nslot > kChainMaxSlots) return p;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_fn((int)nslot), kChainThreads, 0) != hipSuccess ||
+        per_cu < 1)
+        return p;
     p.nwg = (int)nwg;
     p.rows_per_wg = (int)rows;
     p.nslot = (int)nslot;
@@ -473,20 +559,13 @@ hipError_t launch_chain(const ChainPlan& p, int64_t gamma, int64_t V, int64_t H,
     uint64_t* slots = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kChainHeader);
     void* args[] = {&g,  &Vv,    &Hh, &rows,   &Ut,     &ht,       &W1t, &W2t, &wt,    &b_conf,
                     &x0, &G,     &force, &tokens, &conf, &survival, &lo,  &bo,  &slots, &header};
-    const void* fn = nullptr;
-    switch (p.nslot) {
-        case 1: fn = reinterpret_cast<const void*>(&sample_chain_b1<1>); break;
-        case 2: fn = reinterpret_cast<const void*>(&sample_chain_b1<2>); break;
-        case 3: fn = reinterpret_cast<const void*>(&sample_chain_b1<3>); break;
-        case 4: fn = reinterpret_cast<const void*>(&sample_chain_b1<4>); break;
-        case 5: fn = reinterpret_cast<const void*>(&sample_chain_b1<5>); break;
-        case 6: fn = reinterpret_cast<const void*>(&sample_chain_b1<6>); break;
-        case 7: fn = reinterpret_cast<const void*>(&sample_chain_b1<7>); break;
-        case 8: fn = reinterpret_cast<const void*>(&sample_chain_b1<8>); break;
-        case 9: fn = reinterpret_cast<const void*>(&sample_chain_b1<9>); break;
-        default: fn = reinterpret_cast<const void*>(&sample_chain_b1<10>); break;
-    }
-    return hipLaunchCooperativeKernel(fn, dim3(p.nwg), dim3(kChainThreads), args, 0, stream);
+    const void* fn = chain_fn(p.nslot);
+    // A plain launch: every workgroup needs a whole CU (its register file) and
+    // the grid has at most one workgroup per CU, so on an otherwise idle GPU
+    // all of them are resident together.  The planner checked that one fits
+    // per CU; the bounded spin turns any other outcome into an error, not a
+    // hang.
+    return hipLaunchKernel(fn, dim3(p.nwg), dim3(kChainThreads), args, 0, stream);
 }
 
 struct Buffers {
@@ -574,7 +653,7 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
 size_t head_sample_workspace(int64_t B, int64_t gamma, int64_t, int64_t r) {
     size_t steps = ((size_t)(8 * B * gamma) + 255) / 256 * 256 + ((size_t)(4 * B * gamma) + 255) / 256 * 256;
     if (B == 1 && r == kChainRank) {
-        const size_t chain = kChainHeader + (size_t)8 * gamma * kChainMaxWGs;
+        const size_t chain = kChainHeader + (size_t)8 * kSlotWords * gamma * kChainMaxWGs;
         if (chain > steps) steps = chain;
     }
     return steps;
@@ -586,7 +665,7 @@ hipError_t head_sample_launch(int64_t B, int64_t gamma, int64_t V, int64_t H, in
                               float* conf, float* survival, float* logits_out, float* bias_out, void* ws,
                               hipStream_t stream) {
     if (chain_eligible(B, r, dtype, W1, W2)) {
-        const ChainPlan p = chain_plan(V);
+        const ChainPlan p = chain_plan(V, H);
         if (p.nwg > 0)
             return launch_chain(p, gamma, V, H, U, h, W1, W2, w_conf, b_conf, x0, gumbel, force, tokens, conf,
                                 survival, logits_out, bias_out, ws, stream);

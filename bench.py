@@ -52,6 +52,33 @@ def accept_call_bytes(N, V, elem=2):
     return 2 * N * V * elem + 4 * N
 
 
+def profiled_traffic(profile: str, sources: list[str]):
+    """HBM bytes per launch measured by the FETCH_SIZE / WRITE_SIZE counter
+    passes recorded in profiles/<profile>, or None when the kernel sources
+    changed since those counters were taken (hash mismatch) or no record
+    exists."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_launch", "source_sha256"):
+            k, v = line.split(":", 1)
+            rec[k] = v.strip()
+    h = hashlib.sha256()
+    for src in sources:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    if rec.get("source_sha256") != h.hexdigest()[:16] or "traffic_bytes_per_launch" not in rec:
+        return None
+    return int(float(rec["traffic_bytes_per_launch"]))
+
+
+SAMPLER_SOURCES = ["draft_head_sampling_amd/csrc/head_sample.hip", "draft_head_sampling_amd/csrc/internal.h"]
+ACCEPT_SOURCES = ["draft_head_sampling_amd/csrc/accept_rate.hip", "draft_head_sampling_amd/csrc/internal.h"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,7 +200,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": profiled_traffic("head_sample_chain_b1_vocab151936.md", SAMPLER_SOURCES),
             "bytes_per_launch": call_bytes,
             "us_per_launch": round(call_us, 3),
         },
@@ -207,7 +234,8 @@ def main():
             "us_per_call": round(a_us, 2), "positions_per_s": round(sa.N / (a_us * 1e-6), 1),
             "roofline": {"kernel": "dspark_accept_rate", "bound": "hbm", "achieved": round(gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": None, "bytes_per_launch": a_bytes},
+                         "traffic": profiled_traffic("accept_rate_rows_2048x151936.md", ACCEPT_SOURCES),
+                         "bytes_per_launch": a_bytes},
         }
         del D, T
 

@@ -65,3 +65,20 @@ def test_repeat_runs_are_bitwise_identical():
 def test_empty():
     z = torch.zeros((0, 10), device="cuda")
     assert dh.accept_rate(z, z).shape == (0,)
+
+
+def test_workspace_reuse_across_shapes():
+    """One zero-filled workspace serves calls of different shapes in a row:
+    every call leaves it zeroed, so results match fresh workspaces bitwise."""
+    import draft_head_sampling_amd as dh_
+
+    shapes = [(64, 151936, "bf16"), (5, 30001, "bf16"), (300, 8192, "f32"), (64, 151936, "bf16"), (1, 151936, "bf16")]
+    big = max(dh_.lib().dspark_accept_rate_workspace_size(N, V, 1) for N, V, _ in shapes)
+    ws = torch.zeros(big, dtype=torch.uint8, device="cuda")
+    for i, (N, V, dt) in enumerate(shapes):
+        d, t = synth.accept_inputs(synth.AcceptShape(N=N, V=V, dtype=dt, d_sd=3, scale=0.8, t_sd=1.5, seed=40 + i))
+        dd, tt = dev(d), dev(t)
+        a = dh.accept_rate(dd, tt, workspace=ws)
+        b = dh.accept_rate(dd, tt)
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (N, V)
+    assert int(ws.count_nonzero()) == 0

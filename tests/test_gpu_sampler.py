@@ -143,3 +143,21 @@ def test_batched_gumbel_full_vocabulary_sampled_requests():
             continue  # a near-tie changes the rest of this request's chain
         assert np.abs(conf[b] - ref["conf"][0]).max() <= 1e-4
         assert np.abs(surv[b] - ref["survival"][0]).max() <= 1e-4
+
+
+def test_workspace_reuse_across_shapes():
+    """One zero-filled workspace serves single-request calls of different
+    vocabulary sizes and block widths; each call leaves it zeroed."""
+    cases = [(151936, 7, False), (1000, 3, True), (70001, 9, False), (151936, 7, True)]
+    big = max(dh.head_sample_workspace_size(1, g, V, 64, 256) for V, g, _ in cases)
+    ws = torch.zeros(big, dtype=torch.uint8, device="cuda")
+    for i, (V, gamma, gumbel) in enumerate(cases):
+        s = synth.SamplerShape(B=1, gamma=gamma, V=V, H=64, r=256, dtype="bf16", w_sd=0.3, U_sd=2.0, wc_sd=0.05,
+                               gumbel=gumbel, seed=500 + i)
+        w, x = synth.sampler_weights(s), synth.sampler_batch(s)
+        args = [dev(v) for v in (x["U"], x["h"], w["W1"], w["W2"], w["w_conf"])] + [0.1, dev(x["x0"]), dev(x["G"])]
+        a = dh.head_sample(*args, workspace=ws)
+        b = dh.head_sample(*args)
+        for k in a:
+            assert torch.equal(a[k], b[k]), (V, k)
+        assert int(ws.count_nonzero()) == 0

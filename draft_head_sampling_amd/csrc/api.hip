@@ -55,7 +55,7 @@ DSPARK_EXPORT dspark_status_t dspark_head_sample(int64_t B, int64_t gamma, int64
     if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return DSPARK_ERR_BAD_DTYPE;
     if (!sampler_shape_ok(B, gamma, V, H, r)) return DSPARK_ERR_BAD_SHAPE;
     if (B == 0 || gamma == 0) return DSPARK_OK;
-    dspark_status_t st = check_workspace(workspace, workspace_bytes, dspark::head_sample_workspace(B, gamma, V, r));
+    dspark_status_t st = check_workspace(workspace, workspace_bytes, dspark::head_sample_workspace(B, gamma, V, r, dtype));
     if (st != DSPARK_OK) return st;
     if (!U || !W1 || !W2 || !w_conf || !x0 || !tokens || !conf || !survival || (H > 0 && !h))
         return DSPARK_ERR_NULL_ARG;
@@ -94,9 +94,9 @@ DSPARK_EXPORT dspark_status_t dspark_prefix_schedule(int64_t B, int64_t gamma, c
 }
 
 DSPARK_EXPORT size_t dspark_head_sample_workspace_size(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r,
-                                                       int32_t) {
+                                                       int32_t dtype) {
     if (!sampler_shape_ok(B, gamma, V, H, r)) return 0;
-    return dspark::head_sample_workspace(B, gamma, V, r);
+    return dspark::head_sample_workspace(B, gamma, V, r, dtype);
 }
 
 DSPARK_EXPORT size_t dspark_accept_rate_workspace_size(int64_t N, int64_t V, int32_t) {

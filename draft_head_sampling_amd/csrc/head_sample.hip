@@ -16,6 +16,8 @@
 //   finish decode tokens, add the Markov part of the confidence logit,
 //           sigmoid, running survival product
 // The [B x V] bias never reaches HBM unless the caller asks for it.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace dspark {
@@ -24,15 +26,31 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTile = 256;  // vocabulary rows per workgroup
 
+// Argmax key of request b at step k: the maximum over the ncopy key copies
+// (layout [ncopy][gamma][B], one key per 128-byte line; copies and spacing
+// spread the cross-workgroup atomics over many lines).
+constexpr int kKeyStride = 16;  // u64 words between argmax keys: one 128-byte line each
+
+__device__ __forceinline__ uint64_t* key_at(uint64_t* keys, int c, int64_t gamma, int64_t B, int k, int64_t b) {
+    return keys + (((int64_t)c * gamma + k) * B + b) * kKeyStride;
+}
+__device__ __forceinline__ uint64_t step_key(const uint64_t* keys, int ncopy, int64_t gamma, int64_t B, int k,
+                                             int64_t b) {
+    uint64_t m = 0;
+    for (int c = 0; c < ncopy; ++c) m = umax64(m, keys[(((int64_t)c * gamma + k) * B + b) * kKeyStride]);
+    return m;
+}
+
 // Previous token of request b at step k (0-based), or -1 once the request
 // has hit an invalid token id.
 __device__ __forceinline__ int32_t prev_token(int64_t b, int k, int64_t B, int64_t gamma, int64_t V,
-                                              const int32_t* x0, const int32_t* force, const uint64_t* keys) {
+                                              const int32_t* x0, const int32_t* force, const uint64_t* keys,
+                                              int ncopy = 1) {
     int64_t x;
     if (k == 0) {
         x = x0[b];
     } else {
-        const uint64_t key = keys[(int64_t)(k - 1) * B + b];
+        const uint64_t key = step_key(keys, ncopy, gamma, B, k - 1, b);
         if (key == 0) return -1;
         const int32_t f = force ? force[b * gamma + k - 1] : -1;
         x = f >= 0 ? f : key_token(key);
@@ -68,11 +86,11 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
 template <typename T>
 __global__ __launch_bounds__(kThreads) void sample_init(int64_t B, int64_t gamma, int64_t H, const T* __restrict__ h,
                                                         const T* __restrict__ w_conf, uint64_t* __restrict__ keys,
-                                                        float* __restrict__ hdot) {
+                                                        int ncopy, float* __restrict__ hdot) {
     __shared__ float red[kThreads / 64];
     const int64_t bk = blockIdx.x;  // b * gamma + k
     const int64_t b = bk / gamma, k = bk % gamma;
-    if (threadIdx.x == 0) keys[k * B + b] = 0;
+    if (threadIdx.x < ncopy) *key_at(keys, threadIdx.x, gamma, B, (int)k, b) = 0;
     float s = 0.f;
     for (int64_t i = threadIdx.x; i < H; i += kThreads) s += load_elem(w_conf, i) * load_elem(h, bk * H + i);
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
@@ -180,34 +198,49 @@ __global__ __launch_bounds__(kThreads) void sample_step(int64_t B, int64_t gamma
     if (tid < BG && b0 + tid < B && xprev[tid] >= 0) {
         uint64_t m = red[tid][0];
         for (int i = 1; i < kThreads / 64; ++i) m = umax64(m, red[tid][i]);
-        atomicMax((unsigned long long*)&keys[(int64_t)k * B + b0 + tid], (unsigned long long)m);
+        atomicMax((unsigned long long*)key_at(keys, 0, gamma, B, k, b0 + tid), (unsigned long long)m);
     }
 }
 
+// One workgroup per request, one wave per step (gamma <= 16): every step's
+// confidence in parallel, then the running survival product.
+constexpr int kFinishMaxGamma = 16;
+
 template <typename T>
-__global__ __launch_bounds__(64) void sample_finish(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r,
-                                                    const T* __restrict__ W1, const T* __restrict__ w_conf,
-                                                    float b_conf, const int32_t* __restrict__ x0,
-                                                    const int32_t* __restrict__ force, const uint64_t* keys,
-                                                    const float* __restrict__ hdot, int32_t* __restrict__ tokens,
-                                                    float* __restrict__ conf, float* __restrict__ survival) {
+__global__ __launch_bounds__(64 * kFinishMaxGamma) void sample_finish(
+    int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, const T* __restrict__ W1, const T* __restrict__ w_conf,
+    float b_conf, const int32_t* __restrict__ x0, const int32_t* __restrict__ force, const uint64_t* keys, int ncopy,
+    const float* __restrict__ hdot, int32_t* __restrict__ tokens, float* __restrict__ conf,
+    float* __restrict__ survival) {
+    __shared__ float cs[kFinishMaxGamma];
     const int64_t b = blockIdx.x;
-    const int lane = threadIdx.x;
-    float A = 1.f;
-    for (int k = 0; k < gamma; ++k) {
-        const int32_t x = prev_token(b, k, B, gamma, V, x0, force, keys);
-        float s = 0.f;
-        if (x >= 0)
-            for (int64_t j = lane; j < r; j += 64) s += load_elem(w_conf, H + j) * load_elem(W1, (int64_t)x * r + j);
-        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-        const float z = hdot[b * gamma + k] + s + b_conf;
-        const float c = x >= 0 ? 1.f / (1.f + expf(-z)) : __builtin_nanf("");
-        A = A * c;
-        if (lane == 0) {
-            tokens[b * gamma + k] = x >= 0 ? key_token(keys[(int64_t)k * B + b]) : -1;
-            conf[b * gamma + k] = c;
-            survival[b * gamma + k] = A;
+    const int lane = threadIdx.x & 63;
+    for (int k0 = 0; k0 < gamma; k0 += kFinishMaxGamma) {  // gamma beyond 16 takes several rounds
+        const int k = k0 + (int)(threadIdx.x >> 6);
+        if (k < gamma) {
+            const int32_t x = prev_token(b, k, B, gamma, V, x0, force, keys, ncopy);
+            float s = 0.f;
+            if (x >= 0)
+                for (int64_t j = lane; j < r; j += 64)
+                    s += load_elem(w_conf, H + j) * load_elem(W1, (int64_t)x * r + j);
+            for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+            const float z = hdot[b * gamma + k] + s + b_conf;
+            const float c = x >= 0 ? 1.f / (1.f + expf(-z)) : __builtin_nanf("");
+            if (lane == 0) {
+                tokens[b * gamma + k] = x >= 0 ? key_token(step_key(keys, ncopy, gamma, B, k, b)) : -1;
+                conf[b * gamma + k] = c;
+                cs[k - k0] = c;
+            }
         }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float A = k0 == 0 ? 1.f : survival[b * gamma + k0 - 1];
+            for (int kk = k0; kk < gamma && kk < k0 + kFinishMaxGamma; ++kk) {
+                A = A * cs[kk - k0];
+                survival[b * gamma + kk] = A;
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -568,16 +601,226 @@ hipError_t launch_chain(const ChainPlan& p, int64_t gamma, int64_t V, int64_t H,
     return hipLaunchKernel(fn, dim3(p.nwg), dim3(kChainThreads), args, 0, stream);
 }
 
+
+// ---------------------------------------------------------------------------
+// Batched step kernel on the matrix cores (bf16, rank 256).
+//
+// The bias of a whole step is the product W2[V, 256] . E^T[256, B], E = the
+// gathered W1 rows of the requests' previous tokens.  Each workgroup takes 128
+// vocabulary rows and up to 64 requests; each wave multiplies its 32 rows by
+// the requests with v_mfma_f32_32x32x16_bf16 (W2 rows as the A operand, E^T
+// as B), straight from HBM; the B operand comes from E in LDS.
+// The accumulator layout leaves each lane with 16 vocabulary rows of one
+// request, so the +U (+G) epilogue and the argmax are in-lane, then one swap
+// between lane halves and a 4-wave reduction in LDS.  The workgroup's U and G
+// tiles (64 requests x 128 rows) are fetched with coalesced 16-byte loads
+// before the products and parked in LDS (in E's space) for the epilogue; with
+// rows that are not 16-byte aligned each lane reads its own elements.  The
+// [B x V] bias never reaches HBM.  Keys go to one of 16 copies by workgroup,
+// to spread atomics.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kMfmaRank = 256;
+constexpr int kMfmaRows = 128;      // vocabulary rows per workgroup (32 per wave)
+constexpr int kKeyCopies = 16;
+constexpr int kMfmaMinBatch = 16;   // smaller batches stay on the vector path
+constexpr int kERow = kMfmaRank + 8;  // LDS row stride of E in bf16 (padding against bank conflicts)
+
+constexpr int kURow = kMfmaRows + 8;   // LDS row stride of the U tile (bf16)
+constexpr int kGRow = kMfmaRows + 4;   // LDS row stride of the G tile (fp32)
+
+template <int NT, bool STAGE>  // 32-request tiles per workgroup: 1 or 2; STAGE: coalesced U/G tiles via LDS
+__global__ __launch_bounds__(256) void sample_step_mfma(int64_t B, int64_t gamma, int k, int64_t V,
+                                                        const bf16_t* __restrict__ U, const bf16_t* __restrict__ W1,
+                                                        const bf16_t* __restrict__ W2, const float* __restrict__ G,
+                                                        const int32_t* __restrict__ x0,
+                                                        const int32_t* __restrict__ force, uint64_t* keys,
+                                                        float* __restrict__ logits_out, float* __restrict__ bias_out) {
+    constexpr int NREQ = 32 * NT;
+    constexpr int kEBytes = NREQ * kERow * 2;
+    constexpr int kTileBytes = NREQ * (kURow * 2 + kGRow * 4);
+    __shared__ __align__(16) uint8_t lds_raw[kEBytes > kTileBytes ? kEBytes : kTileBytes];
+    uint16_t* E_lds = reinterpret_cast<uint16_t*>(lds_raw);
+    uint16_t* U_lds = reinterpret_cast<uint16_t*>(lds_raw);                      // after the products
+    float* G_lds = reinterpret_cast<float*>(lds_raw + NREQ * kURow * 2);
+    __shared__ int32_t xprev[NREQ];
+    __shared__ uint64_t wkey[4][NREQ];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 31, half = lane >> 5;
+    const int64_t b0 = (int64_t)blockIdx.y * NREQ;
+    const int64_t v0 = (int64_t)blockIdx.x * kMfmaRows + wave * 32;
+
+    // Every load below is unconditional from an in-bounds (clamped) address, so
+    // the compiler issues them back to back; results of clamped rows or
+    // requests are discarded in the epilogue.  Order: the small key loads first
+    // (they gate the E gather), then W2, then the U/G tiles.
+    const int bl4 = tid >> 2, part = tid & 3;  // 4 threads per request for keys and the E gather
+    const bool req_ok = bl4 < NREQ && b0 + bl4 < B;
+    const int64_t bq = b0 + (req_ok ? bl4 : 0) < B ? b0 + (req_ok ? bl4 : 0) : B - 1;
+    uint64_t kv[kKeyCopies / 4];
+    if (k > 0) {
+#pragma unroll
+        for (int c = 0; c < kKeyCopies / 4; ++c) kv[c] = *key_at(keys, part * (kKeyCopies / 4) + c, gamma, B, k - 1, bq);
+    }
+
+    // W2 rows of this wave as A fragments: k-step s takes rank elements
+    // 16 s + 8 half .. +7 of row v0 + row (32 contiguous bytes per row per load)
+    uint4 a[16];
+    {
+        const int64_t v = v0 + row < V ? v0 + row : V - 1;
+        const uint4* src = reinterpret_cast<const uint4*>(W2 + v * kMfmaRank + half * 8);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a[i] = src[2 * i];
+    }
+
+    // U (and G) tiles, issued before the products
+    const int64_t vt = (int64_t)blockIdx.x * kMfmaRows;  // first vocabulary row of the tile
+    constexpr int UCH = NREQ * kMfmaRows * 2 / 16 / 256;  // 16-byte chunks per thread
+    constexpr int GCH = NREQ * kMfmaRows * 4 / 16 / 256;
+    uint4 us[STAGE ? UCH : 1], gs[STAGE ? GCH : 1];
+    float u[STAGE ? 1 : NT][16], gn[STAGE ? 1 : NT][16];
+    if constexpr (STAGE) {
+#pragma unroll
+        for (int i = 0; i < UCH; ++i) {
+            const int c = tid + 256 * i, bl = c / 16, col = (c % 16) * 8;
+            const int64_t b = b0 + bl < B ? b0 + bl : B - 1;
+            const int64_t vc = vt + col < V ? vt + col : V - 8;
+            us[i] = *reinterpret_cast<const uint4*>(U + (b * gamma + k) * V + vc);
+        }
+        if (G) {
+#pragma unroll
+            for (int i = 0; i < GCH; ++i) {
+                const int c = tid + 256 * i, bl = c / 32, col = (c % 32) * 4;
+                const int64_t b = b0 + bl < B ? b0 + bl : B - 1;
+                const int64_t vc = vt + col < V ? vt + col : V - 4;
+                gs[i] = *reinterpret_cast<const uint4*>(G + (b * gamma + k) * V + vc);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int64_t b = b0 + nt * 32 + row < B ? b0 + nt * 32 + row : B - 1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t v = v0 + 8 * (r / 4) + 4 * half + (r % 4);
+                const int64_t o = (b * gamma + k) * V + (v < V ? v : V - 1);
+                u[nt][r] = load_elem(U, o);
+                gn[nt][r] = G ? G[o] : 0.f;
+            }
+        }
+    }
+
+    // previous tokens of this workgroup's requests
+    {
+        int32_t x = -1;
+        if (k == 0) {
+            x = x0[bq];
+        } else {
+            uint64_t m = 0;
+#pragma unroll
+            for (int c = 0; c < kKeyCopies / 4; ++c) m = umax64(m, kv[c]);
+            m = umax64(m, shfl_xor_u64(m, 1));
+            m = umax64(m, shfl_xor_u64(m, 2));
+            const int32_t f = force ? force[bq * gamma + k - 1] : -1;
+            x = m == 0 ? -1 : (f >= 0 ? f : key_token(m));
+        }
+        if (x >= V) x = -1;
+        if (bl4 < NREQ && part == 0) xprev[bl4] = req_ok ? (x < 0 ? -1 : x) : -1;
+    }
+    __syncthreads();
+    // gather E = W1[x_prev] into LDS: 4 threads per request, 128 bytes each
+    if (bl4 < NREQ) {
+        const int32_t x = xprev[bl4];
+        const uint4* src = reinterpret_cast<const uint4*>(W1 + (int64_t)(x < 0 ? 0 : x) * kMfmaRank + part * 64);
+        uint4 e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = src[i];
+        uint4* dst = reinterpret_cast<uint4*>(E_lds + bl4 * kERow + part * 64);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dst[i] = e[i];
+    }
+    __syncthreads();
+
+    f32x16_t acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[nt][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a[s]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const uint4 bw = *reinterpret_cast<const uint4*>(E_lds + (nt * 32 + row) * kERow + s * 16 + half * 8);
+            acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, bw), acc[nt], 0, 0, 0);
+        }
+    }
+
+    if constexpr (STAGE) {  // E is no longer needed: its space takes the U and G tiles
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < UCH; ++i) {
+            const int c = tid + 256 * i, bl = c / 16, col = (c % 16) * 8;
+            *reinterpret_cast<uint4*>(U_lds + bl * kURow + col) = us[i];
+        }
+        if (G) {
+#pragma unroll
+            for (int i = 0; i < GCH; ++i) {
+                const int c = tid + 256 * i, bl = c / 32, col = (c % 32) * 4;
+                *reinterpret_cast<uint4*>(G_lds + bl * kGRow + col) = gs[i];
+            }
+        }
+        __syncthreads();
+    }
+
+    // epilogue: lane holds vocabulary rows v0 + 8(r/4) + 4 half + r%4 of request nt*32 + row
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int bl = nt * 32 + row;
+        const int64_t b = b0 + bl;
+        uint64_t key = 0;
+        if (b < B && xprev[bl] >= 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t v = v0 + 8 * (r / 4) + 4 * half + (r % 4);
+                if (v < V) {
+                    const int vl = wave * 32 + 8 * (r / 4) + 4 * half + (r % 4);  // row within the tile
+                    const float uu = STAGE ? widen_lo((uint32_t)U_lds[bl * kURow + vl]) : u[STAGE ? 0 : nt][r];
+                    const float gg = !G ? 0.f : (STAGE ? G_lds[bl * kGRow + vl] : gn[STAGE ? 0 : nt][r]);
+                    const float bias = acc[nt][r];
+                    const float lg = uu + bias;
+                    const float sc = G ? lg + gg : lg;
+                    const int64_t o = (b * gamma + k) * V + v;
+                    if (bias_out) bias_out[o] = bias;
+                    if (logits_out) logits_out[o] = lg;
+                    key = umax64(key, argmax_key(sc, (uint32_t)v));
+                }
+            }
+        }
+        key = umax64(key, shfl_xor_u64(key, 32));
+        if (half == 0) wkey[wave][bl] = key;
+    }
+    __syncthreads();
+    if (tid < NREQ && b0 + tid < B) {
+        uint64_t m = umax64(umax64(wkey[0][tid], wkey[1][tid]), umax64(wkey[2][tid], wkey[3][tid]));
+        if (m != 0)
+            atomicMax((unsigned long long*)key_at(keys, (int)(blockIdx.x % kKeyCopies), gamma, B, k, b0 + tid),
+                      (unsigned long long)m);
+    }
+}
+
 struct Buffers {
     uint64_t* keys;
     float* hdot;
 };
 
-Buffers carve(void* ws, int64_t B, int64_t gamma) {
+Buffers carve(void* ws, int64_t B, int64_t gamma, int ncopy) {
     char* p = static_cast<char*>(ws);
     Buffers s;
     s.keys = reinterpret_cast<uint64_t*>(p);
-    p += ((size_t)(8 * B * gamma) + 255) / 256 * 256;
+    p += ((size_t)(8 * kKeyStride * ncopy * B * gamma) + 255) / 256 * 256;
     s.hdot = reinterpret_cast<float*>(p);
     return s;
 }
@@ -618,10 +861,16 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
     const T* W1t = static_cast<const T*>(W1);
     const T* W2t = static_cast<const T*>(W2);
     const T* wt = static_cast<const T*>(w_conf);
-    Buffers s = carve(ws, B, gamma);
+
+    // batched bf16 rank-256 requests go to the matrix cores
+    bool mfma = false;
+    if constexpr (std::is_same_v<T, bf16_t>)
+        mfma = r == kMfmaRank && B >= kMfmaMinBatch && ((uintptr_t)W1 % 16 == 0) && ((uintptr_t)W2 % 16 == 0);
+    const int ncopy = mfma ? kKeyCopies : 1;
+    Buffers s = carve(ws, B, gamma, ncopy);
 
     hipLaunchKernelGGL((sample_init<T>), dim3((uint32_t)(B * gamma)), dim3(kThreads), 0, stream, B, gamma, H,
-                       static_cast<const T*>(h), wt, s.keys, s.hdot);
+                       static_cast<const T*>(h), wt, s.keys, ncopy, s.hdot);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
 
@@ -633,6 +882,25 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
         if ((q & (q - 1)) == 0) lpr = (int)q;
     }
     for (int k = 0; k < gamma; ++k) {
+        if constexpr (std::is_same_v<T, bf16_t>) {
+            if (mfma) {
+                const dim3 grid((uint32_t)((V + kMfmaRows - 1) / kMfmaRows), (uint32_t)((B + 63) / 64));
+                // coalesced tiles need 16-byte aligned U and G rows
+                const bool stage = V % 8 == 0 && (uintptr_t)U % 16 == 0 && (G == nullptr || (uintptr_t)G % 16 == 0);
+#define DSPARK_MFMA(NT, ST)                                                                                         \
+    hipLaunchKernelGGL((sample_step_mfma<NT, ST>), grid, dim3(256), 0, stream, B, gamma, k, V, Ut, W1t, W2t, G, x0, \
+                       force, s.keys, lo, bo)
+                if (B <= 32) {
+                    if (stage) DSPARK_MFMA(1, true); else DSPARK_MFMA(1, false);
+                } else {
+                    if (stage) DSPARK_MFMA(2, true); else DSPARK_MFMA(2, false);
+                }
+#undef DSPARK_MFMA
+                err = hipGetLastError();
+                if (err != hipSuccess) return err;
+                continue;
+            }
+        }
         if (B == 1)
             err = launch_steps<T, 1>(lpr, B, gamma, k, V, r, Ut, W1t, W2t, G, x0, force, s.keys, lo, bo, stream);
         else if (B == 2)
@@ -643,15 +911,18 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
             err = launch_steps<T, 8>(lpr, B, gamma, k, V, r, Ut, W1t, W2t, G, x0, force, s.keys, lo, bo, stream);
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL((sample_finish<T>), dim3((uint32_t)B), dim3(64), 0, stream, B, gamma, V, H, r, W1t, wt, b_conf,
-                       x0, force, s.keys, s.hdot, tokens, conf, survival);
+    const int fwaves = gamma < kFinishMaxGamma ? (int)gamma : kFinishMaxGamma;
+    hipLaunchKernelGGL((sample_finish<T>), dim3((uint32_t)B), dim3(64 * fwaves), 0, stream, B, gamma, V, H, r, W1t, wt,
+                       b_conf, x0, force, s.keys, ncopy, s.hdot, tokens, conf, survival);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t head_sample_workspace(int64_t B, int64_t gamma, int64_t, int64_t r) {
-    size_t steps = ((size_t)(8 * B * gamma) + 255) / 256 * 256 + ((size_t)(4 * B * gamma) + 255) / 256 * 256;
+size_t head_sample_workspace(int64_t B, int64_t gamma, int64_t, int64_t r, int dtype) {
+    const int64_t ncopy = (dtype == kBF16 && r == kMfmaRank && B >= kMfmaMinBatch) ? kKeyCopies : 1;
+    size_t steps = ((size_t)(8 * kKeyStride * ncopy * B * gamma) + 255) / 256 * 256 +
+                   ((size_t)(4 * B * gamma) + 255) / 256 * 256;
     if (B == 1 && r == kChainRank) {
         const size_t chain = kChainHeader + (size_t)8 * kSlotWords * gamma * kChainMaxWGs;
         if (chain > steps) steps = chain;

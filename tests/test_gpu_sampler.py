@@ -50,6 +50,12 @@ def test_tiny_workload_with_logits():
         (1, 9, 163840, 8, 256, "bf16", 0.2, False),  # largest vocabulary held on chip
         (1, 4, 200003, 8, 256, "bf16", 0.2, True),  # beyond it: per-step kernels
         (1, 2, 1, 8, 256, "bf16", 0.5, False),  # single-token vocabulary
+        # batched bf16 rank 256: matrix-core step kernel
+        (16, 4, 4099, 32, 256, "bf16", 0.5, False),  # one 32-request tile, ragged vocabulary
+        (33, 3, 1000, 16, 256, "bf16", 0.5, True),  # two tiles, padded
+        (100, 2, 2053, 16, 256, "bf16", 0.3, True),  # two request blocks
+        (20, 20, 700, 8, 256, "bf16", 0.5, False),  # gamma above 16: confidences in two rounds
+        (3, 18, 500, 8, 32, "f32", 0.5, False),  # same on the vector path
     ],
 )
 def test_shapes(B, gamma, V, H, r, dtype, w_sd, gumbel):

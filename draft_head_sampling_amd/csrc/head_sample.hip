@@ -327,7 +327,60 @@ constexpr int kChainMaxWGs = 256;   // 4 slots per lane when polling
 constexpr int kSlotWords = 16;      // 128-byte stride between slots (key, partial logit, padding)
 constexpr int kChainPoll = kChainMaxWGs / 64;
 constexpr int kChainSpinLimit = 1 << 21;
-constexpr size_t kChainHeader = 256;  // exit counter, status word
+constexpr size_t kChainHeader = 256;  // exit counter, status word, decision word (byte 128)
+
+// Candidate screen.  The Markov bias of a row is bounded by Cauchy-Schwarz,
+// |W2[v] . e| <= |W2[v]| |e|, so at step k only rows whose bias-free score
+// t_v = U_k[v] (+ G_k[v]) lies within twice that bound (plus rounding
+// slack) of the best t can win the argmax.  Two rounds settle the block:
+//   1. every row workgroup publishes, per step, its best ranking key (the
+//      order-preserving image of t with the low 10 bits replaced by the row's
+//      index in the workgroup), a bound on |U| + |G| and its slice of the
+//      hidden part of the confidence logit;
+//   2. workgroup 0, which holds no rows, turns them into a window per step
+//      (best t minus a guess of twice the bound) and broadcasts it; every row
+//      workgroup lists its rows inside the window (at most three per step).
+// Workgroup 0 then stages the W1 and W2 rows of the listed candidates in LDS,
+// precomputes every bias the chain can need, and once the largest W2 row norm
+// is in (the rows stream through registers only for it), walks the chain in
+// one wave.  A step whose candidate set is not provably inside the lists
+// hands the rest of the block to the grid-wide per-step exchange, which then
+// keeps each workgroup's W2 rows in registers.
+constexpr int kScreenMaxGamma = 8;   // U and G of every step stay in registers during the screen
+constexpr int kR1 = 3;               // round-1 words per step: best key, |U|+|G| bound, hidden partial
+constexpr int kR2 = 3;               // round-2 words per step: listed rows
+constexpr int kScreenWaves = kChainWaves / 2;  // row workgroups: waves that screen; the others take the norms
+constexpr int kScreenLanes = 64 * kScreenWaves;
+constexpr int kScreenRows = 3;       // rows per screening lane
+constexpr int kNormLanes = kChainThreads - kScreenLanes;
+constexpr int kNormGroups = kNormLanes / kChainLanesPerRow;  // rows per norm slot
+constexpr int kStreamSlots = 8;      // W2 slots in flight per norm lane
+constexpr int kRegionWords = 64;     // u64 words per workgroup region: one per lane of a wave
+constexpr int kPollRegions = kChainMaxWGs / kChainWaves;  // regions polled per coordinator wave
+constexpr int kCandMax = 32;         // candidate rows staged in LDS
+constexpr int kCandPerWave = kCandMax / kChainWaves;
+constexpr int kSampleRows = kChainThreads / kChainLanesPerRow;  // W2 rows sampled for the window guess
+constexpr int kLidBits = 10;         // row index inside a workgroup (rows_per_wg <= 640)
+constexpr uint32_t kLidMask = (1u << kLidBits) - 1;
+constexpr uint64_t kEmptyEntry = 1ull << 31;         // no row (low word above any row id + 1)
+constexpr uint64_t kOverflowEntry = (1ull << 31) | 1;  // more rows inside the window than listed
+constexpr uint64_t kTag = 1ull << 32;                // marks a written scalar word
+constexpr uint64_t kDecideDone = 1ull << 63;
+constexpr uint64_t kDecideResume = 1ull << 62;       // | step << 32 | previous token
+constexpr size_t kDecisionOffset = 128;              // bytes into the header
+constexpr size_t kWindowOffset = 160;                // bytes into the header: one word per step
+constexpr float kN2Guess = 1.5f;                     // sampled squared norm -> guess of the largest
+static_assert((kR1 + kR2) * kScreenMaxGamma + 1 <= kRegionWords, "screen region too small");
+static_assert(kWindowOffset + 8 * kScreenMaxGamma <= kChainHeader, "window words outside the header");
+static_assert(kCandMax % kChainWaves == 0, "candidates per wave");
+static_assert(kChainMaxSlots * kChainGroups <= (1 << kLidBits), "row index field too small");
+static_assert(kChainMaxSlots * kChainGroups <= kScreenRows * kScreenLanes, "screening lanes cover the rows");
+// Slack on the bias bound: covers fp32 rounding of the squared norms, of the
+// square roots and of any summation order of a 256-term dot product
+// (relative 256 * 2^-24 each), with a wide margin.
+constexpr float kBetaSlack = 1.0f + 1.0f / 256;
+constexpr float kBetaFloor = 1e-30f;  // products flushed as denormals
+constexpr float kUlp = 0x1p-24f;
 
 __device__ __forceinline__ void load64B(const bf16_t* p, uint32_t (&r)[16]) {
     const uint4* q = reinterpret_cast<const uint4*>(p);
@@ -338,31 +391,657 @@ __device__ __forceinline__ void load64B(const bf16_t* p, uint32_t (&r)[16]) {
     }
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor1, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor2, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppHalfMirror, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppMirror, 0xF, 0xF, false));
+    return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+               max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+    v = __builtin_fmaxf(v, dpp_f32<kDppXor1>(v));
+    v = __builtin_fmaxf(v, dpp_f32<kDppXor2>(v));
+    v = __builtin_fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+    v = __builtin_fmaxf(v, dpp_f32<kDppMirror>(v));
+    return __builtin_fmaxf(__builtin_fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
+                                           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))),
+                           __builtin_fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)),
+                                           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48))));
+}
+
+// Lower end of t over a 32-bit ranking key's bucket; key 0 (no row) is -infinity.
+__device__ __forceinline__ double key_lower(uint32_t q) {
+    return q == 0 ? -__builtin_inf() : (double)from_orderable(q & ~kLidMask);
+}
+// Non-negative float bits with NaN and overflow mapped to +infinity, so an
+// unsigned max over them is a float max that cannot lose a NaN.
+__device__ __forceinline__ uint32_t bound_bits(float a) {
+    return a <= 3.402823466e38f ? __float_as_uint(a) : 0x7f800000u;
+}
+__device__ __forceinline__ bool finite_bits(uint32_t b) { return b < 0x7f800000u; }
+// Largest float not above x (NaN stays NaN).
+__device__ __forceinline__ float float_down(double x) {
+    float f = (float)x;
+    if ((double)f > x) {  // one representable step down
+        const uint32_t b = __float_as_uint(f);
+        f = __uint_as_float(f > 0.f ? b - 1 : f < 0.f ? b + 1 : 0x80000001u);
+    }
+    return f;
+}
+__device__ __forceinline__ uint32_t ranking_key(float t, uint32_t lid) {
+    return (orderable(t) & ~kLidMask) | lid;
+}
+
+constexpr int kERows = kCandMax + 1 + kScreenMaxGamma;  // e rows: candidates' W1 rows, anchor, forced
+constexpr int kERowAnchor = kCandMax;
+constexpr int kERowForced = kCandMax + 1;
+static_assert(kERows <= 64, "one e row per lane");
+
+struct ScreenLds {
+    uint32_t cw2[kCandMax][kChainRank / 2];         // W2 rows of the candidates (bf16 pairs)
+    uint32_t cw1[kCandMax][kChainRank / 2];         // their W1 rows: e of the next step if one wins
+    float bias[kCandMax][kERows];                   // W2[candidate] . e for every possible predecessor
+    uint32_t fw1[kScreenMaxGamma][kChainRank / 2];  // W1 rows of teacher-forced tokens
+    uint32_t e0[kChainRank / 2];                    // W1 row of the anchor
+    uint32_t cv[kCandMax];
+    int cstep[kCandMax];
+    float cu[kCandMax], cg[kCandMax], ct[kCandMax];
+    float esq[kERows], zcm[kERows];                 // |e|^2 and w_e . e of every e row
+    uint32_t stepmask[kScreenMaxGamma];             // candidates of each step
+    float pw[kScreenMaxGamma][kChainWaves];
+    uint32_t wn[kChainWaves];
+    uint32_t smax[kChainWaves][kRegionWords];
+    float ssum[kChainWaves][kRegionWords];
+    uint32_t fmax[kRegionWords];
+    float fsum[kRegionWords];
+    float pk[kScreenMaxGamma];
+    float winf[kScreenMaxGamma];
+    uint32_t m1[kScreenMaxGamma], a1[kScreenMaxGamma];  // row workgroup: round-1 maxima
+    int cnt[kScreenMaxGamma];
+    int sync;                                        // arrivals of the screening waves
+    uint64_t lst[kScreenMaxGamma][kR2];
+    int32_t fv[kScreenMaxGamma];
+    int overflow[kScreenMaxGamma];
+    uint32_t n2, n2s;
+    int ncand, abort;
+    uint64_t decision;
+};
+
+// Hidden part of the confidence logit of every step over this workgroup's
+// slice [h_lo, h_hi) of H, from `nt` threads: per-thread sums over chunks
+// of nt elements, then fixed-order wave sums into s.pw[k][wave].  The loads
+// of a chunk are unconditional from clamped indices (a load under a branch
+// would be waited for at the branch's end, one round trip per load).
+__device__ __forceinline__ void hidden_partials(ScreenLds& s, int gamma, int64_t H, int64_t h_lo, int64_t h_hi,
+                                                const bf16_t* __restrict__ h, const bf16_t* __restrict__ w_conf,
+                                                int t, int nt, int lane, int wave) {
+    float p[kScreenMaxGamma];
+#pragma unroll
+    for (int k = 0; k < kScreenMaxGamma; ++k) p[k] = 0.f;
+    for (int64_t base = h_lo; base < h_hi; base += nt) {  // workgroup-uniform trip count
+        const int64_t i = base + t;
+        const bool use = i < h_hi;
+        const int64_t ic = use ? i : 0;
+        const uint16_t wb = w_conf[ic].bits;
+        uint16_t hb[kScreenMaxGamma];
+#pragma unroll
+        for (int k = 0; k < kScreenMaxGamma; ++k) hb[k] = h[(int64_t)min(k, gamma - 1) * H + ic].bits;
+        const float w = use ? __uint_as_float((uint32_t)wb << 16) : 0.f;
+#pragma unroll
+        for (int k = 0; k < kScreenMaxGamma; ++k) p[k] += w * __uint_as_float((uint32_t)hb[k] << 16);
+    }
+#pragma unroll
+    for (int k = 0; k < kScreenMaxGamma; ++k) {
+        if (k >= gamma) break;
+        const float v = wave_sum_f32(p[k]);
+        if (lane == 0) s.pw[k][wave] = v;
+    }
+}
+
+// Barrier of the screening waves alone (the norm waves keep streaming): each
+// wave's arrival is an LDS increment ordered after its earlier LDS writes.
+__device__ __forceinline__ void screen_sync(ScreenLds& s, int lane, int target) {
+    if (lane == 0) __hip_atomic_fetch_add(&s.sync, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int spin = 0; spin < kChainSpinLimit; ++spin) {  // bounded like every wait here
+        if (__hip_atomic_load(&s.sync, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
 template <int NSLOT>
 __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
-    int gamma, int64_t V, int64_t H, int rows_per_wg, const bf16_t* __restrict__ U, const bf16_t* __restrict__ h,
-    const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W2, const bf16_t* __restrict__ w_conf, float b_conf,
-    const int32_t* __restrict__ x0, const float* __restrict__ G, const int32_t* __restrict__ force,
-    int32_t* __restrict__ tokens, float* __restrict__ conf, float* __restrict__ survival,
-    float* __restrict__ logits_out, float* __restrict__ bias_out, uint64_t* slots, uint32_t* header) {
+    int gamma, int64_t V, int64_t H, int rows_per_wg, int screen, const bf16_t* __restrict__ U,
+    const bf16_t* __restrict__ h, const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W2,
+    const bf16_t* __restrict__ w_conf, float b_conf, const int32_t* __restrict__ x0, const float* __restrict__ G,
+    const int32_t* __restrict__ force, int32_t* __restrict__ tokens, float* __restrict__ conf,
+    float* __restrict__ survival, float* __restrict__ logits_out, float* __restrict__ bias_out, uint64_t* slots,
+    uint64_t* regions, uint32_t* header) {
     __shared__ uint64_t red[kChainWaves];
     __shared__ float fred[kChainWaves];
     __shared__ uint32_t we_lds[kChainRank / 2];  // Markov part of the confidence weights (workgroup 0)
     __shared__ uint64_t winner;
     __shared__ float zpart;
     __shared__ int last_flag;
+    __shared__ ScreenLds sc;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = tid >> 3, sub = tid & 7;
     const int g = blockIdx.x, nwg = gridDim.x;
-    const int64_t row0 = (int64_t)g * rows_per_wg;
-    const bool wg0 = g == 0;
+    const bool wg0 = g == 0;  // the coordinator: no vocabulary rows
+    const int64_t row0 = wg0 ? V : (int64_t)(g - 1) * rows_per_wg;
     const int64_t h_per = (H + nwg - 1) / nwg;  // hidden elements of this workgroup's confidence partial
     const int64_t h_lo = (int64_t)g * h_per < H ? (int64_t)g * h_per : H;
     const int64_t h_hi = h_lo + h_per < H ? h_lo + h_per : H;
+    uint64_t* decision = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(header) + kDecisionOffset);
+    uint64_t* windows = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(header) + kWindowOffset);
+    const int n1 = kR1 * gamma;           // round-1 words
+    const int nwords = n1 + kR2 * gamma + 1;  // then round-2 words, then the largest squared W2 row norm
+    uint64_t* myregion = regions + (int64_t)g * kRegionWords;
 
-    // this workgroup's W2 rows first: the largest load and independent of the anchor
+    const int64_t xa = x0[0];
+    const bool scr = screen && xa >= 0 && xa < V;  // the same in every workgroup
+
+    constexpr int NMINE = NSLOT > 8 ? 2 : 1;  // lane `sub` finishes slots sub and sub + 8
+    int64_t my_v[NMINE];
+    bool my_ok[NMINE];
+#pragma unroll
+    for (int m = 0; m < NMINE; ++m) {
+        const int slot = sub + 8 * m;
+        const int lr = slot * kChainGroups + grp;
+        my_v[m] = row0 + lr;
+        my_ok[m] = slot < NSLOT && lr < rows_per_wg && my_v[m] < V;
+    }
+
     uint32_t w2[NSLOT][16];
+    int k0 = 0;           // first step left to the grid-wide exchange
+    int64_t x = xa;       // token before step k0
+    bool valid = xa >= 0 && xa < V;
+    bool done = false;    // the whole block is settled
+    float A = 1.f;        // running survival (workgroup 0, thread 0)
+
+    if (wg0) {
+        if (tid < kChainRank / 2)
+            we_lds[tid] = (uint32_t)w_conf[H + 2 * tid].bits | ((uint32_t)w_conf[H + 2 * tid + 1].bits << 16);
+        if (scr) {
+            // prologue: anchor row, forced tokens, own hidden slice, and a
+            // sample of W2 rows whose largest norm sets the window guess
+            uint32_t smp[16];
+            load64B(W2 + (int64_t)grp * (V / kSampleRows) * kChainRank + sub * 32, smp);
+            if (tid < kChainRank / 2) sc.e0[tid] = reinterpret_cast<const uint32_t*>(W1 + xa * kChainRank)[tid];
+            if (tid < kScreenMaxGamma) {
+                sc.fv[tid] = (force && tid < gamma) ? force[tid] : -1;
+                sc.overflow[tid] = 0;
+            }
+            if (tid == 0) sc.ncand = 0, sc.abort = 0, sc.n2 = 0;
+            hidden_partials(sc, gamma, H, h_lo, h_hi, h, w_conf, tid, kChainThreads, lane, wave);
+            {
+                float a = 0.f;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) a = dot2(smp[q], smp[q], a);
+                const uint32_t m = wave_max_u32(bound_bits(sum8(a)));
+                if (lane == 0) sc.wn[wave] = m;
+            }
+            __syncthreads();
+            if (tid < gamma) {
+                float ps = 0.f;
+#pragma unroll
+                for (int w = 0; w < kChainWaves; ++w) ps += sc.pw[tid][w];
+                sc.pk[tid] = ps;
+            }
+            if (tid == kChainThreads - 1) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int w = 0; w < kChainWaves; ++w) m = max(m, sc.wn[w]);
+                sc.n2s = m;
+            }
+            if (wave == 0) {
+                const float es = wave_sum_f32(dot2(sc.e0[2 * lane + 1], sc.e0[2 * lane + 1],
+                                                   dot2(sc.e0[2 * lane], sc.e0[2 * lane], 0.f)));
+                if (lane == 0) sc.esq[kERowAnchor] = es;
+            }
+
+            // round 1: wave w polls row workgroups 1 + w + 8 i, lane j reads
+            // word j; the spin only checks that every word is written
+            uint64_t word[kPollRegions];
+            bool ready = false;
+            for (int spin = 0; spin < kChainSpinLimit && !ready; ++spin) {
+                bool all = true;
+#pragma unroll
+                for (int i = 0; i < kPollRegions; ++i) {
+                    const int gg = 1 + wave + kChainWaves * i;
+                    const bool use = gg < nwg && lane < n1;
+                    word[i] = __hip_atomic_load(regions + (use ? (int64_t)gg * kRegionWords + lane : 0),
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    all = all && (!use || word[i] != 0);
+                }
+                ready = __all(all);
+                if (!ready) __builtin_amdgcn_s_sleep(1);
+            }
+            if (!ready && lane == 0) sc.abort = 1;
+            {
+                const int type = lane % kR1;  // 0: best key, 1: |U|+|G| bound, 2: hidden partial
+                uint32_t mx = 0;
+                float sm = 0.f;
+#pragma unroll
+                for (int i = 0; i < kPollRegions; ++i) {
+                    const bool in = 1 + wave + kChainWaves * i < nwg;
+                    const uint32_t v32 = (uint32_t)word[i];
+                    mx = (in && type < 2) ? max(mx, v32) : mx;
+                    sm += (in && type == 2) ? __uint_as_float(v32) : 0.f;
+                }
+                sc.smax[wave][lane] = mx;
+                sc.ssum[wave][lane] = sm;
+            }
+            __syncthreads();
+            if (wave == 0) {
+                uint32_t m = 0;
+                float sm = 0.f;
+#pragma unroll
+                for (int w = 0; w < kChainWaves; ++w) m = max(m, sc.smax[w][lane]), sm += sc.ssum[w][lane];
+                sc.fmax[lane] = m;
+                sc.fsum[lane] = sm;
+            }
+            __syncthreads();
+            // the windows: best t minus twice a guess of the bias bound (the
+            // sampled norm and the anchor row's norm, both enlarged) plus
+            // rounding slack; the walk checks them against the real bound
+            if (tid < gamma) {
+                const float bg = __builtin_sqrtf(__uint_as_float(sc.n2s) * kN2Guess) * 2.f *
+                                     __builtin_sqrtf(sc.esq[kERowAnchor]) * kBetaSlack +
+                                 kBetaFloor;
+                const float a = __uint_as_float(sc.fmax[kR1 * tid + 1]);
+                const float eg = 5.f * kUlp * (a + bg);
+                const float wf = float_down(key_lower(sc.fmax[kR1 * tid]) - 2.0 * ((double)bg + eg));
+                sc.winf[tid] = wf;
+                __hip_atomic_store(windows + tid, kTag | __float_as_uint(wf), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+
+            // round 2: the listed rows
+            ready = false;
+            for (int spin = 0; spin < kChainSpinLimit && !ready; ++spin) {
+                bool all = true;
+#pragma unroll
+                for (int i = 0; i < kPollRegions; ++i) {
+                    const int gg = 1 + wave + kChainWaves * i;
+                    const bool use = gg < nwg && lane < kR2 * gamma;
+                    word[i] = __hip_atomic_load(regions + (use ? (int64_t)gg * kRegionWords + n1 + lane : 0),
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    all = all && (!use || word[i] != 0);
+                }
+                ready = __all(all);
+                if (!ready) __builtin_amdgcn_s_sleep(1);
+            }
+            if (!ready && lane == 0) sc.abort = 1;
+            if (lane < kR2 * gamma) {
+                const int k = lane / kR2;
+#pragma unroll
+                for (int i = 0; i < kPollRegions; ++i) {
+                    if (1 + wave + kChainWaves * i >= nwg) continue;
+                    const uint64_t w = word[i];
+                    const uint32_t id1 = (uint32_t)w;  // row id + 1, or a marker
+                    if (w == kOverflowEntry) {
+                        sc.overflow[k] = 1;
+                    } else if (id1 >= 1 && id1 <= (uint64_t)V) {
+                        const int idx = atomicAdd(&sc.ncand, 1);
+                        if (idx < kCandMax) sc.cv[idx] = id1 - 1, sc.cstep[idx] = k;
+                        else sc.overflow[k] = 1;
+                    }
+                }
+            }
+            __syncthreads();
+            // every row workgroup has read the windows
+            if (tid < gamma)
+                __hip_atomic_store(windows + tid, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool abort = sc.abort != 0;
+            const int nc = sc.ncand < kCandMax ? sc.ncand : kCandMax;
+
+            // stage the candidates' rows (one wave per candidate) and forced tokens' rows
+            if (!abort) {
+                uint2 ra[kCandPerWave], rb[kCandPerWave];
+                float cu[kCandPerWave], cg[kCandPerWave];
+#pragma unroll
+                for (int q = 0; q < kCandPerWave; ++q) {
+                    const int j = wave + kChainWaves * q;
+                    const bool use = j < nc;
+                    const int64_t v = use ? sc.cv[j] : 0;
+                    const int64_t o = use ? (int64_t)sc.cstep[j] * V + v : 0;
+                    ra[q] = reinterpret_cast<const uint2*>(W2 + v * kChainRank)[lane];
+                    rb[q] = reinterpret_cast<const uint2*>(W1 + v * kChainRank)[lane];
+                    cu[q] = load_elem(U, o);
+                    cg[q] = G ? G[o] : 0.f;
+                }
+                const int kf = wave < gamma ? wave : 0;
+                const int32_t f = sc.fv[kf];
+                const bool fuse = wave < gamma && f >= 0 && f < V;
+                const uint2 fr = reinterpret_cast<const uint2*>(W1 + (int64_t)(fuse ? f : 0) * kChainRank)[lane];
+#pragma unroll
+                for (int q = 0; q < kCandPerWave; ++q) {
+                    const int j = wave + kChainWaves * q;
+                    if (j < nc) {
+                        sc.cw2[j][2 * lane] = ra[q].x, sc.cw2[j][2 * lane + 1] = ra[q].y;
+                        sc.cw1[j][2 * lane] = rb[q].x, sc.cw1[j][2 * lane + 1] = rb[q].y;
+                        if (lane == 0) sc.cu[j] = cu[q], sc.cg[j] = cg[q], sc.ct[j] = G ? cu[q] + cg[q] : cu[q];
+                    }
+                }
+                if (fuse) sc.fw1[kf][2 * lane] = fr.x, sc.fw1[kf][2 * lane + 1] = fr.y;
+                if (wave == 0) {
+                    const int cs = lane < nc ? sc.cstep[lane] : -1;
+#pragma unroll
+                    for (int k = 0; k < kScreenMaxGamma; ++k) {
+                        const uint32_t m = (uint32_t)__ballot(cs == k);
+                        if (lane == 0) sc.stepmask[k] = m;
+                    }
+                }
+            }
+            __syncthreads();
+
+            // every quantity the chain can need, in parallel: |e|^2 and
+            // w_e . e of each e row, and W2[j] . e for each candidate j and
+            // each e row that can precede its step
+            if (!abort) {
+                for (int r = wave; r < kERows; r += kChainWaves) {
+                    const uint32_t* er = r < kCandMax ? sc.cw1[r] : r == kERowAnchor ? sc.e0 : sc.fw1[r - kERowForced];
+                    const bool use = r < nc || r == kERowAnchor ||
+                                     (r >= kERowForced && r - kERowForced < gamma && sc.fv[r - kERowForced] >= 0 &&
+                                      sc.fv[r - kERowForced] < V);
+                    if (!use) continue;
+                    const uint32_t ex = er[2 * lane], ey = er[2 * lane + 1];
+                    const float es = wave_sum_f32(dot2(ey, ey, dot2(ex, ex, 0.f)));
+                    const float zc = wave_sum_f32(dot2(we_lds[2 * lane + 1], ey, dot2(we_lds[2 * lane], ex, 0.f)));
+                    if (lane == 0) sc.esq[r] = es, sc.zcm[r] = zc;
+                }
+                for (int j = wave; j < nc; j += kChainWaves) {
+                    const int k = sc.cstep[j];
+                    uint64_t preds;  // e rows that can be e at step k
+                    if (k == 0) preds = 1ull << kERowAnchor;
+                    else if (sc.fv[k - 1] >= 0) preds = 1ull << (kERowForced + k - 1);
+                    else preds = sc.stepmask[k - 1];
+                    const uint32_t wx = sc.cw2[j][2 * lane], wy = sc.cw2[j][2 * lane + 1];
+                    while (preds) {
+                        const int r = __builtin_ctzll(preds);
+                        preds &= preds - 1;
+                        const uint32_t* er = r < kCandMax ? sc.cw1[r] : r == kERowAnchor ? sc.e0 : sc.fw1[r - kERowForced];
+                        const float b = wave_sum_f32(dot2(wy, er[2 * lane + 1], dot2(wx, er[2 * lane], 0.f)));
+                        if (lane == 0) sc.bias[j][r] = b;
+                    }
+                }
+            }
+            // the largest squared W2 row norm, one workgroup per thread
+            if (!abort && tid + 1 < nwg) {
+                const uint64_t* p = regions + (int64_t)(tid + 1) * kRegionWords + nwords - 1;
+                uint64_t w = 0;
+                for (int spin = 0; spin < kChainSpinLimit && w == 0; ++spin) {
+                    w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (w == 0) __builtin_amdgcn_s_sleep(1);
+                }
+                if (w == 0) sc.abort = 1;
+                atomicMax(&sc.n2, (uint32_t)w);
+            }
+            __syncthreads();
+
+            // the walk, in wave 0: lane j holds candidate j, lane r e row r,
+            // lane k the per-step quantities
+            if (wave == 0) {
+                const bool mine = lane < nc;
+                const int cs = mine ? sc.cstep[lane] : -1;
+                const float ct = mine ? sc.ct[lane] : 0.f, cu = mine ? sc.cu[lane] : 0.f, cg = mine ? sc.cg[lane] : 0.f;
+                const uint32_t cv = mine ? sc.cv[lane] : 0u;
+                const float l_esq = lane < kERows ? sc.esq[lane] : 0.f;
+                const int ks = lane < kScreenMaxGamma ? lane : 0;
+                const uint32_t l_ab = sc.fmax[kR1 * ks + 1];
+                const float l_win = sc.winf[ks];
+                const int l_ovf = sc.overflow[ks];
+                const int32_t l_fv = sc.fv[ks];
+                float l_tmax = -__builtin_inff();
+#pragma unroll
+                for (int k = 0; k < kScreenMaxGamma; ++k) {
+                    const float m = wave_max_f32(cs == k ? ct : -__builtin_inff());
+                    if (lane == k) l_tmax = m;
+                }
+                const uint32_t n2b = sc.n2;  // largest squared W2 row norm
+                const float n2 = __builtin_sqrtf(__uint_as_float(n2b));
+                int cur = kERowAnchor;  // e row of the current step
+                int pst = 0;            // e row used at this lane's step (lane k)
+                int32_t tk = -1;        // token of this lane's step (lane k)
+                int k = 0;
+                bool fail = sc.abort != 0;
+                for (; k < gamma && !fail; ++k) {
+                    if (!valid) continue;
+                    const float es = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_esq), cur));
+                    const uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)l_ab, k);
+                    const float tmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_tmax), k));
+                    const float win = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_win), k));
+                    const float beta = n2 * __builtin_sqrtf(es) * kBetaSlack + kBetaFloor;
+                    const float eps = 5.f * kUlp * (__uint_as_float(ab) + beta);
+                    const double thr = (double)tmax - 2.0 * ((double)beta + eps);
+                    const bool ok = __builtin_amdgcn_readlane(l_ovf, k) == 0 && finite_bits(ab) && finite_bits(n2b) &&
+                                    finite_bits(bound_bits(es)) && tmax > -__builtin_inff() && thr >= (double)win;
+                    if (!ok) {
+                        fail = true;
+                        break;
+                    }
+                    const bool cand = cs == k && (double)ct >= thr;
+                    const float lg = cu + (cand ? sc.bias[lane & (kCandMax - 1)][cur] : 0.f);
+                    const uint64_t key = cand ? argmax_key(G ? lg + cg : lg, cv) : 0;
+                    const uint64_t best = wave_max_u64(key);
+                    if (best == 0) {  // cannot happen: the best listed row is always a candidate
+                        fail = true;
+                        break;
+                    }
+                    const int jw = __builtin_ctzll(__ballot(key == best && cand));
+                    const int32_t tok = key_token(best);
+                    if (lane == k) pst = cur, tk = tok;
+                    const int32_t f = __builtin_amdgcn_readlane(l_fv, k);
+                    x = f >= 0 ? f : tok;
+                    valid = x >= 0 && x < V;
+                    cur = f >= 0 ? kERowForced + k : jw;
+                }
+                // confidences of the settled steps in parallel, then the running product
+                const int settled = k;
+                float c = 0.f;
+                if (lane < settled && tk >= 0)
+                    c = 1.f / (1.f + expf(-(sc.pk[lane] + sc.fsum[kR1 * lane + 2] + sc.zcm[pst] + b_conf)));
+                if (lane < settled) tokens[lane] = tk;
+                float surv = 1.f;
+                bool alive = true;
+                for (int q = 0; q < settled; ++q) {
+                    const float cq = __shfl(c, q);
+                    alive = alive && __shfl(tk, q) >= 0;
+                    surv = surv * cq;
+                    if (lane == q) {
+                        conf[q] = alive ? cq : __builtin_nanf("");
+                        survival[q] = alive ? surv : __builtin_nanf("");
+                    }
+                }
+                if (lane == 0) A = surv;
+                if (sc.abort) {  // some workgroup never arrived: report, release the others
+                    if (lane == 0) header[1] = 1u;
+                    for (int j = lane; j < gamma; j += 64)
+                        tokens[j] = -1, conf[j] = __builtin_nanf(""), survival[j] = __builtin_nanf("");
+                }
+                if (lane == 0) {
+                    const uint64_t d = (fail && !sc.abort)
+                                           ? (kDecideResume | ((uint64_t)k << 32) | (uint64_t)(uint32_t)x)
+                                           : kDecideDone;
+                    sc.decision = d;
+                    __hip_atomic_store(decision, d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+            __syncthreads();
+            const uint64_t d = sc.decision;
+            if (d & kDecideDone) {
+                // each row workgroup clears its region once it has read the
+                // decision; when all have, the decision word goes back to zero
+                if (tid + 1 < nwg) {
+                    const uint64_t* r = regions + (int64_t)(tid + 1) * kRegionWords;
+                    for (int spin = 0; spin < kChainSpinLimit; ++spin) {
+                        if (__hip_atomic_load(r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) break;
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                }
+                __syncthreads();
+                if (tid == 0) __hip_atomic_store(decision, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                done = true;
+            } else {
+                k0 = (int)((d >> 32) & 0xffff);
+                x = (int32_t)(uint32_t)d;
+                valid = true;
+            }
+        }
+    } else if (scr) {
+        if (tid < kScreenMaxGamma) sc.m1[tid] = 0, sc.a1[tid] = 0, sc.cnt[tid] = 0;
+        if (tid == 0) sc.sync = 0;
+        __syncthreads();
+        if (wave < kScreenWaves) {
+            // Screening waves: nothing of W2 is in flight here, so every wait
+            // for a small load is exact.  Lane i screens rows i, i + 256, ...
+            hidden_partials(sc, gamma, H, h_lo, h_hi, h, w_conf, tid, kScreenLanes, lane, wave);
+            int64_t sv[kScreenRows];
+            bool sok[kScreenRows];
+            uint16_t ur[kScreenMaxGamma][kScreenRows];
+            float gs[kScreenMaxGamma][kScreenRows];
+#pragma unroll
+            for (int m = 0; m < kScreenRows; ++m) {
+                const int lr = tid + kScreenLanes * m;
+                sv[m] = row0 + lr;
+                sok[m] = lr < rows_per_wg && sv[m] < V;
+            }
+#pragma unroll
+            for (int k = 0; k < kScreenMaxGamma; ++k)
+#pragma unroll
+                for (int m = 0; m < kScreenRows; ++m) {
+                    const int64_t o = (k < gamma && sok[m]) ? (int64_t)k * V + sv[m] : 0;
+                    ur[k][m] = U[o].bits;
+                    gs[k][m] = G ? G[o] : 0.f;
+                }
+            // round 1: the workgroup's best ranking key and |U|+|G| bound per step
+#pragma unroll
+            for (int k = 0; k < kScreenMaxGamma; ++k) {
+                if (k >= gamma) break;
+                uint32_t best = 0, am = 0;
+#pragma unroll
+                for (int m = 0; m < kScreenRows; ++m) {
+                    if (!sok[m]) continue;
+                    const float u = __uint_as_float((uint32_t)ur[k][m] << 16);
+                    am = max(am, bound_bits(__builtin_fabsf(u) + __builtin_fabsf(gs[k][m])));
+                    best = max(best, ranking_key(G ? u + gs[k][m] : u, (uint32_t)(sv[m] - row0)));
+                }
+                best = wave_max_u32(best);
+                am = wave_max_u32(am);
+                if (lane == 0) atomicMax(&sc.m1[k], best), atomicMax(&sc.a1[k], am);
+            }
+            screen_sync(sc, lane, kScreenWaves);
+            if (tid < gamma) {
+                float ps = 0.f;
+#pragma unroll
+                for (int w = 0; w < kScreenWaves; ++w) ps += sc.pw[tid][w];
+                __hip_atomic_store(myregion + kR1 * tid, kTag | sc.m1[tid], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(myregion + kR1 * tid + 1, kTag | sc.a1[tid], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(myregion + kR1 * tid + 2, kTag | __float_as_uint(ps), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                // round 2: the windows
+                uint64_t w = 0;
+                for (int spin = 0; spin < kChainSpinLimit && w == 0; ++spin) {
+                    w = __hip_atomic_load(windows + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (w == 0) __builtin_amdgcn_s_sleep(1);
+                }
+                // no window in time: list nothing and flag the step
+                sc.winf[tid] = w ? __uint_as_float((uint32_t)w) : __builtin_nanf("");
+                if (w == 0) sc.cnt[tid] = kR2 + 1;
+            }
+            screen_sync(sc, lane, 2 * kScreenWaves);
+            // every screening lane lists its rows inside the windows
+#pragma unroll
+            for (int k = 0; k < kScreenMaxGamma; ++k) {
+                if (k >= gamma) break;
+                const float wk = sc.winf[k];
+#pragma unroll
+                for (int m = 0; m < kScreenRows; ++m) {
+                    const float u = __uint_as_float((uint32_t)ur[k][m] << 16);
+                    const float t = G ? u + gs[k][m] : u;
+                    if (sok[m] && t >= wk) {
+                        const int idx = atomicAdd(&sc.cnt[k], 1);
+                        if (idx < kR2)
+                            sc.lst[k][idx] = ((uint64_t)ranking_key(t, (uint32_t)(sv[m] - row0)) << 32) |
+                                             (uint64_t)(sv[m] + 1);
+                    }
+                }
+            }
+            screen_sync(sc, lane, 3 * kScreenWaves);
+            if (tid < kR2 * gamma) {
+                const int k = tid / kR2, e = tid % kR2;
+                const int c = sc.cnt[k];
+                const uint64_t w =
+                    (c > kR2 && e == kR2 - 1) ? kOverflowEntry : e < c ? sc.lst[k][e] : kEmptyEntry;
+                __hip_atomic_store(myregion + n1 + tid, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        } else {
+            // Norm waves: the W2 slice streams through a window of slots for
+            // the largest squared row norm.  Rows past the slice load row 0
+            // and are masked out (a zero fill would wait for the load it
+            // overwrites).
+            const int ng = (tid - kScreenLanes) >> 3;
+            constexpr int NS = (NSLOT * kChainGroups + kNormGroups - 1) / kNormGroups;
+            uint32_t buf[kStreamSlots][16];
+#pragma unroll
+            for (int i = 0; i < kStreamSlots; ++i) {
+                const int lr = i * kNormGroups + ng;
+                const bool in = i < NS && lr < rows_per_wg && row0 + lr < V;
+                load64B(W2 + (in ? row0 + lr : 0) * kChainRank + sub * 32, buf[i]);
+            }
+            uint32_t nb = 0;
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                float a = 0.f;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) a = dot2(buf[i % kStreamSlots][q], buf[i % kStreamSlots][q], a);
+                a = sum8(a);
+                const int lr = i * kNormGroups + ng;
+                if (lr < rows_per_wg && row0 + lr < V) nb = max(nb, bound_bits(a));
+                if (i + kStreamSlots < NS) {
+                    const int lr2 = (i + kStreamSlots) * kNormGroups + ng;
+                    const bool in = lr2 < rows_per_wg && row0 + lr2 < V;
+                    load64B(W2 + (in ? row0 + lr2 : 0) * kChainRank + sub * 32, buf[i % kStreamSlots]);
+                }
+            }
+            nb = wave_max_u32(nb);
+            if (lane == 0) sc.wn[wave] = nb;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int w = kScreenWaves; w < kChainWaves; ++w) m = max(m, sc.wn[w]);
+            __hip_atomic_store(myregion + nwords - 1, kTag | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // wait for the coordinator's decision
+            uint64_t d = 0;
+            for (int spin = 0; spin < kChainSpinLimit && d == 0; ++spin) {
+                d = __hip_atomic_load(decision, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (d == 0) __builtin_amdgcn_s_sleep(2);
+            }
+            sc.decision = d;
+        }
+        __syncthreads();
+        const uint64_t d = sc.decision;
+        if (tid < nwords)  // read by the coordinator before it decided
+            __hip_atomic_store(myregion + tid, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0 || (d & kDecideDone)) {
+            done = true;
+        } else {
+            k0 = (int)((d >> 32) & 0xffff);
+            x = (int32_t)(uint32_t)d;
+            valid = true;
+        }
+    }
+
+    if (done) return;  // settled by the screen: no slots were written, the regions are clear
+
+    // the per-step exchange keeps this workgroup's W2 rows in registers
 #pragma unroll
     for (int i = 0; i < NSLOT; ++i) {
         const int lr = i * kChainGroups + grp;
@@ -375,140 +1054,132 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
         }
     }
 
-    // step-0 row gather (it waits on the anchor id)
-    int64_t x = x0[0];
-    bool valid = x >= 0 && x < V;
-    uint32_t e[16];
-    if (valid) load64B(W1 + x * kChainRank + sub * 32, e);
-
-    constexpr int NMINE = NSLOT > 8 ? 2 : 1;  // lane `sub` finishes slots sub and sub + 8
-    int64_t my_v[NMINE];
-    bool my_ok[NMINE];
-    float u_next[NMINE], g_next[NMINE];
-#pragma unroll
-    for (int m = 0; m < NMINE; ++m) {
-        const int slot = sub + 8 * m;
-        const int lr = slot * kChainGroups + grp;
-        my_v[m] = row0 + lr;
-        my_ok[m] = slot < NSLOT && lr < rows_per_wg && my_v[m] < V;
-        u_next[m] = my_ok[m] ? load_elem(U, my_v[m]) : 0.f;
-        g_next[m] = (my_ok[m] && G) ? G[my_v[m]] : 0.f;
-    }
-    if (wg0 && tid < kChainRank / 2)
-        we_lds[tid] = (uint32_t)w_conf[H + 2 * tid].bits | ((uint32_t)w_conf[H + 2 * tid + 1].bits << 16);
-    __syncthreads();
-
-    float A = 1.f;
-    for (int k = 0; k < gamma; ++k) {
-        if (!valid) {  // identical in every workgroup: no exchange needed
-            if (wg0 && tid == 0) tokens[k] = -1, conf[k] = __builtin_nanf(""), survival[k] = __builtin_nanf("");
-            continue;
-        }
-        // this workgroup's share of the confidence logit: a slice of w_h . h_k
-        // (loaded here, summed after the dot products), plus (workgroup 0) the
-        // Markov part w_e . e
-        float p = 0.f;
-        for (int64_t i = h_lo + tid; i < h_hi; i += kChainThreads)
-            p += load_elem(w_conf, i) * load_elem(h, (int64_t)k * H + i);
-        float acc[NSLOT];
-#pragma unroll
-        for (int i = 0; i < NSLOT; ++i) {
-            float a = 0.f;
-#pragma unroll
-            for (int q = 0; q < 16; ++q) a = dot2(w2[i][q], e[q], a);
-            acc[i] = sum8(a);
-        }
-        uint64_t key = 0;
+    {
+        // the grid-wide per-step exchange, from step k0 on
+        uint32_t e[16];
+        if (valid) load64B(W1 + x * kChainRank + sub * 32, e);
+        float u_next[NMINE], g_next[NMINE];
 #pragma unroll
         for (int m = 0; m < NMINE; ++m) {
-            float bias = 0.f;
-#pragma unroll
-            for (int i = 0; i < NSLOT; ++i) bias = (sub + 8 * m == i) ? acc[i] : bias;
-            if (my_ok[m]) {
-                const float lg = u_next[m] + bias;
-                const float sc = G ? lg + g_next[m] : lg;
-                if (bias_out) bias_out[(int64_t)k * V + my_v[m]] = bias;
-                if (logits_out) logits_out[(int64_t)k * V + my_v[m]] = lg;
-                key = umax64(key, argmax_key(sc, (uint32_t)my_v[m]));
-                if (k + 1 < gamma) {  // next step's inputs do not depend on this step's token
-                    u_next[m] = load_elem(U, (int64_t)(k + 1) * V + my_v[m]);
-                    if (G) g_next[m] = G[(int64_t)(k + 1) * V + my_v[m]];
-                }
-            }
+            const int64_t o = my_ok[m] ? (int64_t)k0 * V + my_v[m] : 0;
+            u_next[m] = load_elem(U, o);
+            g_next[m] = G ? G[o] : 0.f;
         }
-        if (wg0 && tid < 8)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) p = dot2(we_lds[tid * 16 + q], e[q], p);
-        p = wave_sum_f32(p);
-        key = wave_max_u64(key);
-        if (lane == 0) red[wave] = key, fred[wave] = p;
         __syncthreads();
-        if (tid == 0) {
-            uint64_t m = 1;  // a workgroup without rows still publishes a non-zero key
-            float ps = 0.f;
-#pragma unroll
-            for (int w = 0; w < kChainWaves; ++w) m = umax64(m, red[w]), ps += fred[w];
-            uint64_t* slot = slots + ((int64_t)k * nwg + g) * kSlotWords;
-            __hip_atomic_store(slot, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(slot + 1, (1ull << 32) | __float_as_uint(ps), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
 
-        if (wave == 0) {
-            uint64_t best = 0;
-            float zsum = 0.f;
-            for (int spin = 0; spin < kChainSpinLimit; ++spin) {
-                uint64_t sk[kChainPoll], sp[kChainPoll];
+        for (int k = k0; k < gamma; ++k) {
+            if (!valid) {  // identical in every workgroup: no exchange needed
+                if (wg0 && tid == 0) tokens[k] = -1, conf[k] = __builtin_nanf(""), survival[k] = __builtin_nanf("");
+                continue;
+            }
+            // this workgroup's share of the confidence logit: a slice of w_h . h_k
+            // (loaded here, summed after the dot products), plus (workgroup 0) the
+            // Markov part w_e . e
+            float p = 0.f;
+            for (int64_t i = h_lo + tid; i < h_hi; i += kChainThreads)
+                p += load_elem(w_conf, i) * load_elem(h, (int64_t)k * H + i);
+            float acc[NSLOT];
 #pragma unroll
-                for (int i = 0; i < kChainPoll; ++i) {
-                    const int j = lane + 64 * i;
-                    const uint64_t* slot = slots + ((int64_t)k * nwg + j) * kSlotWords;
-                    sk[i] = j < nwg ? __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1ull;
-                    sp[i] = j < nwg ? __hip_atomic_load(slot + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                    : (1ull << 32);
+            for (int i = 0; i < NSLOT; ++i) {
+                float a = 0.f;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) a = dot2(w2[i][q], e[q], a);
+                acc[i] = sum8(a);
+            }
+            uint64_t key = 0;
+#pragma unroll
+            for (int m = 0; m < NMINE; ++m) {
+                float bias = 0.f;
+#pragma unroll
+                for (int i = 0; i < NSLOT; ++i) bias = (sub + 8 * m == i) ? acc[i] : bias;
+                if (my_ok[m]) {
+                    const float lg = u_next[m] + bias;
+                    const float sc2 = G ? lg + g_next[m] : lg;
+                    if (bias_out) bias_out[(int64_t)k * V + my_v[m]] = bias;
+                    if (logits_out) logits_out[(int64_t)k * V + my_v[m]] = lg;
+                    key = umax64(key, argmax_key(sc2, (uint32_t)my_v[m]));
                 }
-                bool all = true;
-                uint64_t m = 0;
+                // next step's inputs do not depend on this step's token; loaded
+                // unconditionally from a clamped index so nothing waits for them here
+                const int64_t on = (my_ok[m] && k + 1 < gamma) ? (int64_t)(k + 1) * V + my_v[m] : 0;
+                u_next[m] = load_elem(U, on);
+                if (G) g_next[m] = G[on];
+            }
+            if (wg0 && tid < 8)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) p = dot2(we_lds[tid * 16 + q], e[q], p);
+            p = wave_sum_f32(p);
+            key = wave_max_u64(key);
+            if (lane == 0) red[wave] = key, fred[wave] = p;
+            __syncthreads();
+            if (tid == 0) {
+                uint64_t m = 1;  // a workgroup without rows still publishes a non-zero key
                 float ps = 0.f;
 #pragma unroll
-                for (int i = 0; i < kChainPoll; ++i) {
-                    all = all && sk[i] != 0 && sp[i] != 0;
-                    m = umax64(m, sk[i]);
-                    ps += __uint_as_float((uint32_t)sp[i]);
-                }
-                if (__all(all)) {
-                    best = wave_max_u64(m);
-                    zsum = wave_sum_f32(ps);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
+                for (int w = 0; w < kChainWaves; ++w) m = umax64(m, red[w]), ps += fred[w];
+                uint64_t* slot = slots + ((int64_t)k * nwg + g) * kSlotWords;
+                __hip_atomic_store(slot, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(slot + 1, (1ull << 32) | __float_as_uint(ps), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
             }
-            if (lane == 0) {
-                winner = best;
-                zpart = zsum;
-                if (best == 0 && wg0) header[1] = 1u;  // timed out: reported as token -1
+
+            if (wave == 0) {
+                uint64_t best = 0;
+                float zsum = 0.f;
+                for (int spin = 0; spin < kChainSpinLimit; ++spin) {
+                    uint64_t sk[kChainPoll], sp[kChainPoll];
+#pragma unroll
+                    for (int i = 0; i < kChainPoll; ++i) {  // clamped, unconditional: all in flight at once
+                        const int j = lane + 64 * i;
+                        const uint64_t* slot = slots + ((int64_t)k * nwg + (j < nwg ? j : 0)) * kSlotWords;
+                        const uint64_t a = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        const uint64_t b = __hip_atomic_load(slot + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        sk[i] = j < nwg ? a : 1ull;
+                        sp[i] = j < nwg ? b : (1ull << 32);
+                    }
+                    bool all = true;
+                    uint64_t m = 0;
+                    float ps = 0.f;
+#pragma unroll
+                    for (int i = 0; i < kChainPoll; ++i) {
+                        all = all && sk[i] != 0 && sp[i] != 0;
+                        m = umax64(m, sk[i]);
+                        ps += __uint_as_float((uint32_t)sp[i]);
+                    }
+                    if (__all(all)) {
+                        best = wave_max_u64(m);
+                        zsum = wave_sum_f32(ps);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                if (lane == 0) {
+                    winner = best;
+                    zpart = zsum;
+                    if (best == 0 && wg0) header[1] = 1u;  // timed out: reported as token -1
+                }
             }
-        }
-        __syncthreads();
-        const uint64_t wk = winner;
-        if (wg0 && tid == 0) {
-            const float c = 1.f / (1.f + expf(-(zpart + b_conf)));
-            A = A * c;
-            conf[k] = c;
-            survival[k] = A;
-        }
-        const int32_t tok = key_token(wk);
-        const int32_t f = (force && wk != 0) ? force[k] : -1;
-        x = f >= 0 ? f : tok;
-        valid = wk != 0 && x >= 0 && x < V;
-        if (valid && k + 1 < gamma) load64B(W1 + x * kChainRank + sub * 32, e);
-        if (wg0 && tid == 0) {
-            tokens[k] = tok;
-            if (wk == 0) conf[k] = __builtin_nanf(""), survival[k] = __builtin_nanf("");
+            __syncthreads();
+            const uint64_t wk = winner;
+            if (wg0 && tid == 0) {
+                const float c = 1.f / (1.f + expf(-(zpart + b_conf)));
+                A = A * c;
+                conf[k] = c;
+                survival[k] = A;
+            }
+            const int32_t tok = key_token(wk);
+            const int32_t f = (force && wk != 0) ? force[k] : -1;
+            x = f >= 0 ? f : tok;
+            valid = wk != 0 && x >= 0 && x < V;
+            if (valid && k + 1 < gamma) load64B(W1 + x * kChainRank + sub * 32, e);
+            if (wg0 && tid == 0) {
+                tokens[k] = tok;
+                if (wk == 0) conf[k] = __builtin_nanf(""), survival[k] = __builtin_nanf("");
+            }
         }
     }
 
-    // leave: the last workgroup out clears the slots for the next call
+    // leave: the last workgroup out clears the slots and the decision word for the next call
     __syncthreads();
     if (tid == 0) {
         const uint32_t old = __hip_atomic_fetch_add(&header[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
@@ -520,7 +1191,10 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             __hip_atomic_store(&slots[i * kSlotWords], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&slots[i * kSlotWords + 1], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (tid == 0) __hip_atomic_store(&header[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) {
+            __hip_atomic_store(decision, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&header[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
@@ -556,24 +1230,29 @@ int device_cus() {
     return cache[dev];
 }
 
+// Workgroup 0 coordinates; workgroups 1.. hold the vocabulary rows.
 ChainPlan chain_plan(int64_t V, int64_t H) {
     ChainPlan p;
     const int cus = device_cus();
-    if (cus <= 0) return p;
-    int64_t nwg = (V + kChainGroups - 1) / kChainGroups;  // at least one full slot of rows per workgroup
-    if (nwg > cus) nwg = cus;
-    if (nwg > kChainMaxWGs) nwg = kChainMaxWGs;
-    const int64_t rows = (V + nwg - 1) / nwg;
+    if (cus < 2) return p;
+    int64_t nrow = (V + kChainGroups - 1) / kChainGroups;  // at least one full slot of rows per workgroup
+    if (nrow > cus - 1) nrow = cus - 1;
+    if (nrow > kChainMaxWGs - 1) nrow = kChainMaxWGs - 1;
+    const int64_t rows = (V + nrow - 1) / nrow;
     const int64_t nslot = (rows + kChainGroups - 1) / kChainGroups;
     if (nslot > kChainMaxSlots) return p;
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_fn((int)nslot), kChainThreads, 0) != hipSuccess ||
         per_cu < 1)
         return p;
-    p.nwg = (int)nwg;
+    p.nwg = (int)nrow + 1;
     p.rows_per_wg = (int)rows;
     p.nslot = (int)nslot;
     return p;
+}
+
+size_t chain_workspace(int64_t gamma) {
+    return kChainHeader + (size_t)8 * kSlotWords * gamma * kChainMaxWGs + (size_t)8 * kRegionWords * kChainMaxWGs;
 }
 
 hipError_t launch_chain(const ChainPlan& p, int64_t gamma, int64_t V, int64_t H, const void* U, const void* h,
@@ -583,6 +1262,8 @@ hipError_t launch_chain(const ChainPlan& p, int64_t gamma, int64_t V, int64_t H,
     int g = (int)gamma;
     int64_t Vv = V, Hh = H;
     int rows = p.rows_per_wg;
+    // the screen needs every step's U and G in registers and no full logit rows requested
+    int screen = (gamma <= kScreenMaxGamma && lo == nullptr && bo == nullptr) ? 1 : 0;
     const bf16_t* Ut = static_cast<const bf16_t*>(U);
     const bf16_t* ht = static_cast<const bf16_t*>(h);
     const bf16_t* W1t = static_cast<const bf16_t*>(W1);
@@ -590,13 +1271,14 @@ hipError_t launch_chain(const ChainPlan& p, int64_t gamma, int64_t V, int64_t H,
     const bf16_t* wt = static_cast<const bf16_t*>(w_conf);
     uint32_t* header = static_cast<uint32_t*>(ws);
     uint64_t* slots = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kChainHeader);
-    void* args[] = {&g,  &Vv,    &Hh, &rows,   &Ut,     &ht,       &W1t, &W2t, &wt,    &b_conf,
-                    &x0, &G,     &force, &tokens, &conf, &survival, &lo,  &bo,  &slots, &header};
+    uint64_t* regions = slots + (size_t)kSlotWords * gamma * kChainMaxWGs;
+    void* args[] = {&g,  &Vv, &Hh,    &rows,   &screen, &Ut,       &ht, &W1t, &W2t,  &wt,      &b_conf,
+                    &x0, &G,  &force, &tokens, &conf,   &survival, &lo, &bo,  &slots, &regions, &header};
     const void* fn = chain_fn(p.nslot);
     // A plain launch: every workgroup needs a whole CU (its register file) and
     // the grid has at most one workgroup per CU, so on an otherwise idle GPU
     // all of them are resident together.  The planner checked that one fits
-    // per CU; the bounded spin turns any other outcome into an error, not a
+    // per CU; the bounded spins turn any other outcome into an error, not a
     // hang.
     return hipLaunchKernel(fn, dim3(p.nwg), dim3(kChainThreads), args, 0, stream);
 }
@@ -924,7 +1606,7 @@ size_t head_sample_workspace(int64_t B, int64_t gamma, int64_t, int64_t r, int d
     size_t steps = ((size_t)(8 * kKeyStride * ncopy * B * gamma) + 255) / 256 * 256 +
                    ((size_t)(4 * B * gamma) + 255) / 256 * 256;
     if (B == 1 && r == kChainRank) {
-        const size_t chain = kChainHeader + (size_t)8 * kSlotWords * gamma * kChainMaxWGs;
+        const size_t chain = chain_workspace(gamma);
         if (chain > steps) steps = chain;
     }
     return steps;

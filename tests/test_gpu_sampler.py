@@ -12,7 +12,7 @@ import torch
 import draft_head_sampling_amd as dh
 import oracle
 import synth
-from helpers import dev, sampler_parity
+from helpers import dev, run_gpu_sampler, sampler_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +47,7 @@ def test_tiny_workload_with_logits():
         # single request, bf16, rank 256: the persistent chain kernel
         (1, 7, 1000, 16, 256, "bf16", 0.5, True),  # few workgroups, Gumbel
         (1, 5, 70001, 72, 256, "bf16", 0.3, False),  # ragged slices, H not a multiple of 64
-        (1, 9, 163840, 8, 256, "bf16", 0.2, False),  # largest vocabulary held on chip
+        (1, 9, 163200, 8, 256, "bf16", 0.2, False),  # largest vocabulary held on chip, gamma above the screen
         (1, 4, 200003, 8, 256, "bf16", 0.2, True),  # beyond it: per-step kernels
         (1, 2, 1, 8, 256, "bf16", 0.5, False),  # single-token vocabulary
         # batched bf16 rank 256: matrix-core step kernel
@@ -129,6 +129,53 @@ def test_single_request_strong_bias():
     got, ref, _ = sampler_parity(x, w)
     plain = np.argmax(synth.bf16_to_f32(x["U"][0]), axis=1)
     assert np.mean(plain != ref["tokens"][0]) > 0.5  # the Markov chain does decide here
+
+
+def test_single_request_gumbel_screened():
+    """B=1 full vocabulary with Gumbel noise and the weak bias of the
+    workload: every step is settled by the candidate screen."""
+    b1 = synth.SAMPLER_B1
+    s = synth.SamplerShape(B=1, gamma=b1.gamma, V=b1.V, H=b1.H, r=b1.r, dtype=b1.dtype, w_sd=b1.w_sd, U_sd=b1.U_sd,
+                           wc_sd=b1.wc_sd, gumbel=True, seed=b1.seed + 77)
+    w = synth.sampler_weights(s)
+    for anchor in range(2):
+        sampler_parity(synth.sampler_batch(s, batch_id=anchor), w)
+
+
+def test_single_request_flat_step_falls_back_mid_block():
+    """A step whose base logits are flat over the whole vocabulary has far
+    more candidates than the per-workgroup lists hold; the block is finished
+    by the grid-wide exchange from that step on."""
+    s = synth.SAMPLER_B1
+    w = synth.sampler_weights(s)
+    x = synth.sampler_batch(s, batch_id=5)
+    x["U"][0, 3, :] = synth.f32_to_bf16(np.full(s.V, 5.0, np.float32))
+    got, ref, ties = sampler_parity(x, w)
+    print(f"flat step 3: {ties} near-tie steps")
+
+
+def test_single_request_teacher_forced_screened():
+    """Forced tokens on the screened path: valid ones replace the sampled
+    token as the next step's previous token; an out-of-range one ends the
+    block's chain (tokens -1, confidences NaN)."""
+    s = synth.SAMPLER_B1
+    w = synth.sampler_weights(s)
+    x = synth.sampler_batch(s, batch_id=9)
+    force = np.full((1, s.gamma), -1, np.int32)
+    force[0, 1] = 1234
+    force[0, 3] = s.V - 1
+    got = run_gpu_sampler(x, w, force, want_logits=False)
+    ref = oracle.head_sample(x["U"], x["h"], w["W1"], w["W2"], w["w_conf"], w["b_conf"], x["x0"], None, force)
+    for k in range(s.gamma):
+        if got["tokens"][0, k] != ref["tokens"][0, k]:
+            assert ref["margin"][0, k] < 1e-3, k
+            break
+        assert abs(got["conf"][0, k] - ref["conf"][0, k]) <= 1e-4
+        assert abs(got["survival"][0, k] - ref["survival"][0, k]) <= 1e-4
+    force[0, 2] = s.V + 5
+    got = run_gpu_sampler(x, w, force, want_logits=False)
+    assert np.all(got["tokens"][0, 3:] == -1) and np.isnan(got["conf"][0, 3:]).all()
+    assert np.all(got["tokens"][0, :3] >= 0) and np.isfinite(got["conf"][0, :3]).all()
 
 
 def test_batched_gumbel_full_vocabulary_sampled_requests():

@@ -332,23 +332,23 @@ constexpr size_t kChainHeader = 256;  // exit counter, status word, decision wor
 // Candidate screen.  The Markov bias of a row is bounded by Cauchy-Schwarz,
 // |W2[v] . e| <= |W2[v]| |e|, so at step k only rows whose bias-free score
 // t_v = U_k[v] (+ G_k[v]) lies within twice that bound (plus rounding
-// slack) of the best t can win the argmax.  Two rounds settle the block:
-//   1. every row workgroup publishes, per step, its best ranking key (the
-//      order-preserving image of t with the low 10 bits replaced by the row's
-//      index in the workgroup), a bound on |U| + |G| and its slice of the
-//      hidden part of the confidence logit;
-//   2. workgroup 0, which holds no rows, turns them into a window per step
-//      (best t minus a guess of twice the bound) and broadcasts it; every row
-//      workgroup lists its rows inside the window (at most three per step).
-// Workgroup 0 then stages the W1 and W2 rows of the listed candidates in LDS,
-// precomputes every bias the chain can need, and once the largest W2 row norm
-// is in (the rows stream through registers only for it), walks the chain in
-// one wave.  A step whose candidate set is not provably inside the lists
-// hands the rest of the block to the grid-wide per-step exchange, which then
-// keeps each workgroup's W2 rows in registers.
+// slack) of the best t can win the argmax.  Every row workgroup publishes,
+// per step, its three best rows by ranking key (the order-preserving image
+// of t with the low 10 bits replaced by the row's index in the workgroup),
+// the fourth key as a cutoff, a bound on |U| + |G| and its slice of the
+// hidden part of the confidence logit.  Workgroup 0, which holds no rows,
+// keeps the entries within a window of the best t (best t minus a guess of
+// twice the bound), stages their W1 and W2 rows in LDS, precomputes every
+// bias the chain can need and walks the chain in one wave, first with the
+// guessed bound and, if the largest W2 row norm turns out larger, again.  The
+// W2 rows stream through registers only for that norm, after the lists are
+// out: behind a full HBM queue every cross-workgroup message takes several
+// microseconds.  A step whose candidate set is not provably inside the
+// lists hands the rest of the block to the grid-wide per-step exchange,
+// which then keeps each workgroup's W2 rows in registers.
 constexpr int kScreenMaxGamma = 8;   // U and G of every step stay in registers during the screen
-constexpr int kR1 = 3;               // round-1 words per step: best key, |U|+|G| bound, hidden partial
-constexpr int kR2 = 3;               // round-2 words per step: listed rows
+constexpr int kScreenStep = 6;       // words per step: 3 entries, cutoff, |U|+|G| bound, hidden partial
+constexpr int kScreenEntries = 3;
 constexpr int kScreenWaves = kChainWaves / 2;  // row workgroups: waves that screen; the others take the norms
 constexpr int kScreenLanes = 64 * kScreenWaves;
 constexpr int kScreenRows = 3;       // rows per screening lane
@@ -363,15 +363,17 @@ constexpr int kSampleRows = kChainThreads / kChainLanesPerRow;  // W2 rows sampl
 constexpr int kLidBits = 10;         // row index inside a workgroup (rows_per_wg <= 640)
 constexpr uint32_t kLidMask = (1u << kLidBits) - 1;
 constexpr uint64_t kEmptyEntry = 1ull << 31;         // no row (low word above any row id + 1)
-constexpr uint64_t kOverflowEntry = (1ull << 31) | 1;  // more rows inside the window than listed
 constexpr uint64_t kTag = 1ull << 32;                // marks a written scalar word
 constexpr uint64_t kDecideDone = 1ull << 63;
 constexpr uint64_t kDecideResume = 1ull << 62;       // | step << 32 | previous token
-constexpr size_t kDecisionOffset = 128;              // bytes into the header
-constexpr size_t kWindowOffset = 160;                // bytes into the header: one word per step
+// Words that every row workgroup polls (the decision, and the go-ahead for
+// its W2 stream) are replicated, one 128-byte line per copy, so the polls
+// spread over memory channels; workgroup g reads copy g % kCopies.
+constexpr int kCopies = 16;
+constexpr int kAuxGo = kCopies * kSlotWords;
+constexpr int kAuxWords = 2 * kCopies * kSlotWords;
 constexpr float kN2Guess = 1.5f;                     // sampled squared norm -> guess of the largest
-static_assert((kR1 + kR2) * kScreenMaxGamma + 1 <= kRegionWords, "screen region too small");
-static_assert(kWindowOffset + 8 * kScreenMaxGamma <= kChainHeader, "window words outside the header");
+static_assert(kScreenStep * kScreenMaxGamma + 1 <= kRegionWords, "screen region too small");
 static_assert(kCandMax % kChainWaves == 0, "candidates per wave");
 static_assert(kChainMaxSlots * kChainGroups <= (1 << kLidBits), "row index field too small");
 static_assert(kChainMaxSlots * kChainGroups <= kScreenRows * kScreenLanes, "screening lanes cover the rows");
@@ -411,9 +413,12 @@ __device__ __forceinline__ float wave_max_f32(float v) {
                                            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48))));
 }
 
-// Lower end of t over a 32-bit ranking key's bucket; key 0 (no row) is -infinity.
+// Ends of t over a 32-bit ranking key's bucket; key 0 (no row) is -infinity.
 __device__ __forceinline__ double key_lower(uint32_t q) {
     return q == 0 ? -__builtin_inf() : (double)from_orderable(q & ~kLidMask);
+}
+__device__ __forceinline__ double key_upper(uint32_t q) {
+    return q == 0 ? -__builtin_inf() : (double)from_orderable(q | kLidMask);
 }
 // Non-negative float bits with NaN and overflow mapped to +infinity, so an
 // unsigned max over them is a float max that cannot lose a NaN.
@@ -458,10 +463,9 @@ struct ScreenLds {
     float fsum[kRegionWords];
     float pk[kScreenMaxGamma];
     float winf[kScreenMaxGamma];
-    uint32_t m1[kScreenMaxGamma], a1[kScreenMaxGamma];  // row workgroup: round-1 maxima
-    int cnt[kScreenMaxGamma];
+    uint32_t wtop[kScreenMaxGamma][kScreenWaves][4];  // row workgroup: each wave's best keys
+    uint32_t a1[kScreenMaxGamma];
     int sync;                                        // arrivals of the screening waves
-    uint64_t lst[kScreenMaxGamma][kR2];
     int32_t fv[kScreenMaxGamma];
     int overflow[kScreenMaxGamma];
     uint32_t n2, n2s;
@@ -517,7 +521,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
     const bf16_t* __restrict__ w_conf, float b_conf, const int32_t* __restrict__ x0, const float* __restrict__ G,
     const int32_t* __restrict__ force, int32_t* __restrict__ tokens, float* __restrict__ conf,
     float* __restrict__ survival, float* __restrict__ logits_out, float* __restrict__ bias_out, uint64_t* slots,
-    uint64_t* regions, uint32_t* header) {
+    uint64_t* regions, uint64_t* aux, uint32_t* header) {
     __shared__ uint64_t red[kChainWaves];
     __shared__ float fred[kChainWaves];
     __shared__ uint32_t we_lds[kChainRank / 2];  // Markov part of the confidence weights (workgroup 0)
@@ -534,10 +538,10 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
     const int64_t h_per = (H + nwg - 1) / nwg;  // hidden elements of this workgroup's confidence partial
     const int64_t h_lo = (int64_t)g * h_per < H ? (int64_t)g * h_per : H;
     const int64_t h_hi = h_lo + h_per < H ? h_lo + h_per : H;
-    uint64_t* decision = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(header) + kDecisionOffset);
-    uint64_t* windows = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(header) + kWindowOffset);
-    const int n1 = kR1 * gamma;           // round-1 words
-    const int nwords = n1 + kR2 * gamma + 1;  // then round-2 words, then the largest squared W2 row norm
+    uint64_t* const dcopy = aux + (g % kCopies) * kSlotWords;           // this workgroup's decision copy
+    uint64_t* const gcopy = aux + kAuxGo + (g % kCopies) * kSlotWords;  // and go-ahead copy
+    const int nlist = kScreenStep * gamma;  // list words
+    const int nwords = nlist + 1;           // then the largest squared W2 row norm
     uint64_t* myregion = regions + (int64_t)g * kRegionWords;
 
     const int64_t xa = x0[0];
@@ -602,8 +606,10 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 if (lane == 0) sc.esq[kERowAnchor] = es;
             }
 
-            // round 1: wave w polls row workgroups 1 + w + 8 i, lane j reads
+            // the lists: wave w polls row workgroups 1 + w + 8 i, lane j reads
             // word j; the spin only checks that every word is written
+            const int type = lane < nlist ? lane % kScreenStep : 7;  // 0-2 entries, 3 cutoff, 4 bound, 5 partial
+            const int kk = lane / kScreenStep;
             uint64_t word[kPollRegions];
             bool ready = false;
             for (int spin = 0; spin < kChainSpinLimit && !ready; ++spin) {
@@ -611,7 +617,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
 #pragma unroll
                 for (int i = 0; i < kPollRegions; ++i) {
                     const int gg = 1 + wave + kChainWaves * i;
-                    const bool use = gg < nwg && lane < n1;
+                    const bool use = gg < nwg && lane < nlist;
                     word[i] = __hip_atomic_load(regions + (use ? (int64_t)gg * kRegionWords + lane : 0),
                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     all = all && (!use || word[i] != 0);
@@ -621,20 +627,24 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             }
             if (!ready && lane == 0) sc.abort = 1;
             {
-                const int type = lane % kR1;  // 0: best key, 1: |U|+|G| bound, 2: hidden partial
                 uint32_t mx = 0;
                 float sm = 0.f;
 #pragma unroll
                 for (int i = 0; i < kPollRegions; ++i) {
                     const bool in = 1 + wave + kChainWaves * i < nwg;
-                    const uint32_t v32 = (uint32_t)word[i];
-                    mx = (in && type < 2) ? max(mx, v32) : mx;
-                    sm += (in && type == 2) ? __uint_as_float(v32) : 0.f;
+                    const uint64_t w = word[i];
+                    const uint32_t v32 = type == 0 ? (uint32_t)(w >> 32) : (uint32_t)w;
+                    mx = (in && (type == 0 || type == 3 || type == 4)) ? max(mx, v32) : mx;
+                    sm += (in && type == 5) ? __uint_as_float(v32) : 0.f;
                 }
                 sc.smax[wave][lane] = mx;
                 sc.ssum[wave][lane] = sm;
             }
             __syncthreads();
+            // every list is in: the row workgroups may start their W2 streams
+            if (tid < kCopies)
+                __hip_atomic_store(aux + kAuxGo + tid * kSlotWords, (uint64_t)1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
             if (wave == 0) {
                 uint32_t m = 0;
                 float sm = 0.f;
@@ -651,50 +661,26 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 const float bg = __builtin_sqrtf(__uint_as_float(sc.n2s) * kN2Guess) * 2.f *
                                      __builtin_sqrtf(sc.esq[kERowAnchor]) * kBetaSlack +
                                  kBetaFloor;
-                const float a = __uint_as_float(sc.fmax[kR1 * tid + 1]);
+                const float a = __uint_as_float(sc.fmax[kScreenStep * tid + 4]);
                 const float eg = 5.f * kUlp * (a + bg);
-                const float wf = float_down(key_lower(sc.fmax[kR1 * tid]) - 2.0 * ((double)bg + eg));
-                sc.winf[tid] = wf;
-                __hip_atomic_store(windows + tid, kTag | __float_as_uint(wf), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                sc.winf[tid] = float_down(key_lower(sc.fmax[kScreenStep * tid]) - 2.0 * ((double)bg + eg));
             }
-
-            // round 2: the listed rows
-            ready = false;
-            for (int spin = 0; spin < kChainSpinLimit && !ready; ++spin) {
-                bool all = true;
-#pragma unroll
-                for (int i = 0; i < kPollRegions; ++i) {
-                    const int gg = 1 + wave + kChainWaves * i;
-                    const bool use = gg < nwg && lane < kR2 * gamma;
-                    word[i] = __hip_atomic_load(regions + (use ? (int64_t)gg * kRegionWords + n1 + lane : 0),
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    all = all && (!use || word[i] != 0);
-                }
-                ready = __all(all);
-                if (!ready) __builtin_amdgcn_s_sleep(1);
-            }
-            if (!ready && lane == 0) sc.abort = 1;
-            if (lane < kR2 * gamma) {
-                const int k = lane / kR2;
+            __syncthreads();
+            // the entries inside the windows, straight from the polled words
+            if (type < kScreenEntries) {
+                const double wk = sc.winf[kk];
 #pragma unroll
                 for (int i = 0; i < kPollRegions; ++i) {
                     if (1 + wave + kChainWaves * i >= nwg) continue;
                     const uint64_t w = word[i];
-                    const uint32_t id1 = (uint32_t)w;  // row id + 1, or a marker
-                    if (w == kOverflowEntry) {
-                        sc.overflow[k] = 1;
-                    } else if (id1 >= 1 && id1 <= (uint64_t)V) {
-                        const int idx = atomicAdd(&sc.ncand, 1);
-                        if (idx < kCandMax) sc.cv[idx] = id1 - 1, sc.cstep[idx] = k;
-                        else sc.overflow[k] = 1;
-                    }
+                    const uint32_t id1 = (uint32_t)w;  // row id + 1, or the empty marker
+                    if (id1 < 1 || id1 > (uint64_t)V || key_upper((uint32_t)(w >> 32)) < wk) continue;
+                    const int idx = atomicAdd(&sc.ncand, 1);
+                    if (idx < kCandMax) sc.cv[idx] = id1 - 1, sc.cstep[idx] = kk;
+                    else sc.overflow[kk] = 1;
                 }
             }
             __syncthreads();
-            // every row workgroup has read the windows
-            if (tid < gamma)
-                __hip_atomic_store(windows + tid, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const bool abort = sc.abort != 0;
             const int nc = sc.ncand < kCandMax ? sc.ncand : kCandMax;
 
@@ -769,9 +755,15 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                     }
                 }
             }
-            // the largest squared W2 row norm, one workgroup per thread
-            if (!abort && tid + 1 < nwg) {
-                const uint64_t* p = regions + (int64_t)(tid + 1) * kRegionWords + nwords - 1;
+            // The walk, in wave 0 (lane j holds candidate j, lane r e row r,
+            // lane k the per-step quantities).  It first runs with the
+            // guessed largest row norm while waves 4-7 collect the real one;
+            // a guess at least as large makes the candidate sets supersets of
+            // the exact ones, inside the windows, so the result stands when
+            // the real norm is no larger.  Otherwise it runs again.
+            const int np = tid - kChainThreads / 2;  // norm poller index
+            if (!abort && np >= 0 && np + 1 < nwg) {
+                const uint64_t* p = regions + (int64_t)(np + 1) * kRegionWords + nwords - 1;
                 uint64_t w = 0;
                 for (int spin = 0; spin < kChainSpinLimit && w == 0; ++spin) {
                     w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -780,10 +772,13 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 if (w == 0) sc.abort = 1;
                 atomicMax(&sc.n2, (uint32_t)w);
             }
-            __syncthreads();
-
-            // the walk, in wave 0: lane j holds candidate j, lane r e row r,
-            // lane k the per-step quantities
+            struct Walk {
+                int k, pst;
+                int32_t tk;
+                int64_t x;
+                bool valid, fail;
+            };
+            Walk wk{};
             if (wave == 0) {
                 const bool mine = lane < nc;
                 const int cs = mine ? sc.cstep[lane] : -1;
@@ -791,7 +786,8 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 const uint32_t cv = mine ? sc.cv[lane] : 0u;
                 const float l_esq = lane < kERows ? sc.esq[lane] : 0.f;
                 const int ks = lane < kScreenMaxGamma ? lane : 0;
-                const uint32_t l_ab = sc.fmax[kR1 * ks + 1];
+                const uint32_t l_ab = sc.fmax[kScreenStep * ks + 4];
+                const uint32_t l_cut = sc.fmax[kScreenStep * ks + 3];
                 const float l_win = sc.winf[ks];
                 const int l_ovf = sc.overflow[ks];
                 const int32_t l_fv = sc.fv[ks];
@@ -801,49 +797,73 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                     const float m = wave_max_f32(cs == k ? ct : -__builtin_inff());
                     if (lane == k) l_tmax = m;
                 }
-                const uint32_t n2b = sc.n2;  // largest squared W2 row norm
-                const float n2 = __builtin_sqrtf(__uint_as_float(n2b));
-                int cur = kERowAnchor;  // e row of the current step
-                int pst = 0;            // e row used at this lane's step (lane k)
-                int32_t tk = -1;        // token of this lane's step (lane k)
-                int k = 0;
-                bool fail = sc.abort != 0;
-                for (; k < gamma && !fail; ++k) {
-                    if (!valid) continue;
-                    const float es = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_esq), cur));
-                    const uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)l_ab, k);
-                    const float tmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_tmax), k));
-                    const float win = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_win), k));
-                    const float beta = n2 * __builtin_sqrtf(es) * kBetaSlack + kBetaFloor;
-                    const float eps = 5.f * kUlp * (__uint_as_float(ab) + beta);
-                    const double thr = (double)tmax - 2.0 * ((double)beta + eps);
-                    const bool ok = __builtin_amdgcn_readlane(l_ovf, k) == 0 && finite_bits(ab) && finite_bits(n2b) &&
-                                    finite_bits(bound_bits(es)) && tmax > -__builtin_inff() && thr >= (double)win;
-                    if (!ok) {
-                        fail = true;
-                        break;
+                const auto walk = [&](uint32_t n2b) {
+                    Walk r{0, 0, -1, xa, true, abort};
+                    const float n2 = __builtin_sqrtf(__uint_as_float(n2b));
+                    int cur = kERowAnchor;  // e row of the current step
+                    for (; r.k < gamma && !r.fail; ++r.k) {
+                        const int k = r.k;
+                        if (!r.valid) continue;
+                        const float es = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_esq), cur));
+                        const uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)l_ab, k);
+                        const float tmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_tmax), k));
+                        const float win = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_win), k));
+                        const float beta = n2 * __builtin_sqrtf(es) * kBetaSlack + kBetaFloor;
+                        const float eps = 5.f * kUlp * (__uint_as_float(ab) + beta);
+                        const double thr = (double)tmax - 2.0 * ((double)beta + eps);
+                        const uint32_t cut = (uint32_t)__builtin_amdgcn_readlane((int)l_cut, k);
+                        const bool ok = __builtin_amdgcn_readlane(l_ovf, k) == 0 && finite_bits(ab) &&
+                                        finite_bits(n2b) && finite_bits(bound_bits(es)) &&
+                                        tmax > -__builtin_inff() && thr >= (double)win && key_upper(cut) < thr;
+                        if (!ok) {
+                            r.fail = true;
+                            break;
+                        }
+                        const bool cand = cs == k && (double)ct >= thr;
+                        const float lg = cu + (cand ? sc.bias[lane & (kCandMax - 1)][cur] : 0.f);
+                        const uint64_t key = cand ? argmax_key(G ? lg + cg : lg, cv) : 0;
+                        const uint64_t best = wave_max_u64(key);
+                        if (best == 0) {  // cannot happen: the best listed row is always a candidate
+                            r.fail = true;
+                            break;
+                        }
+                        const int jw = __builtin_ctzll(__ballot(key == best && cand));
+                        const int32_t tok = key_token(best);
+                        if (lane == k) r.pst = cur, r.tk = tok;
+                        const int32_t f = __builtin_amdgcn_readlane(l_fv, k);
+                        r.x = f >= 0 ? f : tok;
+                        r.valid = r.x >= 0 && r.x < V;
+                        cur = f >= 0 ? kERowForced + k : jw;
                     }
-                    const bool cand = cs == k && (double)ct >= thr;
-                    const float lg = cu + (cand ? sc.bias[lane & (kCandMax - 1)][cur] : 0.f);
-                    const uint64_t key = cand ? argmax_key(G ? lg + cg : lg, cv) : 0;
-                    const uint64_t best = wave_max_u64(key);
-                    if (best == 0) {  // cannot happen: the best listed row is always a candidate
-                        fail = true;
-                        break;
-                    }
-                    const int jw = __builtin_ctzll(__ballot(key == best && cand));
-                    const int32_t tok = key_token(best);
-                    if (lane == k) pst = cur, tk = tok;
-                    const int32_t f = __builtin_amdgcn_readlane(l_fv, k);
-                    x = f >= 0 ? f : tok;
-                    valid = x >= 0 && x < V;
-                    cur = f >= 0 ? kERowForced + k : jw;
-                }
+                    return r;
+                };
+                const float guess = __uint_as_float(sc.n2s) * kN2Guess;
+                wk = walk(bound_bits(guess));
+                // the real norm: waves 4-7 post it before the barrier below
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+                const uint32_t n2b = sc.n2;
+                if (sc.abort || !(__uint_as_float(n2b) <= guess)) wk = walk(n2b);
+            } else {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                __builtin_amdgcn_s_barrier();
+            }
+            // every row workgroup has posted its norm, so all have read the go-ahead
+            if (tid >= kChainThreads - kCopies)
+                __hip_atomic_store(aux + kAuxGo + (tid - (kChainThreads - kCopies)) * kSlotWords, (uint64_t)0,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (wave == 0) {
+                const int k = wk.k;
+                const bool fail = wk.fail;
+                const int pst = wk.pst;
+                const int32_t tk = wk.tk;
+                x = wk.x;
+                valid = wk.valid;
                 // confidences of the settled steps in parallel, then the running product
                 const int settled = k;
                 float c = 0.f;
                 if (lane < settled && tk >= 0)
-                    c = 1.f / (1.f + expf(-(sc.pk[lane] + sc.fsum[kR1 * lane + 2] + sc.zcm[pst] + b_conf)));
+                    c = 1.f / (1.f + expf(-(sc.pk[lane] + sc.fsum[kScreenStep * lane + 5] + sc.zcm[pst] + b_conf)));
                 if (lane < settled) tokens[lane] = tk;
                 float surv = 1.f;
                 bool alive = true;
@@ -862,13 +882,12 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                     for (int j = lane; j < gamma; j += 64)
                         tokens[j] = -1, conf[j] = __builtin_nanf(""), survival[j] = __builtin_nanf("");
                 }
-                if (lane == 0) {
-                    const uint64_t d = (fail && !sc.abort)
-                                           ? (kDecideResume | ((uint64_t)k << 32) | (uint64_t)(uint32_t)x)
-                                           : kDecideDone;
-                    sc.decision = d;
-                    __hip_atomic_store(decision, d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
+                const uint64_t d = (fail && !sc.abort)
+                                       ? (kDecideResume | ((uint64_t)k << 32) | (uint64_t)(uint32_t)x)
+                                       : kDecideDone;
+                if (lane == 0) sc.decision = d;
+                if (lane < kCopies)
+                    __hip_atomic_store(aux + lane * kSlotWords, d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             __syncthreads();
             const uint64_t d = sc.decision;
@@ -883,7 +902,8 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                     }
                 }
                 __syncthreads();
-                if (tid == 0) __hip_atomic_store(decision, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (tid < kCopies)
+                    __hip_atomic_store(aux + tid * kSlotWords, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 done = true;
             } else {
                 k0 = (int)((d >> 32) & 0xffff);
@@ -892,7 +912,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             }
         }
     } else if (scr) {
-        if (tid < kScreenMaxGamma) sc.m1[tid] = 0, sc.a1[tid] = 0, sc.cnt[tid] = 0;
+        if (tid < kScreenMaxGamma) sc.a1[tid] = 0;
         if (tid == 0) sc.sync = 0;
         __syncthreads();
         if (wave < kScreenWaves) {
@@ -917,69 +937,68 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                     ur[k][m] = U[o].bits;
                     gs[k][m] = G ? G[o] : 0.f;
                 }
-            // round 1: the workgroup's best ranking key and |U|+|G| bound per step
+            // each wave's four best ranking keys and |U|+|G| bound per step
 #pragma unroll
             for (int k = 0; k < kScreenMaxGamma; ++k) {
                 if (k >= gamma) break;
-                uint32_t best = 0, am = 0;
+                uint32_t q[kScreenRows];  // this lane's keys, best first
+                uint32_t am = 0;
 #pragma unroll
                 for (int m = 0; m < kScreenRows; ++m) {
-                    if (!sok[m]) continue;
                     const float u = __uint_as_float((uint32_t)ur[k][m] << 16);
-                    am = max(am, bound_bits(__builtin_fabsf(u) + __builtin_fabsf(gs[k][m])));
-                    best = max(best, ranking_key(G ? u + gs[k][m] : u, (uint32_t)(sv[m] - row0)));
+                    am = sok[m] ? max(am, bound_bits(__builtin_fabsf(u) + __builtin_fabsf(gs[k][m]))) : am;
+                    q[m] = sok[m] ? ranking_key(G ? u + gs[k][m] : u, (uint32_t)(sv[m] - row0)) : 0u;
                 }
-                best = wave_max_u32(best);
+#pragma unroll
+                for (int i = 0; i < kScreenRows; ++i)  // sort descending
+#pragma unroll
+                    for (int j = kScreenRows - 1; j > i; --j) {
+                        const uint32_t hi = max(q[j - 1], q[j]), lo = min(q[j - 1], q[j]);
+                        q[j - 1] = hi, q[j] = lo;
+                    }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t mr = wave_max_u32(q[0]);
+                    if (q[0] == mr) {
+#pragma unroll
+                        for (int m = 0; m + 1 < kScreenRows; ++m) q[m] = q[m + 1];
+                        q[kScreenRows - 1] = 0;
+                    }
+                    if (lane == 0) sc.wtop[k][wave][r] = mr;
+                }
                 am = wave_max_u32(am);
-                if (lane == 0) atomicMax(&sc.m1[k], best), atomicMax(&sc.a1[k], am);
+                if (lane == 0) atomicMax(&sc.a1[k], am);
             }
             screen_sync(sc, lane, kScreenWaves);
-            if (tid < gamma) {
+            // wave w merges steps w, w + 4 and publishes their six words each
+#pragma unroll
+            for (int k = wave; k < kScreenMaxGamma; k += kScreenWaves) {
+                if (k >= gamma) break;
+                uint32_t c = lane < 4 * kScreenWaves ? sc.wtop[k][lane >> 2][lane & 3] : 0u;
+                uint32_t t4[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    t4[r] = wave_max_u32(c);
+                    if (c == t4[r]) c = 0;
+                }
                 float ps = 0.f;
 #pragma unroll
-                for (int w = 0; w < kScreenWaves; ++w) ps += sc.pw[tid][w];
-                __hip_atomic_store(myregion + kR1 * tid, kTag | sc.m1[tid], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(myregion + kR1 * tid + 1, kTag | sc.a1[tid], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(myregion + kR1 * tid + 2, kTag | __float_as_uint(ps), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                // round 2: the windows
-                uint64_t w = 0;
-                for (int spin = 0; spin < kChainSpinLimit && w == 0; ++spin) {
-                    w = __hip_atomic_load(windows + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if (w == 0) __builtin_amdgcn_s_sleep(1);
-                }
-                // no window in time: list nothing and flag the step
-                sc.winf[tid] = w ? __uint_as_float((uint32_t)w) : __builtin_nanf("");
-                if (w == 0) sc.cnt[tid] = kR2 + 1;
+                for (int w = 0; w < kScreenWaves; ++w) ps += sc.pw[k][w];
+                const uint32_t te = lane == 0 ? t4[0] : lane == 1 ? t4[1] : t4[2];
+                uint64_t word;
+                if (lane < kScreenEntries)
+                    word = te ? (((uint64_t)te << 32) | (uint64_t)(row0 + (te & kLidMask) + 1)) : kEmptyEntry;
+                else if (lane == 3)
+                    word = kTag | t4[3];
+                else if (lane == 4)
+                    word = kTag | sc.a1[k];
+                else
+                    word = kTag | __float_as_uint(ps);
+                if (lane < kScreenStep)
+                    __hip_atomic_store(myregion + kScreenStep * k + lane, word, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             }
             screen_sync(sc, lane, 2 * kScreenWaves);
-            // every screening lane lists its rows inside the windows
-#pragma unroll
-            for (int k = 0; k < kScreenMaxGamma; ++k) {
-                if (k >= gamma) break;
-                const float wk = sc.winf[k];
-#pragma unroll
-                for (int m = 0; m < kScreenRows; ++m) {
-                    const float u = __uint_as_float((uint32_t)ur[k][m] << 16);
-                    const float t = G ? u + gs[k][m] : u;
-                    if (sok[m] && t >= wk) {
-                        const int idx = atomicAdd(&sc.cnt[k], 1);
-                        if (idx < kR2)
-                            sc.lst[k][idx] = ((uint64_t)ranking_key(t, (uint32_t)(sv[m] - row0)) << 32) |
-                                             (uint64_t)(sv[m] + 1);
-                    }
-                }
-            }
-            screen_sync(sc, lane, 3 * kScreenWaves);
-            if (tid < kR2 * gamma) {
-                const int k = tid / kR2, e = tid % kR2;
-                const int c = sc.cnt[k];
-                const uint64_t w =
-                    (c > kR2 && e == kR2 - 1) ? kOverflowEntry : e < c ? sc.lst[k][e] : kEmptyEntry;
-                __hip_atomic_store(myregion + n1 + tid, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
         } else {
             // Norm waves: the W2 slice streams through a window of slots for
             // the largest squared row norm.  Rows past the slice load row 0
@@ -987,6 +1006,13 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             // overwrites).
             const int ng = (tid - kScreenLanes) >> 3;
             constexpr int NS = (NSLOT * kChainGroups + kNormGroups - 1) / kNormGroups;
+            // Hold the stream back until workgroup 0 has every list: behind a
+            // full HBM queue every cross-workgroup message waits several
+            // microseconds.
+            for (int spin = 0; spin < kChainSpinLimit; ++spin) {
+                if (__hip_atomic_load(gcopy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
             uint32_t buf[kStreamSlots][16];
 #pragma unroll
             for (int i = 0; i < kStreamSlots; ++i) {
@@ -1021,7 +1047,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             // wait for the coordinator's decision
             uint64_t d = 0;
             for (int spin = 0; spin < kChainSpinLimit && d == 0; ++spin) {
-                d = __hip_atomic_load(decision, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                d = __hip_atomic_load(dcopy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (d == 0) __builtin_amdgcn_s_sleep(2);
             }
             sc.decision = d;
@@ -1192,7 +1218,8 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             __hip_atomic_store(&slots[i * kSlotWords + 1], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if (tid == 0) {
-            __hip_atomic_store(decision, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int c = 0; c < kCopies; ++c)
+                __hip_atomic_store(aux + c * kSlotWords, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&header[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
@@ -1252,7 +1279,8 @@ ChainPlan chain_plan(int64_t V, int64_t H) {
 }
 
 size_t chain_workspace(int64_t gamma) {
-    return kChainHeader + (size_t)8 * kSlotWords * gamma * kChainMaxWGs + (size_t)8 * kRegionWords * kChainMaxWGs;
+    return kChainHeader + (size_t)8 * kSlotWords * gamma * kChainMaxWGs + (size_t)8 * kRegionWords * kChainMaxWGs +
+           (size_t)8 * kAuxWords;
 }
 
 hipError_t launch_chain(const ChainPlan& p, int64_t gamma, int64_t V, int64_t H, const void* U, const void* h,
@@ -1272,8 +1300,9 @@ hipError_t launch_chain(const ChainPlan& p, int64_t gamma, int64_t V, int64_t H,
     uint32_t* header = static_cast<uint32_t*>(ws);
     uint64_t* slots = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kChainHeader);
     uint64_t* regions = slots + (size_t)kSlotWords * gamma * kChainMaxWGs;
+    uint64_t* aux = regions + (size_t)kRegionWords * kChainMaxWGs;
     void* args[] = {&g,  &Vv, &Hh,    &rows,   &screen, &Ut,       &ht, &W1t, &W2t,  &wt,      &b_conf,
-                    &x0, &G,  &force, &tokens, &conf,   &survival, &lo, &bo,  &slots, &regions, &header};
+                    &x0, &G,  &force, &tokens, &conf,   &survival, &lo, &bo,  &slots, &regions, &aux, &header};
     const void* fn = chain_fn(p.nslot);
     // A plain launch: every workgroup needs a whole CU (its register file) and
     // the grid has at most one workgroup per CU, so on an otherwise idle GPU

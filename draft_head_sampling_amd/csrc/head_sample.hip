@@ -242,6 +242,12 @@ __global__ __launch_bounds__(64 * kFinishMaxGamma) void sample_finish(
         }
         __syncthreads();
     }
+    // this request's keys and hidden dots are read: the workspace goes back to zero
+    uint64_t* kw = const_cast<uint64_t*>(keys);
+    float* hw = const_cast<float*>(hdot);
+    for (int64_t i = threadIdx.x; i < (int64_t)ncopy * gamma; i += blockDim.x)
+        kw[(((i / gamma) * gamma + i % gamma) * B + b) * kKeyStride] = 0;
+    for (int64_t i = threadIdx.x; i < gamma; i += blockDim.x) hw[b * gamma + i] = 0.f;
 }
 
 
@@ -1522,6 +1528,307 @@ __global__ __launch_bounds__(256) void sample_step_mfma(int64_t B, int64_t gamma
     }
 }
 
+// ---------------------------------------------------------------------------
+// Batched sampler with W2 resident on the matrix cores (bf16, rank 256,
+// 16..64 requests).
+//
+// One persistent workgroup per CU, eight waves.  Workgroup g owns a
+// contiguous range of up to 20 32-row vocabulary tiles of W2 for the whole
+// block: wave w holds tiles t0 + w and t0 + w + 8 in registers as
+// v_mfma_f32_32x32x16_bf16 A fragments, and tiles t0 + 16 .. t0 + 19 sit in
+// LDS (rows padded against bank conflicts), one per wave 0..3.  W2 crosses
+// HBM once per call and a step streams only U (and G).
+// Step k: gather E = W1[x_{k-1}] of every request into LDS (the B operand),
+// multiply each held tile by it, fuse + U (+ G) and the argmax in the
+// accumulator layout (one request per lane, 16 rows in-lane), reduce over
+// the waves, and publish one packed key per request.  Workgroup r < B
+// reduces request r over all workgroups and posts the winner in 8 copies of
+// the 64-word winner array; workgroup g reads copy g % 8 for step k + 1.  Workgroup 0 computes the
+// confidence and the running survival of every request per step.  Every
+// exchanged word is self-validating (never zero when written) and is
+// cleared one step later by its writer, when all its readers are provably
+// past it; the last step's words go to the last workgroup out.
+// ---------------------------------------------------------------------------
+constexpr int kResRegTiles = 2;  // 32-row W2 tiles held in registers per wave
+constexpr int kResWaves = 8;
+constexpr int kResLdsTiles = 4;  // more tiles per workgroup held in LDS
+constexpr int kResThreads = 64 * kResWaves;
+constexpr int kResMaxTiles = kResWaves * kResRegTiles + kResLdsTiles;
+constexpr int kResMaxReq = 64;
+constexpr int kResCopies = 8;   // copies of the winner words
+constexpr int kResMaxWGs = 256;
+constexpr size_t kResHeader = 256;  // exit counter
+
+__device__ __forceinline__ int32_t winner_token(uint64_t key) {  // 0 or 1: no candidate
+    return key <= 1 ? -1 : key_token(key);
+}
+
+template <int NT>
+__global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, int gamma, int64_t V, int tiles_per_wg, const bf16_t* __restrict__ U,
+                      const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W2,
+                      const bf16_t* __restrict__ w_conf, int64_t H, float b_conf, const int32_t* __restrict__ x0,
+                      const float* __restrict__ G, const int32_t* __restrict__ force, int32_t* __restrict__ tokens,
+                      float* __restrict__ conf, float* __restrict__ survival, float* __restrict__ logits_out,
+                      float* __restrict__ bias_out, const float* __restrict__ hdot, uint64_t* pub, uint64_t* win,
+                      uint32_t* header) {
+    constexpr int NREQ = 32 * NT;
+    __shared__ __align__(16) uint16_t E_lds[NREQ * kERow];
+    __shared__ __align__(16) uint16_t T_lds[kResLdsTiles * 32 * kERow];  // W2 tiles held in LDS
+    __shared__ uint64_t wkey[kResWaves][NREQ];
+    __shared__ uint64_t rkey[kResWaves];
+    __shared__ int32_t xprev[NREQ];
+    __shared__ uint32_t we_lds[kMfmaRank / 2];  // Markov part of the confidence weights (workgroup 0)
+    __shared__ int last_flag;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 31, half = lane >> 5;
+    const int g = blockIdx.x, nwg = gridDim.x;
+    const int64_t ntiles = (V + 31) / 32;
+    const int64_t t0 = (int64_t)g * tiles_per_wg;
+    const int64_t t_end = t0 + tiles_per_wg < ntiles ? t0 + tiles_per_wg : ntiles;
+    const uint64_t* wcopy = win + (int64_t)(g % kResCopies) * kResMaxReq;  // step stride kResCopies * 64
+
+    // this wave's W2 tiles, as A fragments: k-step s holds rank elements
+    // 16 s + 8 half .. +7 of row 32 t + row
+    uint4 a[kResRegTiles][16];
+#pragma unroll
+    for (int i = 0; i < kResRegTiles; ++i) {
+        const int64_t t = t0 + wave + kResWaves * i;
+        int64_t v = t * 32 + row;
+        v = (t < t_end && v < V) ? v : 0;  // clamped; its products are never used
+        const uint4* src = reinterpret_cast<const uint4*>(W2 + v * kMfmaRank + half * 8);
+#pragma unroll
+        for (int s = 0; s < 16; ++s) a[i][s] = src[2 * s];
+    }
+    // the LDS tiles: 16 bytes per thread per pass, 4 passes cover 4 x 32 rows
+#pragma unroll
+    for (int pss = 0; pss < kResLdsTiles * 32 * 32 / kResThreads; ++pss) {
+        const int c = tid + kResThreads * pss;  // 16-byte chunk: row c / 32 of the 128, column (c % 32) * 8
+        const int lr = c / 32, col = (c % 32) * 8;
+        const int64_t t = t0 + kResWaves * kResRegTiles + lr / 32;
+        int64_t v = t * 32 + lr % 32;
+        v = (t < t_end && v < V) ? v : 0;
+        *reinterpret_cast<uint4*>(T_lds + lr * kERow + col) =
+            *reinterpret_cast<const uint4*>(W2 + v * kMfmaRank + col);
+    }
+
+    if (g == 0 && tid < kMfmaRank / 2)
+        we_lds[tid] = (uint32_t)w_conf[H + 2 * tid].bits | ((uint32_t)w_conf[H + 2 * tid + 1].bits << 16);
+    float A = 1.f;  // workgroup 0, thread 4 b: running survival of request b
+    for (int k = 0; k < gamma; ++k) {
+        // previous tokens: the anchors, then the winners of the last step
+        if (tid < NREQ) {
+            int64_t x = -1;
+            if (tid < B) {
+                if (k == 0) {
+                    x = x0[tid];
+                } else {
+                    const uint64_t* p = wcopy + (int64_t)(k - 1) * kResCopies * kResMaxReq + tid;
+                    uint64_t w = 0;
+                    for (int spin = 0; spin < kChainSpinLimit && w == 0; ++spin) {
+                        w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (w == 0) __builtin_amdgcn_s_sleep(1);
+                    }
+                    if (w == 0 && g == 0) header[1] = 1u;  // timed out: reported as token -1
+                    const int32_t tok = winner_token(w);
+                    const int32_t f = (force && tok >= 0) ? force[tid * gamma + k - 1] : -1;
+                    x = tok < 0 ? -1 : (f >= 0 ? f : tok);
+                }
+            }
+            xprev[tid] = (x >= 0 && x < V) ? (int32_t)x : -1;
+            // every reducer has read this workgroup's keys of the last step
+            if (k > 0 && tid < B)
+                __hip_atomic_store(pub + ((int64_t)(k - 1) * nwg + g) * kResMaxReq + tid, (uint64_t)0,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        // gather E = W1[x_prev] into LDS: 4 threads per request, 128 bytes each
+        {
+            const int bl = tid >> 2, part = tid & 3;
+            if (bl < NREQ) {
+                const int32_t x = xprev[bl];
+                const uint4* src = reinterpret_cast<const uint4*>(W1 + (int64_t)(x < 0 ? 0 : x) * kMfmaRank + part * 64);
+                uint4 e[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) e[i] = src[i];
+                uint4* dst = reinterpret_cast<uint4*>(E_lds + bl * kERow + part * 64);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) dst[i] = e[i];
+            }
+        }
+        __syncthreads();
+        // workgroup 0: confidence and survival of step k (its Markov part needs e)
+        if (g == 0) {
+            const int bl = tid >> 2, part = tid & 3;
+            if (bl < NREQ) {
+                const uint32_t* er = reinterpret_cast<const uint32_t*>(E_lds + bl * kERow + part * 64);
+                float s = 0.f;
+#pragma unroll 8
+                for (int q = 0; q < 32; ++q) s = dot2(we_lds[part * 32 + q], er[q], s);
+                s += __shfl_xor(s, 1);
+                s += __shfl_xor(s, 2);
+                if (part == 0 && bl < B) {
+                    const bool live = xprev[bl] >= 0;
+                    const float c = 1.f / (1.f + expf(-(hdot[bl * gamma + k] + s + b_conf)));
+                    A = A * c;
+                    conf[bl * gamma + k] = live ? c : __builtin_nanf("");
+                    survival[bl * gamma + k] = live ? A : __builtin_nanf("");
+                }
+            }
+        }
+
+        // the products, the + U (+ G) epilogue and the in-lane argmax
+        uint64_t key[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) key[nt] = 0;
+#pragma unroll
+        for (int i = 0; i < kResRegTiles + 1; ++i) {
+            const bool lds_tile = i == kResRegTiles;
+            if (lds_tile && wave >= kResLdsTiles) continue;  // wave-uniform
+            const int64_t t = lds_tile ? t0 + kResWaves * kResRegTiles + wave : t0 + wave + kResWaves * i;
+            if (t >= t_end) continue;  // wave-uniform
+            // first row of the tile, opaque to the optimiser: the per-row
+            // indices below are cheap to recompute, and hoisting them out of
+            // the step loop spills them
+            int vt = (int)(t * 32);
+            asm volatile("" : "+v"(vt));
+            __builtin_amdgcn_sched_barrier(0);  // one tile's loads in flight at a time: registers are tight
+            // one 32-request tile at a time (registers are tight): U (and G)
+            // first, lane (request nt*32 + row, half h) taking rows
+            // 8 c + 4 h .. +3 for c < 4, then the products, then the epilogue
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int bl = nt * 32 + row;
+                const int64_t base = ((int64_t)(bl < B ? bl : B - 1) * gamma + k) * V;
+                uint2 ur[4];
+                float4 gr[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    int64_t v = vt + 8 * c + 4 * half;
+                    v = v + 4 <= V ? v : V - 4;  // clamped (V is a multiple of 4); masked below
+                    ur[c] = *reinterpret_cast<const uint2*>(U + base + v);
+                    gr[c] = G ? *reinterpret_cast<const float4*>(G + base + v) : float4{0.f, 0.f, 0.f, 0.f};
+                }
+                f32x16_t acc;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+                for (int s = 0; s < 16; ++s) {
+                    const uint4 aw =
+                        lds_tile ? *reinterpret_cast<const uint4*>(T_lds + (wave * 32 + row) * kERow + s * 16 + half * 8)
+                                 : a[i < kResRegTiles ? i : 0][s];
+                    const uint4 bw = *reinterpret_cast<const uint4*>(E_lds + (nt * 32 + row) * kERow + s * 16 + half * 8);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aw),
+                                                                  __builtin_bit_cast(bf16x8_t, bw), acc, 0, 0, 0);
+                }
+                if (bl >= B || xprev[bl] < 0) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int c = r / 4, q = r % 4;
+                    const int64_t v = vt + 8 * c + 4 * half + q;
+                    if (v >= V) continue;
+                    const uint32_t uw = q < 2 ? ur[c].x : ur[c].y;
+                    const float uu = (q & 1) ? widen_hi(uw) : widen_lo(uw);
+                    const float gg = q == 0 ? gr[c].x : q == 1 ? gr[c].y : q == 2 ? gr[c].z : gr[c].w;
+                    const float bias = acc[r];
+                    const float lg = uu + bias;
+                    const float sc = G ? lg + gg : lg;
+                    if (bias_out) bias_out[base + v] = bias;
+                    if (logits_out) logits_out[base + v] = lg;
+                    key[nt] = umax64(key[nt], argmax_key(sc, (uint32_t)v));
+                }
+            }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            key[nt] = umax64(key[nt], shfl_xor_u64(key[nt], 32));
+            if (half == 0) wkey[wave][nt * 32 + row] = key[nt];
+        }
+        __syncthreads();
+        // publish this workgroup's best key per request (1 = no candidate)
+        if (tid < B) {
+            uint64_t m = 0;
+#pragma unroll
+            for (int w = 0; w < kResWaves; ++w) m = umax64(m, wkey[w][tid]);
+            __hip_atomic_store(pub + ((int64_t)k * nwg + g) * kResMaxReq + tid, m ? m : 1ull, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // workgroup g reduces requests g, g + nwg, ... over every workgroup
+        for (int r = g; r < B; r += nwg) {  // workgroup-uniform
+            uint64_t m = 0;
+            if (tid < nwg) {
+                const uint64_t* p = pub + ((int64_t)k * nwg + tid) * kResMaxReq + r;
+                for (int spin = 0; spin < kChainSpinLimit && m == 0; ++spin) {
+                    m = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (m == 0) __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            m = wave_max_u64(m);
+            if (lane == 0) rkey[wave] = m;
+            __syncthreads();
+            uint64_t best = 0;
+#pragma unroll
+            for (int w = 0; w < kResWaves; ++w) best = umax64(best, rkey[w]);
+            if (tid < kResCopies)
+                __hip_atomic_store(win + ((int64_t)k * kResCopies + tid) * kResMaxReq + r, best ? best : 1ull,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (tid == 0) tokens[r * gamma + k] = winner_token(best);
+            // every workgroup has read the winners of the last step: they
+            // published this step's keys after it
+            if (k > 0 && tid >= 64 && tid < 64 + kResCopies)
+                __hip_atomic_store(win + ((int64_t)(k - 1) * kResCopies + (tid - 64)) * kResMaxReq + r, (uint64_t)0,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();  // rkey is reused
+        }
+        __syncthreads();  // wkey and rkey are reused next step
+    }
+
+    // leave: the last workgroup out clears the last step's words
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&header[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = old == (uint32_t)(nwg - 1);
+    }
+    __syncthreads();
+    if (last_flag) {
+        const int64_t k = gamma - 1;
+        for (int64_t i = tid; i < (int64_t)nwg * kResMaxReq; i += kResThreads)
+            __hip_atomic_store(pub + k * nwg * kResMaxReq + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = tid; i < kResCopies * kResMaxReq; i += kResThreads)
+            __hip_atomic_store(win + k * kResCopies * kResMaxReq + i, (uint64_t)0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        for (int64_t i = tid; i < B * gamma; i += kResThreads) const_cast<float*>(hdot)[i] = 0.f;
+        if (tid == 0) __hip_atomic_store(&header[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+struct ResidentPlan {
+    int nwg = 0, tiles_per_wg = 0;
+};
+
+ResidentPlan resident_plan(int64_t B, int64_t V) {
+    ResidentPlan p;
+    const int cus = device_cus();
+    if (cus <= 0 || B < kMfmaMinBatch || B > kResMaxReq || V % 4 != 0) return p;
+    int64_t nwg = cus < kResMaxWGs ? cus : kResMaxWGs;
+    const int64_t ntiles = (V + 31) / 32;
+    if (nwg > ntiles) nwg = ntiles;
+    const int64_t per = (ntiles + nwg - 1) / nwg;
+    if (per > (int64_t)kResMaxTiles) return p;
+    int per_cu = 0;
+    const void* fn = B <= 32 ? reinterpret_cast<const void*>(&sample_batch_resident<1>)
+                             : reinterpret_cast<const void*>(&sample_batch_resident<2>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kResThreads, 0) != hipSuccess || per_cu < 1)
+        return p;
+    p.nwg = (int)nwg;
+    p.tiles_per_wg = (int)per;
+    return p;
+}
+
+size_t resident_workspace(int64_t B, int64_t gamma) {
+    return ((size_t)(4 * B * gamma) + 255) / 256 * 256 + kResHeader +
+           (size_t)8 * gamma * kResMaxWGs * kResMaxReq + (size_t)8 * gamma * kResCopies * kResMaxReq;
+}
+
 struct Buffers {
     uint64_t* keys;
     float* hdot;
@@ -1577,6 +1884,31 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
     bool mfma = false;
     if constexpr (std::is_same_v<T, bf16_t>)
         mfma = r == kMfmaRank && B >= kMfmaMinBatch && ((uintptr_t)W1 % 16 == 0) && ((uintptr_t)W2 % 16 == 0);
+    if constexpr (std::is_same_v<T, bf16_t>) {
+        // resident W2: one persistent kernel for the whole block
+        const ResidentPlan rp = mfma ? resident_plan(B, V) : ResidentPlan{};
+        if (rp.nwg > 0 && (uintptr_t)U % 8 == 0 && (G == nullptr || (uintptr_t)G % 16 == 0)) {
+            char* p = static_cast<char*>(ws);
+            float* hdot = reinterpret_cast<float*>(p);
+            p += ((size_t)(4 * B * gamma) + 255) / 256 * 256;
+            uint32_t* header = reinterpret_cast<uint32_t*>(p);
+            uint64_t* pub = reinterpret_cast<uint64_t*>(p + kResHeader);
+            uint64_t* win = pub + (size_t)gamma * kResMaxWGs * kResMaxReq;
+            hipLaunchKernelGGL((sample_init<T>), dim3((uint32_t)(B * gamma)), dim3(kThreads), 0, stream, B, gamma, H,
+                               static_cast<const T*>(h), wt, (uint64_t*)nullptr, 0, hdot);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            int g = (int)gamma, tpw = rp.tiles_per_wg;
+            int64_t Bb = B, Vv = V, Hh = H;
+            void* args[] = {&Bb,  &g,    &Vv, &tpw,   &Ut,   &W1t,      &W2t, &wt,       &Hh,   &b_conf, &x0,
+                            &G,   &force, &tokens, &conf, &survival, &lo,  &bo,  &hdot, &pub,    &win,  &header};
+            const void* fn = B <= 32 ? reinterpret_cast<const void*>(&sample_batch_resident<1>)
+                                     : reinterpret_cast<const void*>(&sample_batch_resident<2>);
+            // a plain launch: one workgroup per CU at most, all resident together;
+            // the bounded spins turn any other outcome into an error, not a hang
+            return hipLaunchKernel(fn, dim3(rp.nwg), dim3(kResThreads), args, 0, stream);
+        }
+    }
     const int ncopy = mfma ? kKeyCopies : 1;
     Buffers s = carve(ws, B, gamma, ncopy);
 
@@ -1634,6 +1966,10 @@ size_t head_sample_workspace(int64_t B, int64_t gamma, int64_t, int64_t r, int d
     const int64_t ncopy = (dtype == kBF16 && r == kMfmaRank && B >= kMfmaMinBatch) ? kKeyCopies : 1;
     size_t steps = ((size_t)(8 * kKeyStride * ncopy * B * gamma) + 255) / 256 * 256 +
                    ((size_t)(4 * B * gamma) + 255) / 256 * 256;
+    if (dtype == kBF16 && r == kMfmaRank && B >= kMfmaMinBatch && B <= kResMaxReq) {
+        const size_t res = resident_workspace(B, gamma);
+        if (res > steps) steps = res;
+    }
     if (B == 1 && r == kChainRank) {
         const size_t chain = chain_workspace(gamma);
         if (chain > steps) steps = chain;

@@ -199,18 +199,22 @@ def test_batched_gumbel_full_vocabulary_sampled_requests():
 
 
 def test_workspace_reuse_across_shapes():
-    """One zero-filled workspace serves single-request calls of different
-    vocabulary sizes and block widths; each call leaves it zeroed."""
-    cases = [(151936, 7, False), (1000, 3, True), (70001, 9, False), (151936, 7, True)]
-    big = max(dh.head_sample_workspace_size(1, g, V, 64, 256) for V, g, _ in cases)
+    """One zero-filled workspace serves calls of different batch sizes,
+    vocabulary sizes and block widths, on every kernel path (single-request
+    screen and exchange, matrix cores resident and per step, vector); each
+    call leaves it zeroed."""
+    cases = [(1, 151936, 7, False, 0.02), (64, 151936, 7, True, 0.02), (1, 1000, 3, True, 0.3),
+             (17, 4096, 5, False, 0.3), (1, 70001, 9, False, 0.3), (64, 151936, 3, False, 0.02),
+             (1, 151936, 7, True, 0.02), (5, 3000, 4, True, 0.3)]
+    big = max(dh.head_sample_workspace_size(B, g, V, 64, 256) for B, V, g, _, _ in cases)
     ws = torch.zeros(big, dtype=torch.uint8, device="cuda")
-    for i, (V, gamma, gumbel) in enumerate(cases):
-        s = synth.SamplerShape(B=1, gamma=gamma, V=V, H=64, r=256, dtype="bf16", w_sd=0.3, U_sd=2.0, wc_sd=0.05,
+    for i, (B, V, gamma, gumbel, w_sd) in enumerate(cases):
+        s = synth.SamplerShape(B=B, gamma=gamma, V=V, H=64, r=256, dtype="bf16", w_sd=w_sd, U_sd=2.0, wc_sd=0.05,
                                gumbel=gumbel, seed=500 + i)
         w, x = synth.sampler_weights(s), synth.sampler_batch(s)
         args = [dev(v) for v in (x["U"], x["h"], w["W1"], w["W2"], w["w_conf"])] + [0.1, dev(x["x0"]), dev(x["G"])]
         a = dh.head_sample(*args, workspace=ws)
         b = dh.head_sample(*args)
         for k in a:
-            assert torch.equal(a[k], b[k]), (V, k)
-        assert int(ws.count_nonzero()) == 0
+            assert torch.equal(a[k], b[k]), (B, V, k)
+        assert int(ws.count_nonzero()) == 0, (B, V, gamma)

@@ -1551,7 +1551,7 @@ __global__ __launch_bounds__(256) void sample_step_mfma(int64_t B, int64_t gamma
 // ---------------------------------------------------------------------------
 constexpr int kResRegTiles = 2;  // 32-row W2 tiles held in registers per wave
 constexpr int kResWaves = 8;
-constexpr int kResLdsTiles = 4;  // more tiles per workgroup held in LDS
+constexpr int kResLdsTiles = 3;  // more tiles per workgroup held in LDS
 constexpr int kResThreads = 64 * kResWaves;
 constexpr int kResMaxTiles = kResWaves * kResRegTiles + kResLdsTiles;
 constexpr int kResMaxReq = 64;
@@ -1563,17 +1563,43 @@ __device__ __forceinline__ int32_t winner_token(uint64_t key) {  // 0 or 1: no c
     return key <= 1 ? -1 : key_token(key);
 }
 
-template <int NT>
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Read back one 32 x 32 Gumbel unit that buffer_load_dwordx4 ... lds put into
+// LDS (lane l's 16 bytes of load c at c * 1024 + 16 l).  The compiler does
+// not tell apart the LDS slots those loads fill and would wait for every
+// load in flight before any read of them, so the read is written out here.
+// The U words of the same unit are passed in only as a dependency: they were
+// loaded after this unit's Gumbel loads, and vector memory loads complete in
+// order, so the wait the compiler puts in front for them also covers the
+// Gumbel data.  The trailing wait makes the slot free for its next load.
+// There is no memory clobber, which would make the compiler wait for every
+// LDS load in flight, the next unit's included; callers fence the read with
+// scheduling barriers instead.
+__device__ __forceinline__ void read_gumbel_unit(uint32_t lds_addr, const u32x2_t (&dep)[4], f32x4_t (&g)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:1024\n\t"
+        "ds_read_b128 %2, %4 offset:2048\n\t"
+        "ds_read_b128 %3, %4 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(g[0]), "=&v"(g[1]), "=&v"(g[2]), "=&v"(g[3])
+        : "v"(lds_addr), "v"(dep[0]), "v"(dep[1]), "v"(dep[2]), "v"(dep[3]));
+}
+
+template <int NT, bool HG>
 __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, int gamma, int64_t V, int tiles_per_wg, const bf16_t* __restrict__ U,
                       const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W2,
                       const bf16_t* __restrict__ w_conf, int64_t H, float b_conf, const int32_t* __restrict__ x0,
                       const float* __restrict__ G, const int32_t* __restrict__ force, int32_t* __restrict__ tokens,
-                      float* __restrict__ conf, float* __restrict__ survival, float* __restrict__ logits_out,
-                      float* __restrict__ bias_out, const float* __restrict__ hdot, uint64_t* pub, uint64_t* win,
-                      uint32_t* header) {
+                      float* __restrict__ conf, float* __restrict__ survival, const float* __restrict__ hdot,
+                      uint64_t* pub, uint64_t* win, uint32_t* header) {
     constexpr int NREQ = 32 * NT;
     __shared__ __align__(16) uint16_t E_lds[NREQ * kERow];
     __shared__ __align__(16) uint16_t T_lds[kResLdsTiles * 32 * kERow];  // W2 tiles held in LDS
+    __shared__ __align__(16) float G_lds[kResWaves][2][32 * 32];  // per wave: two Gumbel units in flight
     __shared__ uint64_t wkey[kResWaves][NREQ];
     __shared__ uint64_t rkey[kResWaves];
     __shared__ int32_t xprev[NREQ];
@@ -1613,6 +1639,59 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
 
     if (g == 0 && tid < kMfmaRank / 2)
         we_lds[tid] = (uint32_t)w_conf[H + 2 * tid].bits | ((uint32_t)w_conf[H + 2 * tid + 1].bits << 16);
+    // a wave's work per step is a list of units (tile i, 32-request block nt),
+    // unit p = i * NT + nt; the tiles it holds form a prefix of register
+    // tile 0, register tile 1, LDS tile
+    constexpr int kUnits = (kResRegTiles + 1) * NT;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    int ntw = 0;
+    if (t0 + wv < t_end) ntw = 1;
+    if (t0 + wv + kResWaves < t_end) ntw = 2;
+    if (wv < kResLdsTiles && t0 + kResWaves * kResRegTiles + wv < t_end) ntw = 3;
+    const int n_units = ntw * NT;
+    // U of unit p lives in ur[p % 2], its Gumbel values in G_lds[wave][p % 2].
+    // issue(slot, u, kk) starts the loads of unit u of step kk into that slot;
+    // u < 0 is a stand-in (every lane loads the first element group, a cache
+    // hit) so that every path through the unit loop has the same loads in
+    // flight and the waits the compiler places stay at unit depth
+    u32x2_t ur[2][4];
+    // the Gumbel loads go through a buffer descriptor (the caller keeps G
+    // under 2 GiB): the global_load_lds form makes the compiler wait for all
+    // vector memory loads at every later wait, the buffer form does not
+    const __amdgpu_buffer_rsrc_t g_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(G), (short)0, (int)(B * gamma * V * 4), 0x00020000);
+    auto issue = [&](const int slot, const int u, const int kk) {
+        __builtin_amdgcn_sched_barrier(0);
+        const bool real = u >= 0;
+        const int uu = real ? u : 0;
+        const int i = uu / NT, nt = uu % NT;
+        const int64_t t = i < kResRegTiles ? t0 + wv + kResWaves * i : t0 + kResWaves * kResRegTiles + wv;
+        const int bl = nt * 32 + row;
+        const int64_t base = real ? ((int64_t)(bl < B ? bl : B - 1) * gamma + kk) * V : 0;
+        // first row of the tile, opaque to the optimiser: the addresses are
+        // cheap to recompute, and hoisting them out of the step loop spills
+        int vt = (int)(t * 32);
+        asm volatile("" : "+v"(vt));
+        int64_t v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int64_t x = vt + 8 * c + 4 * half;
+            v[c] = !real ? 0 : x + 4 <= V ? x : V - 4;  // clamped (V is a multiple of 4); masked in the epilogue
+        }
+        if constexpr (HG) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(g_rsrc, (lds_void_t*)&G_lds[wv][slot][c * 256], 16,
+                                                         (uint32_t)(base + v[c]) * 4u, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // U strictly after this unit's Gumbel loads
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ur[slot][c] = *reinterpret_cast<const u32x2_t*>(U + base + v[c]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    issue(0, 0 < n_units ? 0 : -1, 0);
+    issue(1, 1 < n_units ? 1 : -1, 0);
+
     float A = 1.f;  // workgroup 0, thread 4 b: running survival of request b
     for (int k = 0; k < gamma; ++k) {
         // previous tokens: the anchors, then the winners of the last step
@@ -1676,67 +1755,82 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
             }
         }
 
-        // the products, the + U (+ G) epilogue and the in-lane argmax
+        // the products, the + U (+ G) epilogue and the in-lane argmax, one unit
+        // at a time with the U and Gumbel loads of the unit after next in flight
         uint64_t key[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) key[nt] = 0;
 #pragma unroll
-        for (int i = 0; i < kResRegTiles + 1; ++i) {
+        for (int p = 0; p < kUnits; ++p) {
+            if (p >= n_units) break;  // wave-uniform; the units held form a prefix
+            const int i = p / NT, nt = p % NT;
             const bool lds_tile = i == kResRegTiles;
-            if (lds_tile && wave >= kResLdsTiles) continue;  // wave-uniform
-            const int64_t t = lds_tile ? t0 + kResWaves * kResRegTiles + wave : t0 + wave + kResWaves * i;
-            if (t >= t_end) continue;  // wave-uniform
-            // first row of the tile, opaque to the optimiser: the per-row
-            // indices below are cheap to recompute, and hoisting them out of
-            // the step loop spills them
-            int vt = (int)(t * 32);
-            asm volatile("" : "+v"(vt));
-            __builtin_amdgcn_sched_barrier(0);  // one tile's loads in flight at a time: registers are tight
-            // one 32-request tile at a time (registers are tight): U (and G)
-            // first, lane (request nt*32 + row, half h) taking rows
-            // 8 c + 4 h .. +3 for c < 4, then the products, then the epilogue
+            const int64_t t = lds_tile ? t0 + kResWaves * kResRegTiles + wv : t0 + wv + kResWaves * i;
+            __builtin_amdgcn_sched_barrier(0);
+            f32x16_t acc;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int bl = nt * 32 + row;
-                const int64_t base = ((int64_t)(bl < B ? bl : B - 1) * gamma + k) * V;
-                uint2 ur[4];
-                float4 gr[4];
+            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    int64_t v = vt + 8 * c + 4 * half;
-                    v = v + 4 <= V ? v : V - 4;  // clamped (V is a multiple of 4); masked below
-                    ur[c] = *reinterpret_cast<const uint2*>(U + base + v);
-                    gr[c] = G ? *reinterpret_cast<const float4*>(G + base + v) : float4{0.f, 0.f, 0.f, 0.f};
-                }
-                f32x16_t acc;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-                for (int s = 0; s < 16; ++s) {
-                    const uint4 aw =
-                        lds_tile ? *reinterpret_cast<const uint4*>(T_lds + (wave * 32 + row) * kERow + s * 16 + half * 8)
-                                 : a[i < kResRegTiles ? i : 0][s];
-                    const uint4 bw = *reinterpret_cast<const uint4*>(E_lds + (nt * 32 + row) * kERow + s * 16 + half * 8);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aw),
-                                                                  __builtin_bit_cast(bf16x8_t, bw), acc, 0, 0, 0);
-                }
-                if (bl >= B || xprev[bl] < 0) continue;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
+            for (int s = 0; s < 16; ++s) {
+                const uint4 aw = lds_tile ? *reinterpret_cast<const uint4*>(T_lds + (wv * 32 + row) * kERow + s * 16 + half * 8)
+                                          : a[i < kResRegTiles ? i : 0][s];
+                const uint4 bw = *reinterpret_cast<const uint4*>(E_lds + (nt * 32 + row) * kERow + s * 16 + half * 8);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aw),
+                                                              __builtin_bit_cast(bf16x8_t, bw), acc, 0, 0, 0);
+            }
+            f32x4_t gr[4];
+            if constexpr (HG) {
+                const uint32_t ga = (uint32_t)(uintptr_t)(lds_void_t*)&G_lds[wv][p & 1][lane * 4];
+                __builtin_amdgcn_sched_barrier(0);
+                read_gumbel_unit(ga, ur[p & 1], gr);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const int bl = nt * 32 + row;
+            if (bl < B && xprev[bl] >= 0) {
+                int vt = (int)(t * 32);
+                asm volatile("" : "+v"(vt));
+                // lane element r is row vt + 8 (r / 4) + 4 half + r % 4: rows rise with r
+                auto score = [&](const int r, float& bias, float& lg) {
                     const int c = r / 4, q = r % 4;
-                    const int64_t v = vt + 8 * c + 4 * half + q;
-                    if (v >= V) continue;
-                    const uint32_t uw = q < 2 ? ur[c].x : ur[c].y;
-                    const float uu = (q & 1) ? widen_hi(uw) : widen_lo(uw);
-                    const float gg = q == 0 ? gr[c].x : q == 1 ? gr[c].y : q == 2 ? gr[c].z : gr[c].w;
-                    const float bias = acc[r];
-                    const float lg = uu + bias;
-                    const float sc = G ? lg + gg : lg;
-                    if (bias_out) bias_out[base + v] = bias;
-                    if (logits_out) logits_out[base + v] = lg;
-                    key[nt] = umax64(key[nt], argmax_key(sc, (uint32_t)v));
+                    const uint32_t uw = ur[p & 1][c][q >> 1];
+                    bias = acc[r];
+                    lg = ((q & 1) ? widen_hi(uw) : widen_lo(uw)) + bias;
+                    if constexpr (HG) return lg + gr[c][q];
+                    return lg;
+                };
+                if (vt + 32 <= V) {  // wave-uniform
+                    // whole tile in range: first maximum in float compares, one
+                    // packed key per unit (+ 0 maps -0 onto +0)
+                    float bias, lg;
+                    float best = score(0, bias, lg);
+                    int bi = 0;
+#pragma unroll
+                    for (int r = 1; r < 16; ++r) {
+                        const float sc = score(r, bias, lg);
+                        if (sc > best) {
+                            best = sc;
+                            bi = r;
+                        }
+                    }
+                    const uint32_t v = (uint32_t)(vt + 8 * (bi >> 2) + 4 * half + (bi & 3));
+                    key[nt] = umax64(key[nt], argmax_key(best + 0.f, v));
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int64_t v = vt + 8 * (r / 4) + 4 * half + r % 4;
+                        if (v >= V) continue;
+                        float bias, lg;
+                        const float sc = score(r, bias, lg);
+                        key[nt] = umax64(key[nt], argmax_key(sc + 0.f, (uint32_t)v));
+                    }
                 }
             }
+            issue(p & 1, p + 2 < n_units ? p + 2 : -1, k);
+        }
+        // the first two units of the next step need nothing from this one
+        if (k + 1 < gamma) {
+            issue(0, 0 < n_units ? 0 : -1, k + 1);
+            issue(1, 1 < n_units ? 1 : -1, k + 1);
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -1815,8 +1909,9 @@ ResidentPlan resident_plan(int64_t B, int64_t V) {
     const int64_t per = (ntiles + nwg - 1) / nwg;
     if (per > (int64_t)kResMaxTiles) return p;
     int per_cu = 0;
-    const void* fn = B <= 32 ? reinterpret_cast<const void*>(&sample_batch_resident<1>)
-                             : reinterpret_cast<const void*>(&sample_batch_resident<2>);
+    // the Gumbel variants use the most LDS and registers
+    const void* fn = B <= 32 ? reinterpret_cast<const void*>(&sample_batch_resident<1, true>)
+                             : reinterpret_cast<const void*>(&sample_batch_resident<2, true>);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kResThreads, 0) != hipSuccess || per_cu < 1)
         return p;
     p.nwg = (int)nwg;
@@ -1887,7 +1982,10 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
     if constexpr (std::is_same_v<T, bf16_t>) {
         // resident W2: one persistent kernel for the whole block
         const ResidentPlan rp = mfma ? resident_plan(B, V) : ResidentPlan{};
-        if (rp.nwg > 0 && (uintptr_t)U % 8 == 0 && (G == nullptr || (uintptr_t)G % 16 == 0)) {
+        // (stored logits or bias go to the general kernel: any store in the
+        // resident kernel's tile loop makes its loads wait for one another)
+        if (rp.nwg > 0 && lo == nullptr && bo == nullptr && (uintptr_t)U % 8 == 0 &&
+            (G == nullptr || ((uintptr_t)G % 16 == 0 && B * gamma * V * 4 < ((int64_t)1 << 31)))) {
             char* p = static_cast<char*>(ws);
             float* hdot = reinterpret_cast<float*>(p);
             p += ((size_t)(4 * B * gamma) + 255) / 256 * 256;
@@ -1900,10 +1998,12 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
             if (e != hipSuccess) return e;
             int g = (int)gamma, tpw = rp.tiles_per_wg;
             int64_t Bb = B, Vv = V, Hh = H;
-            void* args[] = {&Bb,  &g,    &Vv, &tpw,   &Ut,   &W1t,      &W2t, &wt,       &Hh,   &b_conf, &x0,
-                            &G,   &force, &tokens, &conf, &survival, &lo,  &bo,  &hdot, &pub,    &win,  &header};
-            const void* fn = B <= 32 ? reinterpret_cast<const void*>(&sample_batch_resident<1>)
-                                     : reinterpret_cast<const void*>(&sample_batch_resident<2>);
+            void* args[] = {&Bb, &g,     &Vv,     &tpw,  &Ut,       &W1t,  &W2t, &wt,  &Hh,    &b_conf,
+                            &x0, &G,     &force,  &tokens, &conf,   &survival, &hdot, &pub, &win, &header};
+            const void* fn = G ? (B <= 32 ? reinterpret_cast<const void*>(&sample_batch_resident<1, true>)
+                                          : reinterpret_cast<const void*>(&sample_batch_resident<2, true>))
+                               : (B <= 32 ? reinterpret_cast<const void*>(&sample_batch_resident<1, false>)
+                                          : reinterpret_cast<const void*>(&sample_batch_resident<2, false>));
             // a plain launch: one workgroup per CU at most, all resident together;
             // the bounded spins turn any other outcome into an error, not a hang
             return hipLaunchKernel(fn, dim3(rp.nwg), dim3(kResThreads), args, 0, stream);

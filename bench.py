@@ -234,7 +234,7 @@ def main():
             "us_per_call": round(a_us, 2), "positions_per_s": round(sa.N / (a_us * 1e-6), 1),
             "roofline": {"kernel": "dspark_accept_rate", "bound": "hbm", "achieved": round(gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": profiled_traffic("accept_rate_rows_2048x151936.md", ACCEPT_SOURCES),
+                         "traffic": profiled_traffic("accept_rate_cluster_2048x151936.md", ACCEPT_SOURCES),
                          "bytes_per_launch": a_bytes},
         }
         del D, T
@@ -257,9 +257,17 @@ def main():
         us3 = b0.elapsed_time(b1) * 1e3 / 10
         flops = 2.0 * 64 * s3.gamma * s3.V * s3.r
         by3 = sampler_call_bytes(64, 7, s3.V, s3.H, s3.r) + 64 * 7 * s3.V * 4
-        line["extra_b64"] = {"us_per_call": round(us3, 2), "positions_per_s": round(64 * 7 / (us3 * 1e-6), 1),
-                             "GB_s": round(by3 / (us3 * 1e-6) / 1e9, 1),
-                             "mfma_tflops": round(flops / (us3 * 1e-6) / 1e12, 2)}
+        gb3 = by3 / (us3 * 1e-6) / 1e9
+        line["extra_b64"] = {"workload": "Markov-head block sampler, B=64 gamma=7 V=151936 H=5120 r=256 bf16, "
+                                         "Gumbel-max with fp32 noise",
+                             "us_per_call": round(us3, 2), "positions_per_s": round(64 * 7 / (us3 * 1e-6), 1),
+                             "mfma_tflops": round(flops / (us3 * 1e-6) / 1e12, 2),
+                             "roofline": {"kernel": "dspark_head_sample B=64 (sample_init + resident kernel)",
+                                          "bound": "hbm", "achieved": round(gb3, 1), "peak": HBM_PEAK_GBS,
+                                          "unit": "GB/s", "frac": round(gb3 / HBM_PEAK_GBS, 4),
+                                          "traffic": profiled_traffic("head_sample_resident_b64_vocab151936.md",
+                                                                      SAMPLER_SOURCES),
+                                          "bytes_per_launch": by3}}
         s5 = synth.SCHEDULE_TRAIN
         for kind in ("tokens", "steps"):
             c5, _ = dh.prepare_prefix_schedule(to_dev(synth.schedule_conf(s5), dev),

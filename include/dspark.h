@@ -99,7 +99,8 @@ typedef enum {
  *   bias_out   [B][gamma][V] fp32 out, optional (NULL = not written).
  * A token id outside [0, V) in x0 or force makes that request's tokens -1 and
  * its conf and survival NaN from that step on; other requests are unaffected.
- * NaN scores order above +inf.
+ * Scores compare as binary32 values (-0 equals +0, infinities allowed); with a
+ * NaN score anywhere in a step the token of that step is unspecified.
  */
 dspark_status_t dspark_head_sample(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int32_t dtype,
                                    const void* U, const void* h, const void* W1, const void* W2,

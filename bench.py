@@ -262,7 +262,7 @@ def main():
                                          "Gumbel-max with fp32 noise",
                              "us_per_call": round(us3, 2), "positions_per_s": round(64 * 7 / (us3 * 1e-6), 1),
                              "mfma_tflops": round(flops / (us3 * 1e-6) / 1e12, 2),
-                             "roofline": {"kernel": "dspark_head_sample B=64 (sample_init + resident kernel)",
+                             "roofline": {"kernel": "dspark_head_sample B=64 (one resident kernel)",
                                           "bound": "hbm", "achieved": round(gb3, 1), "peak": HBM_PEAK_GBS,
                                           "unit": "GB/s", "frac": round(gb3 / HBM_PEAK_GBS, 4),
                                           "traffic": profiled_traffic("head_sample_resident_b64_vocab151936.md",

@@ -1591,11 +1591,11 @@ __device__ __forceinline__ void read_gumbel_unit(uint32_t lds_addr, const u32x2_
 
 template <int NT, bool HG>
 __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, int gamma, int64_t V, int tiles_per_wg, const bf16_t* __restrict__ U,
-                      const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W2,
+                      const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W2, const bf16_t* __restrict__ h,
                       const bf16_t* __restrict__ w_conf, int64_t H, float b_conf, const int32_t* __restrict__ x0,
                       const float* __restrict__ G, const int32_t* __restrict__ force, int32_t* __restrict__ tokens,
-                      float* __restrict__ conf, float* __restrict__ survival, const float* __restrict__ hdot,
-                      uint64_t* pub, uint64_t* win, uint32_t* header) {
+                      float* __restrict__ conf, float* __restrict__ survival, uint64_t* hword, uint64_t* pub,
+                      uint64_t* win, uint32_t* header) {
     constexpr int NREQ = 32 * NT;
     __shared__ __align__(16) uint16_t E_lds[NREQ * kERow];
     __shared__ __align__(16) uint16_t T_lds[kResLdsTiles * 32 * kERow];  // W2 tiles held in LDS
@@ -1692,6 +1692,38 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
     issue(0, 0 < n_units ? 0 : -1, 0);
     issue(1, 1 < n_units ? 1 : -1, 0);
 
+    // the hidden part of every confidence logit, w_h . h[b, k]: pair
+    // p = b gamma + k goes to wave p of the grid and is posted as a tagged
+    // word that workgroup 0 reads at step k.  No barrier here, so these loads
+    // overlap the W2 loads above.
+    for (int64_t p = (int64_t)g * kResWaves + wv; p < B * gamma; p += (int64_t)nwg * kResWaves) {  // wave-uniform
+        const bf16_t* hr = h + p * H;
+        float hs = 0.f;
+        if (H % 8 == 0 && (uintptr_t)h % 16 == 0 && (uintptr_t)w_conf % 16 == 0) {
+            const uint4* hv = reinterpret_cast<const uint4*>(hr);
+            const uint4* cv = reinterpret_cast<const uint4*>(w_conf);
+            const int64_t n = H / 8;
+            for (int64_t i0 = lane; i0 < n; i0 += 64 * 8) {
+                uint4 a[8], c[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int64_t i = i0 + 64 * j < n ? i0 + 64 * j : 0;  // clamped; masked below
+                    a[j] = hv[i];
+                    c[j] = cv[i];
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (i0 + 64 * j < n)
+                        hs = dot2(c[j].w, a[j].w, dot2(c[j].z, a[j].z, dot2(c[j].y, a[j].y, dot2(c[j].x, a[j].x, hs))));
+            }
+        } else {
+            for (int64_t i = lane; i < H; i += 64) hs += load_elem(w_conf, i) * load_elem(hr, i);
+        }
+        for (int o = 32; o > 0; o >>= 1) hs += __shfl_xor(hs, o);
+        if (lane == 0)
+            __hip_atomic_store(hword + p, kTag | __float_as_uint(hs), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
     float A = 1.f;  // workgroup 0, thread 4 b: running survival of request b
     for (int k = 0; k < gamma; ++k) {
         // previous tokens: the anchors, then the winners of the last step
@@ -1747,7 +1779,13 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
                 s += __shfl_xor(s, 2);
                 if (part == 0 && bl < B) {
                     const bool live = xprev[bl] >= 0;
-                    const float c = 1.f / (1.f + expf(-(hdot[bl * gamma + k] + s + b_conf)));
+                    uint64_t hw = 0;  // posted in the prologue, normally long before
+                    for (int spin = 0; spin < kChainSpinLimit && hw == 0; ++spin) {
+                        hw = __hip_atomic_load(hword + bl * gamma + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (hw == 0) __builtin_amdgcn_s_sleep(1);
+                    }
+                    const float hd = hw != 0 ? __uint_as_float((uint32_t)hw) : __builtin_nanf("");
+                    const float c = 1.f / (1.f + expf(-(hd + s + b_conf)));
                     A = A * c;
                     conf[bl * gamma + k] = live ? c : __builtin_nanf("");
                     survival[bl * gamma + k] = live ? A : __builtin_nanf("");
@@ -1890,7 +1928,8 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
         for (int i = tid; i < kResCopies * kResMaxReq; i += kResThreads)
             __hip_atomic_store(win + k * kResCopies * kResMaxReq + i, (uint64_t)0, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-        for (int64_t i = tid; i < B * gamma; i += kResThreads) const_cast<float*>(hdot)[i] = 0.f;
+        for (int64_t i = tid; i < B * gamma; i += kResThreads)
+            __hip_atomic_store(hword + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (tid == 0) __hip_atomic_store(&header[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -1920,7 +1959,7 @@ ResidentPlan resident_plan(int64_t B, int64_t V) {
 }
 
 size_t resident_workspace(int64_t B, int64_t gamma) {
-    return ((size_t)(4 * B * gamma) + 255) / 256 * 256 + kResHeader +
+    return ((size_t)(8 * B * gamma) + 255) / 256 * 256 + kResHeader +
            (size_t)8 * gamma * kResMaxWGs * kResMaxReq + (size_t)8 * gamma * kResCopies * kResMaxReq;
 }
 
@@ -1987,19 +2026,16 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
         if (rp.nwg > 0 && lo == nullptr && bo == nullptr && (uintptr_t)U % 8 == 0 &&
             (G == nullptr || ((uintptr_t)G % 16 == 0 && B * gamma * V * 4 < ((int64_t)1 << 31)))) {
             char* p = static_cast<char*>(ws);
-            float* hdot = reinterpret_cast<float*>(p);
-            p += ((size_t)(4 * B * gamma) + 255) / 256 * 256;
+            uint64_t* hword = reinterpret_cast<uint64_t*>(p);
+            p += ((size_t)(8 * B * gamma) + 255) / 256 * 256;
             uint32_t* header = reinterpret_cast<uint32_t*>(p);
             uint64_t* pub = reinterpret_cast<uint64_t*>(p + kResHeader);
             uint64_t* win = pub + (size_t)gamma * kResMaxWGs * kResMaxReq;
-            hipLaunchKernelGGL((sample_init<T>), dim3((uint32_t)(B * gamma)), dim3(kThreads), 0, stream, B, gamma, H,
-                               static_cast<const T*>(h), wt, (uint64_t*)nullptr, 0, hdot);
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
+            const T* ht = static_cast<const T*>(h);
             int g = (int)gamma, tpw = rp.tiles_per_wg;
             int64_t Bb = B, Vv = V, Hh = H;
-            void* args[] = {&Bb, &g,     &Vv,     &tpw,  &Ut,       &W1t,  &W2t, &wt,  &Hh,    &b_conf,
-                            &x0, &G,     &force,  &tokens, &conf,   &survival, &hdot, &pub, &win, &header};
+            void* args[] = {&Bb, &g,     &Vv,    &tpw,    &Ut,   &W1t,      &W2t,   &ht,  &wt,  &Hh,    &b_conf,
+                            &x0, &G,     &force, &tokens, &conf, &survival, &hword, &pub, &win, &header};
             const void* fn = G ? (B <= 32 ? reinterpret_cast<const void*>(&sample_batch_resident<1, true>)
                                           : reinterpret_cast<const void*>(&sample_batch_resident<2, true>))
                                : (B <= 32 ? reinterpret_cast<const void*>(&sample_batch_resident<1, false>)

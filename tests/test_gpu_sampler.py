@@ -63,6 +63,25 @@ def test_shapes(B, gamma, V, H, r, dtype, w_sd, gumbel):
     sampler_parity(x, w, want_logits=True)
 
 
+
+@pytest.mark.parametrize(
+    "B,gamma,V,H,gumbel",
+    [
+        (16, 4, 4096, 32, False),  # one 32-request tile, greedy, whole tiles
+        (24, 3, 4100, 13, True),  # ragged last tile, hidden size not a multiple of 8
+        (33, 3, 1000, 16, True),  # two request tiles, fewer workgroups than requests
+        (64, 5, 12000, 40, False),  # 64 requests, greedy
+        (20, 20, 700, 8, False),  # long block
+        (48, 2, 65536, 64, True),  # some waves hold fewer tiles than others
+    ],
+)
+def test_batched_without_stored_logits(B, gamma, V, H, gumbel):
+    """bf16 rank 256 with 16..64 requests and no stored logits or bias: the
+    persistent kernel that keeps W2 in registers and LDS."""
+    x, w = _random_case(0xBA7C4 + B * 131 + V, B, gamma, V, H, 256, "bf16", 0.4, gumbel)
+    sampler_parity(x, w, want_logits=False)
+
+
 def test_all_equal_scores_pick_token_zero():
     B, gamma, V, H, r = 3, 4, 3000, 8, 32
     x = {"U": np.zeros((B, gamma, V), np.float32), "h": np.zeros((B, gamma, H), np.float32),

@@ -172,11 +172,12 @@ __global__ __launch_bounds__(kCThreads) void accept_rate_cluster(int64_t N, int6
                                                                  int64_t vpc, const T* __restrict__ d, int64_t ldd,
                                                                  const T* __restrict__ t, int64_t ldt,
                                                                  float* __restrict__ out, uint64_t* stats,
-                                                                 uint64_t* parts, uint32_t* counters,
+                                                                 uint64_t* parts, uint32_t* counters, uint64_t* nexts,
                                                                  uint32_t* header) {
     static_assert(kCMaxCluster * 4 <= 64, "one wave polls all statistics words of a cluster");
     __shared__ float lds[2 * kCThreads / 64];
     __shared__ float rowstat[4];
+    __shared__ int64_t next_row;
     __shared__ int last_flag;
     constexpr int E = Vec<T>::N;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -201,11 +202,18 @@ __global__ __launch_bounds__(kCThreads) void accept_rate_cluster(int64_t N, int6
             }
         }
     };
+    // Rows after the first are claimed from a shared counter, so that clusters
+    // that run faster (their workgroups are older on their CUs) take more of
+    // them.  Member 0 claims the next row while this one loads; the index
+    // travels to the other members with this row's statistics.
     uint32_t iter = 0;
-    for (int64_t row = q; row < N; row += n_clusters, ++iter) {
+    int64_t row = q;
+    while (row < N) {
         const T* dr = d + row * ldd;
         const T* tr = t + row * ldt;
         load_row(row);
+        uint32_t claim = 0;
+        if (c == 0 && tid == 0) claim = __hip_atomic_fetch_add(&header[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // pass 1: running (max, sum) of this thread's elements
         float md = -INFINITY, sd = 0.f, mt = -INFINITY, st = 0.f;
 #pragma unroll
@@ -231,23 +239,29 @@ __global__ __launch_bounds__(kCThreads) void accept_rate_cluster(int64_t N, int6
         if (C > 1) {  // meet the other chunks of this row
             const uint32_t tag = iter + 1;
             uint64_t* slot = stats + (((int64_t)q * 2 + (iter & 1)) * C) * 4;
+            uint64_t* nslot = nexts + (int64_t)q * 2 + (iter & 1);
             if (tid == 0) {
+                if (c == 0)
+                    __hip_atomic_store(nslot, ((uint64_t)tag << 32) | (uint64_t)(uint32_t)(n_clusters + claim),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(slot + c * 4 + 0, tagged(tag, Md), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(slot + c * 4 + 1, tagged(tag, Sd), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(slot + c * 4 + 2, tagged(tag, Mt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(slot + c * 4 + 3, tagged(tag, St), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             if (tid < 64) {
-                uint64_t w = tagged(tag, 0.f);
+                uint64_t w = tagged(tag, 0.f), nw = 0;
                 bool ok = false;
                 for (int spin = 0; spin < kCSpinLimit && !failed; ++spin) {
                     w = lane < 4 * C ? __hip_atomic_load(slot + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                      : tagged(tag, 0.f);
-                    ok = __all((uint32_t)(w >> 32) == tag);
+                    nw = __hip_atomic_load(nslot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    ok = __all((uint32_t)(w >> 32) == tag && (uint32_t)(nw >> 32) == tag);
                     if (ok) break;
                     __builtin_amdgcn_s_sleep(1);
                 }
                 if (!ok) failed = true;
+                if (tid == 0) next_row = ok ? (int64_t)(uint32_t)nw : N;  // a lost member ends the cluster
                 const float val = __uint_as_float((uint32_t)w);
                 float M1 = -INFINITY, S1 = 0.f, M2 = -INFINITY, S2 = 0.f;  // chunks merged in order 0..C-1
                 for (int k = 0; k < C; ++k) {
@@ -262,6 +276,8 @@ __global__ __launch_bounds__(kCThreads) void accept_rate_cluster(int64_t N, int6
             }
             __syncthreads();
             Md = rowstat[0], Sd = rowstat[1], Mt = rowstat[2], St = rowstat[3];
+        } else {
+            if (tid == 0) next_row = n_clusters + claim;
         }
 
         // pass 2: |p - q| with the normaliser folded into the exponent.  The raw
@@ -322,6 +338,10 @@ __global__ __launch_bounds__(kCThreads) void accept_rate_cluster(int64_t N, int6
                 }
             }
         }
+        __syncthreads();  // next_row is written before the statistics barrier or here
+        row = next_row;
+        ++iter;
+        __syncthreads();  // next_row is rewritten next row
     }
 
     // leave: the last workgroup out clears slots and counters for the next call
@@ -339,7 +359,12 @@ __global__ __launch_bounds__(kCThreads) void accept_rate_cluster(int64_t N, int6
                 __hip_atomic_store(parts + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             for (int64_t i = tid; i < n_clusters; i += kCThreads)
                 __hip_atomic_store(counters + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (tid == 0) __hip_atomic_store(&header[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int64_t i = tid; i < (int64_t)n_clusters * 2; i += kCThreads)
+                __hip_atomic_store(nexts + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (tid == 0) {
+                __hip_atomic_store(&header[2], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&header[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
 }
@@ -418,6 +443,8 @@ size_t cluster_workspace(int64_t N, int64_t V) {
     // sized for the largest cluster count any device could use
     (void)V;
     const int64_t max_clusters = N < 4096 ? N : 4096;
+    // per cluster: statistics slots, partial-sum slots, a counter and the two
+    // next-row words (with alignment slack)
     return kCHeader + (size_t)max_clusters * (2 * kCMaxCluster * 4 * 8 + 2 * kCMaxCluster * 8 + 4 + 252);
 }
 
@@ -437,9 +464,14 @@ hipError_t launch_typed(int64_t N, int64_t V, const void* d, int64_t ldd, const 
             uint64_t* parts = reinterpret_cast<uint64_t*>(w + kCHeader + (size_t)p.n_clusters * 2 * p.C * 4 * 8);
             uint32_t* counters = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(parts) +
                                                              (size_t)p.n_clusters * 2 * p.C * 8);
+            // the claimed next rows: two tagged words per cluster (inside the
+            // per-cluster slack of cluster_workspace)
+            uint64_t* nexts = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(counters) +
+                                                          ((size_t)p.n_clusters * 4 + 7) / 8 * 8);
             int64_t NN = N, VV = V, vpc = p.vpc, ld1 = ldd, ld2 = ldt;
             int C = p.C, nc = p.n_clusters;
-            void* args[] = {&NN, &VV, &C, &nc, &vpc, &dp, &ld1, &tp, &ld2, &out, &stats, &parts, &counters, &header};
+            void* args[] = {&NN,  &VV,    &C,    &nc,       &vpc,  &dp,    &ld1,
+                            &tp,  &ld2,   &out,  &stats,    &parts, &counters, &nexts, &header};
             // at most the resident capacity: all workgroups of a cluster run together
             return hipLaunchKernel(p.fn, dim3((uint32_t)(p.n_clusters * p.C)), dim3(kCThreads), args, 0, stream);
         }

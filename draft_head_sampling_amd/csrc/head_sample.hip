@@ -469,6 +469,9 @@ struct ScreenLds {
     float fsum[kRegionWords];
     float pk[kScreenMaxGamma];
     float winf[kScreenMaxGamma];
+    uint32_t wkey[kScreenMaxGamma];                 // the windows as ranking-key bounds
+    int tj[kScreenMaxGamma][kERows];                // best candidate of step k after e row r (-1: unproven)
+    int32_t ttok[kScreenMaxGamma][kERows];          // and its token
     uint32_t wtop[kScreenMaxGamma][kScreenWaves][4];  // row workgroup: each wave's best keys
     uint32_t a1[kScreenMaxGamma];
     int sync;                                        // arrivals of the screening waves
@@ -669,26 +672,53 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                                  kBetaFloor;
                 const float a = __uint_as_float(sc.fmax[kScreenStep * tid + 4]);
                 const float eg = 5.f * kUlp * (a + bg);
-                sc.winf[tid] = float_down(key_lower(sc.fmax[kScreenStep * tid]) - 2.0 * ((double)bg + eg));
+                const float wf = float_down(key_lower(sc.fmax[kScreenStep * tid]) - 2.0 * ((double)bg + eg));
+                sc.winf[tid] = wf;
+                // a bucket reaches the window iff its upper end does: for non-NaN
+                // floats a >= b iff orderable(a) >= orderable(b), once a zero
+                // window takes the smaller image (-0), so both zeros pass
+                sc.wkey[tid] = wf != wf ? 0xffffffffu : orderable(wf == 0.f ? -0.f : wf);
             }
             __syncthreads();
-            // the entries inside the windows, straight from the polled words
-            if (type < kScreenEntries) {
-                const double wk = sc.winf[kk];
+            // the entries inside the windows, straight from the polled words: a
+            // branch-free hit mask per lane, then the few hits are written out
+            {
+                uint32_t hits = 0;
+                if (type < kScreenEntries) {
+                    const uint32_t wq = sc.wkey[kk];
+                    const uint32_t v32 = (uint32_t)V;  // V < 2^31
 #pragma unroll
-                for (int i = 0; i < kPollRegions; ++i) {
-                    if (1 + wave + kChainWaves * i >= nwg) continue;
-                    const uint64_t w = word[i];
-                    const uint32_t id1 = (uint32_t)w;  // row id + 1, or the empty marker
-                    if (id1 < 1 || id1 > (uint64_t)V || key_upper((uint32_t)(w >> 32)) < wk) continue;
-                    const int idx = atomicAdd(&sc.ncand, 1);
-                    if (idx < kCandMax) sc.cv[idx] = id1 - 1, sc.cstep[idx] = kk;
-                    else sc.overflow[kk] = 1;
+                    for (int i = 0; i < kPollRegions; ++i) {
+                        const uint64_t w = word[i];
+                        const uint32_t id1 = (uint32_t)w;  // row id + 1, or the empty marker
+                        const uint32_t q = (uint32_t)(w >> 32);
+                        // (bitwise ands: no branch per word)
+                        const uint32_t hit = (uint32_t)(1 + wave + kChainWaves * i < nwg) & (uint32_t)(id1 - 1u < v32) &
+                                             (uint32_t)(q != 0) & (uint32_t)((q | kLidMask) >= wq);
+                        hits |= hit << i;
+                    }
+                }
+                if (hits) {
+                    int idx = atomicAdd(&sc.ncand, __popc(hits));
+#pragma unroll
+                    for (int i = 0; i < kPollRegions; ++i) {
+                        if ((hits >> i) & 1u) {
+                            if (idx < kCandMax) sc.cv[idx] = (uint32_t)word[i] - 1, sc.cstep[idx] = kk;
+                            else sc.overflow[kk] = 1;
+                            ++idx;
+                        }
+                    }
                 }
             }
             __syncthreads();
             const bool abort = sc.abort != 0;
             const int nc = sc.ncand < kCandMax ? sc.ncand : kCandMax;
+            // the real norm, posted by every row workgroup after its W2 stream:
+            // a first look now, used after the table below
+            const int np = tid - kChainThreads / 2;  // norm poller index
+            const bool poller = !abort && np >= 0 && np + 1 < nwg;
+            const uint64_t* npw = regions + (int64_t)(poller ? np + 1 : 1) * kRegionWords + nwords - 1;
+            uint64_t nword = poller ? __hip_atomic_load(npw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
 
             // stage the candidates' rows (one wave per candidate) and forced tokens' rows
             if (!abort) {
@@ -761,98 +791,104 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                     }
                 }
             }
-            // The walk, in wave 0 (lane j holds candidate j, lane r e row r,
-            // lane k the per-step quantities).  It first runs with the
-            // guessed largest row norm while waves 4-7 collect the real one;
-            // a guess at least as large makes the candidate sets supersets of
-            // the exact ones, inside the windows, so the result stands when
-            // the real norm is no larger.  Otherwise it runs again.
-            const int np = tid - kChainThreads / 2;  // norm poller index
-            if (!abort && np >= 0 && np + 1 < nwg) {
-                const uint64_t* p = regions + (int64_t)(np + 1) * kRegionWords + nwords - 1;
-                uint64_t w = 0;
-                for (int spin = 0; spin < kChainSpinLimit && w == 0; ++spin) {
-                    w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if (w == 0) __builtin_amdgcn_s_sleep(1);
+            // The walk.  Every step's winner depends on the step before only
+            // through the e row that precedes it, so first a table: for each
+            // step k and each e row r that can precede it, the bound check and
+            // the best candidate (one thread per pair).  The walk itself is then
+            // a chain of lookups in wave 0.  It first runs with the guessed
+            // largest row norm while waves 4-7 collect the real one; a guess at
+            // least as large makes the candidate sets supersets of the exact
+            // ones, inside the windows, so the result stands when the real norm
+            // is no larger.  Otherwise table and walk run again.
+            __syncthreads();  // the bias table is complete
+            const auto build = [&](uint32_t n2b) {
+                for (int p = tid; p < gamma * kERows; p += kChainThreads) {
+                    const int k = p / kERows, r = p % kERows;
+                    bool pv;  // r can be the e row of step k
+                    if (k == 0) pv = r == kERowAnchor;
+                    else if (sc.fv[k - 1] >= 0) pv = r == kERowForced + k - 1;
+                    else pv = r < nc && sc.cstep[r] == k - 1;
+                    int bj = -1;
+                    int32_t bt = -1;
+                    if (pv && !abort) {
+                        const uint32_t m = sc.stepmask[k];
+                        float tmax = -__builtin_inff();
+                        for (uint32_t bits = m; bits; bits &= bits - 1) tmax = fmaxf(tmax, sc.ct[__builtin_ctz(bits)]);
+                        const float n2 = __builtin_sqrtf(__uint_as_float(n2b));
+                        const float es = sc.esq[r];
+                        const uint32_t ab = sc.fmax[kScreenStep * k + 4];
+                        const uint32_t cut = sc.fmax[kScreenStep * k + 3];
+                        const float beta = n2 * __builtin_sqrtf(es) * kBetaSlack + kBetaFloor;
+                        const float eps = 5.f * kUlp * (__uint_as_float(ab) + beta);
+                        const double thr = (double)tmax - 2.0 * ((double)beta + eps);
+                        const bool ok = sc.overflow[k] == 0 && finite_bits(ab) && finite_bits(n2b) &&
+                                        finite_bits(bound_bits(es)) && tmax > -__builtin_inff() &&
+                                        thr >= (double)sc.winf[k] && key_upper(cut) < thr;
+                        if (ok) {
+                            uint64_t best = 0;
+                            for (uint32_t bits = m; bits; bits &= bits - 1) {
+                                const int j = __builtin_ctz(bits);
+                                if ((double)sc.ct[j] >= thr) {
+                                    const float lg = sc.cu[j] + sc.bias[j][r];
+                                    const uint64_t key = argmax_key(G ? lg + sc.cg[j] : lg, sc.cv[j]);
+                                    if (key > best) best = key, bj = j;
+                                }
+                            }
+                            // the best listed row is always a candidate, so best != 0
+                            bt = best != 0 ? key_token(best) : -1;
+                            if (best == 0) bj = -1;
+                        }
+                    }
+                    sc.tj[k][r] = bj;
+                    sc.ttok[k][r] = bt;
                 }
-                if (w == 0) sc.abort = 1;
-                atomicMax(&sc.n2, (uint32_t)w);
-            }
+            };
             struct Walk {
                 int k, pst;
                 int32_t tk;
                 int64_t x;
                 bool valid, fail;
             };
-            Walk wk{};
-            if (wave == 0) {
-                const bool mine = lane < nc;
-                const int cs = mine ? sc.cstep[lane] : -1;
-                const float ct = mine ? sc.ct[lane] : 0.f, cu = mine ? sc.cu[lane] : 0.f, cg = mine ? sc.cg[lane] : 0.f;
-                const uint32_t cv = mine ? sc.cv[lane] : 0u;
-                const float l_esq = lane < kERows ? sc.esq[lane] : 0.f;
-                const int ks = lane < kScreenMaxGamma ? lane : 0;
-                const uint32_t l_ab = sc.fmax[kScreenStep * ks + 4];
-                const uint32_t l_cut = sc.fmax[kScreenStep * ks + 3];
-                const float l_win = sc.winf[ks];
-                const int l_ovf = sc.overflow[ks];
-                const int32_t l_fv = sc.fv[ks];
-                float l_tmax = -__builtin_inff();
-#pragma unroll
-                for (int k = 0; k < kScreenMaxGamma; ++k) {
-                    const float m = wave_max_f32(cs == k ? ct : -__builtin_inff());
-                    if (lane == k) l_tmax = m;
-                }
-                const auto walk = [&](uint32_t n2b) {
-                    Walk r{0, 0, -1, xa, true, abort};
-                    const float n2 = __builtin_sqrtf(__uint_as_float(n2b));
-                    int cur = kERowAnchor;  // e row of the current step
-                    for (; r.k < gamma && !r.fail; ++r.k) {
-                        const int k = r.k;
-                        if (!r.valid) continue;
-                        const float es = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_esq), cur));
-                        const uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)l_ab, k);
-                        const float tmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_tmax), k));
-                        const float win = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_win), k));
-                        const float beta = n2 * __builtin_sqrtf(es) * kBetaSlack + kBetaFloor;
-                        const float eps = 5.f * kUlp * (__uint_as_float(ab) + beta);
-                        const double thr = (double)tmax - 2.0 * ((double)beta + eps);
-                        const uint32_t cut = (uint32_t)__builtin_amdgcn_readlane((int)l_cut, k);
-                        const bool ok = __builtin_amdgcn_readlane(l_ovf, k) == 0 && finite_bits(ab) &&
-                                        finite_bits(n2b) && finite_bits(bound_bits(es)) &&
-                                        tmax > -__builtin_inff() && thr >= (double)win && key_upper(cut) < thr;
-                        if (!ok) {
-                            r.fail = true;
-                            break;
-                        }
-                        const bool cand = cs == k && (double)ct >= thr;
-                        const float lg = cu + (cand ? sc.bias[lane & (kCandMax - 1)][cur] : 0.f);
-                        const uint64_t key = cand ? argmax_key(G ? lg + cg : lg, cv) : 0;
-                        const uint64_t best = wave_max_u64(key);
-                        if (best == 0) {  // cannot happen: the best listed row is always a candidate
-                            r.fail = true;
-                            break;
-                        }
-                        const int jw = __builtin_ctzll(__ballot(key == best && cand));
-                        const int32_t tok = key_token(best);
-                        if (lane == k) r.pst = cur, r.tk = tok;
-                        const int32_t f = __builtin_amdgcn_readlane(l_fv, k);
-                        r.x = f >= 0 ? f : tok;
-                        r.valid = r.x >= 0 && r.x < V;
-                        cur = f >= 0 ? kERowForced + k : jw;
+            const auto walk = [&]() {
+                Walk w{0, 0, -1, xa, true, sc.abort != 0};
+                int cur = kERowAnchor;  // e row of the current step
+                for (; w.k < gamma && !w.fail; ++w.k) {
+                    const int k = w.k;
+                    if (!w.valid) continue;
+                    const int j = sc.tj[k][cur];
+                    if (j < 0) {
+                        w.fail = true;
+                        break;
                     }
-                    return r;
-                };
-                const float guess = __uint_as_float(sc.n2s) * kN2Guess;
-                wk = walk(bound_bits(guess));
-                // the real norm: waves 4-7 post it before the barrier below
-                __builtin_amdgcn_s_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-                const uint32_t n2b = sc.n2;
-                if (sc.abort || !(__uint_as_float(n2b) <= guess)) wk = walk(n2b);
-            } else {
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-                __builtin_amdgcn_s_barrier();
+                    const int32_t tok = sc.ttok[k][cur];
+                    if (lane == k) w.pst = cur, w.tk = tok;
+                    const int32_t f = sc.fv[k];
+                    w.x = f >= 0 ? f : tok;
+                    w.valid = w.x >= 0 && w.x < V;
+                    cur = f >= 0 ? kERowForced + k : j;
+                }
+                return w;
+            };
+            const float guess = __uint_as_float(sc.n2s) * kN2Guess;
+            build(bound_bits(guess));
+            __syncthreads();
+            Walk wk{};
+            if (wave == 0) wk = walk();
+            if (poller) {
+                uint64_t w = nword;
+                for (int spin = 0; spin < kChainSpinLimit && w == 0; ++spin) {
+                    __builtin_amdgcn_s_sleep(1);
+                    w = __hip_atomic_load(npw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                if (w == 0) sc.abort = 1;
+                atomicMax(&sc.n2, (uint32_t)w);
+            }
+            __syncthreads();
+            const uint32_t n2b = sc.n2;
+            if (sc.abort || !(__uint_as_float(n2b) <= guess)) {  // workgroup-uniform
+                build(n2b);
+                __syncthreads();
+                if (wave == 0) wk = walk();
             }
             // every row workgroup has posted its norm, so all have read the go-ahead
             if (tid >= kChainThreads - kCopies)

@@ -45,6 +45,8 @@ def _load():
         lib.oracle_accept_rate.argtypes = [i64, i64, ctypes.c_int, vp, i64, vp, i64, vp, vp]
         lib.oracle_prefix_schedule.restype = ctypes.c_int
         lib.oracle_prefix_schedule.argtypes = [i64, i64, vp, vp, i64, vp, vp, vp, vp, vp]
+        lib.oracle_verify.restype = ctypes.c_int
+        lib.oracle_verify.argtypes = [i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -144,4 +146,39 @@ def prefix_schedule(conf, sps):
         raise ValueError("oracle_prefix_schedule: need B >= 1 and a table of at least B entries")
     out["theta"] = float(th[0])
     out["n_selected"] = int(ns[0])
+    return out
+
+
+def verify(d, t, x, u, G, n_draft=None):
+    """Rejection-sampling verification of one draft block per request (fp64).
+
+    d [B, gamma, V] and t [B, gamma + 1, V] float32 or bfloat16 bits, x
+    [B, gamma] int32 drafted tokens, u [B, gamma] float32 uniforms in [0, 1),
+    G [B, V] float32 Gumbel noise, n_draft [B] int32 or None (= gamma).
+    Returns dict(n_acc, next_token, accept_prob [B, gamma], margin,
+    sample_pos, residual)."""
+    d = np.ascontiguousarray(d)
+    t = np.ascontiguousarray(t)
+    dt = _dtype_of(d)
+    assert _dtype_of(t) == dt
+    B, gamma, V = d.shape
+    assert t.shape == (B, gamma + 1, V)
+    x = np.ascontiguousarray(x, dtype=np.int32)
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    G = np.ascontiguousarray(G, dtype=np.float32)
+    assert x.shape == (B, gamma) and u.shape == (B, gamma) and G.shape == (B, V)
+    if n_draft is not None:
+        n_draft = np.ascontiguousarray(n_draft, dtype=np.int32)
+        assert n_draft.shape == (B,)
+    out = {
+        "n_acc": np.empty(B, np.int32),
+        "next_token": np.empty(B, np.int32),
+        "accept_prob": np.empty((B, gamma), np.float64),
+        "margin": np.empty(B, np.float64),
+        "sample_pos": np.empty(B, np.int32),
+        "residual": np.empty(B, np.int32),
+    }
+    _load().oracle_verify(B, gamma, V, dt, _p(d), _p(t), _p(x), _p(n_draft), _p(u), _p(G), _p(out["n_acc"]),
+                          _p(out["next_token"]), _p(out["accept_prob"]), _p(out["margin"]), _p(out["sample_pos"]),
+                          _p(out["residual"]))
     return out

@@ -239,3 +239,111 @@ int oracle_prefix_schedule(int64_t B, int64_t gamma, const float* conf, const do
     free(ord);
     return 0;
 }
+
+/*
+ * Rejection-sampling verification of one draft block per request ([W] 8.2:
+ * accept a drafted token with probability min(1, p_target / p_draft); on a
+ * rejection drop it and every later one and sample the next token from the
+ * residual max(0, p_target - p_draft); [W] 2.1: the target then adds one
+ * bonus token after an accepted prefix).
+ *
+ * Layouts: d [B][gamma][V] draft logits, t [B][gamma + 1][V] target logits,
+ * x [B][gamma] drafted tokens, n_draft [B] drafted positions to verify (NULL:
+ * gamma; values outside [0, gamma] are clamped), u [B][gamma] uniforms in
+ * [0, 1), G [B][V] Gumbel noise for the one sample each request draws.
+ *
+ * For request b with n drafted tokens, and k = 1..n in order:
+ *   p_d = softmax(d[b,k,:]), p_t = softmax(t[b,k,:]);
+ *   x_k is accepted iff u[b,k] * p_d(x_k) < p_t(x_k), i.e. u < min(1, p_t/p_d)
+ *   for p_d(x_k) > 0 (a token outside [0, V) is rejected);
+ *   the first rejection at k ends the walk: the emitted token is a sample
+ *   from the residual at position k,
+ *       argmax over v with p_t(v) > p_d(v) of  log(p_t(v) - p_d(v)) + G[b,v]
+ *   (Gumbel-max over the normalised residual; an empty residual falls back
+ *   to p_t itself).
+ * If all n are accepted the emitted token is the bonus sample from p_t at
+ * position n + 1: argmax of t[b,n+1,v] + G[b,v].  The argmax is decided in
+ * binary32 on each fp64 score rounded once; ties go to the lowest id.
+ *
+ * Outputs: n_acc [B], next_tok [B], and optionally accept_prob [B][gamma]
+ * (min(1, p_t(x_k)/p_d(x_k)) for k <= n, 0 for an invalid token, NaN past
+ * n), margin [B] (top1 - top2 of the emitted sample's binary32 scores),
+ * sample_pos [B] (0-based position of the sample) and residual [B] (1 when
+ * the sample came from a residual).
+ */
+static double lse_row(const void* p, int dtype, int64_t off, int64_t V) {
+    double m = -INFINITY, s = 0.0;
+    for (int64_t v = 0; v < V; ++v) {
+        double a = val(p, dtype, off + v);
+        if (a > m) m = a;
+    }
+    for (int64_t v = 0; v < V; ++v) s += exp(val(p, dtype, off + v) - m);
+    return m + log(s);
+}
+
+int oracle_verify(int64_t B, int64_t gamma, int64_t V, int dtype, const void* d, const void* t, const int32_t* x,
+                  const int32_t* n_draft, const float* u, const float* G, int32_t* n_acc, int32_t* next_tok,
+                  double* accept_prob, double* margin, int32_t* sample_pos, int32_t* residual) {
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t n = n_draft ? n_draft[b] : gamma;
+        if (n < 0) n = 0;
+        if (n > gamma) n = gamma;
+        if (accept_prob)
+            for (int64_t k = 0; k < gamma; ++k) accept_prob[b * gamma + k] = NAN;
+        int64_t k = 0, pos = n;
+        int res = 0;
+        double Ld = 0.0, Lt = 0.0;
+        for (; k < n; ++k) {
+            const int64_t od = (b * gamma + k) * V, ot = (b * (gamma + 1) + k) * V;
+            const double ld = lse_row(d, dtype, od, V), lt = lse_row(t, dtype, ot, V);
+            const int32_t xk = x[b * gamma + k];
+            int ok = 0;
+            double a = 0.0;
+            if (xk >= 0 && xk < V) {
+                const double pd = exp(val(d, dtype, od + xk) - ld), pt = exp(val(t, dtype, ot + xk) - lt);
+                a = pd > 0.0 ? (pt / pd < 1.0 ? pt / pd : 1.0) : (pt > 0.0 ? 1.0 : 0.0);
+                ok = (double)u[b * gamma + k] * pd < pt;
+            }
+            if (accept_prob) accept_prob[b * gamma + k] = a;
+            if (!ok) {
+                pos = k, res = 1, Ld = ld, Lt = lt;
+                break;
+            }
+        }
+        n_acc[b] = (int32_t)k;
+        /* the sample: residual at the rejected position, else the bonus */
+        const int64_t ot = (b * (gamma + 1) + pos) * V, od = (b * gamma + pos) * V;
+        int have = 0;
+        float best = 0.f, second = -INFINITY;
+        int32_t tok = -1;
+        for (int pass = 0; pass < 2 && !have; ++pass) {
+            /* pass 0: the residual (only after a rejection); pass 1: p_t */
+            if (pass == 0 && !res) continue;
+            best = -INFINITY, second = -INFINITY, tok = -1;
+            for (int64_t v = 0; v < V; ++v) {
+                double sc;
+                if (pass == 0) {
+                    const double r = exp(val(t, dtype, ot + v) - Lt) - exp(val(d, dtype, od + v) - Ld);
+                    if (!(r > 0.0)) continue;
+                    sc = log(r) + (double)G[b * V + v];
+                } else {
+                    sc = val(t, dtype, ot + v) + (double)G[b * V + v];
+                }
+                const float f = (float)sc;
+                if (tok < 0 || f > best) {
+                    if (tok >= 0) second = best;
+                    best = f, tok = (int32_t)v;
+                } else if (f > second) {
+                    second = f;
+                }
+                have = 1;
+            }
+            if (pass == 0 && !have) res = 0; /* empty residual: sample p_t at this position */
+        }
+        next_tok[b] = tok;
+        if (margin) margin[b] = (double)best - (double)second;
+        if (sample_pos) sample_pos[b] = (int32_t)pos;
+        if (residual) residual[b] = res;
+    }
+    return 0;
+}

@@ -400,3 +400,145 @@ def test_schedule_invariants_on_training_workload():
         r, j = divmod(int(pid), s.gamma)
         assert j < ell[r]
     assert 0 < o["n_selected"] < s.B * s.gamma  # the step-rate curve stops early
+
+
+# ---------------------------------------------------------------------------
+# rejection-sampling verification ([W] 8.2)
+# ---------------------------------------------------------------------------
+def _softmax64(z):
+    z = np.asarray(z, np.float64)
+    e = np.exp(z - z.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def _emitted(out, x, n):
+    """The emitted sequence of each request: accepted drafts, then the sample."""
+    seqs = []
+    for b in range(len(out["n_acc"])):
+        a = int(out["n_acc"][b])
+        seqs.append(list(x[b, :a]) + [int(out["next_token"][b])])
+    return seqs
+
+
+@pytest.mark.parametrize("gamma", [1, 2])
+def test_verify_emits_the_target_distribution(gamma):
+    """The theorem [W] 8.2 states: with x_k ~ p_d, the first emitted token
+    follows p_t at position 1 exactly, and given x_1 accepted the next
+    emitted token follows p_t at position 2.  Chi-square over 240,000
+    Monte Carlo draws (drafts from numpy's sampler, not the oracle's)."""
+    rng = _rng(81 + gamma)
+    V, M = 4, 240_000
+    d1 = rng.normal(0, 1.2, (gamma, V))
+    t1 = rng.normal(0, 1.2, (gamma + 1, V))
+    pd, pt = _softmax64(d1), _softmax64(t1)
+    x = np.stack([rng.choice(V, size=M, p=pd[k]) for k in range(gamma)], axis=1).astype(np.int32)
+    d = np.broadcast_to(d1.astype(np.float32), (M, gamma, V))
+    t = np.broadcast_to(t1.astype(np.float32), (M, gamma + 1, V))
+    u = rng.random((M, gamma)).astype(np.float32)
+    G = rng.gumbel(size=(M, V)).astype(np.float32)
+    out = oracle.verify(d, t, x, u, G)
+    seqs = _emitted(out, x, gamma)
+    first = np.array([s[0] for s in seqs])
+    counts = np.bincount(first, minlength=V)
+    chi2 = np.sum((counts - M * pt[0]) ** 2 / (M * pt[0]))
+    assert stats.chi2.sf(chi2, df=V - 1) > 1e-3, (chi2, counts / M, pt[0])
+    # second emitted token given the first draft was accepted
+    acc = out["n_acc"] >= 1
+    second = np.array([s[1] for s, a in zip(seqs, acc) if a])
+    m = len(second)
+    counts2 = np.bincount(second, minlength=V)
+    chi2 = np.sum((counts2 - m * pt[1]) ** 2 / (m * pt[1]))
+    assert stats.chi2.sf(chi2, df=V - 1) > 1e-3, (chi2, counts2 / m, pt[1])
+    # the acceptance frequency of x_1 is sum_v min(p_d, p_t) (the accept rate)
+    assert abs(acc.mean() - np.minimum(pd[0], pt[0]).sum()) < 4e-3
+
+
+def test_verify_worked_by_hand():
+    """V = 3, p_d = (0.5, 0.3, 0.2), p_t = (0.2, 0.3, 0.5), x_1 = 0:
+    accept iff u < 0.4; the residual max(0, p_t - p_d) = (0, 0, 0.3) leaves
+    token 2 whatever the noise."""
+    ld = np.log([0.5, 0.3, 0.2]).astype(np.float32)
+    lt = np.log([0.2, 0.3, 0.5]).astype(np.float32)
+    d = np.tile(ld, (3, 1, 1))
+    t = np.stack([np.stack([lt, lt])] * 3)  # position 2 = the same distribution
+    x = np.zeros((3, 1), np.int32)
+    u = np.array([[0.3], [0.5], [0.39]], np.float32)
+    G = np.array([[9.0, 0.0, 0.0], [9.0, 0.0, 0.0], [0.0, 0.0, 9.0]], np.float32)
+    out = oracle.verify(d, t, x, u, G)
+    assert list(out["n_acc"]) == [1, 0, 1]
+    np.testing.assert_allclose(out["accept_prob"][:, 0], 0.4, rtol=1e-6)
+    assert out["next_token"][1] == 2 and out["residual"][1] == 1  # residual: token 2 only
+    # accepted: bonus = argmax(t[1] + G): token 0 for row 0 (log .2 + 9), token 2 for row 2
+    assert out["next_token"][0] == 0 and out["next_token"][2] == 2
+    assert list(out["sample_pos"]) == [1, 0, 1]
+
+
+def test_verify_identical_distributions_accept_everything():
+    rng = _rng(90)
+    B, gamma, V = 6, 5, 37
+    t = rng.normal(0, 2, (B, gamma + 1, V)).astype(np.float32)
+    d = np.ascontiguousarray(t[:, :gamma])
+    x = rng.integers(0, V, (B, gamma)).astype(np.int32)
+    u = (rng.random((B, gamma)) * 0.999).astype(np.float32)
+    G = rng.gumbel(size=(B, V)).astype(np.float32)
+    n = np.array([5, 4, 0, 1, 3, 5], np.int32)
+    out = oracle.verify(d, t, x, u, G, n_draft=n)
+    assert np.array_equal(out["n_acc"], n)
+    bonus = np.argmax(t[np.arange(B), n] + G, axis=1)  # float32 scores
+    assert np.array_equal(out["next_token"], bonus)
+    assert np.array_equal(out["sample_pos"], n) and not out["residual"].any()
+    for b in range(B):
+        np.testing.assert_allclose(out["accept_prob"][b, : n[b]], 1.0)
+        assert np.all(np.isnan(out["accept_prob"][b, n[b]:]))
+
+
+def test_verify_rejections_zero_target_invalid_token_and_empty_residual():
+    rng = _rng(91)
+    B, gamma, V = 4, 3, 16
+    t = rng.normal(0, 1, (B, gamma + 1, V)).astype(np.float32)
+    d = np.ascontiguousarray(t[:, :gamma]).copy()
+    x = rng.integers(0, V, (B, gamma)).astype(np.int32)
+    u = np.full((B, gamma), 0.5, np.float32)
+    G = rng.gumbel(size=(B, V)).astype(np.float32)
+    t[0, 1, x[0, 1]] = -np.inf        # p_t(x) = 0: rejected at position 2, even for u = 0
+    u[0, 1] = 0.0                     # (0 * p_d < 0 is false: the test is strict)
+    x[1, 0] = V                       # out of range: rejected at position 1
+    x[2, 2] = -1                      # rejected at position 3
+    d[3, 0, :] = rng.normal(0, 1, V)  # differs: a real residual exists at position 1
+    u[3, 0] = 0.99999
+    out = oracle.verify(d, t, x, u, G)
+    assert out["n_acc"][0] == 1 and out["sample_pos"][0] == 1 and out["accept_prob"][0, 1] == 0.0
+    # d == t at the rejected positions of requests 1 and 2: the residual is empty,
+    # so the sample falls back to p_t there
+    for b, k in ((1, 0), (2, 2)):
+        assert out["n_acc"][b] == k and out["residual"][b] == 0
+        assert out["next_token"][b] == np.argmax(t[b, k] + G[b])
+    # request 0: removing x's target mass raises every other p_t above p_d, so
+    # the residual is p_t - p_d on all tokens but x
+    assert out["residual"][0] == 1 and out["next_token"][0] != x[0, 1]
+    r = _softmax64(t[0, 1]) - _softmax64(d[0, 1])
+    sc = np.where(r > 0, np.log(np.where(r > 0, r, 1)) + G[0], -np.inf).astype(np.float32)
+    assert out["next_token"][0] == int(np.argmax(sc))
+    # request 3: if x_1 was rejected, the sample lies where p_t > p_d
+    if out["n_acc"][3] == 0:
+        assert out["residual"][3] == 1
+        v = out["next_token"][3]
+        assert _softmax64(t[3, 0])[v] > _softmax64(d[3, 0])[v]
+
+
+def test_verify_residual_sample_is_gumbel_max_of_log_residual():
+    """Brute force of the residual draw on one rejected position."""
+    rng = _rng(92)
+    V = 50
+    d = rng.normal(0, 1, (1, 1, V)).astype(np.float32)
+    t = rng.normal(0, 1, (1, 2, V)).astype(np.float32)
+    pd, pt = _softmax64(d[0, 0]), _softmax64(t[0, 0])
+    x = np.array([[int(np.argmax(pd / pt))]], np.int32)  # the least acceptable token
+    u = np.array([[0.999]], np.float32)
+    for seed in range(20):
+        G = rng.gumbel(size=(1, V)).astype(np.float32)
+        out = oracle.verify(d, t, x, u, G)
+        assert out["n_acc"][0] == 0 and out["residual"][0] == 1
+        r = pt - pd
+        sc = np.where(r > 0, np.log(np.where(r > 0, r, 1)) + G[0], -np.inf).astype(np.float32)
+        assert out["next_token"][0] == int(np.argmax(sc)), seed

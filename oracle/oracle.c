@@ -266,8 +266,8 @@ int oracle_prefix_schedule(int64_t B, int64_t gamma, const float* conf, const do
  * binary32 on each fp64 score rounded once; ties go to the lowest id.
  *
  * Outputs: n_acc [B], next_tok [B], and optionally accept_prob [B][gamma]
- * (min(1, p_t(x_k)/p_d(x_k)) for k <= n, 0 for an invalid token, NaN past
- * n), margin [B] (top1 - top2 of the emitted sample's binary32 scores),
+ * (min(1, p_t(x_k)/p_d(x_k)) for every drafted k <= n, also past the first
+ * rejection; 0 for an invalid token, NaN past n), margin [B] (top1 - top2 of the emitted sample's binary32 scores),
  * sample_pos [B] (0-based position of the sample) and residual [B] (1 when
  * the sample came from a residual).
  */
@@ -311,6 +311,20 @@ int oracle_verify(int64_t B, int64_t gamma, int64_t V, int dtype, const void* d,
             }
         }
         n_acc[b] = (int32_t)k;
+        /* the probabilities of the drafted tokens past a rejection are reported
+         * too (they take no part in the decisions) */
+        if (accept_prob)
+            for (int64_t j = k + 1; j < n; ++j) {
+                const int64_t od = (b * gamma + j) * V, ot = (b * (gamma + 1) + j) * V;
+                const int32_t xj = x[b * gamma + j];
+                double a = 0.0;
+                if (xj >= 0 && xj < V) {
+                    const double pd = exp(val(d, dtype, od + xj) - lse_row(d, dtype, od, V));
+                    const double pt = exp(val(t, dtype, ot + xj) - lse_row(t, dtype, ot, V));
+                    a = pd > 0.0 ? (pt / pd < 1.0 ? pt / pd : 1.0) : (pt > 0.0 ? 1.0 : 0.0);
+                }
+                accept_prob[b * gamma + j] = a;
+            }
         /* the sample: residual at the rejected position, else the bonus */
         const int64_t ot = (b * (gamma + 1) + pos) * V, od = (b * gamma + pos) * V;
         int have = 0;

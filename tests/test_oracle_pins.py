@@ -508,6 +508,8 @@ def test_verify_rejections_zero_target_invalid_token_and_empty_residual():
     u[3, 0] = 0.99999
     out = oracle.verify(d, t, x, u, G)
     assert out["n_acc"][0] == 1 and out["sample_pos"][0] == 1 and out["accept_prob"][0, 1] == 0.0
+    # probabilities past the rejection are still reported, none past n
+    assert np.all(np.isfinite(out["accept_prob"])) and out["accept_prob"][1, 0] == 0.0
     # d == t at the rejected positions of requests 1 and 2: the residual is empty,
     # so the sample falls back to p_t there
     for b, k in ((1, 0), (2, 2)):

@@ -9,6 +9,7 @@ Entry points (same names as the C ABI):
   head_sample      Markov-head block sampler + confidence head + survival
   accept_rate      analytic accept rate 1 - 1/2 ||softmax(d) - softmax(t)||_1
   prefix_schedule  hardware-aware prefix scheduler (Algorithm 1)
+  verify           rejection-sampling verification of a draft block
 """
 from __future__ import annotations
 
@@ -58,6 +59,10 @@ def lib() -> ctypes.CDLL:
     L.dspark_accept_rate_workspace_size.argtypes = [i64, i64, i32]
     L.dspark_prefix_schedule_workspace_size.restype = sz
     L.dspark_prefix_schedule_workspace_size.argtypes = [i64, i64]
+    L.dspark_verify.restype = i32
+    L.dspark_verify.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dspark_verify_workspace_size.restype = sz
+    L.dspark_verify_workspace_size.argtypes = [i64, i64, i64, i32]
     _lib = L
     return L
 
@@ -223,6 +228,44 @@ def prefix_schedule(conf, sps, *, want_order=True, workspace=None):
     Returns dict(prefix_len [B] int32, survival [B, gamma] float32,
     order [B*gamma] int32, theta [1] float64, n_selected [1] int32)."""
     call, outs = prepare_prefix_schedule(conf, sps, want_order=want_order, workspace=workspace)
+    call()
+    outs.pop("_workspace")
+    return outs
+
+
+def prepare_verify(draft, target, draft_tokens, uniforms, gumbel, n_draft=None, *, want_accept_prob=False,
+                   workspace=None, stream=None):
+    B, gp1, V = target.shape
+    gamma = gp1 - 1
+    dt = _dtype_code(target)
+    dev = target.device
+    outs = {
+        "n_accepted": torch.empty(B, dtype=torch.int32, device=dev),
+        "next_token": torch.empty(B, dtype=torch.int32, device=dev),
+        "accept_prob": torch.empty((B, gamma), dtype=torch.float32, device=dev) if want_accept_prob else None,
+    }
+    ws, wsb = _workspace(int(lib().dspark_verify_workspace_size(B, gamma, V, dt)), dev, workspace)
+    args = (B, gamma, V, dt, _dev(draft, "draft", target.dtype, (B, gamma, V)), _dev(target, "target"),
+            _dev(draft_tokens, "draft_tokens", torch.int32, (B, gamma)), _opt(n_draft, "n_draft", torch.int32, (B,)),
+            _dev(uniforms, "uniforms", torch.float32, (B, gamma)), _dev(gumbel, "gumbel", torch.float32, (B, V)),
+            _dev(outs["n_accepted"], "n_accepted"), _dev(outs["next_token"], "next_token"),
+            _opt(outs["accept_prob"], "accept_prob"), None if ws is None else ws.data_ptr(), wsb,
+            _stream(dev) if stream is None else stream)
+    fn = partial(lib().dspark_verify, *args)
+    outs["_workspace"] = ws
+    return (lambda: _check("dspark_verify", fn())), outs
+
+
+def verify(draft, target, draft_tokens, uniforms, gumbel, n_draft=None, *, want_accept_prob=False, workspace=None):
+    """Rejection-sampling verification of one draft block per request.
+
+    draft [B, gamma, V] and target [B, gamma + 1, V] logits (float32 or
+    bfloat16), draft_tokens [B, gamma] int32, uniforms [B, gamma] float32 in
+    [0, 1), gumbel [B, V] float32, n_draft [B] int32 or None (= gamma).
+    Returns dict(n_accepted [B], next_token [B], accept_prob [B, gamma] or
+    None)."""
+    call, outs = prepare_verify(draft, target, draft_tokens, uniforms, gumbel, n_draft,
+                                want_accept_prob=want_accept_prob, workspace=workspace)
     call()
     outs.pop("_workspace")
     return outs

@@ -93,6 +93,38 @@ DSPARK_EXPORT dspark_status_t dspark_prefix_schedule(int64_t B, int64_t gamma, c
                                                      static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+constexpr int64_t kMaxVerifyRequests = 65535;  // grid.y of the sampling launch
+constexpr int64_t kMaxVerifyGamma = 4096;      // the sample's position travels in 16 bits
+
+bool verify_shape_ok(int64_t B, int64_t gamma, int64_t V) {
+    return B >= 0 && B <= kMaxVerifyRequests && gamma >= 0 && gamma <= kMaxVerifyGamma && V >= 1 && V <= kMaxV &&
+           mul_ok(B * (gamma + 1), V);
+}
+}  // namespace
+
+DSPARK_EXPORT dspark_status_t dspark_verify(int64_t B, int64_t gamma, int64_t V, int32_t dtype, const void* draft,
+                                            const void* target, const int32_t* draft_tokens, const int32_t* n_draft,
+                                            const float* uniforms, const float* gumbel, int32_t* n_accepted,
+                                            int32_t* next_token, float* accept_prob, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+    if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return DSPARK_ERR_BAD_DTYPE;
+    if (!verify_shape_ok(B, gamma, V)) return DSPARK_ERR_BAD_SHAPE;
+    if (B == 0) return DSPARK_OK;
+    dspark_status_t st = check_workspace(workspace, workspace_bytes, dspark::verify_workspace(B, gamma));
+    if (st != DSPARK_OK) return st;
+    if (!target || !gumbel || !n_accepted || !next_token || (gamma > 0 && (!draft || !draft_tokens || !uniforms)))
+        return DSPARK_ERR_NULL_ARG;
+    return hip_status(dspark::verify_launch(B, gamma, V, dtype, draft, target, draft_tokens, n_draft, uniforms, gumbel,
+                                            n_accepted, next_token, accept_prob, workspace,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+DSPARK_EXPORT size_t dspark_verify_workspace_size(int64_t B, int64_t gamma, int64_t V, int32_t) {
+    if (!verify_shape_ok(B, gamma, V)) return 0;
+    return dspark::verify_workspace(B, gamma);
+}
+
 DSPARK_EXPORT size_t dspark_head_sample_workspace_size(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r,
                                                        int32_t dtype) {
     if (!sampler_shape_ok(B, gamma, V, H, r)) return 0;

@@ -1,0 +1,342 @@
+// Rejection-sampling verification of one draft block per request
+// ("基于 DSpark 的投机解码训练框架原理与实现", wangjunjian.com: section 8.2,
+// the verification rule; section 2.1, the bonus token the target adds after
+// an accepted prefix).
+//
+// Request b drafted n = n_draft[b] tokens x_1..x_n.  Position k keeps x_k iff
+// u_k * p_d(x_k) < p_t(x_k), i.e. u_k < min(1, p_t(x_k) / p_d(x_k)), with
+// p_d = softmax(d[b,k,:]) and p_t = softmax(t[b,k,:]).  The first rejection
+// ends the block and the next token is drawn from the residual
+// max(0, p_t - p_d) at that position; when every drafted token is kept the
+// next token is the bonus draw from p_t at position n + 1.  Both draws are
+// Gumbel-max with the request's noise row G[b,:]:
+//   residual  argmax over v with p_t(v) > p_d(v) of ln(p_t(v) - p_d(v)) + G_v
+//   bonus     argmax of t[b,n+1,v] + G_v
+// (an empty residual falls back to the p_t draw at the same position).
+//
+// Four launches on the caller's stream:
+//   verify_stats   one workgroup per drafted (request, position): the two
+//                  rows' log-sum-exp (online max/sum, binary32) and the
+//                  probabilities of the drafted token
+//   verify_decide  one thread per request: the accept walk
+//   verify_sample  (vocabulary chunk, request) workgroups: the draw's packed
+//                  argmax key (score high, complemented id low) merged with
+//                  one 64-bit atomic max per workgroup and key
+//   verify_finish  one thread per request: decode the key; clear the
+//                  request's workspace words for the next call
+// Only the sampled position's rows are read twice; every other row once.
+#include "internal.h"
+
+namespace dspark {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kStatThreads = 1024;
+constexpr int kStatUnroll = 4;  // 16-byte vectors of each row in flight per thread
+constexpr int kSampleThreads = 256;
+constexpr int kSampleVecs = 4;  // vectors per thread per sampling workgroup
+constexpr int kReqThreads = 64;
+
+// Workspace: per (request, position) four binary32 words (the two rows'
+// log2-sum-exp in base 2 and p_d, p_t of the drafted token); per request the
+// sample's position and kind; per request two argmax keys (residual, p_t).
+constexpr size_t kStatWords = 4;
+
+size_t stats_bytes(int64_t B, int64_t gamma) { return ((size_t)(B * gamma) * kStatWords * 4 + 255) / 256 * 256; }
+size_t state_bytes(int64_t B) { return ((size_t)B * 4 + 255) / 256 * 256; }
+size_t keys_bytes(int64_t B) { return ((size_t)B * 16 + 255) / 256 * 256; }
+
+template <typename T>
+struct Vec;
+template <>
+struct Vec<float> {
+    static constexpr int N = 4;
+    __device__ static void unpack(const uint4& r, float (&x)[4]) {
+        x[0] = __uint_as_float(r.x), x[1] = __uint_as_float(r.y), x[2] = __uint_as_float(r.z),
+        x[3] = __uint_as_float(r.w);
+    }
+};
+template <>
+struct Vec<bf16_t> {
+    static constexpr int N = 8;
+    __device__ static void unpack(const uint4& r, float (&x)[8]) {
+        x[0] = widen_lo(r.x), x[1] = widen_hi(r.x), x[2] = widen_lo(r.y), x[3] = widen_hi(r.y);
+        x[4] = widen_lo(r.z), x[5] = widen_hi(r.z), x[6] = widen_lo(r.w), x[7] = widen_hi(r.w);
+    }
+};
+
+// Running (max, sum of exp(x - max)), folded in groups of n values.
+template <int N>
+__device__ __forceinline__ void fold(float& m, float& s, const float (&x)[N]) {
+    float bm = x[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) bm = fmaxf(bm, x[i]);
+    const float mn = fmaxf(m, bm);
+    const float mnl = mn * kLog2e;
+    float acc = (m == -INFINITY) ? 0.f : s * __builtin_amdgcn_exp2f(__builtin_fmaf(m, kLog2e, -mnl));
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc += exp_shifted(x[i], mnl);
+    s = mn == -INFINITY ? 0.f : acc;  // nothing but -inf so far: an empty sum
+    m = mn;
+}
+
+__device__ __forceinline__ void merge(float& m, float& s, float m2, float s2) {
+    const float mn = fmaxf(m, m2);
+    const float a = (m == -INFINITY) ? 0.f : s * __builtin_amdgcn_exp2f((m - mn) * kLog2e);
+    const float b = (m2 == -INFINITY) ? 0.f : s2 * __builtin_amdgcn_exp2f((m2 - mn) * kLog2e);
+    m = mn;
+    s = a + b;
+}
+
+template <int NT>
+__device__ void block_merge2(float& m1, float& s1, float& m2, float& s2, float* lds) {
+    for (int o = 32; o > 0; o >>= 1) {
+        merge(m1, s1, __shfl_xor(m1, o), __shfl_xor(s1, o));
+        merge(m2, s2, __shfl_xor(m2, o), __shfl_xor(s2, o));
+    }
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    if (l == 0) lds[4 * w] = m1, lds[4 * w + 1] = s1, lds[4 * w + 2] = m2, lds[4 * w + 3] = s2;
+    __syncthreads();
+    m1 = lds[0], s1 = lds[1], m2 = lds[2], s2 = lds[3];
+    for (int i = 1; i < NT / 64; ++i) merge(m1, s1, lds[4 * i], lds[4 * i + 1]), merge(m2, s2, lds[4 * i + 2], lds[4 * i + 3]);
+}
+
+__device__ __forceinline__ int32_t clamp_n(const int32_t* n_draft, int64_t b, int64_t gamma) {
+    int64_t n = n_draft ? n_draft[b] : gamma;
+    return (int32_t)(n < 0 ? 0 : n > gamma ? gamma : n);
+}
+
+// VEC: rows start on 16-byte boundaries and V is a whole number of vectors.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kStatThreads) void verify_stats(int64_t gamma, int64_t V, const T* __restrict__ d,
+                                                             const T* __restrict__ t, const int32_t* __restrict__ x,
+                                                             const int32_t* __restrict__ n_draft, float* stats,
+                                                             float* __restrict__ accept_prob) {
+    __shared__ float lds[4 * kStatThreads / 64];
+    const int64_t b = blockIdx.x / gamma, k = blockIdx.x % gamma;
+    const int tid = threadIdx.x;
+    if (k >= clamp_n(n_draft, b, gamma)) {  // not drafted: nothing to verify
+        if (tid == 0 && accept_prob) accept_prob[b * gamma + k] = __builtin_nanf("");
+        return;
+    }
+    const T* dr = d + (b * gamma + k) * V;
+    const T* tr = t + (b * (gamma + 1) + k) * V;
+    float md = -INFINITY, sd = 0.f, mt = -INFINITY, st = 0.f;
+    if (VEC) {
+        constexpr int E = Vec<T>::N;
+        const int64_t nvec = V / E;
+        const uint4* dv = reinterpret_cast<const uint4*>(dr);
+        const uint4* tv = reinterpret_cast<const uint4*>(tr);
+        for (int64_t base = 0; base < nvec; base += (int64_t)kStatThreads * kStatUnroll) {
+            // unconditional loads from clamped indices, masked afterwards: the
+            // compiler then waits for each vector as it is folded
+            uint4 rd[kStatUnroll], rt[kStatUnroll];
+            bool in[kStatUnroll];
+#pragma unroll
+            for (int j = 0; j < kStatUnroll; ++j) {
+                const int64_t i = base + tid + (int64_t)j * kStatThreads;
+                in[j] = i < nvec;
+                rd[j] = dv[in[j] ? i : 0];
+                rt[j] = tv[in[j] ? i : 0];
+            }
+#pragma unroll
+            for (int j = 0; j < kStatUnroll; ++j) {
+                float xd[E], xt[E];
+                Vec<T>::unpack(rd[j], xd);
+                Vec<T>::unpack(rt[j], xt);
+                float md2 = md, sd2 = sd, mt2 = mt, st2 = st;
+                fold<E>(md2, sd2, xd);
+                fold<E>(mt2, st2, xt);
+                md = in[j] ? md2 : md, sd = in[j] ? sd2 : sd;
+                mt = in[j] ? mt2 : mt, st = in[j] ? st2 : st;
+            }
+        }
+    } else {
+        for (int64_t v = tid; v < V; v += kStatThreads) {
+            float xd[1] = {load_elem(dr, v)}, xt[1] = {load_elem(tr, v)};
+            fold<1>(md, sd, xd);
+            fold<1>(mt, st, xt);
+        }
+    }
+    block_merge2<kStatThreads>(md, sd, mt, st, lds);
+    if (tid == 0) {
+        const float cd = md * kLog2e + __builtin_amdgcn_logf(sd);  // log2 of the draft normaliser
+        const float ct = mt * kLog2e + __builtin_amdgcn_logf(st);
+        const int32_t xk = x[b * gamma + k];
+        const bool valid = xk >= 0 && xk < V;
+        const float pd = valid ? exp_shifted(load_elem(dr, xk), cd) : 0.f;
+        const float pt = valid ? exp_shifted(load_elem(tr, xk), ct) : 0.f;
+        float* s = stats + (b * gamma + k) * kStatWords;
+        s[0] = cd, s[1] = ct, s[2] = pd, s[3] = pt;
+        if (accept_prob)
+            accept_prob[b * gamma + k] =
+                !valid ? 0.f : pd > 0.f ? fminf(1.f, pt / pd) : (pt > 0.f ? 1.f : 0.f);
+    }
+}
+
+// One thread per request: keep drafted tokens while u * p_d < p_t.
+__global__ __launch_bounds__(kReqThreads) void verify_decide(int64_t B, int64_t gamma, int64_t V,
+                                                            const int32_t* __restrict__ x,
+                                                            const int32_t* __restrict__ n_draft,
+                                                            const float* __restrict__ u, const float* stats,
+                                                            int32_t* state, int32_t* __restrict__ n_accepted) {
+    const int64_t b = (int64_t)blockIdx.x * kReqThreads + threadIdx.x;
+    if (b >= B) return;
+    const int32_t n = clamp_n(n_draft, b, gamma);
+    int32_t k = 0;
+    bool rejected = false;
+    for (; k < n; ++k) {
+        const int32_t xk = x[b * gamma + k];
+        const float* s = stats + (b * gamma + k) * kStatWords;
+        const bool keep = xk >= 0 && xk < V && u[b * gamma + k] * s[2] < s[3];
+        if (!keep) {
+            rejected = true;
+            break;
+        }
+    }
+    n_accepted[b] = k;
+    state[b] = k | (rejected ? (1 << 30) : 0);  // the sample's position and the residual flag
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kSampleThreads) void verify_sample(int64_t gamma, int64_t V, const T* __restrict__ d,
+                                                                const T* __restrict__ t, const float* __restrict__ G,
+                                                                const float* stats, const int32_t* state,
+                                                                uint64_t* keys) {
+    __shared__ uint64_t red[2][kSampleThreads / 64];
+    const int64_t b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int32_t st = state[b];
+    const int64_t pos = st & 0xffff;
+    const bool res = (st >> 30) & 1;
+    const T* tr = t + (b * (gamma + 1) + pos) * V;
+    const T* dr = d + (b * gamma + (res ? pos : 0)) * V;  // read only for a residual draw
+    const float* g = G + b * V;
+    const float cd = res ? stats[(b * gamma + pos) * kStatWords + 0] : 0.f;
+    const float ct = res ? stats[(b * gamma + pos) * kStatWords + 1] : 0.f;
+    uint64_t kr = 0, kt = 0;  // residual and p_t keys
+    auto consider = [&](float xt, float xd, float gv, int64_t v) {
+        kt = umax64(kt, argmax_key(xt + gv, (uint32_t)v));
+        if (res) {
+            const float r = exp_shifted(xt, ct) - exp_shifted(xd, cd);
+            const float sc = __builtin_fmaf(__builtin_amdgcn_logf(r), kLn2, gv);
+            kr = r > 0.f ? umax64(kr, argmax_key(sc, (uint32_t)v)) : kr;
+        }
+    };
+    if (VEC) {
+        constexpr int E = Vec<T>::N;
+        const int64_t nvec = V / E;
+        const int64_t v0 = (int64_t)blockIdx.x * kSampleThreads * kSampleVecs;
+        uint4 rt[kSampleVecs], rd[kSampleVecs];
+        float4 rg[kSampleVecs][E / 4];
+        bool in[kSampleVecs];
+#pragma unroll
+        for (int j = 0; j < kSampleVecs; ++j) {
+            const int64_t i = v0 + tid + (int64_t)j * kSampleThreads;
+            in[j] = i < nvec;
+            const int64_t ic = in[j] ? i : 0;
+            rt[j] = reinterpret_cast<const uint4*>(tr)[ic];
+            rd[j] = res ? reinterpret_cast<const uint4*>(dr)[ic] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < E / 4; ++q) rg[j][q] = reinterpret_cast<const float4*>(g)[ic * (E / 4) + q];
+        }
+#pragma unroll
+        for (int j = 0; j < kSampleVecs; ++j) {
+            if (!in[j]) continue;
+            float xt[E], xd[E];
+            Vec<T>::unpack(rt[j], xt);
+            Vec<T>::unpack(rd[j], xd);
+            const int64_t v = (v0 + tid + (int64_t)j * kSampleThreads) * E;
+#pragma unroll
+            for (int q = 0; q < E / 4; ++q) {
+                consider(xt[4 * q + 0], xd[4 * q + 0], rg[j][q].x, v + 4 * q + 0);
+                consider(xt[4 * q + 1], xd[4 * q + 1], rg[j][q].y, v + 4 * q + 1);
+                consider(xt[4 * q + 2], xd[4 * q + 2], rg[j][q].z, v + 4 * q + 2);
+                consider(xt[4 * q + 3], xd[4 * q + 3], rg[j][q].w, v + 4 * q + 3);
+            }
+        }
+    } else {
+        const int64_t span = (int64_t)kSampleThreads * kSampleVecs;
+        const int64_t v0 = (int64_t)blockIdx.x * span;
+        const int64_t v1 = v0 + span < V ? v0 + span : V;
+        for (int64_t v = v0 + tid; v < v1; v += kSampleThreads)
+            consider(load_elem(tr, v), res ? load_elem(dr, v) : 0.f, g[v], v);
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        kr = umax64(kr, (uint64_t)__shfl_xor((unsigned long long)kr, o));
+        kt = umax64(kt, (uint64_t)__shfl_xor((unsigned long long)kt, o));
+    }
+    if (lane == 0) red[0][wave] = kr, red[1][wave] = kt;
+    __syncthreads();
+    if (tid == 0) {
+        for (int w = 1; w < kSampleThreads / 64; ++w) kr = umax64(kr, red[0][w]), kt = umax64(kt, red[1][w]);
+        if (kr) atomicMax(reinterpret_cast<unsigned long long*>(keys + 2 * b), (unsigned long long)kr);
+        if (kt) atomicMax(reinterpret_cast<unsigned long long*>(keys + 2 * b + 1), (unsigned long long)kt);
+    }
+}
+
+// One thread per request: the residual draw if there was one with positive
+// mass, else the p_t draw; then the request's workspace words go back to zero.
+__global__ __launch_bounds__(kReqThreads) void verify_finish(int64_t B, int64_t gamma, float* stats, int32_t* state,
+                                                            uint64_t* keys, int32_t* __restrict__ next_token) {
+    const int64_t b = (int64_t)blockIdx.x * kReqThreads + threadIdx.x;
+    if (b >= B) return;
+    const bool res = (state[b] >> 30) & 1;
+    const uint64_t kr = keys[2 * b], kt = keys[2 * b + 1];
+    next_token[b] = key_token(res && kr != 0 ? kr : kt);
+    keys[2 * b] = 0, keys[2 * b + 1] = 0;
+    state[b] = 0;
+    for (int64_t i = 0; i < gamma * (int64_t)kStatWords; ++i) stats[b * gamma * kStatWords + i] = 0.f;
+}
+
+template <typename T>
+hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, const void* d, const void* t, const int32_t* x,
+                        const int32_t* n_draft, const float* u, const float* G, int32_t* n_accepted,
+                        int32_t* next_token, float* accept_prob, void* ws, hipStream_t stream) {
+    constexpr int E = Vec<T>::N;
+    const T* dp = static_cast<const T*>(d);
+    const T* tp = static_cast<const T*>(t);
+    const bool vec = V % E == 0 && (uintptr_t)d % 16 == 0 && (uintptr_t)t % 16 == 0 && (uintptr_t)G % 16 == 0;
+    char* w = static_cast<char*>(ws);
+    float* stats = reinterpret_cast<float*>(w);
+    int32_t* state = reinterpret_cast<int32_t*>(w + stats_bytes(B, gamma));
+    uint64_t* keys = reinterpret_cast<uint64_t*>(w + stats_bytes(B, gamma) + state_bytes(B));
+    if (gamma > 0) {
+        const dim3 grid((uint32_t)(B * gamma));
+        if (vec)
+            hipLaunchKernelGGL((verify_stats<T, true>), grid, dim3(kStatThreads), 0, stream, gamma, V, dp, tp, x,
+                               n_draft, stats, accept_prob);
+        else
+            hipLaunchKernelGGL((verify_stats<T, false>), grid, dim3(kStatThreads), 0, stream, gamma, V, dp, tp, x,
+                               n_draft, stats, accept_prob);
+    }
+    const dim3 rgrid((uint32_t)((B + kReqThreads - 1) / kReqThreads));
+    hipLaunchKernelGGL(verify_decide, rgrid, dim3(kReqThreads), 0, stream, B, gamma, V, x, n_draft, u, stats, state,
+                       n_accepted);
+    const int64_t span = vec ? (int64_t)kSampleThreads * kSampleVecs * E : (int64_t)kSampleThreads * kSampleVecs;
+    const dim3 sgrid((uint32_t)((V + span - 1) / span), (uint32_t)B);
+    if (vec)
+        hipLaunchKernelGGL((verify_sample<T, true>), sgrid, dim3(kSampleThreads), 0, stream, gamma, V, dp, tp, G,
+                           stats, state, keys);
+    else
+        hipLaunchKernelGGL((verify_sample<T, false>), sgrid, dim3(kSampleThreads), 0, stream, gamma, V, dp, tp, G,
+                           stats, state, keys);
+    hipLaunchKernelGGL(verify_finish, rgrid, dim3(kReqThreads), 0, stream, B, gamma, stats, state, keys, next_token);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t verify_workspace(int64_t B, int64_t gamma) { return stats_bytes(B, gamma) + state_bytes(B) + keys_bytes(B); }
+
+hipError_t verify_launch(int64_t B, int64_t gamma, int64_t V, int dtype, const void* d, const void* t,
+                         const int32_t* x, const int32_t* n_draft, const float* u, const float* G,
+                         int32_t* n_accepted, int32_t* next_token, float* accept_prob, void* ws, hipStream_t stream) {
+    if (dtype == kBF16)
+        return launch_typed<bf16_t>(B, gamma, V, d, t, x, n_draft, u, G, n_accepted, next_token, accept_prob, ws,
+                                    stream);
+    return launch_typed<float>(B, gamma, V, d, t, x, n_draft, u, G, n_accepted, next_token, accept_prob, ws, stream);
+}
+
+}  // namespace dspark

@@ -152,11 +152,53 @@ dspark_status_t dspark_prefix_schedule(int64_t B, int64_t gamma, const float* co
                                        double* theta_out, int32_t* n_selected_out, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/*
+ * dspark_verify -- rejection-sampling verification of one draft block per
+ * request ([W] 8.2: keep a drafted token with probability
+ * min(1, p_target / p_draft); at the first rejection drop it and every later
+ * one and draw the next token from the residual max(0, p_target - p_draft);
+ * [W] 2.1: after an accepted prefix the target adds one bonus token).
+ *
+ * For request b with n = n_draft[b] drafted tokens (NULL: n = gamma; values
+ * outside [0, gamma] are clamped) and k = 1..n in order, with
+ * p_d = softmax(draft[b][k-1][:]) and p_t = softmax(target[b][k-1][:]):
+ *   x_k = draft_tokens[b][k-1] is kept iff uniforms[b][k-1] * p_d(x_k) < p_t(x_k)
+ *   (a token outside [0, V) is rejected).
+ * n_accepted[b] = number of kept tokens.  next_token[b] is drawn with the
+ * Gumbel noise row gumbel[b][:]:
+ *   after a rejection at position j: argmax over v with p_t(v) > p_d(v) of
+ *     ln(p_t(v) - p_d(v)) + gumbel[b][v]   (the residual at position j; with
+ *     no such v, the p_t draw below at position j);
+ *   if all n are kept: argmax of target[b][n][v] + gumbel[b][v] (the bonus
+ *     token from p_t at position n + 1).
+ * Probabilities are binary32 with max-shifted exponentials; the argmax takes
+ * the lowest id among equal binary32 scores.
+ *
+ *   B in [0, 65535], gamma in [0, 4096], V >= 1 (V < 2^31); dtype of both
+ *   logit arrays.
+ *   draft         [B][gamma][V]      draft logits (may be NULL when gamma = 0)
+ *   target        [B][gamma + 1][V]  target logits
+ *   draft_tokens  [B][gamma] int32
+ *   n_draft       [B] int32, optional
+ *   uniforms      [B][gamma] fp32 in [0, 1)
+ *   gumbel        [B][V] fp32 (e.g. -ln(-ln u))
+ *   n_accepted    [B] int32 out;  next_token [B] int32 out
+ *   accept_prob   [B][gamma] fp32 out, optional: min(1, p_t(x_k)/p_d(x_k)) for
+ *                 k <= n (0 for an invalid token), NaN past n.
+ * The workspace (dspark_verify_workspace_size bytes) must be zero-filled
+ * before its first use; every completed call leaves it zero-filled again.
+ */
+dspark_status_t dspark_verify(int64_t B, int64_t gamma, int64_t V, int32_t dtype, const void* draft,
+                              const void* target, const int32_t* draft_tokens, const int32_t* n_draft,
+                              const float* uniforms, const float* gumbel, int32_t* n_accepted, int32_t* next_token,
+                              float* accept_prob, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes needed by the entry point of the same name for these
  * shapes; 0 if it needs none.  Pure host functions with no side effects. */
 size_t dspark_head_sample_workspace_size(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int32_t dtype);
 size_t dspark_accept_rate_workspace_size(int64_t N, int64_t V, int32_t dtype);
 size_t dspark_prefix_schedule_workspace_size(int64_t B, int64_t gamma);
+size_t dspark_verify_workspace_size(int64_t B, int64_t gamma, int64_t V, int32_t dtype);
 
 /* Static, NUL-terminated description of a status code. */
 const char* dspark_status_string(dspark_status_t status);

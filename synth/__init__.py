@@ -29,7 +29,8 @@ _lib = None
 
 # one master seed per workload, one tag per tensor
 SEED_BASE = 0xD5A20000
-TAG = {"W1": 1, "W2": 2, "U": 3, "h": 4, "w": 5, "x0": 6, "G": 7, "d": 8, "t": 9, "conf": 10, "sps": 11}
+TAG = {"W1": 1, "W2": 2, "U": 3, "h": 4, "w": 5, "x0": 6, "G": 7, "d": 8, "t": 9, "conf": 10, "sps": 11,
+       "vd": 12, "vt": 13, "vtb": 14, "vx": 15, "vu": 16, "vG": 17}
 
 
 def build(force: bool = True) -> str:
@@ -248,3 +249,41 @@ def sps_table(n_sps: int, kind: str = "tokens") -> np.ndarray:
     if kind == "steps":
         return 1.0 / t
     raise ValueError(kind)
+
+
+@dataclass
+class VerifyShape:
+    """Rejection-sampling verification inputs: draft logits d [B, gamma, V],
+    target logits t [B, gamma + 1, V] with t = scale*d + N(0, t_sd) at the
+    drafted positions and N(0, d_sd) at the bonus position, drafted tokens
+    uniform in [0, V), uniforms u [B, gamma] and Gumbel noise G [B, V]."""
+    B: int
+    gamma: int
+    V: int
+    dtype: str
+    d_sd: float
+    scale: float
+    t_sd: float
+    seed: int
+
+
+# the batched serving shape: 64 requests, gamma 7, the full vocabulary, bf16
+VERIFY_B64 = VerifyShape(B=64, gamma=7, V=151936, dtype="bf16", d_sd=3.0, scale=0.8, t_sd=1.5, seed=SEED_BASE + 6)
+VERIFY_TINY = VerifyShape(B=4, gamma=7, V=4096, dtype="f32", d_sd=2.0, scale=1.0, t_sd=0.5, seed=SEED_BASE + 7)
+
+
+def verify_inputs(s: VerifyShape, B: int | None = None) -> dict:
+    B = s.B if B is None else B
+    g, V = s.gamma, s.V
+    d = normal(key(s.seed, TAG["vd"]), (B, g, V), 0.0, s.d_sd, s.dtype)
+    t_draft = affine_noise(key(s.seed, TAG["vt"]), d, s.scale, 0.0, s.t_sd)
+    t_bonus = normal(key(s.seed, TAG["vtb"]), (B, 1, V), 0.0, s.d_sd, s.dtype)
+    t = np.ascontiguousarray(np.concatenate([t_draft, t_bonus], axis=1))
+    return dict(
+        d=d,
+        t=t,
+        x=uniform_int(key(s.seed, TAG["vx"]), (B, g), 0, V).astype(np.int32),
+        # rounded to binary32 and kept below 1 (the accept test needs u < 1)
+        u=np.minimum(uniform(key(s.seed, TAG["vu"]), (B, g)).astype(np.float32), np.float32(1 - 2**-24)),
+        G=gumbel(key(s.seed, TAG["vG"]), (B, V)).astype(np.float32),
+    )

@@ -107,3 +107,26 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(dh, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         dh.lib()
+
+
+def _vf(L, B=2, gamma=3, V=100, dtype=1, d=FAKE, t=FAKE, x=FAKE, n=None, u=FAKE, G=FAKE, na=FAKE, nt=FAKE, ws=None,
+        wsb=0):
+    return L.dspark_verify(B, gamma, V, dtype, d, t, x, n, u, G, na, nt, None, ws, wsb, None)
+
+
+def test_verify_host_checks(L):
+    need = L.dspark_verify_workspace_size(2, 3, 100, 1)
+    assert need > 0 and need % 256 == 0
+    assert L.dspark_verify_workspace_size(65536, 3, 100, 1) == 0
+    assert _vf(L, dtype=7) == BAD_DTYPE
+    assert _vf(L, B=65536) == BAD_SHAPE
+    assert _vf(L, gamma=4097) == BAD_SHAPE
+    assert _vf(L, V=0) == BAD_SHAPE
+    assert _vf(L, B=0) == OK  # nothing to do: nothing enqueued
+    assert _vf(L) == WORKSPACE  # no workspace
+    assert _vf(L, ws=FAKE * 256, wsb=need - 1) == WORKSPACE
+    for kw in ("t", "G", "na", "nt", "d", "x", "u"):
+        assert _vf(L, ws=FAKE * 256, wsb=need, **{kw: None}) == NULL_ARG, kw
+    # gamma = 0: only the target row of the bonus draw is needed
+    assert _vf(L, gamma=0, d=None, x=None, u=None, t=None, ws=FAKE * 256,
+               wsb=L.dspark_verify_workspace_size(2, 0, 100, 1)) == NULL_ARG

@@ -52,6 +52,20 @@ def accept_call_bytes(N, V, elem=2):
     return 2 * N * V * elem + 4 * N
 
 
+def verify_call_bytes(n_draft, all_kept, V, gamma, elem=2):
+    """Unique bytes of one verify call: the draft and target rows of every
+    drafted position once, the target row of the bonus position for requests
+    that kept every drafted token, each request's Gumbel row, and the small
+    per-position inputs and outputs.  (The rows of a rejected position are
+    read a second time for the residual draw; that is in `traffic`.)"""
+    import numpy as np
+
+    n = np.asarray(n_draft, np.int64)
+    B = n.size
+    rows = int(n.sum()) * 2 + int(np.asarray(all_kept).sum())
+    return rows * V * elem + B * V * 4 + B * gamma * 8 + B * 12
+
+
 def profiled_traffic(profile: str, sources: list[str]):
     """HBM bytes per launch measured by the FETCH_SIZE / WRITE_SIZE counter
     passes recorded in profiles/<profile>, or None when the kernel sources
@@ -76,6 +90,7 @@ def profiled_traffic(profile: str, sources: list[str]):
 
 
 SAMPLER_SOURCES = ["draft_head_sampling_amd/csrc/head_sample.hip", "draft_head_sampling_amd/csrc/internal.h"]
+VERIFY_SOURCES = ["draft_head_sampling_amd/csrc/verify.hip", "draft_head_sampling_amd/csrc/internal.h"]
 ACCEPT_SOURCES = ["draft_head_sampling_amd/csrc/accept_rate.hip", "draft_head_sampling_amd/csrc/internal.h"]
 
 
@@ -87,6 +102,7 @@ def main():
     ap.add_argument("--anchors", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-accept", action="store_true", help="skip the accept-rate measurement")
+    ap.add_argument("--no-verify", action="store_true", help="skip the rejection-sampling verify measurement")
     ap.add_argument("--extra", action="store_true", help="also time the B=64 sampler and the scheduler workload")
     ap.add_argument("--calib-copy", action="store_true", help="run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -238,6 +254,41 @@ def main():
                          "bytes_per_launch": a_bytes},
         }
         del D, T
+
+    # ---------------- rejection-sampling verify on the batched serving shape ----------------
+    if not args.no_verify:
+        sv = synth.VERIFY_B64
+        vin = synth.verify_inputs(sv)
+        vd = {k: to_dev(v, dev) for k, v in vin.items()}
+        del vin
+        vcall, vout = dh.prepare_verify(vd["d"], vd["t"], vd["x"], vd["u"], vd["G"])
+        for _ in range(3):
+            vcall()
+        torch.cuda.synchronize()
+        v0 = torch.cuda.Event(enable_timing=True)
+        v1 = torch.cuda.Event(enable_timing=True)
+        reps = 20
+        v0.record(stream)
+        for _ in range(reps):
+            vcall()
+        v1.record(stream)
+        torch.cuda.synchronize()
+        v_us = v0.elapsed_time(v1) * 1e3 / reps
+        n_acc = vout["n_accepted"].cpu().numpy()
+        v_bytes = verify_call_bytes([sv.gamma] * sv.B, n_acc == sv.gamma, sv.V, sv.gamma)
+        v_gbs = v_bytes / (v_us * 1e-6) / 1e9
+        line["verify"] = {
+            "workload": "rejection-sampling verify, B=64 requests x 7 drafted positions, V=151936 bf16 draft and "
+                        "target logits, fp32 uniforms and Gumbel rows",
+            "us_per_call": round(v_us, 2), "positions_per_s": round(sv.B * sv.gamma / (v_us * 1e-6), 1),
+            "mean_accepted": round(float(n_acc.mean()), 3),
+            "roofline": {"kernel": "dspark_verify (4 launches; verify_stats reads every drafted row)",
+                         "bound": "hbm", "achieved": round(v_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(v_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": profiled_traffic("verify_b64_vocab151936.md", VERIFY_SOURCES),
+                         "bytes_per_launch": v_bytes},
+        }
+        del vd
 
     if args.extra:
         s3 = synth.SAMPLER_B64

@@ -111,7 +111,7 @@ DSPARK_EXPORT dspark_status_t dspark_verify(int64_t B, int64_t gamma, int64_t V,
     if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return DSPARK_ERR_BAD_DTYPE;
     if (!verify_shape_ok(B, gamma, V)) return DSPARK_ERR_BAD_SHAPE;
     if (B == 0) return DSPARK_OK;
-    dspark_status_t st = check_workspace(workspace, workspace_bytes, dspark::verify_workspace(B, gamma));
+    dspark_status_t st = check_workspace(workspace, workspace_bytes, dspark::verify_workspace(B, gamma, V));
     if (st != DSPARK_OK) return st;
     if (!target || !gumbel || !n_accepted || !next_token || (gamma > 0 && (!draft || !draft_tokens || !uniforms)))
         return DSPARK_ERR_NULL_ARG;
@@ -122,7 +122,7 @@ DSPARK_EXPORT dspark_status_t dspark_verify(int64_t B, int64_t gamma, int64_t V,
 
 DSPARK_EXPORT size_t dspark_verify_workspace_size(int64_t B, int64_t gamma, int64_t V, int32_t) {
     if (!verify_shape_ok(B, gamma, V)) return 0;
-    return dspark::verify_workspace(B, gamma);
+    return dspark::verify_workspace(B, gamma, V);
 }
 
 DSPARK_EXPORT size_t dspark_head_sample_workspace_size(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r,

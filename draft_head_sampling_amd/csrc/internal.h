@@ -67,7 +67,7 @@ hipError_t head_sample_launch(int64_t B, int64_t gamma, int64_t V, int64_t H, in
                               float* conf, float* survival, float* logits_out, float* bias_out, void* ws,
                               hipStream_t stream);
 
-size_t verify_workspace(int64_t B, int64_t gamma);
+size_t verify_workspace(int64_t B, int64_t gamma, int64_t V);
 hipError_t verify_launch(int64_t B, int64_t gamma, int64_t V, int dtype, const void* d, const void* t,
                          const int32_t* x, const int32_t* n_draft, const float* u, const float* G,
                          int32_t* n_accepted, int32_t* next_token, float* accept_prob, void* ws, hipStream_t stream);

@@ -14,16 +14,16 @@
 //   bonus     argmax of t[b,n+1,v] + G_v
 // (an empty residual falls back to the p_t draw at the same position).
 //
-// Four launches on the caller's stream:
-//   verify_stats   one workgroup per drafted (request, position): the two
-//                  rows' log-sum-exp (online max/sum, binary32) and the
-//                  probabilities of the drafted token
-//   verify_decide  one thread per request: the accept walk
-//   verify_sample  (vocabulary chunk, request) workgroups: the draw's packed
-//                  argmax key (score high, complemented id low) merged with
-//                  one 64-bit atomic max per workgroup and key
-//   verify_finish  one thread per request: decode the key; clear the
-//                  request's workspace words for the next call
+// Two launches on the caller's stream:
+//   verify_stats   four workgroups per drafted (request, position) row pair:
+//                  each a quarter of both rows' online (max, sum of exp),
+//                  binary32
+//   verify_sample  (vocabulary chunk, request) workgroups: the accept walk
+//                  (one lane per position), then the chunk's part of the draw
+//                  as packed argmax keys (score high, complemented id low)
+//                  in the workgroup's own slot; the last workgroup of a
+//                  request to arrive merges the slots, decodes the token and
+//                  clears the request's workspace words for the next call
 // Only the sampled position's rows are read twice; every other row once.
 #include "internal.h"
 
@@ -32,20 +32,27 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kStatThreads = 1024;
+constexpr int kStatThreads = 512;
 constexpr int kStatUnroll = 4;  // 16-byte vectors of each row in flight per thread
 constexpr int kSampleThreads = 256;
 constexpr int kSampleVecs = 4;  // vectors per thread per sampling workgroup
-constexpr int kReqThreads = 64;
 
-// Workspace: per (request, position) four binary32 words (the two rows'
-// log2-sum-exp in base 2 and p_d, p_t of the drafted token); per request the
-// sample's position and kind; per request two argmax keys (residual, p_t).
+// Workspace: per (request, position, row split) the two rows' partial
+// (max, sum of exp) as four binary32 words; per (request, vocabulary chunk)
+// a slot of two argmax keys (residual, p_t); per request an arrival counter
+// of the sampling workgroups; one status word.
+constexpr int kSplit = 4;  // workgroups per (request, position) row pair
 constexpr size_t kStatWords = 4;
+constexpr uint64_t kNoKey = 1;  // a written slot word without a candidate (below every real key)
+constexpr int kSpinLimit = 1 << 22;
 
-size_t stats_bytes(int64_t B, int64_t gamma) { return ((size_t)(B * gamma) * kStatWords * 4 + 255) / 256 * 256; }
-size_t state_bytes(int64_t B) { return ((size_t)B * 4 + 255) / 256 * 256; }
-size_t keys_bytes(int64_t B) { return ((size_t)B * 16 + 255) / 256 * 256; }
+// vocabulary chunks of the sampling launch, at most (the unvectorised span)
+int64_t max_chunks(int64_t V) { return (V + kSampleThreads * kSampleVecs - 1) / (kSampleThreads * kSampleVecs); }
+size_t stats_bytes(int64_t B, int64_t gamma) {
+    return ((size_t)(B * gamma) * kSplit * kStatWords * 4 + 255) / 256 * 256;
+}
+size_t slots_bytes(int64_t B, int64_t V) { return ((size_t)B * max_chunks(V) * 16 + 255) / 256 * 256; }
+size_t count_bytes(int64_t B) { return ((size_t)(B + 1) * 4 + 255) / 256 * 256; }
 
 template <typename T>
 struct Vec;
@@ -107,28 +114,30 @@ __device__ __forceinline__ int32_t clamp_n(const int32_t* n_draft, int64_t b, in
     return (int32_t)(n < 0 ? 0 : n > gamma ? gamma : n);
 }
 
+// One workgroup per (request, drafted position, row split): the split's
+// partial (max, sum) of the draft row and of the target row.
 // VEC: rows start on 16-byte boundaries and V is a whole number of vectors.
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kStatThreads) void verify_stats(int64_t gamma, int64_t V, const T* __restrict__ d,
-                                                             const T* __restrict__ t, const int32_t* __restrict__ x,
-                                                             const int32_t* __restrict__ n_draft, float* stats,
-                                                             float* __restrict__ accept_prob) {
+                                                             const T* __restrict__ t,
+                                                             const int32_t* __restrict__ n_draft, float* stats) {
     __shared__ float lds[4 * kStatThreads / 64];
-    const int64_t b = blockIdx.x / gamma, k = blockIdx.x % gamma;
+    const int64_t row = blockIdx.x / kSplit;
+    const int sp = blockIdx.x % kSplit;
+    const int64_t b = row / gamma, k = row % gamma;
     const int tid = threadIdx.x;
-    if (k >= clamp_n(n_draft, b, gamma)) {  // not drafted: nothing to verify
-        if (tid == 0 && accept_prob) accept_prob[b * gamma + k] = __builtin_nanf("");
-        return;
-    }
+    if (k >= clamp_n(n_draft, b, gamma)) return;  // not drafted: nothing to verify
     const T* dr = d + (b * gamma + k) * V;
     const T* tr = t + (b * (gamma + 1) + k) * V;
     float md = -INFINITY, sd = 0.f, mt = -INFINITY, st = 0.f;
     if (VEC) {
         constexpr int E = Vec<T>::N;
         const int64_t nvec = V / E;
+        const int64_t per = (nvec + kSplit - 1) / kSplit;
+        const int64_t lo = sp * per, hi = lo + per < nvec ? lo + per : nvec;
         const uint4* dv = reinterpret_cast<const uint4*>(dr);
         const uint4* tv = reinterpret_cast<const uint4*>(tr);
-        for (int64_t base = 0; base < nvec; base += (int64_t)kStatThreads * kStatUnroll) {
+        for (int64_t base = lo; base < hi; base += (int64_t)kStatThreads * kStatUnroll) {
             // unconditional loads from clamped indices, masked afterwards: the
             // compiler then waits for each vector as it is folded
             uint4 rd[kStatUnroll], rt[kStatUnroll];
@@ -136,9 +145,9 @@ __global__ __launch_bounds__(kStatThreads) void verify_stats(int64_t gamma, int6
 #pragma unroll
             for (int j = 0; j < kStatUnroll; ++j) {
                 const int64_t i = base + tid + (int64_t)j * kStatThreads;
-                in[j] = i < nvec;
-                rd[j] = dv[in[j] ? i : 0];
-                rt[j] = tv[in[j] ? i : 0];
+                in[j] = i < hi;
+                rd[j] = dv[in[j] ? i : lo];
+                rt[j] = tv[in[j] ? i : lo];
             }
 #pragma unroll
             for (int j = 0; j < kStatUnroll; ++j) {
@@ -153,7 +162,9 @@ __global__ __launch_bounds__(kStatThreads) void verify_stats(int64_t gamma, int6
             }
         }
     } else {
-        for (int64_t v = tid; v < V; v += kStatThreads) {
+        const int64_t per = (V + kSplit - 1) / kSplit;
+        const int64_t lo = sp * per, hi = lo + per < V ? lo + per : V;
+        for (int64_t v = lo + tid; v < hi; v += kStatThreads) {
             float xd[1] = {load_elem(dr, v)}, xt[1] = {load_elem(tr, v)};
             fold<1>(md, sd, xd);
             fold<1>(mt, st, xt);
@@ -161,60 +172,96 @@ __global__ __launch_bounds__(kStatThreads) void verify_stats(int64_t gamma, int6
     }
     block_merge2<kStatThreads>(md, sd, mt, st, lds);
     if (tid == 0) {
-        const float cd = md * kLog2e + __builtin_amdgcn_logf(sd);  // log2 of the draft normaliser
-        const float ct = mt * kLog2e + __builtin_amdgcn_logf(st);
-        const int32_t xk = x[b * gamma + k];
-        const bool valid = xk >= 0 && xk < V;
-        const float pd = valid ? exp_shifted(load_elem(dr, xk), cd) : 0.f;
-        const float pt = valid ? exp_shifted(load_elem(tr, xk), ct) : 0.f;
-        float* s = stats + (b * gamma + k) * kStatWords;
-        s[0] = cd, s[1] = ct, s[2] = pd, s[3] = pt;
-        if (accept_prob)
-            accept_prob[b * gamma + k] =
-                !valid ? 0.f : pd > 0.f ? fminf(1.f, pt / pd) : (pt > 0.f ? 1.f : 0.f);
+        float* s = stats + ((b * gamma + k) * kSplit + sp) * kStatWords;
+        s[0] = md, s[1] = sd, s[2] = mt, s[3] = st;
     }
 }
 
-// One thread per request: keep drafted tokens while u * p_d < p_t.
-__global__ __launch_bounds__(kReqThreads) void verify_decide(int64_t B, int64_t gamma, int64_t V,
-                                                            const int32_t* __restrict__ x,
-                                                            const int32_t* __restrict__ n_draft,
-                                                            const float* __restrict__ u, const float* stats,
-                                                            int32_t* state, int32_t* __restrict__ n_accepted) {
-    const int64_t b = (int64_t)blockIdx.x * kReqThreads + threadIdx.x;
-    if (b >= B) return;
-    const int32_t n = clamp_n(n_draft, b, gamma);
-    int32_t k = 0;
-    bool rejected = false;
-    for (; k < n; ++k) {
-        const int32_t xk = x[b * gamma + k];
-        const float* s = stats + (b * gamma + k) * kStatWords;
-        const bool keep = xk >= 0 && xk < V && u[b * gamma + k] * s[2] < s[3];
-        if (!keep) {
-            rejected = true;
-            break;
-        }
-    }
-    n_accepted[b] = k;
-    state[b] = k | (rejected ? (1 << 30) : 0);  // the sample's position and the residual flag
-}
-
+// (vocabulary chunk, request) workgroups.  Wave 0 first redoes the request's
+// accept walk, one lane per drafted position: it merges the splits' partials
+// into the two log2-normalisers, takes p_d and p_t of the drafted token and
+// keeps the token while u * p_d < p_t; the first lane that fails is the
+// rejected position.  (Chunk 0 also writes n_accepted and accept_prob.)
+// Then the chunk's part of the draw: the packed argmax keys of the residual
+// and of the p_t draw, stored in the workgroup's own slot (a written word is
+// never zero).  A relaxed arrival counter elects the request's last
+// workgroup, which waits for every slot, takes the maximum, decodes the
+// token and clears the request's workspace words for the next call.  No
+// exchange needs a fence.
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kSampleThreads) void verify_sample(int64_t gamma, int64_t V, const T* __restrict__ d,
-                                                                const T* __restrict__ t, const float* __restrict__ G,
-                                                                const float* stats, const int32_t* state,
-                                                                uint64_t* keys) {
+__global__ __launch_bounds__(kSampleThreads) void verify_sample(
+    int64_t gamma, int64_t V, const T* __restrict__ d, const T* __restrict__ t, const int32_t* __restrict__ x,
+    const int32_t* __restrict__ n_draft, const float* __restrict__ u, const float* __restrict__ G, float* stats,
+    uint64_t* slots, uint32_t* counters, int32_t* __restrict__ n_accepted, float* __restrict__ accept_prob,
+    int32_t* __restrict__ next_token, uint32_t* status) {
+    static_assert(kSampleThreads >= 64, "wave 0 walks the positions");
     __shared__ uint64_t red[2][kSampleThreads / 64];
+    __shared__ int s_pos, s_res;
+    __shared__ float s_cd, s_ct;
+    __shared__ int s_last;
     const int64_t b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int32_t st = state[b];
-    const int64_t pos = st & 0xffff;
-    const bool res = (st >> 30) & 1;
+    const int32_t n = clamp_n(n_draft, b, gamma);
+    constexpr int E = Vec<T>::N;
+    const float* g = G + b * V;
+    // the Gumbel row does not depend on the walk: its loads go out first
+    float4 rg[kSampleVecs][E / 4];
+    if (VEC) {
+        const int64_t nvec = V / E;
+        const int64_t v0 = (int64_t)blockIdx.x * kSampleThreads * kSampleVecs;
+#pragma unroll
+        for (int j = 0; j < kSampleVecs; ++j) {
+            const int64_t i = v0 + tid + (int64_t)j * kSampleThreads;
+            const int64_t ic = i < nvec ? i : 0;
+#pragma unroll
+            for (int q = 0; q < E / 4; ++q) rg[j][q] = reinterpret_cast<const float4*>(g)[ic * (E / 4) + q];
+        }
+    }
+    if (wave == 0) {
+        int pos = n, res = 0;
+        float cdp = 0.f, ctp = 0.f;
+        for (int64_t k0 = 0; k0 < n; k0 += 64) {  // 64 positions per round (gamma <= 4096)
+            const int64_t k = k0 + lane;
+            const bool act = k < n;
+            float cd = 0.f, ct = 0.f, pd = 0.f, pt = 0.f;
+            bool keep = false, valid = false;
+            if (act) {
+                float md = -INFINITY, sd = 0.f, mt = -INFINITY, st = 0.f;
+                const float* s = stats + (b * gamma + k) * kSplit * kStatWords;
+                for (int q = 0; q < kSplit; ++q) {
+                    merge(md, sd, s[q * kStatWords + 0], s[q * kStatWords + 1]);
+                    merge(mt, st, s[q * kStatWords + 2], s[q * kStatWords + 3]);
+                }
+                cd = md * kLog2e + __builtin_amdgcn_logf(sd);
+                ct = mt * kLog2e + __builtin_amdgcn_logf(st);
+                const int32_t xk = x[b * gamma + k];
+                valid = xk >= 0 && xk < V;
+                pd = valid ? exp_shifted(load_elem(d + (b * gamma + k) * V, xk), cd) : 0.f;
+                pt = valid ? exp_shifted(load_elem(t + (b * (gamma + 1) + k) * V, xk), ct) : 0.f;
+                keep = valid && u[b * gamma + k] * pd < pt;
+                if (blockIdx.x == 0 && accept_prob)
+                    accept_prob[b * gamma + k] = !valid ? 0.f : pd > 0.f ? fminf(1.f, pt / pd) : (pt > 0.f ? 1.f : 0.f);
+            }
+            const uint64_t fails = __ballot(act && !keep);
+            if (pos == n && fails) {
+                const int j = __builtin_ctzll(fails);
+                pos = (int)(k0 + j), res = 1;
+                cdp = __shfl(cd, j), ctp = __shfl(ct, j);
+            }
+        }
+        if (lane == 0) {
+            s_pos = pos, s_res = res, s_cd = cdp, s_ct = ctp;
+            if (blockIdx.x == 0) n_accepted[b] = pos;
+        }
+        if (blockIdx.x == 0 && accept_prob)
+            for (int64_t k = n + lane; k < gamma; k += 64) accept_prob[b * gamma + k] = __builtin_nanf("");
+    }
+    __syncthreads();
+    const int64_t pos = s_pos;
+    const bool res = s_res != 0;
+    const float cd = s_cd, ct = s_ct;
     const T* tr = t + (b * (gamma + 1) + pos) * V;
     const T* dr = d + (b * gamma + (res ? pos : 0)) * V;  // read only for a residual draw
-    const float* g = G + b * V;
-    const float cd = res ? stats[(b * gamma + pos) * kStatWords + 0] : 0.f;
-    const float ct = res ? stats[(b * gamma + pos) * kStatWords + 1] : 0.f;
     uint64_t kr = 0, kt = 0;  // residual and p_t keys
     auto consider = [&](float xt, float xd, float gv, int64_t v) {
         kt = umax64(kt, argmax_key(xt + gv, (uint32_t)v));
@@ -225,11 +272,9 @@ __global__ __launch_bounds__(kSampleThreads) void verify_sample(int64_t gamma, i
         }
     };
     if (VEC) {
-        constexpr int E = Vec<T>::N;
         const int64_t nvec = V / E;
         const int64_t v0 = (int64_t)blockIdx.x * kSampleThreads * kSampleVecs;
         uint4 rt[kSampleVecs], rd[kSampleVecs];
-        float4 rg[kSampleVecs][E / 4];
         bool in[kSampleVecs];
 #pragma unroll
         for (int j = 0; j < kSampleVecs; ++j) {
@@ -238,8 +283,6 @@ __global__ __launch_bounds__(kSampleThreads) void verify_sample(int64_t gamma, i
             const int64_t ic = in[j] ? i : 0;
             rt[j] = reinterpret_cast<const uint4*>(tr)[ic];
             rd[j] = res ? reinterpret_cast<const uint4*>(dr)[ic] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int q = 0; q < E / 4; ++q) rg[j][q] = reinterpret_cast<const float4*>(g)[ic * (E / 4) + q];
         }
 #pragma unroll
         for (int j = 0; j < kSampleVecs; ++j) {
@@ -269,25 +312,50 @@ __global__ __launch_bounds__(kSampleThreads) void verify_sample(int64_t gamma, i
     }
     if (lane == 0) red[0][wave] = kr, red[1][wave] = kt;
     __syncthreads();
+    const int nch = gridDim.x;
+    uint64_t* slot = slots + ((int64_t)b * nch + blockIdx.x) * 2;
     if (tid == 0) {
         for (int w = 1; w < kSampleThreads / 64; ++w) kr = umax64(kr, red[0][w]), kt = umax64(kt, red[1][w]);
-        if (kr) atomicMax(reinterpret_cast<unsigned long long*>(keys + 2 * b), (unsigned long long)kr);
-        if (kt) atomicMax(reinterpret_cast<unsigned long long*>(keys + 2 * b + 1), (unsigned long long)kt);
+        __hip_atomic_store(slot, kr ? kr : kNoKey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(slot + 1, kt ? kt : kNoKey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t old = __hip_atomic_fetch_add(counters + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = old == (uint32_t)nch - 1;
     }
-}
-
-// One thread per request: the residual draw if there was one with positive
-// mass, else the p_t draw; then the request's workspace words go back to zero.
-__global__ __launch_bounds__(kReqThreads) void verify_finish(int64_t B, int64_t gamma, float* stats, int32_t* state,
-                                                            uint64_t* keys, int32_t* __restrict__ next_token) {
-    const int64_t b = (int64_t)blockIdx.x * kReqThreads + threadIdx.x;
-    if (b >= B) return;
-    const bool res = (state[b] >> 30) & 1;
-    const uint64_t kr = keys[2 * b], kt = keys[2 * b + 1];
-    next_token[b] = key_token(res && kr != 0 ? kr : kt);
-    keys[2 * b] = 0, keys[2 * b + 1] = 0;
-    state[b] = 0;
-    for (int64_t i = 0; i < gamma * (int64_t)kStatWords; ++i) stats[b * gamma * kStatWords + i] = 0.f;
+    __syncthreads();
+    if (s_last && wave == 0) {
+        // every other workgroup has arrived; wait until its slot words are seen
+        uint64_t mr = 0, mt = 0;
+        bool ok = false;
+        const uint64_t* req = slots + (int64_t)b * nch * 2;
+        for (int spin = 0; spin < kSpinLimit; ++spin) {
+            bool all = true;
+            mr = 0, mt = 0;
+            for (int c = lane; c < nch; c += 64) {
+                const uint64_t a0 = __hip_atomic_load(req + 2 * c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t a1 = __hip_atomic_load(req + 2 * c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                all = all && a0 != 0 && a1 != 0;
+                mr = umax64(mr, a0), mt = umax64(mt, a1);
+            }
+            ok = __all(all);
+            if (ok) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        for (int o = 32; o > 0; o >>= 1) {
+            mr = umax64(mr, (uint64_t)__shfl_xor((unsigned long long)mr, o));
+            mt = umax64(mt, (uint64_t)__shfl_xor((unsigned long long)mt, o));
+        }
+        if (lane == 0) {
+            const uint64_t k = res && mr > kNoKey ? mr : mt;
+            next_token[b] = ok && k > kNoKey ? key_token(k) : -1;
+            if (!ok) status[0] = 1u;
+            __hip_atomic_store(counters + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        for (int c = lane; c < 2 * nch; c += 64)
+            __hip_atomic_store(slots + (int64_t)b * nch * 2 + c, (uint64_t)0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        for (int64_t i = lane; i < gamma * kSplit * (int64_t)kStatWords; i += 64)
+            stats[b * gamma * kSplit * kStatWords + i] = 0.f;
+    }
 }
 
 template <typename T>
@@ -300,35 +368,34 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, const void* d, cons
     const bool vec = V % E == 0 && (uintptr_t)d % 16 == 0 && (uintptr_t)t % 16 == 0 && (uintptr_t)G % 16 == 0;
     char* w = static_cast<char*>(ws);
     float* stats = reinterpret_cast<float*>(w);
-    int32_t* state = reinterpret_cast<int32_t*>(w + stats_bytes(B, gamma));
-    uint64_t* keys = reinterpret_cast<uint64_t*>(w + stats_bytes(B, gamma) + state_bytes(B));
+    uint64_t* slots = reinterpret_cast<uint64_t*>(w + stats_bytes(B, gamma));
+    uint32_t* counters = reinterpret_cast<uint32_t*>(w + stats_bytes(B, gamma) + slots_bytes(B, V));
+    uint32_t* status = counters + B;  // a lost slot (bounded wait ran out): token -1 and this word set
     if (gamma > 0) {
-        const dim3 grid((uint32_t)(B * gamma));
+        const dim3 grid((uint32_t)(B * gamma * kSplit));
         if (vec)
-            hipLaunchKernelGGL((verify_stats<T, true>), grid, dim3(kStatThreads), 0, stream, gamma, V, dp, tp, x,
-                               n_draft, stats, accept_prob);
+            hipLaunchKernelGGL((verify_stats<T, true>), grid, dim3(kStatThreads), 0, stream, gamma, V, dp, tp,
+                               n_draft, stats);
         else
-            hipLaunchKernelGGL((verify_stats<T, false>), grid, dim3(kStatThreads), 0, stream, gamma, V, dp, tp, x,
-                               n_draft, stats, accept_prob);
+            hipLaunchKernelGGL((verify_stats<T, false>), grid, dim3(kStatThreads), 0, stream, gamma, V, dp, tp,
+                               n_draft, stats);
     }
-    const dim3 rgrid((uint32_t)((B + kReqThreads - 1) / kReqThreads));
-    hipLaunchKernelGGL(verify_decide, rgrid, dim3(kReqThreads), 0, stream, B, gamma, V, x, n_draft, u, stats, state,
-                       n_accepted);
     const int64_t span = vec ? (int64_t)kSampleThreads * kSampleVecs * E : (int64_t)kSampleThreads * kSampleVecs;
     const dim3 sgrid((uint32_t)((V + span - 1) / span), (uint32_t)B);
     if (vec)
-        hipLaunchKernelGGL((verify_sample<T, true>), sgrid, dim3(kSampleThreads), 0, stream, gamma, V, dp, tp, G,
-                           stats, state, keys);
+        hipLaunchKernelGGL((verify_sample<T, true>), sgrid, dim3(kSampleThreads), 0, stream, gamma, V, dp, tp, x,
+                           n_draft, u, G, stats, slots, counters, n_accepted, accept_prob, next_token, status);
     else
-        hipLaunchKernelGGL((verify_sample<T, false>), sgrid, dim3(kSampleThreads), 0, stream, gamma, V, dp, tp, G,
-                           stats, state, keys);
-    hipLaunchKernelGGL(verify_finish, rgrid, dim3(kReqThreads), 0, stream, B, gamma, stats, state, keys, next_token);
+        hipLaunchKernelGGL((verify_sample<T, false>), sgrid, dim3(kSampleThreads), 0, stream, gamma, V, dp, tp, x,
+                           n_draft, u, G, stats, slots, counters, n_accepted, accept_prob, next_token, status);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t verify_workspace(int64_t B, int64_t gamma) { return stats_bytes(B, gamma) + state_bytes(B) + keys_bytes(B); }
+size_t verify_workspace(int64_t B, int64_t gamma, int64_t V) {
+    return stats_bytes(B, gamma) + slots_bytes(B, V) + count_bytes(B);
+}
 
 hipError_t verify_launch(int64_t B, int64_t gamma, int64_t V, int dtype, const void* d, const void* t,
                          const int32_t* x, const int32_t* n_draft, const float* u, const float* G,

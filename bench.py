@@ -282,7 +282,7 @@ def main():
                         "target logits, fp32 uniforms and Gumbel rows",
             "us_per_call": round(v_us, 2), "positions_per_s": round(sv.B * sv.gamma / (v_us * 1e-6), 1),
             "mean_accepted": round(float(n_acc.mean()), 3),
-            "roofline": {"kernel": "dspark_verify (4 launches; verify_stats reads every drafted row)",
+            "roofline": {"kernel": "dspark_verify (2 launches; verify_stats reads every drafted row)",
                          "bound": "hbm", "achieved": round(v_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(v_gbs / HBM_PEAK_GBS, 4),
                          "traffic": profiled_traffic("verify_b64_vocab151936.md", VERIFY_SOURCES),

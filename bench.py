@@ -105,6 +105,7 @@ def main():
     ap.add_argument("--no-verify", action="store_true", help="skip the rejection-sampling verify measurement")
     ap.add_argument("--extra", action="store_true", help="also time the B=64 sampler and the scheduler workload")
     ap.add_argument("--calib-copy", action="store_true", help="run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache sampler timing")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the draft-head path is data-parallel by request and this build runs "
@@ -223,6 +224,24 @@ def main():
         "wall_s": round(wall, 3),
     }
 
+    # ---------------- cold caches: a 512 MiB write before each call ----------------
+    # W2 (77.8 MB) fits the 256 MB Infinity Cache, so back-to-back calls read
+    # it from there; here every call first finds the caches full of other
+    # data, and HIP events bracket the call alone.
+    scrub = None
+    if not args.no_cold:
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+        for i, (c0, c1) in enumerate(ev):
+            scrub.fill_(i & 0xFF)
+            c0.record(stream)
+            calls[i % n_anch]()
+            c1.record(stream)
+        torch.cuda.synchronize()
+        cold = sorted(c0.elapsed_time(c1) * 1e3 for c0, c1 in ev)
+        line["cold"] = {"b1_us_per_call_median": round(cold[len(cold) // 2], 2), "calls": len(cold),
+                        "scrub_bytes": 512 << 20}
+
     # ---------------- accept rate on the training-width workload ----------------
     if not args.no_accept:
         sa = synth.ACCEPT_TRAIN
@@ -306,6 +325,16 @@ def main():
         b1.record(stream)
         torch.cuda.synchronize()
         us3 = b0.elapsed_time(b1) * 1e3 / 10
+        if scrub is not None:  # the same call with cold caches
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+            for i, (c0, c1) in enumerate(ev):
+                scrub.fill_(i & 0xFF)
+                c0.record(stream)
+                c3()
+                c1.record(stream)
+            torch.cuda.synchronize()
+            cold3 = sorted(c0.elapsed_time(c1) * 1e3 for c0, c1 in ev)
+            line["cold"]["b64_us_per_call_median"] = round(cold3[len(cold3) // 2], 2)
         flops = 2.0 * 64 * s3.gamma * s3.V * s3.r
         by3 = sampler_call_bytes(64, 7, s3.V, s3.H, s3.r) + 64 * 7 * s3.V * 4
         gb3 = by3 / (us3 * 1e-6) / 1e9

@@ -197,24 +197,16 @@ def test_single_request_teacher_forced_screened():
     assert np.all(got["tokens"][0, :3] >= 0) and np.isfinite(got["conf"][0, :3]).all()
 
 
-def test_batched_gumbel_full_vocabulary_sampled_requests():
-    """B=64 Gumbel-max at full size, all 64 requests in one call; the oracle
-    checks 4 sampled requests one by one."""
+def test_batched_gumbel_full_vocabulary_every_request():
+    """B=64 Gumbel-max at full size, all 64 requests in one call (the resident
+    kernel the benchmark times); the oracle checks every request under the
+    near-tie protocol (about 9 s of oracle time)."""
     s = synth.SAMPLER_B64
     w = synth.sampler_weights(s)
     x = synth.sampler_batch(s)
-    out = dh.head_sample(dev(x["U"]), dev(x["h"]), dev(w["W1"]), dev(w["W2"]), dev(w["w_conf"]), w["b_conf"],
-                         dev(x["x0"]), dev(x["G"]))
-    tok, conf, surv = (out[k].cpu().numpy() for k in ("tokens", "conf", "survival"))
-    for b in (0, 17, 42, 63):
-        xb = {k: (v[b:b + 1] if v is not None else None) for k, v in x.items()}
-        ref = oracle.head_sample(xb["U"], xb["h"], w["W1"], w["W2"], w["w_conf"], w["b_conf"], xb["x0"], xb["G"])
-        if not np.array_equal(tok[b], ref["tokens"][0]):
-            k = int(np.argmax(tok[b] != ref["tokens"][0]))
-            assert ref["margin"][0, k] < 1e-3, (b, k)
-            continue  # a near-tie changes the rest of this request's chain
-        assert np.abs(conf[b] - ref["conf"][0]).max() <= 1e-4
-        assert np.abs(surv[b] - ref["survival"][0]).max() <= 1e-4
+    got, ref, ties = sampler_parity(x, w)
+    assert ties <= 2
+    assert np.all(got["tokens"] >= 0)
 
 
 def test_workspace_reuse_across_shapes():

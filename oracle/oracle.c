@@ -72,22 +72,48 @@ static double val(const void* p, int dtype, int64_t i) {
  * Shapes: U, G [B][gamma][V]; h [B][gamma][H]; W1, W2 [V][r]; w [H + r].
  * Outputs tokens, conf, survival, margin [B][gamma]; logits and bias
  * [B][gamma][V] may be NULL.  Returns 0, or -1 on a token id outside [0, V).
+ *
+ * Gated Markov head ([W] 3.2, the second of the three sequential heads), when
+ * Wg [r][H + r] is given: the embedding is gated by the hidden state and
+ * itself before the projection,
+ *   g[j]      = sigmoid(sum_i Wg[j, i] h[b,k,i] + sum_i Wg[j, H+i] e[i])
+ *   bias[v]   = sum_j W2[v, j] * (g[j] * e[j])
+ * (the pages give B = sigma(Wg [h_k; W1[x_{k-1}]]) (x) W1[x_{k-1}] and leave the
+ * map back to the vocabulary open; the plainest reading is the same W2 as
+ * the vanilla head).  The confidence head still sees e itself.
  */
 int oracle_head_sample(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int dtype, const void* U,
                        const void* h, const void* W1, const void* W2, const void* w, double b_conf,
                        const int32_t* x0, const float* gumbel, const int32_t* force, int32_t* tokens,
-                       double* conf, double* survival, double* margin, double* logits, double* bias) {
+                       double* conf, double* survival, double* margin, double* logits, double* bias,
+                       const void* Wg) {
     double* e = (double*)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
-    if (!e) return -2;
+    double* eb = (double*)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1)); /* what the bias sees */
+    if (!e || !eb) {
+        free(e);
+        free(eb);
+        return -2;
+    }
     for (int64_t b = 0; b < B; ++b) {
         int64_t x = x0[b];
         double A = 1.0;
         for (int64_t k = 0; k < gamma; ++k) {
             if (x < 0 || x >= V) {
                 free(e);
+                free(eb);
                 return -1;
             }
             for (int64_t j = 0; j < r; ++j) e[j] = val(W1, dtype, x * r + j);
+            for (int64_t j = 0; j < r; ++j) {
+                eb[j] = e[j];
+                if (Wg) {
+                    double z = 0.0;
+                    for (int64_t i = 0; i < H; ++i)
+                        z += val(Wg, dtype, j * (H + r) + i) * val(h, dtype, (b * gamma + k) * H + i);
+                    for (int64_t i = 0; i < r; ++i) z += val(Wg, dtype, j * (H + r) + H + i) * e[i];
+                    eb[j] = e[j] / (1.0 + exp(-z));
+                }
+            }
 
             const int64_t row = (b * gamma + k) * V;
             int64_t best = -1;
@@ -95,7 +121,7 @@ int oracle_head_sample(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r
             double top1 = -INFINITY, top2 = -INFINITY;
             for (int64_t v = 0; v < V; ++v) {
                 double s = 0.0;
-                for (int64_t j = 0; j < r; ++j) s += val(W2, dtype, v * r + j) * e[j];
+                for (int64_t j = 0; j < r; ++j) s += val(W2, dtype, v * r + j) * eb[j];
                 double lg = val(U, dtype, row + v) + s;
                 double sc = lg + (gumbel ? (double)gumbel[row + v] : 0.0);
                 if (bias) bias[row + v] = s;
@@ -127,6 +153,7 @@ int oracle_head_sample(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r
         }
     }
     free(e);
+    free(eb);
     return 0;
 }
 

@@ -544,3 +544,55 @@ def test_verify_residual_sample_is_gumbel_max_of_log_residual():
         r = pt - pd
         sc = np.where(r > 0, np.log(np.where(r > 0, r, 1)) + G[0], -np.inf).astype(np.float32)
         assert out["next_token"][0] == int(np.argmax(sc)), seed
+
+
+# ---------------------------------------------------------------------------
+# gated Markov head ([W] 3.2): bias = W2 . (sigmoid(Wg [h_k; e]) * e)
+# ---------------------------------------------------------------------------
+def test_gated_zero_gate_weights_halve_the_bias():
+    """Wg = 0 makes every gate 1/2: the gated head is the vanilla head with
+    W2 / 2 (both scalings are exact)."""
+    rng = _rng(120)
+    p = _sampler_inputs(rng, B=3, gamma=4, V=300, H=12, r=8)
+    Wg = np.zeros((8, 12 + 8), np.float32)
+    g = oracle.head_sample(**p, Wg=Wg, want_logits=True)
+    v = oracle.head_sample(**{**p, "W2": p["W2"] * np.float32(0.5)}, want_logits=True)
+    assert np.array_equal(g["tokens"], v["tokens"])
+    assert np.array_equal(g["bias"], v["bias"])
+    assert np.array_equal(g["conf"], v["conf"])  # the confidence head sees e, not the gated e
+
+
+def test_gated_saturated_gate_is_the_vanilla_head():
+    """Positive embeddings and Wg = [0 | c I] with c e_j > 60 put every gate
+    within 1e-26 of 1."""
+    rng = _rng(121)
+    p = _sampler_inputs(rng, B=2, gamma=5, V=400, H=6, r=8)
+    p["W1"] = (np.abs(p["W1"]) + np.float32(0.5)).astype(np.float32)
+    Wg = np.zeros((8, 6 + 8), np.float32)
+    Wg[:, 6:] = np.eye(8, dtype=np.float32) * np.float32(200.0)
+    g = oracle.head_sample(**p, Wg=Wg, want_logits=True)
+    v = oracle.head_sample(**p, want_logits=True)
+    assert np.array_equal(g["tokens"], v["tokens"])
+    np.testing.assert_allclose(g["bias"], v["bias"], rtol=1e-12, atol=1e-14)
+
+
+def test_gated_hidden_state_switches_each_position():
+    """A gate driven only by the mean of h_k: h_k = +100 opens it (the vanilla
+    token), h_k = -100 closes it (bias ~ 1e-44: the plain argmax of U_k).
+    Teacher forcing fixes every previous token, so each position is checked
+    on its own; a wrong position index for h fails here."""
+    rng = _rng(122)
+    B, gamma, V, H, r = 2, 6, 500, 10, 8
+    p = _sampler_inputs(rng, B=B, gamma=gamma, V=V, H=H, r=r, w_sd=2.0, U_sd=0.5)
+    sign = np.array([[1, -1, -1, 1, 1, -1], [-1, 1, -1, 1, -1, 1]], np.float32)
+    p["h"] = np.repeat((100.0 * sign)[:, :, None], H, axis=2).astype(np.float32)
+    Wg = np.zeros((r, H + r), np.float32)
+    Wg[:, :H] = np.float32(1.0 / H)
+    force = rng.integers(0, V, (B, gamma)).astype(np.int32)
+    g = oracle.head_sample(**p, force=force, Wg=Wg)
+    v = oracle.head_sample(**p, force=force)
+    plain = np.argmax(p["U"], axis=2)
+    on = sign > 0
+    assert np.array_equal(g["tokens"][on], v["tokens"][on])
+    assert np.array_equal(g["tokens"][~on], plain[~on])
+    assert not np.array_equal(v["tokens"][~on], plain[~on])  # the bias matters in this setting

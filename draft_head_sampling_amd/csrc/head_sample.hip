@@ -111,7 +111,8 @@ __global__ __launch_bounds__(kThreads) void sample_step(int64_t B, int64_t gamma
                                                         const T* __restrict__ W2, const float* __restrict__ G,
                                                         const int32_t* __restrict__ x0,
                                                         const int32_t* __restrict__ force, uint64_t* keys,
-                                                        float* __restrict__ logits_out, float* __restrict__ bias_out) {
+                                                        float* __restrict__ logits_out, float* __restrict__ bias_out,
+                                                        const float* __restrict__ eg) {
     extern __shared__ float e_lds[];  // [BG][r]
     __shared__ float bias_lds[BG][kTile];
     __shared__ int32_t xprev[BG];
@@ -123,9 +124,9 @@ __global__ __launch_bounds__(kThreads) void sample_step(int64_t B, int64_t gamma
 
     if (tid < BG) xprev[tid] = (b0 + tid < B) ? prev_token(b0 + tid, k, B, gamma, V, x0, force, keys) : -1;
     __syncthreads();
-    for (int64_t i = tid; i < BG * r; i += kThreads) {
+    for (int64_t i = tid; i < BG * r; i += kThreads) {  // e = W1[x_prev], or the gated embedding
         const int32_t x = xprev[i / r];
-        e_lds[i] = x >= 0 ? load_elem(W1, (int64_t)x * r + i % r) : 0.f;
+        e_lds[i] = x < 0 ? 0.f : eg ? eg[(b0 + i / r) * r + i % r] : load_elem(W1, (int64_t)x * r + i % r);
     }
     __syncthreads();
 
@@ -248,6 +249,66 @@ __global__ __launch_bounds__(64 * kFinishMaxGamma) void sample_finish(
     for (int64_t i = threadIdx.x; i < (int64_t)ncopy * gamma; i += blockDim.x)
         kw[(((i / gamma) * gamma + i % gamma) * B + b) * kKeyStride] = 0;
     for (int64_t i = threadIdx.x; i < gamma; i += blockDim.x) hw[b * gamma + i] = 0.f;
+}
+
+// Zero n words (the gated head's scratch, once the block is done).
+__global__ __launch_bounds__(kThreads) void clear_words(float* p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < n) p[i] = 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// Gated Markov head ("基于 DSpark 的投机解码训练框架原理与实现", wangjunjian.com,
+// section 3.2, GatedMarkovHead): the previous token's embedding e = W1[x_{k-1}]
+// is gated before the projection, e' = sigmoid(Wg [h_k; e]) * e (elementwise,
+// Wg [r][H + r]), and the bias is W2 . e'.  The pages leave the map back to
+// the vocabulary open; this is the vanilla head's W2.  The confidence head
+// still sees e.  The hidden half of the gate, Wg[:, :H] . h_k, does not
+// depend on sampled tokens and is computed once per call; the rest runs per
+// step once the previous token is known.  Gated calls take the general
+// per-step path.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gate_hidden(int64_t H, int64_t r, const T* __restrict__ h,
+                                                        const T* __restrict__ Wg, float* __restrict__ Ah) {
+    const int64_t bk = blockIdx.x;  // b * gamma + k
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const T* hr = h + bk * H;
+    for (int64_t j = wave; j < r; j += kThreads / 64) {  // one gate row per wave
+        const T* wr = Wg + j * (H + r);
+        float s = 0.f;
+        for (int64_t i = lane; i < H; i += 64) s += load_elem(wr, i) * load_elem(hr, i);
+        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+        if (lane == 0) Ah[bk * r + j] = s;
+    }
+}
+
+// One workgroup per request at step k: e' = sigmoid(Ah + Wg[:, H:] . e) * e.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gate_step(int64_t B, int64_t gamma, int k, int64_t V, int64_t H,
+                                                      int64_t r, const T* __restrict__ W1, const T* __restrict__ Wg,
+                                                      const int32_t* __restrict__ x0,
+                                                      const int32_t* __restrict__ force, const uint64_t* keys,
+                                                      const float* __restrict__ Ah, float* __restrict__ eg) {
+    extern __shared__ float e_s[];  // [r]
+    __shared__ int32_t xs;
+    const int64_t b = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (threadIdx.x == 0) xs = prev_token(b, k, B, gamma, V, x0, force, keys);
+    __syncthreads();
+    const int32_t x = xs;
+    for (int64_t i = threadIdx.x; i < r; i += kThreads) e_s[i] = x >= 0 ? load_elem(W1, (int64_t)x * r + i) : 0.f;
+    __syncthreads();
+    for (int64_t j = wave; j < r; j += kThreads / 64) {
+        const T* wr = Wg + j * (H + r) + H;
+        float s = 0.f;
+        for (int64_t i = lane; i < r; i += 64) s += load_elem(wr, i) * e_s[i];
+        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+        if (lane == 0) {
+            const float z = Ah[(b * gamma + k) * r + j] + s;
+            eg[b * r + j] = e_s[j] / (1.f + expf(-z));
+        }
+    }
 }
 
 
@@ -2016,12 +2077,12 @@ Buffers carve(void* ws, int64_t B, int64_t gamma, int ncopy) {
 template <typename T, int BG>
 hipError_t launch_steps(int lpr, int64_t B, int64_t gamma, int k, int64_t V, int64_t r, const T* U, const T* W1,
                         const T* W2, const float* G, const int32_t* x0, const int32_t* force, uint64_t* keys,
-                        float* lo, float* bo, hipStream_t stream) {
+                        float* lo, float* bo, const float* eg, hipStream_t stream) {
     const dim3 grid((uint32_t)((V + kTile - 1) / kTile), (uint32_t)((B + BG - 1) / BG));
     const size_t shm = sizeof(float) * BG * r;
 #define DSPARK_STEP(L)                                                                                           \
     hipLaunchKernelGGL((sample_step<T, BG, L>), grid, dim3(kThreads), shm, stream, B, gamma, k, V, r, U, W1, W2, \
-                       G, x0, force, keys, lo, bo)
+                       G, x0, force, keys, lo, bo, eg)
     switch (lpr) {
         case 1: DSPARK_STEP(1); break;
         case 2: DSPARK_STEP(2); break;
@@ -2044,7 +2105,7 @@ template <typename T>
 hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, const void* U, const void* h,
                         const void* W1, const void* W2, const void* w_conf, float b_conf, const int32_t* x0,
                         const float* G, const int32_t* force, int32_t* tokens, float* conf, float* survival,
-                        float* lo, float* bo, void* ws, hipStream_t stream) {
+                        float* lo, float* bo, void* ws, hipStream_t stream, const void* Wg) {
     const T* Ut = static_cast<const T*>(U);
     const T* W1t = static_cast<const T*>(W1);
     const T* W2t = static_cast<const T*>(W2);
@@ -2053,7 +2114,8 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
     // batched bf16 rank-256 requests go to the matrix cores
     bool mfma = false;
     if constexpr (std::is_same_v<T, bf16_t>)
-        mfma = r == kMfmaRank && B >= kMfmaMinBatch && ((uintptr_t)W1 % 16 == 0) && ((uintptr_t)W2 % 16 == 0);
+        mfma = Wg == nullptr && r == kMfmaRank && B >= kMfmaMinBatch && ((uintptr_t)W1 % 16 == 0) &&
+               ((uintptr_t)W2 % 16 == 0);
     if constexpr (std::is_same_v<T, bf16_t>) {
         // resident W2: one persistent kernel for the whole block
         const ResidentPlan rp = mfma ? resident_plan(B, V) : ResidentPlan{};
@@ -2088,6 +2150,16 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
                        static_cast<const T*>(h), wt, s.keys, ncopy, s.hdot);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    // gated head scratch after the hidden dots: the gate's hidden halves
+    // [B][gamma][r], then the gated embeddings of the current step [B][r]
+    const T* Wgt = static_cast<const T*>(Wg);
+    float* gate_ws = Wg ? s.hdot + ((B * gamma + 63) / 64) * 64 : nullptr;
+    const int64_t gate_words = (gamma + 1) * r;  // per request
+    if (Wg) {
+        hipLaunchKernelGGL((gate_hidden<T>), dim3((uint32_t)(B * gamma)), dim3(kThreads), 0, stream, H, r,
+                           static_cast<const T*>(h), Wgt, gate_ws);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
 
     // lanes per W2 row: 16-byte chunks per row when rows are 16-byte aligned
     const int64_t row_bytes = r * (int64_t)sizeof(T);
@@ -2097,6 +2169,13 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
         if ((q & (q - 1)) == 0) lpr = (int)q;
     }
     for (int k = 0; k < gamma; ++k) {
+        const float* eg = nullptr;
+        if (Wg) {
+            hipLaunchKernelGGL((gate_step<T>), dim3((uint32_t)B), dim3(kThreads), sizeof(float) * r, stream, B, gamma,
+                               k, V, H, r, W1t, Wgt, x0, force, s.keys, gate_ws, gate_ws + B * gamma * r);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+            eg = gate_ws + B * gamma * r;
+        }
         if constexpr (std::is_same_v<T, bf16_t>) {
             if (mfma) {
                 const dim3 grid((uint32_t)((V + kMfmaRows - 1) / kMfmaRows), (uint32_t)((B + 63) / 64));
@@ -2117,18 +2196,23 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
             }
         }
         if (B == 1)
-            err = launch_steps<T, 1>(lpr, B, gamma, k, V, r, Ut, W1t, W2t, G, x0, force, s.keys, lo, bo, stream);
+            err = launch_steps<T, 1>(lpr, B, gamma, k, V, r, Ut, W1t, W2t, G, x0, force, s.keys, lo, bo, eg, stream);
         else if (B == 2)
-            err = launch_steps<T, 2>(lpr, B, gamma, k, V, r, Ut, W1t, W2t, G, x0, force, s.keys, lo, bo, stream);
+            err = launch_steps<T, 2>(lpr, B, gamma, k, V, r, Ut, W1t, W2t, G, x0, force, s.keys, lo, bo, eg, stream);
         else if (B <= 4)
-            err = launch_steps<T, 4>(lpr, B, gamma, k, V, r, Ut, W1t, W2t, G, x0, force, s.keys, lo, bo, stream);
+            err = launch_steps<T, 4>(lpr, B, gamma, k, V, r, Ut, W1t, W2t, G, x0, force, s.keys, lo, bo, eg, stream);
         else
-            err = launch_steps<T, 8>(lpr, B, gamma, k, V, r, Ut, W1t, W2t, G, x0, force, s.keys, lo, bo, stream);
+            err = launch_steps<T, 8>(lpr, B, gamma, k, V, r, Ut, W1t, W2t, G, x0, force, s.keys, lo, bo, eg, stream);
         if (err != hipSuccess) return err;
     }
     const int fwaves = gamma < kFinishMaxGamma ? (int)gamma : kFinishMaxGamma;
     hipLaunchKernelGGL((sample_finish<T>), dim3((uint32_t)B), dim3(64 * fwaves), 0, stream, B, gamma, V, H, r, W1t, wt,
                        b_conf, x0, force, s.keys, ncopy, s.hdot, tokens, conf, survival);
+    if (Wg) {  // the gate words go back to zero for the next call
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL(clear_words, dim3((uint32_t)((B * gate_words + kThreads - 1) / kThreads)), dim3(kThreads),
+                           0, stream, gate_ws, B * gate_words);
+    }
     return hipGetLastError();
 }
 
@@ -2149,12 +2233,18 @@ size_t head_sample_workspace(int64_t B, int64_t gamma, int64_t, int64_t r, int d
     return steps;
 }
 
+size_t head_sample_gated_workspace(int64_t B, int64_t gamma, int64_t r) {
+    // the general path's keys (one copy) and hidden dots, then the gate words
+    return ((size_t)(8 * kKeyStride * B * gamma) + 255) / 256 * 256 + ((size_t)(4 * B * gamma) + 255) / 256 * 256 +
+           ((size_t)(4 * B * (gamma + 1) * r) + 255) / 256 * 256;
+}
+
 hipError_t head_sample_launch(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int dtype, const void* U,
                               const void* h, const void* W1, const void* W2, const void* w_conf, float b_conf,
                               const int32_t* x0, const float* gumbel, const int32_t* force, int32_t* tokens,
                               float* conf, float* survival, float* logits_out, float* bias_out, void* ws,
-                              hipStream_t stream) {
-    if (chain_eligible(B, r, dtype, W1, W2)) {
+                              hipStream_t stream, const void* Wg) {
+    if (Wg == nullptr && chain_eligible(B, r, dtype, W1, W2)) {
         const ChainPlan p = chain_plan(V, H);
         if (p.nwg > 0)
             return launch_chain(p, gamma, V, H, U, h, W1, W2, w_conf, b_conf, x0, gumbel, force, tokens, conf,
@@ -2162,9 +2252,9 @@ hipError_t head_sample_launch(int64_t B, int64_t gamma, int64_t V, int64_t H, in
     }
     if (dtype == kBF16)
         return launch_typed<bf16_t>(B, gamma, V, H, r, U, h, W1, W2, w_conf, b_conf, x0, gumbel, force, tokens,
-                                    conf, survival, logits_out, bias_out, ws, stream);
+                                    conf, survival, logits_out, bias_out, ws, stream, Wg);
     return launch_typed<float>(B, gamma, V, H, r, U, h, W1, W2, w_conf, b_conf, x0, gumbel, force, tokens, conf,
-                               survival, logits_out, bias_out, ws, stream);
+                               survival, logits_out, bias_out, ws, stream, Wg);
 }
 
 }  // namespace dspark

@@ -110,6 +110,29 @@ dspark_status_t dspark_head_sample(int64_t B, int64_t gamma, int64_t V, int64_t 
                                    void* stream);
 
 /*
+ * dspark_head_sample_gated -- the same block sampler with the gated Markov
+ * head ([W] 3.2, GatedMarkovHead): the previous token's embedding
+ * e = W1[x_{k-1}] is gated by the hidden state and itself before the
+ * projection,
+ *   e'[j]   = e[j] * sigmoid( sum_i Wg[j][i] h[b][k][i] + sum_i Wg[j][H + i] e[i] )
+ *   bias[v] = W2[v] . e'
+ * (the pages leave the map back to the vocabulary open; this is the vanilla
+ * head's W2).  The confidence head still sees e.  Every other argument,
+ * output and rule is that of dspark_head_sample.
+ *
+ *   Wg  [r][H + r] gate weights, columns [h ; W1 row], in the dtype of the others.
+ * Workspace: dspark_head_sample_gated_workspace_size bytes, zero-filled before
+ * the first use and left zero-filled by every completed call.  The call runs
+ * the general per-step kernels with one gate launch per step.
+ */
+dspark_status_t dspark_head_sample_gated(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int32_t dtype,
+                                         const void* U, const void* h, const void* W1, const void* W2,
+                                         const void* w_conf, const void* Wg, float b_conf, const int32_t* x0,
+                                         const float* gumbel, const int32_t* force, int32_t* tokens, float* conf,
+                                         float* survival, float* logits_out, float* bias_out, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/*
  * dspark_accept_rate -- analytic accept rate per row ([W] 3.3, paper eq. 8):
  *   accept_rate[n] = 1 - 1/2 * || softmax(draft[n, :V]) - softmax(target[n, :V]) ||_1
  * computed in binary32 with max-shifted exponentials.  No clamp is applied:
@@ -196,6 +219,8 @@ dspark_status_t dspark_verify(int64_t B, int64_t gamma, int64_t V, int32_t dtype
 /* Workspace bytes needed by the entry point of the same name for these
  * shapes; 0 if it needs none.  Pure host functions with no side effects. */
 size_t dspark_head_sample_workspace_size(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int32_t dtype);
+size_t dspark_head_sample_gated_workspace_size(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r,
+                                               int32_t dtype);
 size_t dspark_accept_rate_workspace_size(int64_t N, int64_t V, int32_t dtype);
 size_t dspark_prefix_schedule_workspace_size(int64_t B, int64_t gamma);
 size_t dspark_verify_workspace_size(int64_t B, int64_t gamma, int64_t V, int32_t dtype);

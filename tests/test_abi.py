@@ -130,3 +130,21 @@ def test_verify_host_checks(L):
     # gamma = 0: only the target row of the bonus draw is needed
     assert _vf(L, gamma=0, d=None, x=None, u=None, t=None, ws=FAKE * 256,
                wsb=L.dspark_verify_workspace_size(2, 0, 100, 1)) == NULL_ARG
+
+
+def test_head_sample_gated_host_checks(L):
+    need = L.dspark_head_sample_gated_workspace_size(4, 7, 100, 8, 16, 1)
+    assert need > 0 and need % 256 == 0
+    def g(**kw):
+        a = dict(B=4, gamma=7, V=100, H=8, r=16, dtype=1, U=FAKE, h=FAKE, W1=FAKE, W2=FAKE, w=FAKE, Wg=FAKE, x0=FAKE,
+                 tokens=FAKE, conf=FAKE, surv=FAKE, ws=None, wsb=0)
+        a.update(kw)
+        return L.dspark_head_sample_gated(a["B"], a["gamma"], a["V"], a["H"], a["r"], a["dtype"], a["U"], a["h"],
+                                          a["W1"], a["W2"], a["w"], a["Wg"], 0.0, a["x0"], None, None, a["tokens"],
+                                          a["conf"], a["surv"], None, None, a["ws"], a["wsb"], None)
+    assert g(dtype=9) == BAD_DTYPE
+    assert g(r=0) == BAD_SHAPE
+    assert g(B=0) == OK
+    assert g() == WORKSPACE
+    assert g(ws=FAKE * 256, wsb=need, Wg=None) == NULL_ARG
+    assert g(ws=FAKE * 256, wsb=need, h=None) == NULL_ARG

@@ -229,3 +229,50 @@ def test_workspace_reuse_across_shapes():
         for k in a:
             assert torch.equal(a[k], b[k]), (B, V, k)
         assert int(ws.count_nonzero()) == 0, (B, V, gamma)
+
+
+@pytest.mark.parametrize("gumbel", [False, True])
+def test_gated_head_tiny(gumbel):
+    """Gated Markov head on the tiny fp32 workload (general path), with the
+    stored logits and bias compared too."""
+    s = synth.SAMPLER_TINY
+    w = dict(synth.sampler_weights(s), Wg=synth.gate_weights(s, 0.1))
+    x = synth.sampler_batch(s)
+    if gumbel:
+        x["G"] = synth.gumbel(synth.key(s.seed, 99), x["U"].shape)
+    else:
+        x.pop("G", None)
+    sampler_parity(x, w, want_logits=True)
+
+
+@pytest.mark.parametrize("B,V,gamma,H,r", [(5, 30001, 5, 512, 64), (1, 4099, 9, 96, 32), (17, 2000, 3, 64, 8)])
+def test_gated_head_bf16_shapes(B, V, gamma, H, r):
+    s = synth.SamplerShape(B=B, gamma=gamma, V=V, H=H, r=r, dtype="bf16", w_sd=0.3, U_sd=1.0, wc_sd=0.02,
+                           gumbel=True, seed=synth.SEED_BASE + 40 + V)
+    w = dict(synth.sampler_weights(s), Wg=synth.gate_weights(s, 1.0 / np.sqrt(H + r)))
+    x = synth.sampler_batch(s)
+    sampler_parity(x, w, want_logits=True)
+
+
+def test_gated_head_full_vocabulary():
+    """The serving shape's weights (V=151936, H=5120, r=256, bf16), 8 requests,
+    Gumbel-max; every request checked."""
+    s = synth.SAMPLER_B64
+    w = dict(synth.sampler_weights(s), Wg=synth.gate_weights(s, 0.02))
+    x = synth.sampler_batch(s, B=8)
+    _, _, ties = sampler_parity(x, w)
+    assert ties <= 1
+
+
+def test_gated_head_leaves_workspace_zero():
+    s = synth.SamplerShape(B=3, gamma=4, V=5000, H=64, r=16, dtype="bf16", w_sd=0.3, U_sd=1.0, wc_sd=0.02,
+                           gumbel=False, seed=synth.SEED_BASE + 77)
+    w = dict(synth.sampler_weights(s), Wg=synth.gate_weights(s, 0.1))
+    x = synth.sampler_batch(s)
+    n = dh.lib().dspark_head_sample_gated_workspace_size(3, 4, 5000, 64, 16, 1)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    args = [dev(x["U"]), dev(x["h"]), dev(w["W1"]), dev(w["W2"]), dev(w["w_conf"]), w["b_conf"], dev(x["x0"])]
+    a = dh.head_sample(*args, Wg=dev(w["Wg"]), workspace=ws)
+    assert int(ws.count_nonzero()) == 0
+    b = dh.head_sample(*args, Wg=dev(w["Wg"]))
+    assert torch.equal(a["tokens"], b["tokens"]) and torch.equal(a["conf"], b["conf"])

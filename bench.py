@@ -348,6 +348,29 @@ def main():
                                           "traffic": profiled_traffic("head_sample_resident_b64_vocab151936.md",
                                                                       SAMPLER_SOURCES),
                                           "bytes_per_launch": by3}}
+        # the gated Markov head on the same batch (general per-step path)
+        Wg3 = to_dev(synth.gate_weights(s3, 0.02), dev)
+        cg, _ = dh.prepare_head_sample(to_dev(x3["U"], dev), to_dev(x3["h"], dev), W["W1"], W["W2"], W["w_conf"],
+                                       0.0, to_dev(x3["x0"], dev), to_dev(x3["G"], dev), Wg=Wg3)
+        for _ in range(2):
+            cg()
+        torch.cuda.synchronize()
+        b0.record(stream)
+        for _ in range(5):
+            cg()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        usg = b0.elapsed_time(b1) * 1e3 / 5
+        byg = by3 + s3.r * (s3.H + s3.r) * 2
+        gbg = byg / (usg * 1e-6) / 1e9
+        line["extra_gated_b64"] = {
+            "workload": "gated Markov head, B=64 gamma=7 V=151936 H=5120 r=256 bf16, Gumbel-max with fp32 noise",
+            "us_per_call": round(usg, 2), "positions_per_s": round(64 * 7 / (usg * 1e-6), 1),
+            "roofline": {"kernel": "dspark_head_sample_gated (general path: gate and bias step per position)",
+                         "bound": "hbm", "achieved": round(gbg, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbg / HBM_PEAK_GBS, 4),
+                         "traffic": profiled_traffic("head_sample_gated_b64_vocab151936.md", SAMPLER_SOURCES),
+                         "bytes_per_launch": byg}}
         s5 = synth.SCHEDULE_TRAIN
         for kind in ("tokens", "steps"):
             c5, _ = dh.prepare_prefix_schedule(to_dev(synth.schedule_conf(s5), dev),

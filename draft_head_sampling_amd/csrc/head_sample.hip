@@ -268,45 +268,65 @@ __global__ __launch_bounds__(kThreads) void clear_words(float* p, int64_t n) {
 // step once the previous token is known.  Gated calls take the general
 // per-step path.
 // ---------------------------------------------------------------------------
+// Dot product of n elements over the 64 lanes of a wave (every lane gets the
+// sum); 16-byte loads when both rows are 16-byte aligned and n is a whole
+// number of vectors.
+template <typename T>
+__device__ __forceinline__ float wave_dot(const T* __restrict__ a, const T* __restrict__ b, int64_t n, int lane) {
+    constexpr int E = Chunk<T>::N;
+    float s = 0.f;
+    if (n % E == 0 && (uintptr_t)a % 16 == 0 && (uintptr_t)b % 16 == 0) {
+        for (int64_t i = (int64_t)lane * E; i < n; i += 64 * E) {
+            float x[E], y[E];
+            Chunk<T>::load(a + i, x);
+            Chunk<T>::load(b + i, y);
+#pragma unroll
+            for (int q = 0; q < E; ++q) s = __builtin_fmaf(x[q], y[q], s);
+        }
+    } else {
+        for (int64_t i = lane; i < n; i += 64) s += load_elem(a, i) * load_elem(b, i);
+    }
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    return s;
+}
+
+constexpr int kGateRows = 16;  // gate rows per workgroup (4 per wave)
+
+// grid (B * gamma, r / kGateRows): Ah[bk][j] = Wg[j, :H] . h[bk, :]
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gate_hidden(int64_t H, int64_t r, const T* __restrict__ h,
                                                         const T* __restrict__ Wg, float* __restrict__ Ah) {
     const int64_t bk = blockIdx.x;  // b * gamma + k
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const T* hr = h + bk * H;
-    for (int64_t j = wave; j < r; j += kThreads / 64) {  // one gate row per wave
-        const T* wr = Wg + j * (H + r);
-        float s = 0.f;
-        for (int64_t i = lane; i < H; i += 64) s += load_elem(wr, i) * load_elem(hr, i);
-        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    const int64_t j0 = (int64_t)blockIdx.y * kGateRows;
+    for (int64_t j = j0 + wave; j < j0 + kGateRows && j < r; j += kThreads / 64) {
+        const float s = wave_dot(Wg + j * (H + r), hr, H, lane);
         if (lane == 0) Ah[bk * r + j] = s;
     }
 }
 
-// One workgroup per request at step k: e' = sigmoid(Ah + Wg[:, H:] . e) * e.
+// grid (B, r / kGateRows) at step k: e'[j] = sigmoid(Ah + Wg[j, H:] . e) * e[j].
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gate_step(int64_t B, int64_t gamma, int k, int64_t V, int64_t H,
                                                       int64_t r, const T* __restrict__ W1, const T* __restrict__ Wg,
                                                       const int32_t* __restrict__ x0,
                                                       const int32_t* __restrict__ force, const uint64_t* keys,
                                                       const float* __restrict__ Ah, float* __restrict__ eg) {
-    extern __shared__ float e_s[];  // [r]
     __shared__ int32_t xs;
     const int64_t b = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (threadIdx.x == 0) xs = prev_token(b, k, B, gamma, V, x0, force, keys);
     __syncthreads();
     const int32_t x = xs;
-    for (int64_t i = threadIdx.x; i < r; i += kThreads) e_s[i] = x >= 0 ? load_elem(W1, (int64_t)x * r + i) : 0.f;
-    __syncthreads();
-    for (int64_t j = wave; j < r; j += kThreads / 64) {
-        const T* wr = Wg + j * (H + r) + H;
-        float s = 0.f;
-        for (int64_t i = lane; i < r; i += 64) s += load_elem(wr, i) * e_s[i];
-        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    if (x < 0) return;  // the request stopped: its bias is never formed
+    const T* e = W1 + (int64_t)x * r;
+    const int64_t j0 = (int64_t)blockIdx.y * kGateRows;
+    for (int64_t j = j0 + wave; j < j0 + kGateRows && j < r; j += kThreads / 64) {
+        const float s = wave_dot(Wg + j * (H + r) + H, e, r, lane);
         if (lane == 0) {
             const float z = Ah[(b * gamma + k) * r + j] + s;
-            eg[b * r + j] = e_s[j] / (1.f + expf(-z));
+            eg[b * r + j] = load_elem(e, j) / (1.f + expf(-z));
         }
     }
 }
@@ -2156,8 +2176,9 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
     float* gate_ws = Wg ? s.hdot + ((B * gamma + 63) / 64) * 64 : nullptr;
     const int64_t gate_words = (gamma + 1) * r;  // per request
     if (Wg) {
-        hipLaunchKernelGGL((gate_hidden<T>), dim3((uint32_t)(B * gamma)), dim3(kThreads), 0, stream, H, r,
-                           static_cast<const T*>(h), Wgt, gate_ws);
+        const dim3 grid((uint32_t)(B * gamma), (uint32_t)((r + kGateRows - 1) / kGateRows));
+        hipLaunchKernelGGL((gate_hidden<T>), grid, dim3(kThreads), 0, stream, H, r, static_cast<const T*>(h), Wgt,
+                           gate_ws);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
 
@@ -2171,8 +2192,9 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
     for (int k = 0; k < gamma; ++k) {
         const float* eg = nullptr;
         if (Wg) {
-            hipLaunchKernelGGL((gate_step<T>), dim3((uint32_t)B), dim3(kThreads), sizeof(float) * r, stream, B, gamma,
-                               k, V, H, r, W1t, Wgt, x0, force, s.keys, gate_ws, gate_ws + B * gamma * r);
+            const dim3 grid((uint32_t)B, (uint32_t)((r + kGateRows - 1) / kGateRows));
+            hipLaunchKernelGGL((gate_step<T>), grid, dim3(kThreads), 0, stream, B, gamma, k, V, H, r, W1t, Wgt, x0,
+                               force, s.keys, gate_ws, gate_ws + B * gamma * r);
             if ((err = hipGetLastError()) != hipSuccess) return err;
             eg = gate_ws + B * gamma * r;
         }

@@ -40,7 +40,7 @@ def _load():
         i64, vp, d = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
         lib.oracle_head_sample.restype = ctypes.c_int
         lib.oracle_head_sample.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, d,
-                                           vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+                                           vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.oracle_accept_rate.restype = ctypes.c_int
         lib.oracle_accept_rate.argtypes = [i64, i64, ctypes.c_int, vp, i64, vp, i64, vp, vp]
         lib.oracle_prefix_schedule.restype = ctypes.c_int
@@ -66,15 +66,15 @@ def _p(a):
     return a.ctypes.data
 
 
-def head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=None, want_logits=False, Wg=None):
+def head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=None, want_logits=False, Wg=None, Wr=None):
     """Markov-head block sampler + confidence head + survival (fp64).
 
     U [B, gamma, V], h [B, gamma, H], W1/W2 [V, r], w_conf [H + r] share one
     dtype (float32, or uint16 bfloat16 bits).  x0 [B] int32, gumbel
     [B, gamma, V] float32 or None, force [B, gamma] int32 (-1 = sample) or
-    None.  Wg [r, H + r] (same dtype) selects the gated Markov head.  Returns
-    a dict of tokens, conf, survival, margin (and logits, bias when
-    ``want_logits``).
+    None.  Wg [r, H + r] (same dtype) selects the gated Markov head; Wr =
+    (Wrg, Wrc), each [r, 2r + H], the RNN head.  Returns a dict of tokens,
+    conf, survival, margin (and logits, bias when ``want_logits``).
     """
     U, h, W1, W2, w_conf = (np.ascontiguousarray(a) for a in (U, h, W1, W2, w_conf))
     dt = _dtype_of(U)
@@ -94,6 +94,11 @@ def head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=None, want_
     if Wg is not None:
         Wg = np.ascontiguousarray(Wg)
         assert _dtype_of(Wg) == dt and Wg.shape == (r, H + r)
+    Wrg = Wrc = None
+    if Wr is not None:
+        Wrg, Wrc = (np.ascontiguousarray(a) for a in Wr)
+        for a in (Wrg, Wrc):
+            assert _dtype_of(a) == dt and a.shape == (r, 2 * r + H)
     out = {
         "tokens": np.empty((B, gamma), np.int32),
         "conf": np.empty((B, gamma), np.float64),
@@ -106,7 +111,7 @@ def head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=None, want_
     rc = _load().oracle_head_sample(B, gamma, V, H, r, dt, _p(U), _p(h), _p(W1), _p(W2), _p(w_conf),
                                     float(b_conf), _p(x0), _p(gumbel), _p(force), _p(out["tokens"]),
                                     _p(out["conf"]), _p(out["survival"]), _p(out["margin"]),
-                                    _p(out.get("logits")), _p(out.get("bias")), _p(Wg))
+                                    _p(out.get("logits")), _p(out.get("bias")), _p(Wg), _p(Wrg), _p(Wrc))
     if rc != 0:
         raise ValueError(f"oracle_head_sample failed ({rc}): token id out of range")
     return out

@@ -81,26 +81,42 @@ static double val(const void* p, int dtype, int64_t i) {
  * (the pages give B = sigma(Wg [h_k; W1[x_{k-1}]]) (x) W1[x_{k-1}] and leave the
  * map back to the vocabulary open; the plainest reading is the same W2 as
  * the vanilla head).  The confidence head still sees e itself.
+ *
+ * RNN head ([W] 3.2, paper eq. 6), when Wrg and Wrc [r][2r + H] are given: a
+ * recurrent state s (s_0 = 0) replaces the embedding in the bias,
+ *   z         = [s_{k-1} ; e ; h[b,k,:]]
+ *   u[j]      = sigmoid(sum_i Wrg[j, i] z[i])
+ *   s_k[j]    = u[j] s_{k-1}[j] + (1 - u[j]) tanh(sum_i Wrc[j, i] z[i])
+ *   bias[v]   = sum_j W2[v, j] s_k[j]
+ * (the pages' "(1-sigma)(Wg z)" is read as 1 - sigmoid(Wg z), the GRU-style
+ * update; the map back to the vocabulary is read as W2).  The confidence head
+ * still sees e.
  */
 int oracle_head_sample(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int dtype, const void* U,
                        const void* h, const void* W1, const void* W2, const void* w, double b_conf,
                        const int32_t* x0, const float* gumbel, const int32_t* force, int32_t* tokens,
                        double* conf, double* survival, double* margin, double* logits, double* bias,
-                       const void* Wg) {
-    double* e = (double*)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
-    double* eb = (double*)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1)); /* what the bias sees */
-    if (!e || !eb) {
+                       const void* Wg, const void* Wrg, const void* Wrc) {
+    const size_t rn = (size_t)(r > 0 ? r : 1);
+    double* e = (double*)malloc(sizeof(double) * rn);
+    double* eb = (double*)malloc(sizeof(double) * rn); /* what the bias sees */
+    double* st = (double*)malloc(sizeof(double) * rn); /* the RNN state */
+    if (!e || !eb || !st) {
         free(e);
         free(eb);
+        free(st);
         return -2;
     }
+    const int64_t Z = 2 * r + H; /* RNN input width */
     for (int64_t b = 0; b < B; ++b) {
         int64_t x = x0[b];
         double A = 1.0;
+        for (int64_t j = 0; j < r; ++j) st[j] = 0.0;
         for (int64_t k = 0; k < gamma; ++k) {
             if (x < 0 || x >= V) {
                 free(e);
                 free(eb);
+                free(st);
                 return -1;
             }
             for (int64_t j = 0; j < r; ++j) e[j] = val(W1, dtype, x * r + j);
@@ -113,6 +129,27 @@ int oracle_head_sample(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r
                     for (int64_t i = 0; i < r; ++i) z += val(Wg, dtype, j * (H + r) + H + i) * e[i];
                     eb[j] = e[j] / (1.0 + exp(-z));
                 }
+            }
+            if (Wrg && Wrc) {
+                const int64_t hz = (b * gamma + k) * H;
+                for (int64_t j = 0; j < r; ++j) {
+                    double zg = 0.0, zc = 0.0;
+                    for (int64_t i = 0; i < r; ++i) {
+                        zg += val(Wrg, dtype, j * Z + i) * st[i];
+                        zc += val(Wrc, dtype, j * Z + i) * st[i];
+                    }
+                    for (int64_t i = 0; i < r; ++i) {
+                        zg += val(Wrg, dtype, j * Z + r + i) * e[i];
+                        zc += val(Wrc, dtype, j * Z + r + i) * e[i];
+                    }
+                    for (int64_t i = 0; i < H; ++i) {
+                        zg += val(Wrg, dtype, j * Z + 2 * r + i) * val(h, dtype, hz + i);
+                        zc += val(Wrc, dtype, j * Z + 2 * r + i) * val(h, dtype, hz + i);
+                    }
+                    const double u = 1.0 / (1.0 + exp(-zg));
+                    eb[j] = u * st[j] + (1.0 - u) * tanh(zc);
+                }
+                for (int64_t j = 0; j < r; ++j) st[j] = eb[j];
             }
 
             const int64_t row = (b * gamma + k) * V;
@@ -154,6 +191,7 @@ int oracle_head_sample(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r
     }
     free(e);
     free(eb);
+    free(st);
     return 0;
 }
 

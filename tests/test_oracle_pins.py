@@ -596,3 +596,74 @@ def test_gated_hidden_state_switches_each_position():
     assert np.array_equal(g["tokens"][on], v["tokens"][on])
     assert np.array_equal(g["tokens"][~on], plain[~on])
     assert not np.array_equal(v["tokens"][~on], plain[~on])  # the bias matters in this setting
+
+
+# ---------------------------------------------------------------------------
+# RNN head ([W] 3.2, paper eq. 6): s_k = u s_{k-1} + (1 - u) tanh(Wc z),
+# u = sigmoid(Wg z), z = [s_{k-1}; e; h_k], s_0 = 0, bias = W2 . s_k
+# ---------------------------------------------------------------------------
+def _rnn_setup(seed, B=2, gamma=5, V=400, H=10, r=8):
+    rng = _rng(seed)
+    p = _sampler_inputs(rng, B=B, gamma=gamma, V=V, H=H, r=r, w_sd=0.5, U_sd=0.3)
+    p["W1"] = (np.abs(p["W1"]) + np.float32(0.5)).astype(np.float32)  # e_j >= 0.5
+    force = rng.integers(0, V, (B, gamma)).astype(np.int32)
+    Z = 2 * r + H
+    return p, force, np.zeros((r, Z), np.float32), np.zeros((r, Z), np.float32)
+
+
+def _expected_tokens(U, bias_rows):
+    """argmax of the binary32 score U + bias per (request, position)."""
+    return np.argmax((U.astype(np.float64) + bias_rows).astype(np.float32), axis=2)
+
+
+def test_rnn_zero_weights_give_no_bias():
+    p, force, Wrg, Wrc = _rnn_setup(130)
+    out = oracle.head_sample(**p, force=force, Wr=(Wrg, Wrc), want_logits=True)
+    assert np.all(out["bias"] == 0.0)  # u = 1/2, tanh(0) = 0: the state stays 0
+    assert np.array_equal(out["tokens"], np.argmax(p["U"], axis=2))
+
+
+def test_rnn_recurrence_is_geometric():
+    """u = 1/2 and a saturated candidate (tanh(200 e) = 1): s_k = 1 - 2^-k."""
+    p, force, Wrg, Wrc = _rnn_setup(131)
+    r = 8
+    Wrc[:, r:2 * r] = np.eye(r, dtype=np.float32) * np.float32(200.0)
+    out = oracle.head_sample(**p, force=force, Wr=(Wrg, Wrc), want_logits=True)
+    rows = p["W2"].astype(np.float64).sum(axis=1)
+    k = np.arange(1, 6)
+    want = (1.0 - 2.0 ** -k)[None, :, None] * rows[None, None, :]
+    np.testing.assert_allclose(out["bias"], np.broadcast_to(want, out["bias"].shape), rtol=1e-12, atol=1e-12)
+    assert np.array_equal(out["tokens"], _expected_tokens(p["U"], want))
+
+
+def test_rnn_closed_update_gate_follows_h_of_each_position():
+    """u ~ 0 (sigmoid(-200 e)) and a candidate driven by the mean of h_k:
+    h_k = +-100 gives s_k = +-1, bias = +-rowsum(W2), position by position."""
+    p, force, Wrg, Wrc = _rnn_setup(132, H=10)
+    r, H = 8, 10
+    Wrg[:, r:2 * r] = -np.eye(r, dtype=np.float32) * np.float32(200.0)
+    Wrc[:, 2 * r:] = np.float32(1.0 / H)
+    sign = np.array([[1, -1, 1, 1, -1], [-1, -1, 1, -1, 1]], np.float64)
+    p["h"] = np.repeat((100.0 * sign)[:, :, None], H, axis=2).astype(np.float32)
+    out = oracle.head_sample(**p, force=force, Wr=(Wrg, Wrc), want_logits=True)
+    rows = p["W2"].astype(np.float64).sum(axis=1)
+    want = sign[:, :, None] * rows[None, None, :]
+    np.testing.assert_allclose(out["bias"], want, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(out["tokens"], _expected_tokens(p["U"], want))
+
+
+def test_rnn_state_feeds_the_next_step():
+    """u ~ 0, candidate = tanh(1000 s_{k-1} + mean(h_k)): h_1 = +100 sets s_1 = 1
+    and the state alone keeps it at 1 (h_k = 0 afterwards); without s in z it
+    would fall back to 0."""
+    p, force, Wrg, Wrc = _rnn_setup(133, H=10)
+    r, H = 8, 10
+    Wrg[:, r:2 * r] = -np.eye(r, dtype=np.float32) * np.float32(200.0)
+    Wrc[:, :r] = np.eye(r, dtype=np.float32) * np.float32(1000.0)
+    Wrc[:, 2 * r:] = np.float32(1.0 / H)
+    h = np.zeros_like(p["h"])
+    h[:, 0, :] = 100.0
+    p["h"] = h
+    out = oracle.head_sample(**p, force=force, Wr=(Wrg, Wrc), want_logits=True)
+    rows = p["W2"].astype(np.float64).sum(axis=1)
+    np.testing.assert_allclose(out["bias"], np.broadcast_to(rows, out["bias"].shape), rtol=1e-12, atol=1e-12)

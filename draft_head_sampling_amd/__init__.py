@@ -57,6 +57,11 @@ def lib() -> ctypes.CDLL:
     L.dspark_head_sample_gated.restype = i32
     L.dspark_head_sample_gated.argtypes = [i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp,
                                            vp, vp, vp, vp, vp, sz, vp]
+    L.dspark_head_sample_rnn.restype = i32
+    L.dspark_head_sample_rnn.argtypes = [i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp,
+                                         vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dspark_head_sample_rnn_workspace_size.restype = sz
+    L.dspark_head_sample_rnn_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32]
     L.dspark_head_sample_gated_workspace_size.restype = sz
     L.dspark_head_sample_gated_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32]
     L.dspark_head_sample_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32]
@@ -120,10 +125,11 @@ def head_sample_workspace_size(B, gamma, V, H, r, dtype=DSPARK_BF16) -> int:
 
 
 def prepare_head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=None, *, tokens=None, conf=None,
-                        survival=None, logits_out=None, bias_out=None, workspace=None, stream=None, Wg=None):
+                        survival=None, logits_out=None, bias_out=None, workspace=None, stream=None, Wg=None, Wr=None):
     """Validate once and return (call, outputs): ``call()`` enqueues
     dspark_head_sample (or, with gate weights Wg [r, H + r], the gated head
-    dspark_head_sample_gated) on the stream with these exact buffers."""
+    dspark_head_sample_gated; with Wr = (Wrg, Wrc), each [r, 2r + H], the RNN
+    head dspark_head_sample_rnn) on the stream with these exact buffers."""
     B, gamma, V = U.shape
     r = W1.shape[1]
     H = h.shape[2] if h is not None else 0
@@ -150,7 +156,16 @@ def prepare_head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=Non
         _opt(bias_out, "bias_out", torch.float32, (B, gamma, V)),
     )
     st = _stream(dev) if stream is None else stream
-    if Wg is None:
+    if Wg is not None and Wr is not None:
+        raise ValueError("Wg (gated head) and Wr (RNN head) are exclusive")
+    if Wr is not None:
+        rargs = args[:11] + (_dev(Wr[0], "Wrg", U.dtype, (r, 2 * r + H)),
+                             _dev(Wr[1], "Wrc", U.dtype, (r, 2 * r + H))) + args[11:]
+        ws, wsb = _workspace(int(lib().dspark_head_sample_rnn_workspace_size(B, gamma, V, H, r, dt)), dev,
+                             workspace)
+        fn = partial(lib().dspark_head_sample_rnn, *rargs, None if ws is None else ws.data_ptr(), wsb, st)
+        name = "dspark_head_sample_rnn"
+    elif Wg is None:
         ws, wsb = _workspace(head_sample_workspace_size(B, gamma, V, H, r, dt), dev, workspace)
         fn = partial(lib().dspark_head_sample, *args, None if ws is None else ws.data_ptr(), wsb, st)
         name = "dspark_head_sample"
@@ -169,13 +184,14 @@ def prepare_head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=Non
 
 
 def head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=None, *, want_logits=False, workspace=None,
-                Wg=None):
+                Wg=None, Wr=None):
     """Sample one draft block per request.
 
     U [B, gamma, V], h [B, gamma, H], W1/W2 [V, r], w_conf [H + r]: float32 or
     bfloat16 CUDA tensors of one dtype; x0 [B] int32; gumbel [B, gamma, V]
     float32 or None (greedy); force [B, gamma] int32 (-1 = sample) or None;
-    Wg [r, H + r] (same dtype) selects the gated Markov head.
+    Wg [r, H + r] (same dtype) selects the gated Markov head, Wr = (Wrg,
+    Wrc), each [r, 2r + H], the RNN head.
     Returns dict(tokens [B, gamma] int32, conf, survival [B, gamma] float32
     [, logits, bias [B, gamma, V] float32 when want_logits]).
     """
@@ -184,7 +200,7 @@ def head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=None, *, wa
         lo = torch.empty(U.shape, dtype=torch.float32, device=U.device)
         bo = torch.empty(U.shape, dtype=torch.float32, device=U.device)
     call, outs = prepare_head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel, force, logits_out=lo, bias_out=bo,
-                                     workspace=workspace, Wg=Wg)
+                                     workspace=workspace, Wg=Wg, Wr=Wr)
     call()
     outs.pop("_workspace")
     return outs

@@ -61,7 +61,7 @@ DSPARK_EXPORT dspark_status_t dspark_head_sample(int64_t B, int64_t gamma, int64
         return DSPARK_ERR_NULL_ARG;
     return hip_status(dspark::head_sample_launch(B, gamma, V, H, r, dtype, U, h, W1, W2, w_conf, b_conf, x0, gumbel,
                                                  force, tokens, conf, survival, logits_out, bias_out, workspace,
-                                                 static_cast<hipStream_t>(stream), nullptr));
+                                                 static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr));
 }
 
 DSPARK_EXPORT dspark_status_t dspark_head_sample_gated(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r,
@@ -81,7 +81,34 @@ DSPARK_EXPORT dspark_status_t dspark_head_sample_gated(int64_t B, int64_t gamma,
         return DSPARK_ERR_NULL_ARG;
     return hip_status(dspark::head_sample_launch(B, gamma, V, H, r, dtype, U, h, W1, W2, w_conf, b_conf, x0, gumbel,
                                                  force, tokens, conf, survival, logits_out, bias_out, workspace,
-                                                 static_cast<hipStream_t>(stream), Wg));
+                                                 static_cast<hipStream_t>(stream), Wg, nullptr, nullptr));
+}
+
+DSPARK_EXPORT dspark_status_t dspark_head_sample_rnn(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r,
+                                                     int32_t dtype, const void* U, const void* h, const void* W1,
+                                                     const void* W2, const void* w_conf, const void* Wrg,
+                                                     const void* Wrc, float b_conf, const int32_t* x0,
+                                                     const float* gumbel, const int32_t* force, int32_t* tokens,
+                                                     float* conf, float* survival, float* logits_out,
+                                                     float* bias_out, void* workspace, size_t workspace_bytes,
+                                                     void* stream) {
+    if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return DSPARK_ERR_BAD_DTYPE;
+    if (!sampler_shape_ok(B, gamma, V, H, r) || !mul_ok(r, 2 * r + H) || !mul_ok(B * (2 * gamma + 2), r))
+        return DSPARK_ERR_BAD_SHAPE;
+    if (B == 0 || gamma == 0) return DSPARK_OK;
+    dspark_status_t st = check_workspace(workspace, workspace_bytes, dspark::head_sample_rnn_workspace(B, gamma, r));
+    if (st != DSPARK_OK) return st;
+    if (!U || !W1 || !W2 || !w_conf || !Wrg || !Wrc || !x0 || !tokens || !conf || !survival || (H > 0 && !h))
+        return DSPARK_ERR_NULL_ARG;
+    return hip_status(dspark::head_sample_launch(B, gamma, V, H, r, dtype, U, h, W1, W2, w_conf, b_conf, x0, gumbel,
+                                                 force, tokens, conf, survival, logits_out, bias_out, workspace,
+                                                 static_cast<hipStream_t>(stream), nullptr, Wrg, Wrc));
+}
+
+DSPARK_EXPORT size_t dspark_head_sample_rnn_workspace_size(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r,
+                                                           int32_t) {
+    if (!sampler_shape_ok(B, gamma, V, H, r) || !mul_ok(r, 2 * r + H) || !mul_ok(B * (2 * gamma + 2), r)) return 0;
+    return dspark::head_sample_rnn_workspace(B, gamma, r);
 }
 
 DSPARK_EXPORT dspark_status_t dspark_accept_rate(int64_t N, int64_t V, int32_t dtype, const void* draft,

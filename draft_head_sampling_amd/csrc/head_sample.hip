@@ -331,6 +331,84 @@ __global__ __launch_bounds__(kThreads) void gate_step(int64_t B, int64_t gamma, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// RNN head (the same page, section 3.2, RNNHead; paper eq. 6): a recurrent
+// state replaces the embedding in the bias,
+//   z = [s_{k-1}; e; h_k],  u = sigmoid(Wrg z),  s_k = u s_{k-1} + (1 - u) tanh(Wrc z)
+// with s_0 = 0 and bias = W2 . s_k (Wrg, Wrc [r][2r + H]).  The h_k halves
+// of both products are computed once per call; the rest per step.
+// ---------------------------------------------------------------------------
+// Dot of a row of T with a float vector over a wave (every lane gets the sum).
+template <typename T>
+__device__ __forceinline__ float wave_dot_f(const T* __restrict__ a, const float* __restrict__ b, int64_t n,
+                                            int lane) {
+    constexpr int E = Chunk<T>::N;
+    float s = 0.f;
+    if (n % E == 0 && (uintptr_t)a % 16 == 0) {
+        for (int64_t i = (int64_t)lane * E; i < n; i += 64 * E) {
+            float x[E];
+            Chunk<T>::load(a + i, x);
+#pragma unroll
+            for (int q = 0; q < E; ++q) s = __builtin_fmaf(x[q], b[i + q], s);
+        }
+    } else {
+        for (int64_t i = lane; i < n; i += 64) s += load_elem(a, i) * b[i];
+    }
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    return s;
+}
+
+// grid (B * gamma, r / kGateRows): Ag = Wrg[:, 2r:] . h_k and Ac = Wrc[:, 2r:] . h_k
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rnn_hidden(int64_t H, int64_t r, const T* __restrict__ h,
+                                                       const T* __restrict__ Wrg, const T* __restrict__ Wrc,
+                                                       float* __restrict__ Ag, float* __restrict__ Ac) {
+    const int64_t bk = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t Z = 2 * r + H;
+    const T* hr = h + bk * H;
+    const int64_t j0 = (int64_t)blockIdx.y * kGateRows;
+    for (int64_t j = j0 + wave; j < j0 + kGateRows && j < r; j += kThreads / 64) {
+        const float g = wave_dot(Wrg + j * Z + 2 * r, hr, H, lane);
+        const float c = wave_dot(Wrc + j * Z + 2 * r, hr, H, lane);
+        if (lane == 0) Ag[bk * r + j] = g, Ac[bk * r + j] = c;
+    }
+}
+
+// grid (B, r / kGateRows) at step k: the new state s_k of every request
+// (written to s_out; s_in holds s_{k-1}, ignored at k = 0).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rnn_step(int64_t B, int64_t gamma, int k, int64_t V, int64_t H, int64_t r,
+                                                     const T* __restrict__ W1, const T* __restrict__ Wrg,
+                                                     const T* __restrict__ Wrc, const int32_t* __restrict__ x0,
+                                                     const int32_t* __restrict__ force, const uint64_t* keys,
+                                                     const float* __restrict__ Ag, const float* __restrict__ Ac,
+                                                     const float* __restrict__ s_in, float* __restrict__ s_out) {
+    extern __shared__ float z_s[];  // [2r]: s_{k-1}, then e
+    __shared__ int32_t xs;
+    const int64_t b = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (threadIdx.x == 0) xs = prev_token(b, k, B, gamma, V, x0, force, keys);
+    __syncthreads();
+    const int32_t x = xs;
+    if (x < 0) return;  // the request stopped: its bias is never formed
+    for (int64_t i = threadIdx.x; i < r; i += kThreads) {
+        z_s[i] = k == 0 ? 0.f : s_in[b * r + i];
+        z_s[r + i] = load_elem(W1, (int64_t)x * r + i);
+    }
+    __syncthreads();
+    const int64_t Z = 2 * r + H, bk = b * gamma + k;
+    const int64_t j0 = (int64_t)blockIdx.y * kGateRows;
+    for (int64_t j = j0 + wave; j < j0 + kGateRows && j < r; j += kThreads / 64) {
+        const float zg = Ag[bk * r + j] + wave_dot_f(Wrg + j * Z, z_s, 2 * r, lane);
+        const float zc = Ac[bk * r + j] + wave_dot_f(Wrc + j * Z, z_s, 2 * r, lane);
+        if (lane == 0) {
+            const float u = 1.f / (1.f + expf(-zg));
+            s_out[b * r + j] = u * z_s[j] + (1.f - u) * tanhf(zc);
+        }
+    }
+}
+
 
 // ---------------------------------------------------------------------------
 // Single-request chain kernel (B = 1, bf16, rank 256).
@@ -2125,7 +2203,8 @@ template <typename T>
 hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, const void* U, const void* h,
                         const void* W1, const void* W2, const void* w_conf, float b_conf, const int32_t* x0,
                         const float* G, const int32_t* force, int32_t* tokens, float* conf, float* survival,
-                        float* lo, float* bo, void* ws, hipStream_t stream, const void* Wg) {
+                        float* lo, float* bo, void* ws, hipStream_t stream, const void* Wg, const void* Wrg,
+                        const void* Wrc) {
     const T* Ut = static_cast<const T*>(U);
     const T* W1t = static_cast<const T*>(W1);
     const T* W2t = static_cast<const T*>(W2);
@@ -2134,8 +2213,8 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
     // batched bf16 rank-256 requests go to the matrix cores
     bool mfma = false;
     if constexpr (std::is_same_v<T, bf16_t>)
-        mfma = Wg == nullptr && r == kMfmaRank && B >= kMfmaMinBatch && ((uintptr_t)W1 % 16 == 0) &&
-               ((uintptr_t)W2 % 16 == 0);
+        mfma = Wg == nullptr && Wrg == nullptr && r == kMfmaRank && B >= kMfmaMinBatch &&
+               ((uintptr_t)W1 % 16 == 0) && ((uintptr_t)W2 % 16 == 0);
     if constexpr (std::is_same_v<T, bf16_t>) {
         // resident W2: one persistent kernel for the whole block
         const ResidentPlan rp = mfma ? resident_plan(B, V) : ResidentPlan{};
@@ -2170,11 +2249,22 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
                        static_cast<const T*>(h), wt, s.keys, ncopy, s.hdot);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // gated head scratch after the hidden dots: the gate's hidden halves
-    // [B][gamma][r], then the gated embeddings of the current step [B][r]
+    // scratch of the gated and RNN heads after the hidden dots.  Gated: the
+    // gate's hidden halves [B][gamma][r], then the gated embeddings of the
+    // current step [B][r].  RNN: the two hidden halves [2][B][gamma][r], then
+    // two state buffers [2][B][r] (step k writes buffer k % 2).
     const T* Wgt = static_cast<const T*>(Wg);
-    float* gate_ws = Wg ? s.hdot + ((B * gamma + 63) / 64) * 64 : nullptr;
-    const int64_t gate_words = (gamma + 1) * r;  // per request
+    const T* Wrgt = static_cast<const T*>(Wrg);
+    const T* Wrct = static_cast<const T*>(Wrc);
+    const bool rnn = Wrg != nullptr;
+    float* gate_ws = (Wg || rnn) ? s.hdot + ((B * gamma + 63) / 64) * 64 : nullptr;
+    const int64_t gate_words = (rnn ? 2 * gamma + 2 : gamma + 1) * r;  // per request
+    if (rnn) {
+        const dim3 grid((uint32_t)(B * gamma), (uint32_t)((r + kGateRows - 1) / kGateRows));
+        hipLaunchKernelGGL((rnn_hidden<T>), grid, dim3(kThreads), 0, stream, H, r, static_cast<const T*>(h), Wrgt,
+                           Wrct, gate_ws, gate_ws + B * gamma * r);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
     if (Wg) {
         const dim3 grid((uint32_t)(B * gamma), (uint32_t)((r + kGateRows - 1) / kGateRows));
         hipLaunchKernelGGL((gate_hidden<T>), grid, dim3(kThreads), 0, stream, H, r, static_cast<const T*>(h), Wgt,
@@ -2197,6 +2287,15 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
                                force, s.keys, gate_ws, gate_ws + B * gamma * r);
             if ((err = hipGetLastError()) != hipSuccess) return err;
             eg = gate_ws + B * gamma * r;
+        }
+        if (rnn) {
+            float* st = gate_ws + 2 * B * gamma * r;
+            const dim3 grid((uint32_t)B, (uint32_t)((r + kGateRows - 1) / kGateRows));
+            hipLaunchKernelGGL((rnn_step<T>), grid, dim3(kThreads), sizeof(float) * 2 * r, stream, B, gamma, k, V, H,
+                               r, W1t, Wrgt, Wrct, x0, force, s.keys, gate_ws, gate_ws + B * gamma * r,
+                               st + ((k + 1) % 2) * B * r, st + (k % 2) * B * r);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+            eg = st + (k % 2) * B * r;
         }
         if constexpr (std::is_same_v<T, bf16_t>) {
             if (mfma) {
@@ -2230,7 +2329,7 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
     const int fwaves = gamma < kFinishMaxGamma ? (int)gamma : kFinishMaxGamma;
     hipLaunchKernelGGL((sample_finish<T>), dim3((uint32_t)B), dim3(64 * fwaves), 0, stream, B, gamma, V, H, r, W1t, wt,
                        b_conf, x0, force, s.keys, ncopy, s.hdot, tokens, conf, survival);
-    if (Wg) {  // the gate words go back to zero for the next call
+    if (Wg || rnn) {  // the gate words go back to zero for the next call
         if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL(clear_words, dim3((uint32_t)((B * gate_words + kThreads - 1) / kThreads)), dim3(kThreads),
                            0, stream, gate_ws, B * gate_words);
@@ -2261,12 +2360,18 @@ size_t head_sample_gated_workspace(int64_t B, int64_t gamma, int64_t r) {
            ((size_t)(4 * B * (gamma + 1) * r) + 255) / 256 * 256;
 }
 
+size_t head_sample_rnn_workspace(int64_t B, int64_t gamma, int64_t r) {
+    // the general path's keys (one copy) and hidden dots, then the RNN words
+    return ((size_t)(8 * kKeyStride * B * gamma) + 255) / 256 * 256 + ((size_t)(4 * B * gamma) + 255) / 256 * 256 +
+           ((size_t)(4 * B * (2 * gamma + 2) * r) + 255) / 256 * 256;
+}
+
 hipError_t head_sample_launch(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int dtype, const void* U,
                               const void* h, const void* W1, const void* W2, const void* w_conf, float b_conf,
                               const int32_t* x0, const float* gumbel, const int32_t* force, int32_t* tokens,
                               float* conf, float* survival, float* logits_out, float* bias_out, void* ws,
-                              hipStream_t stream, const void* Wg) {
-    if (Wg == nullptr && chain_eligible(B, r, dtype, W1, W2)) {
+                              hipStream_t stream, const void* Wg, const void* Wrg, const void* Wrc) {
+    if (Wg == nullptr && Wrg == nullptr && chain_eligible(B, r, dtype, W1, W2)) {
         const ChainPlan p = chain_plan(V, H);
         if (p.nwg > 0)
             return launch_chain(p, gamma, V, H, U, h, W1, W2, w_conf, b_conf, x0, gumbel, force, tokens, conf,
@@ -2274,9 +2379,9 @@ hipError_t head_sample_launch(int64_t B, int64_t gamma, int64_t V, int64_t H, in
     }
     if (dtype == kBF16)
         return launch_typed<bf16_t>(B, gamma, V, H, r, U, h, W1, W2, w_conf, b_conf, x0, gumbel, force, tokens,
-                                    conf, survival, logits_out, bias_out, ws, stream, Wg);
+                                    conf, survival, logits_out, bias_out, ws, stream, Wg, Wrg, Wrc);
     return launch_typed<float>(B, gamma, V, H, r, U, h, W1, W2, w_conf, b_conf, x0, gumbel, force, tokens, conf,
-                               survival, logits_out, bias_out, ws, stream, Wg);
+                               survival, logits_out, bias_out, ws, stream, Wg, Wrg, Wrc);
 }
 
 }  // namespace dspark

@@ -62,12 +62,14 @@ hipError_t accept_rate_launch(int64_t N, int64_t V, int dtype, const void* d, in
 
 size_t head_sample_workspace(int64_t B, int64_t gamma, int64_t V, int64_t r, int dtype);
 size_t head_sample_gated_workspace(int64_t B, int64_t gamma, int64_t r);
-// Wg == nullptr: the vanilla Markov head; otherwise the gated head (general path)
+size_t head_sample_rnn_workspace(int64_t B, int64_t gamma, int64_t r);
+// Wg and Wrg == nullptr: the vanilla Markov head; Wg: the gated head; Wrg and
+// Wrc: the RNN head (both on the general path)
 hipError_t head_sample_launch(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int dtype, const void* U,
                               const void* h, const void* W1, const void* W2, const void* w_conf, float b_conf,
                               const int32_t* x0, const float* gumbel, const int32_t* force, int32_t* tokens,
                               float* conf, float* survival, float* logits_out, float* bias_out, void* ws,
-                              hipStream_t stream, const void* Wg);
+                              hipStream_t stream, const void* Wg, const void* Wrg, const void* Wrc);
 
 size_t verify_workspace(int64_t B, int64_t gamma, int64_t V);
 hipError_t verify_launch(int64_t B, int64_t gamma, int64_t V, int dtype, const void* d, const void* t,

@@ -133,6 +133,30 @@ dspark_status_t dspark_head_sample_gated(int64_t B, int64_t gamma, int64_t V, in
                                          size_t workspace_bytes, void* stream);
 
 /*
+ * dspark_head_sample_rnn -- the same block sampler with the RNN head ([W] 3.2,
+ * RNNHead, paper eq. 6): a recurrent state s (s_0 = 0) replaces the embedding
+ * in the bias,
+ *   z = [s_{k-1} ; W1[x_{k-1}] ; h[b][k]]          (length 2r + H)
+ *   u = sigmoid(Wrg z),  s_k = u * s_{k-1} + (1 - u) * tanh(Wrc z)   (elementwise)
+ *   bias[v] = W2[v] . s_k
+ * (the pages' "(1-sigma)(Wg z)" is read as 1 - sigmoid(Wg z); the map back to
+ * the vocabulary as W2).  The confidence head still sees W1[x_{k-1}].  Every
+ * other argument, output and rule is that of dspark_head_sample.
+ *
+ *   Wrg, Wrc  [r][2r + H] update-gate and candidate weights, columns [s ; W1 row ; h],
+ *             in the dtype of the others.
+ * Workspace: dspark_head_sample_rnn_workspace_size bytes, zero-filled before the
+ * first use and left zero-filled by every completed call.  The call runs the
+ * general per-step kernels with one state launch per step.
+ */
+dspark_status_t dspark_head_sample_rnn(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int32_t dtype,
+                                       const void* U, const void* h, const void* W1, const void* W2,
+                                       const void* w_conf, const void* Wrg, const void* Wrc, float b_conf,
+                                       const int32_t* x0, const float* gumbel, const int32_t* force, int32_t* tokens,
+                                       float* conf, float* survival, float* logits_out, float* bias_out,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * dspark_accept_rate -- analytic accept rate per row ([W] 3.3, paper eq. 8):
  *   accept_rate[n] = 1 - 1/2 * || softmax(draft[n, :V]) - softmax(target[n, :V]) ||_1
  * computed in binary32 with max-shifted exponentials.  No clamp is applied:
@@ -221,6 +245,8 @@ dspark_status_t dspark_verify(int64_t B, int64_t gamma, int64_t V, int32_t dtype
 size_t dspark_head_sample_workspace_size(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int32_t dtype);
 size_t dspark_head_sample_gated_workspace_size(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r,
                                                int32_t dtype);
+size_t dspark_head_sample_rnn_workspace_size(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r,
+                                             int32_t dtype);
 size_t dspark_accept_rate_workspace_size(int64_t N, int64_t V, int32_t dtype);
 size_t dspark_prefix_schedule_workspace_size(int64_t B, int64_t gamma);
 size_t dspark_verify_workspace_size(int64_t B, int64_t gamma, int64_t V, int32_t dtype);

@@ -30,7 +30,7 @@ _lib = None
 # one master seed per workload, one tag per tensor
 SEED_BASE = 0xD5A20000
 TAG = {"W1": 1, "W2": 2, "U": 3, "h": 4, "w": 5, "x0": 6, "G": 7, "d": 8, "t": 9, "conf": 10, "sps": 11,
-       "vd": 12, "vt": 13, "vtb": 14, "vx": 15, "vu": 16, "vG": 17, "Wg": 18}
+       "vd": 12, "vt": 13, "vtb": 14, "vx": 15, "vu": 16, "vG": 17, "Wg": 18, "Wrg": 19, "Wrc": 20}
 
 
 def build(force: bool = True) -> str:
@@ -179,6 +179,14 @@ def gate_weights(s: SamplerShape, sd: float) -> np.ndarray:
     """Gate weights Wg [r, H + r] of the gated Markov head, N(0, sd), in the
     workload's dtype."""
     return normal(key(s.seed, TAG["Wg"]), (s.r, s.H + s.r), 0.0, sd, s.dtype)
+
+
+def rnn_weights(s: SamplerShape, sd: float) -> tuple[np.ndarray, np.ndarray]:
+    """Update-gate and candidate weights (Wrg, Wrc) [r, 2r + H] of the RNN head,
+    N(0, sd), in the workload's dtype."""
+    shape = (s.r, 2 * s.r + s.H)
+    return (normal(key(s.seed, TAG["Wrg"]), shape, 0.0, sd, s.dtype),
+            normal(key(s.seed, TAG["Wrc"]), shape, 0.0, sd, s.dtype))
 
 
 def sampler_batch(s: SamplerShape, batch_id: int = 0, B: int | None = None) -> dict:

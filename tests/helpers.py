@@ -44,7 +44,8 @@ def normwise_rel(gpu: np.ndarray, ref: np.ndarray) -> float:
 def run_gpu_sampler(x: dict, w: dict, force: np.ndarray | None, want_logits: bool, device="cuda"):
     out = dh.head_sample(dev(x["U"], device), dev(x["h"], device), dev(w["W1"], device), dev(w["W2"], device),
                          dev(w["w_conf"], device), w["b_conf"], dev(x["x0"], device), dev(x.get("G"), device),
-                         dev(force, device), want_logits=want_logits, Wg=dev(w.get("Wg"), device))
+                         dev(force, device), want_logits=want_logits, Wg=dev(w.get("Wg"), device),
+                         Wr=None if w.get("Wr") is None else tuple(dev(a, device) for a in w["Wr"]))
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 
@@ -64,7 +65,7 @@ def sampler_parity(x: dict, w: dict, want_logits: bool = False, device="cuda"):
     for _ in range(B * gamma + 1):
         f = force if tie.any() else None
         ref = oracle.head_sample(x["U"], x["h"], w["W1"], w["W2"], w["w_conf"], w["b_conf"], x["x0"], x.get("G"),
-                                 f, want_logits=want_logits or tie.any(), Wg=w.get("Wg"))
+                                 f, want_logits=want_logits or tie.any(), Wg=w.get("Wg"), Wr=w.get("Wr"))
         got = run_gpu_sampler(x, w, f, want_logits, device)
         mism = (got["tokens"] != ref["tokens"]) & ~tie
         if not mism.any():

@@ -148,3 +148,20 @@ def test_head_sample_gated_host_checks(L):
     assert g() == WORKSPACE
     assert g(ws=FAKE * 256, wsb=need, Wg=None) == NULL_ARG
     assert g(ws=FAKE * 256, wsb=need, h=None) == NULL_ARG
+
+
+def test_head_sample_rnn_host_checks(L):
+    need = L.dspark_head_sample_rnn_workspace_size(4, 7, 100, 8, 16, 1)
+    assert need > L.dspark_head_sample_gated_workspace_size(4, 7, 100, 8, 16, 1) > 0 and need % 256 == 0
+    def g(**kw):
+        a = dict(B=4, gamma=7, V=100, H=8, r=16, dtype=1, Wrg=FAKE, Wrc=FAKE, ws=None, wsb=0)
+        a.update(kw)
+        return L.dspark_head_sample_rnn(a["B"], a["gamma"], a["V"], a["H"], a["r"], a["dtype"], FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, a["Wrg"], a["Wrc"], 0.0, FAKE, None, None, FAKE, FAKE, FAKE, None,
+                                        None, a["ws"], a["wsb"], None)
+    assert g(dtype=9) == BAD_DTYPE
+    assert g(r=0) == BAD_SHAPE
+    assert g(B=0) == OK
+    assert g() == WORKSPACE
+    assert g(ws=FAKE * 256, wsb=need, Wrg=None) == NULL_ARG
+    assert g(ws=FAKE * 256, wsb=need, Wrc=None) == NULL_ARG

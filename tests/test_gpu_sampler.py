@@ -276,3 +276,39 @@ def test_gated_head_leaves_workspace_zero():
     assert int(ws.count_nonzero()) == 0
     b = dh.head_sample(*args, Wg=dev(w["Wg"]))
     assert torch.equal(a["tokens"], b["tokens"]) and torch.equal(a["conf"], b["conf"])
+
+
+@pytest.mark.parametrize("gumbel", [False, True])
+def test_rnn_head_tiny(gumbel):
+    """RNN head on the tiny fp32 workload (general path), stored logits and
+    bias compared too."""
+    s = synth.SAMPLER_TINY
+    w = dict(synth.sampler_weights(s), Wr=synth.rnn_weights(s, 0.08))
+    x = synth.sampler_batch(s)
+    if gumbel:
+        x["G"] = synth.gumbel(synth.key(s.seed, 97), x["U"].shape)
+    sampler_parity(x, w, want_logits=True)
+
+
+@pytest.mark.parametrize("B,V,gamma,H,r", [(5, 30001, 5, 512, 64), (1, 4099, 9, 96, 32), (17, 2000, 3, 64, 8)])
+def test_rnn_head_bf16_shapes(B, V, gamma, H, r):
+    s = synth.SamplerShape(B=B, gamma=gamma, V=V, H=H, r=r, dtype="bf16", w_sd=0.3, U_sd=1.0, wc_sd=0.02,
+                           gumbel=True, seed=synth.SEED_BASE + 60 + V)
+    w = dict(synth.sampler_weights(s), Wr=synth.rnn_weights(s, 1.0 / np.sqrt(2 * r + H)))
+    x = synth.sampler_batch(s)
+    sampler_parity(x, w, want_logits=True)
+
+
+def test_rnn_head_full_vocabulary_and_workspace():
+    """The serving shape's weights (V=151936, H=5120, r=256, bf16), 8 requests,
+    Gumbel-max, every request checked; the workspace is left zero."""
+    s = synth.SAMPLER_B64
+    w = dict(synth.sampler_weights(s), Wr=synth.rnn_weights(s, 0.015))
+    x = synth.sampler_batch(s, B=8)
+    _, _, ties = sampler_parity(x, w)
+    assert ties <= 1
+    n = dh.lib().dspark_head_sample_rnn_workspace_size(8, 7, s.V, s.H, s.r, 1)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    dh.head_sample(dev(x["U"]), dev(x["h"]), dev(w["W1"]), dev(w["W2"]), dev(w["w_conf"]), w["b_conf"],
+                   dev(x["x0"]), dev(x["G"]), Wr=tuple(dev(a) for a in w["Wr"]), workspace=ws)
+    assert int(ws.count_nonzero()) == 0

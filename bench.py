@@ -371,6 +371,29 @@ def main():
                          "frac": round(gbg / HBM_PEAK_GBS, 4),
                          "traffic": profiled_traffic("head_sample_gated_b64_vocab151936.md", SAMPLER_SOURCES),
                          "bytes_per_launch": byg}}
+        # the RNN head on the same batch (general per-step path)
+        Wr3 = tuple(to_dev(a, dev) for a in synth.rnn_weights(s3, 0.015))
+        cr, _ = dh.prepare_head_sample(to_dev(x3["U"], dev), to_dev(x3["h"], dev), W["W1"], W["W2"], W["w_conf"],
+                                       0.0, to_dev(x3["x0"], dev), to_dev(x3["G"], dev), Wr=Wr3)
+        for _ in range(2):
+            cr()
+        torch.cuda.synchronize()
+        b0.record(stream)
+        for _ in range(5):
+            cr()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        usr = b0.elapsed_time(b1) * 1e3 / 5
+        byr = by3 + 2 * s3.r * (2 * s3.r + s3.H) * 2
+        gbr = byr / (usr * 1e-6) / 1e9
+        line["extra_rnn_b64"] = {
+            "workload": "RNN head, B=64 gamma=7 V=151936 H=5120 r=256 bf16, Gumbel-max with fp32 noise",
+            "us_per_call": round(usr, 2), "positions_per_s": round(64 * 7 / (usr * 1e-6), 1),
+            "roofline": {"kernel": "dspark_head_sample_rnn (general path: state and bias step per position)",
+                         "bound": "hbm", "achieved": round(gbr, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbr / HBM_PEAK_GBS, 4),
+                         "traffic": profiled_traffic("head_sample_rnn_b64_vocab151936.md", SAMPLER_SOURCES),
+                         "bytes_per_launch": byr}}
         s5 = synth.SCHEDULE_TRAIN
         for kind in ("tokens", "steps"):
             c5, _ = dh.prepare_prefix_schedule(to_dev(synth.schedule_conf(s5), dev),

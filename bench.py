@@ -348,7 +348,7 @@ def main():
                                           "traffic": profiled_traffic("head_sample_resident_b64_vocab151936.md",
                                                                       SAMPLER_SOURCES),
                                           "bytes_per_launch": by3}}
-        # the gated Markov head on the same batch (general per-step path)
+        # the gated Markov head on the same batch (per-step path on the matrix cores)
         Wg3 = to_dev(synth.gate_weights(s3, 0.02), dev)
         cg, _ = dh.prepare_head_sample(to_dev(x3["U"], dev), to_dev(x3["h"], dev), W["W1"], W["W2"], W["w_conf"],
                                        0.0, to_dev(x3["x0"], dev), to_dev(x3["G"], dev), Wg=Wg3)
@@ -366,12 +366,13 @@ def main():
         line["extra_gated_b64"] = {
             "workload": "gated Markov head, B=64 gamma=7 V=151936 H=5120 r=256 bf16, Gumbel-max with fp32 noise",
             "us_per_call": round(usg, 2), "positions_per_s": round(64 * 7 / (usg * 1e-6), 1),
-            "roofline": {"kernel": "dspark_head_sample_gated (general path: gate and bias step per position)",
+            "roofline": {"kernel": "dspark_head_sample_gated (per-step matrix-core path: gate and bias "
+                                   "kernels per position)",
                          "bound": "hbm", "achieved": round(gbg, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbg / HBM_PEAK_GBS, 4),
                          "traffic": profiled_traffic("head_sample_gated_b64_vocab151936.md", SAMPLER_SOURCES),
                          "bytes_per_launch": byg}}
-        # the RNN head on the same batch (general per-step path)
+        # the RNN head on the same batch (per-step path on the matrix cores)
         Wr3 = tuple(to_dev(a, dev) for a in synth.rnn_weights(s3, 0.015))
         cr, _ = dh.prepare_head_sample(to_dev(x3["U"], dev), to_dev(x3["h"], dev), W["W1"], W["W2"], W["w_conf"],
                                        0.0, to_dev(x3["x0"], dev), to_dev(x3["G"], dev), Wr=Wr3)
@@ -389,7 +390,8 @@ def main():
         line["extra_rnn_b64"] = {
             "workload": "RNN head, B=64 gamma=7 V=151936 H=5120 r=256 bf16, Gumbel-max with fp32 noise",
             "us_per_call": round(usr, 2), "positions_per_s": round(64 * 7 / (usr * 1e-6), 1),
-            "roofline": {"kernel": "dspark_head_sample_rnn (general path: state and bias step per position)",
+            "roofline": {"kernel": "dspark_head_sample_rnn (per-step matrix-core path: state and bias "
+                                   "kernels per position)",
                          "bound": "hbm", "achieved": round(gbr, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbr / HBM_PEAK_GBS, 4),
                          "traffic": profiled_traffic("head_sample_rnn_b64_vocab151936.md", SAMPLER_SOURCES),

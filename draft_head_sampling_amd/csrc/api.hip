@@ -75,7 +75,7 @@ DSPARK_EXPORT dspark_status_t dspark_head_sample_gated(int64_t B, int64_t gamma,
     if (!sampler_shape_ok(B, gamma, V, H, r) || !mul_ok(r, H + r) || !mul_ok(B * (gamma + 1), r))
         return DSPARK_ERR_BAD_SHAPE;
     if (B == 0 || gamma == 0) return DSPARK_OK;
-    dspark_status_t st = check_workspace(workspace, workspace_bytes, dspark::head_sample_gated_workspace(B, gamma, r));
+    dspark_status_t st = check_workspace(workspace, workspace_bytes, dspark::head_sample_gated_workspace(B, gamma, r, dtype));
     if (st != DSPARK_OK) return st;
     if (!U || !W1 || !W2 || !w_conf || !Wg || !x0 || !tokens || !conf || !survival || (H > 0 && !h))
         return DSPARK_ERR_NULL_ARG;
@@ -96,7 +96,7 @@ DSPARK_EXPORT dspark_status_t dspark_head_sample_rnn(int64_t B, int64_t gamma, i
     if (!sampler_shape_ok(B, gamma, V, H, r) || !mul_ok(r, 2 * r + H) || !mul_ok(B * (2 * gamma + 2), r))
         return DSPARK_ERR_BAD_SHAPE;
     if (B == 0 || gamma == 0) return DSPARK_OK;
-    dspark_status_t st = check_workspace(workspace, workspace_bytes, dspark::head_sample_rnn_workspace(B, gamma, r));
+    dspark_status_t st = check_workspace(workspace, workspace_bytes, dspark::head_sample_rnn_workspace(B, gamma, r, dtype));
     if (st != DSPARK_OK) return st;
     if (!U || !W1 || !W2 || !w_conf || !Wrg || !Wrc || !x0 || !tokens || !conf || !survival || (H > 0 && !h))
         return DSPARK_ERR_NULL_ARG;
@@ -106,9 +106,9 @@ DSPARK_EXPORT dspark_status_t dspark_head_sample_rnn(int64_t B, int64_t gamma, i
 }
 
 DSPARK_EXPORT size_t dspark_head_sample_rnn_workspace_size(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r,
-                                                           int32_t) {
+                                                           int32_t dtype) {
     if (!sampler_shape_ok(B, gamma, V, H, r) || !mul_ok(r, 2 * r + H) || !mul_ok(B * (2 * gamma + 2), r)) return 0;
-    return dspark::head_sample_rnn_workspace(B, gamma, r);
+    return dspark::head_sample_rnn_workspace(B, gamma, r, dtype);
 }
 
 DSPARK_EXPORT dspark_status_t dspark_accept_rate(int64_t N, int64_t V, int32_t dtype, const void* draft,
@@ -179,9 +179,9 @@ DSPARK_EXPORT size_t dspark_head_sample_workspace_size(int64_t B, int64_t gamma,
 }
 
 DSPARK_EXPORT size_t dspark_head_sample_gated_workspace_size(int64_t B, int64_t gamma, int64_t V, int64_t H,
-                                                             int64_t r, int32_t) {
+                                                             int64_t r, int32_t dtype) {
     if (!sampler_shape_ok(B, gamma, V, H, r) || !mul_ok(r, H + r) || !mul_ok(B * (gamma + 1), r)) return 0;
-    return dspark::head_sample_gated_workspace(B, gamma, r);
+    return dspark::head_sample_gated_workspace(B, gamma, r, dtype);
 }
 
 DSPARK_EXPORT size_t dspark_accept_rate_workspace_size(int64_t N, int64_t V, int32_t) {

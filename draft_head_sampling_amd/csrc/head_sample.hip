@@ -83,6 +83,31 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// step_key and prev_token over a whole wave (every lane calls, every lane
+// gets the result): lane c reads key copy c, so the copies cost one round
+// trip instead of one each.
+__device__ __forceinline__ uint64_t wave_step_key(const uint64_t* keys, int ncopy, int64_t gamma, int64_t B, int k,
+                                                  int64_t b, int lane) {
+    uint64_t m = 0;
+    for (int c = lane; c < ncopy; c += 64) m = umax64(m, keys[(((int64_t)c * gamma + k) * B + b) * kKeyStride]);
+    for (int o = 32; o > 0; o >>= 1) m = umax64(m, shfl_xor_u64(m, o));
+    return m;
+}
+__device__ __forceinline__ int32_t wave_prev_token(int64_t b, int k, int64_t B, int64_t gamma, int64_t V,
+                                                   const int32_t* x0, const int32_t* force, const uint64_t* keys,
+                                                   int ncopy, int lane) {
+    int64_t x;
+    if (k == 0) {
+        x = x0[b];
+    } else {
+        const uint64_t key = wave_step_key(keys, ncopy, gamma, B, k - 1, b, lane);
+        if (key == 0) return -1;
+        const int32_t f = force ? force[b * gamma + k - 1] : -1;
+        x = f >= 0 ? f : key_token(key);
+    }
+    return (x >= 0 && x < V) ? (int32_t)x : -1;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void sample_init(int64_t B, int64_t gamma, int64_t H, const T* __restrict__ h,
                                                         const T* __restrict__ w_conf, uint64_t* __restrict__ keys,
@@ -219,7 +244,8 @@ __global__ __launch_bounds__(64 * kFinishMaxGamma) void sample_finish(
     for (int k0 = 0; k0 < gamma; k0 += kFinishMaxGamma) {  // gamma beyond 16 takes several rounds
         const int k = k0 + (int)(threadIdx.x >> 6);
         if (k < gamma) {
-            const int32_t x = prev_token(b, k, B, gamma, V, x0, force, keys, ncopy);
+            const int32_t x = wave_prev_token(b, k, B, gamma, V, x0, force, keys, ncopy, lane);
+            const uint64_t key = wave_step_key(keys, ncopy, gamma, B, k, b, lane);
             float s = 0.f;
             if (x >= 0)
                 for (int64_t j = lane; j < r; j += 64)
@@ -228,7 +254,7 @@ __global__ __launch_bounds__(64 * kFinishMaxGamma) void sample_finish(
             const float z = hdot[b * gamma + k] + s + b_conf;
             const float c = x >= 0 ? 1.f / (1.f + expf(-z)) : __builtin_nanf("");
             if (lane == 0) {
-                tokens[b * gamma + k] = x >= 0 ? key_token(step_key(keys, ncopy, gamma, B, k, b)) : -1;
+                tokens[b * gamma + k] = x >= 0 ? key_token(key) : -1;
                 conf[b * gamma + k] = c;
                 cs[k - k0] = c;
             }
@@ -265,8 +291,8 @@ __global__ __launch_bounds__(kThreads) void clear_words(float* p, int64_t n) {
 // the vocabulary open; this is the vanilla head's W2.  The confidence head
 // still sees e.  The hidden half of the gate, Wg[:, :H] . h_k, does not
 // depend on sampled tokens and is computed once per call; the rest runs per
-// step once the previous token is known.  Gated calls take the general
-// per-step path.
+// step once the previous token is known.  Gated calls take the per-step
+// path (on the matrix cores for bf16, r = 256, B >= 16).
 // ---------------------------------------------------------------------------
 // Dot product of n elements over the 64 lanes of a wave (every lane gets the
 // sum); 16-byte loads when both rows are 16-byte aligned and n is a whole
@@ -312,11 +338,15 @@ __global__ __launch_bounds__(kThreads) void gate_step(int64_t B, int64_t gamma, 
                                                       int64_t r, const T* __restrict__ W1, const T* __restrict__ Wg,
                                                       const int32_t* __restrict__ x0,
                                                       const int32_t* __restrict__ force, const uint64_t* keys,
-                                                      const float* __restrict__ Ah, float* __restrict__ eg) {
+                                                      int ncopy, const float* __restrict__ Ah,
+                                                      float* __restrict__ eg) {
     __shared__ int32_t xs;
     const int64_t b = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (threadIdx.x == 0) xs = prev_token(b, k, B, gamma, V, x0, force, keys);
+    if (threadIdx.x < 64) {
+        const int32_t x = wave_prev_token(b, k, B, gamma, V, x0, force, keys, ncopy, lane);
+        if (lane == 0) xs = x;
+    }
     __syncthreads();
     const int32_t x = xs;
     if (x < 0) return;  // the request stopped: its bias is never formed
@@ -382,13 +412,17 @@ __global__ __launch_bounds__(kThreads) void rnn_step(int64_t B, int64_t gamma, i
                                                      const T* __restrict__ W1, const T* __restrict__ Wrg,
                                                      const T* __restrict__ Wrc, const int32_t* __restrict__ x0,
                                                      const int32_t* __restrict__ force, const uint64_t* keys,
-                                                     const float* __restrict__ Ag, const float* __restrict__ Ac,
+                                                     int ncopy, const float* __restrict__ Ag,
+                                                     const float* __restrict__ Ac,
                                                      const float* __restrict__ s_in, float* __restrict__ s_out) {
     extern __shared__ float z_s[];  // [2r]: s_{k-1}, then e
     __shared__ int32_t xs;
     const int64_t b = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (threadIdx.x == 0) xs = prev_token(b, k, B, gamma, V, x0, force, keys);
+    if (threadIdx.x < 64) {
+        const int32_t x = wave_prev_token(b, k, B, gamma, V, x0, force, keys, ncopy, lane);
+        if (lane == 0) xs = x;
+    }
     __syncthreads();
     const int32_t x = xs;
     if (x < 0) return;  // the request stopped: its bias is never formed
@@ -1533,6 +1567,9 @@ hipError_t launch_chain(const ChainPlan& p, int64_t gamma, int64_t V, int64_t H,
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+// 16 bytes as a first-class vector: staged copies global -> registers -> LDS
+// stay in registers (a uint4 struct copy becomes a memcpy through scratch)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaRank = 256;
 constexpr int kMfmaRows = 128;      // vocabulary rows per workgroup (32 per wave)
@@ -1543,15 +1580,87 @@ constexpr int kERow = kMfmaRank + 8;  // LDS row stride of E in bf16 (padding ag
 constexpr int kURow = kMfmaRows + 8;   // LDS row stride of the U tile (bf16)
 constexpr int kGRow = kMfmaRows + 4;   // LDS row stride of the G tile (fp32)
 
-template <int NT, bool STAGE>  // 32-request tiles per workgroup: 1 or 2; STAGE: coalesced U/G tiles via LDS
+// Hidden halves of the gated and RNN heads on the matrix cores (bf16):
+//   out_z[bk][j] = W_z[j, off : off + H] . h[bk, :]   for bk < M = B gamma, j < r
+// with z = blockIdx.z choosing (Wa, outa) or (Wb, outb); W rows have stride ld.
+// grid (r / 32, ceil(M / 32), 1 or 2), 512 threads: a workgroup owns a 32 x 32
+// output tile, its eight waves take interleaved runs of 16 k-steps (of 16
+// each; the loads of a run are all in flight at once), and the eight partial
+// tiles are summed in wave order (deterministic).  Requires r % 32 == 0,
+// H % 16 == 0, ld % 8 == 0, off % 8 == 0 and 16-byte aligned W and h.
+constexpr int kHidWaves = 8;
+__global__ __launch_bounds__(64 * kHidWaves) void hidden_mfma(int64_t M, int64_t H, int64_t r, int64_t ld,
+                                                              int64_t off, const bf16_t* __restrict__ h,
+                                                              const bf16_t* __restrict__ Wa,
+                                                              const bf16_t* __restrict__ Wb, float* __restrict__ outa,
+                                                              float* __restrict__ outb) {
+    __shared__ float part[kHidWaves][16 * 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, row = lane & 31, half = lane >> 5;
+    const bf16_t* W = blockIdx.z ? Wb : Wa;
+    float* out = blockIdx.z ? outb : outa;
+    const int64_t j0 = (int64_t)blockIdx.x * 32, m0 = (int64_t)blockIdx.y * 32;
+    const int64_t mr = m0 + row < M ? m0 + row : M - 1;  // clamped rows are computed, never stored
+    const uint4* ap = reinterpret_cast<const uint4*>(W + (j0 + row) * ld + off + half * 8);
+    const uint4* bp = reinterpret_cast<const uint4*>(h + mr * H + half * 8);
+    const int steps = (int)(H / 16);
+    f32x16_t acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    constexpr int kU = 16;  // k-steps in flight per wave
+    for (int s0 = wave * kU; s0 < steps; s0 += kHidWaves * kU) {
+        uint4 a[kU], b[kU];
+#pragma unroll
+        for (int i = 0; i < kU; ++i) {
+            const int s = s0 + i < steps ? s0 + i : steps - 1;
+            a[i] = ap[2 * s];
+            b[i] = bp[2 * s];
+        }
+#pragma unroll
+        for (int i = 0; i < kU; ++i)
+            if (s0 + i < steps)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[i]),
+                                                              __builtin_bit_cast(bf16x8_t, b[i]), acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part[wave][i * 64 + lane] = acc[i];
+    __syncthreads();
+    // element e = i * 64 + l of a wave's tile: W row j0 + 8(i/4) + 4(l/32) + i%4, h row m0 + l%32
+#pragma unroll
+    for (int q = 0; q < 16 * 64 / (64 * kHidWaves); ++q) {
+        const int e = tid + 64 * kHidWaves * q, i = e >> 6, l = e & 63;
+        float v = part[0][e];
+#pragma unroll
+        for (int w = 1; w < kHidWaves; ++w) v += part[w][e];
+        const int64_t m = m0 + (l & 31), j = j0 + 8 * (i >> 2) + 4 * (l >> 5) + (i & 3);
+        if (m < M) out[m * r + j] = v;
+    }
+}
+
+bool hidden_mfma_ok(int64_t H, int64_t r, int64_t ld, int64_t off, const void* h, const void* W) {
+    return H > 0 && H % 16 == 0 && r % 32 == 0 && ld % 8 == 0 && off % 8 == 0 && (uintptr_t)h % 16 == 0 &&
+           (uintptr_t)W % 16 == 0;
+}
+
+// bf16 bits of a finite binary32 value, rounded to nearest even
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// EG: the embedding of a gated or RNN head is a binary32 vector per request
+// (eg [B][256]), not a bf16 row of W1.  It enters the products as two bf16
+// operands, hi = bf16(e) and lo = bf16(e - hi), whose sum is e to about 2^-17
+// relative, so the bias keeps binary32 accuracy at two MFMAs per k-step.
+template <int NT, bool STAGE, bool EG>  // 32-request tiles per workgroup: 1 or 2; STAGE: coalesced U/G tiles via LDS
 __global__ __launch_bounds__(256) void sample_step_mfma(int64_t B, int64_t gamma, int k, int64_t V,
                                                         const bf16_t* __restrict__ U, const bf16_t* __restrict__ W1,
                                                         const bf16_t* __restrict__ W2, const float* __restrict__ G,
                                                         const int32_t* __restrict__ x0,
                                                         const int32_t* __restrict__ force, uint64_t* keys,
-                                                        float* __restrict__ logits_out, float* __restrict__ bias_out) {
+                                                        float* __restrict__ logits_out, float* __restrict__ bias_out,
+                                                        const float* __restrict__ eg) {
     constexpr int NREQ = 32 * NT;
-    constexpr int kEBytes = NREQ * kERow * 2;
+    constexpr int kEBytes = NREQ * kERow * 2 * (EG ? 2 : 1);
     constexpr int kTileBytes = NREQ * (kURow * 2 + kGRow * 4);
     __shared__ __align__(16) uint8_t lds_raw[kEBytes > kTileBytes ? kEBytes : kTileBytes];
     uint16_t* E_lds = reinterpret_cast<uint16_t*>(lds_raw);
@@ -1591,7 +1700,7 @@ __global__ __launch_bounds__(256) void sample_step_mfma(int64_t B, int64_t gamma
     const int64_t vt = (int64_t)blockIdx.x * kMfmaRows;  // first vocabulary row of the tile
     constexpr int UCH = NREQ * kMfmaRows * 2 / 16 / 256;  // 16-byte chunks per thread
     constexpr int GCH = NREQ * kMfmaRows * 4 / 16 / 256;
-    uint4 us[STAGE ? UCH : 1], gs[STAGE ? GCH : 1];
+    u32x4_t us[STAGE ? UCH : 1], gs[STAGE ? GCH : 1];
     float u[STAGE ? 1 : NT][16], gn[STAGE ? 1 : NT][16];
     if constexpr (STAGE) {
 #pragma unroll
@@ -1599,7 +1708,7 @@ __global__ __launch_bounds__(256) void sample_step_mfma(int64_t B, int64_t gamma
             const int c = tid + 256 * i, bl = c / 16, col = (c % 16) * 8;
             const int64_t b = b0 + bl < B ? b0 + bl : B - 1;
             const int64_t vc = vt + col < V ? vt + col : V - 8;
-            us[i] = *reinterpret_cast<const uint4*>(U + (b * gamma + k) * V + vc);
+            us[i] = *reinterpret_cast<const u32x4_t*>(U + (b * gamma + k) * V + vc);
         }
         if (G) {
 #pragma unroll
@@ -1607,7 +1716,7 @@ __global__ __launch_bounds__(256) void sample_step_mfma(int64_t B, int64_t gamma
                 const int c = tid + 256 * i, bl = c / 32, col = (c % 32) * 4;
                 const int64_t b = b0 + bl < B ? b0 + bl : B - 1;
                 const int64_t vc = vt + col < V ? vt + col : V - 4;
-                gs[i] = *reinterpret_cast<const uint4*>(G + (b * gamma + k) * V + vc);
+                gs[i] = *reinterpret_cast<const u32x4_t*>(G + (b * gamma + k) * V + vc);
             }
         }
     } else {
@@ -1642,16 +1751,38 @@ __global__ __launch_bounds__(256) void sample_step_mfma(int64_t B, int64_t gamma
         if (bl4 < NREQ && part == 0) xprev[bl4] = req_ok ? (x < 0 ? -1 : x) : -1;
     }
     __syncthreads();
-    // gather E = W1[x_prev] into LDS: 4 threads per request, 128 bytes each
+    // gather E = W1[x_prev] (EG: the hi and lo halves of eg) into LDS: 4
+    // threads per request, 64 rank elements each
+    uint16_t* El_lds = E_lds + NREQ * kERow;  // EG: the lo operand
     if (bl4 < NREQ) {
         const int32_t x = xprev[bl4];
-        const uint4* src = reinterpret_cast<const uint4*>(W1 + (int64_t)(x < 0 ? 0 : x) * kMfmaRank + part * 64);
-        uint4 e[8];
+        if constexpr (EG) {
+            const float4* src = reinterpret_cast<const float4*>(eg + bq * kMfmaRank + part * 64);
+            float4 e[16];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = src[i];
-        uint4* dst = reinterpret_cast<uint4*>(E_lds + bl4 * kERow + part * 64);
+            for (int i = 0; i < 16; ++i) e[i] = src[i];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dst[i] = e[i];
+            for (int i = 0; i < 16; ++i) {
+                const float f[4] = {e[i].x, e[i].y, e[i].z, e[i].w};
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    hi[j] = bf16_rne(f[j]);
+                    lo[j] = bf16_rne(f[j] - __uint_as_float(hi[j] << 16));
+                }
+                const int o = bl4 * kERow + part * 64 + 4 * i;
+                *reinterpret_cast<uint2*>(E_lds + o) = make_uint2(hi[0] | hi[1] << 16, hi[2] | hi[3] << 16);
+                *reinterpret_cast<uint2*>(El_lds + o) = make_uint2(lo[0] | lo[1] << 16, lo[2] | lo[3] << 16);
+            }
+        } else {
+            const uint4* src = reinterpret_cast<const uint4*>(W1 + (int64_t)(x < 0 ? 0 : x) * kMfmaRank + part * 64);
+            uint4 e[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) e[i] = src[i];
+            uint4* dst = reinterpret_cast<uint4*>(E_lds + bl4 * kERow + part * 64);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dst[i] = e[i];
+        }
     }
     __syncthreads();
 
@@ -1667,6 +1798,11 @@ __global__ __launch_bounds__(256) void sample_step_mfma(int64_t B, int64_t gamma
         for (int nt = 0; nt < NT; ++nt) {
             const uint4 bw = *reinterpret_cast<const uint4*>(E_lds + (nt * 32 + row) * kERow + s * 16 + half * 8);
             acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, bw), acc[nt], 0, 0, 0);
+            if constexpr (EG) {
+                const uint4 bl = *reinterpret_cast<const uint4*>(El_lds + (nt * 32 + row) * kERow + s * 16 + half * 8);
+                acc[nt] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, bl), acc[nt], 0, 0, 0);
+            }
         }
     }
 
@@ -1675,13 +1811,13 @@ __global__ __launch_bounds__(256) void sample_step_mfma(int64_t B, int64_t gamma
 #pragma unroll
         for (int i = 0; i < UCH; ++i) {
             const int c = tid + 256 * i, bl = c / 16, col = (c % 16) * 8;
-            *reinterpret_cast<uint4*>(U_lds + bl * kURow + col) = us[i];
+            *reinterpret_cast<u32x4_t*>(U_lds + bl * kURow + col) = us[i];
         }
         if (G) {
 #pragma unroll
             for (int i = 0; i < GCH; ++i) {
                 const int c = tid + 256 * i, bl = c / 32, col = (c % 32) * 4;
-                *reinterpret_cast<uint4*>(G_lds + bl * kGRow + col) = gs[i];
+                *reinterpret_cast<u32x4_t*>(G_lds + bl * kGRow + col) = gs[i];
             }
         }
         __syncthreads();
@@ -2210,14 +2346,16 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
     const T* W2t = static_cast<const T*>(W2);
     const T* wt = static_cast<const T*>(w_conf);
 
-    // batched bf16 rank-256 requests go to the matrix cores
+    // batched bf16 rank-256 requests go to the matrix cores (a gated or RNN
+    // head reads its binary32 embeddings from the workspace with 16-byte loads)
+    const bool headed = Wg != nullptr || Wrg != nullptr;
     bool mfma = false;
     if constexpr (std::is_same_v<T, bf16_t>)
-        mfma = Wg == nullptr && Wrg == nullptr && r == kMfmaRank && B >= kMfmaMinBatch &&
-               ((uintptr_t)W1 % 16 == 0) && ((uintptr_t)W2 % 16 == 0);
+        mfma = r == kMfmaRank && B >= kMfmaMinBatch && ((uintptr_t)W1 % 16 == 0) && ((uintptr_t)W2 % 16 == 0) &&
+               (!headed || (uintptr_t)ws % 16 == 0);
     if constexpr (std::is_same_v<T, bf16_t>) {
-        // resident W2: one persistent kernel for the whole block
-        const ResidentPlan rp = mfma ? resident_plan(B, V) : ResidentPlan{};
+        // resident W2 (the plain Markov head only): one persistent kernel for the whole block
+        const ResidentPlan rp = (mfma && !headed) ? resident_plan(B, V) : ResidentPlan{};
         // (stored logits or bias go to the general kernel: any store in the
         // resident kernel's tile loop makes its loads wait for one another)
         if (rp.nwg > 0 && lo == nullptr && bo == nullptr && (uintptr_t)U % 8 == 0 &&
@@ -2259,13 +2397,31 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
     const bool rnn = Wrg != nullptr;
     float* gate_ws = (Wg || rnn) ? s.hdot + ((B * gamma + 63) / 64) * 64 : nullptr;
     const int64_t gate_words = (rnn ? 2 * gamma + 2 : gamma + 1) * r;  // per request
-    if (rnn) {
+    // the hidden halves: a bf16 contraction [B gamma, H] x [H, r] on the
+    // matrix cores where the shapes allow, else one wave per dot
+    bool hmfma = false;
+    if constexpr (std::is_same_v<T, bf16_t>) {
+        if (rnn)
+            hmfma = hidden_mfma_ok(H, r, 2 * r + H, 2 * r, h, Wrg) && (uintptr_t)Wrc % 16 == 0;
+        else if (Wg)
+            hmfma = hidden_mfma_ok(H, r, H + r, 0, h, Wg);
+        if (hmfma) {
+            const int64_t M = B * gamma;
+            const dim3 grid((uint32_t)(r / 32), (uint32_t)((M + 31) / 32), rnn ? 2u : 1u);
+            hipLaunchKernelGGL(hidden_mfma, grid, dim3(64 * kHidWaves), 0, stream, M, H, r, rnn ? 2 * r + H : H + r,
+                               rnn ? 2 * r : (int64_t)0, static_cast<const bf16_t*>(h),
+                               static_cast<const bf16_t*>(rnn ? Wrg : Wg), static_cast<const bf16_t*>(Wrc), gate_ws,
+                               gate_ws + B * gamma * r);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
+    }
+    if (rnn && !hmfma) {
         const dim3 grid((uint32_t)(B * gamma), (uint32_t)((r + kGateRows - 1) / kGateRows));
         hipLaunchKernelGGL((rnn_hidden<T>), grid, dim3(kThreads), 0, stream, H, r, static_cast<const T*>(h), Wrgt,
                            Wrct, gate_ws, gate_ws + B * gamma * r);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    if (Wg) {
+    if (Wg && !hmfma) {
         const dim3 grid((uint32_t)(B * gamma), (uint32_t)((r + kGateRows - 1) / kGateRows));
         hipLaunchKernelGGL((gate_hidden<T>), grid, dim3(kThreads), 0, stream, H, r, static_cast<const T*>(h), Wgt,
                            gate_ws);
@@ -2284,7 +2440,7 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
         if (Wg) {
             const dim3 grid((uint32_t)B, (uint32_t)((r + kGateRows - 1) / kGateRows));
             hipLaunchKernelGGL((gate_step<T>), grid, dim3(kThreads), 0, stream, B, gamma, k, V, H, r, W1t, Wgt, x0,
-                               force, s.keys, gate_ws, gate_ws + B * gamma * r);
+                               force, s.keys, ncopy, gate_ws, gate_ws + B * gamma * r);
             if ((err = hipGetLastError()) != hipSuccess) return err;
             eg = gate_ws + B * gamma * r;
         }
@@ -2292,7 +2448,7 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
             float* st = gate_ws + 2 * B * gamma * r;
             const dim3 grid((uint32_t)B, (uint32_t)((r + kGateRows - 1) / kGateRows));
             hipLaunchKernelGGL((rnn_step<T>), grid, dim3(kThreads), sizeof(float) * 2 * r, stream, B, gamma, k, V, H,
-                               r, W1t, Wrgt, Wrct, x0, force, s.keys, gate_ws, gate_ws + B * gamma * r,
+                               r, W1t, Wrgt, Wrct, x0, force, s.keys, ncopy, gate_ws, gate_ws + B * gamma * r,
                                st + ((k + 1) % 2) * B * r, st + (k % 2) * B * r);
             if ((err = hipGetLastError()) != hipSuccess) return err;
             eg = st + (k % 2) * B * r;
@@ -2302,13 +2458,19 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
                 const dim3 grid((uint32_t)((V + kMfmaRows - 1) / kMfmaRows), (uint32_t)((B + 63) / 64));
                 // coalesced tiles need 16-byte aligned U and G rows
                 const bool stage = V % 8 == 0 && (uintptr_t)U % 16 == 0 && (G == nullptr || (uintptr_t)G % 16 == 0);
-#define DSPARK_MFMA(NT, ST)                                                                                         \
-    hipLaunchKernelGGL((sample_step_mfma<NT, ST>), grid, dim3(256), 0, stream, B, gamma, k, V, Ut, W1t, W2t, G, x0, \
-                       force, s.keys, lo, bo)
-                if (B <= 32) {
-                    if (stage) DSPARK_MFMA(1, true); else DSPARK_MFMA(1, false);
+#define DSPARK_MFMA(NT, ST, EG)                                                                                   \
+    hipLaunchKernelGGL((sample_step_mfma<NT, ST, EG>), grid, dim3(256), 0, stream, B, gamma, k, V, Ut, W1t, W2t, G, \
+                       x0, force, s.keys, lo, bo, eg)
+                if (eg) {
+                    if (B <= 32) {
+                        if (stage) DSPARK_MFMA(1, true, true); else DSPARK_MFMA(1, false, true);
+                    } else {
+                        if (stage) DSPARK_MFMA(2, true, true); else DSPARK_MFMA(2, false, true);
+                    }
+                } else if (B <= 32) {
+                    if (stage) DSPARK_MFMA(1, true, false); else DSPARK_MFMA(1, false, false);
                 } else {
-                    if (stage) DSPARK_MFMA(2, true); else DSPARK_MFMA(2, false);
+                    if (stage) DSPARK_MFMA(2, true, false); else DSPARK_MFMA(2, false, false);
                 }
 #undef DSPARK_MFMA
                 err = hipGetLastError();
@@ -2354,16 +2516,20 @@ size_t head_sample_workspace(int64_t B, int64_t gamma, int64_t, int64_t r, int d
     return steps;
 }
 
-size_t head_sample_gated_workspace(int64_t B, int64_t gamma, int64_t r) {
-    // the general path's keys (one copy) and hidden dots, then the gate words
-    return ((size_t)(8 * kKeyStride * B * gamma) + 255) / 256 * 256 + ((size_t)(4 * B * gamma) + 255) / 256 * 256 +
-           ((size_t)(4 * B * (gamma + 1) * r) + 255) / 256 * 256;
+// the per-step path's keys (kKeyCopies copies on the matrix-core path, else
+// one) and hidden dots, then a gated or RNN head's words
+size_t headed_workspace(int64_t B, int64_t gamma, int64_t r, int dtype, int64_t words_per_request) {
+    const int64_t ncopy = (dtype == kBF16 && r == kMfmaRank && B >= kMfmaMinBatch) ? kKeyCopies : 1;
+    return ((size_t)(8 * kKeyStride * ncopy * B * gamma) + 255) / 256 * 256 +
+           ((size_t)(4 * B * gamma) + 255) / 256 * 256 + ((size_t)(4 * B * words_per_request) + 255) / 256 * 256;
 }
 
-size_t head_sample_rnn_workspace(int64_t B, int64_t gamma, int64_t r) {
-    // the general path's keys (one copy) and hidden dots, then the RNN words
-    return ((size_t)(8 * kKeyStride * B * gamma) + 255) / 256 * 256 + ((size_t)(4 * B * gamma) + 255) / 256 * 256 +
-           ((size_t)(4 * B * (2 * gamma + 2) * r) + 255) / 256 * 256;
+size_t head_sample_gated_workspace(int64_t B, int64_t gamma, int64_t r, int dtype) {
+    return headed_workspace(B, gamma, r, dtype, (gamma + 1) * r);
+}
+
+size_t head_sample_rnn_workspace(int64_t B, int64_t gamma, int64_t r, int dtype) {
+    return headed_workspace(B, gamma, r, dtype, (2 * gamma + 2) * r);
 }
 
 hipError_t head_sample_launch(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int dtype, const void* U,

@@ -61,8 +61,8 @@ hipError_t accept_rate_launch(int64_t N, int64_t V, int dtype, const void* d, in
                               int64_t ldt, float* out, void* ws, hipStream_t stream);
 
 size_t head_sample_workspace(int64_t B, int64_t gamma, int64_t V, int64_t r, int dtype);
-size_t head_sample_gated_workspace(int64_t B, int64_t gamma, int64_t r);
-size_t head_sample_rnn_workspace(int64_t B, int64_t gamma, int64_t r);
+size_t head_sample_gated_workspace(int64_t B, int64_t gamma, int64_t r, int dtype);
+size_t head_sample_rnn_workspace(int64_t B, int64_t gamma, int64_t r, int dtype);
 // Wg and Wrg == nullptr: the vanilla Markov head; Wg: the gated head; Wrg and
 // Wrc: the RNN head (both on the general path)
 hipError_t head_sample_launch(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int dtype, const void* U,

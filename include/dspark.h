@@ -123,7 +123,10 @@ dspark_status_t dspark_head_sample(int64_t B, int64_t gamma, int64_t V, int64_t 
  *   Wg  [r][H + r] gate weights, columns [h ; W1 row], in the dtype of the others.
  * Workspace: dspark_head_sample_gated_workspace_size bytes, zero-filled before
  * the first use and left zero-filled by every completed call.  The call runs
- * the general per-step kernels with one gate launch per step.
+ * the per-step kernels with one gate launch per step; bf16 with r = 256,
+ * B >= 16 and a 16-byte aligned workspace takes the bias on the matrix cores,
+ * with e' split into two bf16 operands (hi, and the rounding remainder) so
+ * that the bias keeps binary32 accuracy.
  */
 dspark_status_t dspark_head_sample_gated(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int32_t dtype,
                                          const void* U, const void* h, const void* W1, const void* W2,
@@ -147,7 +150,8 @@ dspark_status_t dspark_head_sample_gated(int64_t B, int64_t gamma, int64_t V, in
  *             in the dtype of the others.
  * Workspace: dspark_head_sample_rnn_workspace_size bytes, zero-filled before the
  * first use and left zero-filled by every completed call.  The call runs the
- * general per-step kernels with one state launch per step.
+ * per-step kernels with one state launch per step (matrix cores as for
+ * dspark_head_sample_gated).
  */
 dspark_status_t dspark_head_sample_rnn(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int32_t dtype,
                                        const void* U, const void* h, const void* W1, const void* W2,

@@ -41,15 +41,16 @@ def normwise_rel(gpu: np.ndarray, ref: np.ndarray) -> float:
     return float((num / den).max())
 
 
-def run_gpu_sampler(x: dict, w: dict, force: np.ndarray | None, want_logits: bool, device="cuda"):
+def run_gpu_sampler(x: dict, w: dict, force: np.ndarray | None, want_logits: bool, device="cuda", workspace=None):
     out = dh.head_sample(dev(x["U"], device), dev(x["h"], device), dev(w["W1"], device), dev(w["W2"], device),
                          dev(w["w_conf"], device), w["b_conf"], dev(x["x0"], device), dev(x.get("G"), device),
                          dev(force, device), want_logits=want_logits, Wg=dev(w.get("Wg"), device),
-                         Wr=None if w.get("Wr") is None else tuple(dev(a, device) for a in w["Wr"]))
+                         Wr=None if w.get("Wr") is None else tuple(dev(a, device) for a in w["Wr"]),
+                         workspace=workspace)
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 
-def sampler_parity(x: dict, w: dict, want_logits: bool = False, device="cuda"):
+def sampler_parity(x: dict, w: dict, want_logits: bool = False, device="cuda", workspace=None):
     """Compare the HIP sampler with the oracle under the near-tie protocol.
 
     At the first unexplained token mismatch of a request the oracle's margin
@@ -66,7 +67,7 @@ def sampler_parity(x: dict, w: dict, want_logits: bool = False, device="cuda"):
         f = force if tie.any() else None
         ref = oracle.head_sample(x["U"], x["h"], w["W1"], w["W2"], w["w_conf"], w["b_conf"], x["x0"], x.get("G"),
                                  f, want_logits=want_logits or tie.any(), Wg=w.get("Wg"), Wr=w.get("Wr"))
-        got = run_gpu_sampler(x, w, f, want_logits, device)
+        got = run_gpu_sampler(x, w, f, want_logits, device, workspace)
         mism = (got["tokens"] != ref["tokens"]) & ~tie
         if not mism.any():
             break

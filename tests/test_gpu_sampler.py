@@ -264,6 +264,32 @@ def test_gated_head_full_vocabulary():
     assert ties <= 1
 
 
+@pytest.mark.parametrize("B,V,gamma", [(16, 4099, 3), (40, 30001, 5)])
+def test_gated_head_matrix_core_shapes(B, V, gamma):
+    """Rank 256 and B >= 16 in bf16 put the gated head's bias on the matrix
+    cores (one and two 32-request tiles, ragged vocabulary tail); stored logits
+    and bias compared too."""
+    s = synth.SamplerShape(B=B, gamma=gamma, V=V, H=256, r=256, dtype="bf16", w_sd=0.3, U_sd=1.0, wc_sd=0.02,
+                           gumbel=True, seed=synth.SEED_BASE + 140 + V)
+    w = dict(synth.sampler_weights(s), Wg=synth.gate_weights(s, 1.0 / np.sqrt(512)))
+    x = synth.sampler_batch(s)
+    sampler_parity(x, w, want_logits=True)
+
+
+def test_gated_head_batched_serving_workload():
+    """B=64 at the serving shape (V=151936, H=5120, r=256, bf16, Gumbel-max) in
+    the launch configuration the benchmark times; every request checked and
+    the workspace left zero."""
+    s = synth.SAMPLER_B64
+    w = dict(synth.sampler_weights(s), Wg=synth.gate_weights(s, 0.02))
+    x = synth.sampler_batch(s)
+    n = dh.lib().dspark_head_sample_gated_workspace_size(64, 7, s.V, s.H, s.r, 1)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    _, _, ties = sampler_parity(x, w, workspace=ws)
+    assert ties <= 2
+    assert int(ws.count_nonzero()) == 0
+
+
 def test_gated_head_leaves_workspace_zero():
     s = synth.SamplerShape(B=3, gamma=4, V=5000, H=64, r=16, dtype="bf16", w_sd=0.3, U_sd=1.0, wc_sd=0.02,
                            gumbel=False, seed=synth.SEED_BASE + 77)
@@ -297,6 +323,28 @@ def test_rnn_head_bf16_shapes(B, V, gamma, H, r):
     w = dict(synth.sampler_weights(s), Wr=synth.rnn_weights(s, 1.0 / np.sqrt(2 * r + H)))
     x = synth.sampler_batch(s)
     sampler_parity(x, w, want_logits=True)
+
+
+@pytest.mark.parametrize("B,V,gamma", [(16, 4099, 3), (40, 30001, 5)])
+def test_rnn_head_matrix_core_shapes(B, V, gamma):
+    s = synth.SamplerShape(B=B, gamma=gamma, V=V, H=256, r=256, dtype="bf16", w_sd=0.3, U_sd=1.0, wc_sd=0.02,
+                           gumbel=True, seed=synth.SEED_BASE + 160 + V)
+    w = dict(synth.sampler_weights(s), Wr=synth.rnn_weights(s, 1.0 / np.sqrt(768)))
+    x = synth.sampler_batch(s)
+    sampler_parity(x, w, want_logits=True)
+
+
+def test_rnn_head_batched_serving_workload():
+    """B=64 at the serving shape in the benchmark's launch configuration;
+    every request checked and the workspace left zero."""
+    s = synth.SAMPLER_B64
+    w = dict(synth.sampler_weights(s), Wr=synth.rnn_weights(s, 0.015))
+    x = synth.sampler_batch(s)
+    n = dh.lib().dspark_head_sample_rnn_workspace_size(64, 7, s.V, s.H, s.r, 1)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    _, _, ties = sampler_parity(x, w, workspace=ws)
+    assert ties <= 2
+    assert int(ws.count_nonzero()) == 0
 
 
 def test_rnn_head_full_vocabulary_and_workspace():

@@ -117,7 +117,19 @@ __global__ __launch_bounds__(kThreads) void sample_init(int64_t B, int64_t gamma
     const int64_t b = bk / gamma, k = bk % gamma;
     if (threadIdx.x < ncopy) *key_at(keys, threadIdx.x, gamma, B, (int)k, b) = 0;
     float s = 0.f;
-    for (int64_t i = threadIdx.x; i < H; i += kThreads) s += load_elem(w_conf, i) * load_elem(h, bk * H + i);
+    constexpr int E = Chunk<T>::N;  // 16-byte loads where rows allow
+    const T* hr = h + bk * H;
+    if (H % E == 0 && (uintptr_t)w_conf % 16 == 0 && (uintptr_t)hr % 16 == 0) {
+        for (int64_t i = (int64_t)threadIdx.x * E; i < H; i += (int64_t)kThreads * E) {
+            float x[E], y[E];
+            Chunk<T>::load(w_conf + i, x);
+            Chunk<T>::load(hr + i, y);
+#pragma unroll
+            for (int q = 0; q < E; ++q) s = __builtin_fmaf(x[q], y[q], s);
+        }
+    } else {
+        for (int64_t i = threadIdx.x; i < H; i += kThreads) s += load_elem(w_conf, i) * load_elem(hr, i);
+    }
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
     __syncthreads();
@@ -1595,10 +1607,17 @@ __global__ __launch_bounds__(64 * kHidWaves) void hidden_mfma(int64_t M, int64_t
                                                               const bf16_t* __restrict__ Wb, float* __restrict__ outa,
                                                               float* __restrict__ outb) {
     __shared__ float part[kHidWaves][16 * 64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, row = lane & 31, half = lane >> 5;
+    // the wave index as a scalar: the k-step guards below are then uniform branches
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row = lane & 31, half = lane >> 5;
     const bf16_t* W = blockIdx.z ? Wb : Wa;
     float* out = blockIdx.z ? outb : outa;
-    const int64_t j0 = (int64_t)blockIdx.x * 32, m0 = (int64_t)blockIdx.y * 32;
+    // Workgroups go round-robin over the 8 XCDs (each with its own L2); when
+    // the tile count allows, XCD x takes the x-th eighth of the tiles in
+    // row-major order, so it reads a few h rows and W once instead of all of h.
+    const uint32_t nj = gridDim.x, T = gridDim.x * gridDim.y, L = blockIdx.x + nj * blockIdx.y;
+    const uint32_t t = T % 8 == 0 ? (L % 8) * (T / 8) + L / 8 : L;
+    const int64_t j0 = (int64_t)(t % nj) * 32, m0 = (int64_t)(t / nj) * 32;
     const int64_t mr = m0 + row < M ? m0 + row : M - 1;  // clamped rows are computed, never stored
     const uint4* ap = reinterpret_cast<const uint4*>(W + (j0 + row) * ld + off + half * 8);
     const uint4* bp = reinterpret_cast<const uint4*>(h + mr * H + half * 8);
@@ -1607,20 +1626,23 @@ __global__ __launch_bounds__(64 * kHidWaves) void hidden_mfma(int64_t M, int64_t
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
     constexpr int kU = 16;  // k-steps in flight per wave
-    for (int s0 = wave * kU; s0 < steps; s0 += kHidWaves * kU) {
+    int s0 = wave * kU;
+    for (; s0 + kU <= steps; s0 += kHidWaves * kU) {  // whole runs, no guards
         uint4 a[kU], b[kU];
 #pragma unroll
         for (int i = 0; i < kU; ++i) {
-            const int s = s0 + i < steps ? s0 + i : steps - 1;
-            a[i] = ap[2 * s];
-            b[i] = bp[2 * s];
+            a[i] = ap[2 * (s0 + i)];
+            b[i] = bp[2 * (s0 + i)];
         }
+        __builtin_amdgcn_sched_barrier(0);  // every load of the run issued before the first product
 #pragma unroll
         for (int i = 0; i < kU; ++i)
-            if (s0 + i < steps)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[i]),
-                                                              __builtin_bit_cast(bf16x8_t, b[i]), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[i]),
+                                                          __builtin_bit_cast(bf16x8_t, b[i]), acc, 0, 0, 0);
     }
+    for (int s = s0; s < steps && s < s0 + kU; ++s)  // the one partial run, if any
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ap[2 * s]),
+                                                      __builtin_bit_cast(bf16x8_t, bp[2 * s]), acc, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) part[wave][i * 64 + lane] = acc[i];
     __syncthreads();

@@ -47,6 +47,8 @@ def _load():
         lib.oracle_prefix_schedule.argtypes = [i64, i64, vp, vp, i64, vp, vp, vp, vp, vp]
         lib.oracle_verify.restype = ctypes.c_int
         lib.oracle_verify.argtypes = [i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_block_loss.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, d, vp, vp,
+                                          vp, d, d, d, d, vp, vp, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -190,4 +192,32 @@ def verify(d, t, x, u, G, n_draft=None):
     _load().oracle_verify(B, gamma, V, dt, _p(d), _p(t), _p(x), _p(n_draft), _p(u), _p(G), _p(out["n_acc"]),
                           _p(out["next_token"]), _p(out["accept_prob"]), _p(out["margin"]), _p(out["sample_pos"]),
                           _p(out["residual"]))
+    return out
+
+
+def block_loss(U, t, h, W1, W2, w_conf, b_conf, xp, y, mask=None, decay=4.0, a_ce=0.1, a_l1=0.9, a_conf=1.0):
+    """Teacher-forced block bias with the joint loss (fp64).
+
+    U, t [N, gamma, V], h [N, gamma, H], W1, W2 [V, r], w_conf [H + r] in
+    float32 or bfloat16 bits; xp, y [N, gamma] int32 (given previous tokens,
+    target ids); mask [N, gamma] float32 or None.  Returns dict(ce, l1, conf,
+    bce [N, gamma], loss, L_ce, L_l1, L_conf)."""
+    U, t, h, W1, W2, w_conf = (np.ascontiguousarray(a) for a in (U, t, h, W1, W2, w_conf))
+    dt = _dtype_of(U)
+    N, gamma, V = U.shape
+    H = h.shape[2]
+    r = W1.shape[1]
+    assert t.shape == U.shape and W2.shape == (V, r) and w_conf.shape == (H + r,)
+    xp = np.ascontiguousarray(xp, dtype=np.int32)
+    y = np.ascontiguousarray(y, dtype=np.int32)
+    mask = None if mask is None else np.ascontiguousarray(mask, dtype=np.float32)
+    out = {k: np.empty((N, gamma), np.float64) for k in ("ce", "l1", "conf", "bce")}
+    loss = np.empty(4, np.float64)
+    rc = _load().oracle_block_loss(N, gamma, V, H, r, dt, _p(U), _p(t), _p(h), _p(W1), _p(W2), _p(w_conf),
+                                   float(b_conf), _p(xp), _p(y), _p(mask), float(decay), float(a_ce), float(a_l1),
+                                   float(a_conf), _p(out["ce"]), _p(out["l1"]), _p(out["conf"]), _p(out["bce"]),
+                                   _p(loss))
+    if rc != 0:
+        raise MemoryError("oracle_block_loss: allocation failed")
+    out.update(loss=float(loss[0]), L_ce=float(loss[1]), L_l1=float(loss[2]), L_conf=float(loss[3]))
     return out

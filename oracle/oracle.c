@@ -426,3 +426,93 @@ int oracle_verify(int64_t B, int64_t gamma, int64_t V, int dtype, const void* d,
     }
     return 0;
 }
+
+/*
+ * Teacher-forced block bias with the joint loss ([W] section 7.2, the joint
+ * loss of the training loop; the training loop's apply_block_logits step
+ * applies the sequential head with given previous tokens).  Positions are
+ * [N][gamma]; for each position (n, k), k = 0..gamma-1, with x = xp[n][k]
+ * (the given previous token) and y = y[n][k] (the target id):
+ *   e[j]     = W1[x, j]
+ *   d[v]     = U[n,k,v] + sum_j W2[v, j] e[j]          (draft logits, eq. 5)
+ *   ce       = logsumexp(d) - d[y]                     (cross-entropy)
+ *   l1       = 1/2 sum_v |softmax(d)_v - softmax(t_nk)_v|
+ *   cstar    = 1 - l1                                  (eq. 8)
+ *   conf     = sigmoid(sum_i w[i] h[n,k,i] + sum_j w[H+j] e[j] + b_conf)
+ *   bce      = -(cstar log(conf) + (1 - cstar) log(1 - conf))
+ *   omega    = mask[n][k] * exp(-k / decay)            (position weight,
+ *              exp(-(k-1)/gamma_decay) for 1-based k)
+ * and the loss is a_ce L_ce + a_l1 L_l1 + a_conf L_conf with each term the
+ * omega-weighted mean over the positions that count,
+ *   L_x = sum omega x / sum omega        (0 when sum omega = 0).
+ * Readings: the pages name the three terms, their weights and the decay but
+ * not the reduction over positions; the weighted mean is the plainest one.
+ * A position counts when its mask is non-zero and x and y lie in [0, V); a
+ * position whose x or y is out of range gets NaN in every per-position
+ * output.  mask may be NULL (all ones).
+ * Outputs: ce, l1, conf, bce [N][gamma]; loss[4] = (L, L_ce, L_l1, L_conf).
+ */
+int oracle_block_loss(int64_t N, int64_t gamma, int64_t V, int64_t H, int64_t r, int dtype, const void* U,
+                      const void* t, const void* h, const void* W1, const void* W2, const void* w, double b_conf,
+                      const int32_t* xp, const int32_t* y, const float* mask, double decay, double a_ce,
+                      double a_l1, double a_conf, double* ce, double* l1, double* conf, double* bce, double* loss) {
+    double* d = (double*)malloc(sizeof(double) * (size_t)(V > 0 ? V : 1));
+    if (!d) return -2;
+    double sw = 0.0, s_ce = 0.0, s_l1 = 0.0, s_bce = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < gamma; ++k) {
+            const int64_t pos = n * gamma + k;
+            const int32_t x = xp[pos], yy = y[pos];
+            if (x < 0 || x >= V || yy < 0 || yy >= V) {
+                ce[pos] = l1[pos] = conf[pos] = bce[pos] = NAN;
+                continue;
+            }
+            for (int64_t v = 0; v < V; ++v) {
+                double b = 0.0;
+                for (int64_t j = 0; j < r; ++j) b += val(W2, dtype, v * r + j) * val(W1, dtype, (int64_t)x * r + j);
+                d[v] = val(U, dtype, pos * V + v) + b;
+            }
+            double md = -INFINITY, mt = -INFINITY;
+            for (int64_t v = 0; v < V; ++v) {
+                if (d[v] > md) md = d[v];
+                const double tv = val(t, dtype, pos * V + v);
+                if (tv > mt) mt = tv;
+            }
+            double sd = 0.0, st = 0.0;
+            for (int64_t v = 0; v < V; ++v) {
+                sd += exp(d[v] - md);
+                st += exp(val(t, dtype, pos * V + v) - mt);
+            }
+            double dist = 0.0;
+            for (int64_t v = 0; v < V; ++v)
+                dist += fabs(exp(d[v] - md) / sd - exp(val(t, dtype, pos * V + v) - mt) / st);
+            const double c_ce = md + log(sd) - d[yy];
+            const double c_l1 = 0.5 * dist;
+            const double cstar = 1.0 - c_l1;
+            double z = b_conf;
+            for (int64_t i = 0; i < H; ++i) z += val(w, dtype, i) * val(h, dtype, pos * H + i);
+            for (int64_t j = 0; j < r; ++j) z += val(w, dtype, H + j) * val(W1, dtype, (int64_t)x * r + j);
+            const double c = 1.0 / (1.0 + exp(-z));
+            const double c_bce = -(cstar * log(c) + (1.0 - cstar) * log(1.0 - c));
+            ce[pos] = c_ce;
+            l1[pos] = c_l1;
+            conf[pos] = c;
+            bce[pos] = c_bce;
+            const double om = (mask ? (double)mask[pos] : 1.0) * exp(-(double)k / decay);
+            if (om != 0.0) {
+                sw += om;
+                s_ce += om * c_ce;
+                s_l1 += om * c_l1;
+                s_bce += om * c_bce;
+            }
+        }
+    }
+    free(d);
+    const double Lce = sw != 0.0 ? s_ce / sw : 0.0, Ll1 = sw != 0.0 ? s_l1 / sw : 0.0,
+                 Lcf = sw != 0.0 ? s_bce / sw : 0.0;
+    loss[0] = a_ce * Lce + a_l1 * Ll1 + a_conf * Lcf;
+    loss[1] = Lce;
+    loss[2] = Ll1;
+    loss[3] = Lcf;
+    return 0;
+}

@@ -667,3 +667,124 @@ def test_rnn_state_feeds_the_next_step():
     out = oracle.head_sample(**p, force=force, Wr=(Wrg, Wrc), want_logits=True)
     rows = p["W2"].astype(np.float64).sum(axis=1)
     np.testing.assert_allclose(out["bias"], np.broadcast_to(rows, out["bias"].shape), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Teacher-forced block bias with the joint loss ([W] section 7.2): pinned by
+# closed forms, by the accept-rate oracle, and by the binary entropy.
+# ---------------------------------------------------------------------------
+def _bl_inputs(N, gamma, V, H, r, seed=0):
+    rng = np.random.default_rng(seed)
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    return dict(U=f(N, gamma, V), t=f(N, gamma, V), h=f(N, gamma, H), W1=f(V, r), W2=f(V, r), w_conf=f(H + r),
+                b_conf=0.0, xp=rng.integers(0, V, (N, gamma)).astype(np.int32),
+                y=rng.integers(0, V, (N, gamma)).astype(np.int32))
+
+
+def test_block_loss_uniform_draft_closed_form():
+    """W2 = 0 and U = 0 make the draft uniform: CE = log V; t = U gives L1 = 0,
+    c* = 1; w = 0, b = 0 give conf = 1/2 and BCE = log 2."""
+    V = 37
+    x = _bl_inputs(2, 3, V, 4, 5)
+    x.update(U=np.zeros((2, 3, V), np.float32), t=np.zeros((2, 3, V), np.float32),
+             W2=np.zeros((V, 5), np.float32), w_conf=np.zeros(9, np.float32))
+    o = oracle.block_loss(**x)
+    np.testing.assert_allclose(o["ce"], np.log(V), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o["l1"], 0.0, atol=1e-15)
+    np.testing.assert_allclose(o["conf"], 0.5, atol=1e-15)
+    np.testing.assert_allclose(o["bce"], np.log(2.0), atol=1e-12)
+    assert abs(o["loss"] - (0.1 * np.log(V) + np.log(2.0))) < 1e-12
+
+
+def test_block_loss_disjoint_supports():
+    """Draft and target concentrated on different tokens: L1 = 1, c* = 0."""
+    V = 20
+    x = _bl_inputs(1, 2, V, 3, 2)
+    U = np.zeros((1, 2, V), np.float32)
+    t = np.zeros((1, 2, V), np.float32)
+    U[0, :, 3] = 200.0
+    t[0, :, 11] = 200.0
+    x.update(U=U, t=t, W2=np.zeros((V, 2), np.float32), y=np.array([[3, 11]], np.int32))
+    o = oracle.block_loss(**x)
+    np.testing.assert_allclose(o["l1"], 1.0, atol=1e-12)
+    assert abs(o["ce"][0, 0]) < 1e-12 and abs(o["ce"][0, 1] - 200.0) < 1e-9
+    # with c* = 0 the BCE is -log(1 - conf)
+    np.testing.assert_allclose(o["bce"], -np.log1p(-o["conf"]), rtol=1e-12)
+
+
+def test_block_loss_uses_the_given_previous_token():
+    """W1 = I and W2 = c I (r = V): the bias is c on the given previous token
+    only, so with U = 0 and y = x, CE = log(V - 1 + e^c) - c; with y != x,
+    CE = log(V - 1 + e^c)."""
+    V, c = 12, 2.5
+    x = _bl_inputs(2, 4, V, 3, V, seed=3)
+    x.update(U=np.zeros((2, 4, V), np.float32), W1=np.eye(V, dtype=np.float32),
+             W2=(c * np.eye(V)).astype(np.float32))
+    xp = np.array([[1, 5, 5, 0], [11, 2, 7, 3]], np.int32)
+    y = np.array([[1, 5, 6, 0], [10, 2, 7, 4]], np.int32)
+    x.update(xp=xp, y=y)
+    o = oracle.block_loss(**x)
+    lse = np.log(V - 1 + np.exp(c))
+    np.testing.assert_allclose(o["ce"], np.where(y == xp, lse - c, lse), rtol=1e-12)
+
+
+def test_block_loss_l1_matches_accept_rate_oracle():
+    """With W2 = 0 the draft logits are U, so 1 - L1 is the accept-rate
+    oracle's c* of (U, t) row by row."""
+    x = _bl_inputs(3, 4, 300, 6, 8, seed=9)
+    x["W2"] = np.zeros_like(x["W2"])
+    o = oracle.block_loss(**x)
+    cs = oracle.accept_rate(x["U"].reshape(12, 300), x["t"].reshape(12, 300))
+    np.testing.assert_allclose(1.0 - o["l1"].reshape(-1), cs, atol=1e-13)
+
+
+def test_block_loss_bce_is_binary_entropy_at_calibration():
+    """V = 2: p_d = (1/2, 1/2), p_t = (1/4, 3/4) give L1 = 1/4, c* = 3/4; with
+    conf = sigmoid(log 3) = 3/4 the BCE is the binary entropy H(3/4), its
+    minimum over conf."""
+    x = _bl_inputs(1, 1, 2, 2, 1)
+    x.update(U=np.zeros((1, 1, 2), np.float32), t=np.array([[[0.0, np.log(3.0)]]], np.float32),
+             W2=np.zeros((2, 1), np.float32), w_conf=np.zeros(3, np.float32), b_conf=float(np.log(3.0)))
+    o = oracle.block_loss(**x)
+    assert abs(o["l1"][0, 0] - 0.25) < 1e-7
+    Hb = -(0.75 * np.log(0.75) + 0.25 * np.log(0.25))
+    assert abs(o["conf"][0, 0] - 0.75) < 1e-7 and abs(o["bce"][0, 0] - Hb) < 1e-6
+    for b in (np.log(2.0), np.log(4.0)):  # any other confidence costs more
+        x["b_conf"] = float(b)
+        assert oracle.block_loss(**x)["bce"][0, 0] > Hb + 1e-3
+
+
+def test_block_loss_confidence_head_sees_h_and_the_previous_embedding():
+    V, H, r = 9, 4, 3
+    x = _bl_inputs(1, 2, V, H, r, seed=5)
+    w = np.zeros(H + r, np.float32)
+    w[1], w[H + 2] = 0.5, -2.0
+    x.update(w_conf=w, b_conf=0.25)
+    o = oracle.block_loss(**x)
+    z = 0.5 * x["h"][0, :, 1].astype(np.float64) - 2.0 * x["W1"][x["xp"][0], 2].astype(np.float64) + 0.25
+    np.testing.assert_allclose(o["conf"][0], 1 / (1 + np.exp(-z)), rtol=1e-12)
+
+
+def test_block_loss_position_weights_and_mask():
+    """One unmasked position: each term is that position's value.  Positions
+    k = 1 and 3 (1-based): weights 1 and exp(-(3-1)/4) ([W] 7.2).  Invalid
+    tokens give NaN and drop out."""
+    x = _bl_inputs(1, 4, 40, 3, 4, seed=2)
+    o = oracle.block_loss(**x)
+    m = np.zeros((1, 4), np.float32)
+    m[0, 2] = 1.0
+    one = oracle.block_loss(**x, mask=m)
+    assert abs(one["L_ce"] - o["ce"][0, 2]) < 1e-12 and abs(one["L_l1"] - o["l1"][0, 2]) < 1e-12
+    assert abs(one["L_conf"] - o["bce"][0, 2]) < 1e-12
+    m = np.array([[1, 0, 1, 0]], np.float32)
+    two = oracle.block_loss(**x, mask=m, a_ce=1.0, a_l1=0.0, a_conf=0.0)
+    w3 = np.exp(-(3 - 1) / 4.0)
+    assert abs(two["loss"] - (o["ce"][0, 0] + w3 * o["ce"][0, 2]) / (1 + w3)) < 1e-12
+    x["y"][0, 1] = 40
+    x["xp"][0, 3] = -1
+    bad = oracle.block_loss(**x)
+    assert np.isnan(bad["ce"][0, 1]) and np.isnan(bad["bce"][0, 3])
+    w = np.exp(-np.array([0, 2]) / 4.0)
+    assert abs(bad["L_l1"] - (w[0] * o["l1"][0, 0] + w[1] * o["l1"][0, 2]) / w.sum()) < 1e-12
+    m0 = np.zeros((1, 4), np.float32)
+    assert oracle.block_loss(**x, mask=m0)["loss"] == 0.0

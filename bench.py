@@ -92,6 +92,7 @@ def profiled_traffic(profile: str, sources: list[str]):
 SAMPLER_SOURCES = ["draft_head_sampling_amd/csrc/head_sample.hip", "draft_head_sampling_amd/csrc/internal.h"]
 VERIFY_SOURCES = ["draft_head_sampling_amd/csrc/verify.hip", "draft_head_sampling_amd/csrc/internal.h"]
 ACCEPT_SOURCES = ["draft_head_sampling_amd/csrc/accept_rate.hip", "draft_head_sampling_amd/csrc/internal.h"]
+LOSS_SOURCES = ["draft_head_sampling_amd/csrc/block_loss.hip", "draft_head_sampling_amd/csrc/internal.h"]
 
 
 def main():
@@ -409,6 +410,37 @@ def main():
             b1.record(stream)
             torch.cuda.synchronize()
             line[f"extra_sched_{kind}_us"] = round(b0.elapsed_time(b1) * 1e3 / 50, 2)
+        # the teacher-forced block bias with the joint loss at 2048 training positions
+        s6 = synth.LOSS_TRAIN
+        x6 = synth.loss_inputs(s6)
+        d6 = {k: (to_dev(v, dev) if isinstance(v, np.ndarray) else v) for k, v in x6.items()}
+        del x6
+        c6, _ = dh.prepare_block_loss(d6["U"], d6["t"], d6["h"], d6["W1"], d6["W2"], d6["w_conf"], d6["b_conf"],
+                                      d6["xp"], d6["y"])
+        for _ in range(2):
+            c6()
+        torch.cuda.synchronize()
+        b0.record(stream)
+        for _ in range(5):
+            c6()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        us6 = b0.elapsed_time(b1) * 1e3 / 5
+        M6 = s6.N * s6.gamma
+        by6 = (2 * M6 * s6.V * 2 + s6.V * s6.r * 2 + M6 * s6.r * 2 + M6 * s6.H * 2 + (s6.H + s6.r) * 2 + 8 * M6
+               + 16 * M6 + 16)
+        gb6 = by6 / (us6 * 1e-6) / 1e9
+        line["extra_block_loss"] = {
+            "workload": "teacher-forced block bias + joint loss (CE, L1, confidence BCE), 2048 positions "
+                        "(128 anchors x block 16), V=151936 H=5120 r=256 bf16",
+            "us_per_call": round(us6, 2), "positions_per_s": round(M6 / (us6 * 1e-6), 1),
+            "mfma_tflops": round(2 * M6 * s6.V * s6.r / (us6 * 1e-6) / 1e12, 2),
+            "roofline": {"kernel": "dspark_block_loss (two tile passes over U and t, W2 on the matrix cores)",
+                         "bound": "hbm", "achieved": round(gb6, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gb6 / HBM_PEAK_GBS, 4),
+                         "traffic": profiled_traffic("block_loss_2048x151936.md", LOSS_SOURCES),
+                         "bytes_per_launch": by6}}
+        del d6
 
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

@@ -73,6 +73,11 @@ def lib() -> ctypes.CDLL:
     L.dspark_verify.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dspark_verify_workspace_size.restype = sz
     L.dspark_verify_workspace_size.argtypes = [i64, i64, i64, i32]
+    L.dspark_block_loss.restype = i32
+    L.dspark_block_loss.argtypes = [i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, f32, f32,
+                                    f32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dspark_block_loss_workspace_size.restype = sz
+    L.dspark_block_loss_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32]
     _lib = L
     return L
 
@@ -298,6 +303,43 @@ def verify(draft, target, draft_tokens, uniforms, gumbel, n_draft=None, *, want_
     None)."""
     call, outs = prepare_verify(draft, target, draft_tokens, uniforms, gumbel, n_draft,
                                 want_accept_prob=want_accept_prob, workspace=workspace)
+    call()
+    outs.pop("_workspace")
+    return outs
+
+
+def prepare_block_loss(U, t, h, W1, W2, w_conf, b_conf, xp, y, mask=None, *, decay=4.0, a_ce=0.1, a_l1=0.9,
+                       a_conf=1.0, workspace=None, stream=None):
+    """Validate once and return (call, outputs) for dspark_block_loss: the
+    teacher-forced block bias with the joint loss over U, t [N, gamma, V],
+    h [N, gamma, H], W1, W2 [V, 256], w_conf [H + 256] (bfloat16), xp, y
+    [N, gamma] int32 and mask [N, gamma] float32 or None."""
+    N, gamma, V = U.shape
+    r = W1.shape[1]
+    H = h.shape[2] if h is not None else 0
+    dt = _dtype_code(U)
+    dev = U.device
+    outs = {k: torch.empty((N, gamma), dtype=torch.float32, device=dev) for k in ("ce", "l1", "conf", "bce")}
+    outs["loss"] = torch.empty(4, dtype=torch.float32, device=dev)
+    ws, wsb = _workspace(int(lib().dspark_block_loss_workspace_size(N, gamma, V, H, r, dt)), dev, workspace)
+    args = (N, gamma, V, H, r, dt, _dev(U, "U", U.dtype, (N, gamma, V)), _dev(t, "t", U.dtype, (N, gamma, V)),
+            _opt(h, "h", U.dtype, (N, gamma, H)), _dev(W1, "W1", U.dtype, (V, r)), _dev(W2, "W2", U.dtype, (V, r)),
+            _dev(w_conf, "w_conf", U.dtype, (H + r,)), float(b_conf), _dev(xp, "xp", torch.int32, (N, gamma)),
+            _dev(y, "y", torch.int32, (N, gamma)), _opt(mask, "mask", torch.float32, (N, gamma)), float(decay),
+            float(a_ce), float(a_l1), float(a_conf), _dev(outs["ce"], "ce"), _dev(outs["l1"], "l1"),
+            _dev(outs["conf"], "conf"), _dev(outs["bce"], "bce"), _dev(outs["loss"], "loss"),
+            None if ws is None else ws.data_ptr(), wsb, _stream(dev) if stream is None else stream)
+    fn = partial(lib().dspark_block_loss, *args)
+    outs["_workspace"] = ws
+    return (lambda: _check("dspark_block_loss", fn())), outs
+
+
+def block_loss(U, t, h, W1, W2, w_conf, b_conf, xp, y, mask=None, *, decay=4.0, a_ce=0.1, a_l1=0.9, a_conf=1.0,
+               workspace=None):
+    """Teacher-forced block bias with the joint loss.  Returns dict(ce, l1,
+    conf, bce [N, gamma], loss [4] = (L, L_ce, L_l1, L_conf))."""
+    call, outs = prepare_block_loss(U, t, h, W1, W2, w_conf, b_conf, xp, y, mask, decay=decay, a_ce=a_ce,
+                                    a_l1=a_l1, a_conf=a_conf, workspace=workspace)
     call()
     outs.pop("_workspace")
     return outs

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libdspark.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "accept_rate.hip", "head_sample.hip", "prefix_schedule.hip", "verify.hip"]
+SOURCES = ["api.hip", "accept_rate.hip", "block_loss.hip", "head_sample.hip", "prefix_schedule.hip", "verify.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [

@@ -193,3 +193,39 @@ DSPARK_EXPORT size_t dspark_prefix_schedule_workspace_size(int64_t B, int64_t ga
     if (B < 1 || gamma < 0 || !mul_ok(B, gamma) || B * gamma > kMaxSchedPairs) return 0;
     return dspark::prefix_schedule_workspace(B, gamma);
 }
+
+namespace {
+constexpr int64_t kMaxLossChunks = 65535;  // vocabulary chunks of 512 rows along grid.y
+
+bool block_loss_dims_ok(int64_t N, int64_t gamma, int64_t V, int64_t H) {
+    if (N < 0 || gamma < 0 || V < 1 || V > kMaxLossChunks * 512 || H < 0) return false;
+    return mul_ok(N, gamma) && N * gamma <= 0x7fffffff && mul_ok(N * gamma, V) && mul_ok(N * gamma, H);
+}
+}  // namespace
+
+DSPARK_EXPORT size_t dspark_block_loss_workspace_size(int64_t N, int64_t gamma, int64_t V, int64_t H, int64_t r,
+                                                      int32_t) {
+    if (!block_loss_dims_ok(N, gamma, V, H) || r < 1) return 0;
+    return dspark::block_loss_workspace(N * gamma, V);
+}
+
+DSPARK_EXPORT dspark_status_t dspark_block_loss(int64_t N, int64_t gamma, int64_t V, int64_t H, int64_t r,
+                                                int32_t dtype, const void* U, const void* t, const void* h,
+                                                const void* W1, const void* W2, const void* w_conf, float b_conf,
+                                                const int32_t* xp, const int32_t* y, const float* mask, float decay,
+                                                float a_ce, float a_l1, float a_conf, float* ce, float* l1,
+                                                float* conf, float* bce, float* loss, void* workspace,
+                                                size_t workspace_bytes, void* stream) {
+    if (dtype != DSPARK_BF16) return DSPARK_ERR_BAD_DTYPE;
+    if (!block_loss_dims_ok(N, gamma, V, H) || !(decay > 0.f)) return DSPARK_ERR_BAD_SHAPE;
+    const int64_t M = N * gamma;
+    if (!loss) return DSPARK_ERR_NULL_ARG;
+    if (M > 0 && (!U || !t || !W1 || !W2 || !w_conf || !xp || !y || !ce || !l1 || !conf || !bce || (H > 0 && !h)))
+        return DSPARK_ERR_NULL_ARG;
+    dspark_status_t st = check_workspace(workspace, workspace_bytes, dspark::block_loss_workspace(M, V));
+    if (st != DSPARK_OK) return st;
+    if (!dspark::block_loss_shape_ok(r, W1, W2, workspace)) return DSPARK_ERR_BAD_SHAPE;
+    return hip_status(dspark::block_loss_launch(N, gamma, V, H, U, t, h, W1, W2, w_conf, b_conf, xp, y, mask, decay,
+                                                a_ce, a_l1, a_conf, ce, l1, conf, bce, loss, workspace,
+                                                static_cast<hipStream_t>(stream)));
+}

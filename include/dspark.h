@@ -244,6 +244,44 @@ dspark_status_t dspark_verify(int64_t B, int64_t gamma, int64_t V, int32_t dtype
                               const float* uniforms, const float* gumbel, int32_t* n_accepted, int32_t* next_token,
                               float* accept_prob, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * dspark_block_loss -- the teacher-forced block bias with the joint training
+ * loss ([W] 7.2, the joint loss; the training loop's sequential-head step with
+ * given previous tokens, [W] 3.2 and paper eq. 5 for the bias).  Positions
+ * are [N][gamma] (N anchors, block gamma); for position (n, k), k = 0-based,
+ * with x = xp[n][k] and target id y = y[n][k]:
+ *   d[v]  = U[n][k][v] + W2[v] . W1[x]                 (draft logits)
+ *   ce    = logsumexp(d) - d[y]
+ *   l1    = 1/2 sum_v |softmax(d)_v - softmax(t[n][k])_v|,   c* = 1 - l1
+ *   conf  = sigmoid(w_conf . [h[n][k]; W1[x]] + b_conf)
+ *   bce   = -(c* log conf + (1 - c*) log(1 - conf))
+ *   omega = mask[n][k] * exp(-k / decay)   (exp(-(k-1)/decay), k 1-based)
+ *   loss  = a_ce L_ce + a_l1 L_l1 + a_conf L_conf,  L_x = sum omega x / sum omega
+ * (the pages name the terms, their weights 0.1 / 0.9 / 1.0 and the decay 4.0,
+ * not the reduction over positions; the weighted mean is the reading here; 0
+ * when no position counts).  A position counts when its mask is non-zero and
+ * x and y lie in [0, V); one with x or y out of range gets NaN outputs.
+ *
+ *   dtype must be DSPARK_BF16 and r must be 256 (the matrix-core tile);
+ *   W1 and W2 16-byte aligned; otherwise DSPARK_ERR_BAD_DTYPE / _BAD_SHAPE.
+ *   V <= 65535 * 512; decay > 0.
+ *   U, t          [N][gamma][V] bf16  draft backbone and target logits
+ *   h             [N][gamma][H] bf16  (NULL when H = 0)
+ *   W1, W2        [V][256] bf16;  w_conf [H + 256] bf16
+ *   xp, y         [N][gamma] int32    given previous tokens, target ids
+ *   mask          [N][gamma] fp32, optional (NULL = all ones)
+ *   ce, l1, conf, bce  [N][gamma] fp32 out;  loss [4] fp32 out: (L, L_ce, L_l1, L_conf)
+ * Workspace: dspark_block_loss_workspace_size bytes, any contents (every word
+ * is written before it is read).  Repeated calls give bitwise-identical
+ * results (every reduction has a fixed order).
+ */
+dspark_status_t dspark_block_loss(int64_t N, int64_t gamma, int64_t V, int64_t H, int64_t r, int32_t dtype,
+                                  const void* U, const void* t, const void* h, const void* W1, const void* W2,
+                                  const void* w_conf, float b_conf, const int32_t* xp, const int32_t* y,
+                                  const float* mask, float decay, float a_ce, float a_l1, float a_conf, float* ce,
+                                  float* l1, float* conf, float* bce, float* loss, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* Workspace bytes needed by the entry point of the same name for these
  * shapes; 0 if it needs none.  Pure host functions with no side effects. */
 size_t dspark_head_sample_workspace_size(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int32_t dtype);
@@ -254,6 +292,7 @@ size_t dspark_head_sample_rnn_workspace_size(int64_t B, int64_t gamma, int64_t V
 size_t dspark_accept_rate_workspace_size(int64_t N, int64_t V, int32_t dtype);
 size_t dspark_prefix_schedule_workspace_size(int64_t B, int64_t gamma);
 size_t dspark_verify_workspace_size(int64_t B, int64_t gamma, int64_t V, int32_t dtype);
+size_t dspark_block_loss_workspace_size(int64_t N, int64_t gamma, int64_t V, int64_t H, int64_t r, int32_t dtype);
 
 /* Static, NUL-terminated description of a status code. */
 const char* dspark_status_string(dspark_status_t status);

@@ -30,7 +30,8 @@ _lib = None
 # one master seed per workload, one tag per tensor
 SEED_BASE = 0xD5A20000
 TAG = {"W1": 1, "W2": 2, "U": 3, "h": 4, "w": 5, "x0": 6, "G": 7, "d": 8, "t": 9, "conf": 10, "sps": 11,
-       "vd": 12, "vt": 13, "vtb": 14, "vx": 15, "vu": 16, "vG": 17, "Wg": 18, "Wrg": 19, "Wrc": 20}
+       "vd": 12, "vt": 13, "vtb": 14, "vx": 15, "vu": 16, "vG": 17, "Wg": 18, "Wrg": 19, "Wrc": 20,
+       "lU": 21, "lt": 22, "lh": 23, "ly": 24, "lx": 25}
 
 
 def build(force: bool = True) -> str:
@@ -300,4 +301,51 @@ def verify_inputs(s: VerifyShape, B: int | None = None) -> dict:
         # rounded to binary32 and kept below 1 (the accept test needs u < 1)
         u=np.minimum(uniform(key(s.seed, TAG["vu"]), (B, g)).astype(np.float32), np.float32(1 - 2**-24)),
         G=gumbel(key(s.seed, TAG["vG"]), (B, V)).astype(np.float32),
+    )
+
+
+@dataclass
+class LossShape:
+    """Teacher-forced block-loss inputs: N sequences' anchors x gamma block
+    positions.  Draft backbone logits U ~ N(0, U_sd), target logits t =
+    scale*U + N(0, t_sd), hidden states h ~ N(0, 1), targets y uniform in
+    [0, V); the given previous tokens are the anchor (uniform) at the first
+    position and the previous target after it (teacher forcing).  Weights as
+    for the sampler: W1, W2 ~ N(0, w_sd), w_conf ~ N(0, wc_sd)."""
+    N: int
+    gamma: int
+    V: int
+    H: int
+    r: int
+    U_sd: float
+    scale: float
+    t_sd: float
+    w_sd: float
+    wc_sd: float
+    seed: int
+
+
+# 2048 training positions (8 sequences x 16 anchors x block 16) at the full vocabulary
+LOSS_TRAIN = LossShape(N=128, gamma=16, V=151936, H=5120, r=256, U_sd=3.0, scale=0.8, t_sd=1.5, w_sd=0.02,
+                       wc_sd=0.01, seed=SEED_BASE + 8)
+
+
+def loss_inputs(s: LossShape, N: int | None = None) -> dict:
+    N = s.N if N is None else N
+    g, V = s.gamma, s.V
+    U = normal(key(s.seed, TAG["lU"]), (N, g, V), 0.0, s.U_sd, "bf16")
+    y = uniform_int(key(s.seed, TAG["ly"]), (N, g), 0, V).astype(np.int32)
+    xp = np.empty((N, g), np.int32)
+    xp[:, 0] = uniform_int(key(s.seed, TAG["lx"]), (N,), 0, V).astype(np.int32)
+    xp[:, 1:] = y[:, :-1]
+    return dict(
+        U=U,
+        t=affine_noise(key(s.seed, TAG["lt"]), U, s.scale, 0.0, s.t_sd),
+        h=normal(key(s.seed, TAG["lh"]), (N, g, s.H), 0.0, 1.0, "bf16"),
+        W1=normal(key(s.seed, TAG["W1"]), (V, s.r), 0.0, s.w_sd, "bf16"),
+        W2=normal(key(s.seed, TAG["W2"]), (V, s.r), 0.0, s.w_sd, "bf16"),
+        w_conf=normal(key(s.seed, TAG["w"]), (s.H + s.r,), 0.0, s.wc_sd, "bf16"),
+        b_conf=0.0,
+        xp=xp,
+        y=y,
     )

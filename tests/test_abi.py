@@ -165,3 +165,26 @@ def test_head_sample_rnn_host_checks(L):
     assert g() == WORKSPACE
     assert g(ws=FAKE * 256, wsb=need, Wrg=None) == NULL_ARG
     assert g(ws=FAKE * 256, wsb=need, Wrc=None) == NULL_ARG
+
+
+def _bl(L, N=2, gamma=3, V=100, H=8, r=256, dtype=1, U=FAKE, t=FAKE, h=FAKE, W1=FAKE, W2=FAKE, w=FAKE, xp=FAKE,
+        y=FAKE, decay=4.0, ce=FAKE, l1=FAKE, conf=FAKE, bce=FAKE, loss=FAKE, ws=None, wsb=0):
+    return L.dspark_block_loss(N, gamma, V, H, r, dtype, U, t, h, W1, W2, w, 0.0, xp, y, None, decay, 0.1, 0.9, 1.0,
+                               ce, l1, conf, bce, loss, ws, wsb, None)
+
+
+def test_block_loss_host_checks(L):
+    need = L.dspark_block_loss_workspace_size(2, 3, 100, 8, 256, 1)
+    assert need > 0 and need % 256 == 0
+    assert L.dspark_block_loss_workspace_size(2, 3, 65535 * 512 + 1, 8, 256, 1) == 0
+    assert _bl(L, dtype=0) == BAD_DTYPE  # bf16 only
+    assert _bl(L, V=0) == BAD_SHAPE
+    assert _bl(L, N=-1) == BAD_SHAPE
+    assert _bl(L, decay=0.0) == BAD_SHAPE
+    assert _bl(L, loss=None) == NULL_ARG
+    for kw in ("U", "t", "h", "W1", "W2", "w", "xp", "y", "ce", "l1", "conf", "bce"):
+        assert _bl(L, **{kw: None}) == NULL_ARG, kw
+    assert _bl(L) == WORKSPACE
+    assert _bl(L, ws=FAKE * 256, wsb=need - 1) == WORKSPACE
+    assert _bl(L, r=128, ws=FAKE * 256, wsb=need) == BAD_SHAPE  # the tiles are rank 256
+    assert _bl(L, W2=FAKE + 2, ws=FAKE * 256, wsb=need) == BAD_SHAPE  # 16-byte rows

@@ -1,0 +1,122 @@
+"""GPU parity of dspark_block_loss (teacher-forced block bias with the joint
+loss) against the CPU oracle.
+
+Tolerances, from the arithmetic (bf16 inputs, fp32 accumulation and fp32
+exp/log against the oracle's fp64):
+  l1 (and so c* = 1 - l1)   abs <= 1e-4 (the accept-rate tolerance)
+  ce = lse(d) - d[y]        abs <= 2e-4 + 1e-5 |ce| (lse of a 151936-term row)
+  conf                      abs <= 1e-5
+  bce                       abs <= 2e-4 + 1e-5 |bce|
+  loss terms                rel <= 1e-4
+Per-position outputs of positions with an out-of-range token are NaN on both
+sides.  At the full training size the oracle checks three whole sequences (48
+positions) and the loss is checked against the fp64 weighted mean of the
+GPU's own per-position outputs, which holds at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import draft_head_sampling_amd as dh
+import oracle
+import synth
+from helpers import dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _tiny(N, gamma, V, H=64, seed=0):
+    s = synth.LossShape(N=N, gamma=gamma, V=V, H=H, r=256, U_sd=3.0, scale=0.8, t_sd=1.5, w_sd=0.05, wc_sd=0.05,
+                        seed=synth.SEED_BASE + 300 + seed)
+    return synth.loss_inputs(s)
+
+
+def _gpu(x, mask=None, **kw):
+    out = dh.block_loss(dev(x["U"]), dev(x["t"]), dev(x["h"]), dev(x["W1"]), dev(x["W2"]), dev(x["w_conf"]),
+                        x["b_conf"], dev(x["xp"]), dev(x["y"]), dev(mask), **kw)
+    return {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
+
+
+def _check_positions(got, ref, sl=slice(None)):
+    for k in ("ce", "l1", "conf", "bce"):
+        g, r = got[k][sl], ref[k]
+        assert np.array_equal(np.isnan(g), np.isnan(r)), k
+    fin = np.isfinite(ref["ce"])
+    tol = {"ce": 2e-4 + 1e-5 * np.abs(ref["ce"]), "l1": 1e-4, "conf": 1e-5, "bce": 2e-4 + 1e-5 * np.abs(ref["bce"])}
+    for k, t in tol.items():
+        err = np.abs(got[k][sl] - ref[k])
+        t = np.broadcast_to(t, err.shape)
+        assert (err[fin] <= t[fin]).all(), f"{k}: max err {err[fin].max():.3g}"
+
+
+def _check_loss(got, ref):
+    for i, k in enumerate(("loss", "L_ce", "L_l1", "L_conf")):
+        assert abs(got["loss"][i] - ref[k]) <= 1e-4 * max(1.0, abs(ref[k])), (k, got["loss"][i], ref[k])
+
+
+def _ref(x, mask=None, **kw):
+    return oracle.block_loss(x["U"], x["t"], x["h"], x["W1"], x["W2"], x["w_conf"], x["b_conf"], x["xp"], x["y"],
+                             mask, **kw)
+
+
+@pytest.mark.parametrize("N,gamma,V", [(2, 3, 1000), (5, 7, 777), (9, 16, 2053), (3, 16, 4099), (1, 1, 8)])
+def test_shapes(N, gamma, V):
+    """Several position tiles and vocabulary chunks, ragged tails, V not a
+    multiple of 8 (element loads)."""
+    x = _tiny(N, gamma, V, seed=V)
+    got, ref = _gpu(x), _ref(x)
+    _check_positions(got, ref)
+    _check_loss(got, ref)
+
+
+def test_mask_weights_coefficients_and_invalid_tokens():
+    x = _tiny(4, 8, 3001, seed=1)
+    x["y"][0, 2] = 3001
+    x["xp"][1, 5] = -4
+    x["y"][3, 7] = -1
+    mask = (np.arange(32).reshape(4, 8) % 3 != 0).astype(np.float32)
+    mask[2, 1] = 0.25
+    kw = dict(decay=2.5, a_ce=0.3, a_l1=0.5, a_conf=2.0)
+    got, ref = _gpu(x, mask, **kw), _ref(x, mask, **kw)
+    _check_positions(got, ref)
+    _check_loss(got, ref)
+    assert np.isnan(got["ce"][0, 2]) and np.isnan(got["bce"][1, 5])
+
+
+def test_all_masked_and_no_positions():
+    x = _tiny(2, 4, 500, seed=2)
+    got = _gpu(x, np.zeros((2, 4), np.float32))
+    assert np.all(got["loss"] == 0.0)
+    z = torch.zeros((0, 4, 500), dtype=torch.bfloat16, device="cuda")
+    out = dh.block_loss(z, z, torch.zeros((0, 4, 64), dtype=torch.bfloat16, device="cuda"), dev(x["W1"]),
+                        dev(x["W2"]), dev(x["w_conf"]), 0.0, torch.zeros((0, 4), dtype=torch.int32, device="cuda"),
+                        torch.zeros((0, 4), dtype=torch.int32, device="cuda"))
+    assert torch.all(out["loss"] == 0)
+
+
+def test_repeat_calls_are_bitwise_identical():
+    x = _tiny(6, 16, 9000, seed=3)
+    args = [dev(x[k]) for k in ("U", "t", "h", "W1", "W2", "w_conf")] + [0.0, dev(x["xp"]), dev(x["y"])]
+    ws = torch.full((dh.lib().dspark_block_loss_workspace_size(6, 16, 9000, 64, 256, 1),), 77, dtype=torch.uint8,
+                    device="cuda")  # any contents: every word is written before it is read
+    a = dh.block_loss(*args, workspace=ws)
+    b = dh.block_loss(*args)
+    for k in a:
+        assert torch.equal(a[k].view(torch.int32), b[k].view(torch.int32)), k
+
+
+def test_training_workload_full_size():
+    """2048 positions x V=151936 bf16, the launch configuration the benchmark
+    times: three whole sequences against the oracle, the loss against the fp64
+    weighted mean of the per-position outputs."""
+    s = synth.LOSS_TRAIN
+    x = synth.loss_inputs(s)
+    got = _gpu(x)
+    for n in (0, 77, 127):
+        sub = {k: (v[n:n + 1] if k in ("U", "t", "h", "xp", "y") else v) for k, v in x.items()}
+        _check_positions(got, _ref(sub), sl=slice(n, n + 1))
+    w = np.exp(-np.arange(s.gamma) / 4.0)[None, :] * np.ones((s.N, 1))
+    terms = [np.sum(w * got[k]) / w.sum() for k in ("ce", "l1", "bce")]
+    want = [0.1 * terms[0] + 0.9 * terms[1] + 1.0 * terms[2]] + terms
+    assert np.allclose(got["loss"], want, rtol=1e-5, atol=1e-6), (got["loss"], want)
+    assert np.all((got["l1"] > 0) & (got["l1"] < 1))

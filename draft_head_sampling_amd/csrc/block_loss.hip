@@ -13,7 +13,7 @@
 //                  through LDS; per lane an online max/sum of d and t; the
 //                  partial (max, sum) pairs of each vocabulary chunk go to
 //                  the workspace, and the chunk holding y writes d[y];
-//   loss_merge     per position: the chunk partials merged in chunk order
+//   loss_merge     per position: the chunk partials merged in a fixed order
 //                  into logsumexp(d) and logsumexp(t), and the confidence
 //                  logit w . [h; W1[xp]] + b;
 //   loss_tiles<2>  the same tiles again, summing |p_d - p_t| per chunk;
@@ -79,11 +79,11 @@ __device__ __forceinline__ void load_tile(const bf16_t* __restrict__ X, int64_t 
 }
 
 // grid (ceil(M / 64), ceil(V / 512)), 256 threads.  PASS 1 writes the
-// chunk's (max, sum) of d and t per position to stats [chunks][M][4] and d[y]
+// chunk's (max, sum) of d and t per position to stats [M][chunks][4] and d[y]
 // to dy [M]; PASS 2 reads lse [M][2] and writes the chunk's sum of
-// |p_d - p_t| to l1p [chunks][M].
+// |p_d - p_t| to l1p [M][chunks].
 template <int PASS, bool VEC>
-__global__ __launch_bounds__(256) void loss_tiles(int64_t M, int64_t V, const bf16_t* __restrict__ U,
+__global__ __launch_bounds__(256) void loss_tiles(int64_t M, int64_t V, int64_t nchunk, const bf16_t* __restrict__ U,
                                                   const bf16_t* __restrict__ T, const bf16_t* __restrict__ W1,
                                                   const bf16_t* __restrict__ W2, const int32_t* __restrict__ xp,
                                                   const int32_t* __restrict__ y, float* __restrict__ stats,
@@ -165,33 +165,40 @@ __global__ __launch_bounds__(256) void loss_tiles(int64_t M, int64_t V, const bf
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             const int pl = nt * 32 + row;
-            float dv[16], tv[16];
-            float mdn = -INFINITY, mtn = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            // d and t of element r (rows past V: -inf); read again from LDS
+            // in each sweep rather than held, which keeps the register count
+            // at two waves per SIMD
+            auto dval = [&](int r) {
                 const int vl = wave * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-                const int64_t v = vt + vl;
-                const bool ok = v < V;
-                dv[r] = ok ? bf(U_lds[pl * kTRow + vl]) + acc[nt][r] : -INFINITY;
-                tv[r] = ok ? bf(T_lds[pl * kTRow + vl]) : -INFINITY;
-                if (PASS == 1) {
-                    mdn = fmaxf(mdn, dv[r]);
-                    mtn = fmaxf(mtn, tv[r]);
-                    if (ok && v == yv[nt] && p0 + pl < M) dy[p0 + pl] = dv[r];
-                }
-            }
+                return vt + vl < V ? bf(U_lds[pl * kTRow + vl]) + acc[nt][r] : -INFINITY;
+            };
+            auto tval = [&](int r) {
+                const int vl = wave * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                return vt + vl < V ? bf(T_lds[pl * kTRow + vl]) : -INFINITY;
+            };
             if (PASS == 1) {
+                float mdn = -INFINITY, mtn = -INFINITY;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float dr = dval(r);
+                    mdn = fmaxf(mdn, dr);
+                    mtn = fmaxf(mtn, tval(r));
+                    const int64_t v = vt + wave * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                    if (v == yv[nt] && v < V && p0 + pl < M) dy[p0 + pl] = dr;
+                }
                 if (mdn > -INFINITY) {  // the lane has rows in this tile
                     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) s1 += __expf(dv[r] - mdn), s2 += __expf(tv[r] - mtn);
+                    for (int r = 0; r < 16; ++r) s1 += __expf(dval(r) - mdn), s2 += __expf(tval(r) - mtn);
                     merge_ms(md[nt], sd[nt], mdn, s1);
                     merge_ms(mt[nt], st[nt], mtn, s2);
                 }
             } else {
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (dv[r] > -INFINITY) l1[nt] += fabsf(__expf(dv[r] - ld[nt]) - __expf(tv[r] - lt[nt]));
+                for (int r = 0; r < 16; ++r) {
+                    const float dr = dval(r);
+                    if (dr > -INFINITY) l1[nt] += fabsf(__expf(dr - ld[nt]) - __expf(tval(r) - lt[nt]));
+                }
             }
         }
     }
@@ -225,9 +232,9 @@ __global__ __launch_bounds__(256) void loss_tiles(int64_t M, int64_t V, const bf
             }
             float4 o;
             o.x = m1, o.y = s1, o.z = m2, o.w = s2;
-            reinterpret_cast<float4*>(stats)[chunk * M + p] = o;
+            reinterpret_cast<float4*>(stats)[p * nchunk + chunk] = o;
         } else {
-            l1p[chunk * M + p] = ((red[0][tid][0] + red[1][tid][0]) + red[2][tid][0]) + red[3][tid][0];
+            l1p[p * nchunk + chunk] = ((red[0][tid][0] + red[1][tid][0]) + red[2][tid][0]) + red[3][tid][0];
         }
     }
 }
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(256) void loss_merge(int64_t M, int64_t V, int64_t 
     const int tid = threadIdx.x;
     float m1 = -INFINITY, s1 = 0.f, m2 = -INFINITY, s2 = 0.f;
     for (int64_t c = tid; c < nchunk; c += 256) {
-        const float4 o = reinterpret_cast<const float4*>(stats)[c * M + p];
+        const float4 o = reinterpret_cast<const float4*>(stats)[p * nchunk + c];
         merge_ms(m1, s1, o.x, o.y);
         merge_ms(m2, s2, o.z, o.w);
     }
@@ -272,7 +279,9 @@ __global__ __launch_bounds__(256) void loss_merge(int64_t M, int64_t V, int64_t 
     }
 }
 
-// grid ceil(M / 256): per-position outputs and weighted terms [M][4].
+// grid ceil(M / 4), 256 threads: one wave per position (the chunk partials
+// summed lane-strided, then across the wave in a fixed order); per-position
+// outputs and weighted terms [M][4].
 __global__ __launch_bounds__(256) void loss_final(int64_t M, int64_t gamma, int64_t V, int64_t nchunk,
                                                   const float* __restrict__ l1p, const float* __restrict__ dy,
                                                   const float* __restrict__ lse, const float* __restrict__ zc,
@@ -281,16 +290,19 @@ __global__ __launch_bounds__(256) void loss_final(int64_t M, int64_t gamma, int6
                                                   float* __restrict__ ce, float* __restrict__ l1,
                                                   float* __restrict__ conf, float* __restrict__ bce,
                                                   float* __restrict__ terms) {
-    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (p >= M) return;
+    const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (p >= M) return;  // whole waves
+    float s = 0.f;
+    for (int64_t c = lane; c < nchunk; c += 64) s += l1p[p * nchunk + c];
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    if (lane != 0) return;
     const int32_t x = xp[p], yy = y[p];
     float4 tm;
     tm.x = tm.y = tm.z = tm.w = 0.f;
     if (x < 0 || x >= V || yy < 0 || yy >= V) {
         ce[p] = l1[p] = conf[p] = bce[p] = __builtin_nanf("");
     } else {
-        float s = 0.f;
-        for (int64_t c = 0; c < nchunk; ++c) s += l1p[c * M + p];
         const float d1 = 0.5f * s;
         const float c_ce = lse[2 * p] - dy[p];
         const float cstar = 1.f - d1;
@@ -391,10 +403,10 @@ hipError_t block_loss_launch(int64_t N, int64_t gamma, int64_t V, int64_t H, con
     const bool vec = V % 8 == 0 && (uintptr_t)U % 16 == 0 && (uintptr_t)t % 16 == 0;
     const dim3 grid((uint32_t)((M + kPos - 1) / kPos), (uint32_t)nchunk);
     if (vec)
-        hipLaunchKernelGGL((loss_tiles<1, true>), grid, dim3(256), 0, stream, M, V, Ub, Tb, W1b, W2b, xp, y, s.stats,
-                           s.dy, s.lse, s.l1p);
+        hipLaunchKernelGGL((loss_tiles<1, true>), grid, dim3(256), 0, stream, M, V, nchunk, Ub, Tb, W1b, W2b, xp, y,
+                           s.stats, s.dy, s.lse, s.l1p);
     else
-        hipLaunchKernelGGL((loss_tiles<1, false>), grid, dim3(256), 0, stream, M, V, Ub, Tb, W1b, W2b, xp, y,
+        hipLaunchKernelGGL((loss_tiles<1, false>), grid, dim3(256), 0, stream, M, V, nchunk, Ub, Tb, W1b, W2b, xp, y,
                            s.stats, s.dy, s.lse, s.l1p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -403,13 +415,13 @@ hipError_t block_loss_launch(int64_t N, int64_t gamma, int64_t V, int64_t H, con
                        s.zc);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (vec)
-        hipLaunchKernelGGL((loss_tiles<2, true>), grid, dim3(256), 0, stream, M, V, Ub, Tb, W1b, W2b, xp, y, s.stats,
-                           s.dy, s.lse, s.l1p);
+        hipLaunchKernelGGL((loss_tiles<2, true>), grid, dim3(256), 0, stream, M, V, nchunk, Ub, Tb, W1b, W2b, xp, y,
+                           s.stats, s.dy, s.lse, s.l1p);
     else
-        hipLaunchKernelGGL((loss_tiles<2, false>), grid, dim3(256), 0, stream, M, V, Ub, Tb, W1b, W2b, xp, y,
+        hipLaunchKernelGGL((loss_tiles<2, false>), grid, dim3(256), 0, stream, M, V, nchunk, Ub, Tb, W1b, W2b, xp, y,
                            s.stats, s.dy, s.lse, s.l1p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(loss_final, dim3((uint32_t)((M + 255) / 256)), dim3(256), 0, stream, M, gamma, V, nchunk,
+    hipLaunchKernelGGL(loss_final, dim3((uint32_t)((M + 3) / 4)), dim3(256), 0, stream, M, gamma, V, nchunk,
                        s.l1p, s.dy, s.lse, s.zc, xp, y, mask, decay, ce, l1, conf, bce, s.terms);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(loss_reduce, dim3(1), dim3(kReduceThreads), 0, stream, M, s.terms, a_ce, a_l1, a_conf, loss);

@@ -92,7 +92,8 @@ def profiled_traffic(profile: str, sources: list[str]):
 SAMPLER_SOURCES = ["draft_head_sampling_amd/csrc/head_sample.hip", "draft_head_sampling_amd/csrc/internal.h"]
 VERIFY_SOURCES = ["draft_head_sampling_amd/csrc/verify.hip", "draft_head_sampling_amd/csrc/internal.h"]
 ACCEPT_SOURCES = ["draft_head_sampling_amd/csrc/accept_rate.hip", "draft_head_sampling_amd/csrc/internal.h"]
-LOSS_SOURCES = ["draft_head_sampling_amd/csrc/block_loss.hip", "draft_head_sampling_amd/csrc/internal.h"]
+LOSS_SOURCES = ["draft_head_sampling_amd/csrc/block_loss.hip", "draft_head_sampling_amd/csrc/block_loss.h",
+                "draft_head_sampling_amd/csrc/internal.h"]
 
 
 def main():

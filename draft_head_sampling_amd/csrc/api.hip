@@ -3,6 +3,7 @@
 // enqueued, and no C++ exception crosses the interface.
 #include "dspark.h"
 #include "internal.h"
+#include "block_loss.h"
 
 #define DSPARK_EXPORT extern "C" __attribute__((visibility("default")))
 

@@ -23,7 +23,7 @@
 // Every workspace word is written before it is read, so the workspace needs
 // no clearing, and every reduction runs in a fixed order: repeated calls are
 // bitwise identical.
-#include "internal.h"
+#include "block_loss.h"
 
 namespace dspark {
 namespace {
@@ -83,7 +83,7 @@ __device__ __forceinline__ void load_tile(const bf16_t* __restrict__ X, int64_t 
 // to dy [M]; PASS 2 reads lse [M][2] and writes the chunk's sum of
 // |p_d - p_t| to l1p [M][chunks].
 template <int PASS, bool VEC>
-__global__ __launch_bounds__(256) void loss_tiles(int64_t M, int64_t V, int64_t nchunk, const bf16_t* __restrict__ U,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void loss_tiles(int64_t M, int64_t V, int64_t nchunk, const bf16_t* __restrict__ U,
                                                   const bf16_t* __restrict__ T, const bf16_t* __restrict__ W1,
                                                   const bf16_t* __restrict__ W2, const int32_t* __restrict__ xp,
                                                   const int32_t* __restrict__ y, float* __restrict__ stats,
@@ -123,21 +123,35 @@ __global__ __launch_bounds__(256) void loss_tiles(int64_t M, int64_t V, int64_t 
     }
     __syncthreads();
 
+    // In pass 2 the loads of tile i + 1 (W2 fragments, U and t pieces) are
+    // issued once tile i's products are done and its U/t pieces are in LDS, so
+    // they are in flight during tile i's epilogue.  Pass 1 issues each tile's
+    // loads at the tile's start: its epilogue holds more state, and at two
+    // waves per SIMD the prefetched registers would spill.
+    constexpr bool kPrefetch = PASS == 2;
+    // W2 rows of a wave as A fragments: k-step s takes rank elements 16 s + 8 half .. + 7
+    auto issue = [&](int64_t vt, uint4(&a)[16], u32x4_t(&us)[4], u32x4_t(&ts)[4]) {
+        const int64_t v = vt + wave * 32 + row < V ? vt + wave * 32 + row : V - 1;
+        const uint4* src = reinterpret_cast<const uint4*>(W2 + v * kRank + half * 8);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a[i] = src[2 * i];
+        load_tile<VEC>(U, M, V, p0, vt, tid, us);
+        load_tile<VEC>(T, M, V, p0, vt, tid, ts);
+    };
+    uint4 a_pf[16];
+    u32x4_t us_pf[4], ts_pf[4];
+    if (kPrefetch) issue(chunk * kChunk, a_pf, us_pf, ts_pf);  // the grid has no chunk past V
     for (int tile = 0; tile < kTiles; ++tile) {
         const int64_t vt = chunk * kChunk + (int64_t)tile * kRows;
         if (vt >= V) break;  // the same for the whole workgroup
-        const int64_t v0 = vt + wave * 32;
-        // W2 rows of this wave as A fragments: k-step s takes rank elements 16 s + 8 half .. + 7
-        uint4 a[16];
-        {
-            const int64_t v = v0 + row < V ? v0 + row : V - 1;
-            const uint4* src = reinterpret_cast<const uint4*>(W2 + v * kRank + half * 8);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) a[i] = src[2 * i];
-        }
-        u32x4_t us[4], ts[4];
-        load_tile<VEC>(U, M, V, p0, vt, tid, us);
-        load_tile<VEC>(T, M, V, p0, vt, tid, ts);
+        const int64_t vn = vt + kRows;
+        const bool next = tile + 1 < kTiles && vn < V;
+        uint4 a_loc[16];
+        u32x4_t us_loc[4], ts_loc[4];
+        uint4(&a)[16] = kPrefetch ? a_pf : a_loc;
+        u32x4_t(&us)[4] = kPrefetch ? us_pf : us_loc;
+        u32x4_t(&ts)[4] = kPrefetch ? ts_pf : ts_loc;
+        if (!kPrefetch) issue(vt, a, us, ts);
         f32x16_t acc[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
@@ -161,6 +175,7 @@ __global__ __launch_bounds__(256) void loss_tiles(int64_t M, int64_t V, int64_t 
             *reinterpret_cast<u32x4_t*>(T_lds + pl * kTRow + col) = ts[i];
         }
         __syncthreads();
+        if (kPrefetch && next) issue(vn, a, us, ts);
         // lane holds rows vt + wave*32 + 8(r/4) + 4 half + r%4 of position nt*32 + row
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {

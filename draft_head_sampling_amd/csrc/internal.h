@@ -76,15 +76,6 @@ hipError_t verify_launch(int64_t B, int64_t gamma, int64_t V, int dtype, const v
                          const int32_t* x, const int32_t* n_draft, const float* u, const float* G,
                          int32_t* n_accepted, int32_t* next_token, float* accept_prob, void* ws, hipStream_t stream);
 
-size_t block_loss_workspace(int64_t M, int64_t V);
-// bf16, rank 256, 16-byte aligned W1, W2 and workspace
-bool block_loss_shape_ok(int64_t r, const void* W1, const void* W2, const void* ws);
-hipError_t block_loss_launch(int64_t N, int64_t gamma, int64_t V, int64_t H, const void* U, const void* t,
-                             const void* h, const void* W1, const void* W2, const void* w_conf, float b_conf,
-                             const int32_t* xp, const int32_t* y, const float* mask, float decay, float a_ce,
-                             float a_l1, float a_conf, float* ce, float* l1, float* conf, float* bce, float* loss,
-                             void* ws, hipStream_t stream);
-
 size_t prefix_schedule_workspace(int64_t B, int64_t gamma);
 hipError_t prefix_schedule_launch(int64_t B, int64_t gamma, const float* conf, const double* sps, int64_t n_sps,
                                   int32_t* prefix_len, float* survival_out, int32_t* order_out, double* theta_out,

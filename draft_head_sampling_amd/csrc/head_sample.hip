@@ -373,6 +373,62 @@ __global__ __launch_bounds__(kThreads) void gate_step(int64_t B, int64_t gamma, 
     }
 }
 
+// 8-lane-chunk dot of two bf16 vectors held as 16-byte pieces, summed over the wave.
+__device__ __forceinline__ float wave_dot8(uint4 a, uint4 b) {
+    float s = 0.f;
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        s = __builtin_fmaf(widen_lo(aw[q]), widen_lo(bw[q]), s);
+        s = __builtin_fmaf(widen_hi(aw[q]), widen_hi(bw[q]), s);
+    }
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    return s;
+}
+
+constexpr int kGateRowsPerWave = kGateRows / (kThreads / 64);
+
+// gate_step for bf16 with r <= 512, r % 8 == 0 and 16-byte aligned rows: lane
+// l holds rank elements 8l .. 8l + 7.  The gate weights and the hidden halves
+// do not depend on the previous token, so their loads are issued before it is
+// known and overlap that round trip.
+__global__ __launch_bounds__(kThreads) void gate_step_bf16(int64_t B, int64_t gamma, int k, int64_t V, int64_t H,
+                                                           int64_t r, const bf16_t* __restrict__ W1,
+                                                           const bf16_t* __restrict__ Wg,
+                                                           const int32_t* __restrict__ x0,
+                                                           const int32_t* __restrict__ force, const uint64_t* keys,
+                                                           int ncopy, const float* __restrict__ Ah,
+                                                           float* __restrict__ eg) {
+    __shared__ int32_t xs;
+    const int64_t b = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t j0 = (int64_t)blockIdx.y * kGateRows;
+    const bool mine = 8 * lane < r;
+    uint4 wv[kGateRowsPerWave];
+    float ah[kGateRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kGateRowsPerWave; ++i) {
+        const int64_t j = j0 + wave + (kThreads / 64) * i;
+        wv[i] = (j < r && mine) ? *reinterpret_cast<const uint4*>(Wg + j * (H + r) + H + 8 * lane) : uint4{0, 0, 0, 0};
+        ah[i] = j < r ? Ah[(b * gamma + k) * r + j] : 0.f;
+    }
+    if (threadIdx.x < 64) {
+        const int32_t x = wave_prev_token(b, k, B, gamma, V, x0, force, keys, ncopy, lane);
+        if (lane == 0) xs = x;
+    }
+    __syncthreads();
+    const int32_t x = xs;
+    if (x < 0) return;  // the request stopped: its bias is never formed
+    const bf16_t* e = W1 + (int64_t)x * r;
+    const uint4 ev = mine ? *reinterpret_cast<const uint4*>(e + 8 * lane) : uint4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < kGateRowsPerWave; ++i) {
+        const int64_t j = j0 + wave + (kThreads / 64) * i;
+        const float sdot = wave_dot8(wv[i], ev);
+        if (lane == 0 && j < r) eg[b * r + j] = load_elem(e, j) / (1.f + expf(-(ah[i] + sdot)));
+    }
+}
+
 // ---------------------------------------------------------------------------
 // RNN head (the same page, section 3.2, RNNHead; paper eq. 6): a recurrent
 // state replaces the embedding in the bias,
@@ -455,6 +511,78 @@ __global__ __launch_bounds__(kThreads) void rnn_step(int64_t B, int64_t gamma, i
     }
 }
 
+// rnn_step for bf16 with r <= 256, r % 8 == 0 and 16-byte aligned rows: lane
+// l holds elements 8l .. 8l + 7 of z's first 2r entries [s_{k-1}; e].  The
+// weights, the hidden halves and s_{k-1} do not depend on the previous token,
+// so their loads are issued before it is known.
+__global__ __launch_bounds__(kThreads) void rnn_step_bf16(int64_t B, int64_t gamma, int k, int64_t V, int64_t H,
+                                                          int64_t r, const bf16_t* __restrict__ W1,
+                                                          const bf16_t* __restrict__ Wrg,
+                                                          const bf16_t* __restrict__ Wrc,
+                                                          const int32_t* __restrict__ x0,
+                                                          const int32_t* __restrict__ force, const uint64_t* keys,
+                                                          int ncopy, const float* __restrict__ Ag,
+                                                          const float* __restrict__ Ac,
+                                                          const float* __restrict__ s_in, float* __restrict__ s_out) {
+    __shared__ int32_t xs;
+    const int64_t b = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t Z = 2 * r + H, bk = b * gamma + k;
+    const int64_t j0 = (int64_t)blockIdx.y * kGateRows;
+    const int c0 = 8 * lane;  // first z element of this lane
+    const bool sp = c0 < r, ep = !sp && c0 < 2 * r;  // state part, embedding part
+    uint4 wg[kGateRowsPerWave], wc[kGateRowsPerWave];
+    float ag[kGateRowsPerWave], ac[kGateRowsPerWave], sj[kGateRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kGateRowsPerWave; ++i) {
+        const int64_t j = j0 + wave + (kThreads / 64) * i;
+        const bool ok = j < r && (sp || ep);
+        wg[i] = ok ? *reinterpret_cast<const uint4*>(Wrg + j * Z + c0) : uint4{0, 0, 0, 0};
+        wc[i] = ok ? *reinterpret_cast<const uint4*>(Wrc + j * Z + c0) : uint4{0, 0, 0, 0};
+        ag[i] = j < r ? Ag[bk * r + j] : 0.f;
+        ac[i] = j < r ? Ac[bk * r + j] : 0.f;
+        sj[i] = (j < r && k > 0) ? s_in[b * r + j] : 0.f;
+    }
+    float zs[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) zs[q] = 0.f;
+    if (sp && k > 0) {
+        const float4 a = *reinterpret_cast<const float4*>(s_in + b * r + c0);
+        const float4 c = *reinterpret_cast<const float4*>(s_in + b * r + c0 + 4);
+        zs[0] = a.x, zs[1] = a.y, zs[2] = a.z, zs[3] = a.w, zs[4] = c.x, zs[5] = c.y, zs[6] = c.z, zs[7] = c.w;
+    }
+    if (threadIdx.x < 64) {
+        const int32_t x = wave_prev_token(b, k, B, gamma, V, x0, force, keys, ncopy, lane);
+        if (lane == 0) xs = x;
+    }
+    __syncthreads();
+    const int32_t x = xs;
+    if (x < 0) return;  // the request stopped: its bias is never formed
+    if (ep) {
+        const uint4 e = *reinterpret_cast<const uint4*>(W1 + (int64_t)x * r + (c0 - r));
+        const uint32_t ew[4] = {e.x, e.y, e.z, e.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) zs[2 * q] = widen_lo(ew[q]), zs[2 * q + 1] = widen_hi(ew[q]);
+    }
+#pragma unroll
+    for (int i = 0; i < kGateRowsPerWave; ++i) {
+        const int64_t j = j0 + wave + (kThreads / 64) * i;
+        float g = 0.f, c = 0.f;
+        const uint32_t gw[4] = {wg[i].x, wg[i].y, wg[i].z, wg[i].w}, cw[4] = {wc[i].x, wc[i].y, wc[i].z, wc[i].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            g = __builtin_fmaf(widen_lo(gw[q]), zs[2 * q], g);
+            g = __builtin_fmaf(widen_hi(gw[q]), zs[2 * q + 1], g);
+            c = __builtin_fmaf(widen_lo(cw[q]), zs[2 * q], c);
+            c = __builtin_fmaf(widen_hi(cw[q]), zs[2 * q + 1], c);
+        }
+        for (int o = 32; o > 0; o >>= 1) g += __shfl_xor(g, o), c += __shfl_xor(c, o);
+        if (lane == 0 && j < r) {
+            const float u = 1.f / (1.f + expf(-(ag[i] + g)));
+            s_out[b * r + j] = u * sj[i] + (1.f - u) * tanhf(ac[i] + c);
+        }
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Single-request chain kernel (B = 1, bf16, rank 256).
@@ -2450,6 +2578,15 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
 
+    // bf16 gate and state steps with every lane's rank elements in one 16-byte piece
+    bool fast_gate = false, fast_rnn = false;
+    if constexpr (std::is_same_v<T, bf16_t>) {
+        const bool rows16 = r % 8 == 0 && H % 8 == 0 && (uintptr_t)W1 % 16 == 0;
+        fast_gate = Wg && rows16 && r <= 512 && (uintptr_t)Wg % 16 == 0;
+        fast_rnn = rnn && rows16 && r <= 256 && (uintptr_t)Wrg % 16 == 0 && (uintptr_t)Wrc % 16 == 0 &&
+                   (uintptr_t)ws % 16 == 0;
+    }
+
     // lanes per W2 row: 16-byte chunks per row when rows are 16-byte aligned
     const int64_t row_bytes = r * (int64_t)sizeof(T);
     int lpr = 0;
@@ -2461,17 +2598,28 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
         const float* eg = nullptr;
         if (Wg) {
             const dim3 grid((uint32_t)B, (uint32_t)((r + kGateRows - 1) / kGateRows));
-            hipLaunchKernelGGL((gate_step<T>), grid, dim3(kThreads), 0, stream, B, gamma, k, V, H, r, W1t, Wgt, x0,
-                               force, s.keys, ncopy, gate_ws, gate_ws + B * gamma * r);
+            if (fast_gate)
+                hipLaunchKernelGGL(gate_step_bf16, grid, dim3(kThreads), 0, stream, B, gamma, k, V, H, r,
+                                   reinterpret_cast<const bf16_t*>(W1t), reinterpret_cast<const bf16_t*>(Wgt), x0,
+                                   force, s.keys, ncopy, gate_ws, gate_ws + B * gamma * r);
+            else
+                hipLaunchKernelGGL((gate_step<T>), grid, dim3(kThreads), 0, stream, B, gamma, k, V, H, r, W1t, Wgt,
+                                   x0, force, s.keys, ncopy, gate_ws, gate_ws + B * gamma * r);
             if ((err = hipGetLastError()) != hipSuccess) return err;
             eg = gate_ws + B * gamma * r;
         }
         if (rnn) {
             float* st = gate_ws + 2 * B * gamma * r;
             const dim3 grid((uint32_t)B, (uint32_t)((r + kGateRows - 1) / kGateRows));
-            hipLaunchKernelGGL((rnn_step<T>), grid, dim3(kThreads), sizeof(float) * 2 * r, stream, B, gamma, k, V, H,
-                               r, W1t, Wrgt, Wrct, x0, force, s.keys, ncopy, gate_ws, gate_ws + B * gamma * r,
-                               st + ((k + 1) % 2) * B * r, st + (k % 2) * B * r);
+            if (fast_rnn)
+                hipLaunchKernelGGL(rnn_step_bf16, grid, dim3(kThreads), 0, stream, B, gamma, k, V, H, r,
+                                   reinterpret_cast<const bf16_t*>(W1t), reinterpret_cast<const bf16_t*>(Wrgt),
+                                   reinterpret_cast<const bf16_t*>(Wrct), x0, force, s.keys, ncopy, gate_ws,
+                                   gate_ws + B * gamma * r, st + ((k + 1) % 2) * B * r, st + (k % 2) * B * r);
+            else
+                hipLaunchKernelGGL((rnn_step<T>), grid, dim3(kThreads), sizeof(float) * 2 * r, stream, B, gamma, k, V,
+                                   H, r, W1t, Wrgt, Wrct, x0, force, s.keys, ncopy, gate_ws, gate_ws + B * gamma * r,
+                                   st + ((k + 1) % 2) * B * r, st + (k % 2) * B * r);
             if ((err = hipGetLastError()) != hipSuccess) return err;
             eg = st + (k % 2) * B * r;
         }

@@ -245,7 +245,8 @@ def test_gated_head_tiny(gumbel):
     sampler_parity(x, w, want_logits=True)
 
 
-@pytest.mark.parametrize("B,V,gamma,H,r", [(5, 30001, 5, 512, 64), (1, 4099, 9, 96, 32), (17, 2000, 3, 64, 8)])
+@pytest.mark.parametrize("B,V,gamma,H,r", [(5, 30001, 5, 512, 64), (1, 4099, 9, 96, 32), (17, 2000, 3, 64, 8),
+                                           (3, 2000, 4, 60, 12)])  # the last: generic gate step (r % 8 != 0)
 def test_gated_head_bf16_shapes(B, V, gamma, H, r):
     s = synth.SamplerShape(B=B, gamma=gamma, V=V, H=H, r=r, dtype="bf16", w_sd=0.3, U_sd=1.0, wc_sd=0.02,
                            gumbel=True, seed=synth.SEED_BASE + 40 + V)
@@ -316,7 +317,8 @@ def test_rnn_head_tiny(gumbel):
     sampler_parity(x, w, want_logits=True)
 
 
-@pytest.mark.parametrize("B,V,gamma,H,r", [(5, 30001, 5, 512, 64), (1, 4099, 9, 96, 32), (17, 2000, 3, 64, 8)])
+@pytest.mark.parametrize("B,V,gamma,H,r", [(5, 30001, 5, 512, 64), (1, 4099, 9, 96, 32), (17, 2000, 3, 64, 8),
+                                           (3, 2000, 4, 60, 12)])  # the last: generic state step (r % 8 != 0)
 def test_rnn_head_bf16_shapes(B, V, gamma, H, r):
     s = synth.SamplerShape(B=B, gamma=gamma, V=V, H=H, r=r, dtype="bf16", w_sd=0.3, U_sd=1.0, wc_sd=0.02,
                            gumbel=True, seed=synth.SEED_BASE + 60 + V)

@@ -120,3 +120,15 @@ def test_training_workload_full_size():
     want = [0.1 * terms[0] + 0.9 * terms[1] + 1.0 * terms[2]] + terms
     assert np.allclose(got["loss"], want, rtol=1e-5, atol=1e-6), (got["loss"], want)
     assert np.all((got["l1"] > 0) & (got["l1"] < 1))
+
+
+def test_no_hidden_state():
+    """H = 0: the confidence head sees only the Markov embedding (h absent)."""
+    x = _tiny(3, 5, 1500, H=0, seed=4)
+    out = dh.block_loss(dev(x["U"]), dev(x["t"]), None, dev(x["W1"]), dev(x["W2"]), dev(x["w_conf"]), x["b_conf"],
+                        dev(x["xp"]), dev(x["y"]))
+    got = {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
+    ref = oracle.block_loss(x["U"], x["t"], np.zeros((3, 5, 0), np.uint16), x["W1"], x["W2"], x["w_conf"],
+                            x["b_conf"], x["xp"], x["y"])
+    _check_positions(got, ref)
+    _check_loss(got, ref)

@@ -10,6 +10,12 @@ Entry points (same names as the C ABI):
   accept_rate      analytic accept rate 1 - 1/2 ||softmax(d) - softmax(t)||_1
   prefix_schedule  hardware-aware prefix scheduler (Algorithm 1)
   verify           rejection-sampling verification of a draft block
+  block_loss       teacher-forced block bias with the joint training loss
+  workspace_status give-up status and path flags of a workspace
+  set_wait_limit   poll limit of the waits between workgroups
+
+Environment: DSPARK_DEBUG=1 makes every call synchronise and raise on an
+asynchronous HIP error or a wait that gave up.
 """
 from __future__ import annotations
 
@@ -78,6 +84,10 @@ def lib() -> ctypes.CDLL:
                                     f32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dspark_block_loss_workspace_size.restype = sz
     L.dspark_block_loss_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32]
+    L.dspark_workspace_status.restype = i32
+    L.dspark_workspace_status.argtypes = [vp, sz, vp, vp]
+    L.dspark_set_wait_limit.restype = i32
+    L.dspark_set_wait_limit.argtypes = [i64, ctypes.POINTER(i64)]
     _lib = L
     return L
 
@@ -123,6 +133,56 @@ def _workspace(nbytes: int, device, workspace):
 def _check(fn: str, status: int):
     if status != 0:
         raise DsparkError(fn, status)
+
+
+class DsparkGaveUp(RuntimeError):
+    """A bounded wait between workgroups ran out (the outputs of that call are
+    unspecified; zero-fill the workspace before reusing it)."""
+
+
+PATH_B1_REBUILD, PATH_B1_EXCHANGE, PATH_RESIDENT, PATH_ACCEPT_CLUSTER = 1, 2, 4, 8
+
+
+def workspace_status(workspace: torch.Tensor) -> tuple[int, int]:
+    """(give-up status, path flags) of a sampler / accept-rate / verify
+    workspace, read in stream order (dspark_workspace_status); clears the
+    path flags.  Synchronises the current stream to return host integers."""
+    out = torch.zeros(2, dtype=torch.int32, device=workspace.device)
+    _check("dspark_workspace_status",
+           lib().dspark_workspace_status(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                         out.data_ptr(), _stream(workspace.device)))
+    st, paths = out.cpu().tolist()
+    return int(st), int(paths) & 0xFFFFFFFF
+
+
+def set_wait_limit(polls: int) -> int:
+    """Process-wide poll limit of the waits between workgroups (negative =
+    each kernel's default); returns the previous value (dspark_set_wait_limit)."""
+    prev = ctypes.c_int64(0)
+    _check("dspark_set_wait_limit", lib().dspark_set_wait_limit(int(polls), ctypes.byref(prev)))
+    return int(prev.value)
+
+
+def _debug() -> bool:
+    return os.environ.get("DSPARK_DEBUG", "") == "1"
+
+
+def _caller(name: str, fn, ws):
+    """The enqueue function of a prepared call.  With DSPARK_DEBUG=1 every
+    call synchronises, surfaces asynchronous HIP errors, and raises
+    DsparkGaveUp when the workspace's give-up word is set."""
+    if not _debug():
+        return lambda: _check(name, fn())
+
+    def call():
+        _check(name, fn())
+        torch.cuda.synchronize()
+        if ws is not None and name != "dspark_block_loss":
+            st, _ = workspace_status(ws)
+            if st:
+                raise DsparkGaveUp(f"{name}: a wait between workgroups gave up (were other kernels holding "
+                                   "compute units?); outputs are unspecified; zero-fill the workspace")
+    return call
 
 
 def head_sample_workspace_size(B, gamma, V, H, r, dtype=DSPARK_BF16) -> int:
@@ -185,7 +245,7 @@ def prepare_head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=Non
         outs["logits"] = logits_out
     if bias_out is not None:
         outs["bias"] = bias_out
-    return (lambda: _check(name, fn())), outs
+    return _caller(name, fn, ws), outs
 
 
 def head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=None, *, want_logits=False, workspace=None,
@@ -225,7 +285,7 @@ def prepare_accept_rate(draft, target, V=None, *, out=None, workspace=None, stre
             _dev(out, "accept_rate", torch.float32, (N,)), None if ws is None else ws.data_ptr(), wsb,
             _stream(dev) if stream is None else stream)
     fn = partial(lib().dspark_accept_rate, *args)
-    return (lambda: _check("dspark_accept_rate", fn())), {"accept_rate": out, "_workspace": ws}
+    return _caller("dspark_accept_rate", fn, ws), {"accept_rate": out, "_workspace": ws}
 
 
 def accept_rate(draft, target, V=None, *, workspace=None):
@@ -256,7 +316,7 @@ def prepare_prefix_schedule(conf, sps, *, want_order=True, workspace=None, strea
             None if ws is None else ws.data_ptr(), wsb, _stream(dev) if stream is None else stream)
     fn = partial(lib().dspark_prefix_schedule, *args)
     outs["_workspace"] = ws
-    return (lambda: _check("dspark_prefix_schedule", fn())), outs
+    return _caller("dspark_prefix_schedule", fn, ws), outs
 
 
 def prefix_schedule(conf, sps, *, want_order=True, workspace=None):
@@ -290,7 +350,7 @@ def prepare_verify(draft, target, draft_tokens, uniforms, gumbel, n_draft=None, 
             _stream(dev) if stream is None else stream)
     fn = partial(lib().dspark_verify, *args)
     outs["_workspace"] = ws
-    return (lambda: _check("dspark_verify", fn())), outs
+    return _caller("dspark_verify", fn, ws), outs
 
 
 def verify(draft, target, draft_tokens, uniforms, gumbel, n_draft=None, *, want_accept_prob=False, workspace=None):
@@ -331,7 +391,7 @@ def prepare_block_loss(U, t, h, W1, W2, w_conf, b_conf, xp, y, mask=None, *, dec
             None if ws is None else ws.data_ptr(), wsb, _stream(dev) if stream is None else stream)
     fn = partial(lib().dspark_block_loss, *args)
     outs["_workspace"] = ws
-    return (lambda: _check("dspark_block_loss", fn())), outs
+    return _caller("dspark_block_loss", fn, ws), outs
 
 
 def block_loss(U, t, h, W1, W2, w_conf, b_conf, xp, y, mask=None, *, decay=4.0, a_ce=0.1, a_l1=0.9, a_conf=1.0,

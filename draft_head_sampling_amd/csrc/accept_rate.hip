@@ -151,7 +151,7 @@ constexpr int kCThreads = 256;
 constexpr int kCMaxVec = 10;     // 16-byte vectors per thread per row chunk
 constexpr int kCMaxCluster = 16;
 constexpr int kCSpinLimit = 1 << 22;
-constexpr size_t kCHeader = 256;
+constexpr size_t kCHeader = kWsHeader;  // words 0 (exit counter), 1 (status), 2 (row counter), 3 (paths)
 
 template <typename T>
 __device__ __forceinline__ void unpack16(const uint4& r, float (&x)[Vec<T>::N]);
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kCThreads) void accept_rate_cluster(int64_t N, int6
                                                                  const T* __restrict__ t, int64_t ldt,
                                                                  float* __restrict__ out, uint64_t* stats,
                                                                  uint64_t* parts, uint32_t* counters, uint64_t* nexts,
-                                                                 uint32_t* header) {
+                                                                 uint32_t* header, int spin_limit) {
     static_assert(kCMaxCluster * 4 <= 64, "one wave polls all statistics words of a cluster");
     __shared__ float lds[2 * kCThreads / 64];
     __shared__ float rowstat[4];
@@ -187,6 +187,7 @@ __global__ __launch_bounds__(kCThreads) void accept_rate_cluster(int64_t N, int6
     const int64_t v1 = v0 + vpc < nvec ? v0 + vpc : nvec;
     const bool tail_owner = c == C - 1;
     bool failed = false;
+    if (blockIdx.x == 0 && tid == 0) mark_path(header, kPathAcceptCluster);
 
     // raw 16-byte vectors of this workgroup's chunk of the current row pair
     uint4 rd[NV], rt[NV];
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(kCThreads) void accept_rate_cluster(int64_t N, int6
             if (tid < 64) {
                 uint64_t w = tagged(tag, 0.f), nw = 0;
                 bool ok = false;
-                for (int spin = 0; spin < kCSpinLimit && !failed; ++spin) {
+                for (int spin = 0; spin < spin_limit && !failed; ++spin) {
                     w = lane < 4 * C ? __hip_atomic_load(slot + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                      : tagged(tag, 0.f);
                     nw = __hip_atomic_load(nslot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(kCThreads) void accept_rate_cluster(int64_t N, int6
                 if (tid == 0) {
                     rowstat[0] = failed ? __builtin_nanf("") : M1, rowstat[1] = S1;
                     rowstat[2] = M2, rowstat[3] = S2;
-                    if (failed) header[1] = 1u;
+                    if (failed) mark_gave_up(header);
                 }
             }
             __syncthreads();
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(kCThreads) void accept_rate_cluster(int64_t N, int6
             if (old == (uint32_t)C * (iter + 1) - 1) {  // last chunk of this row in: finish it
                 uint64_t w = tagged(tag, 0.f);
                 bool ok = false;
-                for (int spin = 0; spin < kCSpinLimit; ++spin) {
+                for (int spin = 0; spin < spin_limit; ++spin) {
                     w = lane < C ? __hip_atomic_load(part + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                  : tagged(tag, 0.f);
                     ok = __all((uint32_t)(w >> 32) == tag);
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(kCThreads) void accept_rate_cluster(int64_t N, int6
                 for (int k = 0; k < C; ++k) sum += __shfl(val, k);
                 if (tid == 0) {
                     out[row] = ok ? 1.f - 0.5f * sum : __builtin_nanf("");
-                    if (!ok) header[1] = 1u;
+                    if (!ok) mark_gave_up(header);
                 }
             }
         }
@@ -345,7 +346,8 @@ __global__ __launch_bounds__(kCThreads) void accept_rate_cluster(int64_t N, int6
     }
 
     // leave: the last workgroup out clears slots and counters for the next call
-    if (C > 1) {
+    // (also with C == 1: the row counter header[2] is claimed from either way)
+    {
         __syncthreads();
         if (tid == 0) {
             const uint32_t old = __hip_atomic_fetch_add(&header[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
@@ -470,8 +472,9 @@ hipError_t launch_typed(int64_t N, int64_t V, const void* d, int64_t ldd, const 
                                                           ((size_t)p.n_clusters * 4 + 7) / 8 * 8);
             int64_t NN = N, VV = V, vpc = p.vpc, ld1 = ldd, ld2 = ldt;
             int C = p.C, nc = p.n_clusters;
-            void* args[] = {&NN,  &VV,    &C,    &nc,       &vpc,  &dp,    &ld1,
-                            &tp,  &ld2,   &out,  &stats,    &parts, &counters, &nexts, &header};
+            int lim = wait_limit(kCSpinLimit);
+            void* args[] = {&NN,  &VV,    &C,    &nc,       &vpc,  &dp,    &ld1,   &tp,
+                            &ld2, &out,   &stats, &parts,   &counters, &nexts, &header, &lim};
             // at most the resident capacity: all workgroups of a cluster run together
             return hipLaunchKernel(p.fn, dim3((uint32_t)(p.n_clusters * p.C)), dim3(kCThreads), args, 0, stream);
         }

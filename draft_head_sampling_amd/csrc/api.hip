@@ -1,6 +1,8 @@
 // C ABI of the draft-head hot path: host-side argument checks, workspace
 // queries and dispatch to the kernels.  Every check runs before anything is
 // enqueued, and no C++ exception crosses the interface.
+#include <atomic>
+
 #include "dspark.h"
 #include "internal.h"
 #include "block_loss.h"
@@ -33,7 +35,41 @@ bool sampler_shape_ok(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r)
 
 dspark_status_t hip_status(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP; }
 
+// Poll limit set by dspark_set_wait_limit; negative: each kernel's own default.
+std::atomic<int64_t> g_wait_limit{-1};
+constexpr int64_t kMaxWaitLimit = (int64_t)1 << 30;
+
+// One thread: copy the give-up status and the path flags of a workspace
+// header, then clear the path flags.
+__global__ void workspace_status_kernel(uint32_t* header, uint32_t* out) {
+    out[0] = __hip_atomic_load(header + dspark::kHdrStatus, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    out[1] = __hip_atomic_exchange(header + dspark::kHdrPaths, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace
+
+namespace dspark {
+int wait_limit(int kernel_default) {
+    const int64_t v = g_wait_limit.load(std::memory_order_relaxed);
+    return v < 0 ? kernel_default : (int)v;
+}
+}  // namespace dspark
+
+DSPARK_EXPORT dspark_status_t dspark_set_wait_limit(int64_t polls, int64_t* previous) {
+    if (polls > kMaxWaitLimit) return DSPARK_ERR_BAD_SHAPE;
+    const int64_t old = g_wait_limit.exchange(polls < 0 ? -1 : polls, std::memory_order_relaxed);
+    if (previous) *previous = old;
+    return DSPARK_OK;
+}
+
+DSPARK_EXPORT dspark_status_t dspark_workspace_status(void* workspace, size_t workspace_bytes, uint32_t* out,
+                                                      void* stream) {
+    if (!workspace || !out) return DSPARK_ERR_NULL_ARG;
+    if (workspace_bytes < dspark::kWsHeader || ((uintptr_t)workspace % 256) != 0) return DSPARK_ERR_WORKSPACE;
+    hipLaunchKernelGGL(workspace_status_kernel, dim3(1), dim3(1), 0, static_cast<hipStream_t>(stream),
+                       static_cast<uint32_t*>(workspace), out);
+    return hip_status(hipGetLastError());
+}
 
 DSPARK_EXPORT const char* dspark_status_string(dspark_status_t s) {
     switch (s) {

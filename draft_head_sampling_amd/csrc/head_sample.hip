@@ -666,7 +666,7 @@ constexpr int kChainMaxWGs = 256;   // 4 slots per lane when polling
 constexpr int kSlotWords = 16;      // 128-byte stride between slots (key, partial logit, padding)
 constexpr int kChainPoll = kChainMaxWGs / 64;
 constexpr int kChainSpinLimit = 1 << 21;
-constexpr size_t kChainHeader = 256;  // exit counter, status word, decision word (byte 128)
+constexpr size_t kChainHeader = kWsHeader;  // words 0 (exit counter), 1 (status), 3 (paths)
 
 // Candidate screen.  The Markov bias of a row is bounded by Cauchy-Schwarz,
 // |W2[v] . e| <= |W2[v]| |e|, so at step k only rows whose bias-free score
@@ -863,7 +863,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
     const bf16_t* __restrict__ w_conf, float b_conf, const int32_t* __restrict__ x0, const float* __restrict__ G,
     const int32_t* __restrict__ force, int32_t* __restrict__ tokens, float* __restrict__ conf,
     float* __restrict__ survival, float* __restrict__ logits_out, float* __restrict__ bias_out, uint64_t* slots,
-    uint64_t* regions, uint64_t* aux, uint32_t* header) {
+    uint64_t* regions, uint64_t* aux, uint32_t* header, int spin_limit) {
     __shared__ uint64_t red[kChainWaves];
     __shared__ float fred[kChainWaves];
     __shared__ uint32_t we_lds[kChainRank / 2];  // Markov part of the confidence weights (workgroup 0)
@@ -954,7 +954,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             const int kk = lane / kScreenStep;
             uint64_t word[kPollRegions];
             bool ready = false;
-            for (int spin = 0; spin < kChainSpinLimit && !ready; ++spin) {
+            for (int spin = 0; spin < spin_limit && !ready; ++spin) {
                 bool all = true;
 #pragma unroll
                 for (int i = 0; i < kPollRegions; ++i) {
@@ -1209,7 +1209,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             if (wave == 0) wk = walk();
             if (poller) {
                 uint64_t w = nword;
-                for (int spin = 0; spin < kChainSpinLimit && w == 0; ++spin) {
+                for (int spin = 0; spin < spin_limit && w == 0; ++spin) {
                     __builtin_amdgcn_s_sleep(1);
                     w = __hip_atomic_load(npw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
@@ -1219,6 +1219,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             __syncthreads();
             const uint32_t n2b = sc.n2;
             if (sc.abort || !(__uint_as_float(n2b) <= guess)) {  // workgroup-uniform
+                if (tid == 0 && !sc.abort) mark_path(header, kPathB1Rebuild);
                 build(n2b);
                 __syncthreads();
                 if (wave == 0) wk = walk();
@@ -1253,7 +1254,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 }
                 if (lane == 0) A = surv;
                 if (sc.abort) {  // some workgroup never arrived: report, release the others
-                    if (lane == 0) header[1] = 1u;
+                    if (lane == 0) mark_gave_up(header);
                     for (int j = lane; j < gamma; j += 64)
                         tokens[j] = -1, conf[j] = __builtin_nanf(""), survival[j] = __builtin_nanf("");
                 }
@@ -1271,7 +1272,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 // decision; when all have, the decision word goes back to zero
                 if (tid + 1 < nwg) {
                     const uint64_t* r = regions + (int64_t)(tid + 1) * kRegionWords;
-                    for (int spin = 0; spin < kChainSpinLimit; ++spin) {
+                    for (int spin = 0; spin < spin_limit; ++spin) {
                         if (__hip_atomic_load(r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) break;
                         __builtin_amdgcn_s_sleep(2);
                     }
@@ -1384,7 +1385,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             // Hold the stream back until workgroup 0 has every list: behind a
             // full HBM queue every cross-workgroup message waits several
             // microseconds.
-            for (int spin = 0; spin < kChainSpinLimit; ++spin) {
+            for (int spin = 0; spin < spin_limit; ++spin) {
                 if (__hip_atomic_load(gcopy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
                 __builtin_amdgcn_s_sleep(2);
             }
@@ -1421,10 +1422,11 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             __hip_atomic_store(myregion + nwords - 1, kTag | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             // wait for the coordinator's decision
             uint64_t d = 0;
-            for (int spin = 0; spin < kChainSpinLimit && d == 0; ++spin) {
+            for (int spin = 0; spin < spin_limit && d == 0; ++spin) {
                 d = __hip_atomic_load(dcopy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (d == 0) __builtin_amdgcn_s_sleep(2);
             }
+            if (d == 0) mark_gave_up(header);  // the coordinator was lost
             sc.decision = d;
         }
         __syncthreads();
@@ -1457,6 +1459,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
 
     {
         // the grid-wide per-step exchange, from step k0 on
+        if (wg0 && tid == 0) mark_path(header, kPathB1Exchange);
         uint32_t e[16];
         if (valid) load64B(W1 + x * kChainRank + sub * 32, e);
         float u_next[NMINE], g_next[NMINE];
@@ -1527,7 +1530,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             if (wave == 0) {
                 uint64_t best = 0;
                 float zsum = 0.f;
-                for (int spin = 0; spin < kChainSpinLimit; ++spin) {
+                for (int spin = 0; spin < spin_limit; ++spin) {
                     uint64_t sk[kChainPoll], sp[kChainPoll];
 #pragma unroll
                     for (int i = 0; i < kChainPoll; ++i) {  // clamped, unconditional: all in flight at once
@@ -1557,7 +1560,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 if (lane == 0) {
                     winner = best;
                     zpart = zsum;
-                    if (best == 0 && wg0) header[1] = 1u;  // timed out: reported as token -1
+                    if (best == 0) mark_gave_up(header);  // timed out: reported as token -1
                 }
             }
             __syncthreads();
@@ -1676,8 +1679,9 @@ hipError_t launch_chain(const ChainPlan& p, int64_t gamma, int64_t V, int64_t H,
     uint64_t* slots = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kChainHeader);
     uint64_t* regions = slots + (size_t)kSlotWords * gamma * kChainMaxWGs;
     uint64_t* aux = regions + (size_t)kRegionWords * kChainMaxWGs;
-    void* args[] = {&g,  &Vv, &Hh,    &rows,   &screen, &Ut,       &ht, &W1t, &W2t,  &wt,      &b_conf,
-                    &x0, &G,  &force, &tokens, &conf,   &survival, &lo, &bo,  &slots, &regions, &aux, &header};
+    int lim = wait_limit(kChainSpinLimit);
+    void* args[] = {&g,     &Vv,    &Hh,       &rows, &screen, &Ut,    &ht,      &W1t, &W2t,    &wt,   &b_conf, &x0,
+                    &G,     &force, &tokens,   &conf, &survival, &lo,  &bo,      &slots, &regions, &aux, &header, &lim};
     const void* fn = chain_fn(p.nslot);
     // A plain launch: every workgroup needs a whole CU (its register file) and
     // the grid has at most one workgroup per CU, so on an otherwise idle GPU
@@ -2038,7 +2042,7 @@ constexpr int kResMaxTiles = kResWaves * kResRegTiles + kResLdsTiles;
 constexpr int kResMaxReq = 64;
 constexpr int kResCopies = 8;   // copies of the winner words
 constexpr int kResMaxWGs = 256;
-constexpr size_t kResHeader = 256;  // exit counter
+constexpr size_t kResHeader = kWsHeader;  // words 0 (exit counter), 1 (status), 3 (paths)
 
 __device__ __forceinline__ int32_t winner_token(uint64_t key) {  // 0 or 1: no candidate
     return key <= 1 ? -1 : key_token(key);
@@ -2076,13 +2080,14 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
                       const bf16_t* __restrict__ w_conf, int64_t H, float b_conf, const int32_t* __restrict__ x0,
                       const float* __restrict__ G, const int32_t* __restrict__ force, int32_t* __restrict__ tokens,
                       float* __restrict__ conf, float* __restrict__ survival, uint64_t* hword, uint64_t* pub,
-                      uint64_t* win, uint32_t* header) {
+                      uint64_t* win, uint32_t* header, int spin_limit) {
     constexpr int NREQ = 32 * NT;
     __shared__ __align__(16) uint16_t E_lds[NREQ * kERow];
     __shared__ __align__(16) uint16_t T_lds[kResLdsTiles * 32 * kERow];  // W2 tiles held in LDS
     __shared__ __align__(16) float G_lds[kResWaves][2][32 * 32];  // per wave: two Gumbel units in flight
     __shared__ uint64_t wkey[kResWaves][NREQ];
     __shared__ uint64_t rkey[kResWaves];
+    __shared__ int rlost[kResWaves];
     __shared__ int32_t xprev[NREQ];
     __shared__ uint32_t we_lds[kMfmaRank / 2];  // Markov part of the confidence weights (workgroup 0)
     __shared__ int last_flag;
@@ -2093,6 +2098,7 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
     const int64_t t0 = (int64_t)g * tiles_per_wg;
     const int64_t t_end = t0 + tiles_per_wg < ntiles ? t0 + tiles_per_wg : ntiles;
     const uint64_t* wcopy = win + (int64_t)(g % kResCopies) * kResMaxReq;  // step stride kResCopies * 64
+    if (g == 0 && tid == 0) mark_path(header, kPathResident);
 
     // this wave's W2 tiles, as A fragments: k-step s holds rank elements
     // 16 s + 8 half .. +7 of row 32 t + row
@@ -2216,11 +2222,11 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
                 } else {
                     const uint64_t* p = wcopy + (int64_t)(k - 1) * kResCopies * kResMaxReq + tid;
                     uint64_t w = 0;
-                    for (int spin = 0; spin < kChainSpinLimit && w == 0; ++spin) {
+                    for (int spin = 0; spin < spin_limit && w == 0; ++spin) {
                         w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         if (w == 0) __builtin_amdgcn_s_sleep(1);
                     }
-                    if (w == 0 && g == 0) header[1] = 1u;  // timed out: reported as token -1
+                    if (w == 0) mark_gave_up(header);  // timed out: reported as token -1
                     const int32_t tok = winner_token(w);
                     const int32_t f = (force && tok >= 0) ? force[tid * gamma + k - 1] : -1;
                     x = tok < 0 ? -1 : (f >= 0 ? f : tok);
@@ -2261,10 +2267,11 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
                 if (part == 0 && bl < B) {
                     const bool live = xprev[bl] >= 0;
                     uint64_t hw = 0;  // posted in the prologue, normally long before
-                    for (int spin = 0; spin < kChainSpinLimit && hw == 0; ++spin) {
+                    for (int spin = 0; spin < spin_limit && hw == 0; ++spin) {
                         hw = __hip_atomic_load(hword + bl * gamma + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         if (hw == 0) __builtin_amdgcn_s_sleep(1);
                     }
+                    if (hw == 0) mark_gave_up(header);  // reported as NaN confidence
                     const float hd = hw != 0 ? __uint_as_float((uint32_t)hw) : __builtin_nanf("");
                     const float c = 1.f / (1.f + expf(-(hd + s + b_conf)));
                     A = A * c;
@@ -2370,17 +2377,23 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
             uint64_t m = 0;
             if (tid < nwg) {
                 const uint64_t* p = pub + ((int64_t)k * nwg + tid) * kResMaxReq + r;
-                for (int spin = 0; spin < kChainSpinLimit && m == 0; ++spin) {
+                for (int spin = 0; spin < spin_limit && m == 0; ++spin) {
                     m = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     if (m == 0) __builtin_amdgcn_s_sleep(1);
                 }
             }
+            // a workgroup whose key never arrived leaves the step without a
+            // winner (token -1), not with the best of the others
+            const bool lost = __any(tid < nwg && m == 0);
             m = wave_max_u64(m);
-            if (lane == 0) rkey[wave] = m;
+            if (lane == 0) rkey[wave] = m, rlost[wave] = lost ? 1 : 0;
             __syncthreads();
             uint64_t best = 0;
+            bool missing = false;
 #pragma unroll
-            for (int w = 0; w < kResWaves; ++w) best = umax64(best, rkey[w]);
+            for (int w = 0; w < kResWaves; ++w) missing = missing || rlost[w] != 0, best = umax64(best, rkey[w]);
+            if (missing) best = 0;
+            if (missing && tid == 0) mark_gave_up(header);
             if (tid < kResCopies)
                 __hip_atomic_store(win + ((int64_t)k * kResCopies + tid) * kResMaxReq + r, best ? best : 1ull,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2440,7 +2453,7 @@ ResidentPlan resident_plan(int64_t B, int64_t V) {
 }
 
 size_t resident_workspace(int64_t B, int64_t gamma) {
-    return ((size_t)(8 * B * gamma) + 255) / 256 * 256 + kResHeader +
+    return kResHeader + ((size_t)(8 * B * gamma) + 255) / 256 * 256 +
            (size_t)8 * gamma * kResMaxWGs * kResMaxReq + (size_t)8 * gamma * kResCopies * kResMaxReq;
 }
 
@@ -2450,7 +2463,7 @@ struct Buffers {
 };
 
 Buffers carve(void* ws, int64_t B, int64_t gamma, int ncopy) {
-    char* p = static_cast<char*>(ws);
+    char* p = static_cast<char*>(ws) + kWsHeader;
     Buffers s;
     s.keys = reinterpret_cast<uint64_t*>(p);
     p += ((size_t)(8 * kKeyStride * ncopy * B * gamma) + 255) / 256 * 256;
@@ -2511,16 +2524,18 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
         if (rp.nwg > 0 && lo == nullptr && bo == nullptr && (uintptr_t)U % 8 == 0 &&
             (G == nullptr || ((uintptr_t)G % 16 == 0 && B * gamma * V * 4 < ((int64_t)1 << 31)))) {
             char* p = static_cast<char*>(ws);
+            uint32_t* header = reinterpret_cast<uint32_t*>(p);
+            p += kResHeader;
             uint64_t* hword = reinterpret_cast<uint64_t*>(p);
             p += ((size_t)(8 * B * gamma) + 255) / 256 * 256;
-            uint32_t* header = reinterpret_cast<uint32_t*>(p);
-            uint64_t* pub = reinterpret_cast<uint64_t*>(p + kResHeader);
+            uint64_t* pub = reinterpret_cast<uint64_t*>(p);
             uint64_t* win = pub + (size_t)gamma * kResMaxWGs * kResMaxReq;
+            int lim = wait_limit(kChainSpinLimit);
             const T* ht = static_cast<const T*>(h);
             int g = (int)gamma, tpw = rp.tiles_per_wg;
             int64_t Bb = B, Vv = V, Hh = H;
             void* args[] = {&Bb, &g,     &Vv,    &tpw,    &Ut,   &W1t,      &W2t,   &ht,  &wt,  &Hh,    &b_conf,
-                            &x0, &G,     &force, &tokens, &conf, &survival, &hword, &pub, &win, &header};
+                            &x0, &G,     &force, &tokens, &conf, &survival, &hword, &pub, &win, &header, &lim};
             const void* fn = G ? (B <= 32 ? reinterpret_cast<const void*>(&sample_batch_resident<1, true>)
                                           : reinterpret_cast<const void*>(&sample_batch_resident<2, true>))
                                : (B <= 32 ? reinterpret_cast<const void*>(&sample_batch_resident<1, false>)
@@ -2673,7 +2688,7 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
 
 size_t head_sample_workspace(int64_t B, int64_t gamma, int64_t, int64_t r, int dtype) {
     const int64_t ncopy = (dtype == kBF16 && r == kMfmaRank && B >= kMfmaMinBatch) ? kKeyCopies : 1;
-    size_t steps = ((size_t)(8 * kKeyStride * ncopy * B * gamma) + 255) / 256 * 256 +
+    size_t steps = kWsHeader + ((size_t)(8 * kKeyStride * ncopy * B * gamma) + 255) / 256 * 256 +
                    ((size_t)(4 * B * gamma) + 255) / 256 * 256;
     if (dtype == kBF16 && r == kMfmaRank && B >= kMfmaMinBatch && B <= kResMaxReq) {
         const size_t res = resident_workspace(B, gamma);
@@ -2690,7 +2705,7 @@ size_t head_sample_workspace(int64_t B, int64_t gamma, int64_t, int64_t r, int d
 // one) and hidden dots, then a gated or RNN head's words
 size_t headed_workspace(int64_t B, int64_t gamma, int64_t r, int dtype, int64_t words_per_request) {
     const int64_t ncopy = (dtype == kBF16 && r == kMfmaRank && B >= kMfmaMinBatch) ? kKeyCopies : 1;
-    return ((size_t)(8 * kKeyStride * ncopy * B * gamma) + 255) / 256 * 256 +
+    return kWsHeader + ((size_t)(8 * kKeyStride * ncopy * B * gamma) + 255) / 256 * 256 +
            ((size_t)(4 * B * gamma) + 255) / 256 * 256 + ((size_t)(4 * B * words_per_request) + 255) / 256 * 256;
 }
 

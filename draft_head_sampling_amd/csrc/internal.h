@@ -54,6 +54,35 @@ __device__ __forceinline__ float exp_shifted(float x, float m_log2e) {
 }
 
 // ---------------------------------------------------------------------------
+// Workspace header.  Every workspace of the sampler, accept-rate and verify
+// entry points begins with these 256 bytes:
+//   word 0  private to the kernel that uses the workspace (exit counter)
+//   word 1  give-up status: set to 1 by any workgroup whose bounded wait for
+//           another workgroup ran out (its outputs are then -1 / NaN and the
+//           workspace may be left dirty)
+//   word 2  private (the accept-rate row counter)
+//   word 3  path flags: kernels only OR bits into it and never read it
+// ---------------------------------------------------------------------------
+constexpr size_t kWsHeader = 256;
+constexpr int kHdrStatus = 1;
+constexpr int kHdrPaths = 3;
+constexpr uint32_t kPathB1Rebuild = 1u;    // B=1 screen: the norm guess was low, table rebuilt
+constexpr uint32_t kPathB1Exchange = 2u;   // B=1: steps settled by the grid-wide per-step exchange
+constexpr uint32_t kPathResident = 4u;     // batched sampler: the resident-W2 kernel ran
+constexpr uint32_t kPathAcceptCluster = 8u;  // accept rate: the cluster kernel ran
+
+__device__ __forceinline__ void mark_gave_up(uint32_t* header) {
+    __hip_atomic_store(header + kHdrStatus, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void mark_path(uint32_t* header, uint32_t bit) {
+    __hip_atomic_fetch_or(header + kHdrPaths, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Poll limit of every wait for another workgroup: the kernel's own default
+// (a negative value) unless dspark_set_wait_limit set one.
+int wait_limit(int kernel_default);
+
+// ---------------------------------------------------------------------------
 // Host-side launchers (argument checks already done by the ABI layer).
 // ---------------------------------------------------------------------------
 size_t accept_rate_workspace(int64_t N, int64_t V);

@@ -40,7 +40,8 @@ constexpr int kSampleVecs = 4;  // vectors per thread per sampling workgroup
 // Workspace: per (request, position, row split) the two rows' partial
 // (max, sum of exp) as four binary32 words; per (request, vocabulary chunk)
 // a slot of two argmax keys (residual, p_t); per request an arrival counter
-// of the sampling workgroups; one status word.
+// of the sampling workgroups; all after the common 256-byte header, whose
+// word 1 is the give-up status.
 constexpr int kSplit = 4;  // workgroups per (request, position) row pair
 constexpr size_t kStatWords = 4;
 constexpr uint64_t kNoKey = 1;  // a written slot word without a candidate (below every real key)
@@ -52,7 +53,7 @@ size_t stats_bytes(int64_t B, int64_t gamma) {
     return ((size_t)(B * gamma) * kSplit * kStatWords * 4 + 255) / 256 * 256;
 }
 size_t slots_bytes(int64_t B, int64_t V) { return ((size_t)B * max_chunks(V) * 16 + 255) / 256 * 256; }
-size_t count_bytes(int64_t B) { return ((size_t)(B + 1) * 4 + 255) / 256 * 256; }
+size_t count_bytes(int64_t B) { return ((size_t)B * 4 + 255) / 256 * 256; }
 
 template <typename T>
 struct Vec;
@@ -193,7 +194,7 @@ __global__ __launch_bounds__(kSampleThreads) void verify_sample(
     int64_t gamma, int64_t V, const T* __restrict__ d, const T* __restrict__ t, const int32_t* __restrict__ x,
     const int32_t* __restrict__ n_draft, const float* __restrict__ u, const float* __restrict__ G, float* stats,
     uint64_t* slots, uint32_t* counters, int32_t* __restrict__ n_accepted, float* __restrict__ accept_prob,
-    int32_t* __restrict__ next_token, uint32_t* status) {
+    int32_t* __restrict__ next_token, uint32_t* header, int spin_limit) {
     static_assert(kSampleThreads >= 64, "wave 0 walks the positions");
     __shared__ uint64_t red[2][kSampleThreads / 64];
     __shared__ int s_pos, s_res;
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(kSampleThreads) void verify_sample(
         uint64_t mr = 0, mt = 0;
         bool ok = false;
         const uint64_t* req = slots + (int64_t)b * nch * 2;
-        for (int spin = 0; spin < kSpinLimit; ++spin) {
+        for (int spin = 0; spin < spin_limit; ++spin) {
             bool all = true;
             mr = 0, mt = 0;
             for (int c = lane; c < nch; c += 64) {
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(kSampleThreads) void verify_sample(
         if (lane == 0) {
             const uint64_t k = res && mr > kNoKey ? mr : mt;
             next_token[b] = ok && k > kNoKey ? key_token(k) : -1;
-            if (!ok) status[0] = 1u;
+            if (!ok) mark_gave_up(header);
             __hip_atomic_store(counters + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         for (int c = lane; c < 2 * nch; c += 64)
@@ -366,11 +367,12 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, const void* d, cons
     const T* dp = static_cast<const T*>(d);
     const T* tp = static_cast<const T*>(t);
     const bool vec = V % E == 0 && (uintptr_t)d % 16 == 0 && (uintptr_t)t % 16 == 0 && (uintptr_t)G % 16 == 0;
-    char* w = static_cast<char*>(ws);
+    uint32_t* header = static_cast<uint32_t*>(ws);  // word 1: a lost slot (bounded wait ran out) -> token -1
+    char* w = static_cast<char*>(ws) + kWsHeader;
     float* stats = reinterpret_cast<float*>(w);
     uint64_t* slots = reinterpret_cast<uint64_t*>(w + stats_bytes(B, gamma));
     uint32_t* counters = reinterpret_cast<uint32_t*>(w + stats_bytes(B, gamma) + slots_bytes(B, V));
-    uint32_t* status = counters + B;  // a lost slot (bounded wait ran out): token -1 and this word set
+    const int lim = wait_limit(kSpinLimit);
     if (gamma > 0) {
         const dim3 grid((uint32_t)(B * gamma * kSplit));
         if (vec)
@@ -384,17 +386,17 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, const void* d, cons
     const dim3 sgrid((uint32_t)((V + span - 1) / span), (uint32_t)B);
     if (vec)
         hipLaunchKernelGGL((verify_sample<T, true>), sgrid, dim3(kSampleThreads), 0, stream, gamma, V, dp, tp, x,
-                           n_draft, u, G, stats, slots, counters, n_accepted, accept_prob, next_token, status);
+                           n_draft, u, G, stats, slots, counters, n_accepted, accept_prob, next_token, header, lim);
     else
         hipLaunchKernelGGL((verify_sample<T, false>), sgrid, dim3(kSampleThreads), 0, stream, gamma, V, dp, tp, x,
-                           n_draft, u, G, stats, slots, counters, n_accepted, accept_prob, next_token, status);
+                           n_draft, u, G, stats, slots, counters, n_accepted, accept_prob, next_token, header, lim);
     return hipGetLastError();
 }
 
 }  // namespace
 
 size_t verify_workspace(int64_t B, int64_t gamma, int64_t V) {
-    return stats_bytes(B, gamma) + slots_bytes(B, V) + count_bytes(B);
+    return kWsHeader + stats_bytes(B, gamma) + slots_bytes(B, V) + count_bytes(B);
 }
 
 hipError_t verify_launch(int64_t B, int64_t gamma, int64_t V, int dtype, const void* d, const void* t,

@@ -14,7 +14,8 @@
  *   - Array pointers are DEVICE pointers on the current HIP device, owned by
  *     the caller.  Scalars are host values.  The library keeps no pointer
  *     after a call returns, allocates no memory and holds no mutable global
- *     state; concurrent calls are safe when they use distinct workspaces.
+ *     state apart from the wait limit (dspark_set_wait_limit); concurrent
+ *     calls are safe when they use distinct workspaces.
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null
  *     stream) without host synchronisation.  Outputs are valid once the
  *     stream has reached the point of the call.
@@ -22,10 +23,24 @@
  *     returns the bytes an entry point needs for given shapes (0 means the
  *     workspace argument may be NULL).  A workspace must be at least that
  *     large and 256-byte aligned; workspace_bytes is its size.  It must be
- *     zero-filled before its first use; every call that completes leaves it
- *     zero-filled again, so one workspace serves any number of calls in
- *     stream order (after a call that reports a timeout, zero it again).
+ *     zero-filled before its first use; every call that completes without a
+ *     give-up (below) leaves it zero-filled again, except for the path-flags
+ *     word, so one workspace serves any number of calls in stream order.
  *     Calls that may overlap in time must not share a workspace.
+ *   - Persistent kernels and give-ups.  The B = 1 and batched (16 <= B <= 64,
+ *     bf16, r = 256) samplers, the accept rate on 16-byte aligned rows and
+ *     the draw of dspark_verify let workgroups wait for one another through
+ *     the workspace.  The first three size their grids so that every
+ *     workgroup is resident at once on a GPU that runs nothing else (at most
+ *     one workgroup per compute unit, or the occupancy limit); they do not
+ *     use cooperative launch.  Every such wait is bounded (about 2^21 to
+ *     2^22 polls by default, see dspark_set_wait_limit).  When a wait runs
+ *     out -- typically because other work held compute units and a
+ *     workgroup could not start -- the kernel still finishes, the affected
+ *     outputs are token -1 / NaN (outputs of such a call are unspecified),
+ *     and word 1 of the workspace header is set.  Read it with
+ *     dspark_workspace_status.  Recovery: zero-fill the whole workspace
+ *     before its next use (words of the lost workgroups may still be set).
  *   - Errors: every argument check runs on the host before anything is
  *     enqueued; on failure a non-zero status is returned and nothing is
  *     enqueued.  A failed launch returns DSPARK_ERR_HIP.  No C++ exception
@@ -293,6 +308,39 @@ size_t dspark_accept_rate_workspace_size(int64_t N, int64_t V, int32_t dtype);
 size_t dspark_prefix_schedule_workspace_size(int64_t B, int64_t gamma);
 size_t dspark_verify_workspace_size(int64_t B, int64_t gamma, int64_t V, int32_t dtype);
 size_t dspark_block_loss_workspace_size(int64_t N, int64_t gamma, int64_t V, int64_t H, int64_t r, int32_t dtype);
+
+/*
+ * dspark_workspace_status -- give-up status and path flags of a workspace of
+ * dspark_head_sample, dspark_head_sample_gated, dspark_head_sample_rnn,
+ * dspark_accept_rate or dspark_verify (each of those workspaces starts with a
+ * 256-byte header).  Enqueued on `stream` after the calls to inspect; writes
+ * two words to the DEVICE array out[2]:
+ *   out[0]  0, or 1 if a bounded wait of some earlier call on this workspace
+ *           ran out (see "Persistent kernels and give-ups" above).  It stays
+ *           set until the caller zero-fills the workspace.
+ *   out[1]  path flags ORed by the calls since the last query, which this
+ *           call clears: 1 = the B = 1 candidate screen's guess of the largest
+ *           W2 row norm was too small and its step table was rebuilt with the
+ *           measured norm; 2 = a B = 1 call settled steps with the grid-wide
+ *           per-step exchange; 4 = the batched resident-W2 sampler ran; 8 = the
+ *           accept rate's cluster kernel ran.  Diagnostic only: no kernel
+ *           reads this word, so its value never affects a result.
+ * workspace_bytes >= 256, 256-byte aligned.  Errors as for the other calls.
+ */
+dspark_status_t dspark_workspace_status(void* workspace, size_t workspace_bytes, uint32_t* out, void* stream);
+
+/*
+ * dspark_set_wait_limit -- process-wide number of polls after which every
+ * wait for another workgroup gives up, for the calls enqueued after it
+ * returns; polls < 0 restores each kernel's default.  polls = 0 makes every
+ * such wait give up at once: the kernels still run to completion and report
+ * the give-up as described above (a test of the failure path that needs no
+ * stalled workgroup).  *previous (optional, host) receives the former value
+ * (-1 = defaults).  polls > 2^30 returns DSPARK_ERR_BAD_SHAPE.  This is the
+ * library's only mutable global state; it does not affect calls already
+ * enqueued.
+ */
+dspark_status_t dspark_set_wait_limit(int64_t polls, int64_t* previous);
 
 /* Static, NUL-terminated description of a status code. */
 const char* dspark_status_string(dspark_status_t status);

@@ -34,6 +34,15 @@ def dev(a: np.ndarray | None, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
+def workspace_dirty_bytes(ws: torch.Tensor) -> int:
+    """Non-zero bytes of a workspace after a call, not counting the header's
+    path-flags word (bytes 12-15), which kernels only OR into and no kernel
+    reads.  A call that completes leaves every other byte zero."""
+    b = ws.view(torch.uint8).clone()
+    b[12:16] = 0
+    return int(b.count_nonzero())
+
+
 def normwise_rel(gpu: np.ndarray, ref: np.ndarray) -> float:
     """max over rows of max|gpu - ref| / max|ref| (rows = last axis)."""
     num = np.abs(gpu.astype(np.float64) - ref).max(axis=-1)

@@ -6,7 +6,7 @@ import torch
 import draft_head_sampling_amd as dh
 import oracle
 import synth
-from helpers import PROB_ATOL, dev
+from helpers import PROB_ATOL, dev, workspace_dirty_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +47,10 @@ def test_training_workload_sampled_rows():
     """N=2048 rows x V=151936 bf16 in one launch; the oracle checks 48 rows."""
     s = synth.ACCEPT_TRAIN
     d, t = synth.accept_inputs(s)
-    got = dh.accept_rate(dev(d), dev(t)).cpu().numpy()
+    out = torch.full((s.N,), float("nan"), dtype=torch.float32, device="cuda")  # an unwritten row stays NaN
+    call, _ = dh.prepare_accept_rate(dev(d), dev(t), out=out)
+    call()
+    got = out.cpu().numpy()
     rows = np.unique(np.concatenate([[0, 1, s.N - 1], np.random.default_rng(3).integers(0, s.N, 45)]))
     ref = oracle.accept_rate(np.ascontiguousarray(d[rows]), np.ascontiguousarray(t[rows]))
     assert np.abs(got[rows] - ref).max() <= PROB_ATOL
@@ -81,4 +84,47 @@ def test_workspace_reuse_across_shapes():
         a = dh.accept_rate(dd, tt, workspace=ws)
         b = dh.accept_rate(dd, tt)
         assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (N, V)
-    assert int(ws.count_nonzero()) == 0
+    assert workspace_dirty_bytes(ws) == 0
+
+
+def _nan_filled_call(d, t, ws):
+    out = torch.full((d.shape[0],), float("nan"), dtype=torch.float32, device="cuda")
+    call, _ = dh.prepare_accept_rate(d, t, out=out, workspace=ws)
+    call()
+    return out
+
+
+def test_whole_row_clusters_leave_the_row_counter_clear():
+    """Regression: with rows short enough for one workgroup each (a cluster
+    of one), rows after the first wave of clusters are still claimed from
+    the workspace's row counter.  Every call must leave that counter at
+    zero, or the next call on the same workspace skips rows.  More rows than
+    fit on the GPU at once, twice on one workspace, then the training-width
+    workload on the same workspace; every output starts as NaN."""
+    import draft_head_sampling_amd as dh_
+
+    small = synth.AcceptShape(N=4096, V=8192, dtype="f32", d_sd=3, scale=0.8, t_sd=1.5, seed=77)
+    big = synth.ACCEPT_TRAIN
+    nbytes = max(dh_.lib().dspark_accept_rate_workspace_size(small.N, small.V, 0),
+                 dh_.lib().dspark_accept_rate_workspace_size(big.N, big.V, 1))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    d, t = synth.accept_inputs(small)
+    ref = oracle.accept_rate(d, t)
+    dd, tt = dev(d), dev(t)
+    for _ in range(2):
+        got = _nan_filled_call(dd, tt, ws).cpu().numpy()
+        assert np.all(np.isfinite(got))
+        assert np.abs(got - ref).max() <= PROB_ATOL
+        assert workspace_dirty_bytes(ws) == 0
+    del dd, tt
+    d, t = synth.accept_inputs(big)
+    dd, tt = dev(d), dev(t)
+    got = _nan_filled_call(dd, tt, ws)
+    fresh = _nan_filled_call(dd, tt, None)
+    assert torch.equal(got.view(torch.int32), fresh.view(torch.int32))
+    g = got.cpu().numpy()
+    assert np.all(np.isfinite(g))
+    rows = np.array([0, 1, 777, big.N - 1])
+    ref = oracle.accept_rate(np.ascontiguousarray(d[rows]), np.ascontiguousarray(t[rows]))
+    assert np.abs(g[rows] - ref).max() <= PROB_ATOL
+    assert workspace_dirty_bytes(ws) == 0

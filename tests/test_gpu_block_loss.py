@@ -10,8 +10,9 @@ exp/log against the oracle's fp64):
   loss terms                rel <= 1e-4
 Per-position outputs of positions with an out-of-range token are NaN on both
 sides.  At the full training size the oracle checks three whole sequences (48
-positions) and the loss is checked against the fp64 weighted mean of the
-GPU's own per-position outputs, which holds at any size.
+positions); the loss is checked against the oracle's loss with every other
+sequence masked out, and against the fp64 weighted mean of the GPU's own
+per-position outputs, which holds at any size.
 """
 import numpy as np
 import pytest
@@ -108,13 +109,21 @@ def test_repeat_calls_are_bitwise_identical():
 def test_training_workload_full_size():
     """2048 positions x V=151936 bf16, the launch configuration the benchmark
     times: three whole sequences against the oracle, the loss against the fp64
-    weighted mean of the per-position outputs."""
+    weighted mean of the per-position outputs.  A second call masks every
+    other sequence out, so its loss (the full 2048-position reduction path)
+    is the oracle's loss over those three sequences."""
     s = synth.LOSS_TRAIN
     x = synth.loss_inputs(s)
     got = _gpu(x)
-    for n in (0, 77, 127):
-        sub = {k: (v[n:n + 1] if k in ("U", "t", "h", "xp", "y") else v) for k, v in x.items()}
-        _check_positions(got, _ref(sub), sl=slice(n, n + 1))
+    seqs = np.array([0, 77, 127])
+    sub = {k: (v[seqs] if k in ("U", "t", "h", "xp", "y") else v) for k, v in x.items()}
+    ref = _ref(sub)
+    _check_positions(got, ref, sl=seqs)
+    mask = np.zeros((s.N, s.gamma), np.float32)
+    mask[seqs] = 1.0
+    masked = _gpu(x, mask)
+    _check_positions(masked, ref, sl=seqs)
+    _check_loss(masked, ref)
     w = np.exp(-np.arange(s.gamma) / 4.0)[None, :] * np.ones((s.N, 1))
     terms = [np.sum(w * got[k]) / w.sum() for k in ("ce", "l1", "bce")]
     want = [0.1 * terms[0] + 0.9 * terms[1] + 1.0 * terms[2]] + terms

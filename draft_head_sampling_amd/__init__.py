@@ -84,6 +84,9 @@ def lib() -> ctypes.CDLL:
                                     f32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dspark_block_loss_workspace_size.restype = sz
     L.dspark_block_loss_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32]
+    L.dspark_head_sample_noalloc.restype = i32
+    L.dspark_head_sample_noalloc.argtypes = [i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp,
+                                             vp, vp, vp, vp, vp]
     L.dspark_workspace_status.restype = i32
     L.dspark_workspace_status.argtypes = [vp, sz, vp, vp]
     L.dspark_set_wait_limit.restype = i32
@@ -268,6 +271,27 @@ def head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=None, *, wa
                                      workspace=workspace, Wg=Wg, Wr=Wr)
     call()
     outs.pop("_workspace")
+    return outs
+
+
+def head_sample_noalloc(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=None):
+    """dspark_head_sample_noalloc: the sampler on the library's static
+    per-GPU scratch array (no workspace argument, nothing allocated by the
+    library).  Same arguments and outputs as head_sample (no stored logits)."""
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    H = h.shape[2] if h is not None else 0
+    dev = U.device
+    outs = {"tokens": torch.empty((B, gamma), dtype=torch.int32, device=dev),
+            "conf": torch.empty((B, gamma), dtype=torch.float32, device=dev),
+            "survival": torch.empty((B, gamma), dtype=torch.float32, device=dev)}
+    st = lib().dspark_head_sample_noalloc(
+        B, gamma, V, H, r, _dtype_code(U), _dev(U, "U", U.dtype, (B, gamma, V)), _opt(h, "h", U.dtype, (B, gamma, H)),
+        _dev(W1, "W1", U.dtype, (V, r)), _dev(W2, "W2", U.dtype, (V, r)), _dev(w_conf, "w_conf", U.dtype, (H + r,)),
+        float(b_conf), _dev(x0, "x0", torch.int32, (B,)), _opt(gumbel, "gumbel", torch.float32, (B, gamma, V)),
+        _opt(force, "force", torch.int32, (B, gamma)), _dev(outs["tokens"], "tokens"), _dev(outs["conf"], "conf"),
+        _dev(outs["survival"], "survival"), None, None, _stream(dev))
+    _check("dspark_head_sample_noalloc", st)
     return outs
 
 

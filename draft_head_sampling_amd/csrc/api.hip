@@ -2,6 +2,7 @@
 // queries and dispatch to the kernels.  Every check runs before anything is
 // enqueued, and no C++ exception crosses the interface.
 #include <atomic>
+#include <mutex>
 
 #include "dspark.h"
 #include "internal.h"
@@ -265,4 +266,79 @@ DSPARK_EXPORT dspark_status_t dspark_block_loss(int64_t N, int64_t gamma, int64_
     return hip_status(dspark::block_loss_launch(N, gamma, V, H, U, t, h, W1, W2, w_conf, b_conf, xp, y, mask, decay,
                                                 a_ce, a_l1, a_conf, ce, l1, conf, bce, loss, workspace,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant of dspark_head_sample for callers that cannot
+// allocate (graph capture, tight serving loops): its workspace is a static
+// device array of kScratchBytes per GPU, held until the process ends.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+// In host code `scratch` names a host-side stand-in; kernels get the device
+// address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kScratchMaxDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    void* ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kScratchMaxDevices];
+
+// Device address of this device's copy of `scratch`, looked up once per
+// device with that device current.
+hipError_t scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchMaxDevices) return hipErrorInvalidDevice;
+    ScratchSlot& s = g_scratch[dev];
+    std::call_once(s.once, [&s]() {
+        void* p = nullptr;
+        s.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        s.ptr = s.err == hipSuccess ? p : nullptr;
+    });
+    if (s.err != hipSuccess) return s.err;
+    if (s.ptr == nullptr) return hipErrorInvalidSymbol;
+    *out = s.ptr;
+    return hipSuccess;
+}
+
+// Zero n bytes (a multiple of 16) with vector stores: the kernels expect a
+// zero-filled workspace, and the array keeps whatever the last call left.
+__global__ void zero_words(uint4* p, int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+}  // namespace
+
+DSPARK_EXPORT dspark_status_t dspark_head_sample_noalloc(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r,
+                                                         int32_t dtype, const void* U, const void* h, const void* W1,
+                                                         const void* W2, const void* w_conf, float b_conf,
+                                                         const int32_t* x0, const float* gumbel, const int32_t* force,
+                                                         int32_t* tokens, float* conf, float* survival,
+                                                         float* logits_out, float* bias_out, void* stream) {
+    if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return DSPARK_ERR_BAD_DTYPE;
+    if (!sampler_shape_ok(B, gamma, V, H, r)) return DSPARK_ERR_BAD_SHAPE;
+    if (B == 0 || gamma == 0) return DSPARK_OK;
+    const size_t need = (dspark::head_sample_workspace(B, gamma, V, r, dtype) + 255) / 256 * 256;
+    if (need > kScratchBytes) return DSPARK_ERR_WORKSPACE;
+    if (!U || !W1 || !W2 || !w_conf || !x0 || !tokens || !conf || !survival || (H > 0 && !h))
+        return DSPARK_ERR_NULL_ARG;
+    void* ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess) return DSPARK_ERR_HIP;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t n16 = (int64_t)(need / 16);
+    const int64_t blocks = (n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024;
+    hipLaunchKernelGGL(zero_words, dim3((uint32_t)blocks), dim3(256), 0, st, static_cast<uint4*>(ws), n16);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return DSPARK_ERR_HIP;
+    return hip_status(dspark::head_sample_launch(B, gamma, V, H, r, dtype, U, h, W1, W2, w_conf, b_conf, x0, gumbel,
+                                                 force, tokens, conf, survival, logits_out, bias_out, ws, st, nullptr,
+                                                 nullptr, nullptr));
 }

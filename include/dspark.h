@@ -125,6 +125,29 @@ dspark_status_t dspark_head_sample(int64_t B, int64_t gamma, int64_t V, int64_t 
                                    void* stream);
 
 /*
+ * dspark_head_sample_noalloc -- dspark_head_sample for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, outputs and rules as
+ * dspark_head_sample, without the workspace: the call uses a static device
+ * array of 4 MiB that the library holds on each GPU it runs on until the
+ * process ends, zeroes the part it needs at the start of every call (one
+ * small fill kernel on `stream`) and calls no allocating routine.
+ *   - Shapes whose workspace (dspark_head_sample_workspace_size) exceeds
+ *     4 MiB return DSPARK_ERR_WORKSPACE before anything is enqueued (for
+ *     example B = 1 any V, or B = 64 with gamma = 7, fit).
+ *   - Every call on one GPU shares that GPU's array: calls that may overlap
+ *     in time on one GPU (different streams, or other threads) race and give
+ *     wrong results; serialise them.
+ *   - The first call on each device looks the array's device address up
+ *     (hipGetSymbolAddress); a failure there returns DSPARK_ERR_HIP.
+ */
+dspark_status_t dspark_head_sample_noalloc(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r,
+                                           int32_t dtype, const void* U, const void* h, const void* W1,
+                                           const void* W2, const void* w_conf, float b_conf, const int32_t* x0,
+                                           const float* gumbel, const int32_t* force, int32_t* tokens, float* conf,
+                                           float* survival, float* logits_out, float* bias_out, void* stream);
+
+/*
  * dspark_head_sample_gated -- the same block sampler with the gated Markov
  * head ([W] 3.2, GatedMarkovHead): the previous token's embedding
  * e = W1[x_{k-1}] is gated by the hidden state and itself before the

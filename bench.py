@@ -7,14 +7,20 @@ called once for each of 1000 seeded anchors, back to back, then the prefix
 scheduler runs once over the 1000 x 7 confidences.  `value` is draft
 positions per second (bias + sample + confidence) over the timed steps.
 
-The same run also times the analytic accept rate on the training-width
-workload (2048 positions x V=151936, bf16) and reports it as GB/s under
-`accept_rate`, and times the CPU oracle on a bounded sample of the step
-(`cpu_baseline`).  Inputs are synthetic (seeded generator), resident in HBM
-before the timed region starts.
+The same run times every other workload once, each as its own object with an
+HBM (or matrix-core) roofline: the B=1 sampler with cold caches and with a
+strong Markov bias (the grid-wide exchange path); the batched Gumbel-max
+sampler (B=64) with its matrix-core figures; the gated and RNN heads; the
+analytic accept rate on 2048 training positions; the prefix scheduler on 256 x
+16 confidences with both throughput tables; rejection-sampling verify; and the
+teacher-forced block loss.  The CPU oracle is timed on a bounded sample of the
+step, single-threaded and on every host core, and its tokens are compared with
+the GPU's.  Inputs are synthetic (seeded generator) and resident in HBM before
+any timed region starts.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--anchors 1000]
-                       [--no-cpu] [--no-accept] [--extra]
+                       [--legs all|b1,cold,strong,accept,verify,b64,gated,rnn,schedule,loss,cpu]
+                       [--no-cpu] [--no-accept] [--no-verify] [--no-cold] [--calib-copy]
 """
 from __future__ import annotations
 
@@ -28,7 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
-BF16_MFMA_PEAK_TFLOPS = 2500.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores
+ALL_LEGS = ("b1", "cold", "strong", "accept", "verify", "b64", "gated", "rnn", "schedule", "loss", "cpu")
 
 
 def to_dev(a, device):
@@ -94,6 +101,29 @@ VERIFY_SOURCES = ["draft_head_sampling_amd/csrc/verify.hip", "draft_head_samplin
 ACCEPT_SOURCES = ["draft_head_sampling_amd/csrc/accept_rate.hip", "draft_head_sampling_amd/csrc/internal.h"]
 LOSS_SOURCES = ["draft_head_sampling_amd/csrc/block_loss.hip", "draft_head_sampling_amd/csrc/block_loss.h",
                 "draft_head_sampling_amd/csrc/internal.h"]
+SCHED_SOURCES = ["draft_head_sampling_amd/csrc/prefix_schedule.hip", "draft_head_sampling_amd/csrc/internal.h"]
+
+
+def hbm_roofline(kernel, nbytes, us, profile=None, sources=None, cold_us=None):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    r = {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(gbs / HBM_PEAK_GBS, 4),
+         "traffic": profiled_traffic(profile, sources) if profile else None,
+         "bytes_per_launch": int(nbytes), "us_per_launch": round(us, 3)}
+    if cold_us is not None:
+        cg = nbytes / (cold_us * 1e-6) / 1e9
+        r["cold"] = {"us_per_launch": round(cold_us, 3), "achieved": round(cg, 1), "frac": round(cg / HBM_PEAK_GBS, 4)}
+    return r
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -102,17 +132,26 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--anchors", type=int, default=1000)
+    ap.add_argument("--legs", default="all", help="comma list of " + ",".join(ALL_LEGS) + " (b1 always runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-accept", action="store_true", help="skip the accept-rate measurement")
     ap.add_argument("--no-verify", action="store_true", help="skip the rejection-sampling verify measurement")
-    ap.add_argument("--extra", action="store_true", help="also time the B=64 sampler and the scheduler workload")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timings")
+    ap.add_argument("--extra", action="store_true", help="(accepted for compatibility: every leg runs by default)")
     ap.add_argument("--calib-copy", action="store_true", help="run a plain 1 GiB device copy (counter calibration)")
-    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache sampler timing")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the draft-head path is data-parallel by request and this build runs "
               "on a single MI355X; --gpus above 1 is not supported.", file=sys.stderr)
         sys.exit(2)
+    legs = set(ALL_LEGS) if args.legs == "all" else set(args.legs.split(",")) | {"b1"}
+    unknown = legs - set(ALL_LEGS)
+    if unknown:
+        ap.error(f"unknown legs {sorted(unknown)}")
+    for flag, leg in ((args.no_cpu, "cpu"), (args.no_accept, "accept"), (args.no_verify, "verify"),
+                      (args.no_cold, "cold")):
+        if flag:
+            legs.discard(leg)
 
     import numpy as np
     import torch
@@ -125,7 +164,35 @@ def main():
     dh.lib()  # fails loudly if the HIP library is missing
     stream = torch.cuda.current_stream(dev)
 
-    # ---------------- inputs (host generation, then resident in HBM) ----------------
+    def timed(call, reps):
+        """Average microseconds per call of `reps` back-to-back calls (HIP
+        events on the launch stream)."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if "cold" in legs else None
+
+    def timed_cold(call, reps):
+        """Median microseconds of one call after a 512 MiB write has evicted
+        the caches (W2 would otherwise be re-read from the 256 MB Infinity
+        Cache); the events bracket the call alone."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i, (c0, c1) in enumerate(ev):
+            scrub.fill_(i & 0xFF)
+            c0.record(stream)
+            call()
+            c1.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(c0.elapsed_time(c1) * 1e3 for c0, c1 in ev)
+        return t[len(t) // 2]
+
+    # ---------------- B=1 step inputs (host generation, then resident in HBM) ----------------
     s = synth.SAMPLER_B1
     n_anch = args.anchors
     w = synth.sampler_weights(s)
@@ -134,24 +201,30 @@ def main():
     Hh = torch.empty((n_anch, s.gamma, s.H), dtype=torch.bfloat16, device=dev)
     X0 = torch.empty((n_anch,), dtype=torch.int32, device=dev)
     host_batches = []
+    n_keep = 64
     for a in range(n_anch):
         x = synth.sampler_batch(s, batch_id=a)
         U[a].copy_(to_dev(x["U"][0], dev))
         Hh[a].copy_(to_dev(x["h"][0], dev))
         X0[a : a + 1].copy_(torch.from_numpy(x["x0"]))
-        if a < 64:
+        if a < n_keep:
             host_batches.append(x)
     tokens = torch.empty((n_anch, s.gamma), dtype=torch.int32, device=dev)
     conf = torch.empty((n_anch, s.gamma), dtype=torch.float32, device=dev)
     surv = torch.empty((n_anch, s.gamma), dtype=torch.float32, device=dev)
     ws = torch.zeros(max(dh.head_sample_workspace_size(1, s.gamma, s.V, s.H, s.r), 256), dtype=torch.uint8,
                      device=dev)
-    calls = []
-    for a in range(n_anch):
-        c, _ = dh.prepare_head_sample(U[a : a + 1], Hh[a : a + 1], W["W1"], W["W2"], W["w_conf"], w["b_conf"],
-                                      X0[a : a + 1], tokens=tokens[a : a + 1], conf=conf[a : a + 1],
-                                      survival=surv[a : a + 1], workspace=ws)
-        calls.append(c)
+
+    def anchor_calls(Wd, tok, cf, sv):
+        calls = []
+        for a in range(n_anch):
+            c, _ = dh.prepare_head_sample(U[a : a + 1], Hh[a : a + 1], Wd["W1"], Wd["W2"], Wd["w_conf"], 0.0,
+                                          X0[a : a + 1], tokens=tok[a : a + 1], conf=cf[a : a + 1],
+                                          survival=sv[a : a + 1], workspace=ws)
+            calls.append(c)
+        return calls
+
+    calls = anchor_calls(W, tokens, conf, surv)
     n_sps = n_anch * (s.gamma + 1)
     sps_host = synth.sps_table(n_sps, "steps")
     sps = to_dev(sps_host, dev)
@@ -189,10 +262,10 @@ def main():
     ms_per_step = total_ms / args.steps
     positions = n_anch * s.gamma
     value = positions * args.steps / (total_ms / 1e3)
-
     call_us = float(np.mean(samp_ms)) * 1e3 / n_anch
     call_bytes = sampler_call_bytes(1, s.gamma, s.V, s.H, s.r)
-    achieved = call_bytes / (call_us * 1e-6) / 1e9
+    st_b1, paths_b1 = dh.workspace_status(ws)
+    cold_b1 = timed_cold(lambda: calls[0](), 50) if scrub is not None else None
 
     line = {
         "metric": "draft positions/sec (bias+sample+conf) and accept-rate GB/s vs HBM roofline",
@@ -212,40 +285,39 @@ def main():
                         f"r=256 bf16 greedy + prefix scheduler over {n_anch}x7 confidences",
             "B": 1, "gamma": s.gamma, "V": s.V, "H": s.H, "r": s.r, "anchors_per_step": n_anch,
         },
-        "roofline": {
-            "kernel": "dspark_head_sample (one call = one anchor)",
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": profiled_traffic("head_sample_chain_b1_vocab151936.md", SAMPLER_SOURCES),
-            "bytes_per_launch": call_bytes,
-            "us_per_launch": round(call_us, 3),
-        },
+        "roofline": hbm_roofline("dspark_head_sample (one call = one anchor; W2 read once per call)", call_bytes,
+                                 call_us, "head_sample_chain_b1_vocab151936.md", SAMPLER_SOURCES, cold_b1),
+        "b1_paths": {"give_up": st_b1, "path_flags": paths_b1},
         "wall_s": round(wall, 3),
     }
 
-    # ---------------- cold caches: a 512 MiB write before each call ----------------
-    # W2 (77.8 MB) fits the 256 MB Infinity Cache, so back-to-back calls read
-    # it from there; here every call first finds the caches full of other
-    # data, and HIP events bracket the call alone.
-    scrub = None
-    if not args.no_cold:
-        scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
-        for i, (c0, c1) in enumerate(ev):
-            scrub.fill_(i & 0xFF)
-            c0.record(stream)
-            calls[i % n_anch]()
-            c1.record(stream)
+    # ---------------- B=1 with a strong Markov bias: the grid-wide exchange ----------------
+    if "strong" in legs:
+        ws_strong = synth.sampler_weights(s, w_sd=0.5)
+        Ws = {k: to_dev(v, dev) for k, v in ws_strong.items() if k != "b_conf"}
+        tok_s = torch.empty_like(tokens)
+        conf_s = torch.empty_like(conf)
+        surv_s = torch.empty_like(surv)
+        n_str = min(200, n_anch)
+        scalls = anchor_calls(Ws, tok_s, conf_s, surv_s)[:n_str]
+        dh.workspace_status(ws)  # clear the path flags
+        for c in scalls[:10]:
+            c()
         torch.cuda.synchronize()
-        cold = sorted(c0.elapsed_time(c1) * 1e3 for c0, c1 in ev)
-        line["cold"] = {"b1_us_per_call_median": round(cold[len(cold) // 2], 2), "calls": len(cold),
-                        "scrub_bytes": 512 << 20}
+        us_s = timed(lambda: [c() for c in scalls], 1) / n_str
+        st_s, paths_s = dh.workspace_status(ws)
+        line["b1_strong_bias"] = {
+            "workload": f"B=1 gamma=7 V=151936 H=5120 r=256 bf16 greedy, W1 and W2 ~ N(0, 0.5), {n_str} anchors "
+                        "back to back: the bias decides most tokens and the steps go to the grid-wide exchange",
+            "us_per_call": round(us_s, 3), "positions_per_s": round(s.gamma / (us_s * 1e-6), 1),
+            "give_up": st_s, "path_flags": paths_s,
+            "roofline": hbm_roofline("dspark_head_sample (persistent kernel, per-step exchange)", call_bytes, us_s,
+                                     None, None, timed_cold(lambda: scalls[0](), 20) if scrub is not None else None),
+        }
+        del Ws
 
     # ---------------- accept rate on the training-width workload ----------------
-    if not args.no_accept:
+    if "accept" in legs:
         sa = synth.ACCEPT_TRAIN
         d, t = synth.accept_inputs(sa)
         D, T = to_dev(d, dev), to_dev(t, dev)
@@ -254,30 +326,21 @@ def main():
         for _ in range(3):
             acall()
         torch.cuda.synchronize()
-        a0 = torch.cuda.Event(enable_timing=True)
-        a1 = torch.cuda.Event(enable_timing=True)
-        reps = 20
-        a0.record(stream)
-        for _ in range(reps):
-            acall()
-        a1.record(stream)
-        torch.cuda.synchronize()
-        a_us = a0.elapsed_time(a1) * 1e3 / reps
+        a_us = timed(acall, 20)
+        a_cold = timed_cold(acall, 10) if scrub is not None else None
         a_bytes = accept_call_bytes(sa.N, sa.V)
         gbs = a_bytes / (a_us * 1e-6) / 1e9
         line["accept_rate"] = {
             "value": round(gbs, 1), "unit": "GB/s",
             "workload": "analytic accept rate, 2048 positions x V=151936 bf16 draft/target logits",
             "us_per_call": round(a_us, 2), "positions_per_s": round(sa.N / (a_us * 1e-6), 1),
-            "roofline": {"kernel": "dspark_accept_rate", "bound": "hbm", "achieved": round(gbs, 1),
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": profiled_traffic("accept_rate_cluster_2048x151936.md", ACCEPT_SOURCES),
-                         "bytes_per_launch": a_bytes},
+            "roofline": hbm_roofline("dspark_accept_rate (cluster kernel)", a_bytes, a_us,
+                                     "accept_rate_cluster_2048x151936.md", ACCEPT_SOURCES, a_cold),
         }
-        del D, T
+        del D, T, aout
 
     # ---------------- rejection-sampling verify on the batched serving shape ----------------
-    if not args.no_verify:
+    if "verify" in legs:
         sv = synth.VERIFY_B64
         vin = synth.verify_inputs(sv)
         vd = {k: to_dev(v, dev) for k, v in vin.items()}
@@ -286,132 +349,106 @@ def main():
         for _ in range(3):
             vcall()
         torch.cuda.synchronize()
-        v0 = torch.cuda.Event(enable_timing=True)
-        v1 = torch.cuda.Event(enable_timing=True)
-        reps = 20
-        v0.record(stream)
-        for _ in range(reps):
-            vcall()
-        v1.record(stream)
-        torch.cuda.synchronize()
-        v_us = v0.elapsed_time(v1) * 1e3 / reps
+        v_us = timed(vcall, 20)
         n_acc = vout["n_accepted"].cpu().numpy()
         v_bytes = verify_call_bytes([sv.gamma] * sv.B, n_acc == sv.gamma, sv.V, sv.gamma)
-        v_gbs = v_bytes / (v_us * 1e-6) / 1e9
         line["verify"] = {
             "workload": "rejection-sampling verify, B=64 requests x 7 drafted positions, V=151936 bf16 draft and "
                         "target logits, fp32 uniforms and Gumbel rows",
             "us_per_call": round(v_us, 2), "positions_per_s": round(sv.B * sv.gamma / (v_us * 1e-6), 1),
             "mean_accepted": round(float(n_acc.mean()), 3),
-            "roofline": {"kernel": "dspark_verify (2 launches; verify_stats reads every drafted row)",
-                         "bound": "hbm", "achieved": round(v_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(v_gbs / HBM_PEAK_GBS, 4),
-                         "traffic": profiled_traffic("verify_b64_vocab151936.md", VERIFY_SOURCES),
-                         "bytes_per_launch": v_bytes},
+            "roofline": hbm_roofline("dspark_verify (2 launches; verify_stats reads every drafted row)", v_bytes,
+                                     v_us, "verify_b64_vocab151936.md", VERIFY_SOURCES),
         }
-        del vd
+        del vd, vout
 
-    if args.extra:
-        s3 = synth.SAMPLER_B64
+    # ---------------- batched Gumbel-max sampler (B=64) and the gated / RNN heads ----------------
+    s3 = synth.SAMPLER_B64
+    if legs & {"b64", "gated", "rnn"}:
         x3 = synth.sampler_batch(s3)
-        c3, _ = dh.prepare_head_sample(to_dev(x3["U"], dev), to_dev(x3["h"], dev), W["W1"], W["W2"], W["w_conf"],
-                                       0.0, to_dev(x3["x0"], dev), to_dev(x3["G"], dev))
+        d3 = {k: to_dev(x3[k], dev) for k in ("U", "h", "x0", "G")}
+        del x3
+        by3 = sampler_call_bytes(64, 7, s3.V, s3.H, s3.r) + 64 * 7 * s3.V * 4
+        flops = 2.0 * 64 * s3.gamma * s3.V * s3.r
+        # matrix-core bound with every byte read once: flops / (bytes at peak HBM)
+        attain = flops / (by3 / (HBM_PEAK_GBS * 1e9)) / 1e12
+    if "b64" in legs:
+        ws3 = torch.zeros(dh.head_sample_workspace_size(64, 7, s3.V, s3.H, s3.r), dtype=torch.uint8, device=dev)
+        c3, _ = dh.prepare_head_sample(d3["U"], d3["h"], W["W1"], W["W2"], W["w_conf"], 0.0, d3["x0"], d3["G"],
+                                       workspace=ws3)
         for _ in range(3):
             c3()
         torch.cuda.synchronize()
-        b0 = torch.cuda.Event(enable_timing=True)
-        b1 = torch.cuda.Event(enable_timing=True)
-        b0.record(stream)
-        for _ in range(10):
-            c3()
-        b1.record(stream)
-        torch.cuda.synchronize()
-        us3 = b0.elapsed_time(b1) * 1e3 / 10
-        if scrub is not None:  # the same call with cold caches
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-            for i, (c0, c1) in enumerate(ev):
-                scrub.fill_(i & 0xFF)
-                c0.record(stream)
-                c3()
-                c1.record(stream)
-            torch.cuda.synchronize()
-            cold3 = sorted(c0.elapsed_time(c1) * 1e3 for c0, c1 in ev)
-            line["cold"]["b64_us_per_call_median"] = round(cold3[len(cold3) // 2], 2)
-        flops = 2.0 * 64 * s3.gamma * s3.V * s3.r
-        by3 = sampler_call_bytes(64, 7, s3.V, s3.H, s3.r) + 64 * 7 * s3.V * 4
-        gb3 = by3 / (us3 * 1e-6) / 1e9
-        line["extra_b64"] = {"workload": "Markov-head block sampler, B=64 gamma=7 V=151936 H=5120 r=256 bf16, "
-                                         "Gumbel-max with fp32 noise",
-                             "us_per_call": round(us3, 2), "positions_per_s": round(64 * 7 / (us3 * 1e-6), 1),
-                             "mfma_tflops": round(flops / (us3 * 1e-6) / 1e12, 2),
-                             "roofline": {"kernel": "dspark_head_sample B=64 (one resident kernel)",
-                                          "bound": "hbm", "achieved": round(gb3, 1), "peak": HBM_PEAK_GBS,
-                                          "unit": "GB/s", "frac": round(gb3 / HBM_PEAK_GBS, 4),
-                                          "traffic": profiled_traffic("head_sample_resident_b64_vocab151936.md",
-                                                                      SAMPLER_SOURCES),
-                                          "bytes_per_launch": by3}}
-        # the gated Markov head on the same batch (per-step path on the matrix cores)
+        us3 = timed(c3, 20)
+        cold3 = timed_cold(c3, 10) if scrub is not None else None
+        tf = flops / (us3 * 1e-6) / 1e12
+        line["b64"] = {
+            "workload": "Markov-head block sampler, B=64 gamma=7 V=151936 H=5120 r=256 bf16, Gumbel-max with fp32 "
+                        "noise",
+            "us_per_call": round(us3, 2), "positions_per_s": round(64 * 7 / (us3 * 1e-6), 1),
+            "mfma": {"tflops": round(tf, 2), "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
+                     "frac_of_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "attainable_tflops": round(attain, 1),
+                     "attainable_frac_of_peak": round(attain / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "frac_of_attainable": round(tf / attain, 4),
+                     "note": "bias GEMM 34.85 GFLOP per call; with W2, U and G each read once at 8 TB/s the matrix "
+                             "cores cannot pass attainable_tflops"},
+            "path_flags": dh.workspace_status(ws3)[1],
+            "roofline": hbm_roofline("dspark_head_sample B=64 (one resident kernel)", by3, us3,
+                                     "head_sample_resident_b64_vocab151936.md", SAMPLER_SOURCES, cold3),
+        }
+        del ws3
+    if "gated" in legs:
         Wg3 = to_dev(synth.gate_weights(s3, 0.02), dev)
-        cg, _ = dh.prepare_head_sample(to_dev(x3["U"], dev), to_dev(x3["h"], dev), W["W1"], W["W2"], W["w_conf"],
-                                       0.0, to_dev(x3["x0"], dev), to_dev(x3["G"], dev), Wg=Wg3)
+        cg, _ = dh.prepare_head_sample(d3["U"], d3["h"], W["W1"], W["W2"], W["w_conf"], 0.0, d3["x0"], d3["G"],
+                                       Wg=Wg3)
         for _ in range(2):
             cg()
         torch.cuda.synchronize()
-        b0.record(stream)
-        for _ in range(5):
-            cg()
-        b1.record(stream)
-        torch.cuda.synchronize()
-        usg = b0.elapsed_time(b1) * 1e3 / 5
+        usg = timed(cg, 10)
         byg = by3 + s3.r * (s3.H + s3.r) * 2
-        gbg = byg / (usg * 1e-6) / 1e9
-        line["extra_gated_b64"] = {
+        line["gated_b64"] = {
             "workload": "gated Markov head, B=64 gamma=7 V=151936 H=5120 r=256 bf16, Gumbel-max with fp32 noise",
             "us_per_call": round(usg, 2), "positions_per_s": round(64 * 7 / (usg * 1e-6), 1),
-            "roofline": {"kernel": "dspark_head_sample_gated (per-step matrix-core path: gate and bias "
-                                   "kernels per position)",
-                         "bound": "hbm", "achieved": round(gbg, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbg / HBM_PEAK_GBS, 4),
-                         "traffic": profiled_traffic("head_sample_gated_b64_vocab151936.md", SAMPLER_SOURCES),
-                         "bytes_per_launch": byg}}
-        # the RNN head on the same batch (per-step path on the matrix cores)
+            "roofline": hbm_roofline("dspark_head_sample_gated", byg, usg, "head_sample_gated_b64_vocab151936.md",
+                                     SAMPLER_SOURCES)}
+        del Wg3
+    if "rnn" in legs:
         Wr3 = tuple(to_dev(a, dev) for a in synth.rnn_weights(s3, 0.015))
-        cr, _ = dh.prepare_head_sample(to_dev(x3["U"], dev), to_dev(x3["h"], dev), W["W1"], W["W2"], W["w_conf"],
-                                       0.0, to_dev(x3["x0"], dev), to_dev(x3["G"], dev), Wr=Wr3)
+        cr, _ = dh.prepare_head_sample(d3["U"], d3["h"], W["W1"], W["W2"], W["w_conf"], 0.0, d3["x0"], d3["G"],
+                                       Wr=Wr3)
         for _ in range(2):
             cr()
         torch.cuda.synchronize()
-        b0.record(stream)
-        for _ in range(5):
-            cr()
-        b1.record(stream)
-        torch.cuda.synchronize()
-        usr = b0.elapsed_time(b1) * 1e3 / 5
+        usr = timed(cr, 10)
         byr = by3 + 2 * s3.r * (2 * s3.r + s3.H) * 2
-        gbr = byr / (usr * 1e-6) / 1e9
-        line["extra_rnn_b64"] = {
+        line["rnn_b64"] = {
             "workload": "RNN head, B=64 gamma=7 V=151936 H=5120 r=256 bf16, Gumbel-max with fp32 noise",
             "us_per_call": round(usr, 2), "positions_per_s": round(64 * 7 / (usr * 1e-6), 1),
-            "roofline": {"kernel": "dspark_head_sample_rnn (per-step matrix-core path: state and bias "
-                                   "kernels per position)",
-                         "bound": "hbm", "achieved": round(gbr, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbr / HBM_PEAK_GBS, 4),
-                         "traffic": profiled_traffic("head_sample_rnn_b64_vocab151936.md", SAMPLER_SOURCES),
-                         "bytes_per_launch": byr}}
+            "roofline": hbm_roofline("dspark_head_sample_rnn", byr, usr, "head_sample_rnn_b64_vocab151936.md",
+                                     SAMPLER_SOURCES)}
+        del Wr3
+    if legs & {"b64", "gated", "rnn"}:
+        del d3
+
+    # ---------------- prefix scheduler at training block width ----------------
+    if "schedule" in legs:
         s5 = synth.SCHEDULE_TRAIN
+        sch = {"workload": "prefix scheduler (Algorithm 1), B=256 requests x gamma=16, 4096-entry throughput "
+                           "table; 'tokens': SPS(n) = n/(2+0.004n) as stated, 'steps': SPS(n) = 1/(2+0.004n)",
+               "bound": "latency (one workgroup)"}
         for kind in ("tokens", "steps"):
-            c5, _ = dh.prepare_prefix_schedule(to_dev(synth.schedule_conf(s5), dev),
-                                               to_dev(synth.sps_table(s5.n_sps, kind), dev))
+            c5, o5 = dh.prepare_prefix_schedule(to_dev(synth.schedule_conf(s5), dev),
+                                                to_dev(synth.sps_table(s5.n_sps, kind), dev))
             for _ in range(5):
                 c5()
             torch.cuda.synchronize()
-            b0.record(stream)
-            for _ in range(50):
-                c5()
-            b1.record(stream)
-            torch.cuda.synchronize()
-            line[f"extra_sched_{kind}_us"] = round(b0.elapsed_time(b1) * 1e3 / 50, 2)
-        # the teacher-forced block bias with the joint loss at 2048 training positions
+            sch[f"{kind}_us_per_call"] = round(timed(c5, 100), 2)
+            sch[f"{kind}_n_selected"] = int(o5["n_selected"].item())
+        line["schedule"] = sch
+
+    # ---------------- teacher-forced block bias with the joint loss ----------------
+    if "loss" in legs:
         s6 = synth.LOSS_TRAIN
         x6 = synth.loss_inputs(s6)
         d6 = {k: (to_dev(v, dev) if isinstance(v, np.ndarray) else v) for k, v in x6.items()}
@@ -421,26 +458,16 @@ def main():
         for _ in range(2):
             c6()
         torch.cuda.synchronize()
-        b0.record(stream)
-        for _ in range(5):
-            c6()
-        b1.record(stream)
-        torch.cuda.synchronize()
-        us6 = b0.elapsed_time(b1) * 1e3 / 5
+        us6 = timed(c6, 5)
         M6 = s6.N * s6.gamma
         by6 = (2 * M6 * s6.V * 2 + s6.V * s6.r * 2 + M6 * s6.r * 2 + M6 * s6.H * 2 + (s6.H + s6.r) * 2 + 8 * M6
                + 16 * M6 + 16)
-        gb6 = by6 / (us6 * 1e-6) / 1e9
-        line["extra_block_loss"] = {
+        line["block_loss"] = {
             "workload": "teacher-forced block bias + joint loss (CE, L1, confidence BCE), 2048 positions "
                         "(128 anchors x block 16), V=151936 H=5120 r=256 bf16",
             "us_per_call": round(us6, 2), "positions_per_s": round(M6 / (us6 * 1e-6), 1),
             "mfma_tflops": round(2 * M6 * s6.V * s6.r / (us6 * 1e-6) / 1e12, 2),
-            "roofline": {"kernel": "dspark_block_loss (two tile passes over U and t, W2 on the matrix cores)",
-                         "bound": "hbm", "achieved": round(gb6, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gb6 / HBM_PEAK_GBS, 4),
-                         "traffic": profiled_traffic("block_loss_2048x151936.md", LOSS_SOURCES),
-                         "bytes_per_launch": by6}}
+            "roofline": hbm_roofline("dspark_block_loss", by6, us6, "block_loss_2048x151936.md", LOSS_SOURCES)}
         del d6
 
     if args.calib_copy:
@@ -451,29 +478,70 @@ def main():
         torch.cuda.synchronize()
         line["calib_copy_bytes"] = 1 << 30
 
-    # ---------------- CPU oracle on a bounded sample ----------------
-    if not args.no_cpu:
+    # ---------------- CPU oracle on a bounded sample, and parity of those anchors ----------------
+    if "cpu" in legs:
+        from concurrent.futures import ThreadPoolExecutor
+
         import oracle
 
-        n_cpu = 0
+        ref = []
         tc0 = time.perf_counter()
-        while n_cpu < len(host_batches) and (time.perf_counter() - tc0) < 12.0:
-            x = host_batches[n_cpu]
-            oracle.head_sample(x["U"], x["h"], w["W1"], w["W2"], w["w_conf"], w["b_conf"], x["x0"])
-            n_cpu += 1
-        t_samp = time.perf_counter() - tc0
+        while len(ref) < len(host_batches) and (time.perf_counter() - tc0) < 10.0:
+            x = host_batches[len(ref)]
+            ref.append(oracle.head_sample(x["U"], x["h"], w["W1"], w["W2"], w["w_conf"], w["b_conf"], x["x0"]))
+        t_one = (time.perf_counter() - tc0) / len(ref)
         conf_host = conf.cpu().numpy()
         tc1 = time.perf_counter()
         oracle.prefix_schedule(conf_host, sps_host)
         t_sched = time.perf_counter() - tc1
-        # one step = n_anch sampler calls + one schedule: scale the sample
-        cpu_step_s = t_samp / n_cpu * n_anch + t_sched
+        # every host core: independent anchors on a thread pool (the C oracle
+        # releases the interpreter lock while it runs)
+        nthreads = os.cpu_count() or 1
+        n_par = min(len(host_batches), 4 * nthreads)
+        batch = host_batches[:n_par]
+        with ThreadPoolExecutor(max_workers=nthreads) as ex:
+            tp0 = time.perf_counter()
+            list(ex.map(lambda x: oracle.head_sample(x["U"], x["h"], w["W1"], w["W2"], w["w_conf"], w["b_conf"],
+                                                      x["x0"]), batch))
+            t_par = (time.perf_counter() - tp0) / n_par
+        cpu_step_1 = t_one * n_anch + t_sched
+        cpu_step_n = t_par * n_anch + t_sched
         line["cpu_baseline"] = {
-            "value": round(positions / cpu_step_s, 2), "unit": "draft positions/s", "cores": 1, "kind": "oracle",
-            "sample": f"oracle sampler on {n_cpu} of the {n_anch} anchors ({t_samp:.1f} s, fp64, single thread), "
-                      f"scaled to {n_anch}, plus one oracle schedule of the {n_anch}x7 confidences "
-                      f"({t_sched * 1e3:.1f} ms); host: {os.cpu_count()} logical CPUs",
+            "value": round(positions / cpu_step_n, 2), "unit": "draft positions/s", "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"oracle sampler (fp64 C) on {n_par} of the {n_anch} anchors over {nthreads} threads "
+                      f"({t_par * n_par:.1f} s) and on {len(ref)} anchors on one thread ({t_one * len(ref):.1f} s), "
+                      f"each scaled to {n_anch} anchors, plus one oracle schedule of the {n_anch}x7 confidences "
+                      f"({t_sched * 1e3:.1f} ms)",
+            "single_thread_value": round(positions / cpu_step_1, 2),
+            "nproc": nthreads, "cpu_model": cpu_model(),
         }
+        # parity of the anchors the oracle computed against the GPU's tokens of
+        # the timed steps: tokens up to the first difference, which must be a
+        # near-tie (oracle margin < 1e-3)
+        gtok = tokens.cpu().numpy()
+        gconf = conf_host
+        gsurv = surv.cpu().numpy()
+        n_pos = n_eq = n_tie = n_bad = 0
+        cerr = serr = 0.0
+        for a, r in enumerate(ref):
+            for k in range(s.gamma):
+                n_pos += 1
+                cerr = max(cerr, abs(float(gconf[a, k]) - r["conf"][0, k]))
+                serr = max(serr, abs(float(gsurv[a, k]) - r["survival"][0, k]))
+                if gtok[a, k] == r["tokens"][0, k]:
+                    n_eq += 1
+                    continue
+                if r["margin"][0, k] < 1e-3:
+                    n_tie += 1
+                else:
+                    n_bad += 1
+                break
+        line["parity"] = {"anchors": len(ref), "positions_compared": n_pos, "tokens_equal": n_eq,
+                          "near_tie_stops": n_tie, "unexplained_mismatches": n_bad,
+                          "conf_max_abs_err": float(f"{cerr:.3g}"), "survival_max_abs_err": float(f"{serr:.3g}"),
+                          "rule": "per anchor, tokens compared in order up to the first difference, which must be "
+                                  "an oracle near-tie (margin < 1e-3); conf and survival to 1e-4 over those steps"}
 
     print(json.dumps(line), flush=True)
 

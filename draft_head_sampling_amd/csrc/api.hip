@@ -168,7 +168,7 @@ DSPARK_EXPORT dspark_status_t dspark_prefix_schedule(int64_t B, int64_t gamma, c
                                                      int64_t n_sps, int32_t* prefix_len, float* survival_out,
                                                      int32_t* order_out, double* theta_out, int32_t* n_selected_out,
                                                      void* workspace, size_t workspace_bytes, void* stream) {
-    if (B < 1 || gamma < 0 || n_sps < B || !mul_ok(B, gamma) || B * gamma > kMaxSchedPairs)
+    if (B < 1 || B > kMaxSchedPairs || gamma < 0 || n_sps < B || !mul_ok(B, gamma) || B * gamma > kMaxSchedPairs)
         return DSPARK_ERR_BAD_SHAPE;
     dspark_status_t st = check_workspace(workspace, workspace_bytes, dspark::prefix_schedule_workspace(B, gamma));
     if (st != DSPARK_OK) return st;
@@ -228,7 +228,7 @@ DSPARK_EXPORT size_t dspark_accept_rate_workspace_size(int64_t N, int64_t V, int
 }
 
 DSPARK_EXPORT size_t dspark_prefix_schedule_workspace_size(int64_t B, int64_t gamma) {
-    if (B < 1 || gamma < 0 || !mul_ok(B, gamma) || B * gamma > kMaxSchedPairs) return 0;
+    if (B < 1 || B > kMaxSchedPairs || gamma < 0 || !mul_ok(B, gamma) || B * gamma > kMaxSchedPairs) return 0;
     return dspark::prefix_schedule_workspace(B, gamma);
 }
 

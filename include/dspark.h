@@ -226,7 +226,7 @@ dspark_status_t dspark_accept_rate(int64_t N, int64_t V, int32_t dtype, const vo
  *   Theta_best = Theta), else stop.  prefix_len[r] = number of accepted pairs
  *   of request r.  The result equals that sequential binary64 scan bit for bit.
  *
- *   B >= 1, gamma >= 0, B * gamma <= 8192.
+ *   1 <= B <= 8192, gamma >= 0, B * gamma <= 8192.
  *   conf [B][gamma] fp32, values in [0, 1].
  *   sps  [n_sps] fp64, sps[n-1] = SPS(n): the throughput of a verification
  *        batch of n tokens; n_sps >= B.

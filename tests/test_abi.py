@@ -93,6 +93,7 @@ def test_prefix_schedule_validation(L):
     assert f(4, 4, FAKE, FAKE, 3, FAKE, None, None, None, None, None, 0, None) == BAD_SHAPE  # n_sps < B
     assert f(1024, 9, FAKE, FAKE, 20000, FAKE, None, None, None, None, None, 0, None) == BAD_SHAPE  # > 8192 pairs
     assert f(4, -1, FAKE, FAKE, 10, FAKE, None, None, None, None, None, 0, None) == BAD_SHAPE
+    assert f(8193, 0, FAKE, FAKE, 9000, FAKE, None, None, None, None, None, 0, None) == BAD_SHAPE  # > 8192 requests
     need = L.dspark_prefix_schedule_workspace_size(4, 4)
     ws = FAKE if need else None
     assert f(4, 4, None, FAKE, 10, FAKE, None, None, None, None, ws, need, None) == NULL_ARG

@@ -58,9 +58,9 @@ def test_ties_zeros_ones_and_empty_block():
     _check(np.full((3, 2), 0.5), np.array([1.0, 1.0, 3.0, 0.1, 0.1, 0.1, 0.1, 0.1]))  # first pair lowers Theta
 
 
-def test_tiny_survivals_take_the_sequential_finish():
+def test_tiny_survivals_past_the_exact_run():
     # survivals far below 2^-17 under an increasing curve: the scan runs past
-    # the exactly-summable run and finishes pair by pair
+    # the exactly-summable run (the rounded increments of the tail)
     rng = np.random.default_rng(5)
     conf = rng.uniform(1e-4, 0.05, (64, 16)).astype(np.float32)
     conf[:, 0] = rng.uniform(0.5, 1.0, 64).astype(np.float32)
@@ -78,3 +78,20 @@ def test_largest_supported_pair_count():
 def test_single_request():
     _check(np.array([[0.9, 0.8, 0.7, 0.2]], np.float32), synth.sps_table(5, "steps"))
     _check(np.array([[0.9, 0.8, 0.7, 0.2]], np.float32), np.array([1.0]))
+
+
+def test_tail_ties_and_binade_crossings_finish_in_order():
+    """Past the exactly-summable run the kernel sums rounded increments in
+    parallel; an increment exactly half-way between two binary64 steps (a
+    tie) or a running sum that crosses a power of two makes it finish pair by
+    pair instead.  Both must give the sequential scan's result bit for bit."""
+    tie = np.float32(1.5 * 2.0**-50)  # half-way between multiples of 2^-50 (tau in [4, 8))
+    conf = np.array([[0.9, 0.8], [0.7, 0.5], [tie, 0.5], [np.float32(3 * 2.0**-52), 1.0]], np.float32)
+    _check(conf, synth.sps_table(16, "tokens"))
+    # one request: tau = 2 - 2^-20 after the first pair, then 63 survivals of
+    # about 2^-24 carry it past 2 (the binade of the running sum changes)
+    conf = np.ones((1, 64), np.float32)
+    conf[0, 0] = np.float32(1 - 2.0**-20)
+    conf[0, 1] = np.float32(2.0**-24)
+    r = _check(conf, synth.sps_table(80, "tokens"))
+    assert r["n_selected"] == 64

@@ -17,18 +17,26 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "liboracle.so")
+# DSPARK_ORACLE_SANITIZE=1 selects a build with AddressSanitizer and
+# UndefinedBehaviorSanitizer (CPU only; the process needs libasan preloaded,
+# see run_sanitized.sh beside this file).
+_SANITIZE = os.environ.get("DSPARK_ORACLE_SANITIZE", "") == "1"
+_SO = os.path.join(_HERE, "liboracle_san.so" if _SANITIZE else "liboracle.so")
 _lib = None
 
 F32, BF16 = 0, 1
 
 
-def build(force: bool = True) -> str:
-    if force or not os.path.exists(_SO):
-        tmp = _SO + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-o", tmp, os.path.join(_HERE, "oracle.c"), "-lm"])
-        os.replace(tmp, _SO)
-    return _SO
+def build(force: bool = True, sanitize: bool | None = None) -> str:
+    san = _SANITIZE if sanitize is None else sanitize
+    so = os.path.join(_HERE, "liboracle_san.so" if san else "liboracle.so")
+    if force or not os.path.exists(so):
+        tmp = so + ".tmp"
+        flags = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                 "-fno-sanitize-recover=undefined"] if san else ["-O2"]
+        subprocess.check_call(["gcc", *flags, "-fPIC", "-shared", "-o", tmp, os.path.join(_HERE, "oracle.c"), "-lm"])
+        os.replace(tmp, so)
+    return so
 
 
 def _load():

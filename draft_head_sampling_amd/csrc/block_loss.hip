@@ -7,22 +7,29 @@
 //   d[p][v] = U[p][v] + W2[v] . W1[xp[p]]            (draft logits)
 // and the loss needs, per position, logsumexp(d), d[y], and
 // L1 = 1/2 sum_v |softmax(d)_v - softmax(t)_v|, which needs both row
-// normalisers before it can be summed.  Four launches:
-//   loss_tiles<1>  a 64-position x 512-row tile of d on the matrix cores
-//                  (bf16 in, fp32 accumulate) with the U and t tiles staged
-//                  through LDS; per lane an online max/sum of d and t; the
-//                  partial (max, sum) pairs of each vocabulary chunk go to
-//                  the workspace, and the chunk holding y writes d[y];
-//   loss_merge     per position: the chunk partials merged in a fixed order
-//                  into logsumexp(d) and logsumexp(t), and the confidence
-//                  logit w . [h; W1[xp]] + b;
-//   loss_tiles<2>  the same tiles again, summing |p_d - p_t| per chunk;
-//   loss_final     per position: L1, CE, c* = 1 - L1, conf, BCE and the
-//                  position's weighted terms; then one workgroup sums the
-//                  terms over positions in a fixed order.
-// Every workspace word is written before it is read, so the workspace needs
-// no clearing, and every reduction runs in a fixed order: repeated calls are
-// bitwise identical.
+// normalisers before it can be summed.  Five launches:
+//   loss_stream<1>  a workgroup takes a 256-row vocabulary chunk, holds
+//                   those W2 rows in registers as matrix-core A fragments and
+//                   streams up to 1024 positions through them, 32 at a time:
+//                   d on the matrix cores (bf16 in, fp32 accumulate), the U
+//                   and t tiles and the embeddings W1[xp] staged through LDS
+//                   with two blocks of loads in flight in registers; per
+//                   position and chunk it writes (max, sum) of d and t, and
+//                   the chunk holding y writes d[y];
+//   loss_merge      per position: the chunk partials merged in a fixed order
+//                   into logsumexp(d) and logsumexp(t), and the confidence
+//                   logit w . [h; W1[xp]] + b;
+//   loss_stream<2>  the same stream again, summing |p_d - p_t| per chunk;
+//   loss_final      per position: L1, CE, c* = 1 - L1, conf, BCE and the
+//                   position's weighted terms;
+//   loss_reduce     one workgroup sums the terms over positions in a fixed
+//                   order.
+// W2 crosses HBM once per (chunk, position group) work item, U and t once
+// per pass.  Every workspace word is written before it is read, so the
+// workspace needs no clearing, and every reduction runs in a fixed order:
+// repeated calls are bitwise identical.
+#include <type_traits>
+
 #include "block_loss.h"
 
 namespace dspark {
@@ -33,12 +40,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRank = 256;          // Markov rank of the matrix-core tiles
-constexpr int kRows = 128;          // vocabulary rows per tile (32 per wave)
-constexpr int kPos = 64;            // positions per workgroup (two 32-wide MFMA tiles)
-constexpr int kTiles = 4;           // tiles per vocabulary chunk
-constexpr int kChunk = kRows * kTiles;
-constexpr int kERow = kRank + 8;    // LDS row stride of the embeddings (bf16)
-constexpr int kTRow = kRows + 8;    // LDS row stride of the U and t tiles (bf16)
+constexpr int kSWaves = 8;          // waves per streaming workgroup, 32 vocabulary rows each
+constexpr int kSThreads = 64 * kSWaves;
+constexpr int kChunk = 32 * kSWaves;  // vocabulary rows per chunk (one work item's W2 rows)
+constexpr int kBlk = 32;            // positions per block (one 32-wide MFMA tile)
+constexpr int kGroupPos = 1024;     // positions per work item
+constexpr int kRow = kRank + 8;     // LDS row stride (bf16) of E and of the U and t tiles (both 256 wide)
 constexpr int kReduceThreads = 1024;
 
 __device__ __forceinline__ float bf(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -51,205 +58,234 @@ __device__ __forceinline__ void merge_ms(float& m, float& s, float mb, float sb)
     m = mm;
 }
 
-// A 64-position x 128-row tile of X (U or t) as 16-byte pieces, 4 per thread:
-// piece c covers position c / 16, rows 8 (c % 16) .. + 7.  Positions past M
-// repeat the last one; rows past V read as zero (and are never used).
-template <bool VEC>
-__device__ __forceinline__ void load_tile(const bf16_t* __restrict__ X, int64_t M, int64_t V, int64_t p0,
-                                          int64_t vt, int tid, u32x4_t (&s)[4]) {
+// One block's loads, held in registers until they are staged in LDS.  Thread
+// t covers position t / 16 of the block and 16 consecutive columns from
+// 16 (t % 16): of the U and t tiles (vocabulary rows vt + ...) and of the
+// embedding W1[xp] (rank elements).  Positions past the end repeat the last
+// one; rows past V read as zero (and are never used).
+struct BlockRegs {
+    u32x4_t u[2], t[2], e[2];
+    float l0, l1;  // pass 2: logsumexp of d and t of the lane's position (lane % 32)
+    int32_t yy;    // pass 1: the lane's position's target id
+};
+
+// The item's previous tokens (and targets or normalisers) sit in LDS, so no
+// load here waits for another load.
+struct ItemSide {
+    int32_t x[kGroupPos];
+    float a[kGroupPos], b[kGroupPos];  // pass 1: a = target id (bits); pass 2: a, b = the two logsumexps
+};
+
+template <int PASS, bool VEC>
+__device__ __forceinline__ void load_block(BlockRegs& r, const bf16_t* __restrict__ U, const bf16_t* __restrict__ T,
+                                           const bf16_t* __restrict__ W1, const ItemSide& side, int64_t V,
+                                           int64_t p_begin, int64_t pb, int64_t p_end, int64_t vt, int tid) {
+    const int pl = tid >> 4, c0 = (tid & 15) * 16;
+    const int64_t p = pb + pl < p_end ? pb + pl : p_end - 1;
+    const int32_t x = side.x[p - p_begin];  // already made a valid row
+    const u32x4_t* er = reinterpret_cast<const u32x4_t*>(W1 + (int64_t)x * kRank + c0);
+    r.e[0] = er[0];
+    r.e[1] = er[1];
+    const uint16_t* ur = reinterpret_cast<const uint16_t*>(U + p * V);
+    const uint16_t* tr = reinterpret_cast<const uint16_t*>(T + p * V);
+    const int64_t v = vt + c0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i, pl = c / 16, col = (c % 16) * 8;
-        const int64_t p = p0 + pl < M ? p0 + pl : M - 1;
-        const int64_t v = vt + col;
-        const uint16_t* row = reinterpret_cast<const uint16_t*>(X + p * V);
-        if (VEC && v + 8 <= V) {
-            s[i] = *reinterpret_cast<const u32x4_t*>(row + v);
+    for (int i = 0; i < 2; ++i) {
+        const int64_t vi = v + 8 * i;
+        if (VEC) {  // V % 8 == 0: a piece is wholly in or out; out of range, read the last (never used)
+            const int64_t vc = vi + 8 <= V ? vi : V - 8;
+            r.u[i] = *reinterpret_cast<const u32x4_t*>(ur + vc);
+            r.t[i] = *reinterpret_cast<const u32x4_t*>(tr + vc);
         } else {
-            uint32_t w[4];
+            uint32_t wu[4], wt[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t lo = v + 2 * j < V ? row[v + 2 * j] : 0u;
-                const uint32_t hi = v + 2 * j + 1 < V ? row[v + 2 * j + 1] : 0u;
-                w[j] = lo | hi << 16;
+                wu[j] = (vi + 2 * j < V ? ur[vi + 2 * j] : 0u) | (vi + 2 * j + 1 < V ? (uint32_t)ur[vi + 2 * j + 1] << 16 : 0u);
+                wt[j] = (vi + 2 * j < V ? tr[vi + 2 * j] : 0u) | (vi + 2 * j + 1 < V ? (uint32_t)tr[vi + 2 * j + 1] << 16 : 0u);
             }
-            s[i] = u32x4_t{w[0], w[1], w[2], w[3]};
+            r.u[i] = u32x4_t{wu[0], wu[1], wu[2], wu[3]};
+            r.t[i] = u32x4_t{wt[0], wt[1], wt[2], wt[3]};
         }
+    }
+    const int lane = tid & 63;
+    const int64_t q = (pb + (lane & 31) < p_end ? pb + (lane & 31) : p_end - 1) - p_begin;
+    if (PASS == 1) r.yy = __float_as_int(side.a[q]);
+    if (PASS == 2) r.l0 = side.a[q], r.l1 = side.b[q];
+}
+
+__device__ __forceinline__ void stage_block(const BlockRegs& r, uint16_t* E, uint16_t* Ut, uint16_t* Tt, int tid) {
+    const int pl = tid >> 4, c0 = (tid & 15) * 16;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        *reinterpret_cast<u32x4_t*>(E + pl * kRow + c0 + 8 * i) = r.e[i];
+        *reinterpret_cast<u32x4_t*>(Ut + pl * kRow + c0 + 8 * i) = r.u[i];
+        *reinterpret_cast<u32x4_t*>(Tt + pl * kRow + c0 + 8 * i) = r.t[i];
     }
 }
 
-// grid (ceil(M / 64), ceil(V / 512)), 256 threads.  PASS 1 writes the
-// chunk's (max, sum) of d and t per position to stats [M][chunks][4] and d[y]
-// to dy [M]; PASS 2 reads lse [M][2] and writes the chunk's sum of
-// |p_d - p_t| to l1p [M][chunks].
+// Persistent grid (at most one workgroup per compute unit), kSThreads
+// threads.  Work item i = (chunk i % nchunk, position group i / nchunk).
+// PASS 1 writes the chunk's (max, sum) of d and t per position to stats
+// [M][chunks][4] and d[y] to dy [M]; PASS 2 reads lse [M][2] and writes the
+// chunk's sum of |p_d - p_t| to l1p [M][chunks].
 template <int PASS, bool VEC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void loss_tiles(int64_t M, int64_t V, int64_t nchunk, const bf16_t* __restrict__ U,
-                                                  const bf16_t* __restrict__ T, const bf16_t* __restrict__ W1,
-                                                  const bf16_t* __restrict__ W2, const int32_t* __restrict__ xp,
-                                                  const int32_t* __restrict__ y, float* __restrict__ stats,
-                                                  float* __restrict__ dy, const float* __restrict__ lse,
-                                                  float* __restrict__ l1p) {
-    __shared__ __align__(16) uint16_t E_lds[kPos * kERow];
-    __shared__ __align__(16) uint16_t U_lds[kPos * kTRow];
-    __shared__ __align__(16) uint16_t T_lds[kPos * kTRow];
-    __shared__ float red[4][kPos][4];
+__global__ __launch_bounds__(kSThreads) void loss_stream(int64_t M, int64_t V, int64_t nchunk, int64_t nitems,
+                                                         const bf16_t* __restrict__ U, const bf16_t* __restrict__ T,
+                                                         const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W2,
+                                                         const int32_t* __restrict__ xp,
+                                                         const int32_t* __restrict__ y, float* __restrict__ stats,
+                                                         float* __restrict__ dy, const float* __restrict__ lse,
+                                                         float* __restrict__ l1p) {
+    __shared__ __align__(16) uint16_t E_lds[2][kBlk * kRow];
+    __shared__ __align__(16) uint16_t U_lds[2][kBlk * kRow];
+    __shared__ __align__(16) uint16_t T_lds[2][kBlk * kRow];
+    __shared__ float red[kSWaves][kBlk][4];
+    __shared__ ItemSide side;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, row = lane & 31, half = lane >> 5;
-    const int64_t p0 = (int64_t)blockIdx.x * kPos;
-    const int64_t chunk = blockIdx.y;
 
-    // embeddings W1[xp] of the 64 positions: 4 threads per position, 128 bytes each
-    {
-        const int pl = tid >> 2, part = tid & 3;
-        const int64_t p = p0 + pl < M ? p0 + pl : M - 1;
-        int32_t x = xp[p];
-        if (x < 0 || x >= V) x = 0;  // such a position's outputs are NaN; any row will do
-        const uint4* src = reinterpret_cast<const uint4*>(W1 + (int64_t)x * kRank + part * 64);
-        uint4 e[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = src[i];
-        uint4* dst = reinterpret_cast<uint4*>(E_lds + pl * kERow + part * 64);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) dst[i] = e[i];
-    }
-    float md[2], sd[2], mt[2], st[2], l1[2], ld[2], lt[2];
-    int32_t yv[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int64_t p = p0 + nt * 32 + row, pc = p < M ? p : M - 1;
-        md[nt] = mt[nt] = -INFINITY;
-        sd[nt] = st[nt] = l1[nt] = 0.f;
-        yv[nt] = y[pc];
-        if (PASS == 2) ld[nt] = lse[2 * pc], lt[nt] = lse[2 * pc + 1];
-    }
-    __syncthreads();
+    for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {  // workgroup-uniform
+        const int64_t chunk = item % nchunk, group = item / nchunk;
+        const int64_t vt = chunk * kChunk;
+        const int64_t p_begin = group * kGroupPos;
+        const int64_t p_end = p_begin + kGroupPos < M ? p_begin + kGroupPos : M;
+        const int nblk = (int)((p_end - p_begin + kBlk - 1) / kBlk);
 
-    // In pass 2 the loads of tile i + 1 (W2 fragments, U and t pieces) are
-    // issued once tile i's products are done and its U/t pieces are in LDS, so
-    // they are in flight during tile i's epilogue.  Pass 1 issues each tile's
-    // loads at the tile's start: its epilogue holds more state, and at two
-    // waves per SIMD the prefetched registers would spill.
-    constexpr bool kPrefetch = PASS == 2;
-    // W2 rows of a wave as A fragments: k-step s takes rank elements 16 s + 8 half .. + 7
-    auto issue = [&](int64_t vt, uint4(&a)[16], u32x4_t(&us)[4], u32x4_t(&ts)[4]) {
-        const int64_t v = vt + wave * 32 + row < V ? vt + wave * 32 + row : V - 1;
-        const uint4* src = reinterpret_cast<const uint4*>(W2 + v * kRank + half * 8);
+        // this wave's 32 W2 rows as A fragments: k-step s takes rank
+        // elements 16 s + 8 half .. + 7 of row vt + 32 wave + row
+        uint4 a[16];
+        {
+            int64_t v = vt + wave * 32 + row;
+            v = v < V ? v : V - 1;  // clamped; its products are never used
+            const uint4* src = reinterpret_cast<const uint4*>(W2 + v * kRank + half * 8);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) a[i] = src[2 * i];
-        load_tile<VEC>(U, M, V, p0, vt, tid, us);
-        load_tile<VEC>(T, M, V, p0, vt, tid, ts);
-    };
-    uint4 a_pf[16];
-    u32x4_t us_pf[4], ts_pf[4];
-    if (kPrefetch) issue(chunk * kChunk, a_pf, us_pf, ts_pf);  // the grid has no chunk past V
-    for (int tile = 0; tile < kTiles; ++tile) {
-        const int64_t vt = chunk * kChunk + (int64_t)tile * kRows;
-        if (vt >= V) break;  // the same for the whole workgroup
-        const int64_t vn = vt + kRows;
-        const bool next = tile + 1 < kTiles && vn < V;
-        uint4 a_loc[16];
-        u32x4_t us_loc[4], ts_loc[4];
-        uint4(&a)[16] = kPrefetch ? a_pf : a_loc;
-        u32x4_t(&us)[4] = kPrefetch ? us_pf : us_loc;
-        u32x4_t(&ts)[4] = kPrefetch ? ts_pf : ts_loc;
-        if (!kPrefetch) issue(vt, a, us, ts);
-        f32x16_t acc[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[nt][r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a[s]);
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const uint4 bw = *reinterpret_cast<const uint4*>(E_lds + (nt * 32 + row) * kERow + s * 16 + half * 8);
-                acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, bw), acc[nt], 0, 0,
-                                                                  0);
-            }
+            for (int s = 0; s < 16; ++s) a[s] = src[2 * s];
         }
-        __syncthreads();  // the previous tile's epilogue is done with the staged tiles
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + 256 * i, pl = c / 16, col = (c % 16) * 8;
-            *reinterpret_cast<u32x4_t*>(U_lds + pl * kTRow + col) = us[i];
-            *reinterpret_cast<u32x4_t*>(T_lds + pl * kTRow + col) = ts[i];
+        __syncthreads();  // the previous item is done with the LDS
+        for (int i = tid; i < p_end - p_begin; i += kSThreads) {
+            int32_t x = xp[p_begin + i];
+            if (x < 0 || x >= V) x = 0;  // such a position's outputs are NaN; any row will do
+            side.x[i] = x;
+            if (PASS == 1) side.a[i] = __int_as_float(y[p_begin + i]);
+            if (PASS == 2) side.a[i] = lse[2 * (p_begin + i)], side.b[i] = lse[2 * (p_begin + i) + 1];
         }
         __syncthreads();
-        if (kPrefetch && next) issue(vn, a, us, ts);
-        // lane holds rows vt + wave*32 + 8(r/4) + 4 half + r%4 of position nt*32 + row
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int pl = nt * 32 + row;
-            // d and t of element r (rows past V: -inf); read again from LDS
-            // in each sweep rather than held, which keeps the register count
-            // at two waves per SIMD
-            auto dval = [&](int r) {
-                const int vl = wave * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-                return vt + vl < V ? bf(U_lds[pl * kTRow + vl]) + acc[nt][r] : -INFINITY;
-            };
-            auto tval = [&](int r) {
-                const int vl = wave * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-                return vt + vl < V ? bf(T_lds[pl * kTRow + vl]) : -INFINITY;
-            };
-            if (PASS == 1) {
-                float mdn = -INFINITY, mtn = -INFINITY;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float dr = dval(r);
-                    mdn = fmaxf(mdn, dr);
-                    mtn = fmaxf(mtn, tval(r));
-                    const int64_t v = vt + wave * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-                    if (v == yv[nt] && v < V && p0 + pl < M) dy[p0 + pl] = dr;
-                }
-                if (mdn > -INFINITY) {  // the lane has rows in this tile
-                    float s1 = 0.f, s2 = 0.f;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) s1 += __expf(dval(r) - mdn), s2 += __expf(tval(r) - mtn);
-                    merge_ms(md[nt], sd[nt], mdn, s1);
-                    merge_ms(mt[nt], st[nt], mtn, s2);
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float dr = dval(r);
-                    if (dr > -INFINITY) l1[nt] += fabsf(__expf(dr - ld[nt]) - __expf(tval(r) - lt[nt]));
-                }
-            }
-        }
-    }
+        BlockRegs rg[2];
+        load_block<PASS, VEC>(rg[0], U, T, W1, side, V, p_begin, p_begin, p_end, vt, tid);
+        load_block<PASS, VEC>(rg[1], U, T, W1, side, V, p_begin, p_begin + kBlk, p_end, vt, tid);
+        stage_block(rg[0], E_lds[0], U_lds[0], T_lds[0], tid);
+        float cur_l0 = rg[0].l0, cur_l1 = rg[0].l1;
+        int32_t cur_y = rg[0].yy;
+        load_block<PASS, VEC>(rg[0], U, T, W1, side, V, p_begin, p_begin + 2 * kBlk, p_end, vt, tid);
+        __syncthreads();
 
-    // the two lanes of a position (half 0 and 1), then the four waves, in order
+        // One block: SLOT holds block b; nr holds block b + 1 (in flight),
+        // the other register set block b + 2.  The two sets swap roles from
+        // block to block, so the loop is unrolled by two and each set is
+        // named statically (selecting between them at run time would wait
+        // for both).
+        auto block = [&](auto slot_c, BlockRegs& nr, int b) {
+            constexpr int slot = decltype(slot_c)::value;
+            const int64_t pb = p_begin + (int64_t)b * kBlk;
+            // d of this wave's 32 rows for the block's 32 positions
+            f32x16_t acc;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int pl = nt * 32 + row;
-        if (PASS == 1) {
-            const float m2 = __shfl_xor(md[nt], 32), s2 = __shfl_xor(sd[nt], 32);
-            const float m3 = __shfl_xor(mt[nt], 32), s3 = __shfl_xor(st[nt], 32);
+            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const uint4 bw = *reinterpret_cast<const uint4*>(&E_lds[slot][row * kRow + s * 16 + half * 8]);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[s]),
+                                                              __builtin_bit_cast(bf16x8_t, bw), acc, 0, 0, 0);
+            }
+            // lane: position pb + row, vocabulary rows vt + 32 wave + 8 (r / 4) + 4 half + r % 4;
+            // the U and t values stay packed (two per register) and are widened where used
+            const uint16_t* ul = &U_lds[slot][row * kRow + wave * 32 + 4 * half];
+            const uint16_t* tl = &T_lds[slot][row * kRow + wave * 32 + 4 * half];
+            uint2 uu[4], tt[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uu[q] = *reinterpret_cast<const uint2*>(ul + 8 * q);
+                tt[q] = *reinterpret_cast<const uint2*>(tl + 8 * q);
+            }
+            const int64_t v0 = vt + wave * 32 + 4 * half;
+            auto word = [](const uint2& w, int j) { return j < 2 ? w.x : w.y; };
+            auto d_at = [&](int r) {
+                const uint32_t w = word(uu[r / 4], r % 4);
+                const float u = (r & 1) ? widen_hi(w) : widen_lo(w);
+                return v0 + 8 * (r / 4) + (r % 4) < V ? u + acc[r] : -INFINITY;
+            };
+            auto t_at = [&](int r) {
+                const uint32_t w = word(tt[r / 4], r % 4);
+                const float t = (r & 1) ? widen_hi(w) : widen_lo(w);
+                return v0 + 8 * (r / 4) + (r % 4) < V ? t : -INFINITY;
+            };
+            const bool live = pb + row < p_end;
+            float o0, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+            if (PASS == 1) {
+                float md = -INFINITY, mt = -INFINITY, dyv = 0.f;
+                bool hit = false;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float dr = d_at(r);
+                    md = fmaxf(md, dr);
+                    mt = fmaxf(mt, t_at(r));
+                    const int64_t v = v0 + 8 * (r / 4) + (r % 4);
+                    hit = hit || v == cur_y;
+                    dyv = v == cur_y ? dr : dyv;
+                }
+                if (live && hit) dy[pb + row] = dyv;
+                float sd = 0.f, st = 0.f;
+                if (md > -INFINITY) {  // the lane has rows in this chunk
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sd += __expf(d_at(r) - md), st += __expf(t_at(r) - mt);
+                }
+                const float m2 = __shfl_xor(md, 32), s2 = __shfl_xor(sd, 32);
+                const float m3 = __shfl_xor(mt, 32), s3 = __shfl_xor(st, 32);
+                merge_ms(md, sd, m2, s2);
+                merge_ms(mt, st, m3, s3);
+                o0 = md, o1 = sd, o2 = mt, o3 = st;
+            } else {
+                float sum = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float dr = d_at(r);
+                    if (dr > -INFINITY) sum += fabsf(__expf(dr - cur_l0) - __expf(t_at(r) - cur_l1));
+                }
+                o0 = sum + __shfl_xor(sum, 32);
+            }
             if (half == 0) {
-                merge_ms(md[nt], sd[nt], m2, s2);
-                merge_ms(mt[nt], st[nt], m3, s3);
-                red[wave][pl][0] = md[nt], red[wave][pl][1] = sd[nt];
-                red[wave][pl][2] = mt[nt], red[wave][pl][3] = st[nt];
+                red[wave][row][0] = o0;
+                if (PASS == 1) red[wave][row][1] = o1, red[wave][row][2] = o2, red[wave][row][3] = o3;
             }
-        } else {
-            const float o = __shfl_xor(l1[nt], 32);
-            if (half == 0) red[wave][pl][0] = l1[nt] + o;
-        }
-    }
-    __syncthreads();
-    if (tid < kPos && p0 + tid < M) {
-        const int64_t p = p0 + tid;
-        if (PASS == 1) {
-            float m1 = red[0][tid][0], s1 = red[0][tid][1], m2 = red[0][tid][2], s2 = red[0][tid][3];
-            for (int w = 1; w < 4; ++w) {
-                merge_ms(m1, s1, red[w][tid][0], red[w][tid][1]);
-                merge_ms(m2, s2, red[w][tid][2], red[w][tid][3]);
+            __syncthreads();  // red is complete; every wave is done with this slot
+            if (tid < kBlk && pb + tid < p_end) {  // the eight waves, in order
+                const int64_t p = pb + tid;
+                if (PASS == 1) {
+                    float m1 = red[0][tid][0], s1 = red[0][tid][1], m2 = red[0][tid][2], s2 = red[0][tid][3];
+                    for (int w = 1; w < kSWaves; ++w) {
+                        merge_ms(m1, s1, red[w][tid][0], red[w][tid][1]);
+                        merge_ms(m2, s2, red[w][tid][2], red[w][tid][3]);
+                    }
+                    float4 o;
+                    o.x = m1, o.y = s1, o.z = m2, o.w = s2;
+                    reinterpret_cast<float4*>(stats)[p * nchunk + chunk] = o;
+                } else {
+                    float t = red[0][tid][0];
+                    for (int w = 1; w < kSWaves; ++w) t += red[w][tid][0];
+                    l1p[p * nchunk + chunk] = t;
+                }
             }
-            float4 o;
-            o.x = m1, o.y = s1, o.z = m2, o.w = s2;
-            reinterpret_cast<float4*>(stats)[p * nchunk + chunk] = o;
-        } else {
-            l1p[p * nchunk + chunk] = ((red[0][tid][0] + red[1][tid][0]) + red[2][tid][0]) + red[3][tid][0];
+            // block b + 1 into the other slot; its registers then take block
+            // b + 3 (unconditionally: past the last block they re-read the last
+            // position, in bounds and never used, which keeps the waits one
+            // block deep)
+            stage_block(nr, E_lds[slot ^ 1], U_lds[slot ^ 1], T_lds[slot ^ 1], tid);
+            cur_l0 = nr.l0, cur_l1 = nr.l1, cur_y = nr.yy;
+            load_block<PASS, VEC>(nr, U, T, W1, side, V, p_begin, pb + 3 * kBlk, p_end, vt, tid);
+            __syncthreads();  // slot b + 1 is staged; red may be rewritten
+        };
+        for (int b = 0; b < nblk; b += 2) {
+            block(std::integral_constant<int, 0>{}, rg[1], b);
+            if (b + 1 < nblk) block(std::integral_constant<int, 1>{}, rg[0], b + 1);
         }
     }
 }
@@ -416,13 +452,18 @@ hipError_t block_loss_launch(int64_t N, int64_t gamma, int64_t V, int64_t H, con
         return hipGetLastError();
     }
     const bool vec = V % 8 == 0 && (uintptr_t)U % 16 == 0 && (uintptr_t)t % 16 == 0;
-    const dim3 grid((uint32_t)((M + kPos - 1) / kPos), (uint32_t)nchunk);
+    const int64_t nitems = nchunk * ((M + kGroupPos - 1) / kGroupPos);
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    const dim3 grid((uint32_t)(nitems < cus ? nitems : cus));
     if (vec)
-        hipLaunchKernelGGL((loss_tiles<1, true>), grid, dim3(256), 0, stream, M, V, nchunk, Ub, Tb, W1b, W2b, xp, y,
-                           s.stats, s.dy, s.lse, s.l1p);
+        hipLaunchKernelGGL((loss_stream<1, true>), grid, dim3(kSThreads), 0, stream, M, V, nchunk, nitems, Ub, Tb, W1b,
+                           W2b, xp, y, s.stats, s.dy, s.lse, s.l1p);
     else
-        hipLaunchKernelGGL((loss_tiles<1, false>), grid, dim3(256), 0, stream, M, V, nchunk, Ub, Tb, W1b, W2b, xp, y,
-                           s.stats, s.dy, s.lse, s.l1p);
+        hipLaunchKernelGGL((loss_stream<1, false>), grid, dim3(kSThreads), 0, stream, M, V, nchunk, nitems, Ub, Tb,
+                           W1b, W2b, xp, y, s.stats, s.dy, s.lse, s.l1p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(loss_merge, dim3((uint32_t)M), dim3(256), 0, stream, M, V, H, nchunk, s.stats,
@@ -430,11 +471,11 @@ hipError_t block_loss_launch(int64_t N, int64_t gamma, int64_t V, int64_t H, con
                        s.zc);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (vec)
-        hipLaunchKernelGGL((loss_tiles<2, true>), grid, dim3(256), 0, stream, M, V, nchunk, Ub, Tb, W1b, W2b, xp, y,
-                           s.stats, s.dy, s.lse, s.l1p);
+        hipLaunchKernelGGL((loss_stream<2, true>), grid, dim3(kSThreads), 0, stream, M, V, nchunk, nitems, Ub, Tb, W1b,
+                           W2b, xp, y, s.stats, s.dy, s.lse, s.l1p);
     else
-        hipLaunchKernelGGL((loss_tiles<2, false>), grid, dim3(256), 0, stream, M, V, nchunk, Ub, Tb, W1b, W2b, xp, y,
-                           s.stats, s.dy, s.lse, s.l1p);
+        hipLaunchKernelGGL((loss_stream<2, false>), grid, dim3(kSThreads), 0, stream, M, V, nchunk, nitems, Ub, Tb,
+                           W1b, W2b, xp, y, s.stats, s.dy, s.lse, s.l1p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(loss_final, dim3((uint32_t)((M + 3) / 4)), dim3(256), 0, stream, M, gamma, V, nchunk,
                        s.l1p, s.dy, s.lse, s.zc, xp, y, mask, decay, ce, l1, conf, bce, s.terms);

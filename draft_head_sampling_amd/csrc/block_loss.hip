@@ -48,7 +48,13 @@ constexpr int kGroupPos = 1024;     // positions per work item
 constexpr int kRow = kRank + 8;     // LDS row stride (bf16) of E and of the U and t tiles (both 256 wide)
 constexpr int kReduceThreads = 1024;
 
+constexpr uint32_t kNegInf2 = 0xff80ff80u;  // two bf16 -inf
+constexpr float kLog2e = 1.4426950408889634f;
+
 __device__ __forceinline__ float bf(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// e^(x - m) as 2^(x log2 e - m log2 e), the argument in one fused step; mk = m log2 e
+__device__ __forceinline__ float exp_shift(float x, float mk) { return __builtin_amdgcn_exp2f(fmaf(x, kLog2e, -mk)); }
 
 // (m, s) pairs of an online softmax normaliser: merge b into a.
 __device__ __forceinline__ void merge_ms(float& m, float& s, float mb, float sb) {
@@ -62,7 +68,8 @@ __device__ __forceinline__ void merge_ms(float& m, float& s, float mb, float sb)
 // t covers position t / 16 of the block and 16 consecutive columns from
 // 16 (t % 16): of the U and t tiles (vocabulary rows vt + ...) and of the
 // embedding W1[xp] (rank elements).  Positions past the end repeat the last
-// one; rows past V read as zero (and are never used).
+// one; rows past V read as bf16 -inf in both tiles, so they drop out of every
+// max, exponential and sum without a test in the epilogue.
 struct BlockRegs {
     u32x4_t u[2], t[2], e[2];
     float l0, l1;  // pass 2: logsumexp of d and t of the lane's position (lane % 32)
@@ -92,16 +99,21 @@ __device__ __forceinline__ void load_block(BlockRegs& r, const bf16_t* __restric
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int64_t vi = v + 8 * i;
-        if (VEC) {  // V % 8 == 0: a piece is wholly in or out; out of range, read the last (never used)
-            const int64_t vc = vi + 8 <= V ? vi : V - 8;
-            r.u[i] = *reinterpret_cast<const u32x4_t*>(ur + vc);
-            r.t[i] = *reinterpret_cast<const u32x4_t*>(tr + vc);
+        if (VEC) {  // V % 8 == 0: a piece is wholly in or out
+            const bool in = vi + 8 <= V;
+            const int64_t vc = in ? vi : V - 8;  // out of range: an in-bounds read, replaced below
+            const u32x4_t uw = *reinterpret_cast<const u32x4_t*>(ur + vc);
+            const u32x4_t tw = *reinterpret_cast<const u32x4_t*>(tr + vc);
+            const u32x4_t ninf = {kNegInf2, kNegInf2, kNegInf2, kNegInf2};
+            r.u[i] = in ? uw : ninf;
+            r.t[i] = in ? tw : ninf;
         } else {
             uint32_t wu[4], wt[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                wu[j] = (vi + 2 * j < V ? ur[vi + 2 * j] : 0u) | (vi + 2 * j + 1 < V ? (uint32_t)ur[vi + 2 * j + 1] << 16 : 0u);
-                wt[j] = (vi + 2 * j < V ? tr[vi + 2 * j] : 0u) | (vi + 2 * j + 1 < V ? (uint32_t)tr[vi + 2 * j + 1] << 16 : 0u);
+                const int64_t a = vi + 2 * j, b = a + 1;
+                wu[j] = (a < V ? ur[a] : 0xff80u) | (b < V ? (uint32_t)ur[b] << 16 : 0xff800000u);
+                wt[j] = (a < V ? tr[a] : 0xff80u) | (b < V ? (uint32_t)tr[b] << 16 : 0xff800000u);
             }
             r.u[i] = u32x4_t{wu[0], wu[1], wu[2], wu[3]};
             r.t[i] = u32x4_t{wt[0], wt[1], wt[2], wt[3]};
@@ -124,12 +136,14 @@ __device__ __forceinline__ void stage_block(const BlockRegs& r, uint16_t* E, uin
 }
 
 // Persistent grid (at most one workgroup per compute unit), kSThreads
-// threads.  Work item i = (chunk i % nchunk, position group i / nchunk).
+// threads.  The work is nchunk x nb blocks (nb = ceil(M / kBlk)), chunk
+// major; workgroup g takes the contiguous share [g total / G, (g + 1) total
+// / G), cut into items of one chunk and at most kGroupPos positions.
 // PASS 1 writes the chunk's (max, sum) of d and t per position to stats
 // [M][chunks][4] and d[y] to dy [M]; PASS 2 reads lse [M][2] and writes the
 // chunk's sum of |p_d - p_t| to l1p [M][chunks].
 template <int PASS, bool VEC>
-__global__ __launch_bounds__(kSThreads) void loss_stream(int64_t M, int64_t V, int64_t nchunk, int64_t nitems,
+__global__ __launch_bounds__(kSThreads) void loss_stream(int64_t M, int64_t V, int64_t nchunk,
                                                          const bf16_t* __restrict__ U, const bf16_t* __restrict__ T,
                                                          const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W2,
                                                          const int32_t* __restrict__ xp,
@@ -143,12 +157,17 @@ __global__ __launch_bounds__(kSThreads) void loss_stream(int64_t M, int64_t V, i
     __shared__ ItemSide side;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, row = lane & 31, half = lane >> 5;
 
-    for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {  // workgroup-uniform
-        const int64_t chunk = item % nchunk, group = item / nchunk;
+    const int64_t nb = (M + kBlk - 1) / kBlk, total = nchunk * nb;
+    const int64_t u_hi = total * (blockIdx.x + 1) / gridDim.x;
+    for (int64_t u = total * blockIdx.x / gridDim.x; u < u_hi;) {  // workgroup-uniform
+        const int64_t chunk = u / nb, b0 = u % nb;
+        int64_t b1 = b0 + kGroupPos / kBlk < nb ? b0 + kGroupPos / kBlk : nb;
+        b1 = b1 - b0 < u_hi - u ? b1 : b0 + (u_hi - u);
+        u += b1 - b0;
         const int64_t vt = chunk * kChunk;
-        const int64_t p_begin = group * kGroupPos;
-        const int64_t p_end = p_begin + kGroupPos < M ? p_begin + kGroupPos : M;
-        const int nblk = (int)((p_end - p_begin + kBlk - 1) / kBlk);
+        const int64_t p_begin = b0 * kBlk;
+        const int64_t p_end = b1 * kBlk < M ? b1 * kBlk : M;
+        const int nblk = (int)(b1 - b0);
 
         // this wave's 32 W2 rows as A fragments: k-step s takes rank
         // elements 16 s + 8 half .. + 7 of row vt + 32 wave + row
@@ -208,15 +227,13 @@ __global__ __launch_bounds__(kSThreads) void loss_stream(int64_t M, int64_t V, i
             }
             const int64_t v0 = vt + wave * 32 + 4 * half;
             auto word = [](const uint2& w, int j) { return j < 2 ? w.x : w.y; };
-            auto d_at = [&](int r) {
+            auto d_at = [&](int r) {  // rows past V: -inf (the U tile holds -inf there)
                 const uint32_t w = word(uu[r / 4], r % 4);
-                const float u = (r & 1) ? widen_hi(w) : widen_lo(w);
-                return v0 + 8 * (r / 4) + (r % 4) < V ? u + acc[r] : -INFINITY;
+                return ((r & 1) ? widen_hi(w) : widen_lo(w)) + acc[r];
             };
             auto t_at = [&](int r) {
                 const uint32_t w = word(tt[r / 4], r % 4);
-                const float t = (r & 1) ? widen_hi(w) : widen_lo(w);
-                return v0 + 8 * (r / 4) + (r % 4) < V ? t : -INFINITY;
+                return (r & 1) ? widen_hi(w) : widen_lo(w);
             };
             const bool live = pb + row < p_end;
             float o0, o1 = 0.f, o2 = 0.f, o3 = 0.f;
@@ -233,23 +250,22 @@ __global__ __launch_bounds__(kSThreads) void loss_stream(int64_t M, int64_t V, i
                     dyv = v == cur_y ? dr : dyv;
                 }
                 if (live && hit) dy[pb + row] = dyv;
+                // a lane whose rows are all -inf on one side sums zeros there (shift 0, not -inf)
                 float sd = 0.f, st = 0.f;
-                if (md > -INFINITY) {  // the lane has rows in this chunk
+                const float mdk = md > -INFINITY ? md * kLog2e : 0.f, mtk = mt > -INFINITY ? mt * kLog2e : 0.f;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) sd += __expf(d_at(r) - md), st += __expf(t_at(r) - mt);
-                }
+                for (int r = 0; r < 16; ++r) sd += exp_shift(d_at(r), mdk), st += exp_shift(t_at(r), mtk);
                 const float m2 = __shfl_xor(md, 32), s2 = __shfl_xor(sd, 32);
                 const float m3 = __shfl_xor(mt, 32), s3 = __shfl_xor(st, 32);
                 merge_ms(md, sd, m2, s2);
                 merge_ms(mt, st, m3, s3);
                 o0 = md, o1 = sd, o2 = mt, o3 = st;
             } else {
+                // every row counts, a -inf logit as probability 0 (rows past V: 0 on both sides)
                 float sum = 0.f;
+                const float l0k = cur_l0 * kLog2e, l1k = cur_l1 * kLog2e;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float dr = d_at(r);
-                    if (dr > -INFINITY) sum += fabsf(__expf(dr - cur_l0) - __expf(t_at(r) - cur_l1));
-                }
+                for (int r = 0; r < 16; ++r) sum += fabsf(exp_shift(d_at(r), l0k) - exp_shift(t_at(r), l1k));
                 o0 = sum + __shfl_xor(sum, 32);
             }
             if (half == 0) {
@@ -452,17 +468,17 @@ hipError_t block_loss_launch(int64_t N, int64_t gamma, int64_t V, int64_t H, con
         return hipGetLastError();
     }
     const bool vec = V % 8 == 0 && (uintptr_t)U % 16 == 0 && (uintptr_t)t % 16 == 0;
-    const int64_t nitems = nchunk * ((M + kGroupPos - 1) / kGroupPos);
+    const int64_t total = nchunk * ((M + kBlk - 1) / kBlk);
     int cus = 0, dev = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         cus = 256;
-    const dim3 grid((uint32_t)(nitems < cus ? nitems : cus));
+    const dim3 grid((uint32_t)(total < cus ? total : cus));
     if (vec)
-        hipLaunchKernelGGL((loss_stream<1, true>), grid, dim3(kSThreads), 0, stream, M, V, nchunk, nitems, Ub, Tb, W1b,
+        hipLaunchKernelGGL((loss_stream<1, true>), grid, dim3(kSThreads), 0, stream, M, V, nchunk, Ub, Tb, W1b,
                            W2b, xp, y, s.stats, s.dy, s.lse, s.l1p);
     else
-        hipLaunchKernelGGL((loss_stream<1, false>), grid, dim3(kSThreads), 0, stream, M, V, nchunk, nitems, Ub, Tb,
+        hipLaunchKernelGGL((loss_stream<1, false>), grid, dim3(kSThreads), 0, stream, M, V, nchunk, Ub, Tb,
                            W1b, W2b, xp, y, s.stats, s.dy, s.lse, s.l1p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -471,10 +487,10 @@ hipError_t block_loss_launch(int64_t N, int64_t gamma, int64_t V, int64_t H, con
                        s.zc);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (vec)
-        hipLaunchKernelGGL((loss_stream<2, true>), grid, dim3(kSThreads), 0, stream, M, V, nchunk, nitems, Ub, Tb, W1b,
+        hipLaunchKernelGGL((loss_stream<2, true>), grid, dim3(kSThreads), 0, stream, M, V, nchunk, Ub, Tb, W1b,
                            W2b, xp, y, s.stats, s.dy, s.lse, s.l1p);
     else
-        hipLaunchKernelGGL((loss_stream<2, false>), grid, dim3(kSThreads), 0, stream, M, V, nchunk, nitems, Ub, Tb,
+        hipLaunchKernelGGL((loss_stream<2, false>), grid, dim3(kSThreads), 0, stream, M, V, nchunk, Ub, Tb,
                            W1b, W2b, xp, y, s.stats, s.dy, s.lse, s.l1p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(loss_final, dim3((uint32_t)((M + 3) / 4)), dim3(256), 0, stream, M, gamma, V, nchunk,

@@ -84,6 +84,29 @@ def test_mask_weights_coefficients_and_invalid_tokens():
     assert np.isnan(got["ce"][0, 2]) and np.isnan(got["bce"][1, 5])
 
 
+def test_minus_infinity_logits_count_as_zero_probability():
+    """Masked vocabulary entries (-inf in U or in t) are probability 0 on that
+    side and still enter |p_d - p_t|; a whole 256-row stretch of -inf leaves
+    some lanes with no finite row.  V a multiple of 8 (vector loads) and not."""
+    for V, seed in ((4096, 5), (3001, 6)):
+        x = _tiny(3, 8, V, seed=seed)
+        rng = np.random.default_rng(seed)
+        ninf = np.uint16(0xFF80)
+        y = x["y"]
+        y.reshape(24)[4] = 100  # outside the -inf stretch planted below
+        for arr in ("U", "t"):
+            a = x[arr].reshape(24, V)
+            hit = rng.random(a.shape) < 0.05
+            hit[np.arange(24), np.clip(y.reshape(24), 0, V - 1)] = False  # keep d[y] finite
+            a[hit] = ninf
+        x["U"].reshape(24, V)[4, 512:768] = ninf
+        x["t"].reshape(24, V)[9, 0:300] = ninf
+        got, ref = _gpu(x), _ref(x)
+        _check_positions(got, ref)
+        _check_loss(got, ref)
+        assert np.isfinite(got["l1"]).all()
+
+
 def test_all_masked_and_no_positions():
     x = _tiny(2, 4, 500, seed=2)
     got = _gpu(x, np.zeros((2, 4), np.float32))

@@ -194,13 +194,15 @@ __global__ __launch_bounds__(kCThreads) void accept_rate_cluster(int64_t N, int6
     auto load_row = [&](int64_t row) {
         const T* dr = d + row * ldd;
         const T* tr = t + row * ldt;
+        // lanes past the chunk re-read its last vector (never used; no chunk
+        // is empty): a load under a lane condition merges with the register's
+        // old value, and that merge waits for each load as it is issued
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-            const int64_t idx = v0 + tid + (int64_t)j * kCThreads;
-            if (idx < v1) {
-                rd[j] = *reinterpret_cast<const uint4*>(dr + idx * E);
-                rt[j] = *reinterpret_cast<const uint4*>(tr + idx * E);
-            }
+            int64_t idx = v0 + tid + (int64_t)j * kCThreads;
+            idx = idx < v1 ? idx : v1 - 1;
+            rd[j] = *reinterpret_cast<const uint4*>(dr + idx * E);
+            rt[j] = *reinterpret_cast<const uint4*>(tr + idx * E);
         }
     };
     // Rows after the first are claimed from a shared counter, so that clusters
@@ -418,10 +420,12 @@ ClusterPlan plan_cluster(int64_t N, int64_t V) {
     ClusterPlan p;
     constexpr int E = Vec<T>::N;
     const int64_t nvec = V / E;
+    if (nvec == 0) return p;  // rows shorter than one vector: the row kernel
     const int64_t per_wg = (int64_t)kCThreads * kCMaxVec;
-    int64_t C = nvec > 0 ? (nvec + per_wg - 1) / per_wg : 1;
+    const int64_t C = (nvec + per_wg - 1) / per_wg;
     if (C > kCMaxCluster) return p;
-    const int64_t vpc = nvec > 0 ? (nvec + C - 1) / C : 0;
+    // no chunk is empty: (C - 1) ceil(nvec / C) < nvec because C (C - 1) < nvec
+    const int64_t vpc = (nvec + C - 1) / C;
     const int nv = (int)((vpc + kCThreads - 1) / kCThreads);
     const void* fn = cluster_fn_nv<T>(nv < 1 ? 1 : nv);
     const int cus = device_cus_ar();

@@ -7,7 +7,10 @@
 //   d[p][v] = U[p][v] + W2[v] . W1[xp[p]]            (draft logits)
 // and the loss needs, per position, logsumexp(d), d[y], and
 // L1 = 1/2 sum_v |softmax(d)_v - softmax(t)_v|, which needs both row
-// normalisers before it can be summed.  Five launches:
+// normalisers before it can be summed.  Both distributions sum to one, so
+// L1 = 1 - sum_v min(p_v, q_v), and the min of two probabilities is the
+// exponential of the smaller exponent: one exponential per row instead of
+// two.  Five launches:
 //   loss_stream<1>  a workgroup takes a 256-row vocabulary chunk, holds
 //                   those W2 rows in registers as matrix-core A fragments and
 //                   streams up to 1024 positions through them, 32 at a time:
@@ -19,7 +22,7 @@
 //   loss_merge      per position: the chunk partials merged in a fixed order
 //                   into logsumexp(d) and logsumexp(t), and the confidence
 //                   logit w . [h; W1[xp]] + b;
-//   loss_stream<2>  the same stream again, summing |p_d - p_t| per chunk;
+//   loss_stream<2>  the same stream again, summing min(p_d, p_t) per chunk;
 //   loss_final      per position: L1, CE, c* = 1 - L1, conf, BCE and the
 //                   position's weighted terms;
 //   loss_reduce     one workgroup sums the terms over positions in a fixed
@@ -141,7 +144,7 @@ __device__ __forceinline__ void stage_block(const BlockRegs& r, uint16_t* E, uin
 // / G), cut into items of one chunk and at most kGroupPos positions.
 // PASS 1 writes the chunk's (max, sum) of d and t per position to stats
 // [M][chunks][4] and d[y] to dy [M]; PASS 2 reads lse [M][2] and writes the
-// chunk's sum of |p_d - p_t| to l1p [M][chunks].
+// chunk's sum of min(p_d, p_t) to l1p [M][chunks].
 template <int PASS, bool VEC>
 __global__ __launch_bounds__(kSThreads) void loss_stream(int64_t M, int64_t V, int64_t nchunk,
                                                          const bf16_t* __restrict__ U, const bf16_t* __restrict__ T,
@@ -261,11 +264,13 @@ __global__ __launch_bounds__(kSThreads) void loss_stream(int64_t M, int64_t V, i
                 merge_ms(mt, st, m3, s3);
                 o0 = md, o1 = sd, o2 = mt, o3 = st;
             } else {
-                // every row counts, a -inf logit as probability 0 (rows past V: 0 on both sides)
+                // sum of min(p_d, p_t): one exponential per row; a -inf logit is
+                // probability 0 (rows past V: 0 on both sides)
                 float sum = 0.f;
                 const float l0k = cur_l0 * kLog2e, l1k = cur_l1 * kLog2e;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sum += fabsf(exp_shift(d_at(r), l0k) - exp_shift(t_at(r), l1k));
+                for (int r = 0; r < 16; ++r)
+                    sum += __builtin_amdgcn_exp2f(fminf(fmaf(d_at(r), kLog2e, -l0k), fmaf(t_at(r), kLog2e, -l1k)));
                 o0 = sum + __shfl_xor(sum, 32);
             }
             if (half == 0) {
@@ -370,9 +375,11 @@ __global__ __launch_bounds__(256) void loss_final(int64_t M, int64_t gamma, int6
     if (x < 0 || x >= V || yy < 0 || yy >= V) {
         ce[p] = l1[p] = conf[p] = bce[p] = __builtin_nanf("");
     } else {
-        const float d1 = 0.5f * s;
+        // sum of min(p_d, p_t) = 1 - L1, kept in [0, 1] (rounding can put the
+        // sum a few 1e-7 past 1 when the distributions agree)
+        const float cstar = fminf(s, 1.f);
+        const float d1 = 1.f - cstar;
         const float c_ce = lse[2 * p] - dy[p];
-        const float cstar = 1.f - d1;
         const float z = zc[p];
         // -(c log sigmoid(z) + (1 - c) log(1 - sigmoid(z))) = softplus(z) - c z
         const float sp = fmaxf(z, 0.f) + log1pf(__expf(-fabsf(z)));

@@ -1726,24 +1726,29 @@ constexpr int kGRow = kMfmaRows + 4;   // LDS row stride of the G tile (fp32)
 
 // Hidden halves of the gated and RNN heads on the matrix cores (bf16):
 //   out_z[bk][j] = W_z[j, off : off + H] . h[bk, :]   for bk < M = B gamma, j < r
-// with z = blockIdx.z choosing (Wa, outa) or (Wb, outb); W rows have stride ld.
-// grid (r / 32, ceil(M / 32), 1 or 2), 512 threads: a workgroup owns a 32 x 32
-// output tile, its eight waves take interleaved runs of 16 k-steps (of 16
-// each; the loads of a run are all in flight at once), and the eight partial
-// tiles are summed in wave order (deterministic).  Requires r % 32 == 0,
-// H % 16 == 0, ld % 8 == 0, off % 8 == 0 and 16-byte aligned W and h.
+// with z choosing (Wa, outa) or (Wb, outb); W rows have stride ld.  grid
+// (r / 32, ceil(M / 32), (1 or 2) KS), 512 threads, blockIdx.z = z KS + ks: a
+// workgroup owns a 32 x 32 output tile and the ks-th of KS equal ranges of
+// the k-steps (of 16 each), its eight waves take interleaved runs of KU
+// k-steps (the loads of a run are all in flight at once), and the eight
+// partial tiles are summed in wave order (deterministic).  Range ks goes to
+// out_z + ks M r; the KS partials are summed by the consumer.  Requires
+// r % 32 == 0, H % 16 == 0, ld % 8 == 0, off % 8 == 0 and 16-byte aligned W
+// and h.
 constexpr int kHidWaves = 8;
+template <int KU>
 __global__ __launch_bounds__(64 * kHidWaves) void hidden_mfma(int64_t M, int64_t H, int64_t r, int64_t ld,
                                                               int64_t off, const bf16_t* __restrict__ h,
                                                               const bf16_t* __restrict__ Wa,
                                                               const bf16_t* __restrict__ Wb, float* __restrict__ outa,
-                                                              float* __restrict__ outb) {
+                                                              float* __restrict__ outb, int KS) {
     __shared__ float part[kHidWaves][16 * 64];
     // the wave index as a scalar: the k-step guards below are then uniform branches
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int row = lane & 31, half = lane >> 5;
-    const bf16_t* W = blockIdx.z ? Wb : Wa;
-    float* out = blockIdx.z ? outb : outa;
+    const int zm = (int)blockIdx.z / KS, ks = (int)blockIdx.z % KS;
+    const bf16_t* W = zm ? Wb : Wa;
+    float* out = (zm ? outb : outa) + (int64_t)ks * M * r;
     // Workgroups go round-robin over the 8 XCDs (each with its own L2); when
     // the tile count allows, XCD x takes the x-th eighth of the tiles in
     // row-major order, so it reads a few h rows and W once instead of all of h.
@@ -1753,12 +1758,13 @@ __global__ __launch_bounds__(64 * kHidWaves) void hidden_mfma(int64_t M, int64_t
     const int64_t mr = m0 + row < M ? m0 + row : M - 1;  // clamped rows are computed, never stored
     const uint4* ap = reinterpret_cast<const uint4*>(W + (j0 + row) * ld + off + half * 8);
     const uint4* bp = reinterpret_cast<const uint4*>(h + mr * H + half * 8);
-    const int steps = (int)(H / 16);
+    const int nsteps = (int)(H / 16);
+    const int s_lo = (int)((int64_t)nsteps * ks / KS), steps = (int)((int64_t)nsteps * (ks + 1) / KS);
     f32x16_t acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    constexpr int kU = 16;  // k-steps in flight per wave
-    int s0 = wave * kU;
+    constexpr int kU = KU;  // k-steps in flight per wave
+    int s0 = s_lo + wave * kU;
     for (; s0 + kU <= steps; s0 += kHidWaves * kU) {  // whole runs, no guards
         uint4 a[kU], b[kU];
 #pragma unroll
@@ -1788,6 +1794,14 @@ __global__ __launch_bounds__(64 * kHidWaves) void hidden_mfma(int64_t M, int64_t
         const int64_t m = m0 + (l & 31), j = j0 + 8 * (i >> 2) + 4 * (l >> 5) + (i & 3);
         if (m < M) out[m * r + j] = v;
     }
+}
+
+// split-K ranges of the resident path's hidden halves: about 64 k-steps each
+// (one run of 8 per wave), at most kHidMaxSplits
+constexpr int kHidMaxSplits = 8;
+int hidden_splits(int64_t H) {
+    (void)H;
+    return 1;  // several ranges measured no faster at B gamma = 448, H = 5120
 }
 
 bool hidden_mfma_ok(int64_t H, int64_t r, int64_t ld, int64_t off, const void* h, const void* W) {
@@ -2043,6 +2057,7 @@ constexpr int kResMaxReq = 64;
 constexpr int kResCopies = 8;   // copies of the winner words
 constexpr int kResMaxWGs = 256;
 constexpr size_t kResHeader = kWsHeader;  // words 0 (exit counter), 1 (status), 3 (paths)
+constexpr int kResMaxGamma = 8;  // block width of the gated and RNN heads in this kernel
 
 __device__ __forceinline__ int32_t winner_token(uint64_t key) {  // 0 or 1: no candidate
     return key <= 1 ? -1 : key_token(key);
@@ -2074,17 +2089,44 @@ __device__ __forceinline__ void read_gumbel_unit(uint32_t lds_addr, const u32x2_
         : "v"(lds_addr), "v"(dep[0]), "v"(dep[1]), "v"(dep[2]), "v"(dep[3]));
 }
 
-template <int NT, bool HG>
+// HD: the sequential head.  0: the Markov head (E = W1[x_{k-1}]).  1: the
+// gated head and 2: the RNN head, whose binary32 embedding enters the
+// products as hi and lo bf16 halves (see sample_step_mfma).  With HD != 0,
+// workgroup g < r computes column j = g of every request's embedding per
+// step and posts it as tagged words; every workgroup then reads all columns
+// back.  Wh, Wh2: Wg, or Wrg and Wrc; hid: their hidden halves as hks
+// split-K partials of [B][gamma][r] each (Wrg's, then Wrc's for the RNN
+// head); ebw: the posted columns, two step slots of [64][r] words.  HD != 0
+// needs NT == 2, at least r workgroups and gamma <= kResMaxGamma.
+template <int NT, bool HG, int HD>
 __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, int gamma, int64_t V, int tiles_per_wg, const bf16_t* __restrict__ U,
                       const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W2, const bf16_t* __restrict__ h,
                       const bf16_t* __restrict__ w_conf, int64_t H, float b_conf, const int32_t* __restrict__ x0,
                       const float* __restrict__ G, const int32_t* __restrict__ force, int32_t* __restrict__ tokens,
                       float* __restrict__ conf, float* __restrict__ survival, uint64_t* hword, uint64_t* pub,
-                      uint64_t* win, uint32_t* header, int spin_limit) {
+                      uint64_t* win, uint32_t* header, int spin_limit, const bf16_t* __restrict__ Wh,
+                      const bf16_t* __restrict__ Wh2, float* __restrict__ hid, int hks, uint64_t* ebw) {
     constexpr int NREQ = 32 * NT;
-    __shared__ __align__(16) uint16_t E_lds[NREQ * kERow];
+    constexpr bool EG = HD != 0;
+    static_assert(!EG || NT == 2, "the gated and RNN heads run with two request blocks");
+    // the hi and lo halves need a second E; with Gumbel noise that space
+    // comes from a single Gumbel slot per wave
+    constexpr int kGSlots = (EG && HG) ? 1 : 2;
+    __shared__ __align__(16) uint16_t E_lds[NREQ * kERow * (EG ? 2 : 1)];
+    uint16_t* const El_lds = E_lds + (EG ? NREQ * kERow : 0);  // EG: the lo halves
     __shared__ __align__(16) uint16_t T_lds[kResLdsTiles * 32 * kERow];  // W2 tiles held in LDS
-    __shared__ __align__(16) float G_lds[kResWaves][2][32 * 32];  // per wave: two Gumbel units in flight
+    __shared__ __align__(16) float G_lds[kResWaves][kGSlots][32 * 32];  // per wave: Gumbel units in flight
+    // EG: this workgroup's row of the head weights as bf16 pairs (gated: the
+    // embedding half of Wg; RNN: the state and embedding halves of Wrg, then
+    // of Wrc), and for the RNN head its column of the state and the state
+    // halves of the next step's two products
+    constexpr int kHWords = HD == 2 ? 2 * kMfmaRank : (HD == 1 ? kMfmaRank / 2 : 1);
+    __shared__ uint32_t hrow[kHWords];
+    __shared__ float zs_lds[2][HD == 2 ? NREQ : 1];
+    __shared__ float s_lds[HD == 2 ? NREQ : 1];
+    // EG: the hidden halves of column g for every request and step (gated:
+    // Wg's; RNN: Wrg's then Wrc's), read once at the start
+    __shared__ float hcol[EG ? HD * kResMaxReq * kResMaxGamma : 1];
     __shared__ uint64_t wkey[kResWaves][NREQ];
     __shared__ uint64_t rkey[kResWaves];
     __shared__ int rlost[kResWaves];
@@ -2126,6 +2168,30 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
 
     if (g == 0 && tid < kMfmaRank / 2)
         we_lds[tid] = (uint32_t)w_conf[H + 2 * tid].bits | ((uint32_t)w_conf[H + 2 * tid + 1].bits << 16);
+    if constexpr (HD == 1) {
+        if (g < kMfmaRank && tid < kMfmaRank / 2) {
+            const bf16_t* wr = Wh + (int64_t)g * (H + kMfmaRank) + H + 2 * tid;
+            hrow[tid] = (uint32_t)wr[0].bits | ((uint32_t)wr[1].bits << 16);
+        }
+    }
+    if constexpr (HD == 2) {
+        if (g < kMfmaRank) {  // kResThreads == 2 r: one pair per thread
+            const bf16_t* wr = (tid < kMfmaRank ? Wh : Wh2) + (int64_t)g * (2 * kMfmaRank + H) + 2 * (tid % kMfmaRank);
+            hrow[tid] = (uint32_t)wr[0].bits | ((uint32_t)wr[1].bits << 16);
+        }
+        if (tid < NREQ) zs_lds[0][tid] = zs_lds[1][tid] = s_lds[tid] = 0.f;  // s_0 = 0
+    }
+    if constexpr (EG) {
+        if (g < kMfmaRank) {
+            const int64_t mr = B * gamma * kMfmaRank;
+            for (int i = tid; i < HD * B * gamma; i += kResThreads) {  // i = (m B + b) gamma + k
+                const int64_t m = i / (B * gamma), bk = i % (B * gamma);
+                float v = 0.f;
+                for (int ks = 0; ks < hks; ++ks) v += hid[(m * hks + ks) * mr + bk * kMfmaRank + g];
+                hcol[i] = v;
+            }
+        }
+    }
     // a wave's work per step is a list of units (tile i, 32-request block nt),
     // unit p = i * NT + nt; the tiles it holds form a prefix of register
     // tile 0, register tile 1, LDS tile
@@ -2168,7 +2234,7 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
         if constexpr (HG) {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(g_rsrc, (lds_void_t*)&G_lds[wv][slot][c * 256], 16,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(g_rsrc, (lds_void_t*)&G_lds[wv][kGSlots == 1 ? 0 : slot][c * 256], 16,
                                                          (uint32_t)(base + v[c]) * 4u, 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);  // U strictly after this unit's Gumbel loads
@@ -2177,7 +2243,7 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
         __builtin_amdgcn_sched_barrier(0);
     };
     issue(0, 0 < n_units ? 0 : -1, 0);
-    issue(1, 1 < n_units ? 1 : -1, 0);
+    if constexpr (kGSlots == 2) issue(1, 1 < n_units ? 1 : -1, 0);
 
     // the hidden part of every confidence logit, w_h . h[b, k]: pair
     // p = b gamma + k goes to wave p of the grid and is posted as a tagged
@@ -2213,6 +2279,7 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
 
     float A = 1.f;  // workgroup 0, thread 4 b: running survival of request b
     for (int k = 0; k < gamma; ++k) {
+
         // previous tokens: the anchors, then the winners of the last step
         if (tid < NREQ) {
             int64_t x = -1;
@@ -2281,8 +2348,125 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
             }
         }
 
+        if constexpr (EG) {
+            // the head's embedding.  Column j = g of every request, from the
+            // bf16 rows e = W1[x_{k-1}] in E (8 threads per request, 32 rank
+            // elements each), posted as a word tagged with the step
+            const int bl = tid >> 3, part = tid & 7;
+            if (g < kMfmaRank) {
+                const uint32_t* er = reinterpret_cast<const uint32_t*>(E_lds + bl * kERow + part * 32);
+                float d1 = 0.f, d2 = 0.f;  // embedding halves of the products with this row
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const uint32_t ev = er[q];
+                    if constexpr (HD == 1) {
+                        d1 = dot2(hrow[part * 16 + q], ev, d1);
+                    } else {
+                        d1 = dot2(hrow[kMfmaRank / 2 + part * 16 + q], ev, d1);
+                        d2 = dot2(hrow[kMfmaRank + kMfmaRank / 2 + part * 16 + q], ev, d2);
+                    }
+                }
+                d1 += __shfl_xor(d1, 1);
+                d1 += __shfl_xor(d1, 2);
+                d1 += __shfl_xor(d1, 4);
+                if constexpr (HD == 2) {
+                    d2 += __shfl_xor(d2, 1);
+                    d2 += __shfl_xor(d2, 2);
+                    d2 += __shfl_xor(d2, 4);
+                }
+                if (part == 0) {  // requests past B: any finite column
+                    const int64_t bk = (int64_t)(bl < B ? bl : B - 1) * gamma + k;
+                    const float hg = hcol[bk];
+                    float val;
+                    if constexpr (HD == 1) {
+                        // eb_j = e_j sigmoid(Wg[j] . [h_k; e])
+                        const float ej = __uint_as_float((uint32_t)E_lds[bl * kERow + g] << 16);
+                        val = ej / (1.f + expf(-(hg + d1)));
+                    } else {
+                        // s_k[j] = u s_{k-1}[j] + (1 - u) tanh(Wrc[j] . z), u = sigmoid(Wrg[j] . z)
+                        const float zg = hg + zs_lds[0][bl] + d1;
+                        const float zc = hcol[B * gamma + bk] + zs_lds[1][bl] + d2;
+                        const float u = 1.f / (1.f + expf(-zg));
+                        val = u * s_lds[bl] + (1.f - u) * tanhf(zc);
+                        s_lds[bl] = val;
+                    }
+                    __hip_atomic_store(ebw + ((int64_t)(k & 1) * kResMaxReq + bl) * kMfmaRank + g,
+                                       ((uint64_t)(k + 1) << 32) | __float_as_uint(val), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+            __syncthreads();  // E's bf16 rows are read: their space takes the hi halves
+            // every column comes back as the hi and lo bf16 halves of E: wave w
+            // reads requests 8 w .. 8 w + 7, lane l columns 2 l, 2 l + 1 and
+            // 128 + 2 l, 129 + 2 l of each (consecutive lanes, consecutive
+            // words), in two runs of four requests with all their loads in
+            // flight.  The RNN head also forms the state halves of the next
+            // step's two products, one wave sum per request.
+            {
+                const uint64_t* src = ebw + (int64_t)(k & 1) * kResMaxReq * kMfmaRank;
+                const uint32_t want = (uint32_t)(k + 1);
+                const int wvr = __builtin_amdgcn_readfirstlane(wave);
+                bool all = true;
+#pragma unroll
+                for (int run = 0; run < 2; ++run) {
+                    uint64_t w[16];  // request q of the run, column c: w[4 q + c]
+                    auto addr = [&](int i) {
+                        const int q = i >> 2, c = i & 3;
+                        const int col = (c < 2 ? 0 : kMfmaRank / 2) + 2 * lane + (c & 1);
+                        return src + (int64_t)(wvr * 8 + run * 4 + q) * kMfmaRank + col;
+                    };
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) w[i] = __hip_atomic_load(addr(i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    bool ok = true;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) ok = ok && (uint32_t)(w[i] >> 32) == want;
+                    for (int spin = 0; !__all(ok) && spin < spin_limit; ++spin) {
+                        __builtin_amdgcn_s_sleep(1);
+                        ok = true;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            if ((uint32_t)(w[i] >> 32) != want)
+                                w[i] = __hip_atomic_load(addr(i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            ok = ok && (uint32_t)(w[i] >> 32) == want;
+                        }
+                    }
+                    all = all && __all(ok);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int bq = wvr * 8 + run * 4 + q;
+                        float zg = 0.f, zc = 0.f;
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) {  // columns 2 l (+ 128), and the next
+                            const float f0 = __uint_as_float((uint32_t)w[4 * q + 2 * hh]);
+                            const float f1 = __uint_as_float((uint32_t)w[4 * q + 2 * hh + 1]);
+                            const uint32_t h0 = bf16_rne(f0), h1 = bf16_rne(f1);
+                            const uint32_t l0 = bf16_rne(f0 - __uint_as_float(h0 << 16));
+                            const uint32_t l1 = bf16_rne(f1 - __uint_as_float(h1 << 16));
+                            const int o = bq * kERow + hh * (kMfmaRank / 2) + 2 * lane;
+                            *reinterpret_cast<uint32_t*>(E_lds + o) = (h0 & 0xffffu) | (h1 << 16);
+                            *reinterpret_cast<uint32_t*>(El_lds + o) = (l0 & 0xffffu) | (l1 << 16);
+                            if constexpr (HD == 2) {
+                                const int pr = hh * (kMfmaRank / 4) + lane;  // state-half pair of Wrg / Wrc
+                                zg = __builtin_fmaf(widen_hi(hrow[pr]), f1, __builtin_fmaf(widen_lo(hrow[pr]), f0, zg));
+                                zc = __builtin_fmaf(widen_hi(hrow[kMfmaRank + pr]), f1,
+                                                    __builtin_fmaf(widen_lo(hrow[kMfmaRank + pr]), f0, zc));
+                            }
+                        }
+                        if constexpr (HD == 2) {
+                            zg = wave_sum_f32(zg);
+                            zc = wave_sum_f32(zc);
+                            if (lane == 0) zs_lds[0][bq] = zg, zs_lds[1][bq] = zc;
+                        }
+                    }
+                }
+                if (!all && lane == 0) mark_gave_up(header);  // a column never came: the step's tokens are unspecified
+            }
+            __syncthreads();
+        }
+
         // the products, the + U (+ G) epilogue and the in-lane argmax, one unit
         // at a time with the U and Gumbel loads of the unit after next in flight
+        // (with one Gumbel slot, of the next unit)
         uint64_t key[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) key[nt] = 0;
@@ -2303,13 +2487,24 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
                 const uint4 bw = *reinterpret_cast<const uint4*>(E_lds + (nt * 32 + row) * kERow + s * 16 + half * 8);
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aw),
                                                               __builtin_bit_cast(bf16x8_t, bw), acc, 0, 0, 0);
+                if constexpr (EG) {
+                    const uint4 bw2 = *reinterpret_cast<const uint4*>(El_lds + (nt * 32 + row) * kERow + s * 16 + half * 8);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aw),
+                                                                  __builtin_bit_cast(bf16x8_t, bw2), acc, 0, 0, 0);
+                }
             }
             f32x4_t gr[4];
             if constexpr (HG) {
-                const uint32_t ga = (uint32_t)(uintptr_t)(lds_void_t*)&G_lds[wv][p & 1][lane * 4];
+                const uint32_t ga = (uint32_t)(uintptr_t)(lds_void_t*)&G_lds[wv][kGSlots == 1 ? 0 : (p & 1)][lane * 4];
                 __builtin_amdgcn_sched_barrier(0);
                 read_gumbel_unit(ga, ur[p & 1], gr);
                 __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (kGSlots == 1) {
+                // the one Gumbel slot is free: the next unit's loads (after the
+                // last unit, the next step's first; the unit count is even)
+                const bool last = p + 1 >= n_units;
+                issue((p + 1) & 1, last ? (k + 1 < gamma ? 0 : -1) : p + 1, last ? k + 1 : k);
             }
             const int bl = nt * 32 + row;
             if (bl < B && xprev[bl] >= 0) {
@@ -2351,10 +2546,10 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
                     }
                 }
             }
-            issue(p & 1, p + 2 < n_units ? p + 2 : -1, k);
+            if constexpr (kGSlots == 2) issue(p & 1, p + 2 < n_units ? p + 2 : -1, k);
         }
         // the first two units of the next step need nothing from this one
-        if (k + 1 < gamma) {
+        if (kGSlots == 2 && k + 1 < gamma) {
             issue(0, 0 < n_units ? 0 : -1, k + 1);
             issue(1, 1 < n_units ? 1 : -1, k + 1);
         }
@@ -2424,6 +2619,11 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
                                __HIP_MEMORY_SCOPE_AGENT);
         for (int64_t i = tid; i < B * gamma; i += kResThreads)
             __hip_atomic_store(hword + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (EG) {  // both step slots of the posted columns, and the hidden halves
+            for (int i = tid; i < 2 * kResMaxReq * kMfmaRank; i += kResThreads)
+                __hip_atomic_store(ebw + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int64_t i = tid; i < HD * hks * B * gamma * kMfmaRank; i += kResThreads) hid[i] = 0.f;
+        }
         if (tid == 0) __hip_atomic_store(&header[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -2432,7 +2632,7 @@ struct ResidentPlan {
     int nwg = 0, tiles_per_wg = 0;
 };
 
-ResidentPlan resident_plan(int64_t B, int64_t V) {
+ResidentPlan resident_plan(int64_t B, int64_t V, int hd = 0) {
     ResidentPlan p;
     const int cus = device_cus();
     if (cus <= 0 || B < kMfmaMinBatch || B > kResMaxReq || V % 4 != 0) return p;
@@ -2443,8 +2643,10 @@ ResidentPlan resident_plan(int64_t B, int64_t V) {
     if (per > (int64_t)kResMaxTiles) return p;
     int per_cu = 0;
     // the Gumbel variants use the most LDS and registers
-    const void* fn = B <= 32 ? reinterpret_cast<const void*>(&sample_batch_resident<1, true>)
-                             : reinterpret_cast<const void*>(&sample_batch_resident<2, true>);
+    const void* fn = hd == 1   ? reinterpret_cast<const void*>(&sample_batch_resident<2, true, 1>)
+                     : hd == 2 ? reinterpret_cast<const void*>(&sample_batch_resident<2, true, 2>)
+                     : B <= 32 ? reinterpret_cast<const void*>(&sample_batch_resident<1, true, 0>)
+                               : reinterpret_cast<const void*>(&sample_batch_resident<2, true, 0>);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kResThreads, 0) != hipSuccess || per_cu < 1)
         return p;
     p.nwg = (int)nwg;
@@ -2455,6 +2657,14 @@ ResidentPlan resident_plan(int64_t B, int64_t V) {
 size_t resident_workspace(int64_t B, int64_t gamma) {
     return kResHeader + ((size_t)(8 * B * gamma) + 255) / 256 * 256 +
            (size_t)8 * gamma * kResMaxWGs * kResMaxReq + (size_t)8 * gamma * kResCopies * kResMaxReq;
+}
+
+// the gated (hd 1) or RNN (hd 2) head in the resident kernel: its hidden
+// halves ([B][gamma][r] floats, two sets for the RNN head) and the posted
+// columns (two step slots of [64][r] words) follow the resident words
+size_t resident_head_workspace(int64_t B, int64_t gamma, int hd) {
+    return resident_workspace(B, gamma) + ((size_t)(4 * hd * kHidMaxSplits * B * gamma * kMfmaRank) + 255) / 256 * 256 +
+           (size_t)8 * 2 * kResMaxReq * kMfmaRank;
 }
 
 struct Buffers {
@@ -2517,8 +2727,17 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
         mfma = r == kMfmaRank && B >= kMfmaMinBatch && ((uintptr_t)W1 % 16 == 0) && ((uintptr_t)W2 % 16 == 0) &&
                (!headed || (uintptr_t)ws % 16 == 0);
     if constexpr (std::is_same_v<T, bf16_t>) {
-        // resident W2 (the plain Markov head only): one persistent kernel for the whole block
-        const ResidentPlan rp = (mfma && !headed) ? resident_plan(B, V) : ResidentPlan{};
+        // resident W2: one persistent kernel for the whole block.  The gated
+        // and RNN heads qualify too with two request blocks (B > 32), their
+        // hidden halves on the matrix cores, and a workgroup per rank column
+        const int hd = Wrg != nullptr ? 2 : (Wg != nullptr ? 1 : 0);
+        bool res_ok = mfma;
+        if (hd == 1) res_ok = res_ok && B > 32 && gamma <= kResMaxGamma && hidden_mfma_ok(H, r, H + r, 0, h, Wg);
+        if (hd == 2)
+            res_ok = res_ok && B > 32 && gamma <= kResMaxGamma && hidden_mfma_ok(H, r, 2 * r + H, 2 * r, h, Wrg) &&
+                     (uintptr_t)Wrc % 16 == 0;
+        ResidentPlan rp = res_ok ? resident_plan(B, V, hd) : ResidentPlan{};
+        if (hd != 0 && rp.nwg < kMfmaRank) rp.nwg = 0;
         // (stored logits or bias go to the general kernel: any store in the
         // resident kernel's tile loop makes its loads wait for one another)
         if (rp.nwg > 0 && lo == nullptr && bo == nullptr && (uintptr_t)U % 8 == 0 &&
@@ -2530,16 +2749,45 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
             p += ((size_t)(8 * B * gamma) + 255) / 256 * 256;
             uint64_t* pub = reinterpret_cast<uint64_t*>(p);
             uint64_t* win = pub + (size_t)gamma * kResMaxWGs * kResMaxReq;
+            float* hid = nullptr;
+            uint64_t* ebw = nullptr;
+            if (hd != 0) {
+                char* q = static_cast<char*>(ws) + resident_workspace(B, gamma);
+                hid = reinterpret_cast<float*>(q);
+                ebw = reinterpret_cast<uint64_t*>(q + ((size_t)(4 * hd * kHidMaxSplits * B * gamma * kMfmaRank) + 255) /
+                                                          256 * 256);
+                const int64_t M = B * gamma;
+                const int ks = hidden_splits(H);
+                const dim3 grid((uint32_t)(r / 32), (uint32_t)((M + 31) / 32), (uint32_t)(hd * ks));
+                hipLaunchKernelGGL(hidden_mfma<16>, grid, dim3(64 * kHidWaves), 0, stream, M, H, r,
+                                   hd == 2 ? 2 * r + H : H + r, hd == 2 ? 2 * r : (int64_t)0,
+                                   static_cast<const bf16_t*>(h), static_cast<const bf16_t*>(hd == 2 ? Wrg : Wg),
+                                   static_cast<const bf16_t*>(Wrc), hid, hid + ks * M * r, ks);
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+            }
             int lim = wait_limit(kChainSpinLimit);
+            int hks = hidden_splits(H);
             const T* ht = static_cast<const T*>(h);
+            const bf16_t* Wh = static_cast<const bf16_t*>(hd == 2 ? Wrg : Wg);
+            const bf16_t* Wh2 = static_cast<const bf16_t*>(Wrc);
             int g = (int)gamma, tpw = rp.tiles_per_wg;
             int64_t Bb = B, Vv = V, Hh = H;
-            void* args[] = {&Bb, &g,     &Vv,    &tpw,    &Ut,   &W1t,      &W2t,   &ht,  &wt,  &Hh,    &b_conf,
-                            &x0, &G,     &force, &tokens, &conf, &survival, &hword, &pub, &win, &header, &lim};
-            const void* fn = G ? (B <= 32 ? reinterpret_cast<const void*>(&sample_batch_resident<1, true>)
-                                          : reinterpret_cast<const void*>(&sample_batch_resident<2, true>))
-                               : (B <= 32 ? reinterpret_cast<const void*>(&sample_batch_resident<1, false>)
-                                          : reinterpret_cast<const void*>(&sample_batch_resident<2, false>));
+            void* args[] = {&Bb, &g,     &Vv,    &tpw,    &Ut,   &W1t,      &W2t,   &ht,  &wt,  &Hh,     &b_conf, &x0,
+                            &G,  &force, &tokens, &conf, &survival, &hword, &pub, &win, &header, &lim, &Wh, &Wh2,
+                            &hid, &hks, &ebw};
+            const void* fn;
+            if (hd == 1)
+                fn = G ? reinterpret_cast<const void*>(&sample_batch_resident<2, true, 1>)
+                       : reinterpret_cast<const void*>(&sample_batch_resident<2, false, 1>);
+            else if (hd == 2)
+                fn = G ? reinterpret_cast<const void*>(&sample_batch_resident<2, true, 2>)
+                       : reinterpret_cast<const void*>(&sample_batch_resident<2, false, 2>);
+            else
+                fn = G ? (B <= 32 ? reinterpret_cast<const void*>(&sample_batch_resident<1, true, 0>)
+                                  : reinterpret_cast<const void*>(&sample_batch_resident<2, true, 0>))
+                       : (B <= 32 ? reinterpret_cast<const void*>(&sample_batch_resident<1, false, 0>)
+                                  : reinterpret_cast<const void*>(&sample_batch_resident<2, false, 0>));
             // a plain launch: one workgroup per CU at most, all resident together;
             // the bounded spins turn any other outcome into an error, not a hang
             return hipLaunchKernel(fn, dim3(rp.nwg), dim3(kResThreads), args, 0, stream);
@@ -2573,10 +2821,10 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
         if (hmfma) {
             const int64_t M = B * gamma;
             const dim3 grid((uint32_t)(r / 32), (uint32_t)((M + 31) / 32), rnn ? 2u : 1u);
-            hipLaunchKernelGGL(hidden_mfma, grid, dim3(64 * kHidWaves), 0, stream, M, H, r, rnn ? 2 * r + H : H + r,
-                               rnn ? 2 * r : (int64_t)0, static_cast<const bf16_t*>(h),
+            hipLaunchKernelGGL(hidden_mfma<16>, grid, dim3(64 * kHidWaves), 0, stream, M, H, r,
+                               rnn ? 2 * r + H : H + r, rnn ? 2 * r : (int64_t)0, static_cast<const bf16_t*>(h),
                                static_cast<const bf16_t*>(rnn ? Wrg : Wg), static_cast<const bf16_t*>(Wrc), gate_ws,
-                               gate_ws + B * gamma * r);
+                               gate_ws + B * gamma * r, 1);
             if ((err = hipGetLastError()) != hipSuccess) return err;
         }
     }
@@ -2710,11 +2958,21 @@ size_t headed_workspace(int64_t B, int64_t gamma, int64_t r, int dtype, int64_t 
 }
 
 size_t head_sample_gated_workspace(int64_t B, int64_t gamma, int64_t r, int dtype) {
-    return headed_workspace(B, gamma, r, dtype, (gamma + 1) * r);
+    size_t w = headed_workspace(B, gamma, r, dtype, (gamma + 1) * r);
+    if (dtype == kBF16 && r == kMfmaRank && B > 32 && B <= kResMaxReq && gamma <= kResMaxGamma) {
+        const size_t res = resident_head_workspace(B, gamma, 1);
+        if (res > w) w = res;
+    }
+    return w;
 }
 
 size_t head_sample_rnn_workspace(int64_t B, int64_t gamma, int64_t r, int dtype) {
-    return headed_workspace(B, gamma, r, dtype, (2 * gamma + 2) * r);
+    size_t w = headed_workspace(B, gamma, r, dtype, (2 * gamma + 2) * r);
+    if (dtype == kBF16 && r == kMfmaRank && B > 32 && B <= kResMaxReq && gamma <= kResMaxGamma) {
+        const size_t res = resident_head_workspace(B, gamma, 2);
+        if (res > w) w = res;
+    }
+    return w;
 }
 
 hipError_t head_sample_launch(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int dtype, const void* U,

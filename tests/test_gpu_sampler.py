@@ -333,6 +333,34 @@ def test_gated_head_leaves_workspace_zero():
     assert torch.equal(a["tokens"], b["tokens"]) and torch.equal(a["conf"], b["conf"])
 
 
+@pytest.mark.parametrize("head", ["gated", "rnn"])
+@pytest.mark.parametrize("gumbel", [False, True])
+def test_gated_and_rnn_heads_on_the_resident_kernel(head, gumbel):
+    """B=40 (two 32-request blocks) at V=30000, rank 256, bf16: the gated and
+    RNN heads run in the resident-W2 kernel, where each workgroup forms one
+    column of the head's embedding per step and reads the others back; every
+    request checked, the path flag and a zero workspace verified."""
+    s = synth.SamplerShape(B=40, gamma=5, V=30000, H=256, r=256, dtype="bf16", w_sd=0.3, U_sd=1.0, wc_sd=0.02,
+                           gumbel=gumbel, seed=synth.SEED_BASE + 180 + int(gumbel) + (2 if head == "rnn" else 0))
+    w = synth.sampler_weights(s)
+    if head == "gated":
+        w["Wg"] = synth.gate_weights(s, 1.0 / np.sqrt(512))
+        n = dh.lib().dspark_head_sample_gated_workspace_size(40, 5, 30000, 256, 256, 1)
+    else:
+        w["Wr"] = synth.rnn_weights(s, 1.0 / np.sqrt(768))
+        n = dh.lib().dspark_head_sample_rnn_workspace_size(40, 5, 30000, 256, 256, 1)
+    x = synth.sampler_batch(s)
+    if not gumbel:
+        x.pop("G", None)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    sampler_parity(x, w, workspace=ws)
+    st, paths = dh.workspace_status(ws)
+    assert st == 0
+    if torch.cuda.get_device_properties(0).multi_processor_count >= 256:  # a workgroup per rank column
+        assert paths & dh.PATH_RESIDENT
+    assert workspace_dirty_bytes(ws) == 0
+
+
 @pytest.mark.parametrize("gumbel", [False, True])
 def test_rnn_head_tiny(gumbel):
     """RNN head on the tiny fp32 workload (general path), stored logits and

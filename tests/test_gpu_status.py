@@ -35,12 +35,14 @@ def _sampler_case(B, gamma, V, gumbel, seed):
     return s, args
 
 
-def _fresh_then_give_up_then_recover(s, args, expect_paths):
-    ws = torch.zeros(dh.head_sample_workspace_size(s.B, s.gamma, s.V, 64, 256), dtype=torch.uint8, device="cuda")
-    good = dh.head_sample(*args)  # a workspace of its own
+def _fresh_then_give_up_then_recover(s, args, expect_paths, ws_bytes=None, **head):
+    if ws_bytes is None:
+        ws_bytes = dh.head_sample_workspace_size(s.B, s.gamma, s.V, 64, 256)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    good = dh.head_sample(*args, **head)  # a workspace of its own
     prev = dh.set_wait_limit(0)
     try:
-        bad = dh.head_sample(*args, workspace=ws)
+        bad = dh.head_sample(*args, workspace=ws, **head)
         st, paths = dh.workspace_status(ws)
     finally:
         dh.set_wait_limit(prev)
@@ -49,7 +51,7 @@ def _fresh_then_give_up_then_recover(s, args, expect_paths):
     assert torch.all(bad["tokens"] == -1)
     assert torch.all(torch.isnan(bad["conf"])) and torch.all(torch.isnan(bad["survival"]))
     ws.zero_()  # the documented recovery
-    again = dh.head_sample(*args, workspace=ws)
+    again = dh.head_sample(*args, workspace=ws, **head)
     assert dh.workspace_status(ws)[0] == 0
     for k in good:
         assert torch.equal(good[k].view(torch.int32) if good[k].dtype == torch.float32 else good[k],
@@ -75,6 +77,21 @@ def test_batched_resident_gives_up():
     """B=64, bf16, rank 256: the resident-W2 kernel's per-step exchange."""
     s, args = _sampler_case(64, 4, 20000, True, 903)
     _fresh_then_give_up_then_recover(s, args, dh.PATH_RESIDENT)
+
+
+@pytest.mark.parametrize("head", ["gated", "rnn"])
+def test_batched_resident_gated_and_rnn_heads_give_up(head):
+    """B=64, bf16, rank 256 with a gated or RNN head: the resident kernel's
+    exchange of the head's embedding columns gives up too."""
+    s, args = _sampler_case(64, 3, 20000, True, 905)
+    if head == "gated":
+        extra = {"Wg": dev(synth.gate_weights(s, 0.05))}
+        n = dh.lib().dspark_head_sample_gated_workspace_size(64, 3, 20000, 64, 256, 1)
+    else:
+        extra = {"Wr": tuple(dev(a) for a in synth.rnn_weights(s, 0.05))}
+        n = dh.lib().dspark_head_sample_rnn_workspace_size(64, 3, 20000, 64, 256, 1)
+    paths = dh.PATH_RESIDENT if torch.cuda.get_device_properties(0).multi_processor_count >= 256 else 0
+    _fresh_then_give_up_then_recover(s, args, paths, ws_bytes=n, **extra)
 
 
 def test_accept_rate_cluster_gives_up(no_waits):

@@ -438,42 +438,13 @@ def main():
                            "table; 'tokens': SPS(n) = n/(2+0.004n) as stated, 'steps': SPS(n) = 1/(2+0.004n)",
                "bound": "latency (one workgroup)"}
         for kind in ("tokens", "steps"):
-            conf5 = to_dev(synth.schedule_conf(s5), dev)
-            sps5 = to_dev(synth.sps_table(s5.n_sps, kind), dev)
-            c5, o5 = dh.prepare_prefix_schedule(conf5, sps5)
+            c5, o5 = dh.prepare_prefix_schedule(to_dev(synth.schedule_conf(s5), dev),
+                                                to_dev(synth.sps_table(s5.n_sps, kind), dev), want_order=False)
             for _ in range(5):
                 c5()
             torch.cuda.synchronize()
             sch[f"{kind}_us_per_call"] = round(timed(c5, 100), 2)
             sch[f"{kind}_n_selected"] = int(o5["n_selected"].item())
-            # the same calls replayed from a HIP graph: device time per call
-            # without the host's launch cost, which the line above includes
-            # (the kernel is shorter than a Python-level launch)
-            gs = torch.cuda.Stream(dev)
-            gs.wait_stream(torch.cuda.current_stream(dev))
-            with torch.cuda.stream(gs):
-                cg, og = dh.prepare_prefix_schedule(conf5, sps5)
-                cg()
-            gs.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph, stream=gs):
-                for _ in range(20):
-                    cg()
-            for key in ("prefix_len", "order", "n_selected"):
-                og[key].fill_(-7)
-            og["theta"].fill_(-7.0)
-            for _ in range(2):
-                graph.replay()
-            torch.cuda.synchronize()
-            same = all(torch.equal(og[key], o5[key]) for key in ("prefix_len", "order", "theta", "n_selected"))
-            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            g0.record(gs)
-            for _ in range(10):
-                graph.replay()
-            g1.record(gs)
-            torch.cuda.synchronize()
-            sch[f"{kind}_graph_us_per_call"] = round(g0.elapsed_time(g1) * 1e3 / 200, 2)
-            sch[f"{kind}_graph_matches_eager"] = bool(same)
         line["schedule"] = sch
 
     # ---------------- teacher-forced block bias with the joint loss ----------------

@@ -137,7 +137,6 @@ def main():
     ap.add_argument("--no-accept", action="store_true", help="skip the accept-rate measurement")
     ap.add_argument("--no-verify", action="store_true", help="skip the rejection-sampling verify measurement")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timings")
-    ap.add_argument("--extra", action="store_true", help="(accepted for compatibility: every leg runs by default)")
     ap.add_argument("--calib-copy", action="store_true", help="run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -312,7 +311,8 @@ def main():
             "us_per_call": round(us_s, 3), "positions_per_s": round(s.gamma / (us_s * 1e-6), 1),
             "give_up": st_s, "path_flags": paths_s,
             "roofline": hbm_roofline("dspark_head_sample (persistent kernel, per-step exchange)", call_bytes, us_s,
-                                     None, None, timed_cold(lambda: scalls[0](), 20) if scrub is not None else None),
+                                     "head_sample_chain_b1_strong_bias_vocab151936.md", SAMPLER_SOURCES,
+                                     timed_cold(lambda: scalls[0](), 20) if scrub is not None else None),
         }
         del Ws
 

@@ -17,11 +17,11 @@
 //                   d on the matrix cores (bf16 in, fp32 accumulate), the U
 //                   and t tiles and the embeddings W1[xp] staged through LDS
 //                   with two blocks of loads in flight in registers; per
-//                   position and chunk it writes (max, sum) of d and t, and
-//                   the chunk holding y writes d[y];
+//                   position and chunk it writes (max, sum) of d and t;
 //   loss_merge      per position: the chunk partials merged in a fixed order
-//                   into logsumexp(d) and logsumexp(t), and the confidence
-//                   logit w . [h; W1[xp]] + b;
+//                   into logsumexp(d) and logsumexp(t), the target's logit
+//                   d[y] = U[y] + W2[y] . W1[xp], and the confidence logit
+//                   w . [h; W1[xp]] + b;
 //   loss_stream<2>  the same stream again, summing min(p_d, p_t) per chunk;
 //   loss_final      per position: L1, CE, c* = 1 - L1, conf, BCE and the
 //                   position's weighted terms;
@@ -76,14 +76,13 @@ __device__ __forceinline__ void merge_ms(float& m, float& s, float mb, float sb)
 struct BlockRegs {
     u32x4_t u[2], t[2], e[2];
     float l0, l1;  // pass 2: logsumexp of d and t of the lane's position (lane % 32)
-    int32_t yy;    // pass 1: the lane's position's target id
 };
 
-// The item's previous tokens (and targets or normalisers) sit in LDS, so no
-// load here waits for another load.
+// The item's previous tokens (and in pass 2 its normalisers) sit in LDS, so
+// no load here waits for another load.
 struct ItemSide {
     int32_t x[kGroupPos];
-    float a[kGroupPos], b[kGroupPos];  // pass 1: a = target id (bits); pass 2: a, b = the two logsumexps
+    float a[kGroupPos], b[kGroupPos];  // pass 2: the two logsumexps
 };
 
 template <int PASS, bool VEC>
@@ -124,7 +123,6 @@ __device__ __forceinline__ void load_block(BlockRegs& r, const bf16_t* __restric
     }
     const int lane = tid & 63;
     const int64_t q = (pb + (lane & 31) < p_end ? pb + (lane & 31) : p_end - 1) - p_begin;
-    if (PASS == 1) r.yy = __float_as_int(side.a[q]);
     if (PASS == 2) r.l0 = side.a[q], r.l1 = side.b[q];
 }
 
@@ -143,16 +141,14 @@ __device__ __forceinline__ void stage_block(const BlockRegs& r, uint16_t* E, uin
 // major; workgroup g takes the contiguous share [g total / G, (g + 1) total
 // / G), cut into items of one chunk and at most kGroupPos positions.
 // PASS 1 writes the chunk's (max, sum) of d and t per position to stats
-// [M][chunks][4] and d[y] to dy [M]; PASS 2 reads lse [M][2] and writes the
-// chunk's sum of min(p_d, p_t) to l1p [M][chunks].
+// [M][chunks][4]; PASS 2 reads lse [M][2] and writes the chunk's sum of
+// min(p_d, p_t) to l1p [M][chunks].
 template <int PASS, bool VEC>
 __global__ __launch_bounds__(kSThreads) void loss_stream(int64_t M, int64_t V, int64_t nchunk,
                                                          const bf16_t* __restrict__ U, const bf16_t* __restrict__ T,
                                                          const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W2,
-                                                         const int32_t* __restrict__ xp,
-                                                         const int32_t* __restrict__ y, float* __restrict__ stats,
-                                                         float* __restrict__ dy, const float* __restrict__ lse,
-                                                         float* __restrict__ l1p) {
+                                                         const int32_t* __restrict__ xp, float* __restrict__ stats,
+                                                         const float* __restrict__ lse, float* __restrict__ l1p) {
     __shared__ __align__(16) uint16_t E_lds[2][kBlk * kRow];
     __shared__ __align__(16) uint16_t U_lds[2][kBlk * kRow];
     __shared__ __align__(16) uint16_t T_lds[2][kBlk * kRow];
@@ -187,7 +183,6 @@ __global__ __launch_bounds__(kSThreads) void loss_stream(int64_t M, int64_t V, i
             int32_t x = xp[p_begin + i];
             if (x < 0 || x >= V) x = 0;  // such a position's outputs are NaN; any row will do
             side.x[i] = x;
-            if (PASS == 1) side.a[i] = __int_as_float(y[p_begin + i]);
             if (PASS == 2) side.a[i] = lse[2 * (p_begin + i)], side.b[i] = lse[2 * (p_begin + i) + 1];
         }
         __syncthreads();
@@ -196,7 +191,6 @@ __global__ __launch_bounds__(kSThreads) void loss_stream(int64_t M, int64_t V, i
         load_block<PASS, VEC>(rg[1], U, T, W1, side, V, p_begin, p_begin + kBlk, p_end, vt, tid);
         stage_block(rg[0], E_lds[0], U_lds[0], T_lds[0], tid);
         float cur_l0 = rg[0].l0, cur_l1 = rg[0].l1;
-        int32_t cur_y = rg[0].yy;
         load_block<PASS, VEC>(rg[0], U, T, W1, side, V, p_begin, p_begin + 2 * kBlk, p_end, vt, tid);
         __syncthreads();
 
@@ -228,7 +222,6 @@ __global__ __launch_bounds__(kSThreads) void loss_stream(int64_t M, int64_t V, i
                 uu[q] = *reinterpret_cast<const uint2*>(ul + 8 * q);
                 tt[q] = *reinterpret_cast<const uint2*>(tl + 8 * q);
             }
-            const int64_t v0 = vt + wave * 32 + 4 * half;
             auto word = [](const uint2& w, int j) { return j < 2 ? w.x : w.y; };
             auto d_at = [&](int r) {  // rows past V: -inf (the U tile holds -inf there)
                 const uint32_t w = word(uu[r / 4], r % 4);
@@ -238,21 +231,11 @@ __global__ __launch_bounds__(kSThreads) void loss_stream(int64_t M, int64_t V, i
                 const uint32_t w = word(tt[r / 4], r % 4);
                 return (r & 1) ? widen_hi(w) : widen_lo(w);
             };
-            const bool live = pb + row < p_end;
             float o0, o1 = 0.f, o2 = 0.f, o3 = 0.f;
             if (PASS == 1) {
-                float md = -INFINITY, mt = -INFINITY, dyv = 0.f;
-                bool hit = false;
+                float md = -INFINITY, mt = -INFINITY;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float dr = d_at(r);
-                    md = fmaxf(md, dr);
-                    mt = fmaxf(mt, t_at(r));
-                    const int64_t v = v0 + 8 * (r / 4) + (r % 4);
-                    hit = hit || v == cur_y;
-                    dyv = v == cur_y ? dr : dyv;
-                }
-                if (live && hit) dy[pb + row] = dyv;
+                for (int r = 0; r < 16; ++r) md = fmaxf(md, d_at(r)), mt = fmaxf(mt, t_at(r));
                 // a lane whose rows are all -inf on one side sums zeros there (shift 0, not -inf)
                 float sd = 0.f, st = 0.f;
                 const float mdk = md > -INFINITY ? md * kLog2e : 0.f, mtk = mt > -INFINITY ? mt * kLog2e : 0.f;
@@ -278,29 +261,40 @@ __global__ __launch_bounds__(kSThreads) void loss_stream(int64_t M, int64_t V, i
                 if (PASS == 1) red[wave][row][1] = o1, red[wave][row][2] = o2, red[wave][row][3] = o3;
             }
             __syncthreads();  // red is complete; every wave is done with this slot
-            if (tid < kBlk && pb + tid < p_end) {  // the eight waves, in order
-                const int64_t p = pb + tid;
-                if (PASS == 1) {
-                    float m1 = red[0][tid][0], s1 = red[0][tid][1], m2 = red[0][tid][2], s2 = red[0][tid][3];
-                    for (int w = 1; w < kSWaves; ++w) {
-                        merge_ms(m1, s1, red[w][tid][0], red[w][tid][1]);
-                        merge_ms(m2, s2, red[w][tid][2], red[w][tid][3]);
-                    }
-                    float4 o;
-                    o.x = m1, o.y = s1, o.z = m2, o.w = s2;
-                    reinterpret_cast<float4*>(stats)[p * nchunk + chunk] = o;
-                } else {
-                    float t = red[0][tid][0];
-                    for (int w = 1; w < kSWaves; ++w) t += red[w][tid][0];
-                    l1p[p * nchunk + chunk] = t;
+            if (PASS == 1 && tid < 2 * kBlk) {
+                // the eight waves' (max, sum) pairs of one position and one side
+                // (lanes 0-31: d, 32-63: t): the maximum first, then the
+                // rescaled sums in wave order, all eight exponentials at once
+                const int pl = tid & 31, q = (tid >> 5) * 2;
+                float mw[kSWaves], sw[kSWaves];
+#pragma unroll
+                for (int w = 0; w < kSWaves; ++w) mw[w] = red[w][pl][q], sw[w] = red[w][pl][q + 1];
+                float mm = mw[0];
+#pragma unroll
+                for (int w = 1; w < kSWaves; ++w) mm = fmaxf(mm, mw[w]);
+                float ss = 0.f;
+                if (mm > -INFINITY) {  // else every wave saw only -inf: an empty sum
+#pragma unroll
+                    for (int w = 0; w < kSWaves; ++w) ss += sw[w] * __expf(mw[w] - mm);
                 }
+                const float mt2 = __shfl_down(mm, 32), st2 = __shfl_down(ss, 32);
+                if (tid < kBlk && pb + tid < p_end) {
+                    float4 o;
+                    o.x = mm, o.y = ss, o.z = mt2, o.w = st2;
+                    reinterpret_cast<float4*>(stats)[(pb + tid) * nchunk + chunk] = o;
+                }
+            }
+            if (PASS == 2 && tid < kBlk && pb + tid < p_end) {  // the eight waves, in order
+                float t = red[0][tid][0];
+                for (int w = 1; w < kSWaves; ++w) t += red[w][tid][0];
+                l1p[(pb + tid) * nchunk + chunk] = t;
             }
             // block b + 1 into the other slot; its registers then take block
             // b + 3 (unconditionally: past the last block they re-read the last
             // position, in bounds and never used, which keeps the waits one
             // block deep)
             stage_block(nr, E_lds[slot ^ 1], U_lds[slot ^ 1], T_lds[slot ^ 1], tid);
-            cur_l0 = nr.l0, cur_l1 = nr.l1, cur_y = nr.yy;
+            cur_l0 = nr.l0, cur_l1 = nr.l1;
             load_block<PASS, VEC>(nr, U, T, W1, side, V, p_begin, pb + 3 * kBlk, p_end, vt, tid);
             __syncthreads();  // slot b + 1 is staged; red may be rewritten
         };
@@ -312,14 +306,19 @@ __global__ __launch_bounds__(kSThreads) void loss_stream(int64_t M, int64_t V, i
 }
 
 // grid M, 256 threads: lse [M][2] = (logsumexp d, logsumexp t) from the chunk
-// partials, and the confidence logit z [M] = w . [h; W1[xp]] + b.
+// partials, the target's draft logit dy [M] = U[y] + W2[y] . W1[xp] (rank
+// kRank, one product per thread) and the confidence logit
+// zc [M] = w . [h; W1[xp]] + b.
 __global__ __launch_bounds__(256) void loss_merge(int64_t M, int64_t V, int64_t H, int64_t nchunk,
-                                                  const float* __restrict__ stats, const bf16_t* __restrict__ h,
-                                                  const bf16_t* __restrict__ W1, const bf16_t* __restrict__ w,
+                                                  const float* __restrict__ stats, const bf16_t* __restrict__ U,
+                                                  const bf16_t* __restrict__ h, const bf16_t* __restrict__ W1,
+                                                  const bf16_t* __restrict__ W2, const bf16_t* __restrict__ w,
                                                   float b_conf, const int32_t* __restrict__ xp,
-                                                  float* __restrict__ lse, float* __restrict__ zc) {
+                                                  const int32_t* __restrict__ y, float* __restrict__ lse,
+                                                  float* __restrict__ dy, float* __restrict__ zc) {
+    static_assert(kRank == 256, "one rank element per thread");
     __shared__ float rm[256][4];
-    __shared__ float rz[4];
+    __shared__ float rz[4], rd[4];
     const int64_t p = blockIdx.x;
     const int tid = threadIdx.x;
     float m1 = -INFINITY, s1 = 0.f, m2 = -INFINITY, s2 = 0.f;
@@ -329,13 +328,15 @@ __global__ __launch_bounds__(256) void loss_merge(int64_t M, int64_t V, int64_t 
         merge_ms(m2, s2, o.z, o.w);
     }
     rm[tid][0] = m1, rm[tid][1] = s1, rm[tid][2] = m2, rm[tid][3] = s2;
-    int32_t x = xp[p];
+    int32_t x = xp[p], yy = y[p];
     if (x < 0 || x >= V) x = 0;
+    if (yy < 0 || yy >= V) yy = 0;  // such a position's outputs are NaN; any row will do
     float z = 0.f;
     for (int64_t i = tid; i < H + kRank; i += 256)
         z += load_elem(w, i) * (i < H ? load_elem(h, p * H + i) : load_elem(W1, (int64_t)x * kRank + (i - H)));
-    for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
-    if ((tid & 63) == 0) rz[tid >> 6] = z;
+    float d = load_elem(W2, (int64_t)yy * kRank + tid) * load_elem(W1, (int64_t)x * kRank + tid);
+    for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o), d += __shfl_xor(d, o);
+    if ((tid & 63) == 0) rz[tid >> 6] = z, rd[tid >> 6] = d;
     __syncthreads();
     for (int n = 128; n > 0; n >>= 1) {  // tree over threads, fixed order
         if (tid < n) {
@@ -347,6 +348,7 @@ __global__ __launch_bounds__(256) void loss_merge(int64_t M, int64_t V, int64_t 
     if (tid == 0) {
         lse[2 * p] = rm[0][0] + __logf(rm[0][1]);
         lse[2 * p + 1] = rm[0][2] + __logf(rm[0][3]);
+        dy[p] = load_elem(U, p * V + yy) + (((rd[0] + rd[1]) + rd[2]) + rd[3]);
         zc[p] = ((rz[0] + rz[1]) + rz[2]) + rz[3] + b_conf;
     }
 }
@@ -483,22 +485,22 @@ hipError_t block_loss_launch(int64_t N, int64_t gamma, int64_t V, int64_t H, con
     const dim3 grid((uint32_t)(total < cus ? total : cus));
     if (vec)
         hipLaunchKernelGGL((loss_stream<1, true>), grid, dim3(kSThreads), 0, stream, M, V, nchunk, Ub, Tb, W1b,
-                           W2b, xp, y, s.stats, s.dy, s.lse, s.l1p);
+                           W2b, xp, s.stats, s.lse, s.l1p);
     else
         hipLaunchKernelGGL((loss_stream<1, false>), grid, dim3(kSThreads), 0, stream, M, V, nchunk, Ub, Tb,
-                           W1b, W2b, xp, y, s.stats, s.dy, s.lse, s.l1p);
+                           W1b, W2b, xp, s.stats, s.lse, s.l1p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(loss_merge, dim3((uint32_t)M), dim3(256), 0, stream, M, V, H, nchunk, s.stats,
-                       static_cast<const bf16_t*>(h), W1b, static_cast<const bf16_t*>(w_conf), b_conf, xp, s.lse,
-                       s.zc);
+    hipLaunchKernelGGL(loss_merge, dim3((uint32_t)M), dim3(256), 0, stream, M, V, H, nchunk, s.stats, Ub,
+                       static_cast<const bf16_t*>(h), W1b, W2b, static_cast<const bf16_t*>(w_conf), b_conf, xp, y,
+                       s.lse, s.dy, s.zc);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (vec)
         hipLaunchKernelGGL((loss_stream<2, true>), grid, dim3(kSThreads), 0, stream, M, V, nchunk, Ub, Tb, W1b,
-                           W2b, xp, y, s.stats, s.dy, s.lse, s.l1p);
+                           W2b, xp, s.stats, s.lse, s.l1p);
     else
         hipLaunchKernelGGL((loss_stream<2, false>), grid, dim3(kSThreads), 0, stream, M, V, nchunk, Ub, Tb,
-                           W1b, W2b, xp, y, s.stats, s.dy, s.lse, s.l1p);
+                           W1b, W2b, xp, s.stats, s.lse, s.l1p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(loss_final, dim3((uint32_t)((M + 3) / 4)), dim3(256), 0, stream, M, gamma, V, nchunk,
                        s.l1p, s.dy, s.lse, s.zc, xp, y, mask, decay, ce, l1, conf, bce, s.terms);

@@ -49,6 +49,7 @@ constexpr int kChunk = 32 * kSWaves;  // vocabulary rows per chunk (one work ite
 constexpr int kBlk = 32;            // positions per block (one 32-wide MFMA tile)
 constexpr int kGroupPos = 1024;     // positions per work item
 constexpr int kRow = kRank + 8;     // LDS row stride (bf16) of E and of the U and t tiles (both 256 wide)
+static_assert(kChunk == kRank && kSThreads == 2 * kBlk * 8, "16 threads per position, two 8-column pieces each");
 constexpr int kReduceThreads = 1024;
 
 constexpr uint32_t kNegInf2 = 0xff80ff80u;  // two bf16 -inf
@@ -68,9 +69,11 @@ __device__ __forceinline__ void merge_ms(float& m, float& s, float mb, float sb)
 }
 
 // One block's loads, held in registers until they are staged in LDS.  Thread
-// t covers position t / 16 of the block and 16 consecutive columns from
-// 16 (t % 16): of the U and t tiles (vocabulary rows vt + ...) and of the
-// embedding W1[xp] (rank elements).  Positions past the end repeat the last
+// t covers position t / 16 of the block and two pieces of 8 columns,
+// 8 (t % 16) and 128 + 8 (t % 16): of the U and t tiles (vocabulary rows
+// vt + ...) and of the embedding W1[xp] (rank elements).  So the 16 threads
+// of a position read 256 contiguous bytes per load instruction, four whole
+// 64-byte lines.  Positions past the end repeat the last
 // one; rows past V read as bf16 -inf in both tiles, so they drop out of every
 // max, exponential and sum without a test in the epilogue.
 struct BlockRegs {
@@ -89,18 +92,18 @@ template <int PASS, bool VEC>
 __device__ __forceinline__ void load_block(BlockRegs& r, const bf16_t* __restrict__ U, const bf16_t* __restrict__ T,
                                            const bf16_t* __restrict__ W1, const ItemSide& side, int64_t V,
                                            int64_t p_begin, int64_t pb, int64_t p_end, int64_t vt, int tid) {
-    const int pl = tid >> 4, c0 = (tid & 15) * 16;
+    const int pl = tid >> 4, c0 = (tid & 15) * 8;
     const int64_t p = pb + pl < p_end ? pb + pl : p_end - 1;
     const int32_t x = side.x[p - p_begin];  // already made a valid row
     const u32x4_t* er = reinterpret_cast<const u32x4_t*>(W1 + (int64_t)x * kRank + c0);
     r.e[0] = er[0];
-    r.e[1] = er[1];
+    r.e[1] = er[kRank / 2 / 8];
     const uint16_t* ur = reinterpret_cast<const uint16_t*>(U + p * V);
     const uint16_t* tr = reinterpret_cast<const uint16_t*>(T + p * V);
     const int64_t v = vt + c0;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int64_t vi = v + 8 * i;
+        const int64_t vi = v + kChunk / 2 * i;
         if (VEC) {  // V % 8 == 0: a piece is wholly in or out
             const bool in = vi + 8 <= V;
             const int64_t vc = in ? vi : V - 8;  // out of range: an in-bounds read, replaced below
@@ -127,12 +130,12 @@ __device__ __forceinline__ void load_block(BlockRegs& r, const bf16_t* __restric
 }
 
 __device__ __forceinline__ void stage_block(const BlockRegs& r, uint16_t* E, uint16_t* Ut, uint16_t* Tt, int tid) {
-    const int pl = tid >> 4, c0 = (tid & 15) * 16;
+    const int pl = tid >> 4, c0 = (tid & 15) * 8;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        *reinterpret_cast<u32x4_t*>(E + pl * kRow + c0 + 8 * i) = r.e[i];
-        *reinterpret_cast<u32x4_t*>(Ut + pl * kRow + c0 + 8 * i) = r.u[i];
-        *reinterpret_cast<u32x4_t*>(Tt + pl * kRow + c0 + 8 * i) = r.t[i];
+        *reinterpret_cast<u32x4_t*>(E + pl * kRow + c0 + kRank / 2 * i) = r.e[i];
+        *reinterpret_cast<u32x4_t*>(Ut + pl * kRow + c0 + kChunk / 2 * i) = r.u[i];
+        *reinterpret_cast<u32x4_t*>(Tt + pl * kRow + c0 + kChunk / 2 * i) = r.t[i];
     }
 }
 

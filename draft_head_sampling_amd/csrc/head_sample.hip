@@ -2078,7 +2078,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // There is no memory clobber, which would make the compiler wait for every
 // LDS load in flight, the next unit's included; callers fence the read with
 // scheduling barriers instead.
-__device__ __forceinline__ void read_gumbel_unit(uint32_t lds_addr, const u32x2_t (&dep)[4], f32x4_t (&g)[4]) {
+__device__ __forceinline__ void read_gumbel_unit(uint32_t lds_addr, const u32x4_t (&dep)[2], f32x4_t (&g)[4]) {
     asm volatile(
         "ds_read_b128 %0, %4\n\t"
         "ds_read_b128 %1, %4 offset:1024\n\t"
@@ -2086,7 +2086,7 @@ __device__ __forceinline__ void read_gumbel_unit(uint32_t lds_addr, const u32x2_
         "ds_read_b128 %3, %4 offset:3072\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(g[0]), "=&v"(g[1]), "=&v"(g[2]), "=&v"(g[3])
-        : "v"(lds_addr), "v"(dep[0]), "v"(dep[1]), "v"(dep[2]), "v"(dep[3]));
+        : "v"(lds_addr), "v"(dep[0]), "v"(dep[1]));
 }
 
 // HD: the sequential head.  0: the Markov head (E = W1[x_{k-1}]).  1: the
@@ -2202,12 +2202,17 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
     if (t0 + wv + kResWaves < t_end) ntw = 2;
     if (wv < kResLdsTiles && t0 + kResWaves * kResRegTiles + wv < t_end) ntw = 3;
     const int n_units = ntw * NT;
-    // U of unit p lives in ur[p % 2], its Gumbel values in G_lds[wave][p % 2].
+    // U of unit p lives in uq[p % 2], its Gumbel values in G_lds[wave][p % 2].
     // issue(slot, u, kk) starts the loads of unit u of step kk into that slot;
     // u < 0 is a stand-in (every lane loads the first element group, a cache
     // hit) so that every path through the unit loop has the same loads in
     // flight and the waits the compiler places stay at unit depth
-    u32x2_t ur[2][4];
+    // Lane (row, half) loads the U rows vt + 16 i + 8 half .. + 7 (i = 0, 1)
+    // as two 16-byte pieces, so the two lanes of a request read 32
+    // contiguous bytes per instruction; the epilogue's rows
+    // vt + 8 c + 4 half .. + 3 are then one swap of 8-byte halves between
+    // lanes l and l + 32 away (unit_u).
+    u32x4_t uq[2][2];
     // the Gumbel loads go through a buffer descriptor (the caller keeps G
     // under 2 GiB): the global_load_lds form makes the compiler wait for all
     // vector memory loads at every later wait, the buffer form does not
@@ -2225,11 +2230,16 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
         // cheap to recompute, and hoisting them out of the step loop spills
         int vt = (int)(t * 32);
         asm volatile("" : "+v"(vt));
-        int64_t v[4];
+        int64_t v[4], vu[2];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int64_t x = vt + 8 * c + 4 * half;
-            v[c] = !real ? 0 : x + 4 <= V ? x : V - 4;  // clamped (V is a multiple of 4); masked in the epilogue
+            v[c] = !real ? 0 : x + 4 <= V ? x : V - 4;  // clamped (V is a multiple of 8); masked in the epilogue
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int64_t x = vt + 16 * i + 8 * half;
+            vu[i] = !real ? 0 : x + 8 <= V ? x : V - 8;
         }
         if constexpr (HG) {
 #pragma unroll
@@ -2239,8 +2249,21 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
         }
         __builtin_amdgcn_sched_barrier(0);  // U strictly after this unit's Gumbel loads
 #pragma unroll
-        for (int c = 0; c < 4; ++c) ur[slot][c] = *reinterpret_cast<const u32x2_t*>(U + base + v[c]);
+        for (int i = 0; i < 2; ++i) uq[slot][i] = *reinterpret_cast<const u32x4_t*>(U + base + vu[i]);
         __builtin_amdgcn_sched_barrier(0);
+    };
+    // The lane's epilogue rows from the unit's two pieces, in place: after
+    // swapping the high 8 bytes of lanes 0-31 with the low 8 bytes of lanes
+    // 32-63, piece i's low half holds rows 16 i + 4 half .. + 3 and its high
+    // half rows 16 i + 8 + 4 half .. + 3 in every lane, so rows
+    // 8 c + 4 half .. + 3 are words 2 (c % 2), + 1 of piece c / 2.
+    auto unit_u = [&](const int slot) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const auto s0 = __builtin_amdgcn_permlane32_swap(uq[slot][i][0], uq[slot][i][2], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(uq[slot][i][1], uq[slot][i][3], false, false);
+            uq[slot][i] = u32x4_t{s0[0], s1[0], s0[1], s1[1]};
+        }
     };
     issue(0, 0 < n_units ? 0 : -1, 0);
     if constexpr (kGSlots == 2) issue(1, 1 < n_units ? 1 : -1, 0);
@@ -2493,11 +2516,12 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
                                                                   __builtin_bit_cast(bf16x8_t, bw2), acc, 0, 0, 0);
                 }
             }
+            unit_u(p & 1);
             f32x4_t gr[4];
             if constexpr (HG) {
                 const uint32_t ga = (uint32_t)(uintptr_t)(lds_void_t*)&G_lds[wv][kGSlots == 1 ? 0 : (p & 1)][lane * 4];
                 __builtin_amdgcn_sched_barrier(0);
-                read_gumbel_unit(ga, ur[p & 1], gr);
+                read_gumbel_unit(ga, uq[p & 1], gr);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (kGSlots == 1) {
@@ -2513,7 +2537,7 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
                 // lane element r is row vt + 8 (r / 4) + 4 half + r % 4: rows rise with r
                 auto score = [&](const int r, float& bias, float& lg) {
                     const int c = r / 4, q = r % 4;
-                    const uint32_t uw = ur[p & 1][c][q >> 1];
+                    const uint32_t uw = uq[p & 1][c >> 1][2 * (c & 1) + (q >> 1)];
                     bias = acc[r];
                     lg = ((q & 1) ? widen_hi(uw) : widen_lo(uw)) + bias;
                     if constexpr (HG) return lg + gr[c][q];
@@ -2635,7 +2659,7 @@ struct ResidentPlan {
 ResidentPlan resident_plan(int64_t B, int64_t V, int hd = 0) {
     ResidentPlan p;
     const int cus = device_cus();
-    if (cus <= 0 || B < kMfmaMinBatch || B > kResMaxReq || V % 4 != 0) return p;
+    if (cus <= 0 || B < kMfmaMinBatch || B > kResMaxReq || V % 8 != 0) return p;
     int64_t nwg = cus < kResMaxWGs ? cus : kResMaxWGs;
     const int64_t ntiles = (V + 31) / 32;
     if (nwg > ntiles) nwg = ntiles;
@@ -2740,7 +2764,7 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
         if (hd != 0 && rp.nwg < kMfmaRank) rp.nwg = 0;
         // (stored logits or bias go to the general kernel: any store in the
         // resident kernel's tile loop makes its loads wait for one another)
-        if (rp.nwg > 0 && lo == nullptr && bo == nullptr && (uintptr_t)U % 8 == 0 &&
+        if (rp.nwg > 0 && lo == nullptr && bo == nullptr && (uintptr_t)U % 16 == 0 &&
             (G == nullptr || ((uintptr_t)G % 16 == 0 && B * gamma * V * 4 < ((int64_t)1 << 31)))) {
             char* p = static_cast<char*>(ws);
             uint32_t* header = reinterpret_cast<uint32_t*>(p);

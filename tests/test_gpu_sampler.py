@@ -68,18 +68,26 @@ def test_shapes(B, gamma, V, H, r, dtype, w_sd, gumbel):
     "B,gamma,V,H,gumbel",
     [
         (16, 4, 4096, 32, False),  # one 32-request tile, greedy, whole tiles
-        (24, 3, 4100, 13, True),  # ragged last tile, hidden size not a multiple of 8
+        (24, 3, 4104, 13, True),  # ragged last tile, hidden size not a multiple of 8
         (33, 3, 1000, 16, True),  # two request tiles, fewer workgroups than requests
         (64, 5, 12000, 40, False),  # 64 requests, greedy
-        (20, 20, 700, 8, False),  # long block
+        (20, 20, 712, 8, False),  # long block
         (48, 2, 65536, 64, True),  # some waves hold fewer tiles than others
+        (40, 3, 4100, 13, True),  # V % 8 = 4: the per-step matrix-core kernel instead
     ],
 )
 def test_batched_without_stored_logits(B, gamma, V, H, gumbel):
     """bf16 rank 256 with 16..64 requests and no stored logits or bias: the
-    persistent kernel that keeps W2 in registers and LDS."""
+    persistent kernel that keeps W2 in registers and LDS (its U loads take
+    16-byte pieces, so it needs V % 8 = 0; other vocabularies take the
+    per-step kernel)."""
     x, w = _random_case(0xBA7C4 + B * 131 + V, B, gamma, V, H, 256, "bf16", 0.4, gumbel)
-    sampler_parity(x, w, want_logits=False)
+    ws = torch.zeros(dh.head_sample_workspace_size(B, gamma, V, H, 256), dtype=torch.uint8, device="cuda")
+    sampler_parity(x, w, want_logits=False, workspace=ws)
+    st, paths = dh.workspace_status(ws)
+    assert st == 0
+    assert bool(paths & dh.PATH_RESIDENT) == (V % 8 == 0), paths
+    assert workspace_dirty_bytes(ws) == 0
 
 
 def test_all_equal_scores_pick_token_zero():

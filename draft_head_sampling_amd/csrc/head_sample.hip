@@ -2182,6 +2182,8 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
         if (tid < NREQ) zs_lds[0][tid] = zs_lds[1][tid] = s_lds[tid] = 0.f;  // s_0 = 0
     }
     if constexpr (EG) {
+        // this workgroup's column of the hidden halves, which no other
+        // workgroup reads: it zeroes the words once they are loaded
         if (g < kMfmaRank) {
             const int64_t mr = B * gamma * kMfmaRank;
             for (int i = tid; i < HD * B * gamma; i += kResThreads) {  // i = (m B + b) gamma + k
@@ -2189,6 +2191,7 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
                 float v = 0.f;
                 for (int ks = 0; ks < hks; ++ks) v += hid[(m * hks + ks) * mr + bk * kMfmaRank + g];
                 hcol[i] = v;
+                for (int ks = 0; ks < hks; ++ks) hid[(m * hks + ks) * mr + bk * kMfmaRank + g] = 0.f;
             }
         }
     }
@@ -2622,6 +2625,24 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
             if (k > 0 && tid >= 64 && tid < 64 + kResCopies)
                 __hip_atomic_store(win + ((int64_t)(k - 1) * kResCopies + (tid - 64)) * kResMaxReq + r, (uint64_t)0,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if constexpr (EG) {
+                // after the last step's keys every workgroup is past its last
+                // read of the posted columns: request r's words of both step
+                // slots are cleared here, and those of padding row r + B if
+                // there is one (every row up to kResMaxReq is posted; B > 32
+                // gives each padding row one reducer).  After a give-up a late
+                // workgroup may still post; the last one out clears everything
+                // then.
+                if (k == gamma - 1 && !missing) {
+                    const int nrow = r + B < kResMaxReq ? 2 : 1;
+                    for (int i = tid; i < nrow * 2 * kMfmaRank; i += kResThreads) {
+                        const int row = i < 2 * kMfmaRank ? r : r + (int)B, j = i % (2 * kMfmaRank);
+                        __hip_atomic_store(ebw + ((int64_t)(j / kMfmaRank) * kResMaxReq + row) * kMfmaRank +
+                                               j % kMfmaRank,
+                                           (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            }
             __syncthreads();  // rkey is reused
         }
         __syncthreads();  // wkey and rkey are reused next step
@@ -2643,10 +2664,10 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
                                __HIP_MEMORY_SCOPE_AGENT);
         for (int64_t i = tid; i < B * gamma; i += kResThreads)
             __hip_atomic_store(hword + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if constexpr (EG) {  // both step slots of the posted columns, and the hidden halves
-            for (int i = tid; i < 2 * kResMaxReq * kMfmaRank; i += kResThreads)
-                __hip_atomic_store(ebw + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            for (int64_t i = tid; i < HD * hks * B * gamma * kMfmaRank; i += kResThreads) hid[i] = 0.f;
+        if constexpr (EG) {  // after a give-up: both step slots of the posted columns
+            if (__hip_atomic_load(header + kHdrStatus, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+                for (int i = tid; i < 2 * kResMaxReq * kMfmaRank; i += kResThreads)
+                    __hip_atomic_store(ebw + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if (tid == 0) __hip_atomic_store(&header[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }

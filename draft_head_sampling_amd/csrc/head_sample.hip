@@ -1729,23 +1729,32 @@ constexpr int kGRow = kMfmaRows + 4;   // LDS row stride of the G tile (fp32)
 // with z choosing (Wa, outa) or (Wb, outb); W rows have stride ld.  grid
 // (r / 32, ceil(M / 32), (1 or 2) KS), 512 threads, blockIdx.z = z KS + ks: a
 // workgroup owns a 32 x 32 output tile and the ks-th of KS equal ranges of
-// the k-steps (of 16 each), its eight waves take interleaved runs of KU
+// the k-steps (of 32 each), its eight waves take interleaved runs of KU
 // k-steps (the loads of a run are all in flight at once), and the eight
-// partial tiles are summed in wave order (deterministic).  Range ks goes to
-// out_z + ks M r; the KS partials are summed by the consumer.  Requires
-// r % 32 == 0, H % 16 == 0, ld % 8 == 0, off % 8 == 0 and 16-byte aligned W
-// and h.
+// partial tiles are summed in wave order (deterministic).  The products are
+// v_mfma_f32_16x16x32_bf16, four per k-step (two 16-row halves of W times two
+// of h): lane l holds 8 consecutive k of row l % 16, so the four lanes of a
+// row read 64 contiguous bytes and a load instruction fills 16 whole cache
+// lines.  Range ks goes to out_z + ks M r, as [M][r] or, with colmajor,
+// [r][M] (each column contiguous); the KS partials are summed by the
+// consumer.  Requires r % 32 == 0, H % 32 == 0, ld % 8 == 0, off % 8 == 0 and
+// 16-byte aligned W and h.
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 constexpr int kHidWaves = 8;
+#ifndef DSPARK_HID_KU
+#define DSPARK_HID_KU 4
+#endif
+constexpr int kHidKU = DSPARK_HID_KU;  // k-steps of 32 per run: 16 loads of 16 bytes in flight per lane
 template <int KU>
 __global__ __launch_bounds__(64 * kHidWaves) void hidden_mfma(int64_t M, int64_t H, int64_t r, int64_t ld,
                                                               int64_t off, const bf16_t* __restrict__ h,
                                                               const bf16_t* __restrict__ Wa,
                                                               const bf16_t* __restrict__ Wb, float* __restrict__ outa,
-                                                              float* __restrict__ outb, int KS) {
+                                                              float* __restrict__ outb, int KS, int colmajor) {
     __shared__ float part[kHidWaves][16 * 64];
     // the wave index as a scalar: the k-step guards below are then uniform branches
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int row = lane & 31, half = lane >> 5;
+    const int row = lane & 15, kq = lane >> 4;
     const int zm = (int)blockIdx.z / KS, ks = (int)blockIdx.z % KS;
     const bf16_t* W = zm ? Wb : Wa;
     float* out = (zm ? outb : outa) + (int64_t)ks * M * r;
@@ -1755,57 +1764,78 @@ __global__ __launch_bounds__(64 * kHidWaves) void hidden_mfma(int64_t M, int64_t
     const uint32_t nj = gridDim.x, T = gridDim.x * gridDim.y, L = blockIdx.x + nj * blockIdx.y;
     const uint32_t t = T % 8 == 0 ? (L % 8) * (T / 8) + L / 8 : L;
     const int64_t j0 = (int64_t)(t % nj) * 32, m0 = (int64_t)(t / nj) * 32;
-    const int64_t mr = m0 + row < M ? m0 + row : M - 1;  // clamped rows are computed, never stored
-    const uint4* ap = reinterpret_cast<const uint4*>(W + (j0 + row) * ld + off + half * 8);
-    const uint4* bp = reinterpret_cast<const uint4*>(h + mr * H + half * 8);
-    const int nsteps = (int)(H / 16);
-    const int s_lo = (int)((int64_t)nsteps * ks / KS), steps = (int)((int64_t)nsteps * (ks + 1) / KS);
-    f32x16_t acc;
+    int64_t mr[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int q = 0; q < 2; ++q) mr[q] = m0 + 16 * q + row < M ? m0 + 16 * q + row : M - 1;  // clamped: never stored
+    const uint4* ap[2];
+    const uint4* bp[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        ap[q] = reinterpret_cast<const uint4*>(W + (j0 + 16 * q + row) * ld + off + kq * 8);
+        bp[q] = reinterpret_cast<const uint4*>(h + mr[q] * H + kq * 8);
+    }
+    const int nsteps = (int)(H / 32);
+    const int s_lo = (int)((int64_t)nsteps * ks / KS), steps = (int)((int64_t)nsteps * (ks + 1) / KS);
+    f32x4v_t acc[2][2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
+    auto step = [&](const uint4 (&a)[2], const uint4 (&b)[2]) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y)
+                acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[x]),
+                                                                   __builtin_bit_cast(bf16x8_t, b[y]), acc[x][y], 0,
+                                                                   0, 0);
+    };
     constexpr int kU = KU;  // k-steps in flight per wave
     int s0 = s_lo + wave * kU;
     for (; s0 + kU <= steps; s0 += kHidWaves * kU) {  // whole runs, no guards
-        uint4 a[kU], b[kU];
-#pragma unroll
-        for (int i = 0; i < kU; ++i) {
-            a[i] = ap[2 * (s0 + i)];
-            b[i] = bp[2 * (s0 + i)];
-        }
-        __builtin_amdgcn_sched_barrier(0);  // every load of the run issued before the first product
+        uint4 a[kU][2], b[kU][2];
 #pragma unroll
         for (int i = 0; i < kU; ++i)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[i]),
-                                                          __builtin_bit_cast(bf16x8_t, b[i]), acc, 0, 0, 0);
-    }
-    for (int s = s0; s < steps && s < s0 + kU; ++s)  // the one partial run, if any
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ap[2 * s]),
-                                                      __builtin_bit_cast(bf16x8_t, bp[2 * s]), acc, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) part[wave][i * 64 + lane] = acc[i];
+            for (int q = 0; q < 2; ++q) a[i][q] = ap[q][4 * (s0 + i)], b[i][q] = bp[q][4 * (s0 + i)];
+        __builtin_amdgcn_sched_barrier(0);  // every load of the run issued before the first product
+#pragma unroll
+        for (int i = 0; i < kU; ++i) step(a[i], b[i]);
+    }
+    for (int s = s0; s < steps && s < s0 + kU; ++s) {  // the one partial run, if any
+        const uint4 a[2] = {ap[0][4 * s], ap[1][4 * s]}, b[2] = {bp[0][4 * s], bp[1][4 * s]};
+        step(a, b);
+    }
+    // register i = 4 (2 x + y) + e of lane l: W row j0 + 16 x + 4 (l / 16) + e, h row m0 + 16 y + l % 16
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[wave][(4 * (2 * x + y) + e) * 64 + lane] = acc[x][y][e];
     __syncthreads();
-    // element e = i * 64 + l of a wave's tile: W row j0 + 8(i/4) + 4(l/32) + i%4, h row m0 + l%32
 #pragma unroll
     for (int q = 0; q < 16 * 64 / (64 * kHidWaves); ++q) {
-        const int e = tid + 64 * kHidWaves * q, i = e >> 6, l = e & 63;
-        float v = part[0][e];
+        const int el = tid + 64 * kHidWaves * q, i = el >> 6, l = el & 63;
+        float v = part[0][el];
 #pragma unroll
-        for (int w = 1; w < kHidWaves; ++w) v += part[w][e];
-        const int64_t m = m0 + (l & 31), j = j0 + 8 * (i >> 2) + 4 * (l >> 5) + (i & 3);
-        if (m < M) out[m * r + j] = v;
+        for (int w = 1; w < kHidWaves; ++w) v += part[w][el];
+        const int x = i >> 3, y = (i >> 2) & 1, e = i & 3;
+        const int64_t m = m0 + 16 * y + (l & 15), j = j0 + 16 * x + 4 * (l >> 4) + e;
+        if (m < M) out[colmajor ? j * M + m : m * r + j] = v;
     }
 }
 
-// split-K ranges of the resident path's hidden halves: about 64 k-steps each
-// (one run of 8 per wave), at most kHidMaxSplits
-constexpr int kHidMaxSplits = 8;
-int hidden_splits(int64_t H) {
-    (void)H;
-    return 1;  // several ranges measured no faster at B gamma = 448, H = 5120
-}
+// split-K ranges of the hidden halves (at most kHidMaxSplits): the gated
+// head's single matrix makes only r / 32 x ceil(B gamma / 32) tiles (112
+// workgroups at B gamma = 448), so two ranges, each with a whole run per
+// wave, bring more compute units in; the RNN head's two matrices already fill
+// the chip
+constexpr int kHidMaxSplits = 2;
+int hidden_splits(int64_t H, int hd) { return hd == 1 && H / 32 >= 2 * kHidWaves * kHidKU ? 2 : 1; }
 
 bool hidden_mfma_ok(int64_t H, int64_t r, int64_t ld, int64_t off, const void* h, const void* W) {
-    return H > 0 && H % 16 == 0 && r % 32 == 0 && ld % 8 == 0 && off % 8 == 0 && (uintptr_t)h % 16 == 0 &&
+    return H > 0 && H % 32 == 0 && r % 32 == 0 && ld % 8 == 0 && off % 8 == 0 && (uintptr_t)h % 16 == 0 &&
            (uintptr_t)W % 16 == 0;
 }
 
@@ -2185,13 +2215,14 @@ __global__ __launch_bounds__(kResThreads) void sample_batch_resident(int64_t B, 
         // this workgroup's column of the hidden halves, which no other
         // workgroup reads: it zeroes the words once they are loaded
         if (g < kMfmaRank) {
+            // column-major halves: the column is B gamma contiguous floats per range
             const int64_t mr = B * gamma * kMfmaRank;
             for (int i = tid; i < HD * B * gamma; i += kResThreads) {  // i = (m B + b) gamma + k
                 const int64_t m = i / (B * gamma), bk = i % (B * gamma);
                 float v = 0.f;
-                for (int ks = 0; ks < hks; ++ks) v += hid[(m * hks + ks) * mr + bk * kMfmaRank + g];
+                for (int ks = 0; ks < hks; ++ks) v += hid[(m * hks + ks) * mr + g * B * gamma + bk];
                 hcol[i] = v;
-                for (int ks = 0; ks < hks; ++ks) hid[(m * hks + ks) * mr + bk * kMfmaRank + g] = 0.f;
+                for (int ks = 0; ks < hks; ++ks) hid[(m * hks + ks) * mr + g * B * gamma + bk] = 0.f;
             }
         }
     }
@@ -2802,17 +2833,17 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
                 ebw = reinterpret_cast<uint64_t*>(q + ((size_t)(4 * hd * kHidMaxSplits * B * gamma * kMfmaRank) + 255) /
                                                           256 * 256);
                 const int64_t M = B * gamma;
-                const int ks = hidden_splits(H);
+                const int ks = hidden_splits(H, hd);
                 const dim3 grid((uint32_t)(r / 32), (uint32_t)((M + 31) / 32), (uint32_t)(hd * ks));
-                hipLaunchKernelGGL(hidden_mfma<16>, grid, dim3(64 * kHidWaves), 0, stream, M, H, r,
+                hipLaunchKernelGGL(hidden_mfma<kHidKU>, grid, dim3(64 * kHidWaves), 0, stream, M, H, r,
                                    hd == 2 ? 2 * r + H : H + r, hd == 2 ? 2 * r : (int64_t)0,
                                    static_cast<const bf16_t*>(h), static_cast<const bf16_t*>(hd == 2 ? Wrg : Wg),
-                                   static_cast<const bf16_t*>(Wrc), hid, hid + ks * M * r, ks);
+                                   static_cast<const bf16_t*>(Wrc), hid, hid + ks * M * r, ks, 1);
                 const hipError_t e = hipGetLastError();
                 if (e != hipSuccess) return e;
             }
             int lim = wait_limit(kChainSpinLimit);
-            int hks = hidden_splits(H);
+            int hks = hidden_splits(H, hd);
             const T* ht = static_cast<const T*>(h);
             const bf16_t* Wh = static_cast<const bf16_t*>(hd == 2 ? Wrg : Wg);
             const bf16_t* Wh2 = static_cast<const bf16_t*>(Wrc);
@@ -2866,10 +2897,10 @@ hipError_t launch_typed(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t 
         if (hmfma) {
             const int64_t M = B * gamma;
             const dim3 grid((uint32_t)(r / 32), (uint32_t)((M + 31) / 32), rnn ? 2u : 1u);
-            hipLaunchKernelGGL(hidden_mfma<16>, grid, dim3(64 * kHidWaves), 0, stream, M, H, r,
+            hipLaunchKernelGGL(hidden_mfma<kHidKU>, grid, dim3(64 * kHidWaves), 0, stream, M, H, r,
                                rnn ? 2 * r + H : H + r, rnn ? 2 * r : (int64_t)0, static_cast<const bf16_t*>(h),
                                static_cast<const bf16_t*>(rnn ? Wrg : Wg), static_cast<const bf16_t*>(Wrc), gate_ws,
-                               gate_ws + B * gamma * r, 1);
+                               gate_ws + B * gamma * r, 1, 0);
             if ((err = hipGetLastError()) != hipSuccess) return err;
         }
     }

@@ -680,9 +680,12 @@ constexpr size_t kChainHeader = kWsHeader;  // words 0 (exit counter), 1 (status
 // twice the bound), stages their W1 and W2 rows in LDS, precomputes every
 // bias the chain can need and walks the chain in one wave, first with the
 // guessed bound and, if the largest W2 row norm turns out larger, again.  The
-// W2 rows stream through registers only for that norm, after the lists are
-// out: behind a full HBM queue every cross-workgroup message takes several
-// microseconds.  A step whose candidate set is not provably inside the
+// W2 rows stream through registers only for that norm, from the start but
+// throttled: two waves per workgroup with one 64-byte row slice in flight
+// per lane, so the stream ends about when the coordinator needs the norm
+// while the lists and the coordinator's reads do not queue behind it (a
+// full-rate stream makes every cross-workgroup message wait several
+// microseconds).  A step whose candidate set is not provably inside the
 // lists hands the rest of the block to the grid-wide per-step exchange,
 // which then keeps each workgroup's W2 rows in registers.
 constexpr int kScreenMaxGamma = 8;   // U and G of every step stay in registers during the screen
@@ -691,9 +694,10 @@ constexpr int kScreenEntries = 3;
 constexpr int kScreenWaves = kChainWaves / 2;  // row workgroups: waves that screen; the others take the norms
 constexpr int kScreenLanes = 64 * kScreenWaves;
 constexpr int kScreenRows = 3;       // rows per screening lane
-constexpr int kNormLanes = kChainThreads - kScreenLanes;
+constexpr int kNormWaves = 2;        // of the other waves, those that stream W2 for the norm
+constexpr int kNormLanes = 64 * kNormWaves;
 constexpr int kNormGroups = kNormLanes / kChainLanesPerRow;  // rows per norm slot
-constexpr int kStreamSlots = 8;      // W2 slots in flight per norm lane
+constexpr int kStreamSlots = 1;      // W2 row slices in flight per norm lane
 constexpr int kRegionWords = 64;     // u64 words per workgroup region: one per lane of a wave
 constexpr int kPollRegions = kChainMaxWGs / kChainWaves;  // regions polled per coordinator wave
 constexpr int kCandMax = 32;         // candidate rows staged in LDS
@@ -705,12 +709,11 @@ constexpr uint64_t kEmptyEntry = 1ull << 31;         // no row (low word above a
 constexpr uint64_t kTag = 1ull << 32;                // marks a written scalar word
 constexpr uint64_t kDecideDone = 1ull << 63;
 constexpr uint64_t kDecideResume = 1ull << 62;       // | step << 32 | previous token
-// Words that every row workgroup polls (the decision, and the go-ahead for
-// its W2 stream) are replicated, one 128-byte line per copy, so the polls
-// spread over memory channels; workgroup g reads copy g % kCopies.
+// The word that every row workgroup polls (the decision) is replicated, one
+// 128-byte line per copy, so the polls spread over memory channels;
+// workgroup g reads copy g % kCopies.
 constexpr int kCopies = 16;
-constexpr int kAuxGo = kCopies * kSlotWords;
-constexpr int kAuxWords = 2 * kCopies * kSlotWords;
+constexpr int kAuxWords = kCopies * kSlotWords;
 constexpr float kN2Guess = 1.5f;                     // sampled squared norm -> guess of the largest
 static_assert(kScreenStep * kScreenMaxGamma + 1 <= kRegionWords, "screen region too small");
 static_assert(kCandMax % kChainWaves == 0, "candidates per wave");
@@ -881,7 +884,6 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
     const int64_t h_lo = (int64_t)g * h_per < H ? (int64_t)g * h_per : H;
     const int64_t h_hi = h_lo + h_per < H ? h_lo + h_per : H;
     uint64_t* const dcopy = aux + (g % kCopies) * kSlotWords;           // this workgroup's decision copy
-    uint64_t* const gcopy = aux + kAuxGo + (g % kCopies) * kSlotWords;  // and go-ahead copy
     const int nlist = kScreenStep * gamma;  // list words
     const int nwords = nlist + 1;           // then the largest squared W2 row norm
     uint64_t* myregion = regions + (int64_t)g * kRegionWords;
@@ -983,10 +985,6 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 sc.ssum[wave][lane] = sm;
             }
             __syncthreads();
-            // every list is in: the row workgroups may start their W2 streams
-            if (tid < kCopies)
-                __hip_atomic_store(aux + kAuxGo + tid * kSlotWords, (uint64_t)1, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
             if (wave == 0) {
                 uint32_t m = 0;
                 float sm = 0.f;
@@ -1224,10 +1222,6 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 __syncthreads();
                 if (wave == 0) wk = walk();
             }
-            // every row workgroup has posted its norm, so all have read the go-ahead
-            if (tid >= kChainThreads - kCopies)
-                __hip_atomic_store(aux + kAuxGo + (tid - (kChainThreads - kCopies)) * kSlotWords, (uint64_t)0,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (wave == 0) {
                 const int k = wk.k;
                 const bool fail = wk.fail;
@@ -1377,38 +1371,34 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             screen_sync(sc, lane, 2 * kScreenWaves);
         } else {
             // Norm waves: the W2 slice streams through a window of slots for
-            // the largest squared row norm.  Rows past the slice load row 0
-            // and are masked out (a zero fill would wait for the load it
-            // overwrites).
+            // the largest squared row norm, at the throttled rate described
+            // above (the remaining waves idle here).  Rows past the slice
+            // load row 0 and are masked out (a zero fill would wait for the
+            // load it overwrites).
             const int ng = (tid - kScreenLanes) >> 3;
             constexpr int NS = (NSLOT * kChainGroups + kNormGroups - 1) / kNormGroups;
-            // Hold the stream back until workgroup 0 has every list: behind a
-            // full HBM queue every cross-workgroup message waits several
-            // microseconds.
-            for (int spin = 0; spin < spin_limit; ++spin) {
-                if (__hip_atomic_load(gcopy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
-                __builtin_amdgcn_s_sleep(2);
-            }
-            uint32_t buf[kStreamSlots][16];
-#pragma unroll
-            for (int i = 0; i < kStreamSlots; ++i) {
-                const int lr = i * kNormGroups + ng;
-                const bool in = i < NS && lr < rows_per_wg && row0 + lr < V;
-                load64B(W2 + (in ? row0 + lr : 0) * kChainRank + sub * 32, buf[i]);
-            }
             uint32_t nb = 0;
+            if (tid < kScreenLanes + kNormLanes) {
+                uint32_t buf[kStreamSlots][16];
 #pragma unroll
-            for (int i = 0; i < NS; ++i) {
-                float a = 0.f;
+                for (int i = 0; i < kStreamSlots; ++i) {
+                    const int lr = i * kNormGroups + ng;
+                    const bool in = i < NS && lr < rows_per_wg && row0 + lr < V;
+                    load64B(W2 + (in ? row0 + lr : 0) * kChainRank + sub * 32, buf[i]);
+                }
 #pragma unroll
-                for (int q = 0; q < 16; ++q) a = dot2(buf[i % kStreamSlots][q], buf[i % kStreamSlots][q], a);
-                a = sum8(a);
-                const int lr = i * kNormGroups + ng;
-                if (lr < rows_per_wg && row0 + lr < V) nb = max(nb, bound_bits(a));
-                if (i + kStreamSlots < NS) {
-                    const int lr2 = (i + kStreamSlots) * kNormGroups + ng;
-                    const bool in = lr2 < rows_per_wg && row0 + lr2 < V;
-                    load64B(W2 + (in ? row0 + lr2 : 0) * kChainRank + sub * 32, buf[i % kStreamSlots]);
+                for (int i = 0; i < NS; ++i) {
+                    float a = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) a = dot2(buf[i % kStreamSlots][q], buf[i % kStreamSlots][q], a);
+                    a = sum8(a);
+                    const int lr = i * kNormGroups + ng;
+                    if (lr < rows_per_wg && row0 + lr < V) nb = max(nb, bound_bits(a));
+                    if (i + kStreamSlots < NS) {
+                        const int lr2 = (i + kStreamSlots) * kNormGroups + ng;
+                        const bool in = lr2 < rows_per_wg && row0 + lr2 < V;
+                        load64B(W2 + (in ? row0 + lr2 : 0) * kChainRank + sub * 32, buf[i % kStreamSlots]);
+                    }
                 }
             }
             nb = wave_max_u32(nb);

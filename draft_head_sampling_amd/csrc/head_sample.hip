@@ -689,7 +689,12 @@ constexpr size_t kChainHeader = kWsHeader;  // words 0 (exit counter), 1 (status
 // lists hands the rest of the block to the grid-wide per-step exchange,
 // which then keeps each workgroup's W2 rows in registers.
 constexpr int kScreenMaxGamma = 8;   // U and G of every step stay in registers during the screen
-constexpr int kScreenStep = 6;       // words per step: 3 entries, cutoff, |U|+|G| bound, hidden partial
+// A row workgroup's region: word k (k < kScreenMaxGamma) is the step-k
+// summary, (best ranking key << 32) | (|U|+|G| bound bits | 1) (the low bit
+// makes the word non-zero and the bound one ulp larger, still a bound), all
+// in the region's first 64 bytes; then kScreenStep list words per step from
+// kListBase (3 entries, cutoff); then the largest squared W2 row norm.
+constexpr int kScreenStep = 4;       // list words per step: 3 entries, cutoff
 constexpr int kScreenEntries = 3;
 constexpr int kScreenWaves = kChainWaves / 2;  // row workgroups: waves that screen; the others take the norms
 constexpr int kScreenLanes = 64 * kScreenWaves;
@@ -715,7 +720,11 @@ constexpr uint64_t kDecideResume = 1ull << 62;       // | step << 32 | previous 
 constexpr int kCopies = 16;
 constexpr int kAuxWords = kCopies * kSlotWords;
 constexpr float kN2Guess = 1.5f;                     // sampled squared norm -> guess of the largest
-static_assert(kScreenStep * kScreenMaxGamma + 1 <= kRegionWords, "screen region too small");
+constexpr int kListBase = kScreenMaxGamma;
+constexpr int kNormWord = kListBase + kScreenStep * kScreenMaxGamma;
+constexpr int kRegionUsed = kNormWord + 1;
+static_assert(kRegionUsed <= kRegionWords, "screen region too small");
+static_assert(kScreenMaxGamma == 8 && kPollRegions % 8 == 0, "one 64-byte summary line per region, 8 regions per load");
 static_assert(kCandMax % kChainWaves == 0, "candidates per wave");
 static_assert(kChainMaxSlots * kChainGroups <= (1 << kLidBits), "row index field too small");
 static_assert(kChainMaxSlots * kChainGroups <= kScreenRows * kScreenLanes, "screening lanes cover the rows");
@@ -799,10 +808,10 @@ struct ScreenLds {
     uint32_t stepmask[kScreenMaxGamma];             // candidates of each step
     float pw[kScreenMaxGamma][kChainWaves];
     uint32_t wn[kChainWaves];
-    uint32_t smax[kChainWaves][kRegionWords];
-    float ssum[kChainWaves][kRegionWords];
-    uint32_t fmax[kRegionWords];
-    float fsum[kRegionWords];
+    uint32_t kmax[kChainWaves][kScreenMaxGamma];  // per wave and step: best ranking key, |U|+|G| bound bits
+    uint32_t bmax[kChainWaves][kScreenMaxGamma];
+    uint32_t fkey[kScreenMaxGamma], fbound[kScreenMaxGamma];  // over all regions
+    uint32_t fcut[kScreenMaxGamma];  // largest cutoff of the regions whose lists were read
     float pk[kScreenMaxGamma];
     float winf[kScreenMaxGamma];
     uint32_t wkey[kScreenMaxGamma];                 // the windows as ranking-key bounds
@@ -884,8 +893,6 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
     const int64_t h_lo = (int64_t)g * h_per < H ? (int64_t)g * h_per : H;
     const int64_t h_hi = h_lo + h_per < H ? h_lo + h_per : H;
     uint64_t* const dcopy = aux + (g % kCopies) * kSlotWords;           // this workgroup's decision copy
-    const int nlist = kScreenStep * gamma;  // list words
-    const int nwords = nlist + 1;           // then the largest squared W2 row norm
     uint64_t* myregion = regions + (int64_t)g * kRegionWords;
 
     const int64_t xa = x0[0];
@@ -923,7 +930,9 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 sc.overflow[tid] = 0;
             }
             if (tid == 0) sc.ncand = 0, sc.abort = 0, sc.n2 = 0;
-            hidden_partials(sc, gamma, H, h_lo, h_hi, h, w_conf, tid, kChainThreads, lane, wave);
+            // the whole hidden part of every confidence logit: the lists
+            // arrive several microseconds after this is done
+            hidden_partials(sc, gamma, H, 0, H, h, w_conf, tid, kChainThreads, lane, wave);
             {
                 float a = 0.f;
 #pragma unroll
@@ -950,48 +959,53 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 if (lane == 0) sc.esq[kERowAnchor] = es;
             }
 
-            // the lists: wave w polls row workgroups 1 + w + 8 i, lane j reads
-            // word j; the spin only checks that every word is written
-            const int type = lane < nlist ? lane % kScreenStep : 7;  // 0-2 entries, 3 cutoff, 4 bound, 5 partial
-            const int kk = lane / kScreenStep;
-            uint64_t word[kPollRegions];
+            // the summaries: wave w polls row workgroups 1 + w + 8 j (j < 32),
+            // eight per load: lane l reads step l % 8 of workgroup
+            // j = 8 q + l / 8 of load q; the spin only checks that every word
+            // is written
+            constexpr int kSumLoads = kPollRegions / 8;
+            const int sk = lane & 7;
+            uint64_t sw[kSumLoads];
+            bool suse[kSumLoads];
+            int sgg[kSumLoads];
+#pragma unroll
+            for (int q = 0; q < kSumLoads; ++q) {
+                sgg[q] = 1 + wave + kChainWaves * (8 * q + (lane >> 3));
+                suse[q] = sgg[q] < nwg && sk < gamma;
+            }
             bool ready = false;
             for (int spin = 0; spin < spin_limit && !ready; ++spin) {
                 bool all = true;
 #pragma unroll
-                for (int i = 0; i < kPollRegions; ++i) {
-                    const int gg = 1 + wave + kChainWaves * i;
-                    const bool use = gg < nwg && lane < nlist;
-                    word[i] = __hip_atomic_load(regions + (use ? (int64_t)gg * kRegionWords + lane : 0),
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    all = all && (!use || word[i] != 0);
+                for (int q = 0; q < kSumLoads; ++q) {
+                    sw[q] = __hip_atomic_load(regions + (suse[q] ? (int64_t)sgg[q] * kRegionWords + sk : 0),
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    all = all && (!suse[q] || sw[q] != 0);
                 }
                 ready = __all(all);
                 if (!ready) __builtin_amdgcn_s_sleep(1);
             }
             if (!ready && lane == 0) sc.abort = 1;
             {
-                uint32_t mx = 0;
-                float sm = 0.f;
+                uint32_t km = 0, bm = 0;
 #pragma unroll
-                for (int i = 0; i < kPollRegions; ++i) {
-                    const bool in = 1 + wave + kChainWaves * i < nwg;
-                    const uint64_t w = word[i];
-                    const uint32_t v32 = type == 0 ? (uint32_t)(w >> 32) : (uint32_t)w;
-                    mx = (in && (type == 0 || type == 3 || type == 4)) ? max(mx, v32) : mx;
-                    sm += (in && type == 5) ? __uint_as_float(v32) : 0.f;
+                for (int q = 0; q < kSumLoads; ++q) {
+                    km = suse[q] ? max(km, (uint32_t)(sw[q] >> 32)) : km;
+                    bm = suse[q] ? max(bm, (uint32_t)sw[q]) : bm;
                 }
-                sc.smax[wave][lane] = mx;
-                sc.ssum[wave][lane] = sm;
+                // lanes of one step: l, l ^ 8, l ^ 16, ...
+#pragma unroll
+                for (int o = 8; o < 64; o <<= 1) km = max(km, (uint32_t)__shfl_xor(km, o)), bm = max(bm, (uint32_t)__shfl_xor(bm, o));
+                if (lane < kScreenMaxGamma) sc.kmax[wave][lane] = km, sc.bmax[wave][lane] = bm;
             }
             __syncthreads();
-            if (wave == 0) {
-                uint32_t m = 0;
-                float sm = 0.f;
+            if (tid < kScreenMaxGamma) {
+                uint32_t km = 0, bm = 0;
 #pragma unroll
-                for (int w = 0; w < kChainWaves; ++w) m = max(m, sc.smax[w][lane]), sm += sc.ssum[w][lane];
-                sc.fmax[lane] = m;
-                sc.fsum[lane] = sm;
+                for (int w = 0; w < kChainWaves; ++w) km = max(km, sc.kmax[w][tid]), bm = max(bm, sc.bmax[w][tid]);
+                sc.fkey[tid] = km;
+                sc.fbound[tid] = bm;
+                sc.fcut[tid] = 0;
             }
             __syncthreads();
             // the windows: best t minus twice a guess of the bias bound (the
@@ -1001,9 +1015,9 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 const float bg = __builtin_sqrtf(__uint_as_float(sc.n2s) * kN2Guess) * 2.f *
                                      __builtin_sqrtf(sc.esq[kERowAnchor]) * kBetaSlack +
                                  kBetaFloor;
-                const float a = __uint_as_float(sc.fmax[kScreenStep * tid + 4]);
+                const float a = __uint_as_float(sc.fbound[tid]);
                 const float eg = 5.f * kUlp * (a + bg);
-                const float wf = float_down(key_lower(sc.fmax[kScreenStep * tid]) - 2.0 * ((double)bg + eg));
+                const float wf = float_down(key_lower(sc.fkey[tid]) - 2.0 * ((double)bg + eg));
                 sc.winf[tid] = wf;
                 // a bucket reaches the window iff its upper end does: for non-NaN
                 // floats a >= b iff orderable(a) >= orderable(b), once a zero
@@ -1011,32 +1025,64 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 sc.wkey[tid] = wf != wf ? 0xffffffffu : orderable(wf == 0.f ? -0.f : wf);
             }
             __syncthreads();
-            // the entries inside the windows, straight from the polled words: a
-            // branch-free hit mask per lane, then the few hits are written out
+            // the lists of the (workgroup, step) pairs whose best key reaches
+            // the window: entries inside it become candidates, and the
+            // cutoffs bound what the lists may have left out (a workgroup
+            // whose best key is outside the window has its cutoff outside
+            // too, below any threshold the walk accepts)
             {
-                uint32_t hits = 0;
-                if (type < kScreenEntries) {
-                    const uint32_t wq = sc.wkey[kk];
-                    const uint32_t v32 = (uint32_t)V;  // V < 2^31
+                const uint32_t wq = sk < gamma ? sc.wkey[sk] : 0xffffffffu;
+                bool flag[kSumLoads];
+                uint64_t lw[kSumLoads][4];
 #pragma unroll
-                    for (int i = 0; i < kPollRegions; ++i) {
-                        const uint64_t w = word[i];
-                        const uint32_t id1 = (uint32_t)w;  // row id + 1, or the empty marker
-                        const uint32_t q = (uint32_t)(w >> 32);
-                        // (bitwise ands: no branch per word)
-                        const uint32_t hit = (uint32_t)(1 + wave + kChainWaves * i < nwg) & (uint32_t)(id1 - 1u < v32) &
-                                             (uint32_t)(q != 0) & (uint32_t)((q | kLidMask) >= wq);
-                        hits |= hit << i;
+                for (int q = 0; q < kSumLoads; ++q) {
+                    flag[q] = suse[q] && ready && (((uint32_t)(sw[q] >> 32) | kLidMask) >= wq);
+                    const uint64_t* src =
+                        regions + (flag[q] ? (int64_t)sgg[q] * kRegionWords + kListBase + kScreenStep * sk : 0);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        lw[q][j] = flag[q] ? __hip_atomic_load(src + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1;
+                }
+                // (the summary is written with the lists, not after them: poll
+                // the few words not yet seen)
+                for (int spin = 0; spin < spin_limit; ++spin) {
+                    bool all = true;
+#pragma unroll
+                    for (int q = 0; q < kSumLoads; ++q)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) all = all && lw[q][j] != 0;
+                    if (__all(all)) break;
+                    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+                    for (int q = 0; q < kSumLoads; ++q) {
+                        const uint64_t* src =
+                            regions + (flag[q] ? (int64_t)sgg[q] * kRegionWords + kListBase + kScreenStep * sk : 0);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (lw[q][j] == 0) lw[q][j] = __hip_atomic_load(src + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
-                if (hits) {
-                    int idx = atomicAdd(&sc.ncand, __popc(hits));
+                const uint32_t v32 = (uint32_t)V;  // V < 2^31
 #pragma unroll
-                    for (int i = 0; i < kPollRegions; ++i) {
-                        if ((hits >> i) & 1u) {
-                            if (idx < kCandMax) sc.cv[idx] = (uint32_t)word[i] - 1, sc.cstep[idx] = kk;
-                            else sc.overflow[kk] = 1;
-                            ++idx;
+                for (int q = 0; q < kSumLoads; ++q) {
+                    if (!flag[q]) continue;
+                    bool seen = true;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) seen = seen && lw[q][j] != 0;
+                    if (!seen) {
+                        sc.abort = 1;
+                        continue;
+                    }
+                    atomicMax(&sc.fcut[sk], (uint32_t)lw[q][3]);
+#pragma unroll
+                    for (int j = 0; j < kScreenEntries; ++j) {
+                        const uint64_t w = lw[q][j];
+                        const uint32_t id1 = (uint32_t)w;  // row id + 1, or the empty marker
+                        const uint32_t qk = (uint32_t)(w >> 32);
+                        if (id1 - 1u < v32 && qk != 0 && (qk | kLidMask) >= wq) {
+                            const int idx = atomicAdd(&sc.ncand, 1);
+                            if (idx < kCandMax) sc.cv[idx] = id1 - 1, sc.cstep[idx] = sk;
+                            else sc.overflow[sk] = 1;
                         }
                     }
                 }
@@ -1048,7 +1094,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             // a first look now, used after the table below
             const int np = tid - kChainThreads / 2;  // norm poller index
             const bool poller = !abort && np >= 0 && np + 1 < nwg;
-            const uint64_t* npw = regions + (int64_t)(poller ? np + 1 : 1) * kRegionWords + nwords - 1;
+            const uint64_t* npw = regions + (int64_t)(poller ? np + 1 : 1) * kRegionWords + kNormWord;
             uint64_t nword = poller ? __hip_atomic_load(npw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
 
             // stage the candidates' rows (one wave per candidate) and forced tokens' rows
@@ -1147,8 +1193,8 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                         for (uint32_t bits = m; bits; bits &= bits - 1) tmax = fmaxf(tmax, sc.ct[__builtin_ctz(bits)]);
                         const float n2 = __builtin_sqrtf(__uint_as_float(n2b));
                         const float es = sc.esq[r];
-                        const uint32_t ab = sc.fmax[kScreenStep * k + 4];
-                        const uint32_t cut = sc.fmax[kScreenStep * k + 3];
+                        const uint32_t ab = sc.fbound[k];
+                        const uint32_t cut = sc.fcut[k];
                         const float beta = n2 * __builtin_sqrtf(es) * kBetaSlack + kBetaFloor;
                         const float eps = 5.f * kUlp * (__uint_as_float(ab) + beta);
                         const double thr = (double)tmax - 2.0 * ((double)beta + eps);
@@ -1233,7 +1279,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 const int settled = k;
                 float c = 0.f;
                 if (lane < settled && tk >= 0)
-                    c = 1.f / (1.f + expf(-(sc.pk[lane] + sc.fsum[kScreenStep * lane + 5] + sc.zcm[pst] + b_conf)));
+                    c = 1.f / (1.f + expf(-(sc.pk[lane] + sc.zcm[pst] + b_conf)));
                 if (lane < settled) tokens[lane] = tk;
                 float surv = 1.f;
                 bool alive = true;
@@ -1288,7 +1334,6 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
         if (wave < kScreenWaves) {
             // Screening waves: nothing of W2 is in flight here, so every wait
             // for a small load is exact.  Lane i screens rows i, i + 256, ...
-            hidden_partials(sc, gamma, H, h_lo, h_hi, h, w_conf, tid, kScreenLanes, lane, wave);
             int64_t sv[kScreenRows];
             bool sok[kScreenRows];
             uint16_t ur[kScreenMaxGamma][kScreenRows];
@@ -1340,7 +1385,8 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 if (lane == 0) atomicMax(&sc.a1[k], am);
             }
             screen_sync(sc, lane, kScreenWaves);
-            // wave w merges steps w, w + 4 and publishes their six words each
+            // wave w merges steps w, w + 4 and publishes their list words
+            // and their summary word each
 #pragma unroll
             for (int k = wave; k < kScreenMaxGamma; k += kScreenWaves) {
                 if (k >= gamma) break;
@@ -1351,22 +1397,19 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                     t4[r] = wave_max_u32(c);
                     if (c == t4[r]) c = 0;
                 }
-                float ps = 0.f;
-#pragma unroll
-                for (int w = 0; w < kScreenWaves; ++w) ps += sc.pw[k][w];
                 const uint32_t te = lane == 0 ? t4[0] : lane == 1 ? t4[1] : t4[2];
                 uint64_t word;
                 if (lane < kScreenEntries)
                     word = te ? (((uint64_t)te << 32) | (uint64_t)(row0 + (te & kLidMask) + 1)) : kEmptyEntry;
                 else if (lane == 3)
                     word = kTag | t4[3];
-                else if (lane == 4)
-                    word = kTag | sc.a1[k];
                 else
-                    word = kTag | __float_as_uint(ps);
+                    word = ((uint64_t)t4[0] << 32) | (sc.a1[k] | 1u);
                 if (lane < kScreenStep)
-                    __hip_atomic_store(myregion + kScreenStep * k + lane, word, __ATOMIC_RELAXED,
+                    __hip_atomic_store(myregion + kListBase + kScreenStep * k + lane, word, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
+                else if (lane == kScreenStep)
+                    __hip_atomic_store(myregion + k, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             screen_sync(sc, lane, 2 * kScreenWaves);
         } else {
@@ -1409,7 +1452,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             uint32_t m = 0;
 #pragma unroll
             for (int w = kScreenWaves; w < kChainWaves; ++w) m = max(m, sc.wn[w]);
-            __hip_atomic_store(myregion + nwords - 1, kTag | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(myregion + kNormWord, kTag | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             // wait for the coordinator's decision
             uint64_t d = 0;
             for (int spin = 0; spin < spin_limit && d == 0; ++spin) {
@@ -1421,7 +1464,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
         }
         __syncthreads();
         const uint64_t d = sc.decision;
-        if (tid < nwords)  // read by the coordinator before it decided
+        if (tid < kRegionUsed)  // read by the coordinator before it decided
             __hip_atomic_store(myregion + tid, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (d == 0 || (d & kDecideDone)) {
             done = true;

@@ -681,7 +681,7 @@ constexpr size_t kChainHeader = kWsHeader;  // words 0 (exit counter), 1 (status
 // bias the chain can need and walks the chain in one wave, first with the
 // guessed bound and, if the largest W2 row norm turns out larger, again.  The
 // W2 rows stream through registers only for that norm, from the start but
-// throttled: two waves per workgroup with one 64-byte row slice in flight
+// throttled: three waves per workgroup with one 64-byte row slice in flight
 // per lane, so the stream ends about when the coordinator needs the norm
 // while the lists and the coordinator's reads do not queue behind it (a
 // full-rate stream makes every cross-workgroup message wait several
@@ -699,7 +699,7 @@ constexpr int kScreenEntries = 3;
 constexpr int kScreenWaves = kChainWaves / 2;  // row workgroups: waves that screen; the others take the norms
 constexpr int kScreenLanes = 64 * kScreenWaves;
 constexpr int kScreenRows = 3;       // rows per screening lane
-constexpr int kNormWaves = 2;        // of the other waves, those that stream W2 for the norm
+constexpr int kNormWaves = 3;        // of the other waves, those that stream W2 for the norm
 constexpr int kNormLanes = 64 * kNormWaves;
 constexpr int kNormGroups = kNormLanes / kChainLanesPerRow;  // rows per norm slot
 constexpr int kStreamSlots = 1;      // W2 row slices in flight per norm lane
@@ -1178,6 +1178,8 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             // ones, inside the windows, so the result stands when the real norm
             // is no larger.  Otherwise table and walk run again.
             __syncthreads();  // the bias table is complete
+            // a second look at the norms (the streams end about now), read after the walk
+            if (poller && nword == 0) nword = __hip_atomic_load(npw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const auto build = [&](uint32_t n2b) {
                 for (int p = tid; p < gamma * kERows; p += kChainThreads) {
                     const int k = p / kERows, r = p % kERows;

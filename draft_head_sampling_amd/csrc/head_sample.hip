@@ -724,6 +724,7 @@ constexpr int kListBase = kScreenMaxGamma;
 constexpr int kNormWord = kListBase + kScreenStep * kScreenMaxGamma;
 constexpr int kRegionUsed = kNormWord + 1;
 static_assert(kRegionUsed <= kRegionWords, "screen region too small");
+static_assert(kChainRank / 2 % 64 == 0, "16-byte aligned rows in LDS");
 static_assert(kScreenMaxGamma == 8 && kPollRegions % 8 == 0, "one 64-byte summary line per region, 8 regions per load");
 static_assert(kCandMax % kChainWaves == 0, "candidates per wave");
 static_assert(kChainMaxSlots * kChainGroups <= (1 << kLidBits), "row index field too small");
@@ -795,7 +796,7 @@ constexpr int kERowAnchor = kCandMax;
 constexpr int kERowForced = kCandMax + 1;
 static_assert(kERows <= 64, "one e row per lane");
 
-struct ScreenLds {
+struct __align__(16) ScreenLds {  // (16-byte rows: the bias table reads them as uint4)
     uint32_t cw2[kCandMax][kChainRank / 2];         // W2 rows of the candidates (bf16 pairs)
     uint32_t cw1[kCandMax][kChainRank / 2];         // their W1 rows: e of the next step if one wins
     float bias[kCandMax][kERows];                   // W2[candidate] . e for every possible predecessor
@@ -878,7 +879,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
     uint64_t* regions, uint64_t* aux, uint32_t* header, int spin_limit) {
     __shared__ uint64_t red[kChainWaves];
     __shared__ float fred[kChainWaves];
-    __shared__ uint32_t we_lds[kChainRank / 2];  // Markov part of the confidence weights (workgroup 0)
+    __shared__ __align__(16) uint32_t we_lds[kChainRank / 2];  // Markov part of the confidence weights (workgroup 0)
     __shared__ uint64_t winner;
     __shared__ float zpart;
     __shared__ int last_flag;
@@ -1140,31 +1141,48 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             // every quantity the chain can need, in parallel: |e|^2 and
             // w_e . e of each e row, and W2[j] . e for each candidate j and
             // each e row that can precede its step
+            // Eight lanes per dot product (the group `grp` of lane `sub`, 16
+            // bf16 pairs each, then a 3-level DPP sum), so a wave forms eight
+            // at once.
             if (!abort) {
-                for (int r = wave; r < kERows; r += kChainWaves) {
-                    const uint32_t* er = r < kCandMax ? sc.cw1[r] : r == kERowAnchor ? sc.e0 : sc.fw1[r - kERowForced];
+                const auto erow = [&](int r) -> const uint32_t* {
+                    return r < kCandMax ? sc.cw1[r] : r == kERowAnchor ? sc.e0 : sc.fw1[r - kERowForced];
+                };
+                const auto dot16 = [&](const uint32_t* x, const uint32_t* y) {
+                    float a = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint4 xv = reinterpret_cast<const uint4*>(x + sub * 16)[q];
+                        const uint4 yv = reinterpret_cast<const uint4*>(y + sub * 16)[q];
+                        a = dot2(xv.x, yv.x, a), a = dot2(xv.y, yv.y, a), a = dot2(xv.z, yv.z, a), a = dot2(xv.w, yv.w, a);
+                    }
+                    return sum8(a);
+                };
+                for (int r = grp; r < kERows; r += kChainGroups) {  // group-uniform
                     const bool use = r < nc || r == kERowAnchor ||
                                      (r >= kERowForced && r - kERowForced < gamma && sc.fv[r - kERowForced] >= 0 &&
                                       sc.fv[r - kERowForced] < V);
                     if (!use) continue;
-                    const uint32_t ex = er[2 * lane], ey = er[2 * lane + 1];
-                    const float es = wave_sum_f32(dot2(ey, ey, dot2(ex, ex, 0.f)));
-                    const float zc = wave_sum_f32(dot2(we_lds[2 * lane + 1], ey, dot2(we_lds[2 * lane], ex, 0.f)));
-                    if (lane == 0) sc.esq[r] = es, sc.zcm[r] = zc;
+                    const uint32_t* er = erow(r);
+                    const float es = dot16(er, er);
+                    const float zc = dot16(we_lds, er);
+                    if (sub == 0) sc.esq[r] = es, sc.zcm[r] = zc;
                 }
+                // candidate j of wave j % 8; its group g takes predecessors
+                // g, g + 8, ... (in bit order)
+                const int g8 = lane >> 3;
                 for (int j = wave; j < nc; j += kChainWaves) {
                     const int k = sc.cstep[j];
                     uint64_t preds;  // e rows that can be e at step k
                     if (k == 0) preds = 1ull << kERowAnchor;
                     else if (sc.fv[k - 1] >= 0) preds = 1ull << (kERowForced + k - 1);
                     else preds = sc.stepmask[k - 1];
-                    const uint32_t wx = sc.cw2[j][2 * lane], wy = sc.cw2[j][2 * lane + 1];
-                    while (preds) {
+                    for (int t = 0; t < g8; ++t) preds &= preds - 1;
+                    while (preds) {  // group-uniform
                         const int r = __builtin_ctzll(preds);
-                        preds &= preds - 1;
-                        const uint32_t* er = r < kCandMax ? sc.cw1[r] : r == kERowAnchor ? sc.e0 : sc.fw1[r - kERowForced];
-                        const float b = wave_sum_f32(dot2(wy, er[2 * lane + 1], dot2(wx, er[2 * lane], 0.f)));
-                        if (lane == 0) sc.bias[j][r] = b;
+                        const float b = dot16(sc.cw2[j], erow(r));
+                        if (sub == 0) sc.bias[j][r] = b;
+                        for (int t = 0; t < 8; ++t) preds &= preds - 1;
                     }
                 }
             }

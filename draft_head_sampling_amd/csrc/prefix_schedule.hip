@@ -13,10 +13,11 @@
 //   2. with every confidence in [0, 1] a product never grows, so each
 //      request's run of values is already ascending: the global order is a
 //      stable merge of the B runs (ties stay in request and position order).
-//      The runs are merged pairwise in LDS, level by level, each thread
-//      writing a few consecutive outputs after one binary search (merge
-//      path).  If some run is not ascending (a confidence above 1), the merge
-//      starts from runs of one pair instead: a plain merge sort, same order;
+//      The runs are merged pairwise in LDS, level by level; each pair finds
+//      its place in the merged run with one binary search in the other run
+//      and moves there.  If some run is not ascending (a confidence outside
+//      [0, 1]), the merge starts from runs of one pair instead: a plain merge
+//      sort, same order;
 //   3. Theta for every prefix of the sorted list from a binary64 prefix sum.
 //      When every summand is a multiple of 2^q and every partial sum stays
 //      below 2^(q+53), binary64 addition is exact in any order, so the
@@ -36,6 +37,12 @@ namespace {
 constexpr int kNT = 1024;
 constexpr int kMaxPairs = 8192;
 constexpr int kPer = kMaxPairs / kNT;  // sorted positions owned by each thread
+constexpr int kConfChunk = 16;         // confidences loaded together per request
+#ifndef DSPARK_SORT_SCALE
+#define DSPARK_SORT_SCALE 1
+#endif
+constexpr int kSortScale = DSPARK_SORT_SCALE;  // outputs per sorting thread, times the minimum
+static_assert(kPer == 8, "the owned keys are read as two 16-byte loads");
 
 __device__ __forceinline__ float val_survival(uint32_t v) { return from_orderable(~v); }
 
@@ -72,6 +79,245 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T* wsum, T& total) {
     return off;
 }
 
+// Sort key of a survival: the complemented orderable bits, so ascending
+// keys are descending survivals.  -0 and +0 are equal survivals: the order
+// uses the key of +0 for both, so their pairs stay in request order.
+__device__ __forceinline__ uint32_t canon_key(uint32_t v) { return v == 0x80000000u ? 0x7fffffffu : v; }
+
+constexpr int kPad = 16;  // slack after each key and id row: window reads may run a few entries past n
+using KeyRows = uint32_t (*)[kMaxPairs + kPad];
+using IdRows = uint16_t (*)[kMaxPairs + kPad];
+
+// The two runs of one merge, first level: run A is request ra and run B
+// request ra + 1 (rb addresses it, clamped to a real request), read from the
+// transposed keys; pair ids follow from the position.
+struct TransposedPair {
+    const uint32_t* scr;
+    int ts, g, ra, rb;
+    __device__ uint32_t ka(int i) const { return canon_key(scr[(i < g ? i : g - 1) * ts + ra]); }
+    __device__ uint32_t kb(int j) const { return canon_key(scr[(j < g ? j : g - 1) * ts + rb]); }
+    // the pair id of A[i] or B[j]
+    __device__ int code_a(int i) const { return ra * g + i; }
+    __device__ int code_b(int j) const { return (ra + 1) * g + j; }
+    __device__ uint16_t id_of(int c) const { return (uint16_t)c; }
+};
+// Later levels: run A at a[sa..], run B at a[sb..] (sb <= n), ids beside them.
+// Reads past a run stay inside the padded row.
+struct NaturalPair {
+    const uint32_t* a;
+    const uint16_t* ai;
+    int sa, sb;
+    __device__ uint32_t ka(int i) const { return a[sa + i]; }
+    __device__ uint32_t kb(int j) const { return a[sb + j]; }
+    // the row position of A[i] or B[j]; its pair id is read from there
+    __device__ int code_a(int i) const { return sa + i; }
+    __device__ int code_b(int j) const { return sb + j; }
+    __device__ uint16_t id_of(int c) const { return ai[c]; }
+};
+
+template <int KC>
+__device__ __forceinline__ void store_run(uint32_t* d, uint16_t* di, const uint32_t (&v)[KC], const uint16_t (&id)[KC]) {
+    if constexpr (KC == 1) {
+        d[0] = v[0];
+        di[0] = id[0];
+    } else if constexpr (KC == 2) {
+        *reinterpret_cast<uint2*>(d) = make_uint2(v[0], v[1]);
+        *reinterpret_cast<uint32_t*>(di) = (uint32_t)id[0] | ((uint32_t)id[1] << 16);
+    } else {
+#pragma unroll
+        for (int k = 0; k < KC; k += 4) {
+            *reinterpret_cast<uint4*>(d + k) = make_uint4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+            *reinterpret_cast<uint2*>(di + k) = make_uint2((uint32_t)id[k] | ((uint32_t)id[k + 1] << 16),
+                                                           (uint32_t)id[k + 2] | ((uint32_t)id[k + 3] << 16));
+        }
+    }
+}
+
+// Outputs dg .. dg+KC-1 of the merge of sorted runs A (lenA >= 1 keys) and B
+// (lenB keys), equal keys from A first (merge path): a binary search finds
+// how many of the first dg outputs come from A, the next KC keys of each run
+// are read together, merged in registers, and written with vector stores at
+// d, di (outputs past the end of the merged run are don't-cares).
+template <int KC, typename Pair>
+__device__ __forceinline__ void merge_path(const Pair& P, int lenA, int lenB, int dg, uint32_t* d, uint16_t* di) {
+    int lo = dg - lenB > 0 ? dg - lenB : 0;
+    int hi = dg < lenA ? dg : lenA;
+    while (lo < hi) {
+        const int i = (lo + hi) >> 1;
+        if (P.ka(i) <= P.kb(dg - i - 1)) lo = i + 1;
+        else hi = i;
+    }
+    int pa = lo, pb = dg - lo;
+    uint32_t wa[KC], wb[KC];
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+        wa[k] = P.ka(pa + k);
+        wb[k] = P.kb(pb + k);
+    }
+    uint32_t ov[KC];
+    uint16_t oid[KC];
+    int oc[KC];
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+        const bool take_a = (pa < lenA) & ((pb >= lenB) | (wa[0] <= wb[0]));
+        ov[k] = take_a ? wa[0] : wb[0];
+        oc[k] = take_a ? P.code_a(pa) : P.code_b(pb);
+        pa += (int)take_a;
+        pb += (int)!take_a;
+#pragma unroll
+        for (int t = 0; t + 1 + k < KC; ++t) {
+            wa[t] = take_a ? wa[t + 1] : wa[t];
+            wb[t] = take_a ? wb[t] : wb[t + 1];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < KC; ++k) oid[k] = P.id_of(oc[k]);
+    store_run<KC>(d, di, ov, oid);
+}
+
+// Stable sort of the n pair keys (ascending; equal keys in pair-id order).
+// Each level merges runs of m pairwise.  Every pair id of a left run is
+// below every pair id of its right run and equal keys take the left run
+// first, so the order of equal keys is pair-id order.  With 2m a multiple of
+// KC, thread t writes the KC consecutive outputs t*KC.. of one merged run
+// (merge_path); otherwise (odd gamma at the first level) each thread moves
+// the pairs t, t + kNT, ..., each to its index in its own run plus the
+// number of pairs of the other run that go before it (smaller keys, and
+// equal ones too when it is in the right run), found by one binary search
+// whose probes are plain loads feeding selects.
+//
+// The keys arrive transposed in vals[0] (pair (r, j) at j * ts + r).  The
+// first level reads them there and, with sorted runs, merges requests 2k and
+// 2k+1 (m = gamma); otherwise it only lays the pairs out in request-major
+// order and the merge starts from runs of one.  The first level also writes
+// the survival output, coalesced.  Returns the row holding the result.
+template <int KC>
+__device__ int sort_pairs(int n, int g, int B, int ts, bool runs_sorted, float* __restrict__ surv_out, KeyRows vals,
+                          IdRows pids) {
+    const int tid = threadIdx.x;
+    const uint32_t* scr = vals[0];
+    if (surv_out) {
+#pragma unroll
+        for (int q = 0; q < KC; ++q) {
+            const int e = tid + kNT * q;
+            if (e < n) {
+                const int r = e / g;
+                surv_out[e] = from_orderable(~scr[(e - r * g) * ts + r]);  // the exact survival, sign included
+            }
+        }
+    }
+    if (runs_sorted && (2 * g) % KC == 0) {
+        const int o0 = tid * KC;
+        if (o0 < n) {
+            const int ra = (o0 / (2 * g)) * 2;
+            const TransposedPair P{scr, ts, g, ra, ra + 1 < B ? ra + 1 : ra};
+            merge_path<KC>(P, g, ra + 1 < B ? g : 0, o0 - ra * g, vals[1] + o0, pids[1] + o0);
+        }
+    } else {
+        uint32_t x[KC];
+        int cnt[KC], rq[KC], jq[KC];
+        bool act[KC];
+#pragma unroll
+        for (int q = 0; q < KC; ++q) {
+            const int e = tid + kNT * q;
+            act[q] = e < n;
+            rq[q] = act[q] ? e / g : 0;
+            jq[q] = act[q] ? e - rq[q] * g : 0;
+            x[q] = canon_key(scr[jq[q] * ts + rq[q]]);
+            cnt[q] = 0;
+        }
+        if (runs_sorted && B > 1) {
+            int top = 1;
+            while (2 * top <= g) top *= 2;
+            for (int st = top; st > 0; st >>= 1) {
+#pragma unroll
+                for (int q = 0; q < KC; ++q) {
+                    const int sr = rq[q] ^ 1;
+                    const bool right = (rq[q] & 1) != 0;
+                    const int jn = cnt[q] + st;
+                    const bool ok = (sr < B) & (jn <= g);
+                    const uint32_t y = canon_key(scr[(ok ? jn - 1 : 0) * ts + (ok ? sr : rq[q])]);
+                    const bool take = ok & ((y < x[q]) | (right & (y == x[q])));
+                    cnt[q] = take ? jn : cnt[q];
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < KC; ++q) {
+            const int e = tid + kNT * q;
+            if (act[q]) {
+                const int pos = runs_sorted ? (rq[q] & ~1) * g + jq[q] + cnt[q] : e;
+                vals[1][pos] = x[q];
+                pids[1][pos] = (uint16_t)e;
+            }
+        }
+    }
+    __syncthreads();
+    int src = 1;
+    const int unit = runs_sorted ? g : 1;  // pairs per run after the first level
+    const int o0 = tid * KC;
+    const int ou = o0 / unit;  // first output in units of the first level's runs
+    int lvl = runs_sorted ? 1 : 0;
+    for (int m = unit << lvl; m < n; m *= 2, ++lvl) {
+        const uint32_t* a = vals[src];
+        const uint16_t* ai = pids[src];
+        uint32_t* d = vals[src ^ 1];
+        uint16_t* di = pids[src ^ 1];
+        if ((2 * m) % KC == 0) {
+            if (o0 < n) {
+                const int s0 = ((ou >> (lvl + 1)) << (lvl + 1)) * unit;  // floor(o0 / 2m) * 2m
+                const int mid = s0 + m < n ? s0 + m : n;
+                const int end = s0 + 2 * m < n ? s0 + 2 * m : n;
+                const NaturalPair P{a, ai, s0, mid};
+                merge_path<KC>(P, mid - s0, end - mid, o0 - s0, d + o0, di + o0);
+            }
+        } else {
+            uint32_t x[KC];
+            uint16_t id[KC];
+            int cnt[KC], sb[KC], sl[KC], run[KC];
+            bool right[KC];
+#pragma unroll
+            for (int q = 0; q < KC; ++q) {
+                const int e = tid + kNT * q;
+                const bool act = e < n;
+                run[q] = (e / unit) >> lvl;
+                const int s0 = run[q] * m;
+                right[q] = (run[q] & 1) != 0;
+                sb[q] = right[q] ? s0 - m : s0 + m;
+                const int rest = n - sb[q];
+                sl[q] = !act ? 0 : (right[q] ? m : (rest < m ? (rest > 0 ? rest : 0) : m));
+                x[q] = a[act ? e : 0];
+                id[q] = ai[act ? e : 0];
+                cnt[q] = 0;
+            }
+            int top = 1;
+            while (2 * top <= m) top *= 2;
+            for (int st = top; st > 0; st >>= 1) {
+#pragma unroll
+                for (int q = 0; q < KC; ++q) {
+                    const int jn = cnt[q] + st;
+                    const bool ok = jn <= sl[q];
+                    const uint32_t y = a[ok ? sb[q] + jn - 1 : 0];
+                    const bool take = ok & ((y < x[q]) | (right[q] & (y == x[q])));
+                    cnt[q] = take ? jn : cnt[q];
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < KC; ++q) {
+                const int e = tid + kNT * q;
+                if (e < n) {
+                    const int pos = (run[q] & ~1) * m + (e - run[q] * m) + cnt[q];
+                    d[pos] = x[q];
+                    di[pos] = id[q];
+                }
+            }
+        }
+        __syncthreads();
+        src ^= 1;
+    }
+    return src;
+}
+
 __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t gamma, const float* __restrict__ conf,
                                                               const double* __restrict__ sps, int64_t n_sps,
                                                               float exact_floor, int32_t* __restrict__ prefix_len,
@@ -79,8 +325,8 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
                                                               int32_t* __restrict__ order_out,
                                                               double* __restrict__ theta_out,
                                                               int32_t* __restrict__ nsel_out) {
-    __shared__ uint32_t vals[2][kMaxPairs];  // ~orderable(survival): ascending = survival descending
-    __shared__ uint16_t pids[2][kMaxPairs];  // pair id r * gamma + j of each value
+    __shared__ __align__(16) uint32_t vals[2][kMaxPairs + kPad];  // sort keys (canon_key): ascending = survival descending
+    __shared__ __align__(16) uint16_t pids[2][kMaxPairs + kPad];  // pair id r * gamma + j of each key
     __shared__ double wsum[2 * kNT / 64];
     __shared__ uint32_t wpar[kNT / 64];
     __shared__ int stop_pos, n_exact, unsorted;
@@ -91,39 +337,49 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
     const int n = (int)(B * gamma);
     const int g = (int)gamma;
     // Thread t owns sorted positions first+1 .. first+kPer.  Their table
-    // entries (and the one before) do not depend on the sort: fetch them now.
+    // entries (and the one before) do not depend on the sort: fetch them now
+    // (B >= 1 and n_sps >= B, so the clamped index is always in the table).
     const int first = tid * kPer;
     double spv[kPer + 1];
 #pragma unroll
     for (int q = 0; q <= kPer; ++q) {
         const int64_t i = B + first - 1 + q;
-        spv[q] = i < n_sps ? sps[i] : 0.0;
+        const double v = sps[i < n_sps ? i : n_sps - 1];
+        spv[q] = i < n_sps ? v : 0.0;
     }
 
     if (tid == 0) stop_pos = 0x7fffffff, n_exact = 0, unsorted = 0;
     __syncthreads();
+    // Keys of the request-major pairs, transposed: pair (r, j) sits at
+    // j * ts + r, so a wave of consecutive requests stores to consecutive
+    // words, and a wave of consecutive positions of one request (stride ts,
+    // odd when it fits) reads from distinct banks.
+    const int ts = (((int)B | 1) * g <= kMaxPairs) ? ((int)B | 1) : (int)B;
+    uint32_t* scr = vals[0];
     if (g > 0) {
         // One thread per request, left to right (the same association as
-        // the sequential product); the confidences come straight from
-        // global memory, eight independent loads at a time.
+        // the sequential product); its confidences are loaded sixteen at a
+        // time, all in flight together.  The stored key keeps the sign of a
+        // zero survival (for the survival output); the order uses the key of
+        // +0 for both zeros (see canon_key).
         for (int r = tid; r < (int)B; r += kNT) {
             float p = 1.f;
             uint32_t prev = 0;
             bool up = true;
-            for (int j0 = 0; j0 < g; j0 += 8) {
-                float c[8];
+            const float* cr = conf + (int64_t)r * g;
+            for (int j0 = 0; j0 < g; j0 += kConfChunk) {
+                float c[kConfChunk];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) c[j] = j0 + j < g ? conf[r * g + j0 + j] : 1.f;
+                for (int j = 0; j < kConfChunk; ++j) c[j] = cr[j0 + j < g ? j0 + j : g - 1];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
+                for (int j = 0; j < kConfChunk; ++j) {
                     if (j0 + j < g) {
-                        const int pid = r * g + j0 + j;
                         p = p * c[j];
                         const uint32_t v = ~orderable(p);
-                        up = up && v >= prev;
-                        prev = v;
-                        vals[0][pid] = v;
-                        pids[0][pid] = (uint16_t)pid;
+                        const uint32_t vc = canon_key(v);
+                        up = up && vc >= prev;
+                        prev = vc;
+                        scr[(j0 + j) * ts + r] = v;
                     }
                 }
             }
@@ -131,64 +387,17 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
         }
     }
     __syncthreads();
-    if (surv_out)  // the survival is recovered exactly from its key
-        for (int i = tid; i < n; i += kNT) surv_out[i] = val_survival(vals[0][i]);
 
-    // Merge levels: runs of m pairs merged pairwise, ping-ponging between the
-    // buffers.  The merge is stable (on equal values the left run goes
-    // first), and every pair id of a left run is below every pair id of its
-    // right run, so sorting the values gives the order (survival desc,
-    // request asc, position asc).  A thread writes kc consecutive outputs: a
-    // binary search finds how many of the first outputs of its merged run come
-    // from the left run, then it merges forward with both run heads in
-    // registers.
+    // Sort (see sort_pairs); kc pairs per thread at most.
     const int kc = (n + kNT - 1) / kNT;
-    int src = 0;
-    for (int m = unsorted ? 1 : g; m > 0 && m < n; m *= 2) {
-        const uint32_t* a = vals[src];
-        const uint16_t* ai = pids[src];
-        uint32_t* d = vals[src ^ 1];
-        uint16_t* di = pids[src ^ 1];
-        const int o0 = tid * kc;
-        if (o0 < n) {
-            int s0 = (o0 / (2 * m)) * (2 * m);
-            int mid = s0 + m < n ? s0 + m : n, end = s0 + 2 * m < n ? s0 + 2 * m : n;
-            const int dg = o0 - s0;
-            int lo = dg - (end - mid) > 0 ? dg - (end - mid) : 0;
-            int hi = dg < mid - s0 ? dg : mid - s0;
-            while (lo < hi) {
-                const int i = (lo + hi) >> 1;
-                if (a[s0 + i] <= a[mid + dg - i - 1]) lo = i + 1;
-                else hi = i;
-            }
-            int ia = s0 + lo, ib = mid + dg - lo;
-            uint32_t va = ia < mid ? a[ia] : 0u, vb = ib < end ? a[ib] : 0u;
-            for (int k = 0; k < kc && o0 + k < n; ++k) {
-                const int o = o0 + k;
-                if (o == end) {  // the next merged run starts
-                    s0 = end;
-                    mid = s0 + m < n ? s0 + m : n;
-                    end = s0 + 2 * m < n ? s0 + 2 * m : n;
-                    ia = s0;
-                    ib = mid;
-                    va = ia < mid ? a[ia] : 0u;
-                    vb = ib < end ? a[ib] : 0u;
-                }
-                if (ia < mid && (ib >= end || va <= vb)) {
-                    d[o] = va;
-                    di[o] = ai[ia];
-                    ++ia;
-                    va = ia < mid ? a[ia] : 0u;
-                } else {
-                    d[o] = vb;
-                    di[o] = ai[ib];
-                    ++ib;
-                    vb = ib < end ? a[ib] : 0u;
-                }
-            }
-        }
-        __syncthreads();
-        src ^= 1;
+    const bool runs_sorted = !unsorted;  // workgroup-uniform after the barrier
+    int src = 1;
+    if (g > 0) {
+        const int kw = kc * kSortScale;
+        if (kw <= 1) src = sort_pairs<1>(n, g, (int)B, ts, runs_sorted, surv_out, vals, pids);
+        else if (kw <= 2) src = sort_pairs<2>(n, g, (int)B, ts, runs_sorted, surv_out, vals, pids);
+        else if (kw <= 4) src = sort_pairs<4>(n, g, (int)B, ts, runs_sorted, surv_out, vals, pids);
+        else src = sort_pairs<8>(n, g, (int)B, ts, runs_sorted, surv_out, vals, pids);
     }
     const uint32_t* keys = vals[src];
     const uint16_t* ids = pids[src];
@@ -196,8 +405,17 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
 
     // Positions p = 1..n_lim may be accepted (the batch B + p must be in the table).
     const int n_lim = (int)((n_sps - B) < (int64_t)n ? (n_sps - B) : (int64_t)n);
+    // The keys of the owned positions, read once (two 16-byte loads).
+    uint32_t kv[kPer];
+    {
+        const uint4 k0 = *reinterpret_cast<const uint4*>(keys + first);
+        const uint4 k1 = *reinterpret_cast<const uint4*>(keys + first + 4);
+        kv[0] = k0.x, kv[1] = k0.y, kv[2] = k0.z, kv[3] = k0.w;
+        kv[4] = k1.x, kv[5] = k1.y, kv[6] = k1.z, kv[7] = k1.w;
+    }
     int my_ex = 0;
-    for (int i = tid; i < n; i += kNT) my_ex += val_survival(keys[i]) >= exact_floor ? 1 : 0;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) my_ex += (first + q < n && val_survival(kv[q]) >= exact_floor) ? 1 : 0;
     for (int o = 32; o > 0; o >>= 1) my_ex += __shfl_xor(my_ex, o);
     if (lane == 0 && my_ex) atomicAdd(&n_exact, my_ex);
     if (order_out)
@@ -213,7 +431,7 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
     double local = 0.0;
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
-        inc[q] = (first + q < P) ? (double)val_survival(keys[first + q]) : 0.0;
+        inc[q] = (first + q < P) ? (double)val_survival(kv[q]) : 0.0;
         local += inc[q];
     }
     double S = 0.0;
@@ -270,7 +488,7 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
         for (int q = 0; q < kPer; ++q) {
             const int p = first + q + 1;
             if (p > P && p <= n_lim) {
-                const double A = (double)val_survival(keys[p - 1]) * inv_u;
+                const double A = (double)val_survival(kv[q]) * inv_u;
                 const double fl = floor(A), fr = A - fl;
                 bad |= !(A >= 0.0 && A < 0x1p40) ? 1 : 0;
                 const bool tie = fr == 0.5;

@@ -95,3 +95,29 @@ def test_tail_ties_and_binade_crossings_finish_in_order():
     conf[0, 1] = np.float32(2.0**-24)
     r = _check(conf, synth.sps_table(80, "tokens"))
     assert r["n_selected"] == 64
+
+
+@pytest.mark.parametrize("B,gamma,seed", [(300, 9, 11), (257, 16, 12), (1000, 7, 13), (8192, 1, 14), (2, 4096, 15),
+                                          (3, 2730, 16), (1, 8192, 17), (640, 12, 18)])
+def test_many_workgroup_tiles_and_ragged_pair_counts(B, gamma, seed):
+    """Pair counts that span several 1024-pair slices with a ragged last one,
+    odd and even request counts (the transposed key layout pads the request
+    stride only when it fits), one request or one position per request, and
+    survivals rounded to eighths so that many pairs tie."""
+    rng = np.random.default_rng(seed)
+    conf = (1 / (1 + np.exp(-rng.normal(1.5, 1.5, (B, gamma))))).astype(np.float32)
+    if seed % 2 == 0:
+        conf = (np.round(conf * 8) / 8).astype(np.float32)
+    n = B * gamma
+    _check(conf, synth.sps_table(B + n, "steps"))
+    _check(conf, synth.sps_table(B + n // 2 + 1, "tokens"))
+
+
+def test_signed_zero_confidences_tie_with_zero():
+    """-0 is a confidence in [0, 1] equal to 0: its pairs tie with those of
+    +0 survivals and keep request and position order; the survival written
+    out keeps the product's sign."""
+    conf = np.array([[-0.0, -0.0, 0.5], [0.0, 0.5, 1.0], [0.3, -0.0, 1.0], [0.9, 0.0, -0.0]], np.float32)
+    for k in (4, 8, 16):
+        _check(conf, synth.sps_table(k, "tokens"))
+        _check(conf, np.ones(k))

@@ -24,8 +24,11 @@
 //      parallel scan equals the sequential running sum bit for bit.  Sorted
 //      survivals at or above 2^(ceil(log2(B(1+gamma)+1)) - 30) satisfy this
 //      (they are multiples of 2^(e-23) and tau <= B(1+gamma)); the scan
-//      covers that leading run in parallel and one wave finishes any
-//      remaining pairs in sorted order, 64 at a time from registers;
+//      covers that leading run in parallel.  Past it the running sum stays
+//      exact in parallel as integer multiples of one binary64 step (see the
+//      tail below); only a sum that crosses a power of two, or a value that
+//      is not finite, leaves the rest to one wave, pair by pair in sorted
+//      order, 64 at a time from registers;
 //   4. the stop is the first prefix whose Theta does not exceed its
 //      predecessor's (or the table's end); prefix lengths count the accepted
 //      pairs per request in LDS.
@@ -53,9 +56,13 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
     return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int o) {
-    const uint32_t lo = __shfl_up((uint32_t)v, o), hi = __shfl_up((uint32_t)(v >> 32), o);
-    return ((uint64_t)hi << 32) | lo;
+// Lowers *stop to the wave's first stopping position: threads own positions
+// in lane order, so the lowest lane that stopped holds the wave's minimum and
+// one atomic per wave suffices (with every lane's atomic, thousands of them
+// serialise on the one LDS word).
+__device__ __forceinline__ void wave_stop(int my_stop, int lane, int* stop) {
+    const uint64_t b = __ballot(my_stop != 0x7fffffff);
+    if (b != 0 && lane == __ffsll((unsigned long long)b) - 1) atomicMin(stop, my_stop);
 }
 
 // Exclusive prefix sum of one value per thread across the workgroup, and the
@@ -329,9 +336,10 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
     __shared__ __align__(16) uint16_t pids[2][kMaxPairs + kPad];  // pair id r * gamma + j of each key
     __shared__ double wsum[2 * kNT / 64];
     __shared__ uint32_t wpar[kNT / 64];
-    __shared__ int stop_pos, n_exact, unsorted;
+    __shared__ int stop_pos, n_exact;
+    __shared__ int wunsorted[kNT / 64];  // per wave: some run of this wave's requests is not ascending
     __shared__ double tail_theta;
-    __shared__ int tail_nsel, tail_mode;
+    __shared__ int tail_nsel;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = (int)(B * gamma);
@@ -348,29 +356,51 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
         spv[q] = i < n_sps ? v : 0.0;
     }
 
-    if (tid == 0) stop_pos = 0x7fffffff, n_exact = 0, unsorted = 0;
-    __syncthreads();
+    // (first read after the barrier that ends the survival phase)
+    if (tid == 0) stop_pos = 0x7fffffff, n_exact = 0;
     // Keys of the request-major pairs, transposed: pair (r, j) sits at
     // j * ts + r, so a wave of consecutive requests stores to consecutive
     // words, and a wave of consecutive positions of one request (stride ts,
     // odd when it fits) reads from distinct banks.
     const int ts = (((int)B | 1) * g <= kMaxPairs) ? ((int)B | 1) : (int)B;
     uint32_t* scr = vals[0];
+    bool all_up = true;
     if (g > 0) {
-        // One thread per request, left to right (the same association as
-        // the sequential product); its confidences are loaded sixteen at a
-        // time, all in flight together.  The stored key keeps the sign of a
-        // zero survival (for the survival output); the order uses the key of
-        // +0 for both zeros (see canon_key).
+        // The confidences, coalesced (four per thread per 16-byte load when
+        // the array is 16-byte aligned), into the transposed layout...
+        const bool vec = ((uintptr_t)conf & 15) == 0;
+        for (int e0 = 4 * tid; e0 < n; e0 += 4 * kNT) {
+            float c[4];
+            if (vec && e0 + 4 <= n) {
+                const float4 v = *reinterpret_cast<const float4*>(conf + e0);
+                c[0] = v.x, c[1] = v.y, c[2] = v.z, c[3] = v.w;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) c[k] = e0 + k < n ? conf[e0 + k] : 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int e = e0 + k;
+                if (e < n) {
+                    const int r = e / g;
+                    scr[(e - r * g) * ts + r] = __float_as_uint(c[k]);
+                }
+            }
+        }
+        __syncthreads();
+        // ...then one thread per request, left to right (the same association
+        // as the sequential product), each key replacing its confidence.  The
+        // stored key keeps the sign of a zero survival (for the survival
+        // output); the order uses the key of +0 for both zeros (see
+        // canon_key).
         for (int r = tid; r < (int)B; r += kNT) {
             float p = 1.f;
             uint32_t prev = 0;
             bool up = true;
-            const float* cr = conf + (int64_t)r * g;
             for (int j0 = 0; j0 < g; j0 += kConfChunk) {
                 float c[kConfChunk];
 #pragma unroll
-                for (int j = 0; j < kConfChunk; ++j) c[j] = cr[j0 + j < g ? j0 + j : g - 1];
+                for (int j = 0; j < kConfChunk; ++j) c[j] = __uint_as_float(scr[(j0 + j < g ? j0 + j : g - 1) * ts + r]);
 #pragma unroll
                 for (int j = 0; j < kConfChunk; ++j) {
                     if (j0 + j < g) {
@@ -383,14 +413,18 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
                     }
                 }
             }
-            if (!up) unsorted = 1;
+            all_up = all_up && up;
         }
+    }
+    {
+        const bool wave_unsorted = __ballot(!all_up) != 0;
+        if (lane == 0) wunsorted[wave] = wave_unsorted ? 1 : 0;
     }
     __syncthreads();
 
     // Sort (see sort_pairs); kc pairs per thread at most.
     const int kc = (n + kNT - 1) / kNT;
-    const bool runs_sorted = !unsorted;  // workgroup-uniform after the barrier
+    const bool runs_sorted = __ballot(lane < kNT / 64 && wunsorted[lane < kNT / 64 ? lane : 0] != 0) == 0;  // uniform
     int src = 1;
     if (g > 0) {
         const int kw = kc * kSortScale;
@@ -443,6 +477,7 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
     {
         double tau_prev = Bd + offset;  // tau after position first (first <= P)
         double th_prev = tau_prev * spv[0];
+        int my_stop = 0x7fffffff;
 #pragma unroll
         for (int q = 0; q < kPer; ++q) {
             const int p = first + q + 1;
@@ -450,12 +485,13 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
             const double tau = tau_prev + inc[q];
             const double th = tau * spv[q + 1];
             if (!(th > th_prev)) {
-                atomicMin(&stop_pos, p);
+                my_stop = p;
                 break;
             }
             tau_prev = tau;
             th_prev = th;
         }
+        wave_stop(my_stop, lane, &stop_pos);
     }
     __syncthreads();
 
@@ -466,13 +502,14 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
     // floor(A) or floor(A) + 1 by the fraction of A, and at a tie (fraction
     // exactly 1/2) the one that makes T even.  So the running sum needs only
     // the parity of T before each tie: after a tie T is even, elsewhere the
-    // parity flips with each odd increment -- a segmented XOR scan.  Then an
-    // exact prefix sum of the increments (integers below 2^40 in binary64)
-    // gives tau at every position at once, equal to the sequential running
-    // sum.  A binade crossing or a non-finite value sends the tail to the
-    // one-wave sequential finish instead.  inc[q] becomes the rounded
-    // increment of an owned position p > P.  Skipped when the scan already
-    // stopped inside the exact run.
+    // parity flips with each odd increment -- a segmented XOR scan, needed
+    // only when some increment is a tie.  Then an exact prefix sum of the
+    // increments (integers below 2^40 in binary64) gives tau at every
+    // position at once, equal to the sequential running sum.  A binade
+    // crossing or a non-finite value sends the tail to the one-wave
+    // sequential finish instead.  inc[q] becomes the rounded increment of an
+    // owned position p > P.  Skipped when the scan already stopped inside
+    // the exact run.
     const bool need_tail = stop_pos == 0x7fffffff && P < n_lim;  // workgroup-uniform
     double u = 0.0, roff = 0.0;
     bool tail_ok = true;
@@ -484,6 +521,7 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
         uint32_t tiemask = 0;  // owned positions with a tie
         uint32_t xr = 0;       // parity of the odd increments since the last owned tie
         int bad = 0;
+        double rloc = 0.0;     // sum of the increments, ties counted at floor(A) for now
 #pragma unroll
         for (int q = 0; q < kPer; ++q) {
             const int p = first + q + 1;
@@ -496,57 +534,97 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
                 const uint32_t odd = (uint32_t)((uint64_t)fl & 1) ^ (fr > 0.5 ? 1u : 0u);
                 tiemask |= tie ? (1u << q) : 0u;
                 xr = tie ? 0u : xr ^ odd;
-            }
-        }
-        // exclusive segmented scan of (parity, has tie) over threads in position order
-        uint32_t x = xr, t = tiemask ? 1u : 0u;
-        for (int o = 1; o < 64; o <<= 1) {  // inclusive within the wave
-            const uint32_t xo = __shfl_up(x, o), to = __shfl_up(t, o);
-            if (lane >= o) {
-                x = t ? x : (xo ^ x);
-                t = t | to;
-            }
-        }
-        if (lane == 63) wpar[wave] = (x << 1) | t;
-        const uint32_t xe = __shfl_up(x, 1), te = __shfl_up(t, 1);  // exclusive within the wave
-        __syncthreads();
-        uint32_t px = 0, pt = 0;  // waves before this one
-        for (int w = 0; w < wave; ++w) {
-            const uint32_t wx = wpar[w] >> 1, wt = wpar[w] & 1u;
-            px = wt ? wx : (px ^ wx);
-            pt |= wt;
-        }
-        if (lane > 0) {
-            px = te ? xe : (px ^ xe);
-            pt |= te;
-        }
-        // parity of T before this thread's first tail position
-        uint32_t e = pt ? px : ((uint32_t)((uint64_t)(tauP * inv_u) & 1) ^ px);
-        double rloc = 0.0;
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-            const int p = first + q + 1;
-            if (p > P && p <= n_lim) {
-                if ((tiemask >> q) & 1u) {
-                    const double fl = inc[q];
-                    const uint32_t odd = (e ^ (uint32_t)((uint64_t)fl & 1)) & 1u;
-                    inc[q] = fl + (double)odd;  // T + increment is even
-                    e = 0;
-                } else {
-                    e ^= (uint32_t)((uint64_t)inc[q] & 1);
-                }
                 rloc += inc[q];
             }
         }
+        // One exchange: the wave sums of the increments, whether the wave
+        // saw a non-finite value or a tie, and its parity summary (x = parity
+        // of the odd increments after its last tie, t = it has a tie).
+        double incl = rloc;
+        for (int o = 1; o < 64; o <<= 1) {
+            const double y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        const bool wave_tie = __ballot(tiemask != 0) != 0;
+        uint32_t x = xr, t = tiemask ? 1u : 0u;
+        if (wave_tie) {  // inclusive segmented scan within the wave
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t xo = __shfl_up(x, o), to = __shfl_up(t, o);
+                if (lane >= o) {
+                    x = t ? x : (xo ^ x);
+                    t = t | to;
+                }
+            }
+        } else {  // no tie: the parity of all the wave's odd increments
+            x = (uint32_t)__popcll(__ballot(xr != 0)) & 1u;
+            t = 0;
+        }
+        const bool wave_bad = __ballot(bad != 0) != 0;
+        if (lane == 63) {
+            wsum[kNT / 64 + wave] = incl;
+            wpar[wave] = (wave_bad ? 4u : 0u) | (x << 1) | t;
+        }
+        __syncthreads();
         double Ktot = 0.0;
-        roff = block_exclusive_scan(rloc, wsum + kNT / 64, Ktot);
-        tail_ok = !__syncthreads_or(bad) && tauP + u * Ktot < ldexp(1.0, ebin);
+        roff = incl - rloc;
+        bool any_bad = false, any_tie = false;
+        for (int w = 0; w < kNT / 64; ++w) {
+            const double ws = wsum[kNT / 64 + w];
+            if (w < wave) roff += ws;
+            Ktot += ws;
+            any_bad |= (wpar[w] & 4u) != 0;
+            any_tie |= (wpar[w] & 1u) != 0;
+        }
+        if (any_tie) {
+            // settle the ties from the parity of T before each one; then
+            // the increments' prefix sums again
+            if (!wave_tie) {  // this wave's lanes need their own exclusive parities
+                x = xr;
+                t = 0;
+                for (int o = 1; o < 64; o <<= 1) {
+                    const uint32_t xo = __shfl_up(x, o);
+                    if (lane >= o) x ^= xo;
+                }
+            }
+            const uint32_t xe = __shfl_up(x, 1), te = __shfl_up(t, 1);  // exclusive within the wave
+            uint32_t px = 0, pt = 0;  // waves before this one
+            for (int w = 0; w < wave; ++w) {
+                const uint32_t wx = (wpar[w] >> 1) & 1u, wt = wpar[w] & 1u;
+                px = wt ? wx : (px ^ wx);
+                pt |= wt;
+            }
+            if (lane > 0) {
+                px = te ? xe : (px ^ xe);
+                pt |= te;
+            }
+            // parity of T before this thread's first tail position
+            uint32_t e = pt ? px : ((uint32_t)((uint64_t)(tauP * inv_u) & 1) ^ px);
+            rloc = 0.0;
+#pragma unroll
+            for (int q = 0; q < kPer; ++q) {
+                const int p = first + q + 1;
+                if (p > P && p <= n_lim) {
+                    if ((tiemask >> q) & 1u) {
+                        const double fl = inc[q];
+                        const uint32_t odd = (e ^ (uint32_t)((uint64_t)fl & 1)) & 1u;
+                        inc[q] = fl + (double)odd;  // T + increment is even
+                        e = 0;
+                    } else {
+                        e ^= (uint32_t)((uint64_t)inc[q] & 1);
+                    }
+                    rloc += inc[q];
+                }
+            }
+            roff = block_exclusive_scan(rloc, wsum, Ktot);  // (wsum[0..) is free again)
+        }
+        tail_ok = !any_bad && tauP + u * Ktot < ldexp(1.0, ebin);
 
-        // Theta on past the exact run (every exact position improved)
+        // Theta on past the exact run (stops inside it are recorded above)
         if (tail_ok) {
             double tau_prev = first <= P ? Bd + offset : tauP + u * roff;  // tau after position first
             double th_prev = tau_prev * spv[0];
             double kq = roff;
+            int my_stop = 0x7fffffff;
 #pragma unroll
             for (int q = 0; q < kPer; ++q) {
                 const int p = first + q + 1;
@@ -560,30 +638,33 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
                 }
                 const double th = tau * spv[q + 1];
                 if (p > P && !(th > th_prev)) {
-                    atomicMin(&stop_pos, p);
+                    my_stop = p;
                     break;
                 }
                 tau_prev = tau;
                 th_prev = th;
             }
+            wave_stop(my_stop, lane, &stop_pos);
         }
-        __syncthreads();
     }
+    __syncthreads();  // every stop is in
 
-    if (wave == 0) {
-        int nsel = 0, mode = 0;
-        double theta = 0.0;
-        if (stop_pos != 0x7fffffff) {
-            nsel = stop_pos - 1;  // Theta filled by the owner of position nsel
-        } else if (P == n_lim || tail_ok) {
-            nsel = n_lim;
-        } else {
+    int nsel = 0;
+    bool seq = false;  // workgroup-uniform
+    if (stop_pos != 0x7fffffff) {
+        nsel = stop_pos - 1;  // Theta filled by the owner of position nsel
+    } else if (P == n_lim || tail_ok) {
+        nsel = n_lim;
+    } else {
+        seq = true;
+    }
+    if (seq) {
+        if (wave == 0) {
             // sequential finish beyond the exact run, in sorted order: 64
             // positions per round in registers, walked with lane reads
-            mode = 1;
             double tau = tauP;
-            theta = tau * sps[B + P - 1];
-            nsel = P;
+            double theta = tau * sps[B + P - 1];
+            int ns = P;
             bool go = true;
             for (int base = P; base < n_lim && go; base += 64) {
                 const int p = base + 1 + lane;
@@ -602,16 +683,16 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
                     }
                     tau = t2;
                     theta = th;
-                    nsel = base + 1 + q;
+                    ns = base + 1 + q;
                 }
             }
+            if (lane == 0) tail_nsel = ns, tail_theta = theta;
         }
-        if (lane == 0) tail_nsel = nsel, tail_theta = theta, tail_mode = mode;
+        __syncthreads();
+        nsel = tail_nsel;
+        if (tid == 0 && theta_out) *theta_out = tail_theta;
     }
-    __syncthreads();
-    const int nsel = tail_nsel;
-    if (tid == 0 && tail_mode && theta_out) *theta_out = tail_theta;
-    if (!tail_mode && theta_out) {
+    if (!seq && theta_out) {
         // the owner of position nsel recomputes Theta there
         if (nsel == 0) {
             if (tid == 0) *theta_out = Bd * spv[0];

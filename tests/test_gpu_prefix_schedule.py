@@ -121,3 +121,27 @@ def test_signed_zero_confidences_tie_with_zero():
     for k in (4, 8, 16):
         _check(conf, synth.sps_table(k, "tokens"))
         _check(conf, np.ones(k))
+
+
+@pytest.mark.parametrize("tie_share,seed", [(0.02, 21), (0.2, 22)])
+def test_tail_ties_spread_over_many_waves(tie_share, seed):
+    """Past the exact run the kernel sums rounded increments in parallel and
+    settles ties (a survival exactly half-way between two binary64 steps of
+    the running sum) from the parity of the sum before each one.  Here the
+    exact run is 512 survivals of 0.5 (tau = 768 after it, so one step is
+    2^-43) and the tail holds 7680 pairs over fifteen waves, some requests'
+    second survival a tie (2k+1) 2^-44: the parity must carry across waves
+    with and without ties (13 and 111 ties here, in waves 1-5 and 1-9).
+    """
+    rng = np.random.default_rng(seed)
+    B, g = 512, 16
+    conf = np.empty((B, g), np.float32)
+    conf[:, 0] = 0.5
+    c = np.exp2(rng.uniform(-42, -30, B)).astype(np.float32)  # many bits below one step: hardly ever a tie
+    tie = rng.random(B) < tie_share
+    k = rng.integers(1, 2**10, B)
+    c[tie] = ((2 * k[tie] + 1) * 2.0**-43).astype(np.float32)
+    conf[:, 1] = c
+    conf[:, 2:] = rng.uniform(0.5, 1.0, (B, g - 2)).astype(np.float32)
+    r = _check(conf, synth.sps_table(B + B * g, "tokens"))
+    assert r["n_selected"] == B * g

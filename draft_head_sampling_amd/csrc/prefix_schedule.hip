@@ -65,26 +65,44 @@ __device__ __forceinline__ void wave_stop(int my_stop, int lane, int* stop) {
     if (b != 0 && lane == __ffsll((unsigned long long)b) - 1) atomicMin(stop, my_stop);
 }
 
+// Inclusive prefix sums over lanes 0..kNT/64-1 of one value each (the other
+// lanes hold 0): a tree of additions.
+__device__ __forceinline__ double wave_totals_scan(double ws) {
+    const int lane = threadIdx.x & 63;
+    for (int o = 1; o < kNT / 64; o <<= 1) {
+        const double y = __shfl_up(ws, o);
+        if (lane >= o) ws += y;
+    }
+    return ws;
+}
+
 // Exclusive prefix sum of one value per thread across the workgroup, and the
-// total (every thread gets both).
-template <typename T>
-__device__ __forceinline__ T block_exclusive_scan(T v, T* wsum, T& total) {
+// total (every thread gets both).  The additions form a tree, so the result
+// is the sequential running sum only where binary64 addition is exact in any
+// order -- which is how the scheduler uses it.
+__device__ __forceinline__ double block_exclusive_scan(double v, double* wsum, double& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    T incl = v;
+    double incl = v;
     for (int o = 1; o < 64; o <<= 1) {
-        const T y = __shfl_up(incl, o);
+        const double y = __shfl_up(incl, o);
         if (lane >= o) incl += y;
     }
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
-    T off = incl - v, tot = 0;
-    for (int w = 0; w < kNT / 64; ++w) {
-        if (w < wave) off += wsum[w];
-        tot += wsum[w];
-    }
-    total = tot;
-    return off;
+    const double ws = wave_totals_scan(lane < kNT / 64 ? wsum[lane] : 0.0);
+    total = __shfl(ws, kNT / 64 - 1);
+    return (wave > 0 ? __shfl(ws, wave - 1) : 0.0) + (incl - v);
 }
+
+// q(e) = floor(e / d) for 0 <= e < 2^13 and 1 <= d < 2^21, from a binary32
+// reciprocal: (e + 1/2) / d lies at least 1/(2d) from an integer, and the two
+// roundings move it by at most (e + 1/2)/d * 2^-23 (1 + 2^-24), which is
+// below (2^13 + d) / d * 2^-23 < 1/(2d).
+struct DivSmall {
+    float inv;
+    __device__ explicit DivSmall(int d) : inv(1.f / (float)d) {}
+    __device__ int q(int e) const { return (int)(((float)e + 0.5f) * inv); }
+};
 
 // Sort key of a survival: the complemented orderable bits, so ascending
 // keys are descending survivals.  -0 and +0 are equal survivals: the order
@@ -203,12 +221,13 @@ __device__ int sort_pairs(int n, int g, int B, int ts, bool runs_sorted, float* 
                           IdRows pids) {
     const int tid = threadIdx.x;
     const uint32_t* scr = vals[0];
+    const DivSmall dg(g);
     if (surv_out) {
 #pragma unroll
         for (int q = 0; q < KC; ++q) {
             const int e = tid + kNT * q;
             if (e < n) {
-                const int r = e / g;
+                const int r = dg.q(e);
                 surv_out[e] = from_orderable(~scr[(e - r * g) * ts + r]);  // the exact survival, sign included
             }
         }
@@ -216,7 +235,7 @@ __device__ int sort_pairs(int n, int g, int B, int ts, bool runs_sorted, float* 
     if (runs_sorted && (2 * g) % KC == 0) {
         const int o0 = tid * KC;
         if (o0 < n) {
-            const int ra = (o0 / (2 * g)) * 2;
+            const int ra = DivSmall(2 * g).q(o0) * 2;
             const TransposedPair P{scr, ts, g, ra, ra + 1 < B ? ra + 1 : ra};
             merge_path<KC>(P, g, ra + 1 < B ? g : 0, o0 - ra * g, vals[1] + o0, pids[1] + o0);
         }
@@ -228,7 +247,7 @@ __device__ int sort_pairs(int n, int g, int B, int ts, bool runs_sorted, float* 
         for (int q = 0; q < KC; ++q) {
             const int e = tid + kNT * q;
             act[q] = e < n;
-            rq[q] = act[q] ? e / g : 0;
+            rq[q] = act[q] ? dg.q(e) : 0;
             jq[q] = act[q] ? e - rq[q] * g : 0;
             x[q] = canon_key(scr[jq[q] * ts + rq[q]]);
             cnt[q] = 0;
@@ -263,7 +282,8 @@ __device__ int sort_pairs(int n, int g, int B, int ts, bool runs_sorted, float* 
     int src = 1;
     const int unit = runs_sorted ? g : 1;  // pairs per run after the first level
     const int o0 = tid * KC;
-    const int ou = o0 / unit;  // first output in units of the first level's runs
+    const DivSmall du(unit);
+    const int ou = du.q(o0);  // first output in units of the first level's runs (o0 < 2^13)
     int lvl = runs_sorted ? 1 : 0;
     for (int m = unit << lvl; m < n; m *= 2, ++lvl) {
         const uint32_t* a = vals[src];
@@ -287,7 +307,7 @@ __device__ int sort_pairs(int n, int g, int B, int ts, bool runs_sorted, float* 
             for (int q = 0; q < KC; ++q) {
                 const int e = tid + kNT * q;
                 const bool act = e < n;
-                run[q] = (e / unit) >> lvl;
+                run[q] = du.q(e) >> lvl;
                 const int s0 = run[q] * m;
                 right[q] = (run[q] & 1) != 0;
                 sb[q] = right[q] ? s0 - m : s0 + m;
@@ -369,6 +389,7 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
         // The confidences, coalesced (four per thread per 16-byte load when
         // the array is 16-byte aligned), into the transposed layout...
         const bool vec = ((uintptr_t)conf & 15) == 0;
+        const DivSmall dg(g);
         for (int e0 = 4 * tid; e0 < n; e0 += 4 * kNT) {
             float c[4];
             if (vec && e0 + 4 <= n) {
@@ -382,7 +403,7 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
             for (int k = 0; k < 4; ++k) {
                 const int e = e0 + k;
                 if (e < n) {
-                    const int r = e / g;
+                    const int r = dg.q(e);
                     scr[(e - r * g) * ts + r] = __float_as_uint(c[k]);
                 }
             }
@@ -565,16 +586,13 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
             wpar[wave] = (wave_bad ? 4u : 0u) | (x << 1) | t;
         }
         __syncthreads();
-        double Ktot = 0.0;
-        roff = incl - rloc;
-        bool any_bad = false, any_tie = false;
-        for (int w = 0; w < kNT / 64; ++w) {
-            const double ws = wsum[kNT / 64 + w];
-            if (w < wave) roff += ws;
-            Ktot += ws;
-            any_bad |= (wpar[w] & 4u) != 0;
-            any_tie |= (wpar[w] & 1u) != 0;
-        }
+        // (integers below 2^53: exact in any order)
+        const double ws = wave_totals_scan(lane < kNT / 64 ? wsum[kNT / 64 + lane] : 0.0);
+        const uint32_t wp = lane < kNT / 64 ? wpar[lane] : 0u;
+        double Ktot = __shfl(ws, kNT / 64 - 1);
+        roff = (wave > 0 ? __shfl(ws, wave - 1) : 0.0) + (incl - rloc);
+        const bool any_bad = __ballot((wp & 4u) != 0) != 0;
+        const bool any_tie = __ballot((wp & 1u) != 0) != 0;
         if (any_tie) {
             // settle the ties from the parity of T before each one; then
             // the increments' prefix sums again

@@ -94,13 +94,13 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double* wsum, d
     return (wave > 0 ? __shfl(ws, wave - 1) : 0.0) + (incl - v);
 }
 
-// q(e) = floor(e / d) for 0 <= e < 2^13 and 1 <= d < 2^21, from a binary32
-// reciprocal: (e + 1/2) / d lies at least 1/(2d) from an integer, and the two
-// roundings move it by at most (e + 1/2)/d * 2^-23 (1 + 2^-24), which is
-// below (2^13 + d) / d * 2^-23 < 1/(2d).
+// q(e) = floor(e / d) for 0 <= e < 2^13 and d >= 1, from a binary32
+// reciprocal within one ulp: (e + 1/2) / d lies at least 1/(2d) from an
+// integer, and the reciprocal's error and the product's rounding move it by
+// less than (e + 1/2)/d * 2^-22 < 2^-9 / d.
 struct DivSmall {
     float inv;
-    __device__ explicit DivSmall(int d) : inv(1.f / (float)d) {}
+    __device__ explicit DivSmall(int d) : inv(__builtin_amdgcn_rcpf((float)d)) {}  // within 1 ulp
     __device__ int q(int e) const { return (int)(((float)e + 0.5f) * inv); }
 };
 
@@ -160,9 +160,14 @@ __device__ __forceinline__ void store_run(uint32_t* d, uint16_t* di, const uint3
 
 // Outputs dg .. dg+KC-1 of the merge of sorted runs A (lenA >= 1 keys) and B
 // (lenB keys), equal keys from A first (merge path): a binary search finds
-// how many of the first dg outputs come from A, the next KC keys of each run
-// are read together, merged in registers, and written with vector stores at
-// d, di (outputs past the end of the merged run are don't-cares).
+// how many of the first dg outputs come from A, then the next KC keys of
+// each run are read together.  Each candidate becomes one 64-bit value, key
+// above its source code (a code of A is below every code of B, and codes
+// rise along a run), so the values are distinct and their order is the
+// merge order.  The elementwise minimum of the A window and the reversed B
+// window holds the KC smallest (a bitonic sequence); half-cleaners sort it.
+// The keys and pair ids go out with vector stores at d, di (outputs past the
+// end of the merged run are don't-cares).
 template <int KC, typename Pair>
 __device__ __forceinline__ void merge_path(const Pair& P, int lenA, int lenB, int dg, uint32_t* d, uint16_t* di) {
     int lo = dg - lenB > 0 ? dg - lenB : 0;
@@ -172,31 +177,36 @@ __device__ __forceinline__ void merge_path(const Pair& P, int lenA, int lenB, in
         if (P.ka(i) <= P.kb(dg - i - 1)) lo = i + 1;
         else hi = i;
     }
-    int pa = lo, pb = dg - lo;
-    uint32_t wa[KC], wb[KC];
+    const int pa = lo, pb = dg - lo;
+    uint64_t c[KC], cb[KC];
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
-        wa[k] = P.ka(pa + k);
-        wb[k] = P.kb(pb + k);
+        const uint64_t va = ((uint64_t)P.ka(pa + k) << 32) | (uint32_t)P.code_a(pa + k);
+        const uint64_t vb = ((uint64_t)P.kb(pb + k) << 32) | (uint32_t)P.code_b(pb + k);
+        c[k] = pa + k < lenA ? va : ~0ull;
+        cb[k] = pb + k < lenB ? vb : ~0ull;
+    }
+#pragma unroll
+    for (int k = 0; k < KC; ++k) c[k] = cb[KC - 1 - k] < c[k] ? cb[KC - 1 - k] : c[k];
+#pragma unroll
+    for (int h = KC / 2; h > 0; h >>= 1) {
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+            if ((k & h) == 0) {
+                const uint64_t x = c[k], y = c[k + h];
+                c[k] = y < x ? y : x;
+                c[k + h] = y < x ? x : y;
+            }
+        }
     }
     uint32_t ov[KC];
     uint16_t oid[KC];
-    int oc[KC];
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
-        const bool take_a = (pa < lenA) & ((pb >= lenB) | (wa[0] <= wb[0]));
-        ov[k] = take_a ? wa[0] : wb[0];
-        oc[k] = take_a ? P.code_a(pa) : P.code_b(pb);
-        pa += (int)take_a;
-        pb += (int)!take_a;
-#pragma unroll
-        for (int t = 0; t + 1 + k < KC; ++t) {
-            wa[t] = take_a ? wa[t + 1] : wa[t];
-            wb[t] = take_a ? wb[t] : wb[t + 1];
-        }
+        ov[k] = (uint32_t)(c[k] >> 32);
+        const uint32_t code = (uint32_t)c[k];
+        oid[k] = P.id_of((int)(code < (uint32_t)(kMaxPairs - 1) ? code : (uint32_t)(kMaxPairs - 1)));
     }
-#pragma unroll
-    for (int k = 0; k < KC; ++k) oid[k] = P.id_of(oc[k]);
     store_run<KC>(d, di, ov, oid);
 }
 
@@ -356,7 +366,8 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
     __shared__ __align__(16) uint16_t pids[2][kMaxPairs + kPad];  // pair id r * gamma + j of each key
     __shared__ double wsum[2 * kNT / 64];
     __shared__ uint32_t wpar[kNT / 64];
-    __shared__ int stop_pos, n_exact;
+    __shared__ int stop_pos;
+    __shared__ int wexact[kNT / 64];  // per wave: its positions in the exact run
     __shared__ int wunsorted[kNT / 64];  // per wave: some run of this wave's requests is not ascending
     __shared__ double tail_theta;
     __shared__ int tail_nsel;
@@ -377,7 +388,7 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
     }
 
     // (first read after the barrier that ends the survival phase)
-    if (tid == 0) stop_pos = 0x7fffffff, n_exact = 0;
+    if (tid == 0) stop_pos = 0x7fffffff;
     // Keys of the request-major pairs, transposed: pair (r, j) sits at
     // j * ts + r, so a wave of consecutive requests stores to consecutive
     // words, and a wave of consecutive positions of one request (stride ts,
@@ -468,29 +479,32 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
         kv[0] = k0.x, kv[1] = k0.y, kv[2] = k0.z, kv[3] = k0.w;
         kv[4] = k1.x, kv[5] = k1.y, kv[6] = k1.z, kv[7] = k1.w;
     }
-    int my_ex = 0;
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) my_ex += (first + q < n && val_survival(kv[q]) >= exact_floor) ? 1 : 0;
-    for (int o = 32; o > 0; o >>= 1) my_ex += __shfl_xor(my_ex, o);
-    if (lane == 0 && my_ex) atomicAdd(&n_exact, my_ex);
     if (order_out)
         for (int i = tid; i < n; i += kNT) order_out[i] = (int32_t)ids[i];
+    // (the last merge level read this row before its barrier; the tallies
+    // start after later barriers)
     for (int r = tid; r < (int)B; r += kNT) counts[r] = 0;
-    __syncthreads();
-    // Leading run of sorted survivals for which the parallel sum is exact.
-    const int P = n_exact < n_lim ? n_exact : n_lim;
-
+    // The exact run: positions 1..P, P = min(survivals at or above the floor,
+    // n_lim); the sorted order puts those survivals first, so each thread
+    // marks its own positions and the count rides on the scan's barrier.
     // tau over positions 1..P: binary64 prefix sums (exact, see above).
     // inc[q] is the survival of an owned position p <= P.
     double inc[kPer];
     double local = 0.0;
+    int wave_ex = 0;  // the wave's positions in the exact run (uniform)
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
-        inc[q] = (first + q < P) ? (double)val_survival(kv[q]) : 0.0;
+        const double a = (double)val_survival(kv[q]);
+        const bool ex = first + q < n_lim && a >= (double)exact_floor;
+        inc[q] = ex ? a : 0.0;
         local += inc[q];
+        wave_ex += __popcll(__ballot(ex));
     }
+    if (lane == 0) wexact[wave] = wave_ex;
     double S = 0.0;
     const double offset = block_exclusive_scan(local, wsum, S);
+    int P = lane < kNT / 64 ? wexact[lane] : 0;  // (written before the scan's barrier)
+    for (int o = 32; o > 0; o >>= 1) P += __shfl_xor(P, o);
     const double Bd = (double)B;
     const double tauP = Bd + S;  // tau after position P
 

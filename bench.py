@@ -436,7 +436,7 @@ def main():
         s5 = synth.SCHEDULE_TRAIN
         sch = {"workload": "prefix scheduler (Algorithm 1), B=256 requests x gamma=16, 4096-entry throughput "
                            "table; 'tokens': SPS(n) = n/(2+0.004n) as stated, 'steps': SPS(n) = 1/(2+0.004n)",
-               "bound": "latency (one workgroup)"}
+               "bound": "one workgroup: its vector ALUs and barriers"}
         for kind in ("tokens", "steps"):
             c5, o5 = dh.prepare_prefix_schedule(to_dev(synth.schedule_conf(s5), dev),
                                                 to_dev(synth.sps_table(s5.n_sps, kind), dev), want_order=False)

@@ -32,6 +32,8 @@
 //   4. the stop is the first prefix whose Theta does not exceed its
 //      predecessor's (or the table's end); prefix lengths count the accepted
 //      pairs per request in LDS.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace dspark {
@@ -65,15 +67,54 @@ __device__ __forceinline__ void wave_stop(int my_stop, int lane, int* stop) {
     if (b != 0 && lane == __ffsll((unsigned long long)b) - 1) atomicMin(stop, my_stop);
 }
 
-// Inclusive prefix sums over lanes 0..kNT/64-1 of one value each (the other
-// lanes hold 0): a tree of additions.
+// DPP moves between lanes (register to register, no LDS round trip): a
+// shift right by n lanes within each row of 16 (lanes near the row's start
+// read 0) and the two broadcasts that join rows (lane 15 of each row into
+// the next, lane 31 into rows 2 and 3; rows outside the mask read 0).
+constexpr int kDppRowShr = 0x110;  // + n, 1 <= n <= 15
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = dpp_u32<CTRL, ROWS>((uint32_t)b), hi = dpp_u32<CTRL, ROWS>((uint32_t)(b >> 32));
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Inclusive prefix sums within each row of 16 lanes (a tree of additions).
+template <typename T, typename Move>
+__device__ __forceinline__ T row_incl_scan(T x, Move mv) {
+    x += mv(x, std::integral_constant<int, kDppRowShr + 1>{});
+    x += mv(x, std::integral_constant<int, kDppRowShr + 2>{});
+    x += mv(x, std::integral_constant<int, kDppRowShr + 4>{});
+    x += mv(x, std::integral_constant<int, kDppRowShr + 8>{});
+    return x;
+}
+struct MoveF64 {
+    template <int C>
+    __device__ double operator()(double v, std::integral_constant<int, C>) const { return dpp_f64<C, 0xf>(v); }
+};
+struct MoveU32 {
+    template <int C>
+    __device__ uint32_t operator()(uint32_t v, std::integral_constant<int, C>) const { return dpp_u32<C, 0xf>(v); }
+};
+
+// Inclusive prefix sums over the wave's 64 lanes: the rows' own scans, then
+// the rows joined (a tree of additions).
+__device__ __forceinline__ double wave_incl_scan_f64(double x) {
+    x = row_incl_scan(x, MoveF64{});
+    x += dpp_f64<kDppRowBcast15, 0xa>(x);
+    x += dpp_f64<kDppRowBcast31, 0xc>(x);
+    return x;
+}
+
+// Inclusive prefix sums over lanes 0..kNT/64-1 (row 0) of one value each.
 __device__ __forceinline__ double wave_totals_scan(double ws) {
-    const int lane = threadIdx.x & 63;
-    for (int o = 1; o < kNT / 64; o <<= 1) {
-        const double y = __shfl_up(ws, o);
-        if (lane >= o) ws += y;
-    }
-    return ws;
+    static_assert(kNT / 64 == 16, "the wave totals fill one row of 16 lanes");
+    return row_incl_scan(ws, MoveF64{});
 }
 
 // Exclusive prefix sum of one value per thread across the workgroup, and the
@@ -82,16 +123,12 @@ __device__ __forceinline__ double wave_totals_scan(double ws) {
 // order -- which is how the scheduler uses it.
 __device__ __forceinline__ double block_exclusive_scan(double v, double* wsum, double& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    double incl = v;
-    for (int o = 1; o < 64; o <<= 1) {
-        const double y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-    }
+    const double incl = wave_incl_scan_f64(v);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     const double ws = wave_totals_scan(lane < kNT / 64 ? wsum[lane] : 0.0);
-    total = __shfl(ws, kNT / 64 - 1);
-    return (wave > 0 ? __shfl(ws, wave - 1) : 0.0) + (incl - v);
+    total = readlane_f64(ws, kNT / 64 - 1);
+    return (wave > 0 ? readlane_f64(ws, wave - 1) : 0.0) + (incl - v);
 }
 
 // q(e) = floor(e / d) for 0 <= e < 2^13 and d >= 1, from a binary32
@@ -396,7 +433,36 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
     const int ts = (((int)B | 1) * g <= kMaxPairs) ? ((int)B | 1) : (int)B;
     uint32_t* scr = vals[0];
     bool all_up = true;
-    if (g > 0) {
+    // gamma a multiple of 4 (up to 16) and a 16-byte aligned array: each
+    // product thread loads its own request's confidences with 16-byte loads,
+    // so they skip the LDS round trip and its barrier
+    const bool direct = ((uintptr_t)conf & 15) == 0 && g > 0 && g % 4 == 0 && g <= kConfChunk;
+    if (direct) {
+        for (int r = tid; r < (int)B; r += kNT) {
+            float c[kConfChunk];
+            const float4* cr = reinterpret_cast<const float4*>(conf + (int64_t)r * g);
+#pragma unroll
+            for (int j4 = 0; j4 < kConfChunk / 4; ++j4) {
+                const float4 v = cr[4 * j4 < g ? j4 : 0];  // past gamma: any in-bounds vector, unused
+                c[4 * j4] = v.x, c[4 * j4 + 1] = v.y, c[4 * j4 + 2] = v.z, c[4 * j4 + 3] = v.w;
+            }
+            float p = 1.f;
+            uint32_t prev = 0;
+            bool up = true;
+#pragma unroll
+            for (int j = 0; j < kConfChunk; ++j) {
+                if (j < g) {
+                    p = p * c[j];
+                    const uint32_t v = ~orderable(p);
+                    const uint32_t vc = canon_key(v);
+                    up = up && vc >= prev;
+                    prev = vc;
+                    scr[j * ts + r] = v;
+                }
+            }
+            all_up = all_up && up;
+        }
+    } else if (g > 0) {
         // The confidences, coalesced (four per thread per 16-byte load when
         // the array is 16-byte aligned), into the transposed layout...
         const bool vec = ((uintptr_t)conf & 15) == 0;
@@ -503,8 +569,9 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
     if (lane == 0) wexact[wave] = wave_ex;
     double S = 0.0;
     const double offset = block_exclusive_scan(local, wsum, S);
-    int P = lane < kNT / 64 ? wexact[lane] : 0;  // (written before the scan's barrier)
-    for (int o = 32; o > 0; o >>= 1) P += __shfl_xor(P, o);
+    // (written before the scan's barrier)
+    const int P = (int)__builtin_amdgcn_readlane(
+        (int)row_incl_scan((uint32_t)(lane < kNT / 64 ? wexact[lane] : 0), MoveU32{}), kNT / 64 - 1);
     const double Bd = (double)B;
     const double tauP = Bd + S;  // tau after position P
 
@@ -575,11 +642,7 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
         // One exchange: the wave sums of the increments, whether the wave
         // saw a non-finite value or a tie, and its parity summary (x = parity
         // of the odd increments after its last tie, t = it has a tie).
-        double incl = rloc;
-        for (int o = 1; o < 64; o <<= 1) {
-            const double y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
-        }
+        const double incl = wave_incl_scan_f64(rloc);
         const bool wave_tie = __ballot(tiemask != 0) != 0;
         uint32_t x = xr, t = tiemask ? 1u : 0u;
         if (wave_tie) {  // inclusive segmented scan within the wave
@@ -603,8 +666,8 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
         // (integers below 2^53: exact in any order)
         const double ws = wave_totals_scan(lane < kNT / 64 ? wsum[kNT / 64 + lane] : 0.0);
         const uint32_t wp = lane < kNT / 64 ? wpar[lane] : 0u;
-        double Ktot = __shfl(ws, kNT / 64 - 1);
-        roff = (wave > 0 ? __shfl(ws, wave - 1) : 0.0) + (incl - rloc);
+        double Ktot = readlane_f64(ws, kNT / 64 - 1);
+        roff = (wave > 0 ? readlane_f64(ws, wave - 1) : 0.0) + (incl - rloc);
         const bool any_bad = __ballot((wp & 4u) != 0) != 0;
         const bool any_tie = __ballot((wp & 1u) != 0) != 0;
         if (any_tie) {
@@ -651,8 +714,9 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
         }
         tail_ok = !any_bad && tauP + u * Ktot < ldexp(1.0, ebin);
 
-        // Theta on past the exact run (stops inside it are recorded above)
-        if (tail_ok) {
+        // Theta on past the exact run (stops inside it are recorded above;
+        // a thread whose positions all lie inside it has nothing to do)
+        if (tail_ok && first + kPer > P) {
             double tau_prev = first <= P ? Bd + offset : tauP + u * roff;  // tau after position first
             double th_prev = tau_prev * spv[0];
             double kq = roff;
@@ -745,7 +809,10 @@ __global__ __launch_bounds__(kNT) void prefix_schedule_kernel(int64_t B, int64_t
         }
     }
     if (tid == 0 && nsel_out) *nsel_out = nsel;
-    for (int i = tid; i < nsel; i += kNT) atomicAdd(&counts[(uint32_t)ids[i] / (uint32_t)g], 1);
+    {
+        const DivSmall dg(g > 0 ? g : 1);
+        for (int i = tid; i < nsel; i += kNT) atomicAdd(&counts[dg.q(ids[i])], 1);
+    }
     __syncthreads();
     for (int r = tid; r < (int)B; r += kNT) prefix_len[r] = counts[r];
 }

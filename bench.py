@@ -350,6 +350,7 @@ def main():
             vcall()
         torch.cuda.synchronize()
         v_us = timed(vcall, 20)
+        v_cold = timed_cold(vcall, 10) if scrub is not None else None
         n_acc = vout["n_accepted"].cpu().numpy()
         v_bytes = verify_call_bytes([sv.gamma] * sv.B, n_acc == sv.gamma, sv.V, sv.gamma)
         line["verify"] = {
@@ -358,7 +359,7 @@ def main():
             "us_per_call": round(v_us, 2), "positions_per_s": round(sv.B * sv.gamma / (v_us * 1e-6), 1),
             "mean_accepted": round(float(n_acc.mean()), 3),
             "roofline": hbm_roofline("dspark_verify (2 launches; verify_stats reads every drafted row)", v_bytes,
-                                     v_us, "verify_b64_vocab151936.md", VERIFY_SOURCES),
+                                     v_us, "verify_b64_vocab151936.md", VERIFY_SOURCES, v_cold),
         }
         del vd, vout
 
@@ -406,12 +407,13 @@ def main():
             cg()
         torch.cuda.synchronize()
         usg = timed(cg, 10)
+        g_cold = timed_cold(cg, 6) if scrub is not None else None
         byg = by3 + s3.r * (s3.H + s3.r) * 2
         line["gated_b64"] = {
             "workload": "gated Markov head, B=64 gamma=7 V=151936 H=5120 r=256 bf16, Gumbel-max with fp32 noise",
             "us_per_call": round(usg, 2), "positions_per_s": round(64 * 7 / (usg * 1e-6), 1),
             "roofline": hbm_roofline("dspark_head_sample_gated", byg, usg, "head_sample_gated_b64_vocab151936.md",
-                                     SAMPLER_SOURCES)}
+                                     SAMPLER_SOURCES, g_cold)}
         del Wg3
     if "rnn" in legs:
         Wr3 = tuple(to_dev(a, dev) for a in synth.rnn_weights(s3, 0.015))
@@ -421,12 +423,13 @@ def main():
             cr()
         torch.cuda.synchronize()
         usr = timed(cr, 10)
+        r_cold = timed_cold(cr, 6) if scrub is not None else None
         byr = by3 + 2 * s3.r * (2 * s3.r + s3.H) * 2
         line["rnn_b64"] = {
             "workload": "RNN head, B=64 gamma=7 V=151936 H=5120 r=256 bf16, Gumbel-max with fp32 noise",
             "us_per_call": round(usr, 2), "positions_per_s": round(64 * 7 / (usr * 1e-6), 1),
             "roofline": hbm_roofline("dspark_head_sample_rnn", byr, usr, "head_sample_rnn_b64_vocab151936.md",
-                                     SAMPLER_SOURCES)}
+                                     SAMPLER_SOURCES, r_cold)}
         del Wr3
     if legs & {"b64", "gated", "rnn"}:
         del d3
@@ -459,6 +462,7 @@ def main():
             c6()
         torch.cuda.synchronize()
         us6 = timed(c6, 5)
+        l_cold = timed_cold(c6, 3) if scrub is not None else None
         M6 = s6.N * s6.gamma
         by6 = (2 * M6 * s6.V * 2 + s6.V * s6.r * 2 + M6 * s6.r * 2 + M6 * s6.H * 2 + (s6.H + s6.r) * 2 + 8 * M6
                + 16 * M6 + 16)
@@ -467,7 +471,8 @@ def main():
                         "(128 anchors x block 16), V=151936 H=5120 r=256 bf16",
             "us_per_call": round(us6, 2), "positions_per_s": round(M6 / (us6 * 1e-6), 1),
             "mfma_tflops": round(2 * M6 * s6.V * s6.r / (us6 * 1e-6) / 1e12, 2),
-            "roofline": hbm_roofline("dspark_block_loss", by6, us6, "block_loss_2048x151936.md", LOSS_SOURCES)}
+            "roofline": hbm_roofline("dspark_block_loss", by6, us6, "block_loss_2048x151936.md", LOSS_SOURCES,
+                                     l_cold)}
         del d6
 
     if args.calib_copy:

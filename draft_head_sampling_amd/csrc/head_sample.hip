@@ -839,7 +839,38 @@ __device__ __forceinline__ void hidden_partials(ScreenLds& s, int gamma, int64_t
     float p[kScreenMaxGamma];
 #pragma unroll
     for (int k = 0; k < kScreenMaxGamma; ++k) p[k] = 0.f;
-    for (int64_t base = h_lo; base < h_hi; base += nt) {  // workgroup-uniform trip count
+    // 16-byte pieces, two per thread, all loads of a round in flight together
+    // (so cold data costs one memory latency per round, not one per element
+    // group); other shapes take the element loop below
+    const bool vec = (h_lo & 7) == 0 && ((h_hi - h_lo) & 7) == 0 && (H & 7) == 0 &&
+                     (((uintptr_t)h | (uintptr_t)w_conf) & 15) == 0;
+    constexpr int kPieces = 2;
+    for (int64_t base = h_lo; vec && base < h_hi; base += (int64_t)8 * nt * kPieces) {  // workgroup-uniform
+        uint4 wv[kPieces], hv[kPieces][kScreenMaxGamma];
+        bool use[kPieces];
+#pragma unroll
+        for (int pc = 0; pc < kPieces; ++pc) {
+            const int64_t i = base + 8 * (t + (int64_t)nt * pc);
+            use[pc] = i < h_hi;
+            const int64_t ic = use[pc] ? i : h_lo;
+            wv[pc] = *reinterpret_cast<const uint4*>(w_conf + ic);
+#pragma unroll
+            for (int k = 0; k < kScreenMaxGamma; ++k)
+                hv[pc][k] = *reinterpret_cast<const uint4*>(h + (int64_t)min(k, gamma - 1) * H + ic);
+        }
+#pragma unroll
+        for (int pc = 0; pc < kPieces; ++pc) {
+            if (!use[pc]) continue;
+            const uint32_t ww[4] = {wv[pc].x, wv[pc].y, wv[pc].z, wv[pc].w};
+#pragma unroll
+            for (int k = 0; k < kScreenMaxGamma; ++k) {
+                const uint32_t hw[4] = {hv[pc][k].x, hv[pc][k].y, hv[pc][k].z, hv[pc][k].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) p[k] = dot2(ww[e], hw[e], p[k]);
+            }
+        }
+    }
+    for (int64_t base = h_lo; !vec && base < h_hi; base += nt) {  // workgroup-uniform trip count
         const int64_t i = base + t;
         const bool use = i < h_hi;
         const int64_t ic = use ? i : 0;

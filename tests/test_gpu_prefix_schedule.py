@@ -2,6 +2,7 @@
 lengths, sorted order, survivals, Theta and the selection count bit-exact."""
 import numpy as np
 import pytest
+import torch
 
 import draft_head_sampling_amd as dh
 import oracle
@@ -145,3 +146,23 @@ def test_tail_ties_spread_over_many_waves(tie_share, seed):
     conf[:, 2:] = rng.uniform(0.5, 1.0, (B, g - 2)).astype(np.float32)
     r = _check(conf, synth.sps_table(B + B * g, "tokens"))
     assert r["n_selected"] == B * g
+
+
+@pytest.mark.parametrize("B,gamma", [(256, 16), (300, 9), (3, 5)])
+def test_confidences_not_16_byte_aligned(B, gamma):
+    """The confidences read with 16-byte loads only from a 16-byte aligned
+    array; a view four bytes into a buffer takes the element-wise path."""
+    rng = np.random.default_rng(B * 31 + gamma)
+    conf = (1 / (1 + np.exp(-rng.normal(1.5, 1.5, (B, gamma))))).astype(np.float32)
+    sps = synth.sps_table(B + B * gamma, "steps")
+    buf = torch.empty(B * gamma + 1, dtype=torch.float32, device="cuda")
+    buf[1:] = dev(conf.ravel())
+    view = buf[1:].view(B, gamma)
+    assert view.data_ptr() % 16 != 0
+    g = {k: (v.cpu().numpy() if v is not None else None) for k, v in dh.prefix_schedule(view, dev(sps)).items()}
+    r = oracle.prefix_schedule(conf, sps)
+    np.testing.assert_array_equal(g["prefix_len"], r["prefix_len"])
+    np.testing.assert_array_equal(g["order"], r["order"])
+    np.testing.assert_array_equal(g["survival"].view(np.uint32), r["survival"].view(np.uint32))
+    assert g["n_selected"][0] == r["n_selected"]
+    assert g["theta"][0] == r["theta"]

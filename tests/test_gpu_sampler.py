@@ -47,6 +47,7 @@ def test_tiny_workload_with_logits():
         # single request, bf16, rank 256: the persistent chain kernel
         (1, 7, 1000, 16, 256, "bf16", 0.5, True),  # few workgroups, Gumbel
         (1, 5, 70001, 72, 256, "bf16", 0.3, False),  # ragged slices, H not a multiple of 64
+        (1, 5, 3001, 13, 256, "bf16", 0.4, False),  # H not a multiple of 8: the hidden dot's element loop
         (1, 9, 163200, 8, 256, "bf16", 0.2, False),  # largest vocabulary held on chip, gamma above the screen
         (1, 4, 200003, 8, 256, "bf16", 0.2, True),  # beyond it: per-step kernels
         (1, 2, 1, 8, 256, "bf16", 0.5, False),  # single-token vocabulary

@@ -9,7 +9,9 @@ positions per second (bias + sample + confidence) over the timed steps.
 
 The same run times every other workload once, each as its own object with an
 HBM (or matrix-core) roofline: the B=1 sampler with cold caches and with a
-strong Markov bias (the grid-wide exchange path); the batched Gumbel-max
+strong Markov bias (the grid-wide exchange path) and with the W2 row-norm
+bound computed once per weight load (dspark_w2_bound; its own cost is
+reported beside it, and `value` does not use it); the batched Gumbel-max
 sampler (B=64) with its matrix-core figures; the gated and RNN heads; the
 analytic accept rate on 2048 training positions; the prefix scheduler on 256 x
 16 confidences with both throughput tables; rejection-sampling verify; and the
@@ -19,7 +21,7 @@ the GPU's.  Inputs are synthetic (seeded generator) and resident in HBM before
 any timed region starts.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--anchors 1000]
-                       [--legs all|b1,cold,strong,accept,verify,b64,gated,rnn,schedule,loss,cpu]
+                       [--legs all|b1,cold,strong,w2bound,accept,verify,b64,gated,rnn,schedule,loss,cpu]
                        [--no-cpu] [--no-accept] [--no-verify] [--no-cold] [--calib-copy]
 """
 from __future__ import annotations
@@ -35,7 +37,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores
-ALL_LEGS = ("b1", "cold", "strong", "accept", "verify", "b64", "gated", "rnn", "schedule", "loss", "cpu")
+ALL_LEGS = ("b1", "cold", "strong", "w2bound", "accept", "verify", "b64", "gated", "rnn", "schedule", "loss", "cpu")
 
 
 def to_dev(a, device):
@@ -315,6 +317,43 @@ def main():
                                      timed_cold(lambda: scalls[0](), 20) if scrub is not None else None),
         }
         del Ws
+
+    # ---------------- B=1 with the weights-only W2 bound computed once per weight load ----------------
+    if "w2bound" in legs:
+        bound = dh.w2_bound(W["W2"])
+        L_ = dh.lib()
+        w2p, bp = W["W2"].data_ptr(), bound.data_ptr()
+        bound_us = timed(lambda: L_.dspark_w2_bound(s.V, s.r, dh.DSPARK_BF16, w2p, bp, stream.cuda_stream), 20)
+        tok_b, conf_b, surv_b = torch.empty_like(tokens), torch.empty_like(conf), torch.empty_like(surv)
+        bcalls = []
+        for a in range(n_anch):
+            c, _ = dh.prepare_head_sample(U[a : a + 1], Hh[a : a + 1], W["W1"], W["W2"], W["w_conf"], 0.0,
+                                          X0[a : a + 1], tokens=tok_b[a : a + 1], conf=conf_b[a : a + 1],
+                                          survival=surv_b[a : a + 1], workspace=ws, w2_bound=bound)
+            bcalls.append(c)
+        dh.workspace_status(ws)  # clear the path flags
+        for c in bcalls[:10]:
+            c()
+        torch.cuda.synchronize()
+        us_b = timed(lambda: [c() for c in bcalls], 1) / n_anch
+        st_b, paths_b = dh.workspace_status(ws)
+        same = int((tok_b == tokens).all(dim=1).sum().item())  # the serving step's tokens, same anchors
+        # what the bounded call reads: U and h of the anchor, w_conf, the anchor's W1 row, the 64 sampled W2
+        # rows and the bound (the few candidate rows the screen stages, at most 32 W1 and W2 rows, not counted)
+        bytes_b = (s.gamma * s.V * 2 + s.gamma * s.H * 2 + (s.H + s.r) * 2 + s.r * 2 + 64 * s.r * 2
+                   + 4 * dh.W2_BOUND_WORDS + 4 + s.gamma * 12)
+        line["b1_w2bound"] = {
+            "workload": f"B=1 gamma=7 V=151936 H=5120 r=256 bf16 greedy, the serving step's {n_anch} anchors back to "
+                        "back with dspark_head_sample_w2bound: the largest W2 row norm computed once per weight load "
+                        "(dspark_w2_bound) instead of a pass over W2 in every call",
+            "us_per_call": round(us_b, 3), "positions_per_s": round(s.gamma / (us_b * 1e-6), 1),
+            "w2_bound_us": round(bound_us, 2), "tokens_equal_to_plain_anchors": same, "anchors": n_anch,
+            "give_up": st_b, "path_flags": paths_b,
+            "roofline": hbm_roofline("dspark_head_sample_w2bound (bytes the call reads; W2 is not streamed)", bytes_b,
+                                     us_b, None, None,
+                                     timed_cold(lambda: bcalls[0](), 50) if scrub is not None else None),
+        }
+        del bcalls
 
     # ---------------- accept rate on the training-width workload ----------------
     if "accept" in legs:

@@ -87,6 +87,11 @@ def lib() -> ctypes.CDLL:
     L.dspark_head_sample_noalloc.restype = i32
     L.dspark_head_sample_noalloc.argtypes = [i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp,
                                              vp, vp, vp, vp, vp]
+    L.dspark_head_sample_w2bound.restype = i32
+    L.dspark_head_sample_w2bound.argtypes = [i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp,
+                                             vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dspark_w2_bound.restype = i32
+    L.dspark_w2_bound.argtypes = [i64, i64, i32, vp, vp, vp]
     L.dspark_workspace_status.restype = i32
     L.dspark_workspace_status.argtypes = [vp, sz, vp, vp]
     L.dspark_set_wait_limit.restype = i32
@@ -144,6 +149,20 @@ class DsparkGaveUp(RuntimeError):
 
 
 PATH_B1_REBUILD, PATH_B1_EXCHANGE, PATH_RESIDENT, PATH_ACCEPT_CLUSTER = 1, 2, 4, 8
+PATH_B1_BOUND, PATH_B1_BOUND_STALE = 16, 32
+W2_BOUND_WORDS = 8
+
+
+def w2_bound(W2: torch.Tensor, stream=None) -> torch.Tensor:
+    """dspark_w2_bound: the weights-only bound of the single-request screen
+    for W2 [V, 256] bfloat16 (CUDA), as W2_BOUND_WORDS int32 words on W2's
+    device; enqueued on the stream.  Pass it to prepare_head_sample(...,
+    w2_bound=...) for as long as W2 is unchanged."""
+    V, r = W2.shape
+    out = torch.zeros(W2_BOUND_WORDS, dtype=torch.int32, device=W2.device)
+    _check("dspark_w2_bound", lib().dspark_w2_bound(V, r, _dtype_code(W2), _dev(W2, "W2"), out.data_ptr(),
+                                                    _stream(W2.device) if stream is None else stream))
+    return out
 
 
 def workspace_status(workspace: torch.Tensor) -> tuple[int, int]:
@@ -193,11 +212,13 @@ def head_sample_workspace_size(B, gamma, V, H, r, dtype=DSPARK_BF16) -> int:
 
 
 def prepare_head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=None, *, tokens=None, conf=None,
-                        survival=None, logits_out=None, bias_out=None, workspace=None, stream=None, Wg=None, Wr=None):
+                        survival=None, logits_out=None, bias_out=None, workspace=None, stream=None, Wg=None, Wr=None,
+                        w2_bound=None):
     """Validate once and return (call, outputs): ``call()`` enqueues
     dspark_head_sample (or, with gate weights Wg [r, H + r], the gated head
     dspark_head_sample_gated; with Wr = (Wrg, Wrc), each [r, 2r + H], the RNN
-    head dspark_head_sample_rnn) on the stream with these exact buffers."""
+    head dspark_head_sample_rnn; with the words of w2_bound(W2),
+    dspark_head_sample_w2bound) on the stream with these exact buffers."""
     B, gamma, V = U.shape
     r = W1.shape[1]
     H = h.shape[2] if h is not None else 0
@@ -226,6 +247,8 @@ def prepare_head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=Non
     st = _stream(dev) if stream is None else stream
     if Wg is not None and Wr is not None:
         raise ValueError("Wg (gated head) and Wr (RNN head) are exclusive")
+    if w2_bound is not None and (Wg is not None or Wr is not None):
+        raise ValueError("w2_bound applies to the Markov head only")
     if Wr is not None:
         rargs = args[:11] + (_dev(Wr[0], "Wrg", U.dtype, (r, 2 * r + H)),
                              _dev(Wr[1], "Wrc", U.dtype, (r, 2 * r + H))) + args[11:]
@@ -233,6 +256,11 @@ def prepare_head_sample(U, h, W1, W2, w_conf, b_conf, x0, gumbel=None, force=Non
                              workspace)
         fn = partial(lib().dspark_head_sample_rnn, *rargs, None if ws is None else ws.data_ptr(), wsb, st)
         name = "dspark_head_sample_rnn"
+    elif Wg is None and w2_bound is not None:
+        ws, wsb = _workspace(head_sample_workspace_size(B, gamma, V, H, r, dt), dev, workspace)
+        bw = _dev(w2_bound, "w2_bound", torch.int32, (W2_BOUND_WORDS,))
+        fn = partial(lib().dspark_head_sample_w2bound, *args, bw, None if ws is None else ws.data_ptr(), wsb, st)
+        name = "dspark_head_sample_w2bound"
     elif Wg is None:
         ws, wsb = _workspace(head_sample_workspace_size(B, gamma, V, H, r, dt), dev, workspace)
         fn = partial(lib().dspark_head_sample, *args, None if ws is None else ws.data_ptr(), wsb, st)

@@ -102,6 +102,35 @@ DSPARK_EXPORT dspark_status_t dspark_head_sample(int64_t B, int64_t gamma, int64
                                                  static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr));
 }
 
+DSPARK_EXPORT dspark_status_t dspark_head_sample_w2bound(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r,
+                                                         int32_t dtype, const void* U, const void* h, const void* W1,
+                                                         const void* W2, const void* w_conf, float b_conf,
+                                                         const int32_t* x0, const float* gumbel, const int32_t* force,
+                                                         int32_t* tokens, float* conf, float* survival,
+                                                         float* logits_out, float* bias_out, const uint32_t* w2_bound,
+                                                         void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return DSPARK_ERR_BAD_DTYPE;
+    if (!sampler_shape_ok(B, gamma, V, H, r)) return DSPARK_ERR_BAD_SHAPE;
+    if (B == 0 || gamma == 0) return DSPARK_OK;
+    dspark_status_t st = check_workspace(workspace, workspace_bytes, dspark::head_sample_workspace(B, gamma, V, r, dtype));
+    if (st != DSPARK_OK) return st;
+    if (!U || !W1 || !W2 || !w_conf || !x0 || !tokens || !conf || !survival || (H > 0 && !h))
+        return DSPARK_ERR_NULL_ARG;
+    return hip_status(dspark::head_sample_launch(B, gamma, V, H, r, dtype, U, h, W1, W2, w_conf, b_conf, x0, gumbel,
+                                                 force, tokens, conf, survival, logits_out, bias_out, workspace,
+                                                 static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr,
+                                                 w2_bound));
+}
+
+DSPARK_EXPORT dspark_status_t dspark_w2_bound(int64_t V, int64_t r, int32_t dtype, const void* W2, uint32_t* bound,
+                                              void* stream) {
+    if (dtype != DSPARK_BF16) return DSPARK_ERR_BAD_DTYPE;
+    if (V < 1 || V > kMaxV || r != 256) return DSPARK_ERR_BAD_SHAPE;
+    if (!W2 || !bound) return DSPARK_ERR_NULL_ARG;
+    if ((uintptr_t)W2 % 16 != 0) return DSPARK_ERR_BAD_SHAPE;  // the screen reads 16-byte pieces
+    return hip_status(dspark::w2_bound_launch(V, W2, bound, static_cast<hipStream_t>(stream)));
+}
+
 DSPARK_EXPORT dspark_status_t dspark_head_sample_gated(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r,
                                                        int32_t dtype, const void* U, const void* h, const void* W1,
                                                        const void* W2, const void* w_conf, const void* Wg,

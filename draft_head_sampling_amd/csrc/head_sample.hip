@@ -907,7 +907,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
     const bf16_t* __restrict__ w_conf, float b_conf, const int32_t* __restrict__ x0, const float* __restrict__ G,
     const int32_t* __restrict__ force, int32_t* __restrict__ tokens, float* __restrict__ conf,
     float* __restrict__ survival, float* __restrict__ logits_out, float* __restrict__ bias_out, uint64_t* slots,
-    uint64_t* regions, uint64_t* aux, uint32_t* header, int spin_limit) {
+    uint64_t* regions, uint64_t* aux, uint32_t* header, int spin_limit, const uint32_t* __restrict__ nbound) {
     __shared__ uint64_t red[kChainWaves];
     __shared__ float fred[kChainWaves];
     __shared__ __align__(16) uint32_t we_lds[kChainRank / 2];  // Markov part of the confidence weights (workgroup 0)
@@ -929,6 +929,21 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
 
     const int64_t xa = x0[0];
     const bool scr = screen && xa >= 0 && xa < V;  // the same in every workgroup
+    // A weights-only bound from dspark_w2_bound, used when its fingerprint
+    // names this W2 (address, vocabulary, rank): the largest squared row norm
+    // and that of the rows the coordinator samples (checked below), in place
+    // of the norm stream.  The same in every workgroup.
+    bool bnd = false;
+    uint32_t bnd_n2 = 0, bnd_n2s = 0;
+    if (scr && nbound != nullptr) {
+        uint32_t bw[kW2BoundWords];
+#pragma unroll
+        for (int i = 0; i < kW2BoundWords; ++i) bw[i] = nbound[i];
+        bnd = bw[7] == kW2BoundTag && (((uint64_t)bw[3] << 32) | bw[2]) == (uint64_t)V && bw[4] == (uint32_t)kChainRank &&
+              (((uint64_t)bw[6] << 32) | bw[5]) == (uint64_t)(uintptr_t)W2;
+        bnd_n2 = bw[0];
+        bnd_n2s = bw[1];
+    }
 
     constexpr int NMINE = NSLOT > 8 ? 2 : 1;  // lane `sub` finishes slots sub and sub + 8
     int64_t my_v[NMINE];
@@ -1044,7 +1059,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             // sampled norm and the anchor row's norm, both enlarged) plus
             // rounding slack; the walk checks them against the real bound
             if (tid < gamma) {
-                const float bg = __builtin_sqrtf(__uint_as_float(sc.n2s) * kN2Guess) * 2.f *
+                const float bg = __builtin_sqrtf(bnd ? __uint_as_float(bnd_n2) : __uint_as_float(sc.n2s) * kN2Guess) * 2.f *
                                      __builtin_sqrtf(sc.esq[kERowAnchor]) * kBetaSlack +
                                  kBetaFloor;
                 const float a = __uint_as_float(sc.fbound[tid]);
@@ -1297,11 +1312,16 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 }
                 return w;
             };
-            const float guess = __uint_as_float(sc.n2s) * kN2Guess;
-            build(bound_bits(guess));
+            // with a bound whose sampled rows' norm differs from this W2's,
+            // the weights changed after it was computed: nothing is proved
+            // from it, and the whole block takes the per-step exchange
+            const bool stale = bnd && sc.n2s != bnd_n2s;  // workgroup-uniform
+            if (tid == 0 && bnd) mark_path(header, stale ? kPathB1BoundStale : kPathB1Bound);
+            const float guess = bnd ? __uint_as_float(bnd_n2) : __uint_as_float(sc.n2s) * kN2Guess;
+            if (!stale) build(bound_bits(guess));
             __syncthreads();
-            Walk wk{};
-            if (wave == 0) wk = walk();
+            Walk wk{0, 0, -1, xa, true, true};
+            if (wave == 0 && !stale) wk = walk();
             if (poller) {
                 uint64_t w = nword;
                 for (int spin = 0; spin < spin_limit && w == 0; ++spin) {
@@ -1313,7 +1333,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             }
             __syncthreads();
             const uint32_t n2b = sc.n2;
-            if (sc.abort || !(__uint_as_float(n2b) <= guess)) {  // workgroup-uniform
+            if (!stale && (sc.abort || !(__uint_as_float(n2b) <= guess))) {  // workgroup-uniform
                 if (tid == 0 && !sc.abort) mark_path(header, kPathB1Rebuild);
                 build(n2b);
                 __syncthreads();
@@ -1472,7 +1492,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             const int ng = (tid - kScreenLanes) >> 3;
             constexpr int NS = (NSLOT * kChainGroups + kNormGroups - 1) / kNormGroups;
             uint32_t nb = 0;
-            if (tid < kScreenLanes + kNormLanes) {
+            if (!bnd && tid < kScreenLanes + kNormLanes) {
                 uint32_t buf[kStreamSlots][16];
 #pragma unroll
                 for (int i = 0; i < kStreamSlots; ++i) {
@@ -1503,6 +1523,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             uint32_t m = 0;
 #pragma unroll
             for (int w = kScreenWaves; w < kChainWaves; ++w) m = max(m, sc.wn[w]);
+            if (bnd) m = bnd_n2;  // (no stream ran)
             __hip_atomic_store(myregion + kNormWord, kTag | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             // wait for the coordinator's decision
             uint64_t d = 0;
@@ -1687,6 +1708,76 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
     }
 }
 
+// ---------------------------------------------------------------------------
+// The weights-only bound of the B = 1 screen (dspark_w2_bound): the largest
+// squared W2 row norm, with the same per-row arithmetic as the norm stream
+// (eight lanes per row, 32 rank elements each, dot2 then sum8), so the
+// screen proves exactly what the stream would have let it prove; and a
+// fingerprint (the coordinator's sample of 64 rows, computed exactly as the
+// coordinator does, plus V, the rank and the address of W2).
+//   out[0] largest bound_bits of a row's squared norm   out[1] that of the sample
+//   out[2], out[3] V   out[4] rank   out[5], out[6] address of W2   out[7] kW2BoundTag
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kChainThreads) void w2_bound_init(int64_t V, const bf16_t* __restrict__ W2,
+                                                                uint32_t* __restrict__ out) {
+    __shared__ uint32_t wn[kChainWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = tid >> 3, sub = tid & 7;
+    uint32_t smp[16];
+    load64B(W2 + (int64_t)grp * (V / kSampleRows) * kChainRank + sub * 32, smp);
+    float a = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) a = dot2(smp[q], smp[q], a);
+    const uint32_t m = wave_max_u32(bound_bits(sum8(a)));
+    if (lane == 0) wn[wave] = m;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t n2s = 0;
+#pragma unroll
+        for (int w = 0; w < kChainWaves; ++w) n2s = max(n2s, wn[w]);
+        const uint64_t addr = (uint64_t)(uintptr_t)W2;
+        out[0] = 0u;
+        out[1] = n2s;
+        out[2] = (uint32_t)V;
+        out[3] = (uint32_t)((uint64_t)V >> 32);
+        out[4] = (uint32_t)kChainRank;
+        out[5] = (uint32_t)addr;
+        out[6] = (uint32_t)(addr >> 32);
+        out[7] = 0u;
+    }
+}
+
+__global__ __launch_bounds__(kChainThreads) void w2_bound_max(int64_t V, const bf16_t* __restrict__ W2,
+                                                               uint32_t* __restrict__ out) {
+    const int tid = threadIdx.x, lane = tid & 63, grp = tid >> 3, sub = tid & 7;
+    uint32_t nb = 0;
+    // 4 x 64 rows per workgroup and round, all four loads of a lane in
+    // flight together; a row's eight lanes are consecutive
+    constexpr int kU = 4;
+    for (int64_t v0 = (int64_t)blockIdx.x * kSampleRows * kU + grp; v0 < V;
+         v0 += (int64_t)gridDim.x * kSampleRows * kU) {
+        uint32_t b[kU][16];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t v = v0 + (int64_t)u * kSampleRows;
+            load64B(W2 + (v < V ? v : 0) * kChainRank + sub * 32, b[u]);  // past V: row 0, unused
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            float a = 0.f;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) a = dot2(b[u][q], b[u][q], a);
+            a = sum8(a);
+            if (v0 + (int64_t)u * kSampleRows < V) nb = max(nb, bound_bits(a));
+        }
+    }
+    nb = wave_max_u32(nb);
+    if (lane == 0 && nb != 0) __hip_atomic_fetch_max(out, nb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ void w2_bound_tag(uint32_t* __restrict__ out) {
+    if (threadIdx.x == 0) out[7] = kW2BoundTag;
+}
+
 const void* chain_fn(int nslot) {
     switch (nslot) {
         case 1: return reinterpret_cast<const void*>(&sample_chain_b1<1>);
@@ -1748,7 +1839,7 @@ size_t chain_workspace(int64_t gamma) {
 hipError_t launch_chain(const ChainPlan& p, int64_t gamma, int64_t V, int64_t H, const void* U, const void* h,
                         const void* W1, const void* W2, const void* w_conf, float b_conf, const int32_t* x0,
                         const float* G, const int32_t* force, int32_t* tokens, float* conf, float* survival,
-                        float* lo, float* bo, void* ws, hipStream_t stream) {
+                        float* lo, float* bo, void* ws, hipStream_t stream, const uint32_t* nbound) {
     int g = (int)gamma;
     int64_t Vv = V, Hh = H;
     int rows = p.rows_per_wg;
@@ -1765,7 +1856,8 @@ hipError_t launch_chain(const ChainPlan& p, int64_t gamma, int64_t V, int64_t H,
     uint64_t* aux = regions + (size_t)kRegionWords * kChainMaxWGs;
     int lim = wait_limit(kChainSpinLimit);
     void* args[] = {&g,     &Vv,    &Hh,       &rows, &screen, &Ut,    &ht,      &W1t, &W2t,    &wt,   &b_conf, &x0,
-                    &G,     &force, &tokens,   &conf, &survival, &lo,  &bo,      &slots, &regions, &aux, &header, &lim};
+                    &G,     &force, &tokens,   &conf, &survival, &lo,  &bo,      &slots, &regions, &aux, &header, &lim,
+                    &nbound};
     const void* fn = chain_fn(p.nslot);
     // A plain launch: every workgroup needs a whole CU (its register file) and
     // the grid has at most one workgroup per CU, so on an otherwise idle GPU
@@ -1774,6 +1866,7 @@ hipError_t launch_chain(const ChainPlan& p, int64_t gamma, int64_t V, int64_t H,
     // hang.
     return hipLaunchKernel(fn, dim3(p.nwg), dim3(kChainThreads), args, 0, stream);
 }
+
 
 
 // ---------------------------------------------------------------------------
@@ -3135,16 +3228,28 @@ size_t head_sample_rnn_workspace(int64_t B, int64_t gamma, int64_t r, int dtype)
     return w;
 }
 
+hipError_t w2_bound_launch(int64_t V, const void* W2, uint32_t* out, hipStream_t stream) {
+    const bf16_t* W2t = static_cast<const bf16_t*>(W2);
+    hipLaunchKernelGGL(w2_bound_init, dim3(1), dim3(kChainThreads), 0, stream, V, W2t, out);
+    const int cus = device_cus() > 0 ? device_cus() : 1;
+    const int64_t need = (V + 4 * kSampleRows - 1) / (4 * kSampleRows);
+    const int grid = (int)(need < 4 * (int64_t)cus ? need : 4 * (int64_t)cus);
+    hipLaunchKernelGGL(w2_bound_max, dim3(grid > 0 ? grid : 1), dim3(kChainThreads), 0, stream, V, W2t, out);
+    hipLaunchKernelGGL(w2_bound_tag, dim3(1), dim3(64), 0, stream, out);
+    return hipGetLastError();
+}
+
 hipError_t head_sample_launch(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int dtype, const void* U,
                               const void* h, const void* W1, const void* W2, const void* w_conf, float b_conf,
                               const int32_t* x0, const float* gumbel, const int32_t* force, int32_t* tokens,
                               float* conf, float* survival, float* logits_out, float* bias_out, void* ws,
-                              hipStream_t stream, const void* Wg, const void* Wrg, const void* Wrc) {
+                              hipStream_t stream, const void* Wg, const void* Wrg, const void* Wrc,
+                              const uint32_t* w2_bound) {
     if (Wg == nullptr && Wrg == nullptr && chain_eligible(B, r, dtype, W1, W2)) {
         const ChainPlan p = chain_plan(V, H);
         if (p.nwg > 0)
             return launch_chain(p, gamma, V, H, U, h, W1, W2, w_conf, b_conf, x0, gumbel, force, tokens, conf,
-                                survival, logits_out, bias_out, ws, stream);
+                                survival, logits_out, bias_out, ws, stream, w2_bound);
     }
     if (dtype == kBF16)
         return launch_typed<bf16_t>(B, gamma, V, H, r, U, h, W1, W2, w_conf, b_conf, x0, gumbel, force, tokens,

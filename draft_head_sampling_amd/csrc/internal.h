@@ -70,6 +70,10 @@ constexpr uint32_t kPathB1Rebuild = 1u;    // B=1 screen: the norm guess was low
 constexpr uint32_t kPathB1Exchange = 2u;   // B=1: steps settled by the grid-wide per-step exchange
 constexpr uint32_t kPathResident = 4u;     // batched sampler: the resident-W2 kernel ran
 constexpr uint32_t kPathAcceptCluster = 8u;  // accept rate: the cluster kernel ran
+constexpr uint32_t kPathB1Bound = 16u;      // B=1 screen: a precomputed W2 bound replaced the norm stream
+constexpr uint32_t kPathB1BoundStale = 32u;  // B=1: the bound's fingerprint did not match W2 (exchange used)
+constexpr uint32_t kW2BoundTag = 0x5b0d2a7eu;  // last word of a complete dspark_w2_bound result
+constexpr int kW2BoundWords = 8;
 
 __device__ __forceinline__ void mark_gave_up(uint32_t* header) {
     __hip_atomic_store(header + kHdrStatus, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -98,7 +102,10 @@ hipError_t head_sample_launch(int64_t B, int64_t gamma, int64_t V, int64_t H, in
                               const void* h, const void* W1, const void* W2, const void* w_conf, float b_conf,
                               const int32_t* x0, const float* gumbel, const int32_t* force, int32_t* tokens,
                               float* conf, float* survival, float* logits_out, float* bias_out, void* ws,
-                              hipStream_t stream, const void* Wg, const void* Wrg, const void* Wrc);
+                              hipStream_t stream, const void* Wg, const void* Wrg, const void* Wrc,
+                              const uint32_t* w2_bound = nullptr);
+// the weights-only bound of the B = 1 screen (bf16, r = 256): kW2BoundWords words
+hipError_t w2_bound_launch(int64_t V, const void* W2, uint32_t* out, hipStream_t stream);
 
 size_t verify_workspace(int64_t B, int64_t gamma, int64_t V);
 hipError_t verify_launch(int64_t B, int64_t gamma, int64_t V, int dtype, const void* d, const void* t,

@@ -125,6 +125,56 @@ dspark_status_t dspark_head_sample(int64_t B, int64_t gamma, int64_t V, int64_t 
                                    void* stream);
 
 /*
+ * dspark_w2_bound -- weights-only bound for the single-request sampler's
+ * candidate screen ([W] 3.2, the sampling loop: a step's winner is proved
+ * from U and a bound on |W2[v] . e|, and that bound needs the largest row
+ * norm of W2).  Computed once per weight load; dspark_head_sample_w2bound
+ * then skips the pass over W2 that each call otherwise makes for it.
+ *   V >= 1, r == 256, dtype DSPARK_BF16, W2 [V][r] 16-byte aligned (the
+ *   shapes the screen runs on); otherwise DSPARK_ERR_BAD_SHAPE / _BAD_DTYPE.
+ *   bound [DSPARK_W2_BOUND_WORDS] uint32, DEVICE memory, out:
+ *     bound[0]  the largest squared row norm (binary32 bits, rounded as the
+ *               screen rounds it)
+ *     bound[1]  the same over the rows the screen samples (a fingerprint)
+ *     bound[2..6]  V, r and the address of W2 (the rest of the fingerprint)
+ *     bound[7]  a tag, written last
+ * Three small launches on `stream`: one pass over W2 (its cost is that of
+ * reading W2 once).
+ */
+#define DSPARK_W2_BOUND_WORDS 8
+dspark_status_t dspark_w2_bound(int64_t V, int64_t r, int32_t dtype, const void* W2, uint32_t* bound, void* stream);
+
+/*
+ * dspark_head_sample_w2bound -- dspark_head_sample with the bound of
+ * dspark_w2_bound (w2_bound: DEVICE, DSPARK_W2_BOUND_WORDS words; NULL makes
+ * the call identical to dspark_head_sample).  Same arguments, outputs and
+ * rules otherwise.  Only the single-request screen (B = 1, bf16, r = 256)
+ * uses the bound; every other shape ignores it.
+ *   - Verification: the call uses the bound only when its fingerprint names
+ *     this W2 (address, V, r) and the norm of the sampled rows, which the
+ *     call measures anyway, equals bound[1].  With a fingerprint for another
+ *     W2 the call streams W2 as dspark_head_sample does.  With a matching
+ *     address but different sampled rows (W2 changed in place) it proves
+ *     nothing from the bound and settles every step with the grid-wide
+ *     per-step exchange: correct, slower; path flag 32 of
+ *     dspark_workspace_status reports it (16 = the bound was used).
+ *   - A change of W2 in place that leaves the sampled rows as they were is
+ *     not detected: recompute the bound after every change of W2.
+ *   - With a bound that matches, the screen's bound is the measured one,
+ *     never looser than the guess dspark_head_sample starts from, so it
+ *     proves every step that call proves: the tokens are the same, and conf
+ *     and survival are too wherever both calls settle the same steps on the
+ *     screen (a step settled by the exchange instead may differ in the last
+ *     bits of binary32).
+ */
+dspark_status_t dspark_head_sample_w2bound(int64_t B, int64_t gamma, int64_t V, int64_t H, int64_t r, int32_t dtype,
+                                           const void* U, const void* h, const void* W1, const void* W2,
+                                           const void* w_conf, float b_conf, const int32_t* x0, const float* gumbel,
+                                           const int32_t* force, int32_t* tokens, float* conf, float* survival,
+                                           float* logits_out, float* bias_out, const uint32_t* w2_bound,
+                                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * dspark_head_sample_noalloc -- dspark_head_sample for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, outputs and rules as
@@ -346,7 +396,9 @@ size_t dspark_block_loss_workspace_size(int64_t N, int64_t gamma, int64_t V, int
  *           W2 row norm was too small and its step table was rebuilt with the
  *           measured norm; 2 = a B = 1 call settled steps with the grid-wide
  *           per-step exchange; 4 = the batched resident-W2 sampler ran; 8 = the
- *           accept rate's cluster kernel ran.  Diagnostic only: no kernel
+ *           accept rate's cluster kernel ran; 16 = a B = 1 screen used the
+ *           bound of dspark_w2_bound; 32 = that bound's fingerprint did not
+ *           match W2 and the block took the exchange.  Diagnostic only: no kernel
  *           reads this word, so its value never affects a result.
  * workspace_bytes >= 256, 256-byte aligned.  Errors as for the other calls.
  */

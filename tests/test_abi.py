@@ -189,3 +189,15 @@ def test_block_loss_host_checks(L):
     assert _bl(L, ws=FAKE * 256, wsb=need - 1) == WORKSPACE
     assert _bl(L, r=128, ws=FAKE * 256, wsb=need) == BAD_SHAPE  # the tiles are rank 256
     assert _bl(L, W2=FAKE + 2, ws=FAKE * 256, wsb=need) == BAD_SHAPE  # 16-byte rows
+
+
+def test_w2_bound_validation(L):
+    """Host-side checks of dspark_w2_bound (nothing is enqueued)."""
+    import ctypes
+    buf = ctypes.c_void_p(256)  # never dereferenced: every call below fails its checks first
+    assert L.dspark_w2_bound(1000, 256, 0, buf, buf, None) == 3  # fp32: bad dtype
+    assert L.dspark_w2_bound(1000, 128, 1, buf, buf, None) == 2  # rank other than 256
+    assert L.dspark_w2_bound(0, 256, 1, buf, buf, None) == 2     # empty vocabulary
+    assert L.dspark_w2_bound(1000, 256, 1, None, buf, None) == 1
+    assert L.dspark_w2_bound(1000, 256, 1, buf, None, None) == 1
+    assert L.dspark_w2_bound(1000, 256, 1, ctypes.c_void_p(264), buf, None) == 2  # W2 not 16-byte aligned

@@ -816,8 +816,7 @@ struct __align__(16) ScreenLds {  // (16-byte rows: the bias table reads them as
     float pk[kScreenMaxGamma];
     float winf[kScreenMaxGamma];
     uint32_t wkey[kScreenMaxGamma];                 // the windows as ranking-key bounds
-    int tj[kScreenMaxGamma][kERows];                // best candidate of step k after e row r (-1: unproven)
-    int32_t ttok[kScreenMaxGamma][kERows];          // and its token
+    int2 tjt[kScreenMaxGamma][kERows];  // best candidate of step k after e row r (-1: unproven), its token
     uint32_t wtop[kScreenMaxGamma][kScreenWaves][4];  // row workgroup: each wave's best keys
     uint32_t a1[kScreenMaxGamma];
     int sync;                                        // arrivals of the screening waves
@@ -1244,47 +1243,75 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             __syncthreads();  // the bias table is complete
             // a second look at the norms (the streams end about now), read after the walk
             if (poller && nword == 0) nword = __hip_atomic_load(npw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // one thread per (step, e row) pair; every LDS read of a pair is
+            // issued before the first is used, and the candidates of a step
+            // come four at a time (a repeated last index is harmless: its
+            // key is never strictly larger)
+            static_assert(kScreenMaxGamma * kERows <= kChainThreads, "one pair per thread");
             const auto build = [&](uint32_t n2b) {
-                for (int p = tid; p < gamma * kERows; p += kChainThreads) {
-                    const int k = p / kERows, r = p % kERows;
-                    bool pv;  // r can be the e row of step k
-                    if (k == 0) pv = r == kERowAnchor;
-                    else if (sc.fv[k - 1] >= 0) pv = r == kERowForced + k - 1;
-                    else pv = r < nc && sc.cstep[r] == k - 1;
-                    int bj = -1;
-                    int32_t bt = -1;
-                    if (pv && !abort) {
-                        const uint32_t m = sc.stepmask[k];
-                        float tmax = -__builtin_inff();
-                        for (uint32_t bits = m; bits; bits &= bits - 1) tmax = fmaxf(tmax, sc.ct[__builtin_ctz(bits)]);
-                        const float n2 = __builtin_sqrtf(__uint_as_float(n2b));
-                        const float es = sc.esq[r];
-                        const uint32_t ab = sc.fbound[k];
-                        const uint32_t cut = sc.fcut[k];
-                        const float beta = n2 * __builtin_sqrtf(es) * kBetaSlack + kBetaFloor;
-                        const float eps = 5.f * kUlp * (__uint_as_float(ab) + beta);
-                        const double thr = (double)tmax - 2.0 * ((double)beta + eps);
-                        const bool ok = sc.overflow[k] == 0 && finite_bits(ab) && finite_bits(n2b) &&
-                                        finite_bits(bound_bits(es)) && tmax > -__builtin_inff() &&
-                                        thr >= (double)sc.winf[k] && key_upper(cut) < thr;
-                        if (ok) {
-                            uint64_t best = 0;
-                            for (uint32_t bits = m; bits; bits &= bits - 1) {
-                                const int j = __builtin_ctz(bits);
-                                if ((double)sc.ct[j] >= thr) {
-                                    const float lg = sc.cu[j] + sc.bias[j][r];
-                                    const uint64_t key = argmax_key(G ? lg + sc.cg[j] : lg, sc.cv[j]);
-                                    if (key > best) best = key, bj = j;
-                                }
-                            }
-                            // the best listed row is always a candidate, so best != 0
-                            bt = best != 0 ? key_token(best) : -1;
-                            if (best == 0) bj = -1;
-                        }
+                if (tid >= gamma * kERows) return;
+                const int k = tid / kERows, r = tid - k * kERows;
+                const int32_t fprev = sc.fv[k > 0 ? k - 1 : 0];
+                const int csr = sc.cstep[r < kCandMax ? r : 0];
+                const uint32_t m = sc.stepmask[k];
+                const float es = sc.esq[r];
+                const uint32_t ab = sc.fbound[k];
+                const uint32_t cut = sc.fcut[k];
+                const int ovf = sc.overflow[k];
+                const float wf = sc.winf[k];
+                // r can be the e row of step k
+                const bool pv = k == 0 ? r == kERowAnchor
+                                       : fprev >= 0 ? r == kERowForced + k - 1 : r < nc && csr == k - 1;
+                const auto four = [](uint32_t& bits, int (&js)[4]) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        js[u] = bits ? __builtin_ctz(bits) : js[0];
+                        bits &= bits - 1;
                     }
-                    sc.tj[k][r] = bj;
-                    sc.ttok[k][r] = bt;
+                };
+                int bj = -1;
+                int32_t bt = -1;
+                if (pv && !abort) {
+                    float tmax = -__builtin_inff();
+                    for (uint32_t bits = m; bits;) {
+                        int js[4];
+                        four(bits, js);
+                        float a[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) a[u] = sc.ct[js[u]];
+                        tmax = fmaxf(tmax, fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])));
+                    }
+                    const float n2 = __builtin_sqrtf(__uint_as_float(n2b));
+                    const float beta = n2 * __builtin_sqrtf(es) * kBetaSlack + kBetaFloor;
+                    const float eps = 5.f * kUlp * (__uint_as_float(ab) + beta);
+                    const double thr = (double)tmax - 2.0 * ((double)beta + eps);
+                    const bool ok = ovf == 0 && finite_bits(ab) && finite_bits(n2b) && finite_bits(bound_bits(es)) &&
+                                    tmax > -__builtin_inff() && thr >= (double)wf && key_upper(cut) < thr;
+                    if (ok) {
+                        uint64_t best = 0;
+                        for (uint32_t bits = m; bits;) {
+                            int js[4];
+                            four(bits, js);
+                            float c4[4], u4[4], b4[4], g4[4];
+                            uint32_t v4[4];
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                c4[u] = sc.ct[js[u]], u4[u] = sc.cu[js[u]], b4[u] = sc.bias[js[u]][r];
+                                g4[u] = G ? sc.cg[js[u]] : 0.f, v4[u] = sc.cv[js[u]];
+                            }
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                const float lg = u4[u] + b4[u];
+                                const uint64_t key = (double)c4[u] >= thr ? argmax_key(G ? lg + g4[u] : lg, v4[u]) : 0;
+                                if (key > best) best = key, bj = js[u];
+                            }
+                        }
+                        // the best listed row is always a candidate, so best != 0
+                        bt = best != 0 ? key_token(best) : -1;
+                        if (best == 0) bj = -1;
+                    }
                 }
+                sc.tjt[k][r] = make_int2(bj, bt);
             };
             struct Walk {
                 int k, pst;
@@ -1292,23 +1319,35 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 int64_t x;
                 bool valid, fail;
             };
+            // the walk in wave 0: lane r holds column r of the table, and the
+            // chain follows it with lane reads (the e row is wave-uniform)
             const auto walk = [&]() {
                 Walk w{0, 0, -1, xa, true, sc.abort != 0};
+                int2 col[kScreenMaxGamma];
+#pragma unroll
+                for (int k = 0; k < kScreenMaxGamma; ++k) col[k] = sc.tjt[k][lane < kERows ? lane : 0];
+                const int32_t fl = sc.fv[lane < kScreenMaxGamma ? lane : 0];
+                bool run = !w.fail;
                 int cur = kERowAnchor;  // e row of the current step
-                for (; w.k < gamma && !w.fail; ++w.k) {
-                    const int k = w.k;
-                    if (!w.valid) continue;
-                    const int j = sc.tj[k][cur];
-                    if (j < 0) {
-                        w.fail = true;
-                        break;
+#pragma unroll
+                for (int k = 0; k < kScreenMaxGamma; ++k) {
+                    if (run && k < gamma) {  // wave-uniform
+                        if (w.valid) {
+                            const int j = __builtin_amdgcn_readlane(col[k].x, cur);
+                            if (j < 0) {
+                                w.fail = true;
+                                run = false;
+                            } else {
+                                const int32_t tok = __builtin_amdgcn_readlane(col[k].y, cur);
+                                if (lane == k) w.pst = cur, w.tk = tok;
+                                const int32_t f = __builtin_amdgcn_readlane(fl, k);
+                                w.x = f >= 0 ? f : tok;
+                                w.valid = w.x >= 0 && w.x < V;
+                                cur = f >= 0 ? kERowForced + k : j;
+                            }
+                        }
+                        if (run) w.k = k + 1;
                     }
-                    const int32_t tok = sc.ttok[k][cur];
-                    if (lane == k) w.pst = cur, w.tk = tok;
-                    const int32_t f = sc.fv[k];
-                    w.x = f >= 0 ? f : tok;
-                    w.valid = w.x >= 0 && w.x < V;
-                    cur = f >= 0 ? kERowForced + k : j;
                 }
                 return w;
             };
@@ -1322,6 +1361,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             __syncthreads();
             Walk wk{0, 0, -1, xa, true, true};
             if (wave == 0 && !stale) wk = walk();
+            uint32_t nmine = 0;
             if (poller) {
                 uint64_t w = nword;
                 for (int spin = 0; spin < spin_limit && w == 0; ++spin) {
@@ -1329,7 +1369,11 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                     w = __hip_atomic_load(npw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
                 if (w == 0) sc.abort = 1;
-                atomicMax(&sc.n2, (uint32_t)w);
+                nmine = (uint32_t)w;
+            }
+            if (wave >= kChainWaves / 2) {  // the pollers' waves: one LDS atomic each
+                const uint32_t wm = wave_max_u32(nmine);
+                if (lane == 0 && wm != 0) atomicMax(&sc.n2, wm);
             }
             __syncthreads();
             const uint32_t n2b = sc.n2;

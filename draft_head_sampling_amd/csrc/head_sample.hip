@@ -1390,6 +1390,14 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 const int32_t tk = wk.tk;
                 x = wk.x;
                 valid = wk.valid;
+                // the decision first (it needs no confidence), so the row
+                // workgroups are released while this wave writes the outputs
+                const uint64_t d = (fail && !sc.abort)
+                                       ? (kDecideResume | ((uint64_t)k << 32) | (uint64_t)(uint32_t)x)
+                                       : kDecideDone;
+                if (lane == 0) sc.decision = d;
+                if (lane < kCopies)
+                    __hip_atomic_store(aux + lane * kSlotWords, d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 // confidences of the settled steps in parallel, then the running product
                 const int settled = k;
                 float c = 0.f;
@@ -1398,13 +1406,16 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 if (lane < settled) tokens[lane] = tk;
                 float surv = 1.f;
                 bool alive = true;
-                for (int q = 0; q < settled; ++q) {
-                    const float cq = __shfl(c, q);
-                    alive = alive && __shfl(tk, q) >= 0;
-                    surv = surv * cq;
-                    if (lane == q) {
-                        conf[q] = alive ? cq : __builtin_nanf("");
-                        survival[q] = alive ? surv : __builtin_nanf("");
+#pragma unroll
+                for (int q = 0; q < kScreenMaxGamma; ++q) {
+                    if (q < settled) {  // wave-uniform
+                        const float cq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), q));
+                        alive = alive && __builtin_amdgcn_readlane(tk, q) >= 0;
+                        surv = surv * cq;
+                        if (lane == q) {
+                            conf[q] = alive ? cq : __builtin_nanf("");
+                            survival[q] = alive ? surv : __builtin_nanf("");
+                        }
                     }
                 }
                 if (lane == 0) A = surv;
@@ -1413,12 +1424,6 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                     for (int j = lane; j < gamma; j += 64)
                         tokens[j] = -1, conf[j] = __builtin_nanf(""), survival[j] = __builtin_nanf("");
                 }
-                const uint64_t d = (fail && !sc.abort)
-                                       ? (kDecideResume | ((uint64_t)k << 32) | (uint64_t)(uint32_t)x)
-                                       : kDecideDone;
-                if (lane == 0) sc.decision = d;
-                if (lane < kCopies)
-                    __hip_atomic_store(aux + lane * kSlotWords, d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             __syncthreads();
             const uint64_t d = sc.decision;

@@ -816,7 +816,9 @@ struct __align__(16) ScreenLds {  // (16-byte rows: the bias table reads them as
     float pk[kScreenMaxGamma];
     float winf[kScreenMaxGamma];
     uint32_t wkey[kScreenMaxGamma];                 // the windows as ranking-key bounds
-    int2 tjt[kScreenMaxGamma][kERows];  // best candidate of step k after e row r (-1: unproven), its token
+    // after e row r at step k: the e row of step k + 1 (-1: unproven, -2:
+    // the step's token is out of range), and the step's sampled token
+    int2 tjt[kScreenMaxGamma][kERows];
     uint32_t wtop[kScreenMaxGamma][kScreenWaves][4];  // row workgroup: each wave's best keys
     uint32_t a1[kScreenMaxGamma];
     int sync;                                        // arrivals of the screening waves
@@ -1147,16 +1149,24 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             if (!abort) {
                 uint2 ra[kCandPerWave], rb[kCandPerWave];
                 float cu[kCandPerWave], cg[kCandPerWave];
+                // every slot's LDS words first (the slots are in range; unused
+                // ones are discarded below), then every global load unconditionally
+                uint32_t cvl[kCandPerWave];
+                int csl[kCandPerWave];
+#pragma unroll
+                for (int q = 0; q < kCandPerWave; ++q) cvl[q] = sc.cv[wave + kChainWaves * q], csl[q] = sc.cstep[wave + kChainWaves * q];
+                const float* gbase = G ? G : conf;  // without G: some readable word, discarded
 #pragma unroll
                 for (int q = 0; q < kCandPerWave; ++q) {
                     const int j = wave + kChainWaves * q;
                     const bool use = j < nc;
-                    const int64_t v = use ? sc.cv[j] : 0;
-                    const int64_t o = use ? (int64_t)sc.cstep[j] * V + v : 0;
+                    const int64_t v = use ? cvl[q] : 0;
+                    const int64_t o = use ? (int64_t)csl[q] * V + v : 0;
                     ra[q] = reinterpret_cast<const uint2*>(W2 + v * kChainRank)[lane];
                     rb[q] = reinterpret_cast<const uint2*>(W1 + v * kChainRank)[lane];
                     cu[q] = load_elem(U, o);
-                    cg[q] = G ? G[o] : 0.f;
+                    const float gv = gbase[G ? o : 0];
+                    cg[q] = G ? gv : 0.f;
                 }
                 const int kf = wave < gamma ? wave : 0;
                 const int32_t f = sc.fv[kf];
@@ -1252,6 +1262,7 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 if (tid >= gamma * kERows) return;
                 const int k = tid / kERows, r = tid - k * kERows;
                 const int32_t fprev = sc.fv[k > 0 ? k - 1 : 0];
+                const int32_t fk = sc.fv[k];
                 const int csr = sc.cstep[r < kCandMax ? r : 0];
                 const uint32_t m = sc.stepmask[k];
                 const float es = sc.esq[r];
@@ -1311,7 +1322,9 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                         if (best == 0) bj = -1;
                     }
                 }
-                sc.tjt[k][r] = make_int2(bj, bt);
+                const int64_t xk = fk >= 0 ? fk : bt;
+                const int nx = bj < 0 ? -1 : !(xk >= 0 && xk < V) ? -2 : fk >= 0 ? kERowForced + k : bj;
+                sc.tjt[k][r] = make_int2(nx, bt);
             };
             struct Walk {
                 int k, pst;
@@ -1320,7 +1333,8 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 bool valid, fail;
             };
             // the walk in wave 0: lane r holds column r of the table, and the
-            // chain follows it with lane reads (the e row is wave-uniform)
+            // chain follows it with lane reads (the e row is wave-uniform);
+            // lane k keeps step k's e row and token
             const auto walk = [&]() {
                 Walk w{0, 0, -1, xa, true, sc.abort != 0};
                 int2 col[kScreenMaxGamma];
@@ -1329,25 +1343,28 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 const int32_t fl = sc.fv[lane < kScreenMaxGamma ? lane : 0];
                 bool run = !w.fail;
                 int cur = kERowAnchor;  // e row of the current step
+                int last = -1;          // last step with a sampled token
 #pragma unroll
                 for (int k = 0; k < kScreenMaxGamma; ++k) {
                     if (run && k < gamma) {  // wave-uniform
-                        if (w.valid) {
-                            const int j = __builtin_amdgcn_readlane(col[k].x, cur);
-                            if (j < 0) {
-                                w.fail = true;
-                                run = false;
-                            } else {
-                                const int32_t tok = __builtin_amdgcn_readlane(col[k].y, cur);
-                                if (lane == k) w.pst = cur, w.tk = tok;
-                                const int32_t f = __builtin_amdgcn_readlane(fl, k);
-                                w.x = f >= 0 ? f : tok;
-                                w.valid = w.x >= 0 && w.x < V;
-                                cur = f >= 0 ? kERowForced + k : j;
-                            }
+                        const int nx = __builtin_amdgcn_readlane(col[k].x, cur);
+                        if (nx == -1) {
+                            w.fail = true;
+                            run = false;
+                        } else {
+                            const int32_t tok = __builtin_amdgcn_readlane(col[k].y, cur);
+                            if (lane == k) w.pst = cur, w.tk = tok;
+                            last = k;
+                            run = nx >= 0;
+                            w.valid = run;
+                            w.k = run ? k + 1 : gamma;  // past an invalid token the steps are idle
+                            cur = nx;
                         }
-                        if (run) w.k = k + 1;
                     }
+                }
+                if (last >= 0) {
+                    const int32_t f = __builtin_amdgcn_readlane(fl, last);
+                    w.x = f >= 0 ? f : __builtin_amdgcn_readlane(w.tk, last);
                 }
                 return w;
             };

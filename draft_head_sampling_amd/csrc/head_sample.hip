@@ -1413,7 +1413,8 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                                        ? (kDecideResume | ((uint64_t)k << 32) | (uint64_t)(uint32_t)x)
                                        : kDecideDone;
                 if (lane == 0) sc.decision = d;
-                if (lane < kCopies)
+                // (only the copies some row workgroup reads: each is cleared by its last reader)
+                if (lane < kCopies && (lane == 0 ? kCopies : lane) < nwg)
                     __hip_atomic_store(aux + lane * kSlotWords, d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 // confidences of the settled steps in parallel, then the running product
                 const int settled = k;
@@ -1445,18 +1446,9 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
             __syncthreads();
             const uint64_t d = sc.decision;
             if (d & kDecideDone) {
-                // each row workgroup clears its region once it has read the
-                // decision; when all have, the decision word goes back to zero
-                if (tid + 1 < nwg) {
-                    const uint64_t* r = regions + (int64_t)(tid + 1) * kRegionWords;
-                    for (int spin = 0; spin < spin_limit; ++spin) {
-                        if (__hip_atomic_load(r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) break;
-                        __builtin_amdgcn_s_sleep(2);
-                    }
-                }
-                __syncthreads();
-                if (tid < kCopies)
-                    __hip_atomic_store(aux + tid * kSlotWords, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                // each row workgroup clears its own region once it has read
+                // the decision, and the last reader of each decision copy
+                // clears that copy: nothing is left to wait for here
                 done = true;
             } else {
                 k0 = (int)((d >> 32) & 0xffff);
@@ -1598,6 +1590,20 @@ __global__ __launch_bounds__(kChainThreads) void sample_chain_b1(
                 if (d == 0) __builtin_amdgcn_s_sleep(2);
             }
             if (d == 0) mark_gave_up(header);  // the coordinator was lost
+            if (d & kDecideDone) {
+                // count out on this copy (word 1 beside the decision); its
+                // last reader clears both words.  The decision was read above,
+                // before the count.  (Readers of copy c: the workgroups
+                // g >= 1 with g % kCopies == c.)
+                const int c = g % kCopies;
+                const int g0 = c == 0 ? kCopies : c;
+                const uint64_t readers = (uint64_t)((nwg - 1 - g0) / kCopies + 1);
+                const uint64_t prev = __hip_atomic_fetch_add(dcopy + 1, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (prev + 1 == readers) {
+                    __hip_atomic_store(dcopy + 1, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(dcopy, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
             sc.decision = d;
         }
         __syncthreads();
